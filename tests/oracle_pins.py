@@ -1,0 +1,352 @@
+"""Pins for the fp64 oracle: checks against things the oracle does not compute itself.
+
+Each ``pin_*`` takes an implementation namespace (the oracle module, or a planted
+mutant of it in the mutation tests) and raises AssertionError when the
+implementation disagrees with:
+  * hand-worked examples (tests/golden/*.json, each derived by hand from the
+    definitions in the five-fused-kernels table of the mKernel write-up);
+  * brute force built a different way (math.fsum over exact products, element
+    by element, straight from the shards/partials rather than from stacked
+    arrays; Python ``sorted`` over (score, id) pairs for routing);
+  * closed forms (B = I gives C = A; zero peers give the plain GEMM slices;
+    forced routing by a huge bias gives known segment sizes);
+  * exact integer arithmetic (integer-valued inputs make every sum exact);
+  * invariants (segment sizes add up, tokens ascend inside a segment, the
+    gathered rows equal the routed tokens).
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from types import SimpleNamespace
+
+import numpy as np
+
+import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _bf16(x) -> np.ndarray:
+    return wl.f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+def _exact_value(bits: int) -> float:
+    """Value of a bf16 bit pattern from sign/exponent/fraction (IEEE layout), by hand."""
+    sign = -1.0 if bits & 0x8000 else 1.0
+    e = (bits >> 7) & 0xFF
+    f = bits & 0x7F
+    if e == 0:
+        return sign * (f / 128.0) * 2.0 ** -126
+    return sign * (1.0 + f / 128.0) * 2.0 ** (e - 127)
+
+
+def _fsum_dot(row_bits: np.ndarray, col_bits: np.ndarray) -> float:
+    return math.fsum(_exact_value(int(a)) * _exact_value(int(b)) for a, b in zip(row_bits, col_bits))
+
+
+# --------------------------------------------------------------------------------------
+def pin_bf16(impl):
+    g = _golden("bf16_bits.json")
+    for hexbits, val in g["widen"]:
+        got = float(impl.bf16_to_f64(np.array([int(hexbits, 16)], dtype=np.uint16))[0])
+        assert got == val and math.copysign(1, got) == math.copysign(1, val), (hexbits, got, val)
+    # every bf16 pattern that is finite widens to the value given by its fields
+    allbits = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    exp = (allbits >> 7) & 0xFF
+    fin = allbits[exp != 0xFF]
+    got = impl.bf16_to_f64(fin)
+    ref = np.array([_exact_value(int(b)) for b in fin[::97]])
+    assert np.array_equal(got[::97], ref)
+
+
+def pin_ag(impl):
+    g = _golden("ag_hand.json")
+    shards = [_bf16(s) for s in g["a_shards"]]
+    a_g, c = impl.ag_gemm(shards, _bf16(g["b"]))
+    assert np.array_equal(np.asarray(c, dtype=np.float64), np.array(g["c"], dtype=np.float64)), c
+    assert np.array_equal(a_g, np.concatenate(shards, axis=0))
+
+    # brute force on the tiny workload's size: each element from the shards directly
+    shape = wl.AG_TINY
+    d = wl.gen_ag(shape, run=0)
+    a_g, c = impl.ag_gemm(d["a_shards"], d["b"])
+    assert a_g.dtype == np.uint16
+    ref_rms = None
+    rng = np.random.default_rng(5)
+    pts = [(int(rng.integers(shape.m)), int(rng.integers(shape.n))) for _ in range(96)]
+    pts += [(0, 0), (shape.m - 1, shape.n - 1), (shape.m_shard, 7), (2 * shape.m_shard - 1, shape.n - 3)]
+    vals = []
+    for (i, j) in pts:
+        r, ii = divmod(i, shape.m_shard)
+        vals.append(_fsum_dot(d["a_shards"][r][ii], d["b"][:, j]))
+        assert int(a_g[i, 5]) == int(d["a_shards"][r][ii, 5])
+    ref_rms = math.sqrt(sum(v * v for v in vals) / len(vals))
+    for (i, j), v in zip(pts, vals):
+        assert abs(float(c[i, j]) - v) <= 1e-12 * ref_rms, (i, j, float(c[i, j]), v)
+
+    # closed form: B = I (k = n) gives C = A exactly
+    eye = _bf16(np.eye(shape.k, dtype=np.float32))
+    _, c_i = impl.ag_gemm(d["a_shards"], eye)
+    assert np.array_equal(np.asarray(c_i, dtype=np.float64),
+                          np.concatenate([impl.bf16_to_f64(s) for s in d["a_shards"]], axis=0))
+
+    # exact integers: every partial sum is an integer below 2^24
+    di = wl.gen_ag(shape, run=3, kind="int")
+    _, ci = impl.ag_gemm(di["a_shards"], di["b"])
+    ci = np.asarray(ci, dtype=np.float64)
+    assert np.array_equal(ci, np.round(ci))
+    i, j = 3 * shape.m_shard + 17, 200
+    exact = sum(int(_exact_value(int(a))) * int(_exact_value(int(b)))
+                for a, b in zip(di["a_shards"][3][17], di["b"][:, j]))
+    assert ci[i, j] == exact
+
+    # arrival order does not matter: add K-unit contributions in a seeded arrival order
+    order = wl.ag_arrival_order(shape, trial=1)
+    per_unit = np.zeros((shape.m, shape.n), dtype=np.float64)
+    a64 = np.concatenate([impl.bf16_to_f64(s) for s in di["a_shards"]], axis=0)
+    b64 = impl.bf16_to_f64(di["b"])
+    done = np.zeros((shape.n_unit_rows, shape.n_unit_cols), dtype=bool)
+    local = shape.rank
+    spr = shape.m_shard // shape.unit_rows
+    done[local * spr:(local + 1) * spr, :] = True
+    for ur in range(local * spr, (local + 1) * spr):
+        for uc in range(shape.n_unit_cols):
+            rs, cs = ur * shape.unit_rows, uc * shape.unit_cols
+            per_unit[rs:rs + shape.unit_rows] += a64[rs:rs + shape.unit_rows, cs:cs + shape.unit_cols] @ b64[cs:cs + shape.unit_cols]
+    for u in order:
+        ur, uc = divmod(int(u), shape.n_unit_cols)
+        assert not done[ur, uc]
+        done[ur, uc] = True
+        rs, cs = ur * shape.unit_rows, uc * shape.unit_cols
+        per_unit[rs:rs + shape.unit_rows] += a64[rs:rs + shape.unit_rows, cs:cs + shape.unit_cols] @ b64[cs:cs + shape.unit_cols]
+    assert done.all()
+    assert np.array_equal(per_unit, ci)
+
+    # W = 1 reduces to a plain GEMM of the single shard
+    s1 = wl.AGShape(world=1, m_shard=64, k=128, n=64, cfg=wl.CFG_AG_TINY)
+    d1 = wl.gen_ag(s1, run=4, kind="int")
+    _, c1 = impl.ag_gemm(d1["a_shards"], d1["b"])
+    for (i, j) in [(0, 0), (63, 63), (10, 40)]:
+        assert float(c1[i, j]) == _fsum_dot(d1["a_shards"][0][i], d1["b"][:, j])
+
+
+def _rs_brute(a, b, peers, world, rank, i, j):
+    ms = a.shape[0] // world
+    return _fsum_dot(a[rank * ms + i], b[:, j]) + math.fsum(float(peers[q][i, j]) for q in range(world) if q != rank)
+
+
+def pin_rs(impl):
+    g = _golden("rs_hand.json")
+    a, b = _bf16(g["a"]), _bf16(g["b"])
+    for case in g["cases"]:
+        peers = [None] * g["world"]
+        for k_, v in case["peers"].items():
+            peers[int(k_)] = np.array(v, dtype=np.float32)
+        own, outbox = impl.gemm_rs(a, b, peers, g["world"], case["rank"])
+        assert np.array_equal(np.asarray(own, np.float64), np.array(case["own"], np.float64)), (case["rank"], own)
+        for k_, v in case["outbox"].items():
+            assert np.array_equal(np.asarray(outbox[int(k_)], np.float64), np.array(v, np.float64))
+        assert outbox[case["rank"]] is None
+
+    shape = wl.RedShape(m=256, n=96, k=160, world=4, unit_rows=64, unit_cols=32, cfg=wl.CFG_RS)
+    for rank in (0, 2):
+        sh = wl.replace(shape, rank=rank)
+        d = wl.gen_reduce(sh, "rs", run=1)
+        own, outbox = impl.gemm_rs(d["a"], d["b"], d["peers"], sh.world, rank)
+        ms = sh.m_slice
+        rng = np.random.default_rng(rank)
+        pts = [(int(rng.integers(ms)), int(rng.integers(sh.n))) for _ in range(48)] + [(0, 0), (ms - 1, sh.n - 1)]
+        vals = [_rs_brute(d["a"], d["b"], d["peers"], sh.world, rank, i, j) for i, j in pts]
+        sc = math.sqrt(sum(v * v for v in vals) / len(vals))
+        for (i, j), v in zip(pts, vals):
+            assert abs(float(own[i, j]) - v) <= 1e-12 * sc, (rank, i, j)
+        for q in range(sh.world):
+            if q == rank:
+                assert outbox[q] is None
+                continue
+            for (i, j) in pts[:12]:
+                v = _fsum_dot(d["a"][q * ms + i], d["b"][:, j])
+                assert abs(float(outbox[q][i, j]) - v) <= 1e-12 * max(sc, 1.0), (rank, q, i, j)
+
+    # zero peers: own and outboxes are exactly the slices of the plain GEMM (integer inputs)
+    d = wl.gen_reduce(shape, "rs", run=2, kind="int")
+    zero = [None if q == 0 else np.zeros_like(d["peers"][q]) for q in range(shape.world)]
+    own, outbox = impl.gemm_rs(d["a"], d["b"], zero, shape.world, 0)
+    ms = shape.m_slice
+    for q in range(shape.world):
+        blk = own if q == 0 else outbox[q]
+        for (i, j) in [(0, 0), (ms - 1, shape.n - 1), (5, 17)]:
+            assert float(blk[i, j]) == _fsum_dot(d["a"][q * ms + i], d["b"][:, j])
+
+    # cancellation: Q_1 = -P[slice 0] leaves the sum of the other peers
+    own0, _ = impl.gemm_rs(d["a"], d["b"], zero, shape.world, 0)
+    peers = list(d["peers"])
+    peers[1] = (-np.asarray(own0)).astype(np.float32)
+    own, _ = impl.gemm_rs(d["a"], d["b"], peers, shape.world, 0)
+    rest = sum(np.asarray(peers[q], np.float64) for q in range(2, shape.world))
+    assert np.array_equal(np.asarray(own, np.float64), rest)
+
+    # W = 1: own is the whole GEMM, no outbox
+    s1 = wl.RedShape(m=64, n=64, k=64, world=1, cfg=wl.CFG_RS)
+    d1 = wl.gen_reduce(s1, "rs", run=0, kind="int")
+    own, outbox = impl.gemm_rs(d1["a"], d1["b"], d1["peers"], 1, 0)
+    assert outbox == [None]
+    assert float(own[7, 9]) == _fsum_dot(d1["a"][7], d1["b"][:, 9])
+
+
+def pin_ar(impl):
+    g = _golden("ar_hand.json")
+    peers = [None] * g["world"]
+    for k_, v in g["peers"].items():
+        peers[int(k_)] = np.array(v, dtype=np.float32)
+    out = impl.gemm_ar(_bf16(g["a"]), _bf16(g["b"]), peers, g["world"], g["rank"])
+    assert np.array_equal(np.asarray(out, np.float64), np.array(g["out"], np.float64)), out
+
+    shape = wl.RedShape(m=128, n=96, k=192, world=4, unit_rows=64, unit_cols=32, cfg=wl.CFG_AR)
+    for rank in (0, 3):
+        sh = wl.replace(shape, rank=rank)
+        d = wl.gen_reduce(sh, "ar", run=1)
+        out = impl.gemm_ar(d["a"], d["b"], d["peers"], sh.world, rank)
+        rng = np.random.default_rng(10 + rank)
+        pts = [(int(rng.integers(sh.m)), int(rng.integers(sh.n))) for _ in range(48)] + [(sh.m - 1, sh.n - 1)]
+        vals = [_fsum_dot(d["a"][i], d["b"][:, j]) + math.fsum(float(d["peers"][q][i, j]) for q in range(sh.world) if q != rank)
+                for i, j in pts]
+        sc = math.sqrt(sum(v * v for v in vals) / len(vals))
+        for (i, j), v in zip(pts, vals):
+            assert abs(float(out[i, j]) - v) <= 1e-12 * sc, (rank, i, j)
+
+    d = wl.gen_reduce(shape, "ar", run=2, kind="int")
+    zero = [None if q == 0 else np.zeros_like(d["peers"][q]) for q in range(shape.world)]
+    p = impl.gemm_ar(d["a"], d["b"], zero, shape.world, 0)
+    for (i, j) in [(0, 0), (127, 95), (64, 3)]:
+        assert float(p[i, j]) == _fsum_dot(d["a"][i], d["b"][:, j])
+    peers = list(d["peers"])
+    peers[2] = (-np.asarray(p)).astype(np.float32)
+    out = impl.gemm_ar(d["a"], d["b"], peers, shape.world, 0)
+    assert np.array_equal(np.asarray(out, np.float64), np.asarray(peers[1], np.float64) + np.asarray(peers[3], np.float64))
+
+
+def _route_brute(logits, bias, top_k):
+    """Python-level routing: fp32 score per element, sorted on (-score, id)."""
+    out = []
+    for t in range(logits.shape[0]):
+        s = [(-float(np.float32(logits[t, e]) + np.float32(bias[e])), e) for e in range(logits.shape[1])]
+        out.append([e for _, e in sorted(s)[:top_k]])
+    return np.array(out, dtype=np.int32)
+
+
+def pin_moe(impl):
+    g = _golden("moe_hand.json")
+    tokens = [_bf16(t) for t in g["tokens"]]
+    w_up = _bf16(g["w_up"])
+    res = impl.moe_dispatch_gemm(tokens, np.array(g["logits"], np.float32), np.array(g["bias"], np.float32),
+                                 g["top_k"], g["expert_begin"], g["n_local"], w_up)
+    assert np.array_equal(res["topk_idx"], np.array(g["topk_idx"])), res["topk_idx"]
+    assert np.array_equal(res["seg_offsets"], np.array(g["seg_offsets"])), res["seg_offsets"]
+    assert np.array_equal(res["seg_token"], np.array(g["seg_token"])), res["seg_token"]
+    assert np.array_equal(np.asarray(res["y"], np.float64), np.array(g["y"], np.float64)), res["y"]
+    tok_all = np.concatenate(tokens)
+    assert np.array_equal(res["x_seg"], tok_all[np.array(g["seg_token"])])
+
+    # the score is one fp32 add: 1 + 2^-30 rounds to 1 in fp32, so the tie goes to the lower id
+    lg = np.array([[1.0, 1.0, -5.0]], np.float32)
+    bs = np.array([0.0, 2.0 ** -30, 0.0], np.float32)
+    assert impl.moe_route(lg, bs, 1)[0, 0] == 0
+    # ... while a difference fp32 can hold is honoured
+    bs2 = np.array([0.0, 2.0 ** -20, 0.0], np.float32)
+    assert impl.moe_route(lg, bs2, 1)[0, 0] == 1
+
+    # brute-force routing and segments on the small workload
+    shape = wl.MOE_SMALL
+    d = wl.gen_moe(shape, run=0)
+    topk = impl.moe_route(d["logits"], d["bias"], shape.top_k)
+    assert np.array_equal(topk, _route_brute(d["logits"], d["bias"], shape.top_k))
+    offs, seg_token = impl.moe_segments(topk, shape.expert_begin, shape.n_local)
+    segs = [[t for t in range(shape.tokens) if (shape.expert_begin + e) in topk[t].tolist()] for e in range(shape.n_local)]
+    exp_offs = [0]
+    for s in segs:
+        exp_offs.append(exp_offs[-1] + len(s))
+    assert offs.tolist() == exp_offs
+    assert seg_token.tolist() == [t for s in segs for t in s]
+
+    # all experts local: sizes add up to top_k * T, every segment strictly ascending
+    offs_all, st_all = impl.moe_segments(topk, 0, shape.n_experts)
+    assert int(offs_all[-1]) == shape.top_k * shape.tokens
+    assert np.all(np.diff(offs_all) >= 0)
+    for e in range(shape.n_experts):
+        seg = st_all[offs_all[e]:offs_all[e + 1]]
+        assert np.all(np.diff(seg) > 0)
+        assert np.all(np.any(topk[seg] == e, axis=1))
+
+    # forced routing: a huge bias on experts 0 and 1 sends every token to both
+    bias = np.zeros(shape.n_experts, np.float32)
+    bias[:2] = 1e4
+    t2 = impl.moe_route(d["logits"], bias, 2)
+    assert np.array_equal(np.sort(t2, axis=1), np.tile(np.array([0, 1], np.int32), (shape.tokens, 1)))
+    s01 = d["logits"][:, :2].astype(np.float32) + np.float32(1e4)
+    first = np.where(s01[:, 1] > s01[:, 0], 1, 0)  # descending score, ties to the lower id
+    assert np.array_equal(t2[:, 0], first)
+    o2, _ = impl.moe_segments(t2, 0, shape.n_local)
+    assert o2.tolist() == [0, shape.tokens, 2 * shape.tokens] + [2 * shape.tokens] * (shape.n_local - 2)
+    # a huge negative bias on the local experts leaves them empty
+    bias = np.zeros(shape.n_experts, np.float32)
+    bias[:shape.n_local] = -1e4
+    t3 = impl.moe_route(d["logits"], bias, 2)
+    o3, s3 = impl.moe_segments(t3, 0, shape.n_local)
+    assert o3.tolist() == [0] * (shape.n_local + 1) and len(s3) == 0
+
+    # grouped GEMM rows by brute force; gathered rows equal the routed tokens
+    res = impl.moe_dispatch_gemm(d["tokens"], d["logits"], d["bias"], shape.top_k, shape.expert_begin,
+                                 shape.n_local, d["w_up"])
+    tok_all = np.concatenate(d["tokens"])
+    assert np.array_equal(res["x_seg"], tok_all[res["seg_token"]])
+    offs = res["seg_offsets"]
+    y = np.asarray(res["y"], np.float64)
+    rng = np.random.default_rng(3)
+    R = int(offs[-1])
+    rows = [int(rng.integers(R)) for _ in range(24)] + [0, R - 1]
+    for i in rows:
+        e = int(np.searchsorted(offs, i, side="right") - 1)
+        t = int(res["seg_token"][i])
+        for j in (0, shape.ffn - 1, int(rng.integers(shape.ffn))):
+            v = _fsum_dot(tok_all[t], d["w_up"][e][:, j])
+            assert abs(y[i, j] - v) <= 1e-12 * max(1.0, abs(v)), (i, j)
+
+    # a single local expert that every token hits: the grouped GEMM is the plain GEMM of all tokens
+    bias = np.zeros(shape.n_experts, np.float32)
+    bias[0] = 1e4
+    r1 = impl.moe_dispatch_gemm(d["tokens"], d["logits"], bias, 2, 0, 1, d["w_up"][:1])
+    assert r1["seg_offsets"].tolist() == [0, shape.tokens]
+    assert np.array_equal(r1["seg_token"], np.arange(shape.tokens))
+    for t in (0, shape.tokens - 1, 77):
+        assert abs(float(r1["y"][t, 5]) - _fsum_dot(tok_all[t], d["w_up"][0][:, 5])) <= 1e-12 * 10
+
+
+ALL_PINS = [pin_bf16, pin_ag, pin_rs, pin_ar, pin_moe]
+
+
+def run_all(impl):
+    """Names of the pins the implementation fails."""
+    failed = []
+    for p in ALL_PINS:
+        try:
+            p(impl)
+        except AssertionError:
+            failed.append(p.__name__)
+        except (ValueError, IndexError, TypeError, KeyError) as e:  # a broken mutant may also crash
+            failed.append(p.__name__ + ":" + type(e).__name__)
+    return failed
+
+
+def namespace_of(mod, **overrides):
+    ns = SimpleNamespace(**{k: getattr(mod, k) for k in mod.__all__})
+    for k, v in overrides.items():
+        setattr(ns, k, v)
+    return ns

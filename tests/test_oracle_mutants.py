@@ -1,0 +1,212 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the pins catch each one.
+
+Every mutant is a copy of one oracle function with one slip: a dropped term, a
+wrong sign or index, a transposed operand, a wrong precision or tie-break.  The
+test passes when at least one pin fails for every mutant."""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.mk_oracle as M
+import oracle_pins as P
+
+_ORIG_SEGMENTS = M.moe_segments
+
+
+def _bf16_shift15(bits):
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << np.uint32(15)).view(np.float32).astype(np.float64)
+
+
+def _bf16_via_f16(bits):
+    return np.ascontiguousarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def _allgather_reversed(shards):
+    return np.concatenate([np.asarray(s) for s in shards][::-1], axis=0)
+
+
+def _ag_gemm_bt(shards, b):
+    a = M.allgather(shards)
+    return a, M._f64(a) @ M._f64(b).T
+
+
+def _ag_gemm_drop_last(shards, b):
+    a = M.allgather(shards)
+    a64 = M._f64(a)
+    a64[-np.asarray(shards[-1]).shape[0]:] = 0
+    return a, a64 @ M._f64(b)
+
+
+def _rs_drop_peer(a, b, peers, world, rank):
+    ms = a.shape[0] // world
+    p = M._f64(a) @ M._f64(b)
+    own = p[rank * ms:(rank + 1) * ms].copy()
+    for j in range(world - 1):
+        if j != rank:
+            own += M._f64(peers[j])
+    return own, [None if j == rank else p[j * ms:(j + 1) * ms].copy() for j in range(world)]
+
+
+def _rs_slice0(a, b, peers, world, rank):
+    ms = a.shape[0] // world
+    p = M._f64(a) @ M._f64(b)
+    own = p[0:ms].copy()
+    for j in range(world):
+        if j != rank:
+            own += M._f64(peers[j])
+    return own, [None if j == rank else p[j * ms:(j + 1) * ms].copy() for j in range(world)]
+
+
+def _rs_outbox_own_slice(a, b, peers, world, rank):
+    ms = a.shape[0] // world
+    p = M._f64(a) @ M._f64(b)
+    own = p[rank * ms:(rank + 1) * ms].copy()
+    for j in range(world):
+        if j != rank:
+            own += M._f64(peers[j])
+    return own, [None if j == rank else p[rank * ms:(rank + 1) * ms].copy() for j in range(world)]
+
+
+def _rs_sign(a, b, peers, world, rank):
+    ms = a.shape[0] // world
+    p = M._f64(a) @ M._f64(b)
+    own = p[rank * ms:(rank + 1) * ms].copy()
+    for j in range(world):
+        if j != rank:
+            own -= M._f64(peers[j])
+    return own, [None if j == rank else p[j * ms:(j + 1) * ms].copy() for j in range(world)]
+
+
+def _ar_drop_peer(a, b, peers, world, rank):
+    out = M._f64(a) @ M._f64(b)
+    for j in range(1, world - 1):
+        if j != rank:
+            out += M._f64(peers[j])
+    return out
+
+
+def _ar_includes_rank_slot_as_zero_but_skips_first_peer(a, b, peers, world, rank):
+    out = M._f64(a) @ M._f64(b)
+    for j in range(world):
+        if j != rank and j != (rank + 1) % world:
+            out += M._f64(peers[j])
+    return out
+
+
+def _scores_f64(logits, bias):
+    return np.asarray(logits, np.float64) + np.asarray(bias, np.float64)[None, :]
+
+
+def _route_ties_high(logits, bias, top_k):
+    s = M.moe_scores(logits, bias)
+    e = s.shape[1]
+    order = np.argsort(-s[:, ::-1], axis=1, kind="stable")
+    return (e - 1 - order[:, :top_k]).astype(np.int32)
+
+
+def _route_ascending(logits, bias, top_k):
+    s = M.moe_scores(logits, bias)
+    return np.argsort(s, axis=1, kind="stable")[:, :top_k].astype(np.int32)
+
+
+def _route_no_bias(logits, bias, top_k):
+    s = np.asarray(logits, np.float32)
+    return np.argsort(-s, axis=1, kind="stable")[:, :top_k].astype(np.int32)
+
+
+def _segments_first_choice_only(topk_idx, expert_begin, n_local):
+    return _ORIG_SEGMENTS(topk_idx[:, :1], expert_begin, n_local)
+
+
+def _segments_slot_major(topk_idx, expert_begin, n_local):
+    rows = []
+    for e in range(n_local):
+        r = []
+        for k in range(topk_idx.shape[1]):
+            r.extend(np.nonzero(topk_idx[:, k] == expert_begin + e)[0].tolist())
+        rows.append(np.array(r, dtype=np.int32))
+    offs = np.zeros(n_local + 1, dtype=np.int32)
+    offs[1:] = np.cumsum([len(r) for r in rows])
+    return offs, (np.concatenate(rows).astype(np.int32) if rows else np.zeros(0, np.int32))
+
+
+def _segments_ignore_begin(topk_idx, expert_begin, n_local):
+    return _ORIG_SEGMENTS(topk_idx, 0, n_local)
+
+
+def _segments_offsets_shifted(topk_idx, expert_begin, n_local):
+    offs, st = _ORIG_SEGMENTS(topk_idx, expert_begin, n_local)
+    o = offs.copy()
+    o[1:-1] = offs[:-2] if len(offs) > 2 else offs[1:-1]
+    return o, st
+
+
+def _moe_wrong_expert_weight(tokens, logits, bias, top_k, expert_begin, n_local, w_up):
+    res = M.moe_dispatch_gemm(tokens, logits, bias, top_k, expert_begin, n_local, w_up)
+    offs, x = res["seg_offsets"], res["x_seg"]
+    y = np.zeros_like(res["y"])
+    for e in range(n_local):
+        lo, hi = int(offs[e]), int(offs[e + 1])
+        if hi > lo:
+            y[lo:hi] = M._f64(x[lo:hi]) @ M._f64(w_up[(e + 1) % n_local])
+    res["y"] = y
+    return res
+
+
+def _moe_wrong_token_numbering(tokens, logits, bias, top_k, expert_begin, n_local, w_up):
+    res = M.moe_dispatch_gemm(tokens, logits, bias, top_k, expert_begin, n_local, w_up)
+    tok_all = np.concatenate([np.asarray(t) for t in tokens[::-1]], axis=0)
+    res["x_seg"] = tok_all[res["seg_token"]]
+    return res
+
+
+MUTANTS = {
+    "bf16_shift15": ("bf16_to_f64", _bf16_shift15),
+    "bf16_as_fp16": ("bf16_to_f64", _bf16_via_f16),
+    "gather_reversed": ("allgather", _allgather_reversed),
+    "ag_b_transposed": ("ag_gemm", _ag_gemm_bt),
+    "ag_drop_last_shard": ("ag_gemm", _ag_gemm_drop_last),
+    "rs_drop_peer": ("gemm_rs", _rs_drop_peer),
+    "rs_slice0_always": ("gemm_rs", _rs_slice0),
+    "rs_outbox_wrong_slice": ("gemm_rs", _rs_outbox_own_slice),
+    "rs_sign": ("gemm_rs", _rs_sign),
+    "ar_drop_peer": ("gemm_ar", _ar_drop_peer),
+    "ar_skip_next_peer": ("gemm_ar", _ar_includes_rank_slot_as_zero_but_skips_first_peer),
+    "scores_f64": ("moe_scores", _scores_f64),
+    "route_ties_high": ("moe_route", _route_ties_high),
+    "route_ascending": ("moe_route", _route_ascending),
+    "route_no_bias": ("moe_route", _route_no_bias),
+    "segments_first_choice": ("moe_segments", _segments_first_choice_only),
+    "segments_slot_major": ("moe_segments", _segments_slot_major),
+    "segments_ignore_begin": ("moe_segments", _segments_ignore_begin),
+    "segments_offsets_shifted": ("moe_segments", _segments_offsets_shifted),
+    "moe_wrong_expert_weight": ("moe_dispatch_gemm", _moe_wrong_expert_weight),
+    "moe_wrong_token_numbering": ("moe_dispatch_gemm", _moe_wrong_token_numbering),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    if attr in ("moe_dispatch_gemm",):
+        # wrap the original, so keep a handle before patching
+        orig = getattr(M, attr)
+
+        def wrapped(*a, _fn=fn, _orig=orig, **k):
+            monkeypatch.setattr(M, attr, _orig)
+            try:
+                return _fn(*a, **k)
+            finally:
+                monkeypatch.setattr(M, attr, wrapped)
+
+        monkeypatch.setattr(M, attr, wrapped)
+    else:
+        monkeypatch.setattr(M, attr, fn)
+    impl = P.namespace_of(M)
+    failed = P.run_all(impl)
+    assert failed, f"no pin caught mutant {name}"
+
+
+def test_unmutated_oracle_passes_every_pin():
+    assert P.run_all(P.namespace_of(oracle)) == []
