@@ -1,0 +1,81 @@
+"""Build the HIP library (gfx950) and the host-only planning library, in-tree.
+
+    python -m communication_gemm_role_amd.build [--sanitize-host]
+
+libmk.so        every HIP translation unit of csrc/ plus the C ABI, for --offload-arch=gfx950
+libmk_host.so   csrc/mk_host_check.cpp built with g++ alone (no HIP), for CPU tests of the
+                argument validation and planning; --sanitize-host adds ASan/UBSan to it
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libmk.so")
+HOSTLIB = os.path.join(PKG, "libmk_host.so")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+HIP_FLAGS = [
+    "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-Wall", "-Wno-unused-function",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",  # no packed fp32 VALU ops
+    "-I", INCLUDE, "-I", CSRC,
+]
+SOURCES = ["mk_ag_gemm.hip", "mk_gemm_reduce.hip", "mk_moe.hip", "mk_api.cpp"]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("build failed:\n" + " ".join(cmd) + "\n" + r.stdout)
+    return r.stdout
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    lang = ["-x", "hip"] if src.endswith(".cpp") else []
+    _run([HIPCC, *HIP_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+    return obj
+
+
+def build_gpu_lib(jobs: int = 4) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def build_host_lib(sanitize: bool = False) -> str:
+    cmd = ["g++", "-O1", "-g", "-std=c++17", "-shared", "-fPIC", "-Wall", "-I", CSRC]
+    if sanitize:
+        cmd += ["-fsanitize=address,undefined", "-fno-omit-frame-pointer"]
+    tmp = HOSTLIB + ".tmp"
+    _run(cmd + [os.path.join(CSRC, "mk_host_check.cpp"), "-o", tmp])
+    os.replace(tmp, HOSTLIB)
+    return HOSTLIB
+
+
+def build(sanitize_host: bool = False) -> None:
+    build_gpu_lib()
+    build_host_lib(sanitize_host)
+
+
+if __name__ == "__main__":
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--sanitize-host", action="store_true")
+    a = ap.parse_args()
+    build(a.sanitize_host)
+    print(LIB)
+    print(HOSTLIB)
+    sys.exit(0)

@@ -1,0 +1,338 @@
+// C ABI of the fused communication+GEMM library (declared in include/mk.h).
+// Every entry point validates and plans on the host (mk_host_logic.h), then enqueues exactly
+// one persistent kernel on the caller's stream; nothing here allocates or synchronises after
+// mk_ctx_create, except mk_ctx_status which is documented to synchronise.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <new>
+
+#include "../../include/mk.h"
+#include "mk_host_logic.h"
+#include "mk_internal.h"
+
+namespace {
+
+constexpr size_t kDefaultWs = 512ull << 20;
+constexpr size_t kStatusBytes = 256;
+constexpr size_t kCounters = 1u << 20;  // 4 MiB of u32 counters
+constexpr size_t kFlags = 1u << 20;     // 4 MiB of u32 flags
+
+struct DeviceGuard {  // make ctx->device current for the duration of a call
+  int prev = -1;
+  bool ok = false;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) return;
+    ok = (prev == dev) || hipSetDevice(dev) == hipSuccess;
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+mkh::Opts to_opts(const mk_opts* o) {
+  mkh::Opts r;
+  memset(&r, 0, sizeof(r));
+  if (!o) return r;
+  r.n_copy_wg = o->n_copy_wg;
+  r.n_compute_wg = o->n_compute_wg;
+  r.n_reduce_wg = o->n_reduce_wg;
+  r.arrival_mode = o->arrival_mode;
+  r.arrival_order = o->arrival_order;
+  r.arrival_len = o->arrival_len;
+  r.arrival_unit_rows = o->arrival_unit_rows;
+  r.arrival_unit_cols = o->arrival_unit_cols;
+  r.arrival_chunk_tokens = o->arrival_chunk_tokens;
+  r.timeout_us = o->timeout_us;
+  r.test_drop_unit = o->test_drop_unit;
+  return r;
+}
+
+mkh::Ws ws_of(const mk_ctx* c) {
+  mkh::Ws w;
+  w.n_flags = c->n_flags;
+  w.n_counters = c->n_counters;
+  w.inbox_bytes = c->inbox_bytes;
+  w.grid = c->n_cu;
+  return w;
+}
+
+uint64_t timeout_ticks(const mk_opts* o) {
+  const int64_t us = (o && o->timeout_us > 0) ? o->timeout_us : 2000000;
+  return (uint64_t)us * 100ull;  // the device wall clock runs at 100 MHz
+}
+
+// Next epoch; restart from 1 after clearing the flags if the counter would wrap.
+int next_epoch(mk_ctx* c, hipStream_t s) {
+  if (c->epoch >= 0xFFFFFF00u) {
+    if (mk::launch_fill_u32(c->flags, 0u, c->n_flags, s) != hipSuccess) return MK_ERR_HIP;
+    c->epoch = 0;
+  }
+  ++c->epoch;
+  return MK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mk_strerror(int code) {
+  switch (code) {
+    case MK_OK: return "ok";
+    case MK_ERR_INVALID_ARG: return "invalid argument";
+    case MK_ERR_UNSUPPORTED: return "unsupported size, alignment or option";
+    case MK_ERR_WORKSPACE: return "context workspace too small";
+    case MK_ERR_HIP: return "HIP runtime error";
+    case MK_ERR_TIMEOUT: return "device wait timed out";
+    case MK_ERR_CAPACITY: return "routed rows exceed capacity";
+    default: return "unknown error";
+  }
+}
+
+int mk_ctx_create(int device, size_t workspace_bytes, mk_ctx** out) {
+  if (!out) return MK_ERR_INVALID_ARG;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess) return MK_ERR_HIP;
+  if (device < 0 || device >= ndev) return MK_ERR_INVALID_ARG;
+  if (workspace_bytes == 0) workspace_bytes = kDefaultWs;
+  const size_t fixed = kStatusBytes + (kCounters + kFlags) * 4;
+  if (workspace_bytes < fixed) return MK_ERR_WORKSPACE;
+  DeviceGuard g(device);
+  if (!g.ok) return MK_ERR_HIP;
+  mk_ctx* c = new (std::nothrow) mk_ctx();
+  if (!c) return MK_ERR_HIP;
+  c->device = device;
+  if (hipDeviceGetAttribute(&c->n_cu, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) {
+    delete c;
+    return MK_ERR_HIP;
+  }
+  void* ws = nullptr;
+  if (hipMalloc(&ws, workspace_bytes) != hipSuccess) {
+    delete c;
+    return MK_ERR_HIP;
+  }
+  c->ws = (char*)ws;
+  c->ws_bytes = workspace_bytes;
+  c->status = (int*)c->ws;
+  c->counters = (uint32_t*)(c->ws + kStatusBytes);
+  c->n_counters = kCounters;
+  c->flags = c->counters + kCounters;
+  c->n_flags = kFlags;
+  c->inbox = (char*)(c->flags + kFlags);
+  c->inbox_bytes = workspace_bytes - fixed;
+  c->epoch = 0;
+  if (hipMemset(c->ws, 0, fixed) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    (void)hipFree(ws);
+    delete c;
+    return MK_ERR_HIP;
+  }
+  *out = c;
+  return MK_OK;
+}
+
+int mk_ctx_destroy(mk_ctx* ctx) {
+  if (!ctx) return MK_ERR_INVALID_ARG;
+  DeviceGuard g(ctx->device);
+  const hipError_t e = hipFree(ctx->ws);
+  delete ctx;
+  return e == hipSuccess ? MK_OK : MK_ERR_HIP;
+}
+
+int mk_ctx_grid(mk_ctx* ctx) { return ctx ? ctx->n_cu : MK_ERR_INVALID_ARG; }
+
+int mk_ctx_status(mk_ctx* ctx, void* stream) {
+  if (!ctx) return MK_ERR_INVALID_ARG;
+  DeviceGuard g(ctx->device);
+  if (!g.ok) return MK_ERR_HIP;
+  hipStream_t s = (hipStream_t)stream;
+  if (hipStreamSynchronize(s) != hipSuccess) return MK_ERR_HIP;
+  int v = 0;
+  if (hipMemcpy(&v, ctx->status, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess) return MK_ERR_HIP;
+  if (v != 0) {
+    const int zero = 0;
+    if (hipMemcpy(ctx->status, &zero, sizeof(int), hipMemcpyHostToDevice) != hipSuccess) return MK_ERR_HIP;
+  }
+  return v;
+}
+
+int mk_ctx_reset(mk_ctx* ctx, void* stream) {
+  if (!ctx) return MK_ERR_INVALID_ARG;
+  DeviceGuard g(ctx->device);
+  if (!g.ok) return MK_ERR_HIP;
+  hipStream_t s = (hipStream_t)stream;
+  if (mk::launch_fill_u32((uint32_t*)ctx->status, 0u, kStatusBytes / 4, s) != hipSuccess) return MK_ERR_HIP;
+  if (mk::launch_fill_u32(ctx->counters, 0u, ctx->n_counters, s) != hipSuccess) return MK_ERR_HIP;
+  if (mk::launch_fill_u32(ctx->flags, 0u, ctx->n_flags, s) != hipSuccess) return MK_ERR_HIP;
+  ctx->epoch = 0;
+  return MK_OK;
+}
+
+int mk_ag_gemm(mk_ctx* ctx, void* stream, const uint16_t* const* a_shards, int world, int rank, int m_shard, int k,
+               const uint16_t* b, int n, uint16_t* a_gathered, float* c, const mk_opts* opts) {
+  if (!ctx) return MK_ERR_INVALID_ARG;
+  const mkh::Opts o = to_opts(opts);
+  mkh::AgPlan P;
+  int code = mkh::plan_ag(ws_of(ctx), opts ? &o : nullptr, (const void* const*)a_shards, world, rank, m_shard, k, b, n,
+                          a_gathered, c, mk::ag_tile_m(), mk::ag_tile_n(), &P);
+  if (code != MK_OK) return code;
+  DeviceGuard g(ctx->device);
+  if (!g.ok) return MK_ERR_HIP;
+  hipStream_t s = (hipStream_t)stream;
+  if ((code = next_epoch(ctx, s)) != MK_OK) return code;
+  mk::AgParams p;
+  memset(&p, 0, sizeof(p));
+  for (int r = 0; r < world; ++r) p.shards[r] = a_shards ? a_shards[r] : nullptr;
+  p.b = b;
+  p.ag = a_gathered;
+  p.c = c;
+  p.order = (P.emulated && opts) ? (const int32_t*)opts->arrival_order : nullptr;
+  p.flags = ctx->flags;
+  p.status = ctx->status;
+  p.world = world;
+  p.rank = rank;
+  p.m_shard = m_shard;
+  p.m = P.m;
+  p.n = n;
+  p.k = k;
+  p.unit_rows = P.unit_rows;
+  p.unit_cols = P.unit_cols;
+  p.n_ucols = P.n_ucols;
+  p.n_urows = P.n_urows;
+  p.n_copy = P.n_copy;
+  p.n_compute = P.n_compute;
+  p.emulated = P.emulated;
+  p.local_in_place = P.local_in_place;
+  p.n_order = P.n_order;
+  p.drop_pos = P.drop_pos;
+  p.tiles_m = P.tiles_m;
+  p.tiles_n = P.tiles_n;
+  p.epoch = ctx->epoch;
+  p.timeout_ticks = timeout_ticks(opts);
+  return mk::launch_ag_gemm(p, P.n_copy + P.n_compute, s) == hipSuccess ? MK_OK : MK_ERR_HIP;
+}
+
+static int gemm_reduce(int is_rs, mk_ctx* ctx, void* stream, const uint16_t* a, const uint16_t* b, int m, int n,
+                       int k, int world, int rank, const float* const* peers, float* out, float* const* outbox,
+                       const mk_opts* opts) {
+  if (!ctx) return MK_ERR_INVALID_ARG;
+  const mkh::Opts o = to_opts(opts);
+  mkh::RedPlan P;
+  int code = mkh::plan_reduce(ws_of(ctx), opts ? &o : nullptr, is_rs, a, b, m, n, k, world, rank,
+                              (const void* const*)peers, out, (void* const*)outbox, mk::red_tile_m(m, n),
+                              mk::red_tile_n(m, n), &P);
+  if (code != MK_OK) return code;
+  DeviceGuard g(ctx->device);
+  if (!g.ok) return MK_ERR_HIP;
+  hipStream_t s = (hipStream_t)stream;
+  if ((code = next_epoch(ctx, s)) != MK_OK) return code;
+  mk::RedParams p;
+  memset(&p, 0, sizeof(p));
+  p.a = a;
+  p.b = b;
+  for (int j = 0; j < world; ++j) {
+    p.peers[j] = (j == rank || !peers) ? nullptr : peers[j];
+    p.outbox[j] = (j == rank || !outbox) ? nullptr : outbox[j];
+  }
+  p.out = out;
+  p.inbox = (float*)ctx->inbox;
+  p.order = (P.emulated && opts) ? (const int32_t*)opts->arrival_order : nullptr;
+  p.flags = ctx->flags;
+  p.presum_flags = ctx->flags + P.n_units;
+  p.status = ctx->status;
+  p.is_rs = is_rs;
+  p.m = m;
+  p.n = n;
+  p.k = k;
+  p.world = world;
+  p.rank = rank;
+  p.m_slice = P.m_slice;
+  p.p_rows = P.p_rows;
+  p.unit_rows = P.unit_rows;
+  p.unit_cols = P.unit_cols;
+  p.n_ucols = P.n_ucols;
+  p.units_per_peer = P.units_per_peer;
+  p.n_copy = P.n_copy;
+  p.n_reduce = P.n_reduce;
+  p.n_compute = P.n_compute;
+  p.emulated = P.emulated;
+  p.n_order = P.n_order;
+  p.drop_pos = P.drop_pos;
+  p.tiles_m = P.tiles_m;
+  p.tiles_n = P.tiles_n;
+  p.own_tile_begin = P.own_tile_begin;
+  p.own_tile_end = P.own_tile_end;
+  p.epoch = ctx->epoch;
+  p.timeout_ticks = timeout_ticks(opts);
+  return mk::launch_gemm_reduce(p, P.n_copy + P.n_reduce + P.n_compute, s) == hipSuccess ? MK_OK : MK_ERR_HIP;
+}
+
+int mk_gemm_rs(mk_ctx* ctx, void* stream, const uint16_t* a, const uint16_t* b, int m, int n, int k, int world,
+               int rank, const float* const* peer_partials, float* owned_out, float* const* outbox,
+               const mk_opts* opts) {
+  return gemm_reduce(1, ctx, stream, a, b, m, n, k, world, rank, peer_partials, owned_out, outbox, opts);
+}
+
+int mk_gemm_ar(mk_ctx* ctx, void* stream, const uint16_t* a, const uint16_t* b, int m, int n, int k, int world,
+               int rank, const float* const* peer_partials, float* out, const mk_opts* opts) {
+  return gemm_reduce(0, ctx, stream, a, b, m, n, k, world, rank, peer_partials, out, nullptr, opts);
+}
+
+int mk_moe_dispatch_gemm(mk_ctx* ctx, void* stream, const uint16_t* const* tokens, int world, int t_local,
+                         int hidden, const float* logits, const float* bias, int n_experts, int top_k,
+                         int expert_begin, int n_local_experts, const uint16_t* w_up, int ffn, int32_t* topk_idx,
+                         int32_t* seg_offsets, int32_t* seg_token, uint16_t* x_seg, float* y, int capacity_rows,
+                         const mk_opts* opts) {
+  if (!ctx) return MK_ERR_INVALID_ARG;
+  const mkh::Opts o = to_opts(opts);
+  mkh::MoePlan P;
+  int code = mkh::plan_moe(ws_of(ctx), opts ? &o : nullptr, (const void* const*)tokens, world, t_local, hidden, logits,
+                           bias, n_experts, top_k, expert_begin, n_local_experts, w_up, ffn, topk_idx, seg_offsets,
+                           seg_token, x_seg, y, capacity_rows, mk::moe_tile_m(), mk::moe_tile_n(), &P);
+  if (code != MK_OK) return code;
+  DeviceGuard g(ctx->device);
+  if (!g.ok) return MK_ERR_HIP;
+  hipStream_t s = (hipStream_t)stream;
+  if ((code = next_epoch(ctx, s)) != MK_OK) return code;
+  mk::MoeParams p;
+  memset(&p, 0, sizeof(p));
+  for (int r = 0; r < world; ++r) p.tokens[r] = tokens[r];
+  p.logits = logits;
+  p.bias = bias;
+  p.w_up = w_up;
+  p.topk_idx = topk_idx;
+  p.seg_offsets = seg_offsets;
+  p.seg_token = seg_token;
+  p.x_seg = x_seg;
+  p.y = y;
+  p.order = (P.emulated && opts) ? (const int32_t*)opts->arrival_order : nullptr;
+  p.counters = ctx->counters;
+  p.flags = ctx->flags;
+  p.status = ctx->status;
+  p.world = world;
+  p.t_local = t_local;
+  p.hidden = hidden;
+  p.n_experts = n_experts;
+  p.top_k = top_k;
+  p.expert_begin = expert_begin;
+  p.n_local = n_local_experts;
+  p.ffn = ffn;
+  p.capacity = capacity_rows;
+  p.n_tokens = P.n_tokens;
+  p.n_chunks = P.n_chunks;
+  p.n_route = P.n_copy;
+  p.n_copy = P.n_copy;
+  p.n_compute = P.n_compute;
+  p.emulated = P.emulated;
+  p.drop_pos = P.drop_pos;
+  p.tiles_n = P.tiles_n;
+  p.max_mtiles = P.max_mtiles;
+  p.epoch = ctx->epoch;
+  p.timeout_ticks = timeout_ticks(opts);
+  p.off_chunk_cnt = P.off_chunk_cnt;
+  p.off_tile_cnt = P.off_tile_cnt;
+  p.off_misc = P.off_misc;
+  return mk::launch_moe(p, P.n_copy + P.n_compute, s) == hipSuccess ? MK_OK : MK_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,304 @@
+// GEMM + ReduceScatter and GEMM + AllReduce, one rank's share, as one persistent launch.
+//
+// Operations (mKernel write-up, news.chathome.org page, five-fused-kernels table, GEMM +
+// AllReduce and GEMM + ReduceScatter rows): C = A @ B is computed in one launch and each
+// output tile is reduced with the other ranks' partials as soon as it is produced; for the
+// reduce-scatter every tile goes to the rank that owns its rows.
+//
+// This rank's partial is P = A @ B.  Owned rows (RS: the rank's slice; AR: all rows) need
+// out = P + sum of the peers' partials; in RS every other tile goes unreduced to the outbox
+// of its owner.
+//
+// Roles, in workgroup-id order (each waits only on lower ids, which dispatch first):
+//   [0, n_copy)                 copy (emulated mode): lands peer-partial units in the inbox in
+//                               the caller's arrival order and raises each unit's flag.
+//   [n_copy, n_copy+n_reduce)   reduce: for each owned tile, waits for its peer units, sums the
+//                               peer partials with coalesced 16-byte fp32 loads, writes the sum
+//                               into the output tile and raises the tile's pre-sum flag.
+//   the rest                    compute: MFMA tile of P; epilogue adds P to the pre-sum (or, with
+//                               no reduce workgroups, sums the peers itself) and stores the owned
+//                               tile, or stores P to the owner's outbox.  Owned tiles are scheduled
+//                               last so the reduce role has had the whole GEMM to pre-sum them.
+#include "mk_internal.h"
+#include "mk_gemm_tile.hpp"
+
+namespace mk {
+
+using RedBig = TileGemm<256, 256, 2, 2>;   // wide outputs (e.g. 8192 x 4096)
+using RedSkinny = TileGemm<128, 64, 4, 1>;  // few output rows (decode-like, m <= 512)
+
+static inline bool red_skinny(int m, int n) { (void)n; return m <= 512; }
+int red_tile_m(int m, int n) { return red_skinny(m, n) ? RedSkinny::BM : RedBig::BM; }
+int red_tile_n(int m, int n) { return red_skinny(m, n) ? RedSkinny::BN : RedBig::BN; }
+
+// Peer partial q (0..world-2) is rank q < rank ? q : q + 1.
+__device__ __forceinline__ int peer_rank(int rank, int q) { return q < rank ? q : q + 1; }
+
+// Source of peer q's partial: landed inbox copy (emulated) or the resident buffer.
+__device__ __forceinline__ const float* peer_src(const RedParams& p, int q) {
+  return p.emulated ? p.inbox + (size_t)q * p.p_rows * p.n : p.peers[peer_rank(p.rank, q)];
+}
+
+// ------------------------------------------------------------------------------------------
+// copy role (emulated landing of peer partials)
+// ------------------------------------------------------------------------------------------
+__device__ void red_copy_role(const RedParams& p, int cid) {
+  const int tid = threadIdx.x;
+  const int cpr = p.unit_cols >> 2;             // 16-byte chunks per unit row (fp32)
+  const int per_t = (p.unit_rows * cpr) >> 8;   // 4 (64x64) .. 16 (128x128)
+  const uint32_t ldb = (uint32_t)p.n * 4u;
+  const int n_units = (p.world - 1) * p.units_per_peer;
+  for (int pos = cid; pos < p.n_order; pos += p.n_copy) {
+    if (pos + 1 == p.drop_pos) continue;
+    const int u = p.order ? p.order[pos] : pos;
+    if (u < 0 || u >= n_units) continue;
+    const int q = u / p.units_per_peer, w = u - q * p.units_per_peer;
+    const int ur = w / p.n_ucols, uc = w - ur * p.n_ucols;
+    const size_t off = (size_t)ur * p.unit_rows * p.n + (size_t)uc * p.unit_cols;
+    const uint32_t extent = ((uint32_t)(p.unit_rows - 1) * (uint32_t)p.n + (uint32_t)p.unit_cols) * 4u;
+    const auto src = make_rsrc(p.peers[peer_rank(p.rank, q)] + off, extent);
+    const auto dst = make_rsrc(p.inbox + (size_t)q * p.p_rows * p.n + off, extent);
+#pragma unroll
+    for (int h = 0; h < 16; h += 8) {
+      if (h >= per_t) break;
+      u32x4 v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (h + i < per_t) {
+          const int c = tid + ((h + i) << 8);
+          const int row = c / cpr, cc = c - row * cpr;
+          v[i] = bload16_nt(src, (uint32_t)row * ldb + (uint32_t)cc * 16u);
+        }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (h + i < per_t) {
+          const int c = tid + ((h + i) << 8);
+          const int row = c / cpr, cc = c - row * cpr;
+          bstore16_sc1(dst, (uint32_t)row * ldb + (uint32_t)cc * 16u, v[i]);
+        }
+    }
+    wait_mem();
+    __syncthreads();
+    if (tid == 0) flag_store(&p.flags[u], p.epoch);
+  }
+}
+
+// Rows of the owned region covered by tile row tm: [lr0, lr1) in partial coordinates
+// (RS: relative to the owned slice; AR: global rows).  Empty when the tile owns nothing.
+template <class T>
+__device__ __forceinline__ void owned_rows(const RedParams& p, int tm, int& lr0, int& lr1) {
+  const int m0 = tm * T::BM, m1 = min(m0 + T::BM, p.m);
+  if (p.is_rs) {
+    const int o0 = p.rank * p.m_slice, o1 = o0 + p.m_slice;
+    lr0 = max(m0, o0) - o0;
+    lr1 = min(m1, o1) - o0;
+  } else {
+    lr0 = m0;
+    lr1 = m1;
+  }
+}
+
+// One lane of wave 0 per call: wait until every peer unit covering partial rows [lr0, lr1),
+// columns [c0, c1) has landed.  All lanes of the wave call it; returns false on timeout/fault.
+__device__ __forceinline__ bool wait_units(const RedParams& p, int lr0, int lr1, int c0, int c1, int lane) {
+  const int ur0 = lr0 / p.unit_rows, ur1 = (lr1 + p.unit_rows - 1) / p.unit_rows;
+  const int uc0 = c0 / p.unit_cols, uc1 = (c1 + p.unit_cols - 1) / p.unit_cols;
+  const int per_peer = (ur1 - ur0) * (uc1 - uc0);
+  const int total = per_peer * (p.world - 1);
+  bool ok = true;
+  for (int base = 0; base < total; base += 64) {
+    const int i = base + lane;
+    if (i < total) {
+      const int q = i / per_peer, w = i - q * per_peer;
+      const int a = w / (uc1 - uc0), b = w - a * (uc1 - uc0);
+      const int u = q * p.units_per_peer + (ur0 + a) * p.n_ucols + (uc0 + b);
+      ok = spin_until_eq(&p.flags[u], p.epoch, p.timeout_ticks, p.status);
+    }
+    if (__ballot(!ok)) return false;
+  }
+  return true;
+}
+
+// ------------------------------------------------------------------------------------------
+// reduce role: pre-sum the peers' partials of owned tiles
+// ------------------------------------------------------------------------------------------
+template <class T>
+__device__ void red_reduce_role(const RedParams& p, int rid, int* s_ok) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int own_rows = p.own_tile_end - p.own_tile_begin;
+  const int n_jobs = own_rows * p.tiles_n;
+  const uint32_t ld = (uint32_t)p.n * 4u;
+  const int cpr = T::BN >> 2;  // 16-byte chunks per tile row
+  for (int job = rid; job < n_jobs; job += p.n_reduce) {
+    const int tm = p.own_tile_begin + job / p.tiles_n, tn = job % p.tiles_n;
+    int lr0, lr1;
+    owned_rows<T>(p, tm, lr0, lr1);
+    const int c0 = tn * T::BN, c1 = min(c0 + T::BN, p.n);
+    if (p.emulated) {
+      if (wave == 0) {
+        const bool ok = wait_units(p, lr0, lr1, c0, c1, lane);
+        if (lane == 0) *s_ok = ok;
+      }
+      __syncthreads();
+      if (!*s_ok) return;
+    }
+    const int rows = lr1 - lr0, cols = c1 - c0;
+    const int ccols = cols >> 2;  // 16-byte chunks per row in this tile
+    const uint32_t extent = ((uint32_t)(rows - 1) * (uint32_t)p.n + (uint32_t)cols) * 4u;
+    const size_t off = (size_t)lr0 * p.n + c0;
+    const auto dst = make_rsrc(p.out + off, extent);
+    const int total = rows * cpr;
+    for (int base = 0; base < total; base += 256 * 4) {
+      f32x4 s[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+      for (int q = 0; q < p.world - 1; ++q) {
+        const auto src = make_rsrc(peer_src(p, q) + off, extent);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c = base + tid + i * 256;
+          const int row = c / cpr, cc = c - row * cpr;
+          if (c < total && cc < ccols)
+            s[i] += __builtin_bit_cast(f32x4, bload16_nt(src, ((uint32_t)row * (uint32_t)p.n + (uint32_t)cc * 4u) * 4u));
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = base + tid + i * 256;
+        const int row = c / cpr, cc = c - row * cpr;
+        if (c < total && cc < ccols)
+          bstore16_sc1(dst, ((uint32_t)row * (uint32_t)p.n + (uint32_t)cc * 4u) * 4u, __builtin_bit_cast(u32x4, s[i]));
+      }
+    }
+    wait_mem();
+    __syncthreads();
+    if (tid == 0) flag_store(&p.presum_flags[tm * p.tiles_n + tn], p.epoch);
+    (void)ld;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// compute role
+// ------------------------------------------------------------------------------------------
+template <class T>
+__device__ void red_compute_role(const RedParams& p, int slot, char* smem, int* s_ok) {
+  T g;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / T::WN, wn = wave % T::WN;
+  const int n_tiles = p.tiles_m * p.tiles_n;
+  const int nk = p.k >> 6;
+  const int C = p.n_compute;
+  const int rs = ((C & 7) == 0) ? (slot & 7) * (C >> 3) + (slot >> 3) : slot;
+  const uint32_t lda_b = (uint32_t)p.k * 2u, ldb_b = (uint32_t)p.n * 2u;
+  char* lds0 = smem;
+  char* lds1 = smem + T::STAGE;
+
+  for (int t = rs; t < n_tiles; t += C) {
+    // logical tile rows start right after the owned rows, so owned tiles come last
+    const int tml = t / p.tiles_n, tn = t - tml * p.tiles_n;
+    const int tm = (tml + p.own_tile_end) % p.tiles_m;
+    const int m0 = tm * T::BM, n0 = tn * T::BN;
+    const int rows_valid = min(T::BM, p.m - m0), cols_valid = min(T::BN, p.n - n0);
+    const auto ar = make_rsrc(p.a + (size_t)m0 * p.k, (uint32_t)rows_valid * lda_b);
+    const auto br = make_rsrc(p.b + n0, ((uint32_t)p.k * (uint32_t)p.n - (uint32_t)n0) * 2u);
+    g.zero();
+    g.load_a(ar, lda_b, 0, tid);
+    g.load_b(br, ldb_b, 0, tid);
+    g.store_a(lds0, tid);
+    g.store_b(lds0 + T::STAGE_A, tid);
+    __syncthreads();
+    for (int s = 0; s < nk; ++s) {
+      const int pf = s + 1;
+      if (pf < nk) {
+        g.load_a(ar, lda_b, (uint32_t)pf * 128u, tid);
+        g.load_b(br, ldb_b, pf * 64, tid);
+      }
+      char* cur = (s & 1) ? lds1 : lds0;
+      g.mma(cur, cur + T::STAGE_A, wm, wn, lane);
+      if (pf < nk) {
+        char* nxt = (pf & 1) ? lds1 : lds0;
+        g.store_a(nxt, tid);
+        g.store_b(nxt + T::STAGE_A, tid);
+      }
+      __syncthreads();
+    }
+
+    int lr0, lr1;
+    owned_rows<T>(p, tm, lr0, lr1);
+    const bool has_owned = lr1 > lr0;
+    const bool presum = has_owned && p.n_reduce > 0;
+    if (has_owned) {
+      // the peer data this tile adds must have landed (emulated) or been pre-summed (reduce role)
+      if (wave == 0) {
+        bool ok = true;
+        if (presum) {
+          if (lane == 0) ok = spin_until_eq(&p.presum_flags[tm * p.tiles_n + tn], p.epoch, p.timeout_ticks, p.status);
+          ok = __ballot(!ok) == 0;
+        } else if (p.emulated) {
+          ok = wait_units(p, lr0, lr1, n0, n0 + cols_valid, lane);
+        }
+        if (lane == 0) *s_ok = ok;
+      }
+      __syncthreads();
+      if (!*s_ok) return;
+    }
+    const int own0 = p.is_rs ? p.rank * p.m_slice : 0;
+    g.epilogue(smem, wm, wn, lane, wave, [&](int row, int col, f32x4 v) {
+      if (row >= rows_valid || col >= cols_valid) return;
+      const int grow = m0 + row, gcol = n0 + col;
+      if (p.is_rs) {
+        const int owner = grow / p.m_slice;
+        if (owner != p.rank) {  // unreduced partial of another rank's slice -> its outbox
+          const int lrow = grow - owner * p.m_slice;
+          *reinterpret_cast<f32x4*>(p.outbox[owner] + (size_t)lrow * p.n + gcol) = v;
+          return;
+        }
+      }
+      const size_t o = (size_t)(grow - own0) * p.n + gcol;
+      if (presum) {
+        v += *reinterpret_cast<const f32x4*>(p.out + o);
+      } else {
+        for (int q = 0; q < p.world - 1; ++q) v += *reinterpret_cast<const f32x4*>(peer_src(p, q) + o);
+      }
+      *reinterpret_cast<f32x4*>(p.out + o) = v;
+    });
+    __syncthreads();  // the next tile's prologue reuses the LDS
+  }
+}
+
+template <class T>
+__global__ __launch_bounds__(256, 1) void gemm_reduce_kernel(RedParams p) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ int s_ok;
+  const int wg = blockIdx.x;
+  if (wg < p.n_copy) {
+    red_copy_role(p, wg);
+    return;
+  }
+  if (wg < p.n_copy + p.n_reduce) {
+    red_reduce_role<T>(p, wg - p.n_copy, &s_ok);
+    return;
+  }
+  const int slot = wg - p.n_copy - p.n_reduce;
+  if (slot < p.n_compute) red_compute_role<T>(p, slot, smem, &s_ok);
+}
+
+template <class T>
+static hipError_t launch_t(const RedParams& p, int grid, hipStream_t s) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_reduce_kernel<T>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       T::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(gemm_reduce_kernel<T>, dim3(grid), dim3(256), T::LDS_BYTES, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_reduce(const RedParams& p, int grid, hipStream_t s) {
+  return red_skinny(p.m, p.n) ? launch_t<RedSkinny>(p, grid, s) : launch_t<RedBig>(p, grid, s);
+}
+
+}  // namespace mk

@@ -1,0 +1,237 @@
+// Host-side planning for the C ABI: argument validation, arrival-unit geometry, role split
+// and workspace layout.  Pure C++ with no HIP dependency, so the same code is compiled into
+// the GPU library and into a host-only check library that runs on machines without a GPU.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#ifndef MK_OK
+#define MK_OK 0
+#define MK_ERR_INVALID_ARG (-1)
+#define MK_ERR_UNSUPPORTED (-2)
+#define MK_ERR_WORKSPACE (-3)
+#define MK_ERR_HIP (-4)
+#define MK_ERR_TIMEOUT (-5)
+#define MK_ERR_CAPACITY (-6)
+#define MK_ARRIVAL_RESIDENT 1
+#define MK_ARRIVAL_EMULATED 2
+#endif
+
+namespace mkh {
+
+constexpr int kMaxWorld = 8;
+constexpr uint64_t k4G = 1ull << 32;
+
+struct Opts {  // mk_opts with defaults applied by the caller's struct (0 = default)
+  int n_copy_wg, n_compute_wg, n_reduce_wg, arrival_mode;
+  const void* arrival_order;
+  int arrival_len, arrival_unit_rows, arrival_unit_cols, arrival_chunk_tokens;
+  int64_t timeout_us;
+  int test_drop_unit;
+};
+
+struct Ws {  // workspace capacities of a context
+  size_t n_flags, n_counters, inbox_bytes;
+  int grid;  // co-resident workgroups of the persistent launch
+};
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool mult64(int v) { return v > 0 && (v & 63) == 0; }
+
+// Role split: copy workgroups first (a multiple of 8 so they spread over the 8 XCDs), then
+// reduce, then compute.  Requested counts are clamped so at least 8 compute workgroups remain.
+inline int split_roles(int grid, int want_copy, int want_reduce, int want_compute, int* n_copy, int* n_reduce,
+                       int* n_compute) {
+  if (want_copy < 0 || want_reduce < 0 || want_compute < 0) return MK_ERR_INVALID_ARG;
+  if (want_copy + want_reduce + 8 > grid) return MK_ERR_UNSUPPORTED;
+  *n_copy = want_copy;
+  *n_reduce = want_reduce;
+  int rest = grid - want_copy - want_reduce;
+  *n_compute = (want_compute > 0 && want_compute < rest) ? want_compute : rest;
+  return MK_OK;
+}
+
+// ---- AllGather + GEMM ---------------------------------------------------------------------
+struct AgPlan {
+  int m, unit_rows, unit_cols, n_urows, n_ucols, n_order, local_in_place, emulated, drop_pos;
+  int n_copy, n_compute, tiles_m, tiles_n;
+};
+
+inline int plan_ag(const Ws& ws, const Opts* o, const void* const* a_shards, int world, int rank, int m_shard, int k,
+                   const void* b, int n, const void* a_gathered, const void* c, int tile_m, int tile_n, AgPlan* P) {
+  if (!b || !a_gathered || !c) return MK_ERR_INVALID_ARG;
+  if (world < 1 || world > kMaxWorld || rank < 0 || rank >= world) return MK_ERR_INVALID_ARG;
+  if (m_shard <= 0 || k <= 0 || n <= 0) return MK_ERR_INVALID_ARG;
+  const int mode = (o && o->arrival_mode) ? o->arrival_mode : MK_ARRIVAL_EMULATED;
+  if (mode != MK_ARRIVAL_RESIDENT && mode != MK_ARRIVAL_EMULATED) return MK_ERR_INVALID_ARG;
+  if (!mult64(m_shard) || !mult64(k) || !mult64(n)) return MK_ERR_UNSUPPORTED;
+  if (!aligned16(b) || !aligned16(a_gathered) || !aligned16(c)) return MK_ERR_UNSUPPORTED;
+  const uint64_t m = (uint64_t)world * (uint64_t)m_shard;
+  if (m * (uint64_t)k * 2 >= k4G || (uint64_t)k * n * 2 >= k4G || m * (uint64_t)n * 4 >= k4G) return MK_ERR_UNSUPPORTED;
+  int ur = o && o->arrival_unit_rows ? o->arrival_unit_rows : ((m_shard % 128 == 0 && k % 128 == 0) ? 128 : 64);
+  int uc = o && o->arrival_unit_cols ? o->arrival_unit_cols : ((m_shard % 128 == 0 && k % 128 == 0) ? 128 : 64);
+  if ((ur != 64 && ur != 128) || (uc != 64 && uc != 128)) return MK_ERR_UNSUPPORTED;
+  if (m_shard % ur || k % uc) return MK_ERR_UNSUPPORTED;
+  if (k / uc > 64) return MK_ERR_UNSUPPORTED;  // K-unit masks are 64 bits wide
+  if (tile_m % ur) return MK_ERR_UNSUPPORTED;
+  P->m = (int)m;
+  P->unit_rows = ur;
+  P->unit_cols = uc;
+  P->n_urows = (int)(m / ur);
+  P->n_ucols = k / uc;
+  P->emulated = mode == MK_ARRIVAL_EMULATED;
+  P->tiles_m = (int)((m + tile_m - 1) / tile_m);
+  P->tiles_n = (n + tile_n - 1) / tile_n;
+  if ((size_t)P->n_urows * (size_t)P->n_ucols > ws.n_flags) return MK_ERR_WORKSPACE;
+  const void* own_rows = (const char*)a_gathered + (size_t)rank * m_shard * k * 2;
+  P->local_in_place = 1;
+  P->n_order = 0;
+  P->drop_pos = 0;
+  if (P->emulated) {
+    if (!a_shards) return MK_ERR_INVALID_ARG;
+    for (int r = 0; r < world; ++r) {
+      if (r == rank && (a_shards[r] == nullptr || a_shards[r] == own_rows)) continue;
+      if (!a_shards[r]) return MK_ERR_INVALID_ARG;
+      if (!aligned16(a_shards[r])) return MK_ERR_UNSUPPORTED;
+    }
+    P->local_in_place = (a_shards[rank] == nullptr || a_shards[rank] == own_rows) ? 1 : 0;
+    const int spr = m_shard / ur;
+    P->n_order = (world - P->local_in_place) * spr * P->n_ucols;
+    if (o && o->arrival_order && o->arrival_len != P->n_order) return MK_ERR_INVALID_ARG;
+    if (o && o->arrival_order && !aligned16(o->arrival_order) && ((uintptr_t)o->arrival_order & 3u)) return MK_ERR_UNSUPPORTED;
+    P->drop_pos = (o && o->test_drop_unit > 0) ? o->test_drop_unit : 0;
+  }
+  const int want_copy = P->emulated ? ((o && o->n_copy_wg) ? o->n_copy_wg : 32) : 0;
+  if (P->emulated && P->n_order > 0 && want_copy == 0) return MK_ERR_INVALID_ARG;
+  int nr = 0;
+  int code = split_roles(ws.grid, P->emulated ? want_copy : 0, 0, o ? o->n_compute_wg : 0, &P->n_copy, &nr, &P->n_compute);
+  if (code != MK_OK) return code;
+  if (P->emulated && P->n_order == 0) P->n_copy = 0;
+  return MK_OK;
+}
+
+// ---- GEMM + ReduceScatter / AllReduce -----------------------------------------------------------
+struct RedPlan {
+  int m_slice, p_rows, unit_rows, unit_cols, n_ucols, units_per_peer, n_units, emulated, n_order, drop_pos;
+  int n_copy, n_reduce, n_compute, tiles_m, tiles_n, own_tile_begin, own_tile_end;
+  size_t inbox_need;
+};
+
+inline int plan_reduce(const Ws& ws, const Opts* o, int is_rs, const void* a, const void* b, int m, int n, int k,
+                       int world, int rank, const void* const* peers, const void* out, void* const* outbox,
+                       int tile_m, int tile_n, RedPlan* P) {
+  if (!a || !b || !out) return MK_ERR_INVALID_ARG;
+  if (world < 1 || world > kMaxWorld || rank < 0 || rank >= world) return MK_ERR_INVALID_ARG;
+  if (m <= 0 || n <= 0 || k <= 0) return MK_ERR_INVALID_ARG;
+  if (is_rs && (m % world)) return MK_ERR_INVALID_ARG;
+  const int mode = (o && o->arrival_mode) ? o->arrival_mode : MK_ARRIVAL_EMULATED;
+  if (mode != MK_ARRIVAL_RESIDENT && mode != MK_ARRIVAL_EMULATED) return MK_ERR_INVALID_ARG;
+  if (world > 1 && !peers) return MK_ERR_INVALID_ARG;
+  if (is_rs && world > 1 && !outbox) return MK_ERR_INVALID_ARG;
+  for (int j = 0; j < world; ++j) {
+    if (j == rank) continue;
+    if (!peers[j]) return MK_ERR_INVALID_ARG;
+    if (is_rs && !outbox[j]) return MK_ERR_INVALID_ARG;
+  }
+  if (!mult64(m) || !mult64(n) || !mult64(k)) return MK_ERR_UNSUPPORTED;
+  P->m_slice = is_rs ? m / world : m;
+  if (is_rs && !mult64(P->m_slice)) return MK_ERR_UNSUPPORTED;
+  if (!aligned16(a) || !aligned16(b) || !aligned16(out)) return MK_ERR_UNSUPPORTED;
+  for (int j = 0; j < world; ++j) {
+    if (j == rank) continue;
+    if (!aligned16(peers[j])) return MK_ERR_UNSUPPORTED;
+    if (is_rs && !aligned16(outbox[j])) return MK_ERR_UNSUPPORTED;
+  }
+  if ((uint64_t)m * k * 2 >= k4G || (uint64_t)k * n * 2 >= k4G || (uint64_t)m * n * 4 >= k4G) return MK_ERR_UNSUPPORTED;
+  P->p_rows = is_rs ? P->m_slice : m;
+  const bool big = (P->p_rows % 128 == 0) && (n % 128 == 0);
+  int ur = o && o->arrival_unit_rows ? o->arrival_unit_rows : (big ? 128 : 64);
+  int uc = o && o->arrival_unit_cols ? o->arrival_unit_cols : (big ? 128 : 64);
+  if ((ur != 64 && ur != 128) || (uc != 64 && uc != 128)) return MK_ERR_UNSUPPORTED;
+  if (P->p_rows % ur || n % uc) return MK_ERR_UNSUPPORTED;
+  P->unit_rows = ur;
+  P->unit_cols = uc;
+  P->n_ucols = n / uc;
+  P->units_per_peer = (P->p_rows / ur) * P->n_ucols;
+  P->n_units = (world - 1) * P->units_per_peer;
+  P->emulated = (mode == MK_ARRIVAL_EMULATED) && world > 1;
+  P->tiles_m = (m + tile_m - 1) / tile_m;
+  P->tiles_n = (n + tile_n - 1) / tile_n;
+  if (is_rs) {
+    const int o0 = rank * P->m_slice, o1 = o0 + P->m_slice;
+    P->own_tile_begin = o0 / tile_m;
+    P->own_tile_end = (o1 + tile_m - 1) / tile_m;
+  } else {
+    P->own_tile_begin = 0;
+    P->own_tile_end = P->tiles_m;
+  }
+  P->n_order = P->emulated ? P->n_units : 0;
+  P->drop_pos = (P->emulated && o && o->test_drop_unit > 0) ? o->test_drop_unit : 0;
+  P->inbox_need = P->emulated ? (size_t)(world - 1) * P->p_rows * (size_t)n * 4 : 0;
+  if (P->inbox_need > ws.inbox_bytes) return MK_ERR_WORKSPACE;
+  if ((size_t)P->n_units + (size_t)P->tiles_m * P->tiles_n > ws.n_flags) return MK_ERR_WORKSPACE;
+  if (P->emulated && o && o->arrival_order && o->arrival_len != P->n_order) return MK_ERR_INVALID_ARG;
+  const int want_copy = P->emulated ? ((o && o->n_copy_wg) ? o->n_copy_wg : 32) : 0;
+  const int want_reduce = (world > 1 && o) ? o->n_reduce_wg : 0;
+  int code = split_roles(ws.grid, want_copy, want_reduce, o ? o->n_compute_wg : 0, &P->n_copy, &P->n_reduce,
+                         &P->n_compute);
+  if (code != MK_OK) return code;
+  if (world == 1) P->n_reduce = 0;
+  return MK_OK;
+}
+
+// ---- MoE dispatch + grouped GEMM ----------------------------------------------------------------
+struct MoePlan {
+  int n_tokens, n_chunks, emulated, drop_pos, n_copy, n_compute, tiles_n, max_mtiles;
+  int off_misc, off_chunk_cnt, off_tile_cnt;
+  size_t counters_need;
+};
+
+inline int plan_moe(const Ws& ws, const Opts* o, const void* const* tokens, int world, int t_local, int hidden,
+                    const void* logits, const void* bias, int n_experts, int top_k, int expert_begin, int n_local,
+                    const void* w_up, int ffn, const void* topk_idx, const void* seg_offsets, const void* seg_token,
+                    const void* x_seg, const void* y, int capacity, int tile_m, int tile_n, MoePlan* P) {
+  if (!tokens || !logits || !bias || !w_up || !topk_idx || !seg_offsets) return MK_ERR_INVALID_ARG;
+  if (world < 1 || world > kMaxWorld || t_local <= 0 || hidden <= 0 || ffn <= 0) return MK_ERR_INVALID_ARG;
+  if (n_experts <= 0 || top_k <= 0 || top_k > n_experts) return MK_ERR_INVALID_ARG;
+  if (n_local <= 0 || expert_begin < 0 || expert_begin + n_local > n_experts) return MK_ERR_INVALID_ARG;
+  if (capacity < 0) return MK_ERR_INVALID_ARG;
+  if (capacity > 0 && (!seg_token || !x_seg || !y)) return MK_ERR_INVALID_ARG;
+  for (int r = 0; r < world; ++r)
+    if (!tokens[r]) return MK_ERR_INVALID_ARG;
+  const int mode = (o && o->arrival_mode) ? o->arrival_mode : MK_ARRIVAL_EMULATED;
+  if (mode != MK_ARRIVAL_RESIDENT && mode != MK_ARRIVAL_EMULATED) return MK_ERR_INVALID_ARG;
+  if (top_k > 8 || n_experts > 1024 || (n_experts & 3) || n_local > 64) return MK_ERR_UNSUPPORTED;
+  if (!mult64(t_local) || !mult64(hidden) || !mult64(ffn)) return MK_ERR_UNSUPPORTED;
+  if (o && o->arrival_chunk_tokens && o->arrival_chunk_tokens != 64) return MK_ERR_UNSUPPORTED;
+  if (!aligned16(logits) || !aligned16(bias) || !aligned16(w_up) || ((uintptr_t)topk_idx & 3u) ||
+      ((uintptr_t)seg_offsets & 3u))
+    return MK_ERR_UNSUPPORTED;
+  if (capacity > 0 && (!aligned16(x_seg) || !aligned16(y) || ((uintptr_t)seg_token & 3u))) return MK_ERR_UNSUPPORTED;
+  for (int r = 0; r < world; ++r)
+    if (!aligned16(tokens[r])) return MK_ERR_UNSUPPORTED;
+  const uint64_t T = (uint64_t)world * t_local;
+  if ((uint64_t)t_local * hidden * 2 >= k4G || T * n_experts * 4 >= k4G || (uint64_t)capacity * hidden * 2 >= k4G ||
+      (uint64_t)capacity * ffn * 4 >= k4G || (uint64_t)n_local * hidden * ffn * 2 >= k4G || T * top_k * 4 >= k4G)
+    return MK_ERR_UNSUPPORTED;
+  P->n_tokens = (int)T;
+  P->n_chunks = (int)(T / 64);
+  P->emulated = mode == MK_ARRIVAL_EMULATED;
+  if (P->emulated && o && o->arrival_order && o->arrival_len != P->n_chunks) return MK_ERR_INVALID_ARG;
+  P->drop_pos = (P->emulated && o && o->test_drop_unit > 0) ? o->test_drop_unit : 0;
+  P->tiles_n = (ffn + tile_n - 1) / tile_n;
+  P->max_mtiles = capacity / tile_m + n_local + 1;
+  P->off_misc = 0;
+  P->off_chunk_cnt = 128;
+  P->off_tile_cnt = P->off_chunk_cnt + P->n_chunks * n_local;
+  P->counters_need = (size_t)P->off_tile_cnt + (size_t)P->max_mtiles;
+  if (P->counters_need > ws.n_counters || ws.n_flags < 1) return MK_ERR_WORKSPACE;
+  const int want_copy = (o && o->n_copy_wg) ? o->n_copy_wg : 64;
+  int nr = 0;
+  int code = split_roles(ws.grid, want_copy, 0, o ? o->n_compute_wg : 0, &P->n_copy, &nr, &P->n_compute);
+  if (code != MK_OK) return code;
+  if (P->n_copy < 1) return MK_ERR_INVALID_ARG;
+  return MK_OK;
+}
+
+}  // namespace mkh

@@ -1,0 +1,108 @@
+// Internal interface between the C-ABI host layer and the kernel translation units.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#define MK_MAX_WORLD 8
+
+struct mk_ctx {
+  int device;
+  int n_cu;
+  char* ws;         // one device allocation, carved below
+  size_t ws_bytes;
+  int* status;      // device status word (first fault wins)
+  uint32_t* counters;  // zero-initialised counters, left zeroed by every kernel that uses them
+  size_t n_counters;
+  uint32_t* flags;  // epoch-tagged ready flags
+  size_t n_flags;
+  char* inbox;      // landing buffer for emulated peer partials (RS/AR)
+  size_t inbox_bytes;
+  uint32_t epoch;   // call number; a flag is up when it equals the current epoch
+};
+
+namespace mk {
+
+struct AgParams {
+  const uint16_t* shards[MK_MAX_WORLD];
+  const uint16_t* b;
+  uint16_t* ag;
+  float* c;
+  const int32_t* order;
+  uint32_t* flags;
+  int* status;
+  int world, rank, m_shard, m, n, k;
+  int unit_rows, unit_cols, n_ucols, n_urows;
+  int n_copy, n_compute;
+  int emulated, local_in_place;
+  int n_order, drop_pos;
+  int tiles_m, tiles_n;
+  uint32_t epoch;
+  uint64_t timeout_ticks;
+};
+
+struct RedParams {
+  const uint16_t* a;
+  const uint16_t* b;
+  const float* peers[MK_MAX_WORLD];  // resident peer partials (indexed by rank)
+  float* outbox[MK_MAX_WORLD];       // RS only (indexed by rank)
+  float* out;                        // RS: owned slice; AR: full output
+  float* inbox;                      // EMULATED: landing area, (world-1) partials back to back
+  const int32_t* order;
+  uint32_t* flags;                   // landing flags [n_units], then presum flags [tiles]
+  uint32_t* presum_flags;
+  int* status;
+  int is_rs;
+  int m, n, k, world, rank, m_slice;
+  int p_rows;                        // rows of one peer partial (RS: m_slice, AR: m)
+  int unit_rows, unit_cols, n_ucols, units_per_peer;
+  int n_copy, n_reduce, n_compute;
+  int emulated, n_order, drop_pos;
+  int tiles_m, tiles_n;
+  int own_tile_begin, own_tile_end;  // tile rows overlapping the owned slice (RS) or all (AR)
+  uint32_t epoch;
+  uint64_t timeout_ticks;
+};
+
+struct MoeParams {
+  const uint16_t* tokens[MK_MAX_WORLD];
+  const float* logits;
+  const float* bias;
+  const uint16_t* w_up;
+  int32_t* topk_idx;
+  int32_t* seg_offsets;
+  int32_t* seg_token;
+  uint16_t* x_seg;
+  float* y;
+  const int32_t* order;
+  uint32_t* counters;  // [0] route-done, [1] exit count, [2..] per-chunk counts and m-tile counts
+  uint32_t* flags;     // [0] scan-ready flag
+  int* status;
+  int world, t_local, hidden, n_experts, top_k, expert_begin, n_local, ffn, capacity;
+  int n_tokens, n_chunks;
+  int n_route, n_copy, n_compute;  // roles (route is done by every workgroup first)
+  int emulated, drop_pos;
+  int tiles_n, max_mtiles;         // grouped-GEMM tiling: n-tiles per expert, bound on m-tiles
+  uint32_t epoch;
+  uint64_t timeout_ticks;
+  // counter layout (offsets into `counters`)
+  int off_chunk_cnt;   // [n_chunks * n_local] per-chunk routed counts
+  int off_tile_cnt;    // [max_mtiles] rows landed per global m-tile
+  int off_misc;        // [0] route done, [1] exit count
+};
+
+// Launchers (stream-ordered; return hipError_t of the launch)
+hipError_t launch_ag_gemm(const AgParams& p, int grid, hipStream_t s);
+hipError_t launch_gemm_reduce(const RedParams& p, int grid, hipStream_t s);
+hipError_t launch_moe(const MoeParams& p, int grid, hipStream_t s);
+hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t s);
+
+// Tile sizes the host needs for scheduling and validation
+int ag_tile_m();
+int ag_tile_n();
+int red_tile_m(int m, int n);
+int red_tile_n(int m, int n);
+int moe_tile_m();
+int moe_tile_n();
+
+}  // namespace mk

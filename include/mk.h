@@ -1,0 +1,178 @@
+/*
+ * mk.h — C ABI of the fused communication+GEMM library for one MI355X (gfx950).
+ *
+ * One GPU's share of four persistent, role-specialised fused ops, as the mKernel
+ * write-up describes them (page "mKernel：多GPU、多节点融合内核库，实现GPU驱动通信",
+ * news.chathome.org; section "五种融合内核", the five-fused-kernels table, and
+ * section "mKernel的功能" on persistent kernels whose CTAs self-assign the roles
+ * compute / intra-node comm / send / reduce, with a per-shape number of SMs per role):
+ *
+ *   mk_ag_gemm            AllGather + GEMM
+ *   mk_gemm_rs            GEMM + ReduceScatter
+ *   mk_gemm_ar            GEMM + AllReduce
+ *   mk_moe_dispatch_gemm  MoE token dispatch + per-expert grouped GEMM
+ *
+ * Each call is ONE kernel launch.  Inside it, workgroups take a role from their
+ * id and a per-shape split: copy (lands peer data in a given order and raises a
+ * per-unit ready flag), compute (bf16 MFMA tiles with fp32 accumulation, which
+ * consume a unit the moment its flag is up) and reduce (folds peer partials into
+ * output tiles).  Peers are emulated on the one GPU: their shards and partials
+ * are ordinary device buffers, and "arrival" is the copy role writing them into
+ * the landing buffers in the caller's order.
+ *
+ * Conventions
+ *   - bf16 travels as uint16_t raw bits; fp32 as float.  All matrices are dense,
+ *     row-major, with the leading dimension equal to the column count.
+ *   - Every matrix pointer is a DEVICE pointer, 16-byte aligned.  Per-rank pointer
+ *     arrays (a_shards, peer_partials, outbox, tokens) are HOST arrays of length
+ *     `world`, indexed by rank; the entry at `rank` is unused for peer-only arrays.
+ *   - `stream` is a hipStream_t (NULL = the default stream).
+ *   - The caller owns every buffer; the library never allocates or frees caller
+ *     memory.  Buffers must stay alive until the stream work has completed.
+ *   - Outputs must not alias inputs, except that a_shards[rank] may point at its
+ *     own rows inside a_gathered (then the local shard is already in place).
+ *   - Calls are asynchronous: argument errors return synchronously; faults seen
+ *     on the device (a wait that timed out, a capacity overflow) are recorded in
+ *     the context and returned by mk_ctx_status().
+ *   - A context is bound to one device and is not thread-safe; calls that share a
+ *     context must be issued to one stream (they share flags and counters).
+ */
+#ifndef MK_H_
+#define MK_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes ---------------------------------------------------------------- */
+#define MK_OK 0
+#define MK_ERR_INVALID_ARG (-1)  /* null pointer, size <= 0, world not in [1,8], rank not in [0,world),
+                                    rows not divisible by world (RS), top_k > n_experts, bad expert range */
+#define MK_ERR_UNSUPPORTED (-2)  /* a dimension not a multiple of 64 (hidden/ffn/k/n/m as stated per call),
+                                    a pointer not 16-byte aligned, a unit size the kernels do not take */
+#define MK_ERR_WORKSPACE (-3)    /* the context workspace is too small for this call */
+#define MK_ERR_HIP (-4)          /* a HIP runtime call or kernel launch failed */
+#define MK_ERR_TIMEOUT (-5)      /* device: a wait for a flag or counter exceeded opts.timeout_us */
+#define MK_ERR_CAPACITY (-6)     /* device: routed rows exceeded capacity_rows (nothing past it was written) */
+
+/* ---- arrival emulation --------------------------------------------------------- */
+#define MK_ARRIVAL_RESIDENT 1 /* every operand is already in place; no copy role runs */
+#define MK_ARRIVAL_EMULATED 2 /* copy-role workgroups land peer data in `arrival_order` */
+
+typedef struct mk_ctx mk_ctx;
+
+/* Options; pass NULL for defaults.  Zero in any field means "default". */
+typedef struct mk_opts {
+  int n_copy_wg;      /* workgroups that start in the copy role (0: per-shape default) */
+  int n_compute_wg;   /* workgroups in the compute role (0: all the rest)             */
+  int n_reduce_wg;    /* workgroups in the reduce role, RS/AR only (0: per-shape default) */
+  int arrival_mode;   /* MK_ARRIVAL_RESIDENT or MK_ARRIVAL_EMULATED (0: EMULATED)         */
+  const int32_t* arrival_order; /* DEVICE int32 array, the order in which units land (see each
+                                   call); NULL in EMULATED mode = identity order              */
+  int arrival_len;    /* number of entries in arrival_order (must equal the call's unit count) */
+  int arrival_unit_rows; /* AG and RS/AR landing unit, rows (64 or 128; 0: per-shape default)  */
+  int arrival_unit_cols; /* AG and RS/AR landing unit, cols (64 or 128; 0: per-shape default)  */
+  int arrival_chunk_tokens; /* MoE: tokens per arrival chunk; only 64 is supported (0: 64)    */
+  int64_t timeout_us; /* bound on every device-side wait (0: 2 000 000 us)                     */
+  int test_drop_unit; /* testing: position in arrival_order that the copy role skips, so the
+                         consumer of that unit must time out (-1 or 0 = none; values are
+                         1-based positions)                                                   */
+} mk_opts;
+
+/* ---- context ------------------------------------------------------------------------ */
+/* Creates a context on `device` with a workspace of `workspace_bytes` device bytes (0: 512 MiB),
+ * allocated once here; no later call allocates.  The workspace holds ready flags, counters, the
+ * status word and, in EMULATED RS/AR, the landing inbox for peer partials.
+ * Returns MK_OK and sets *out, or an error code (*out untouched). */
+int mk_ctx_create(int device, size_t workspace_bytes, mk_ctx** out);
+/* Frees the workspace.  The caller must have synchronised every stream that used the context. */
+int mk_ctx_destroy(mk_ctx* ctx);
+/* Synchronises `stream`, then returns and clears the device status word: MK_OK, MK_ERR_TIMEOUT
+ * or MK_ERR_CAPACITY (the first fault recorded since the last call of mk_ctx_status). */
+int mk_ctx_status(mk_ctx* ctx, void* stream);
+/* After a fault: clears flags, counters and the status word on `stream` and restarts the epoch. */
+int mk_ctx_reset(mk_ctx* ctx, void* stream);
+/* Co-resident workgroup count the persistent kernels launch with on this device. */
+int mk_ctx_grid(mk_ctx* ctx);
+const char* mk_strerror(int code);
+
+/* ---- AllGather + GEMM ----------------------------------------------------------------
+ * Five-fused-kernels table, AllGather + GEMM row: every rank holds one row shard of A; while
+ * the shards of the other ranks arrive, the local GEMM consumes each A tile as soon as it lands.
+ *   a_shards[r]  [m_shard, k] bf16, r in [0, world)     (host array of device pointers)
+ *   b            [k, n] bf16 (the local, fully resident operand)
+ *   a_gathered   [world*m_shard, k] bf16, OUT: shard r lands at rows [r*m_shard, (r+1)*m_shard)
+ *   c            [world*m_shard, n] fp32, OUT: c = a_gathered @ b
+ * Arrival units are unit_rows x unit_cols blocks of a_gathered, numbered row-major over the unit
+ * grid (id = unit_row * (k/unit_cols) + unit_col).  In EMULATED mode arrival_order lists the ids
+ * of every unit that must be copied: all units of the peers' shards, plus those of the local
+ * shard when a_shards[rank] is not already in place.  In RESIDENT mode a_gathered must already
+ * hold every shard and a_shards may be NULL.
+ * Sizes: m_shard, k, n multiples of 64; m_shard a multiple of unit_rows, k of unit_cols. */
+int mk_ag_gemm(mk_ctx* ctx, void* stream, const uint16_t* const* a_shards, int world, int rank, int m_shard,
+               int k, const uint16_t* b, int n, uint16_t* a_gathered, float* c, const mk_opts* opts);
+
+/* ---- GEMM + ReduceScatter -------------------------------------------------------------
+ * Five-fused-kernels table, GEMM + ReduceScatter row: C = A @ B is reduce-scattered; each output
+ * tile is reduced and handed to its owner as soon as it is produced.  Rank j owns rows
+ * [j*m/world, (j+1)*m/world).  This call is rank `rank`'s share:
+ *   a [m, k] bf16, b [k, n] bf16                 local operands; P = a @ b is this rank's partial
+ *   peer_partials[j] [m/world, n] fp32, j != rank  peer j's partial of THIS rank's slice
+ *   owned_out [m/world, n] fp32, OUT            P[own slice] + sum_j peer_partials[j]
+ *   outbox[j] [m/world, n] fp32, j != rank, OUT  P[slice j] (this rank's unreduced partial of
+ *                                               j's slice, for owner j to sum)
+ * EMULATED mode: peer partials first land, unit by unit in arrival_order, in an inbox inside the
+ * context workspace (units are unit_rows x unit_cols blocks of one peer partial; id =
+ * peer_index * units_per_partial + unit, peers indexed 0..world-2 in ascending rank skipping
+ * `rank`); the reduction consumes each unit once its flag is up.  RESIDENT mode reads them in place.
+ * Sizes: m, n, k multiples of 64; m/world a multiple of 64 and of unit_rows; n of unit_cols. */
+int mk_gemm_rs(mk_ctx* ctx, void* stream, const uint16_t* a, const uint16_t* b, int m, int n, int k, int world,
+               int rank, const float* const* peer_partials, float* owned_out, float* const* outbox,
+               const mk_opts* opts);
+
+/* ---- GEMM + AllReduce -----------------------------------------------------------------
+ * Five-fused-kernels table, GEMM + AllReduce row: C = A @ B in one launch, and every output tile
+ * is reduced with the partial outputs of all ranks as soon as it is produced.
+ *   a [m, k] bf16, b [k, n] bf16; peer_partials[j] [m, n] fp32 for j != rank
+ *   out [m, n] fp32, OUT: a @ b + sum_j peer_partials[j]
+ * Landing units and modes as in mk_gemm_rs, over [m, n] partials.
+ * Sizes: m, n, k multiples of 64; m a multiple of unit_rows, n of unit_cols. */
+int mk_gemm_ar(mk_ctx* ctx, void* stream, const uint16_t* a, const uint16_t* b, int m, int n, int k, int world,
+               int rank, const float* const* peer_partials, float* out, const mk_opts* opts);
+
+/* ---- MoE dispatch + grouped GEMM ------------------------------------------------------
+ * Five-fused-kernels table, MoE Dispatch + GEMM row: tokens are routed to their experts and the
+ * per-expert grouped GEMM runs in the same kernel on tokens as they arrive, with no staging
+ * round trip (each token row lands directly in its final slot).  This call is the share of the
+ * rank that owns experts [expert_begin, expert_begin + n_local_experts):
+ *   tokens[r] [t_local, hidden] bf16, r in [0, world); global token id g = r*t_local + i
+ *   logits [world*t_local, n_experts] fp32; bias [n_experts] fp32
+ *   score = fp32(logit + bias); each token picks the top_k experts by descending score, equal
+ *   scores going to the lower expert id.
+ *   w_up [n_local_experts, hidden, ffn] bf16
+ *   topk_idx [world*t_local, top_k] int32, OUT: every token's experts, in descending score
+ *   seg_offsets [n_local_experts+1] int32, OUT: exclusive prefix sum of the local experts' row
+ *               counts; seg_offsets[n_local_experts] = R, the routed row count
+ *   seg_token [capacity_rows] int32, OUT: rows [seg_offsets[e], seg_offsets[e+1]) list, in
+ *               ascending global id, the tokens routed to local expert e
+ *   x_seg [capacity_rows, hidden] bf16, OUT: x_seg[i] = token seg_token[i] (bitwise)
+ *   y [capacity_rows, ffn] fp32, OUT: y[segment e] = x_seg[segment e] @ w_up[e]
+ * Rows at and past R are not written.  EMULATED mode lands tokens by 64-token chunks (chunk id =
+ * g / 64) in arrival_order (length world*t_local/64); RESIDENT mode has no order (the same copy
+ * runs in identity order).  If R > capacity_rows, the status becomes MK_ERR_CAPACITY and rows
+ * past capacity_rows are dropped.
+ * Sizes: t_local a multiple of 64, hidden and ffn multiples of 64, top_k in [1, 8],
+ * n_experts <= 1024, n_local_experts <= 64. */
+int mk_moe_dispatch_gemm(mk_ctx* ctx, void* stream, const uint16_t* const* tokens, int world, int t_local,
+                         int hidden, const float* logits, const float* bias, int n_experts, int top_k,
+                         int expert_begin, int n_local_experts, const uint16_t* w_up, int ffn, int32_t* topk_idx,
+                         int32_t* seg_offsets, int32_t* seg_token, uint16_t* x_seg, float* y, int capacity_rows,
+                         const mk_opts* opts);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MK_H_ */

@@ -1,0 +1,214 @@
+"""C-ABI boundary checks that run without a GPU.
+
+* libmk.so loads and exports every function include/mk.h declares (no compute calls);
+* the entry points reject a NULL context synchronously;
+* the host planning logic (argument validation, arrival-unit geometry, role split and
+  workspace layout), built into libmk_host.so from the same header the GPU library
+  uses, returns the documented codes and plans.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mk.h")
+
+MK_OK, INVALID, UNSUP, WS = 0, -1, -2, -3
+RESIDENT, EMULATED = 1, 2
+
+
+@pytest.fixture(scope="module")
+def gpulib():
+    from communication_gemm_role_amd import build as B
+    if not os.path.exists(B.LIB):
+        B.build_gpu_lib()
+    return ctypes.CDLL(B.LIB)
+
+
+@pytest.fixture(scope="module")
+def hostlib():
+    from communication_gemm_role_amd import build as B
+    B.build_host_lib(sanitize=False)
+    return ctypes.CDLL(B.HOSTLIB)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mk_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_four_ops():
+    names = declared_functions()
+    for op in ("mk_ag_gemm", "mk_gemm_rs", "mk_gemm_ar", "mk_moe_dispatch_gemm"):
+        assert op in names
+
+
+def test_library_exports_every_declared_symbol(gpulib):
+    missing = [n for n in declared_functions() if not hasattr(gpulib, n)]
+    assert not missing, f"not exported: {missing}"
+
+
+def test_binding_names_match_header():
+    import communication_gemm_role_amd as mk
+    assert sorted(mk.EXPORTED) == declared_functions()
+    for op in ("mk_ag_gemm", "mk_gemm_rs", "mk_gemm_ar", "mk_moe_dispatch_gemm"):
+        assert callable(getattr(mk, op))
+
+
+def test_null_context_is_rejected_synchronously(gpulib):
+    vp = ctypes.c_void_p
+    gpulib.mk_strerror.restype = ctypes.c_char_p
+    assert gpulib.mk_strerror(-5) == b"device wait timed out"
+    assert gpulib.mk_ag_gemm(None, None, None, 8, 0, 64, 64, vp(16), 64, vp(16), vp(16), None) == INVALID
+    assert gpulib.mk_gemm_rs(None, None, vp(16), vp(16), 64, 64, 64, 1, 0, None, vp(16), None, None) == INVALID
+    assert gpulib.mk_gemm_ar(None, None, vp(16), vp(16), 64, 64, 64, 1, 0, None, vp(16), None) == INVALID
+    assert gpulib.mk_ctx_destroy(None) == INVALID
+    assert gpulib.mk_ctx_create(0, 0, None) == INVALID
+
+
+# ---------------------------------------------------------------------------------------------
+# host planning (libmk_host.so)
+# ---------------------------------------------------------------------------------------------
+class Opts(ctypes.Structure):
+    _fields_ = [("n_copy_wg", ctypes.c_int), ("n_compute_wg", ctypes.c_int), ("n_reduce_wg", ctypes.c_int),
+                ("arrival_mode", ctypes.c_int), ("arrival_order", ctypes.c_void_p), ("arrival_len", ctypes.c_int),
+                ("arrival_unit_rows", ctypes.c_int), ("arrival_unit_cols", ctypes.c_int),
+                ("arrival_chunk_tokens", ctypes.c_int), ("timeout_us", ctypes.c_int64),
+                ("test_drop_unit", ctypes.c_int)]
+
+
+NF, NC, INBOX, GRID = 1 << 20, 1 << 20, 256 << 20, 256
+P = lambda addr: ctypes.c_void_p(addr)  # fake device addresses: only alignment is inspected
+
+
+def ag(hostlib, world=8, rank=0, m_shard=1024, k=4096, n=1792, shards="peers", opts=None, b=0x10000,
+       ag_ptr=0x100000000, c=0x200000000):
+    arr = (ctypes.c_void_p * max(world, 1))()
+    for r in range(world):
+        arr[r] = 0x300000000 + r * 0x10000000
+    if shards == "inplace":
+        arr[rank] = ag_ptr + rank * m_shard * k * 2
+    elif shards == "none":
+        arr = None
+    out = (ctypes.c_int * 16)()
+    code = hostlib.mkh_plan_ag(ctypes.c_size_t(NF), ctypes.c_size_t(NC), ctypes.c_size_t(INBOX), GRID,
+                               ctypes.byref(opts) if opts else None, arr, world, rank, m_shard, k, P(b), n, P(ag_ptr),
+                               P(c), 256, 256, out)
+    keys = ["m", "unit_rows", "unit_cols", "n_urows", "n_ucols", "n_order", "local_in_place", "emulated", "drop_pos",
+            "n_copy", "n_compute", "tiles_m", "tiles_n"]
+    return code, dict(zip(keys, list(out)))
+
+
+def test_plan_ag_full_workload(hostlib):
+    code, p = ag(hostlib)
+    assert code == MK_OK
+    assert (p["m"], p["unit_rows"], p["unit_cols"]) == (8192, 128, 128)
+    assert p["n_order"] == 8 * 8 * 32 and p["local_in_place"] == 0  # shard 0 at another address: copied too
+    code, p = ag(hostlib, shards="inplace")
+    assert code == MK_OK and p["local_in_place"] == 1 and p["n_order"] == 7 * 8 * 32
+    assert (p["n_copy"], p["n_compute"], p["tiles_m"], p["tiles_n"]) == (32, 224, 32, 7)
+
+
+def test_plan_ag_errors(hostlib):
+    assert ag(hostlib, world=0)[0] == INVALID
+    assert ag(hostlib, world=9)[0] == INVALID
+    assert ag(hostlib, rank=8)[0] == INVALID
+    assert ag(hostlib, m_shard=100)[0] == UNSUP
+    assert ag(hostlib, n=1800)[0] == UNSUP
+    assert ag(hostlib, b=0x10008)[0] == UNSUP  # misaligned
+    assert ag(hostlib, b=0)[0] == INVALID
+    assert ag(hostlib, shards="none")[0] == INVALID  # emulated needs shards
+    o = Opts(arrival_mode=RESIDENT)
+    assert ag(hostlib, shards="none", opts=o)[0] == MK_OK
+    o = Opts(arrival_mode=7)
+    assert ag(hostlib, opts=o)[0] == INVALID
+    o = Opts(arrival_unit_rows=96)
+    assert ag(hostlib, opts=o)[0] == UNSUP
+    o = Opts(arrival_order=0x5000, arrival_len=5)
+    assert ag(hostlib, opts=o)[0] == INVALID  # wrong order length
+    o = Opts(arrival_order=0x5000, arrival_len=7 * 8 * 32)
+    assert ag(hostlib, shards="inplace", opts=o)[0] == MK_OK
+    assert ag(hostlib, k=64 * 128 + 128)[0] == UNSUP  # more than 64 K-units
+    o = Opts(n_copy_wg=250)
+    assert ag(hostlib, opts=o)[0] == UNSUP  # fewer than 8 compute workgroups left
+
+
+def test_plan_ag_small_units(hostlib):
+    code, p = ag(hostlib, world=4, m_shard=64, k=256, n=256, shards="inplace")
+    assert code == MK_OK and (p["unit_rows"], p["unit_cols"], p["n_order"]) == (64, 64, 12)
+
+
+def red(hostlib, is_rs=1, m=8192, n=4096, k=1792, world=8, rank=0, opts=None, tile=(256, 256), drop_peer=None,
+        a=0x10000, inbox=INBOX):
+    peers = (ctypes.c_void_p * world)()
+    ob = (ctypes.c_void_p * world)()
+    for j in range(world):
+        if j != rank and j != drop_peer:
+            peers[j] = 0x400000000 + j * 0x10000000
+            ob[j] = 0x500000000 + j * 0x10000000
+    out = (ctypes.c_longlong * 20)()
+    code = hostlib.mkh_plan_reduce(ctypes.c_size_t(NF), ctypes.c_size_t(NC), ctypes.c_size_t(inbox), GRID,
+                                   ctypes.byref(opts) if opts else None, is_rs, P(a), P(0x20000), m, n, k, world,
+                                   rank, peers, P(0x30000), ob, tile[0], tile[1], out)
+    keys = ["m_slice", "p_rows", "unit_rows", "unit_cols", "n_ucols", "units_per_peer", "n_units", "emulated",
+            "n_order", "drop_pos", "n_copy", "n_reduce", "n_compute", "tiles_m", "tiles_n", "own_tile_begin",
+            "own_tile_end", "inbox_need"]
+    return code, dict(zip(keys, list(out)))
+
+
+def test_plan_rs_and_ar(hostlib):
+    code, p = red(hostlib)
+    assert code == MK_OK
+    assert (p["m_slice"], p["units_per_peer"], p["n_units"]) == (1024, 8 * 32, 7 * 256)
+    assert (p["own_tile_begin"], p["own_tile_end"], p["inbox_need"]) == (0, 4, 7 * 1024 * 4096 * 4)
+    code, p = red(hostlib, rank=3)
+    assert (p["own_tile_begin"], p["own_tile_end"]) == (12, 16)
+    code, p = red(hostlib, is_rs=0, m=256, n=8192, k=1024, tile=(128, 64))
+    assert code == MK_OK and p["p_rows"] == 256 and p["n_units"] == 7 * 2 * 64
+    assert (p["own_tile_begin"], p["own_tile_end"]) == (0, 2)
+    assert red(hostlib, world=7)[0] == INVALID  # rows not divisible by world
+    assert red(hostlib, m=8 * 96)[0] == UNSUP  # slice 96 rows
+    assert red(hostlib, drop_peer=2)[0] == INVALID  # missing peer partial
+    assert red(hostlib, a=0x10004)[0] == UNSUP
+    assert red(hostlib, inbox=1 << 20)[0] == WS  # emulated landing needs the inbox
+    assert red(hostlib, inbox=1 << 20, opts=Opts(arrival_mode=RESIDENT))[0] == MK_OK
+    code, p = red(hostlib, opts=Opts(n_reduce_wg=32))
+    assert (p["n_copy"], p["n_reduce"], p["n_compute"]) == (32, 32, 192)
+
+
+def moe(hostlib, world=8, t_local=4096, hidden=4096, E=64, top_k=2, eb=0, nl=8, ffn=1536, cap=65536, opts=None,
+        logits=0x10000):
+    toks = (ctypes.c_void_p * world)()
+    for r in range(world):
+        toks[r] = 0x600000000 + r * 0x10000000
+    out = (ctypes.c_longlong * 16)()
+    code = hostlib.mkh_plan_moe(ctypes.c_size_t(NF), ctypes.c_size_t(NC), ctypes.c_size_t(INBOX), GRID,
+                                ctypes.byref(opts) if opts else None, toks, world, t_local, hidden, P(logits),
+                                P(0x20000), E, top_k, eb, nl, P(0x30000), ffn, P(0x40000), P(0x50000), P(0x60000),
+                                P(0x70000), P(0x80000), cap, 128, 256, out)
+    keys = ["n_tokens", "n_chunks", "emulated", "drop_pos", "n_copy", "n_compute", "tiles_n", "max_mtiles", "off_misc",
+            "off_chunk_cnt", "off_tile_cnt", "counters_need"]
+    return code, dict(zip(keys, list(out)))
+
+
+def test_plan_moe(hostlib):
+    code, p = moe(hostlib)
+    assert code == MK_OK
+    assert (p["n_tokens"], p["n_chunks"], p["tiles_n"]) == (32768, 512, 6)
+    assert p["max_mtiles"] == 65536 // 128 + 8 + 1
+    assert p["off_tile_cnt"] == 128 + 512 * 8 and p["counters_need"] <= NC
+    assert moe(hostlib, top_k=65)[0] == INVALID
+    assert moe(hostlib, top_k=9, E=16)[0] == UNSUP
+    assert moe(hostlib, eb=60)[0] == INVALID  # experts past n_experts
+    assert moe(hostlib, t_local=100)[0] == UNSUP
+    assert moe(hostlib, E=66)[0] == UNSUP  # rows of logits must be 16-byte multiples
+    assert moe(hostlib, logits=0x10004)[0] == UNSUP
+    assert moe(hostlib, cap=-1)[0] == INVALID
+    assert moe(hostlib, opts=Opts(arrival_chunk_tokens=32))[0] == UNSUP
+    assert moe(hostlib, opts=Opts(arrival_order=0x9000, arrival_len=3))[0] == INVALID
+    assert moe(hostlib, opts=Opts(arrival_order=0x9000, arrival_len=512))[0] == MK_OK

@@ -1,0 +1,423 @@
+"""HIP path vs the fp64 oracle, through the C ABI.
+
+Small workloads are compared element by element (several tiles plus a ragged tail); the
+full-size workloads, in the launch configuration bench.py times, are compared on sampled
+rows that the oracle computes on its own.  Integer-valued inputs make every fp32 sum exact,
+so those cases must be bit-identical to the oracle whatever the arrival order.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    import communication_gemm_role_amd as mk
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    c = mk.Context(0)
+    yield c
+    torch.cuda.synchronize()
+    c.close()
+
+
+def _mk():
+    import communication_gemm_role_amd as mk
+    return mk
+
+
+# ----------------------------------------------------------------------------------------------
+# AllGather + GEMM
+# ----------------------------------------------------------------------------------------------
+def _run_ag(ctx, shape, data, order=None, mode=None, in_place=True, poison=False, n_copy=0):
+    from gpu_util import dev_bf16, dev_i32
+    mk = _mk()
+    W, r = shape.world, shape.rank
+    b = dev_bf16(data["b"])
+    ag = torch.empty((shape.m, shape.k), dtype=torch.bfloat16, device="cuda")
+    if poison:
+        ag.view(torch.int16).fill_(0x7FC0)  # bf16 quiet NaN: anything read before it lands shows up
+    c = torch.full((shape.m, shape.n), float("nan"), dtype=torch.float32, device="cuda")
+    shards = [dev_bf16(s) for s in data["a_shards"]]
+    if mode == mk.MK_ARRIVAL_RESIDENT:
+        ag.copy_(torch.cat(shards, 0))
+    elif in_place:
+        ag[r * shape.m_shard:(r + 1) * shape.m_shard].copy_(shards[r])
+        shards[r] = ag[r * shape.m_shard:(r + 1) * shape.m_shard]
+    opts = mk.Opts(arrival_mode=mode or 0, arrival_unit_rows=shape.unit_rows, arrival_unit_cols=shape.unit_cols,
+                   arrival_order=dev_i32(order) if order is not None else None, n_copy_wg=n_copy)
+    mk.mk_ag_gemm(ctx, shards, W, r, b, ag, c, opts=opts)
+    assert ctx.status() == mk.MK_OK
+    return ag, c
+
+
+@pytest.mark.parametrize("kind", ["normal", "int"])
+@pytest.mark.parametrize("variant,trial", [("flat", 0), ("flat", 1), ("flat", 2), ("flat", 3), ("flat", 4),
+                                           ("identity", 0), ("reversed", 0), ("shard", 0)])
+def test_ag_tiny(ctx, kind, variant, trial):
+    from gpu_util import assert_close, assert_exact, host, host_bits
+    s = wl.AG_TINY
+    d = wl.gen_ag(s, run=0, kind=kind)
+    order = wl.ag_arrival_order(s, trial=trial, variant=variant)
+    ag, c = _run_ag(ctx, s, d, order=order, poison=True)
+    a_ref, c_ref = oracle.ag_gemm(d["a_shards"], d["b"])
+    assert_exact(host_bits(ag), a_ref, "a_gathered")
+    if kind == "int":
+        assert_exact(host(c), c_ref.astype(np.float32), "C (integer inputs)")
+    else:
+        assert_close(host(c), c_ref, "C")
+
+
+def test_ag_tiny_resident_matches_emulated(ctx):
+    from gpu_util import assert_exact, host
+    mk = _mk()
+    s = wl.AG_TINY
+    d = wl.gen_ag(s, run=2, kind="int")
+    _, c1 = _run_ag(ctx, s, d, mode=mk.MK_ARRIVAL_RESIDENT)
+    _, c2 = _run_ag(ctx, s, d, order=wl.ag_arrival_order(s, trial=7))
+    assert_exact(host(c1), host(c2), "resident vs emulated")
+
+
+@pytest.mark.parametrize("in_place", [True, False])
+@pytest.mark.parametrize("rank", [0, 2])
+def test_ag_ragged(ctx, in_place, rank):
+    """Several 256x256 tiles with ragged M and N tails, 64x64 units, local shard copied or in place."""
+    from gpu_util import assert_close, assert_exact, host, host_bits
+    s = wl.AGShape(world=3, m_shard=192, k=320, n=448, sigma_a=1.0, sigma_b=0.05, unit_rows=64, unit_cols=64,
+                   rank=rank, cfg=wl.CFG_AG_TINY)
+    d = wl.gen_ag(s, run=5)
+    units = wl.ag_peer_units(s, rank)
+    if not in_place:  # the local shard is copied like a peer's: its units join the order
+        spr = s.m_shard // s.unit_rows
+        local = [ur * s.n_unit_cols + uc for ur in range(rank * spr, (rank + 1) * spr) for uc in range(s.n_unit_cols)]
+        units = np.concatenate([units, np.asarray(local, np.int32)])
+    order = units[np.random.default_rng(11).permutation(len(units))].astype(np.int32)
+    ag, c = _run_ag(ctx, s, d, order=order, in_place=in_place, poison=True)
+    a_ref, c_ref = oracle.ag_gemm(d["a_shards"], d["b"])
+    assert_exact(host_bits(ag), a_ref, "a_gathered")
+    assert_close(host(c), c_ref, "C")
+
+
+def test_ag_identity_order_default(ctx):
+    """arrival_order NULL = identity order."""
+    from gpu_util import assert_close, host
+    s = wl.AG_TINY
+    d = wl.gen_ag(s, run=1)
+    _, c = _run_ag(ctx, s, d, order=None)
+    assert_close(host(c), oracle.ag_gemm(d["a_shards"], d["b"])[1], "C")
+
+
+@pytest.mark.parametrize("mode", ["emulated", "resident"])
+def test_ag_full_sampled(ctx, mode):
+    """The full AllGather+GEMM workload (W=8, M=8192, N=1792, K=4096), bench launch configuration."""
+    from gpu_util import assert_close, assert_exact, host, host_bits, log
+    mk = _mk()
+    s = wl.AG_MLP
+    d = wl.gen_ag(s, run=0)
+    log(f"ag full {mode}: launching")
+    m = mk.MK_ARRIVAL_EMULATED if mode == "emulated" else mk.MK_ARRIVAL_RESIDENT
+    ag, c = _run_ag(ctx, s, d, order=wl.ag_arrival_order(s, trial=0) if mode == "emulated" else None, mode=m)
+    torch.cuda.synchronize()
+    assert_exact(host_bits(ag), oracle.allgather(d["a_shards"]), "a_gathered")
+    rows = np.sort(np.random.default_rng(1).choice(s.m, 48, replace=False))
+    sub = [d["a_shards"][i // s.m_shard][i % s.m_shard][None, :] for i in rows]
+    _, c_ref = oracle.ag_gemm(sub, d["b"])
+    assert_close(host(c)[rows], c_ref, "C sampled rows")
+
+
+def test_ag_full_integer_order_invariant(ctx):
+    """Integer inputs at full size: emulated (two orders) and resident results are bit-identical."""
+    from gpu_util import assert_exact, host
+    mk = _mk()
+    s = wl.AG_MLP
+    d = wl.gen_ag(s, run=1, kind="int")
+    _, c0 = _run_ag(ctx, s, d, mode=mk.MK_ARRIVAL_RESIDENT)
+    _, c1 = _run_ag(ctx, s, d, order=wl.ag_arrival_order(s, trial=1))
+    _, c2 = _run_ag(ctx, s, d, order=wl.ag_arrival_order(s, trial=2, variant="shard"))
+    h0 = host(c0)
+    assert_exact(host(c1), h0, "emulated order 1 vs resident")
+    assert_exact(host(c2), h0, "emulated shard order vs resident")
+    rows = np.array([0, 1023, 1024, 5000, 8191])
+    sub = [d["a_shards"][i // s.m_shard][i % s.m_shard][None, :] for i in rows]
+    _, c_ref = oracle.ag_gemm(sub, d["b"])
+    assert_exact(h0[rows], c_ref.astype(np.float32), "C rows (integer)")
+
+
+# ----------------------------------------------------------------------------------------------
+# GEMM + ReduceScatter / AllReduce
+# ----------------------------------------------------------------------------------------------
+def _run_red(ctx, op, shape, data, mode, order=None, n_reduce=0, n_copy=0):
+    from gpu_util import dev_bf16, dev_f32, dev_i32
+    mk = _mk()
+    W, r = shape.world, shape.rank
+    a, b = dev_bf16(data["a"]), dev_bf16(data["b"])
+    peers = [None if p is None else dev_f32(p) for p in data["peers"]]
+    opts = mk.Opts(arrival_mode=mode, n_reduce_wg=n_reduce, n_copy_wg=n_copy,
+                   arrival_unit_rows=shape.unit_rows, arrival_unit_cols=shape.unit_cols,
+                   arrival_order=dev_i32(order) if order is not None else None)
+    if op == "rs":
+        own = torch.full((shape.m_slice, shape.n), float("nan"), device="cuda")
+        outbox = [None if j == r else torch.full((shape.m_slice, shape.n), float("nan"), device="cuda")
+                  for j in range(W)]
+        mk.mk_gemm_rs(ctx, a, b, W, r, peers, own, outbox, opts=opts)
+        assert ctx.status() == mk.MK_OK
+        return own, outbox
+    out = torch.full((shape.m, shape.n), float("nan"), device="cuda")
+    mk.mk_gemm_ar(ctx, a, b, W, r, peers, out, opts=opts)
+    assert ctx.status() == mk.MK_OK
+    return out, None
+
+
+RED_CASES = [("resident", 0), ("resident", 16), ("emulated", 0), ("emulated", 16)]
+
+
+@pytest.mark.parametrize("mode,n_reduce", RED_CASES)
+@pytest.mark.parametrize("rank", [0, 3])
+@pytest.mark.parametrize("kind", ["normal", "int"])
+def test_rs_small(ctx, mode, n_reduce, rank, kind):
+    from gpu_util import assert_close, assert_exact, host
+    mk = _mk()
+    s = wl.replace(wl.RS_SMALL, rank=rank)
+    d = wl.gen_reduce(s, "rs", run=0, kind=kind)
+    em = mode == "emulated"
+    order = wl.reduce_arrival_order(s, "rs", trial=rank) if em else None
+    own, outbox = _run_red(ctx, "rs", s, d, mk.MK_ARRIVAL_EMULATED if em else mk.MK_ARRIVAL_RESIDENT, order, n_reduce)
+    own_ref, ob_ref = oracle.gemm_rs(d["a"], d["b"], d["peers"], s.world, rank)
+    check = (lambda o, r_, w: assert_exact(o, r_.astype(np.float32), w)) if kind == "int" else assert_close
+    check(host(own), own_ref, "owned slice")
+    for j in range(s.world):
+        if j != rank:
+            check(host(outbox[j]), ob_ref[j], f"outbox[{j}]")
+
+
+@pytest.mark.parametrize("mode,n_reduce", RED_CASES)
+@pytest.mark.parametrize("rank", [0, 5])
+@pytest.mark.parametrize("kind", ["normal", "int"])
+def test_ar_small(ctx, mode, n_reduce, rank, kind):
+    from gpu_util import assert_close, assert_exact, host
+    mk = _mk()
+    s = wl.replace(wl.AR_SMALL, rank=rank)
+    d = wl.gen_reduce(s, "ar", run=0, kind=kind)
+    em = mode == "emulated"
+    order = wl.reduce_arrival_order(s, "ar", trial=rank, variant="reversed" if rank else "flat") if em else None
+    out, _ = _run_red(ctx, "ar", s, d, mk.MK_ARRIVAL_EMULATED if em else mk.MK_ARRIVAL_RESIDENT, order, n_reduce)
+    ref = oracle.gemm_ar(d["a"], d["b"], d["peers"], s.world, rank)
+    if kind == "int":
+        assert_exact(host(out), ref.astype(np.float32), "AR out")
+    else:
+        assert_close(host(out), ref, "AR out")
+
+
+@pytest.mark.parametrize("mode", ["resident", "emulated"])
+def test_rs_full_sampled(ctx, mode):
+    from gpu_util import assert_close, host, log
+    mk = _mk()
+    s = wl.RS_DOWN
+    d = wl.gen_reduce(s, "rs", run=0)
+    em = mode == "emulated"
+    log(f"rs full {mode}: launching")
+    own, outbox = _run_red(ctx, "rs", s, d, mk.MK_ARRIVAL_EMULATED if em else mk.MK_ARRIVAL_RESIDENT,
+                           wl.reduce_arrival_order(s, "rs") if em else None)
+    lr = np.sort(np.random.default_rng(3).choice(s.m_slice, 16, replace=False))
+    a_sub = np.concatenate([d["a"][j * s.m_slice + lr] for j in range(s.world)])
+    peers_sub = [None if p is None else p[lr] for p in d["peers"]]
+    own_ref, ob_ref = oracle.gemm_rs(a_sub, d["b"], peers_sub, s.world, 0)
+    assert_close(host(own)[lr], own_ref, "owned slice rows")
+    for j in range(1, s.world):
+        assert_close(host(outbox[j])[lr], ob_ref[j], f"outbox[{j}] rows")
+
+
+@pytest.mark.parametrize("mode", ["resident", "emulated"])
+def test_ar_full_sampled(ctx, mode):
+    from gpu_util import assert_close, host, log
+    mk = _mk()
+    s = wl.AR_DECODE
+    d = wl.gen_reduce(s, "ar", run=0)
+    em = mode == "emulated"
+    log(f"ar full {mode}: launching")
+    out, _ = _run_red(ctx, "ar", s, d, mk.MK_ARRIVAL_EMULATED if em else mk.MK_ARRIVAL_RESIDENT,
+                      wl.reduce_arrival_order(s, "ar") if em else None)
+    rows = np.sort(np.random.default_rng(4).choice(s.m, 24, replace=False))
+    ref = oracle.gemm_ar(d["a"][rows], d["b"], [None if p is None else p[rows] for p in d["peers"]], s.world, 0)
+    assert_close(host(out)[rows], ref, "AR rows")
+
+
+# ----------------------------------------------------------------------------------------------
+# MoE dispatch + grouped GEMM
+# ----------------------------------------------------------------------------------------------
+def _run_moe(ctx, shape, data, order=None, mode=None, cap=None):
+    from gpu_util import dev_bf16, dev_f32, dev_i32
+    mk = _mk()
+    cap = shape.capacity if cap is None else cap
+    toks = [dev_bf16(t) for t in data["tokens"]]
+    topk = torch.full((shape.tokens, shape.top_k), -7, dtype=torch.int32, device="cuda")
+    offs = torch.full((shape.n_local + 1,), -7, dtype=torch.int32, device="cuda")
+    segt = torch.full((cap,), -7, dtype=torch.int32, device="cuda")
+    x = torch.zeros((cap, shape.hidden), dtype=torch.bfloat16, device="cuda")
+    y = torch.full((cap, shape.ffn), float("nan"), device="cuda")
+    opts = mk.Opts(arrival_mode=mode or 0, arrival_order=dev_i32(order) if order is not None else None)
+    mk.mk_moe_dispatch_gemm(ctx, toks, dev_f32(data["logits"]), dev_f32(data["bias"]), shape.top_k,
+                            shape.expert_begin, dev_bf16(data["w_up"]), topk, offs, segt, x, y, opts=opts)
+    st = ctx.status()
+    return st, topk, offs, segt, x, y
+
+
+@pytest.mark.parametrize("kind", ["normal", "int"])
+@pytest.mark.parametrize("variant,trial", [("flat", 0), ("flat", 1), ("flat", 2), ("identity", 0), ("reversed", 0)])
+def test_moe_small(ctx, kind, variant, trial):
+    from gpu_util import assert_close, assert_exact, host, host_bits
+    mk = _mk()
+    s = wl.MOE_SMALL
+    d = wl.gen_moe(s, run=0, kind=kind)
+    st, topk, offs, segt, x, y = _run_moe(ctx, s, d, order=wl.moe_arrival_order(s, trial, variant))
+    assert st == mk.MK_OK
+    ref = oracle.moe_dispatch_gemm(d["tokens"], d["logits"], d["bias"], s.top_k, s.expert_begin, s.n_local, d["w_up"])
+    R = int(ref["seg_offsets"][-1])
+    assert_exact(host(topk), ref["topk_idx"], "topk_idx")
+    assert_exact(host(offs), ref["seg_offsets"], "seg_offsets")
+    assert_exact(host(segt)[:R], ref["seg_token"], "seg_token")
+    assert_exact(host_bits(x)[:R], ref["x_seg"], "x_seg")
+    if kind == "int":
+        assert_exact(host(y)[:R], ref["y"].astype(np.float32), "y (integer)")
+    else:
+        assert_close(host(y)[:R], ref["y"], "y")
+
+
+def test_moe_forced_routing(ctx):
+    """Huge bias on experts 0 and 1: every token lands in both segments; the other local experts are empty."""
+    from gpu_util import assert_close, assert_exact, host
+    mk = _mk()
+    s = wl.MOE_SMALL
+    bias = np.zeros(s.n_experts, np.float32)
+    bias[:2] = 1e4
+    d = wl.gen_moe(s, run=1, bias_override=bias)
+    st, topk, offs, segt, x, y = _run_moe(ctx, s, d)
+    assert st == mk.MK_OK
+    T = s.tokens
+    assert_exact(host(offs), np.array([0, T, 2 * T] + [2 * T] * (s.n_local - 2), np.int32), "seg_offsets")
+    ref = oracle.moe_dispatch_gemm(d["tokens"], d["logits"], d["bias"], s.top_k, s.expert_begin, s.n_local, d["w_up"])
+    assert_exact(host(segt), ref["seg_token"], "seg_token")
+    assert_close(host(y), ref["y"], "y")
+
+
+def test_moe_no_local_rows(ctx):
+    mk = _mk()
+    from gpu_util import assert_exact, host
+    s = wl.MOE_SMALL
+    bias = np.zeros(s.n_experts, np.float32)
+    bias[:s.n_local] = -1e4
+    d = wl.gen_moe(s, run=1, bias_override=bias)
+    st, topk, offs, segt, x, y = _run_moe(ctx, s, d)
+    assert st == mk.MK_OK
+    assert_exact(host(offs), np.zeros(s.n_local + 1, np.int32), "seg_offsets")
+    assert np.isnan(host(y)).all()  # nothing written
+
+
+def test_moe_full_sampled(ctx):
+    from gpu_util import assert_close, assert_exact, host, host_bits, log
+    mk = _mk()
+    s = wl.MOE_FULL
+    d = wl.gen_moe(s, run=0)
+    log("moe full: launching")
+    st, topk, offs, segt, x, y = _run_moe(ctx, s, d, order=wl.moe_arrival_order(s, 0))
+    assert st == mk.MK_OK
+    topk_ref = oracle.moe_route(d["logits"], d["bias"], s.top_k)
+    offs_ref, segt_ref = oracle.moe_segments(topk_ref, s.expert_begin, s.n_local)
+    R = int(offs_ref[-1])
+    log(f"moe full: R = {R}, n_e = {np.diff(offs_ref).tolist()}")
+    assert_exact(host(topk), topk_ref, "topk_idx")
+    assert_exact(host(offs), offs_ref, "seg_offsets")
+    assert_exact(host(segt)[:R], segt_ref, "seg_token")
+    tok_all = np.concatenate(d["tokens"])
+    xs = host_bits(x)
+    pick = np.sort(np.random.default_rng(9).choice(R, 256, replace=False))
+    assert_exact(xs[pick], tok_all[segt_ref[pick]], "x_seg rows")
+    # y rows: the oracle on the sampled tokens alone (routing is per token, so their rows match)
+    rows = pick[:32]
+    toks = segt_ref[rows]
+    sub = oracle.moe_dispatch_gemm([tok_all[toks]], d["logits"][toks], d["bias"], s.top_k, s.expert_begin, s.n_local,
+                                   d["w_up"])
+    yh = host(y)
+    for i, t in zip(rows, toks):
+        e = int(np.searchsorted(offs_ref, i, side="right") - 1)
+        k = int(np.nonzero(toks == t)[0][0])  # position of token t in the sub-problem
+        # its row in the sub-problem's segment e
+        seg = sub["seg_token"][sub["seg_offsets"][e]:sub["seg_offsets"][e + 1]]
+        j = int(sub["seg_offsets"][e] + np.nonzero(seg == k)[0][0])
+        assert_close(yh[i][None, :], sub["y"][j][None, :], f"y row {i}")
+
+
+# ----------------------------------------------------------------------------------------------
+# faults forced from the host
+# ----------------------------------------------------------------------------------------------
+def test_dropped_unit_times_out_then_reset(ctx):
+    from gpu_util import assert_close, dev_bf16, dev_i32, host
+    mk = _mk()
+    s = wl.AG_TINY
+    d = wl.gen_ag(s, run=0)
+    order = wl.ag_arrival_order(s, trial=0)
+    b = dev_bf16(d["b"])
+    ag = torch.zeros((s.m, s.k), dtype=torch.bfloat16, device="cuda")
+    c = torch.zeros((s.m, s.n), device="cuda")
+    shards = [dev_bf16(x) for x in d["a_shards"]]
+    ag[:s.m_shard].copy_(shards[0])
+    shards[0] = ag[:s.m_shard]
+    opts = mk.Opts(arrival_order=dev_i32(order), test_drop_unit=5, timeout_us=20000)
+    mk.mk_ag_gemm(ctx, shards, s.world, 0, b, ag, c, opts=opts)
+    assert ctx.status() == mk.MK_ERR_TIMEOUT
+    ctx.reset()
+    assert ctx.status() == mk.MK_OK
+    mk.mk_ag_gemm(ctx, shards, s.world, 0, b, ag, c, opts=mk.Opts(arrival_order=dev_i32(order)))
+    assert ctx.status() == mk.MK_OK
+    assert_close(host(c), oracle.ag_gemm(d["a_shards"], d["b"])[1], "C after reset")
+
+
+def test_rs_dropped_unit_times_out(ctx):
+    mk = _mk()
+    s = wl.RS_SMALL
+    d = wl.gen_reduce(s, "rs", run=0)
+    from gpu_util import dev_bf16, dev_f32
+    a, b = dev_bf16(d["a"]), dev_bf16(d["b"])
+    peers = [None if p is None else dev_f32(p) for p in d["peers"]]
+    own = torch.zeros((s.m_slice, s.n), device="cuda")
+    ob = [None] + [torch.zeros((s.m_slice, s.n), device="cuda") for _ in range(1, s.world)]
+    opts = mk.Opts(test_drop_unit=3, timeout_us=20000, arrival_unit_rows=64, arrival_unit_cols=64)
+    mk.mk_gemm_rs(ctx, a, b, s.world, 0, peers, own, ob, opts=opts)
+    assert ctx.status() == mk.MK_ERR_TIMEOUT
+    ctx.reset()
+
+
+def test_moe_capacity_overflow(ctx):
+    mk = _mk()
+    s = wl.MOE_SMALL
+    d = wl.gen_moe(s, run=0)
+    ref = oracle.moe_dispatch_gemm(d["tokens"], d["logits"], d["bias"], s.top_k, s.expert_begin, s.n_local, d["w_up"])
+    R = int(ref["seg_offsets"][-1])
+    st, topk, offs, segt, x, y = _run_moe(ctx, s, d, cap=R // 2 // 64 * 64)
+    assert st == mk.MK_ERR_CAPACITY
+    from gpu_util import assert_exact, host
+    assert_exact(host(offs), ref["seg_offsets"], "seg_offsets still exact")
+    ctx.reset()
+
+
+def test_calls_do_not_leak_state(ctx):
+    """Back-to-back calls of different ops on one context: epoch-tagged flags need no clearing."""
+    from gpu_util import assert_close, host
+    mk = _mk()
+    s = wl.AG_TINY
+    d = wl.gen_ag(s, run=3)
+    for t in range(3):
+        _, c = _run_ag(ctx, s, d, order=wl.ag_arrival_order(s, trial=t))
+        assert_close(host(c), oracle.ag_gemm(d["a_shards"], d["b"])[1], f"C call {t}")
+        sm = wl.MOE_SMALL
+        dm = wl.gen_moe(sm, run=t)
+        st, *_ = _run_moe(ctx, sm, dm)
+        assert st == mk.MK_OK
