@@ -30,7 +30,7 @@ MK_ARRIVAL_RESIDENT = 1
 MK_ARRIVAL_EMULATED = 2
 
 EXPORTED = ["mk_ctx_create", "mk_ctx_destroy", "mk_ctx_status", "mk_ctx_reset", "mk_ctx_grid", "mk_strerror",
-            "mk_ag_gemm", "mk_gemm_rs", "mk_gemm_ar", "mk_moe_dispatch_gemm"]
+            "mk_selftest_flags", "mk_ag_gemm", "mk_gemm_rs", "mk_gemm_ar", "mk_moe_dispatch_gemm"]
 
 
 class MkError(RuntimeError):
@@ -110,8 +110,9 @@ def lib() -> ctypes.CDLL:
         L.mk_gemm_rs.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp, vp]
         L.mk_gemm_ar.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp]
         L.mk_moe_dispatch_gemm.argtypes = [vp, vp, vp, i, i, i, vp, vp, i, i, i, i, vp, i, vp, vp, vp, vp, vp, i, vp]
+        L.mk_selftest_flags.argtypes = [i, i, i, i, ctypes.POINTER(i64), ctypes.POINTER(i64)]
         for name in ("mk_ctx_create", "mk_ctx_destroy", "mk_ctx_status", "mk_ctx_reset", "mk_ctx_grid",
-                     "mk_ag_gemm", "mk_gemm_rs", "mk_gemm_ar", "mk_moe_dispatch_gemm"):
+                     "mk_selftest_flags", "mk_ag_gemm", "mk_gemm_rs", "mk_gemm_ar", "mk_moe_dispatch_gemm"):
             getattr(L, name).restype = i
         _lib_handle = L
     return _lib_handle
@@ -197,6 +198,15 @@ class Context:
             pass
 
 
+def mk_selftest_flags(device: int = 0, mode: int = 0, pairs: int = 64, rounds: int = 4096):
+    """Cross-XCD handshake self-test (see mk.h); returns (mismatches, timeouts)."""
+    mm, to = ctypes.c_int64(-1), ctypes.c_int64(-1)
+    rc = lib().mk_selftest_flags(int(device), int(mode), int(pairs), int(rounds), ctypes.byref(mm), ctypes.byref(to))
+    if rc != MK_OK:
+        raise MkError(rc, "mk_selftest_flags")
+    return int(mm.value), int(to.value)
+
+
 def _call(rc: int, what: str):
     if rc != MK_OK:
         raise MkError(rc, what)
@@ -279,6 +289,6 @@ def mk_moe_dispatch_gemm(ctx: Context, tokens: Sequence, logits, bias, top_k: in
           "mk_moe_dispatch_gemm")
 
 
-__all__ = ["Context", "Opts", "MkError", "mk_ag_gemm", "mk_gemm_rs", "mk_gemm_ar", "mk_moe_dispatch_gemm", "lib",
+__all__ = ["Context", "Opts", "MkError", "mk_selftest_flags", "mk_ag_gemm", "mk_gemm_rs", "mk_gemm_ar", "mk_moe_dispatch_gemm", "lib",
            "strerror", "MK_OK", "MK_ERR_INVALID_ARG", "MK_ERR_UNSUPPORTED", "MK_ERR_WORKSPACE", "MK_ERR_HIP",
            "MK_ERR_TIMEOUT", "MK_ERR_CAPACITY", "MK_ARRIVAL_RESIDENT", "MK_ARRIVAL_EMULATED", "EXPORTED"]

@@ -29,7 +29,7 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",  # no packed fp32 VALU ops
     "-I", INCLUDE, "-I", CSRC,
 ]
-SOURCES = ["mk_ag_gemm.hip", "mk_gemm_reduce.hip", "mk_moe.hip", "mk_api.cpp"]
+SOURCES = ["mk_ag_gemm.hip", "mk_gemm_reduce.hip", "mk_moe.hip", "mk_selftest.hip", "mk_api.cpp"]
 
 
 def _run(cmd):

@@ -23,7 +23,7 @@
 
 namespace mk {
 
-using AgTile = TileGemm<256, 256, 2, 2>;
+using AgTile = TileGemmDma<256, 128, 2, 2>;
 
 int ag_tile_m() { return AgTile::BM; }
 int ag_tile_n() { return AgTile::BN; }
@@ -135,9 +135,10 @@ __device__ __forceinline__ int ag_pick(const AgParams& p, int ur0, int n_ur, uin
   return u;
 }
 
-__device__ void ag_compute_role(const AgParams& p, int slot, char* smem, int* s_next, uint64_t* s_done) {
+__device__ void ag_compute_role(const AgParams& p, int slot, char* st0, char* st1, int* s_next, uint64_t* s_done) {
   AgTile g;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  (void)tid;
   const int wm = wave / AgTile::WN, wn = wave % AgTile::WN;
   const int n_tiles = p.tiles_m * p.tiles_n;
   const int nk = p.k >> 6;
@@ -148,21 +149,25 @@ __device__ void ag_compute_role(const AgParams& p, int slot, char* smem, int* s_
   // A row blocks) go to one XCD so its L2 keeps reusing them.
   const int rs = ((C & 7) == 0) ? (slot & 7) * (C >> 3) + (slot >> 3) : slot;
   const uint32_t lda_b = (uint32_t)p.k * 2u, ldb_b = (uint32_t)p.n * 2u;
-  char* lds0 = smem;
-  char* lds1 = smem + AgTile::STAGE;
+  g.init(wm, wn, lane, lda_b, ldb_b);
 
   for (int t = rs; t < n_tiles; t += C) {
     const int tm = t / p.tiles_n, tn = t - tm * p.tiles_n;
     const int m0 = tm * AgTile::BM, n0 = tn * AgTile::BN;
     const int rows_valid = min(AgTile::BM, p.m - m0), cols_valid = min(AgTile::BN, p.n - n0);
     const int ur0 = m0 / p.unit_rows, n_ur = rows_valid / p.unit_rows;
-    // Operand windows of one K-unit: rows of the tile over unit_cols columns of A, and unit_cols
-    // rows of B from column n0.  Rebased (scalar work) whenever the loop moves to another unit,
-    // so the per-step offsets stay the same small affine ones as a plain K loop.
-    const uint32_t a_ext = ((uint32_t)(rows_valid - 1) * (uint32_t)p.k + (uint32_t)p.unit_cols) * 2u;
-    const uint32_t b_ext = ((uint32_t)(p.unit_cols - 1) * (uint32_t)p.n + (uint32_t)(p.n - n0)) * 2u;
-    auto a_win = [&](int u) { return make_rsrc(p.ag + (size_t)m0 * p.k + (size_t)u * p.unit_cols, a_ext); };
-    auto b_win = [&](int u) { return make_rsrc(p.b + (size_t)u * p.unit_cols * p.n + n0, b_ext); };
+    // Operand windows of the k-step: A rows of the tile from the step's first column, B rows of
+    // the step from column n0.  Only scalar values change from step to step.
+    const char* a_tile = reinterpret_cast<const char*>(p.ag + (size_t)m0 * p.k);
+    const uint32_t a_tile_bytes = (uint32_t)rows_valid * lda_b;
+    const char* b_col = reinterpret_cast<const char*>(p.b + n0);
+    const uint32_t b_col_bytes = ((uint32_t)p.k * (uint32_t)p.n - (uint32_t)n0) * 2u;
+    auto load_step = [&](int ks, char* dst) {
+      const uint32_t ca = (uint32_t)ks * 128u;           // byte column of the step in A
+      const uint32_t rb = (uint32_t)ks * 64u * ldb_b;    // byte row of the step in B
+      g.dma_a(a_tile + ca, a_tile_bytes - ca, lda_b, dst, wave);
+      g.dma_b(b_col + rb, b_col_bytes - rb, ldb_b, dst, wave);
+    };
 
     g.zero();
 
@@ -179,19 +184,22 @@ __device__ void ag_compute_role(const AgParams& p, int slot, char* smem, int* s_
       }
       __syncthreads();
       unit = __builtin_amdgcn_readfirstlane(s_next[0]);
-      if (unit < 0 || (n_ku > 1 && __builtin_amdgcn_readfirstlane(s_next[1]) < 0)) return;
+      if (unit < 0 || (n_ku > 1 && __builtin_amdgcn_readfirstlane(s_next[1]) < 0)) return;  // before any MFMA
     } else {
       unit = 0;
     }
-    auto ar = a_win(unit);
-    auto br = b_win(unit);
-    g.load_a(ar, lda_b, 0u, tid);
-    g.load_b(br, ldb_b, 0, tid);
-    g.store_a(lds0, tid);
-    g.store_b(lds0 + AgTile::STAGE_A, tid);
+    // A failed wait (watchdog or another workgroup's fault) inside the K loop does not leave the
+    // loop: the remaining steps drain on K-unit 0 (in bounds, result discarded) and the tile's
+    // stores are skipped.  Keeping the loop single-exit keeps the accumulators in AGPRs.
+    bool aborted = false;
+    load_step(unit * spu, st0);
+    wait_mem();
     __syncthreads();
 
-    for (int s = 0; s < nk; ++s) {
+    // One pipeline step: prefetch step s+1 into `nxt` while the MFMAs consume `cur`.  The loop is
+    // unrolled by two so each half names its stage buffers statically: the compiler can then see
+    // that the MFMA operand reads never alias the LDS DMA in flight and issues no wait between them.
+    auto step = [&](int s, char* cur, char* nxt) {
       const int pf = s + 1;
       bool decide = false;
       int jn = 0;
@@ -200,40 +208,39 @@ __device__ void ag_compute_role(const AgParams& p, int slot, char* smem, int* s_
         if (sub == 0) {
           const int j = pf / spu;
           unit = p.emulated ? __builtin_amdgcn_readfirstlane(s_next[j & 1]) : j;
+          aborted |= unit < 0;
+          unit = unit < 0 ? 0 : unit;
           decide = p.emulated && (j + 1 < n_ku);
           jn = j + 1;
-          ar = a_win(unit);
-          br = b_win(unit);
         }
-        g.load_a(ar, lda_b, (uint32_t)sub * 128u, tid);
-        g.load_b(br, ldb_b, sub * 64, tid);
+        load_step(unit * spu + sub, nxt);
       }
-      char* cur = (s & 1) ? lds1 : lds0;
-      g.mma(cur, cur + AgTile::STAGE_A, wm, wn, lane);
-      if (pf < nk) {
-        char* nxt = (pf & 1) ? lds1 : lds0;
-        g.store_a(nxt, tid);
-        g.store_b(nxt + AgTile::STAGE_A, tid);
-      }
+      g.mma(cur);
       if (decide && wave == 0) {
         const int u = ag_pick(p, ur0, n_ur, s_done, lane);
         if (lane == 0) s_next[jn & 1] = u;
       }
+      wait_mem();
       __syncthreads();
-      if (decide && __builtin_amdgcn_readfirstlane(s_next[jn & 1]) < 0) return;  // timeout or fault: drain
+    };
+    for (int s = 0; s < nk; s += 2) {
+      step(s, st0, st1);
+      if (s + 1 < nk) step(s + 1, st1, st0);
     }
 
     // epilogue: fp32 C tile, staged through LDS into row-contiguous 16-byte stores
-    g.epilogue(smem, wm, wn, lane, wave, [&](int row, int col, f32x4 v) {
-      if (row < rows_valid && col < cols_valid)
+    g.epilogue(st0, st1, wm, wn, lane, wave, [&](int row, int col, f32x4 v) {
+      if (!aborted && row < rows_valid && col < cols_valid)
         *reinterpret_cast<f32x4*>(p.c + (size_t)(m0 + row) * p.n + (n0 + col)) = v;
     });
     __syncthreads();  // the next tile's prologue reuses the LDS
+    if (aborted) break;
   }
 }
 
 __global__ __launch_bounds__(256, 1) void ag_gemm_kernel(AgParams p) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ __attribute__((aligned(16))) char st0[AgTile::STAGE];
+  __shared__ __attribute__((aligned(16))) char st1[AgTile::STAGE];
   __shared__ int s_next[2];
   __shared__ uint64_t s_done;
   const int wg = blockIdx.x;
@@ -242,18 +249,11 @@ __global__ __launch_bounds__(256, 1) void ag_gemm_kernel(AgParams p) {
     return;
   }
   const int slot = wg - p.n_copy;
-  if (slot < p.n_compute) ag_compute_role(p, slot, smem, s_next, &s_done);
+  if (slot < p.n_compute) ag_compute_role(p, slot, st0, st1, s_next, &s_done);
 }
 
 hipError_t launch_ag_gemm(const AgParams& p, int grid, hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)ag_gemm_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       AgTile::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  hipLaunchKernelGGL(ag_gemm_kernel, dim3(grid), dim3(256), AgTile::LDS_BYTES, s, p);
+  hipLaunchKernelGGL(ag_gemm_kernel, dim3(grid), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

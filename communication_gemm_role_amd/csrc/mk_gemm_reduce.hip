@@ -24,8 +24,8 @@
 
 namespace mk {
 
-using RedBig = TileGemm<256, 256, 2, 2>;   // wide outputs (e.g. 8192 x 4096)
-using RedSkinny = TileGemm<128, 64, 4, 1>;  // few output rows (decode-like, m <= 512)
+using RedBig = TileGemmDma<256, 128, 2, 2>;   // wide outputs (e.g. 8192 x 4096)
+using RedSkinny = TileGemmDma<128, 64, 4, 1>;  // few output rows (decode-like, m <= 512)
 
 static inline bool red_skinny(int m, int n) { (void)n; return m <= 512; }
 int red_tile_m(int m, int n) { return red_skinny(m, n) ? RedSkinny::BM : RedBig::BM; }
@@ -124,7 +124,7 @@ __device__ __forceinline__ bool wait_units(const RedParams& p, int lr0, int lr1,
 // ------------------------------------------------------------------------------------------
 template <class T>
 __device__ void red_reduce_role(const RedParams& p, int rid, int* s_ok) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int own_rows = p.own_tile_end - p.own_tile_begin;
   const int n_jobs = own_rows * p.tiles_n;
   const uint32_t ld = (uint32_t)p.n * 4u;
@@ -182,17 +182,16 @@ __device__ void red_reduce_role(const RedParams& p, int rid, int* s_ok) {
 // compute role
 // ------------------------------------------------------------------------------------------
 template <class T>
-__device__ void red_compute_role(const RedParams& p, int slot, char* smem, int* s_ok) {
+__device__ void red_compute_role(const RedParams& p, int slot, char* st0, char* st1, int* s_ok) {
   T g;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / T::WN, wn = wave % T::WN;
   const int n_tiles = p.tiles_m * p.tiles_n;
   const int nk = p.k >> 6;
   const int C = p.n_compute;
   const int rs = ((C & 7) == 0) ? (slot & 7) * (C >> 3) + (slot >> 3) : slot;
   const uint32_t lda_b = (uint32_t)p.k * 2u, ldb_b = (uint32_t)p.n * 2u;
-  char* lds0 = smem;
-  char* lds1 = smem + T::STAGE;
+  g.init(wm, wn, lane, lda_b, ldb_b);
 
   for (int t = rs; t < n_tiles; t += C) {
     // logical tile rows start right after the owned rows, so owned tiles come last
@@ -200,28 +199,29 @@ __device__ void red_compute_role(const RedParams& p, int slot, char* smem, int* 
     const int tm = (tml + p.own_tile_end) % p.tiles_m;
     const int m0 = tm * T::BM, n0 = tn * T::BN;
     const int rows_valid = min(T::BM, p.m - m0), cols_valid = min(T::BN, p.n - n0);
-    const auto ar = make_rsrc(p.a + (size_t)m0 * p.k, (uint32_t)rows_valid * lda_b);
-    const auto br = make_rsrc(p.b + n0, ((uint32_t)p.k * (uint32_t)p.n - (uint32_t)n0) * 2u);
+    const char* a_tile = reinterpret_cast<const char*>(p.a + (size_t)m0 * p.k);
+    const uint32_t a_tile_bytes = (uint32_t)rows_valid * lda_b;
+    const char* b_col = reinterpret_cast<const char*>(p.b + n0);
+    const uint32_t b_col_bytes = ((uint32_t)p.k * (uint32_t)p.n - (uint32_t)n0) * 2u;
+    auto load_step = [&](int ks, char* dst) {
+      const uint32_t ca = (uint32_t)ks * 128u, rb = (uint32_t)ks * 64u * ldb_b;
+      g.dma_a(a_tile + ca, a_tile_bytes - ca, lda_b, dst, wave);
+      g.dma_b(b_col + rb, b_col_bytes - rb, ldb_b, dst, wave);
+    };
     g.zero();
-    g.load_a(ar, lda_b, 0, tid);
-    g.load_b(br, ldb_b, 0, tid);
-    g.store_a(lds0, tid);
-    g.store_b(lds0 + T::STAGE_A, tid);
+    load_step(0, st0);
+    wait_mem();
     __syncthreads();
-    for (int s = 0; s < nk; ++s) {
-      const int pf = s + 1;
-      if (pf < nk) {
-        g.load_a(ar, lda_b, (uint32_t)pf * 128u, tid);
-        g.load_b(br, ldb_b, pf * 64, tid);
-      }
-      char* cur = (s & 1) ? lds1 : lds0;
-      g.mma(cur, cur + T::STAGE_A, wm, wn, lane);
-      if (pf < nk) {
-        char* nxt = (pf & 1) ? lds1 : lds0;
-        g.store_a(nxt, tid);
-        g.store_b(nxt + T::STAGE_A, tid);
-      }
+    // unrolled by two so each half names its stage buffers statically (no DMA/LDS-read alias wait)
+    auto step = [&](int s, char* cur, char* nxt) {
+      if (s + 1 < nk) load_step(s + 1, nxt);
+      g.mma(cur);
+      wait_mem();
       __syncthreads();
+    };
+    for (int s = 0; s < nk; s += 2) {
+      step(s, st0, st1);
+      if (s + 1 < nk) step(s + 1, st1, st0);
     }
 
     int lr0, lr1;
@@ -244,7 +244,7 @@ __device__ void red_compute_role(const RedParams& p, int slot, char* smem, int* 
       if (!*s_ok) return;
     }
     const int own0 = p.is_rs ? p.rank * p.m_slice : 0;
-    g.epilogue(smem, wm, wn, lane, wave, [&](int row, int col, f32x4 v) {
+    g.epilogue(st0, st1, wm, wn, lane, wave, [&](int row, int col, f32x4 v) {
       if (row >= rows_valid || col >= cols_valid) return;
       const int grow = m0 + row, gcol = n0 + col;
       if (p.is_rs) {
@@ -269,7 +269,8 @@ __device__ void red_compute_role(const RedParams& p, int slot, char* smem, int* 
 
 template <class T>
 __global__ __launch_bounds__(256, 1) void gemm_reduce_kernel(RedParams p) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ __attribute__((aligned(16))) char st0[T::STAGE];
+  __shared__ __attribute__((aligned(16))) char st1[T::STAGE];
   __shared__ int s_ok;
   const int wg = blockIdx.x;
   if (wg < p.n_copy) {
@@ -281,19 +282,12 @@ __global__ __launch_bounds__(256, 1) void gemm_reduce_kernel(RedParams p) {
     return;
   }
   const int slot = wg - p.n_copy - p.n_reduce;
-  if (slot < p.n_compute) red_compute_role<T>(p, slot, smem, &s_ok);
+  if (slot < p.n_compute) red_compute_role<T>(p, slot, st0, st1, &s_ok);
 }
 
 template <class T>
 static hipError_t launch_t(const RedParams& p, int grid, hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_reduce_kernel<T>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       T::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  hipLaunchKernelGGL(gemm_reduce_kernel<T>, dim3(grid), dim3(256), T::LDS_BYTES, s, p);
+  hipLaunchKernelGGL(gemm_reduce_kernel<T>, dim3(grid), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -27,7 +27,7 @@
 
 namespace mk {
 
-using MoeTile = TileGemm<128, 256, 2, 2>;
+using MoeTile = TileGemmDma<128, 256, 2, 2>;
 constexpr int MOE_KMAX = 8;
 
 int moe_tile_m() { return MoeTile::BM; }
@@ -103,7 +103,7 @@ __device__ void moe_route_chunk(const MoeParams& p, int chunk, int lane) {
 
 // Exclusive scan of the per-chunk counts (run by one workgroup, the last router).
 __device__ void moe_scan(const MoeParams& p, MoeShared& sh) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   uint32_t* cnt = p.counters + p.off_chunk_cnt;
   // pass 1: per-expert totals
   for (int el = wave; el < p.n_local; el += 4) {
@@ -157,7 +157,7 @@ __device__ void moe_scan(const MoeParams& p, MoeShared& sh) {
 // route + copy role
 // ------------------------------------------------------------------------------------------
 __device__ void moe_copy_role(const MoeParams& p, int cid, MoeShared& sh) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // route: chunks (cid*4 + wave) + i * (n_copy*4)
   for (int c = cid * 4 + wave; c < p.n_chunks; c += p.n_copy * 4) moe_route_chunk(p, c, lane);
   wait_mem();
@@ -272,8 +272,8 @@ __device__ void moe_copy_role(const MoeParams& p, int cid, MoeShared& sh) {
 // ------------------------------------------------------------------------------------------
 // compute role: ragged grouped GEMM
 // ------------------------------------------------------------------------------------------
-__device__ void moe_compute_role(const MoeParams& p, int slot, char* smem, MoeShared& sh) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__device__ void moe_compute_role(const MoeParams& p, int slot, char* st0, char* st1, MoeShared& sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (tid == 0) sh.ok = spin_until_eq(&p.flags[0], p.epoch, p.timeout_ticks, p.status);
   __syncthreads();
   if (!sh.ok) return;
@@ -290,8 +290,7 @@ __device__ void moe_compute_role(const MoeParams& p, int slot, char* smem, MoeSh
   const int C = p.n_compute;
   const int rs = ((C & 7) == 0) ? (slot & 7) * (C >> 3) + (slot >> 3) : slot;
   const uint32_t lda_b = (uint32_t)p.hidden * 2u, ldb_b = (uint32_t)p.ffn * 2u;
-  char* lds0 = smem;
-  char* lds1 = smem + MoeTile::STAGE;
+  g.init(wm, wn, lane, lda_b, ldb_b);
   for (int t = rs; t < n_tiles; t += C) {
     const int gm = t / p.tiles_n, tn = t - gm * p.tiles_n;
     int el = 0;
@@ -308,31 +307,31 @@ __device__ void moe_compute_role(const MoeParams& p, int slot, char* smem, MoeSh
       sh.ok = spin_until_ge(p.counters + p.off_tile_cnt + gm, (uint32_t)rows_valid, p.timeout_ticks, p.status);
     __syncthreads();
     if (!sh.ok) return;
-    const auto ar = make_rsrc(p.x_seg + (size_t)row0 * p.hidden, (uint32_t)rows_valid * lda_b);
-    const uint16_t* w = p.w_up + (size_t)el * p.hidden * p.ffn;
-    const auto br = make_rsrc(w + n0, ((uint32_t)p.hidden * (uint32_t)p.ffn - (uint32_t)n0) * 2u);
+    const char* a_tile = reinterpret_cast<const char*>(p.x_seg + (size_t)row0 * p.hidden);
+    const uint32_t a_tile_bytes = (uint32_t)rows_valid * lda_b;
+    const char* b_col = reinterpret_cast<const char*>(p.w_up + (size_t)el * p.hidden * p.ffn + n0);
+    const uint32_t b_col_bytes = ((uint32_t)p.hidden * (uint32_t)p.ffn - (uint32_t)n0) * 2u;
+    auto load_step = [&](int ks, char* dst) {
+      const uint32_t ca = (uint32_t)ks * 128u, rb = (uint32_t)ks * 64u * ldb_b;
+      g.dma_a(a_tile + ca, a_tile_bytes - ca, lda_b, dst, wave);
+      g.dma_b(b_col + rb, b_col_bytes - rb, ldb_b, dst, wave);
+    };
     g.zero();
-    g.load_a(ar, lda_b, 0, tid);
-    g.load_b(br, ldb_b, 0, tid);
-    g.store_a(lds0, tid);
-    g.store_b(lds0 + MoeTile::STAGE_A, tid);
+    load_step(0, st0);
+    wait_mem();
     __syncthreads();
-    for (int s = 0; s < nk; ++s) {
-      const int pf = s + 1;
-      if (pf < nk) {
-        g.load_a(ar, lda_b, (uint32_t)pf * 128u, tid);
-        g.load_b(br, ldb_b, pf * 64, tid);
-      }
-      char* cur = (s & 1) ? lds1 : lds0;
-      g.mma(cur, cur + MoeTile::STAGE_A, wm, wn, lane);
-      if (pf < nk) {
-        char* nxt = (pf & 1) ? lds1 : lds0;
-        g.store_a(nxt, tid);
-        g.store_b(nxt + MoeTile::STAGE_A, tid);
-      }
+    // unrolled by two so each half names its stage buffers statically (no DMA/LDS-read alias wait)
+    auto step = [&](int s, char* cur, char* nxt) {
+      if (s + 1 < nk) load_step(s + 1, nxt);
+      g.mma(cur);
+      wait_mem();
       __syncthreads();
+    };
+    for (int s = 0; s < nk; s += 2) {
+      step(s, st0, st1);
+      if (s + 1 < nk) step(s + 1, st1, st0);
     }
-    g.epilogue(smem, wm, wn, lane, wave, [&](int row, int col, f32x4 v) {
+    g.epilogue(st0, st1, wm, wn, lane, wave, [&](int row, int col, f32x4 v) {
       if (row < rows_valid && col < cols_valid)
         *reinterpret_cast<f32x4*>(p.y + (size_t)(row0 + row) * p.ffn + (n0 + col)) = v;
     });
@@ -341,11 +340,12 @@ __device__ void moe_compute_role(const MoeParams& p, int slot, char* smem, MoeSh
 }
 
 __global__ __launch_bounds__(256, 1) void moe_kernel(MoeParams p) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ __attribute__((aligned(16))) char st0[MoeTile::STAGE];
+  __shared__ __attribute__((aligned(16))) char st1[MoeTile::STAGE];
   __shared__ MoeShared sh;
   const int wg = blockIdx.x;
   if (wg < p.n_copy) moe_copy_role(p, wg, sh);
-  else if (wg - p.n_copy < p.n_compute) moe_compute_role(p, wg - p.n_copy, smem, sh);
+  else if (wg - p.n_copy < p.n_compute) moe_compute_role(p, wg - p.n_copy, st0, st1, sh);
   // exit accounting: the last workgroup out re-zeroes the counters for the next call
   wait_mem();
   __syncthreads();
@@ -363,14 +363,7 @@ __global__ __launch_bounds__(256, 1) void moe_kernel(MoeParams p) {
 }
 
 hipError_t launch_moe(const MoeParams& p, int grid, hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)moe_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       MoeTile::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  hipLaunchKernelGGL(moe_kernel, dim3(grid), dim3(256), MoeTile::LDS_BYTES, s, p);
+  hipLaunchKernelGGL(moe_kernel, dim3(grid), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

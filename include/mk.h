@@ -99,6 +99,19 @@ int mk_ctx_reset(mk_ctx* ctx, void* stream);
 int mk_ctx_grid(mk_ctx* ctx);
 const char* mk_strerror(int code);
 
+/* Self-test of the cross-workgroup handshake every role relies on: producer workgroups write a
+ * payload with write-through stores and then raise a relaxed agent-scope flag; consumer workgroups
+ * on other XCDs poll the flag and read the payload.  `pairs` producer/consumer pairs exchange
+ * `rounds` payloads.  mode 0: fresh payload addresses every round, ordinary consumer loads (the
+ * kernels' pattern: a payload is written once per launch and never read before its flag);
+ * mode 1: the same addresses every round, device-coherent consumer loads; mode 2: the same
+ * addresses with ordinary loads (diagnostic only: another XCD's L2 may hold a stale copy).
+ * Allocates and frees its own device memory and synchronises the device.  Returns MK_OK with
+ * *mismatches = payload words that did not match and *timeouts = 1 if a wait hit the 2 s watchdog;
+ * MK_ERR_INVALID_ARG for mode not in [0,2], pairs not in [1,128], rounds < 1, or
+ * pairs*rounds > 262144 in mode 0; MK_ERR_HIP on a runtime failure. */
+int mk_selftest_flags(int device, int mode, int pairs, int rounds, int64_t* mismatches, int64_t* timeouts);
+
 /* ---- AllGather + GEMM ----------------------------------------------------------------
  * Five-fused-kernels table, AllGather + GEMM row: every rank holds one row shard of A; while
  * the shards of the other ranks arrive, the local GEMM consumes each A tile as soon as it lands.
