@@ -40,7 +40,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", default="", help="profiling: run only this op (ag, ag_resident, rs, ar, moe)")
+    ap.add_argument("--only", default="",
+                    help="profiling: run only this op (ag, ag_resident, rs, ar, rs_emulated, ar_emulated, moe, copy)")
     return ap.parse_args()
 
 
@@ -201,6 +202,11 @@ def main():
             _, calls = setup_reduce(ctx, a.only[:2], emulated=True)
         elif a.only == "moe":
             _, _, calls = setup_moe(ctx)
+        elif a.only == "copy":
+            # calibration for the HBM byte counters: a plain device copy of 256 MiB per launch
+            src = torch.empty(64 << 20, dtype=torch.float32, device="cuda").fill_(1.0)
+            dst = torch.empty_like(src)
+            calls = [lambda: dst.copy_(src)]
         else:
             raise SystemExit(f"unknown --only {a.only}")
         wall, kern = time_calls(calls, a.steps, a.warmup)

@@ -40,41 +40,92 @@ __device__ __forceinline__ int ag_identity_unit(const AgParams& p, int pos) {
   return ur * p.n_ucols + uc;
 }
 
-__device__ void ag_copy_role(const AgParams& p, int cid) {
+// Units move in batches of 24 sixteen-byte chunks per thread (3 units of 128x128, 6 of 64x128 or
+// 12 of 64x64).  Per batch: write-through stores of the batch, then the loads of the next batch,
+// then a wait that covers only the stores (the next batch's 24 loads stay in flight), a barrier
+// and the flags of the landed units.  A slot past the end of this workgroup's queue (or a dropped
+// unit) uses an empty buffer window, so every batch issues the same instruction count.
+template <int PER_T>
+__device__ __forceinline__ void ag_copy_batched(const AgParams& p, int cid) {
+  constexpr int UB = 24 / PER_T;  // units per batch
   const int tid = threadIdx.x;
-  const int cpr = p.unit_cols >> 3;              // 16-byte chunks per unit row
-  const int per_t = (p.unit_rows * cpr) >> 8;    // chunks per thread: 2 (64x64) or 8 (128x128)
+  const int cpr = p.unit_cols >> 3;  // 16-byte chunks per unit row
   const uint32_t ldb = (uint32_t)p.k * 2u;
+  const uint32_t extent = ((uint32_t)(p.unit_rows - 1) * (uint32_t)p.k + (uint32_t)p.unit_cols) * 2u;
   const int n_units = p.n_urows * p.n_ucols;
-  for (int pos = cid; pos < p.n_order; pos += p.n_copy) {
-    if (pos + 1 == p.drop_pos) continue;  // testing: this unit never lands
+  const int n_mine = p.n_order > cid ? (p.n_order - cid + p.n_copy - 1) / p.n_copy : 0;
+  uint32_t off[PER_T];  // per-thread byte offset of each chunk inside a unit
+#pragma unroll
+  for (int c = 0; c < PER_T; ++c) {
+    const int ch = tid + (c << 8);
+    const int row = ch / cpr, cc = ch - row * cpr;
+    off[c] = (uint32_t)row * ldb + (uint32_t)cc * 16u;
+  }
+  auto unit_at = [&](int i) -> int {  // i-th unit of this workgroup's queue, or -1
+    if (i >= n_mine) return -1;
+    const int pos = cid + i * p.n_copy;
+    if (pos + 1 == p.drop_pos) return -1;  // testing: this unit never lands
     const int u = p.order ? p.order[pos] : ag_identity_unit(p, pos);
-    if (u < 0 || u >= n_units) continue;
+    return (u < 0 || u >= n_units) ? -1 : u;
+  };
+  auto src_of = [&](int u) {
+    if (u < 0) return make_rsrc(p.ag, 0u);
     const int ur = u / p.n_ucols, uc = u - ur * p.n_ucols;
     const int grow = ur * p.unit_rows;
     const int r = grow / p.m_shard, srow = grow - r * p.m_shard;
-    const uint32_t extent = ((uint32_t)(p.unit_rows - 1) * (uint32_t)p.k + (uint32_t)p.unit_cols) * 2u;
-    const auto src = make_rsrc(p.shards[r] + (size_t)srow * p.k + (size_t)uc * p.unit_cols, extent);
-    const auto dst = make_rsrc(p.ag + (size_t)grow * p.k + (size_t)uc * p.unit_cols, extent);
-    u32x4 v[8];
+    return make_rsrc(p.shards[r] + (size_t)srow * p.k + (size_t)uc * p.unit_cols, extent);
+  };
+  auto dst_of = [&](int u) {
+    if (u < 0) return make_rsrc(p.ag, 0u);
+    const int ur = u / p.n_ucols, uc = u - ur * p.n_ucols;
+    return make_rsrc(p.ag + (size_t)ur * p.unit_rows * p.k + (size_t)uc * p.unit_cols, extent);
+  };
+  u32x4 va[UB][PER_T], vb[UB][PER_T];
+  auto load = [&](int i0, u32x4 (&v)[UB][PER_T]) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (i < per_t) {
-        const int c = tid + (i << 8);
-        const int row = c / cpr, cc = c - row * cpr;
-        v[i] = bload16_nt(src, (uint32_t)row * ldb + (uint32_t)cc * 16u);
-      }
+    for (int b = 0; b < UB; ++b) {
+      const auto src = src_of(unit_at(i0 + b));
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (i < per_t) {
-        const int c = tid + (i << 8);
-        const int row = c / cpr, cc = c - row * cpr;
-        bstore16_sc1(dst, (uint32_t)row * ldb + (uint32_t)cc * 16u, v[i]);
-      }
-    wait_mem();
+      for (int c = 0; c < PER_T; ++c) v[b][c] = bload16_nt(src, off[c]);
+    }
+  };
+  auto store = [&](int i0, u32x4 (&v)[UB][PER_T]) {
+#pragma unroll
+    for (int b = 0; b < UB; ++b) {
+      const auto dst = dst_of(unit_at(i0 + b));
+#pragma unroll
+      for (int c = 0; c < PER_T; ++c) bstore16_sc1(dst, off[c], v[b][c]);
+    }
+  };
+  auto raise = [&](int i0) {
     __syncthreads();
-    if (tid == 0) flag_store(&p.flags[u], p.epoch);
+    if (tid == 0)
+      for (int b = 0; b < UB; ++b) {
+        const int u = unit_at(i0 + b);
+        if (u >= 0) flag_store(&p.flags[u], p.epoch);
+      }
+  };
+  if (n_mine == 0) return;
+  load(0, va);
+  for (int i = 0; i < n_mine; i += 2 * UB) {
+    store(i, va);
+    load(i + UB, vb);  // past the end: empty windows, no traffic
+    wait_vm<24>();     // this batch's stores are acknowledged; the next batch's loads may fly on
+    raise(i);
+    if (i + UB >= n_mine) break;
+    store(i + UB, vb);
+    load(i + 2 * UB, va);
+    wait_vm<24>();
+    raise(i + UB);
   }
+}
+
+__device__ __forceinline__ void ag_copy_role(const AgParams& p, int cid) {
+  const int per_t = (p.unit_rows * (p.unit_cols >> 3)) >> 8;  // 2 (64x64), 4 (64x128, 128x64), 8 (128x128)
+  if (per_t == 8) ag_copy_batched<8>(p, cid);
+  else if (per_t == 4) ag_copy_batched<4>(p, cid);
+  else ag_copy_batched<2>(p, cid);
+  wait_mem();
 }
 
 // ------------------------------------------------------------------------------------------
@@ -135,10 +186,39 @@ __device__ __forceinline__ int ag_pick(const AgParams& p, int ur0, int n_ur, uin
   return u;
 }
 
-__device__ void ag_compute_role(const AgParams& p, int slot, char* st0, char* st1, int* s_next, uint64_t* s_done) {
+// Wave 0: flags of the tile's non-local unit rows for K-unit `lane`, loaded without waiting (the
+// values are consumed after the step's MFMAs, so the load latency hides behind them).
+struct AgPoll {
+  uint32_t f[4];
+};
+__device__ __forceinline__ void ag_poll_issue(const AgParams& p, int ur0, int n_ur, int lane, AgPoll& pl) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int ur = ur0 + q;
+    pl.f[q] = (q < n_ur && !ag_row_local(p, ur) && lane < p.n_ucols) ? flag_load(&p.flags[ur * p.n_ucols + lane])
+                                                                       : p.epoch;
+  }
+}
+// Wave 0: pick from an issued poll (falling back to the blocking ag_pick when nothing is ready).
+__device__ __forceinline__ int ag_pick_polled(const AgParams& p, int ur0, int n_ur, uint64_t* s_done, int lane,
+                                              const AgPoll& pl) {
+  const uint64_t all = (p.n_ucols >= 64) ? ~0ull : ((1ull << p.n_ucols) - 1ull);
+  uint64_t ready = all;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) ready &= __ballot(lane >= p.n_ucols || pl.f[q] == p.epoch);
+  volatile uint64_t* vd = s_done;
+  const uint64_t done = uniform64(*vd);
+  const uint64_t cand = ready & ~done;
+  if (!cand) return ag_pick(p, ur0, n_ur, s_done, lane);
+  const int u = __builtin_ctzll(cand);
+  *vd = done | (1ull << u);
+  return u;
+}
+
+__device__ __forceinline__ void ag_compute_role(const AgParams& p, int slot, char* st0, char* st1, char* st2, int* s_sched,
+                                uint64_t* s_done) {
   AgTile g;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  (void)tid;
   const int wm = wave / AgTile::WN, wn = wave % AgTile::WN;
   const int n_tiles = p.tiles_m * p.tiles_n;
   const int nk = p.k >> 6;
@@ -150,6 +230,9 @@ __device__ void ag_compute_role(const AgParams& p, int slot, char* st0, char* st
   const int rs = ((C & 7) == 0) ? (slot & 7) * (C >> 3) + (slot >> 3) : slot;
   const uint32_t lda_b = (uint32_t)p.k * 2u, ldb_b = (uint32_t)p.n * 2u;
   g.init(wm, wn, lane, lda_b, ldb_b);
+  // K-units decided before the loop: unit j is prefetched two steps ahead of step j*spu and must be
+  // decided one iteration before that, so the prologue covers the first 2/spu + 1 units.
+  const int n_pre = min(n_ku, 2 / spu + 1);
 
   for (int t = rs; t < n_tiles; t += C) {
     const int tm = t / p.tiles_n, tn = t - tm * p.tiles_n;
@@ -163,70 +246,59 @@ __device__ void ag_compute_role(const AgParams& p, int slot, char* st0, char* st
     const char* b_col = reinterpret_cast<const char*>(p.b + n0);
     const uint32_t b_col_bytes = ((uint32_t)p.k * (uint32_t)p.n - (uint32_t)n0) * 2u;
     auto load_step = [&](int ks, char* dst) {
-      const uint32_t ca = (uint32_t)ks * 128u;           // byte column of the step in A
-      const uint32_t rb = (uint32_t)ks * 64u * ldb_b;    // byte row of the step in B
+      const uint32_t ca = (uint32_t)ks * 128u;         // byte column of the step in A
+      const uint32_t rb = (uint32_t)ks * 64u * ldb_b;  // byte row of the step in B
       g.dma_a(a_tile + ca, a_tile_bytes - ca, lda_b, dst, wave);
       g.dma_b(b_col + rb, b_col_bytes - rb, ldb_b, dst, wave);
     };
 
     g.zero();
-
-    int unit;  // K-unit of the step being prefetched
     if (p.emulated) {
       if (wave == 0) {
         *(volatile uint64_t*)s_done = 0;
-        const int u0 = ag_pick(p, ur0, n_ur, s_done, lane);
-        const int u1 = (u0 >= 0 && n_ku > 1) ? ag_pick(p, ur0, n_ur, s_done, lane) : (u0 >= 0 ? 0 : -1);
-        if (lane == 0) {
-          s_next[0] = u0;
-          s_next[1] = u1;
+        for (int j = 0; j < n_pre; ++j) {
+          const int u = ag_pick(p, ur0, n_ur, s_done, lane);
+          if (lane == 0) s_sched[j] = u;
+          if (u < 0) break;
         }
       }
       __syncthreads();
-      unit = __builtin_amdgcn_readfirstlane(s_next[0]);
-      if (unit < 0 || (n_ku > 1 && __builtin_amdgcn_readfirstlane(s_next[1]) < 0)) return;  // before any MFMA
-    } else {
-      unit = 0;
+      bool bad = false;
+      for (int j = 0; j < n_pre; ++j) bad |= __builtin_amdgcn_readfirstlane(s_sched[j]) < 0;
+      if (bad) return;  // before any MFMA of this tile
     }
     // A failed wait (watchdog or another workgroup's fault) inside the K loop does not leave the
     // loop: the remaining steps drain on K-unit 0 (in bounds, result discarded) and the tile's
     // stores are skipped.  Keeping the loop single-exit keeps the accumulators in AGPRs.
     bool aborted = false;
-    load_step(unit * spu, st0);
-    wait_mem();
-    __syncthreads();
-
-    // One pipeline step: prefetch step s+1 into `nxt` while the MFMAs consume `cur`.  The loop is
-    // unrolled by two so each half names its stage buffers statically: the compiler can then see
-    // that the MFMA operand reads never alias the LDS DMA in flight and issues no wait between them.
-    auto step = [&](int s, char* cur, char* nxt) {
-      const int pf = s + 1;
-      bool decide = false;
-      int jn = 0;
-      if (pf < nk) {
-        const int sub = pf % spu;
-        if (sub == 0) {
-          const int j = pf / spu;
-          unit = p.emulated ? __builtin_amdgcn_readfirstlane(s_next[j & 1]) : j;
-          aborted |= unit < 0;
-          unit = unit < 0 ? 0 : unit;
-          decide = p.emulated && (j + 1 < n_ku);
-          jn = j + 1;
-        }
-        load_step(unit * spu + sub, nxt);
-      }
-      g.mma(cur);
-      if (decide && wave == 0) {
-        const int u = ag_pick(p, ur0, n_ur, s_done, lane);
-        if (lane == 0) s_next[jn & 1] = u;
-      }
-      wait_mem();
-      __syncthreads();
+    AgPoll pl;
+    bool polled = false;
+    auto unit_of = [&](int q) -> int {  // K-unit of step q
+      const int j = q / spu;
+      if (!p.emulated) return j;
+      const int u = __builtin_amdgcn_readfirstlane(s_sched[j]);
+      aborted |= u < 0;
+      return u < 0 ? 0 : u;
     };
-    for (int s = 0; s < nk; s += 2) {
-      step(s, st0, st1);
-      if (s + 1 < nk) step(s + 1, st1, st0);
-    }
+    // the unit decided at step q (when step q+2 starts a unit, the one after it), or -1
+    auto decided_at = [&](int q) -> int {
+      const int pf = q + 2;
+      if (!p.emulated || pf >= nk || pf % spu) return -1;
+      const int jn = pf / spu + 1;
+      return (jn >= n_pre && jn < n_ku) ? jn : -1;
+    };
+    auto before_load = [&](int q) {
+      polled = decided_at(q) >= 0 && wave == 0;
+      if (polled) ag_poll_issue(p, ur0, n_ur, lane, pl);
+    };
+    auto load = [&](int q, char* dst) { load_step(unit_of(q) * spu + q % spu, dst); };
+    auto before_wait = [&](int q) {
+      if (polled) {
+        const int u = ag_pick_polled(p, ur0, n_ur, s_done, lane, pl);
+        if (lane == 0) s_sched[decided_at(q)] = u;
+      }
+    };
+    k_loop3(g, nk, st0, st1, st2, before_load, load, before_wait);
 
     // epilogue: fp32 C tile, staged through LDS into row-contiguous 16-byte stores
     g.epilogue(st0, st1, wm, wn, lane, wave, [&](int row, int col, f32x4 v) {
@@ -241,7 +313,8 @@ __device__ void ag_compute_role(const AgParams& p, int slot, char* st0, char* st
 __global__ __launch_bounds__(256, 1) void ag_gemm_kernel(AgParams p) {
   __shared__ __attribute__((aligned(16))) char st0[AgTile::STAGE];
   __shared__ __attribute__((aligned(16))) char st1[AgTile::STAGE];
-  __shared__ int s_next[2];
+  __shared__ __attribute__((aligned(16))) char st2[AgTile::STAGE];
+  __shared__ int s_sched[64];
   __shared__ uint64_t s_done;
   const int wg = blockIdx.x;
   if (wg < p.n_copy) {
@@ -249,7 +322,7 @@ __global__ __launch_bounds__(256, 1) void ag_gemm_kernel(AgParams p) {
     return;
   }
   const int slot = wg - p.n_copy;
-  if (slot < p.n_compute) ag_compute_role(p, slot, st0, st1, s_next, &s_done);
+  if (slot < p.n_compute) ag_compute_role(p, slot, st0, st1, st2, s_sched, &s_done);
 }
 
 hipError_t launch_ag_gemm(const AgParams& p, int grid, hipStream_t s) {

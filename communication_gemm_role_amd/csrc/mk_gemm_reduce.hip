@@ -42,7 +42,7 @@ __device__ __forceinline__ const float* peer_src(const RedParams& p, int q) {
 // ------------------------------------------------------------------------------------------
 // copy role (emulated landing of peer partials)
 // ------------------------------------------------------------------------------------------
-__device__ void red_copy_role(const RedParams& p, int cid) {
+__device__ __forceinline__ void red_copy_role(const RedParams& p, int cid) {
   const int tid = threadIdx.x;
   const int cpr = p.unit_cols >> 2;             // 16-byte chunks per unit row (fp32)
   const int per_t = (p.unit_rows * cpr) >> 8;   // 4 (64x64) .. 16 (128x128)
@@ -123,7 +123,7 @@ __device__ __forceinline__ bool wait_units(const RedParams& p, int lr0, int lr1,
 // reduce role: pre-sum the peers' partials of owned tiles
 // ------------------------------------------------------------------------------------------
 template <class T>
-__device__ void red_reduce_role(const RedParams& p, int rid, int* s_ok) {
+__device__ __forceinline__ void red_reduce_role(const RedParams& p, int rid, int* s_ok) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int own_rows = p.own_tile_end - p.own_tile_begin;
   const int n_jobs = own_rows * p.tiles_n;
@@ -182,7 +182,7 @@ __device__ void red_reduce_role(const RedParams& p, int rid, int* s_ok) {
 // compute role
 // ------------------------------------------------------------------------------------------
 template <class T>
-__device__ void red_compute_role(const RedParams& p, int slot, char* st0, char* st1, int* s_ok) {
+__device__ __forceinline__ void red_compute_role(const RedParams& p, int slot, char* st0, char* st1, char* st2, int* s_ok) {
   T g;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / T::WN, wn = wave % T::WN;
@@ -209,20 +209,7 @@ __device__ void red_compute_role(const RedParams& p, int slot, char* st0, char* 
       g.dma_b(b_col + rb, b_col_bytes - rb, ldb_b, dst, wave);
     };
     g.zero();
-    load_step(0, st0);
-    wait_mem();
-    __syncthreads();
-    // unrolled by two so each half names its stage buffers statically (no DMA/LDS-read alias wait)
-    auto step = [&](int s, char* cur, char* nxt) {
-      if (s + 1 < nk) load_step(s + 1, nxt);
-      g.mma(cur);
-      wait_mem();
-      __syncthreads();
-    };
-    for (int s = 0; s < nk; s += 2) {
-      step(s, st0, st1);
-      if (s + 1 < nk) step(s + 1, st1, st0);
-    }
+    k_loop3(g, nk, st0, st1, st2, load_step, [](int) {});
 
     int lr0, lr1;
     owned_rows<T>(p, tm, lr0, lr1);
@@ -271,6 +258,7 @@ template <class T>
 __global__ __launch_bounds__(256, 1) void gemm_reduce_kernel(RedParams p) {
   __shared__ __attribute__((aligned(16))) char st0[T::STAGE];
   __shared__ __attribute__((aligned(16))) char st1[T::STAGE];
+  __shared__ __attribute__((aligned(16))) char st2[T::STAGE];
   __shared__ int s_ok;
   const int wg = blockIdx.x;
   if (wg < p.n_copy) {
@@ -282,7 +270,7 @@ __global__ __launch_bounds__(256, 1) void gemm_reduce_kernel(RedParams p) {
     return;
   }
   const int slot = wg - p.n_copy - p.n_reduce;
-  if (slot < p.n_compute) red_compute_role<T>(p, slot, st0, st1, &s_ok);
+  if (slot < p.n_compute) red_compute_role<T>(p, slot, st0, st1, st2, &s_ok);
 }
 
 template <class T>

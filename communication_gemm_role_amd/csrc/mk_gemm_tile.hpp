@@ -361,4 +361,53 @@ struct TileGemmDma {
   }
 };
 
+// s_waitcnt immediate that waits until at most `n` vector-memory operations of this wave are
+// outstanding (expcnt / lgkmcnt left unconstrained).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Three-stage K loop over static stage buffers st0..st2: the DMA for step q+2 is issued before
+// the MFMAs of step q, and the end-of-step wait leaves that newest step's loads in flight, so
+// every load has two steps of MFMA work to land.  `load(step, stage)` issues one step's DMA
+// (DMA_PER_STEP instructions per wave); `before_wait(q)` runs after the MFMAs of step q.
+template <class G, class Load, class After>
+__device__ __forceinline__ void k_loop3(G& g, int nk, char* st0, char* st1, char* st2, Load&& load,
+                                        After&& before_wait) {
+  k_loop3(g, nk, st0, st1, st2, [](int) {}, load, before_wait);
+}
+
+// As above, with `before_load(q)` run at the start of step q, before the step's DMA is issued.
+template <class G, class Pre, class Load, class After>
+__device__ __forceinline__ void k_loop3(G& g, int nk, char* st0, char* st1, char* st2, Pre&& before_load,
+                                        Load&& load, After&& before_wait) {
+  constexpr int D = G::A_INSTR + G::B_INSTR;
+  load(0, st0);
+  if (nk > 1) {
+    load(1, st1);
+    wait_vm<D>();
+  } else {
+    wait_vm<0>();
+  }
+  __syncthreads();
+  auto sub = [&](int q, char* cur, char* pf) {
+    if (q >= nk) return;
+    const bool more = q + 2 < nk;
+    before_load(q);
+    if (more) load(q + 2, pf);
+    g.mma(cur);
+    before_wait(q);
+    if (more) wait_vm<D>();
+    else wait_vm<0>();
+    __syncthreads();
+  };
+  for (int q = 0; q < nk; q += 3) {
+    sub(q, st0, st2);
+    sub(q + 1, st1, st0);
+    sub(q + 2, st2, st1);
+  }
+}
+
 }  // namespace mk

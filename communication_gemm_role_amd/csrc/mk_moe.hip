@@ -50,7 +50,7 @@ __device__ __forceinline__ uint32_t* moe_misc(const MoeParams& p) { return p.cou
 // ------------------------------------------------------------------------------------------
 // route (one wave per 64-token chunk)
 // ------------------------------------------------------------------------------------------
-__device__ void moe_route_chunk(const MoeParams& p, int chunk, int lane) {
+__device__ __forceinline__ void moe_route_chunk(const MoeParams& p, int chunk, int lane) {
   const int t = chunk * 64 + lane;
   float tv[MOE_KMAX];
   int ti[MOE_KMAX];
@@ -102,7 +102,7 @@ __device__ void moe_route_chunk(const MoeParams& p, int chunk, int lane) {
 }
 
 // Exclusive scan of the per-chunk counts (run by one workgroup, the last router).
-__device__ void moe_scan(const MoeParams& p, MoeShared& sh) {
+__device__ __forceinline__ void moe_scan(const MoeParams& p, MoeShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   uint32_t* cnt = p.counters + p.off_chunk_cnt;
   // pass 1: per-expert totals
@@ -156,7 +156,7 @@ __device__ void moe_scan(const MoeParams& p, MoeShared& sh) {
 // ------------------------------------------------------------------------------------------
 // route + copy role
 // ------------------------------------------------------------------------------------------
-__device__ void moe_copy_role(const MoeParams& p, int cid, MoeShared& sh) {
+__device__ __forceinline__ void moe_copy_role(const MoeParams& p, int cid, MoeShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // route: chunks (cid*4 + wave) + i * (n_copy*4)
   for (int c = cid * 4 + wave; c < p.n_chunks; c += p.n_copy * 4) moe_route_chunk(p, c, lane);
@@ -272,7 +272,7 @@ __device__ void moe_copy_role(const MoeParams& p, int cid, MoeShared& sh) {
 // ------------------------------------------------------------------------------------------
 // compute role: ragged grouped GEMM
 // ------------------------------------------------------------------------------------------
-__device__ void moe_compute_role(const MoeParams& p, int slot, char* st0, char* st1, MoeShared& sh) {
+__device__ __forceinline__ void moe_compute_role(const MoeParams& p, int slot, char* st0, char* st1, char* st2, MoeShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (tid == 0) sh.ok = spin_until_eq(&p.flags[0], p.epoch, p.timeout_ticks, p.status);
   __syncthreads();
@@ -317,20 +317,7 @@ __device__ void moe_compute_role(const MoeParams& p, int slot, char* st0, char* 
       g.dma_b(b_col + rb, b_col_bytes - rb, ldb_b, dst, wave);
     };
     g.zero();
-    load_step(0, st0);
-    wait_mem();
-    __syncthreads();
-    // unrolled by two so each half names its stage buffers statically (no DMA/LDS-read alias wait)
-    auto step = [&](int s, char* cur, char* nxt) {
-      if (s + 1 < nk) load_step(s + 1, nxt);
-      g.mma(cur);
-      wait_mem();
-      __syncthreads();
-    };
-    for (int s = 0; s < nk; s += 2) {
-      step(s, st0, st1);
-      if (s + 1 < nk) step(s + 1, st1, st0);
-    }
+    k_loop3(g, nk, st0, st1, st2, load_step, [](int) {});
     g.epilogue(st0, st1, wm, wn, lane, wave, [&](int row, int col, f32x4 v) {
       if (row < rows_valid && col < cols_valid)
         *reinterpret_cast<f32x4*>(p.y + (size_t)(row0 + row) * p.ffn + (n0 + col)) = v;
@@ -342,10 +329,11 @@ __device__ void moe_compute_role(const MoeParams& p, int slot, char* st0, char* 
 __global__ __launch_bounds__(256, 1) void moe_kernel(MoeParams p) {
   __shared__ __attribute__((aligned(16))) char st0[MoeTile::STAGE];
   __shared__ __attribute__((aligned(16))) char st1[MoeTile::STAGE];
+  __shared__ __attribute__((aligned(16))) char st2[MoeTile::STAGE];
   __shared__ MoeShared sh;
   const int wg = blockIdx.x;
   if (wg < p.n_copy) moe_copy_role(p, wg, sh);
-  else if (wg - p.n_copy < p.n_compute) moe_compute_role(p, wg - p.n_copy, st0, st1, sh);
+  else if (wg - p.n_copy < p.n_compute) moe_compute_role(p, wg - p.n_copy, st0, st1, st2, sh);
   // exit accounting: the last workgroup out re-zeroes the counters for the next call
   wait_mem();
   __syncthreads();
