@@ -23,7 +23,9 @@
 
 namespace mk {
 
-using AgTile = TileGemmDma<256, 128, 2, 2>;
+// 256 x 256 output tile, eight waves of 128 x 64: one k-step moves 64 KiB of operands for 8.4 MFLOP.
+using AgTile = TileGemmDma<256, 256, 2, 4>;
+constexpr int AG_THREADS = AgTile::NW * 64;
 
 int ag_tile_m() { return AgTile::BM; }
 int ag_tile_n() { return AgTile::BN; }
@@ -40,14 +42,14 @@ __device__ __forceinline__ int ag_identity_unit(const AgParams& p, int pos) {
   return ur * p.n_ucols + uc;
 }
 
-// Units move in batches of 24 sixteen-byte chunks per thread (3 units of 128x128, 6 of 64x128 or
-// 12 of 64x64).  Per batch: write-through stores of the batch, then the loads of the next batch,
-// then a wait that covers only the stores (the next batch's 24 loads stay in flight), a barrier
-// and the flags of the landed units.  A slot past the end of this workgroup's queue (or a dropped
+// Units move in batches of 12 sixteen-byte chunks per thread (3 units of 128x128, 6 of 64x128 or
+// 12 of 64x64 with 512 threads).  Per batch: write-through stores of the batch, then the loads of
+// the next batch, then a wait that covers only the stores (the next batch's 12 loads stay in
+// flight), a barrier and the flags of the landed units.  A slot past the end of this workgroup's queue (or a dropped
 // unit) uses an empty buffer window, so every batch issues the same instruction count.
 template <int PER_T>
 __device__ __forceinline__ void ag_copy_batched(const AgParams& p, int cid) {
-  constexpr int UB = 24 / PER_T;  // units per batch
+  constexpr int UB = 12 / PER_T;  // units per batch
   const int tid = threadIdx.x;
   const int cpr = p.unit_cols >> 3;  // 16-byte chunks per unit row
   const uint32_t ldb = (uint32_t)p.k * 2u;
@@ -57,7 +59,7 @@ __device__ __forceinline__ void ag_copy_batched(const AgParams& p, int cid) {
   uint32_t off[PER_T];  // per-thread byte offset of each chunk inside a unit
 #pragma unroll
   for (int c = 0; c < PER_T; ++c) {
-    const int ch = tid + (c << 8);
+    const int ch = tid + c * AG_THREADS;
     const int row = ch / cpr, cc = ch - row * cpr;
     off[c] = (uint32_t)row * ldb + (uint32_t)cc * 16u;
   }
@@ -110,21 +112,22 @@ __device__ __forceinline__ void ag_copy_batched(const AgParams& p, int cid) {
   for (int i = 0; i < n_mine; i += 2 * UB) {
     store(i, va);
     load(i + UB, vb);  // past the end: empty windows, no traffic
-    wait_vm<24>();     // this batch's stores are acknowledged; the next batch's loads may fly on
+    wait_vm<12>();     // this batch's stores are acknowledged; the next batch's loads may fly on
     raise(i);
     if (i + UB >= n_mine) break;
     store(i + UB, vb);
     load(i + 2 * UB, va);
-    wait_vm<24>();
+    wait_vm<12>();
     raise(i + UB);
   }
 }
 
 __device__ __forceinline__ void ag_copy_role(const AgParams& p, int cid) {
-  const int per_t = (p.unit_rows * (p.unit_cols >> 3)) >> 8;  // 2 (64x64), 4 (64x128, 128x64), 8 (128x128)
-  if (per_t == 8) ag_copy_batched<8>(p, cid);
-  else if (per_t == 4) ag_copy_batched<4>(p, cid);
-  else ag_copy_batched<2>(p, cid);
+  // chunks per thread: 1 (64x64), 2 (64x128, 128x64), 4 (128x128)
+  const int per_t = (p.unit_rows * (p.unit_cols >> 3)) / AG_THREADS;
+  if (per_t == 4) ag_copy_batched<4>(p, cid);
+  else if (per_t == 2) ag_copy_batched<2>(p, cid);
+  else ag_copy_batched<1>(p, cid);
   wait_mem();
 }
 
@@ -215,8 +218,8 @@ __device__ __forceinline__ int ag_pick_polled(const AgParams& p, int ur0, int n_
   return u;
 }
 
-__device__ __forceinline__ void ag_compute_role(const AgParams& p, int slot, char* st0, char* st1, char* st2, int* s_sched,
-                                uint64_t* s_done) {
+__device__ __forceinline__ void ag_compute_role(const AgParams& p, int slot, char* st0, char* st1, char* st2,
+                                                int* s_sched, uint64_t* s_done) {
   AgTile g;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / AgTile::WN, wn = wave % AgTile::WN;
@@ -230,9 +233,12 @@ __device__ __forceinline__ void ag_compute_role(const AgParams& p, int slot, cha
   const int rs = ((C & 7) == 0) ? (slot & 7) * (C >> 3) + (slot >> 3) : slot;
   const uint32_t lda_b = (uint32_t)p.k * 2u, ldb_b = (uint32_t)p.n * 2u;
   g.init(wm, wn, lane, lda_b, ldb_b);
-  // K-units decided before the loop: unit j is prefetched two steps ahead of step j*spu and must be
-  // decided one iteration before that, so the prologue covers the first 2/spu + 1 units.
-  const int n_pre = min(n_ku, 2 / spu + 1);
+  // K-units decided before the loop.  Step q+PD is prefetched during step q, and a decision taken
+  // at step q (after its MFMAs) names the unit after the one step q+PD starts; the first decision
+  // falls on the step whose prefetch starts unit ceil(PD/spu), so the prologue decides units
+  // 0 .. ceil(PD/spu).
+  constexpr int PD = k_stages<AgTile>() - 1;  // prefetch distance of the K loop
+  const int n_pre = min(n_ku, (PD + spu - 1) / spu + 1);
 
   for (int t = rs; t < n_tiles; t += C) {
     const int tm = t / p.tiles_n, tn = t - tm * p.tiles_n;
@@ -280,9 +286,9 @@ __device__ __forceinline__ void ag_compute_role(const AgParams& p, int slot, cha
       aborted |= u < 0;
       return u < 0 ? 0 : u;
     };
-    // the unit decided at step q (when step q+2 starts a unit, the one after it), or -1
+    // the unit decided at step q (when step q+PD starts a unit, the one after it), or -1
     auto decided_at = [&](int q) -> int {
-      const int pf = q + 2;
+      const int pf = q + PD;
       if (!p.emulated || pf >= nk || pf % spu) return -1;
       const int jn = pf / spu + 1;
       return (jn >= n_pre && jn < n_ku) ? jn : -1;
@@ -298,7 +304,7 @@ __device__ __forceinline__ void ag_compute_role(const AgParams& p, int slot, cha
         if (lane == 0) s_sched[decided_at(q)] = u;
       }
     };
-    k_loop3(g, nk, st0, st1, st2, before_load, load, before_wait);
+    k_loop(g, nk, st0, st1, st2, before_load, load, before_wait);
 
     // epilogue: fp32 C tile, staged through LDS into row-contiguous 16-byte stores
     g.epilogue(st0, st1, wm, wn, lane, wave, [&](int row, int col, f32x4 v) {
@@ -310,10 +316,10 @@ __device__ __forceinline__ void ag_compute_role(const AgParams& p, int slot, cha
   }
 }
 
-__global__ __launch_bounds__(256, 1) void ag_gemm_kernel(AgParams p) {
+__global__ __launch_bounds__(AG_THREADS, 1) void ag_gemm_kernel(AgParams p) {
   __shared__ __attribute__((aligned(16))) char st0[AgTile::STAGE];
   __shared__ __attribute__((aligned(16))) char st1[AgTile::STAGE];
-  __shared__ __attribute__((aligned(16))) char st2[AgTile::STAGE];
+  __shared__ __attribute__((aligned(16))) char st2[k_stages<AgTile>() == 3 ? AgTile::STAGE : 16];
   __shared__ int s_sched[64];
   __shared__ uint64_t s_done;
   const int wg = blockIdx.x;
@@ -326,7 +332,7 @@ __global__ __launch_bounds__(256, 1) void ag_gemm_kernel(AgParams p) {
 }
 
 hipError_t launch_ag_gemm(const AgParams& p, int grid, hipStream_t s) {
-  hipLaunchKernelGGL(ag_gemm_kernel, dim3(grid), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(ag_gemm_kernel, dim3(grid), dim3(AG_THREADS), 0, s, p);
   return hipGetLastError();
 }
 

@@ -24,7 +24,7 @@
 
 namespace mk {
 
-using RedBig = TileGemmDma<256, 128, 2, 2>;   // wide outputs (e.g. 8192 x 4096)
+using RedBig = TileGemmDma<256, 256, 2, 4>;   // wide outputs (e.g. 8192 x 4096), eight waves
 using RedSkinny = TileGemmDma<128, 64, 4, 1>;  // few output rows (decode-like, m <= 512)
 
 static inline bool red_skinny(int m, int n) { (void)n; return m <= 512; }
@@ -42,10 +42,11 @@ __device__ __forceinline__ const float* peer_src(const RedParams& p, int q) {
 // ------------------------------------------------------------------------------------------
 // copy role (emulated landing of peer partials)
 // ------------------------------------------------------------------------------------------
+template <int NT>
 __device__ __forceinline__ void red_copy_role(const RedParams& p, int cid) {
   const int tid = threadIdx.x;
   const int cpr = p.unit_cols >> 2;             // 16-byte chunks per unit row (fp32)
-  const int per_t = (p.unit_rows * cpr) >> 8;   // 4 (64x64) .. 16 (128x128)
+  const int per_t = (p.unit_rows * cpr) / NT;   // 1024 (64x64) .. 4096 (128x128) chunks over NT threads
   const uint32_t ldb = (uint32_t)p.n * 4u;
   const int n_units = (p.world - 1) * p.units_per_peer;
   for (int pos = cid; pos < p.n_order; pos += p.n_copy) {
@@ -65,14 +66,14 @@ __device__ __forceinline__ void red_copy_role(const RedParams& p, int cid) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         if (h + i < per_t) {
-          const int c = tid + ((h + i) << 8);
+          const int c = tid + (h + i) * NT;
           const int row = c / cpr, cc = c - row * cpr;
           v[i] = bload16_nt(src, (uint32_t)row * ldb + (uint32_t)cc * 16u);
         }
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         if (h + i < per_t) {
-          const int c = tid + ((h + i) << 8);
+          const int c = tid + (h + i) * NT;
           const int row = c / cpr, cc = c - row * cpr;
           bstore16_sc1(dst, (uint32_t)row * ldb + (uint32_t)cc * 16u, v[i]);
         }
@@ -124,6 +125,7 @@ __device__ __forceinline__ bool wait_units(const RedParams& p, int lr0, int lr1,
 // ------------------------------------------------------------------------------------------
 template <class T>
 __device__ __forceinline__ void red_reduce_role(const RedParams& p, int rid, int* s_ok) {
+  constexpr int NT = T::NW * 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int own_rows = p.own_tile_end - p.own_tile_begin;
   const int n_jobs = own_rows * p.tiles_n;
@@ -148,7 +150,7 @@ __device__ __forceinline__ void red_reduce_role(const RedParams& p, int rid, int
     const size_t off = (size_t)lr0 * p.n + c0;
     const auto dst = make_rsrc(p.out + off, extent);
     const int total = rows * cpr;
-    for (int base = 0; base < total; base += 256 * 4) {
+    for (int base = 0; base < total; base += NT * 4) {
       f32x4 s[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) s[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -157,7 +159,7 @@ __device__ __forceinline__ void red_reduce_role(const RedParams& p, int rid, int
         const auto src = make_rsrc(peer_src(p, q) + off, extent);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int c = base + tid + i * 256;
+          const int c = base + tid + i * NT;
           const int row = c / cpr, cc = c - row * cpr;
           if (c < total && cc < ccols)
             s[i] += __builtin_bit_cast(f32x4, bload16_nt(src, ((uint32_t)row * (uint32_t)p.n + (uint32_t)cc * 4u) * 4u));
@@ -165,7 +167,7 @@ __device__ __forceinline__ void red_reduce_role(const RedParams& p, int rid, int
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int c = base + tid + i * 256;
+        const int c = base + tid + i * NT;
         const int row = c / cpr, cc = c - row * cpr;
         if (c < total && cc < ccols)
           bstore16_sc1(dst, ((uint32_t)row * (uint32_t)p.n + (uint32_t)cc * 4u) * 4u, __builtin_bit_cast(u32x4, s[i]));
@@ -209,7 +211,7 @@ __device__ __forceinline__ void red_compute_role(const RedParams& p, int slot, c
       g.dma_b(b_col + rb, b_col_bytes - rb, ldb_b, dst, wave);
     };
     g.zero();
-    k_loop3(g, nk, st0, st1, st2, load_step, [](int) {});
+    k_loop(g, nk, st0, st1, st2, [](int) {}, load_step, [](int) {});
 
     int lr0, lr1;
     owned_rows<T>(p, tm, lr0, lr1);
@@ -255,14 +257,14 @@ __device__ __forceinline__ void red_compute_role(const RedParams& p, int slot, c
 }
 
 template <class T>
-__global__ __launch_bounds__(256, 1) void gemm_reduce_kernel(RedParams p) {
+__global__ __launch_bounds__(T::NW * 64, 1) void gemm_reduce_kernel(RedParams p) {
   __shared__ __attribute__((aligned(16))) char st0[T::STAGE];
   __shared__ __attribute__((aligned(16))) char st1[T::STAGE];
-  __shared__ __attribute__((aligned(16))) char st2[T::STAGE];
+  __shared__ __attribute__((aligned(16))) char st2[k_stages<T>() == 3 ? T::STAGE : 16];
   __shared__ int s_ok;
   const int wg = blockIdx.x;
   if (wg < p.n_copy) {
-    red_copy_role(p, wg);
+    red_copy_role<T::NW * 64>(p, wg);
     return;
   }
   if (wg < p.n_copy + p.n_reduce) {
@@ -275,7 +277,7 @@ __global__ __launch_bounds__(256, 1) void gemm_reduce_kernel(RedParams p) {
 
 template <class T>
 static hipError_t launch_t(const RedParams& p, int grid, hipStream_t s) {
-  hipLaunchKernelGGL(gemm_reduce_kernel<T>, dim3(grid), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(gemm_reduce_kernel<T>, dim3(grid), dim3(T::NW * 64), 0, s, p);
   return hipGetLastError();
 }
 

@@ -26,7 +26,8 @@ struct TileGemm {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
   static constexpr int BK = 64;
   static constexpr int NT = 256;
-  static_assert(WM * WN == 4, "4 waves");
+  static constexpr int NW = WM * WN;  // waves per workgroup
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
   static_assert(FM * 32 == WTM && FN * 32 == WTN, "wave tile must be a multiple of 32");
@@ -206,7 +207,8 @@ template <int BM_, int BN_, int WM_, int WN_>
 struct TileGemmDma {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
   static constexpr int BK = 64;
-  static_assert(WM * WN == 4, "4 waves");
+  static constexpr int NW = WM * WN;  // waves per workgroup
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
   static_assert(FM * 32 == WTM && FN * 32 == WTN, "wave tile must be a multiple of 32");
@@ -214,9 +216,11 @@ struct TileGemmDma {
   static constexpr int STAGE_B = BN * BK * 2;
   static constexpr int STAGE = STAGE_A + STAGE_B;
   static constexpr int LDS_BYTES = 2 * STAGE;
-  static constexpr int A_INSTR = STAGE_A / 4 / 1024;  // 1 KiB DMA instructions per wave
-  static constexpr int B_INSTR = STAGE_B / 4 / 1024;
-  static_assert(A_INSTR * 4096 == STAGE_A && B_INSTR * 4096 == STAGE_B, "stage must split into 1 KiB per wave");
+  static constexpr int A_INSTR = STAGE_A / NW / 1024;  // 1 KiB DMA instructions per wave
+  static constexpr int B_INSTR = STAGE_B / NW / 1024;
+  static_assert(A_INSTR * NW * 1024 == STAGE_A && B_INSTR * NW * 1024 == STAGE_B,
+                "stage must split into 1 KiB per wave");
+  static_assert((BM / NW) % 8 == 0, "each wave's A rows form whole 8-row groups");
   static constexpr int ROW_B = BN * 2;  // bytes per B row in LDS
   static_assert(ROW_B <= 1024 && 1024 % ROW_B == 0, "a DMA instruction covers whole B rows");
 
@@ -276,7 +280,7 @@ struct TileGemmDma {
   __device__ __forceinline__ void dma_a(const char* abase, uint32_t a_bytes, uint32_t lda_b, char* lds, int wave) {
 #pragma unroll
     for (int i = 0; i < A_INSTR; ++i) {
-      const int r0 = wave * (BM / 4) + i * 8;
+      const int r0 = wave * (BM / NW) + i * 8;
       const auto rs = rsrc_at(abase, a_bytes, (uint32_t)r0 * lda_b);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(lds + r0 * 128), 16,
                                                a_dma[i & 1], 0, 0, 0);
@@ -286,7 +290,7 @@ struct TileGemmDma {
   __device__ __forceinline__ void dma_b(const char* bbase, uint32_t b_bytes, uint32_t ldb_b, char* lds, int wave) {
 #pragma unroll
     for (int i = 0; i < B_INSTR; ++i) {
-      const int byte0 = wave * (STAGE_B / 4) + i * 1024;
+      const int byte0 = wave * (STAGE_B / NW) + i * 1024;
       const int k0 = byte0 / ROW_B;
       const auto rs = rsrc_at(bbase, b_bytes, (uint32_t)k0 * ldb_b);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(lds + STAGE_A + byte0),
@@ -326,18 +330,18 @@ struct TileGemmDma {
     }
   }
 
-  // Epilogue through LDS (see TileGemm::epilogue); waves 0-1 stage in `st_lo`, waves 2-3 in `st_hi`
-  // (each a different stage buffer, so the slabs fit after the mainloop).
+  // Epilogue through LDS (see TileGemm::epilogue); the first half of the waves stage in `st_lo`,
+  // the second half in `st_hi` (each a different stage buffer, so the slabs fit after the mainloop).
   static constexpr int EPI_STRIDE = WTN + 8;
   static constexpr int EPI_WAVE = 32 * EPI_STRIDE * 4;
-  static_assert(2 * EPI_WAVE <= STAGE, "two waves' staging must fit in one stage buffer");
+  static_assert((NW / 2) * EPI_WAVE <= STAGE, "half the waves' staging must fit in one stage buffer");
   template <class F>
   __device__ __forceinline__ void epilogue(char* st_lo, char* st_hi, int wm, int wn, int lane_in, int wave, F&& f) {
     // The staging addresses do not depend on the tile; an opaque copy of the lane id stops the
     // compiler from hoisting all of them out of the persistent tile loop (64+ live registers).
     int lane = lane_in;
     asm volatile("" : "+v"(lane));
-    float* wl = reinterpret_cast<float*>((wave < 2 ? st_lo : st_hi) + (wave & 1) * EPI_WAVE);
+    float* wl = reinterpret_cast<float*>((wave < NW / 2 ? st_lo : st_hi) + (wave % (NW / 2)) * EPI_WAVE);
     constexpr int C4 = WTN / 4;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -408,6 +412,46 @@ __device__ __forceinline__ void k_loop3(G& g, int nk, char* st0, char* st1, char
     sub(q + 1, st1, st0);
     sub(q + 2, st2, st1);
   }
+}
+
+// Two-stage K loop for tiles whose stage is too large for three buffers: the DMA for step q+1 is
+// issued before the MFMAs of step q and must land by the end of that step.
+template <class G, class Pre, class Load, class After>
+__device__ __forceinline__ void k_loop2(G& g, int nk, char* st0, char* st1, Pre&& before_load, Load&& load,
+                                        After&& before_wait) {
+  load(0, st0);
+  wait_vm<0>();
+  __syncthreads();
+  auto sub = [&](int q, char* cur, char* pf) {
+    if (q >= nk) return;
+    before_load(q);
+    if (q + 1 < nk) load(q + 1, pf);
+    g.mma(cur);
+    before_wait(q);
+    wait_vm<0>();
+    __syncthreads();
+  };
+  for (int q = 0; q < nk; q += 2) {
+    sub(q, st0, st1);
+    sub(q + 1, st1, st0);
+  }
+}
+
+// Stage buffers a tile's K loop uses: three when they fit in the 160 KiB of LDS beside a few KiB
+// of bookkeeping, else two.
+template <class G>
+constexpr int k_stages() {
+  return 3 * G::STAGE <= 150 * 1024 ? 3 : 2;
+}
+
+// The K loop for tile G on its stage count (st2 is unused with two stages).
+template <class G, class Pre, class Load, class After>
+__device__ __forceinline__ void k_loop(G& g, int nk, char* st0, char* st1, char* st2, Pre&& before_load, Load&& load,
+                                       After&& before_wait) {
+  if constexpr (k_stages<G>() == 3)
+    k_loop3(g, nk, st0, st1, st2, before_load, load, before_wait);
+  else
+    k_loop2(g, nk, st0, st1, before_load, load, before_wait);
 }
 
 }  // namespace mk

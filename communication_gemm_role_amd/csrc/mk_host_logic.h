@@ -51,6 +51,15 @@ inline int split_roles(int grid, int want_copy, int want_reduce, int want_comput
   return MK_OK;
 }
 
+// A compute role larger than the tile count leaves workgroups idle; with the XCD-contiguous tile
+// order those idle slots would all fall on the last XCDs.  Unless a count was requested, keep just
+// enough compute workgroups for one tile each, rounded up to whole XCD rounds.
+inline int fit_compute(int n_compute, int tiles, const Opts* o) {
+  if (o && o->n_compute_wg > 0) return n_compute;
+  const int need = (tiles + 7) & ~7;
+  return need < n_compute ? need : n_compute;
+}
+
 // ---- AllGather + GEMM ---------------------------------------------------------------------
 struct AgPlan {
   int m, unit_rows, unit_cols, n_urows, n_ucols, n_order, local_in_place, emulated, drop_pos;
@@ -107,6 +116,7 @@ inline int plan_ag(const Ws& ws, const Opts* o, const void* const* a_shards, int
   int code = split_roles(ws.grid, P->emulated ? want_copy : 0, 0, o ? o->n_compute_wg : 0, &P->n_copy, &nr, &P->n_compute);
   if (code != MK_OK) return code;
   if (P->emulated && P->n_order == 0) P->n_copy = 0;
+  P->n_compute = fit_compute(P->n_compute, P->tiles_m * P->tiles_n, o);
   return MK_OK;
 }
 

@@ -112,6 +112,13 @@ def test_plan_ag_full_workload(hostlib):
     code, p = ag(hostlib, shards="inplace")
     assert code == MK_OK and p["local_in_place"] == 1 and p["n_order"] == 7 * 8 * 32
     assert (p["n_copy"], p["n_compute"], p["tiles_m"], p["tiles_n"]) == (32, 224, 32, 7)
+    # resident: no copy role, and the compute role is cut to the 224 tiles (whole XCD rounds)
+    code, p = ag(hostlib, shards="none", opts=Opts(arrival_mode=RESIDENT))
+    assert code == MK_OK and (p["n_copy"], p["n_compute"]) == (0, 224)
+    code, p = ag(hostlib, m_shard=64, world=3, rank=0, shards="none", opts=Opts(arrival_mode=RESIDENT))
+    assert code == MK_OK and p["tiles_m"] == 1 and p["n_compute"] == 8
+    code, p = ag(hostlib, shards="none", opts=Opts(arrival_mode=RESIDENT, n_compute_wg=250))
+    assert code == MK_OK and p["n_compute"] == 250  # an explicit request is kept
 
 
 def test_plan_ag_errors(hostlib):
