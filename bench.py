@@ -32,6 +32,44 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
 N_SETS = 4
 
+# HBM traffic of the AG+GEMM kernel comes from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) kept
+# in profiles/, each scaled by what the same counter reads for a plain copy of known size.  The
+# figures are valid only for the kernel they were taken on: the file records a hash of the sources
+# that make up the kernel and its launch, and the traffic is reported as null once they differ.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ag_gemm_kernel_mlp_ag_traffic.md")
+KERNEL_SOURCES = ["mk_ag_gemm.hip", "mk_gemm_tile.hpp", "mk_device.hpp", "mk_internal.h", "mk_host_logic.h",
+                  "mk_api.cpp"]
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "communication_gemm_role_amd", "csrc", f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def ag_algorithmic_bytes(s) -> int:
+    """HBM bytes one fused AG+GEMM launch must move with the local shard in place: the W-1 peer
+    shards read and written into the gathered A, the gathered A and B read once, C written once."""
+    copy = (s.world - 1) * s.m_shard * s.k * 2
+    return 2 * copy + s.m * s.k * 2 + s.k * s.n * 2 + s.m * s.n * 4
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed counter summary, or None if absent or stale."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            kv = dict(line.strip()[2:].split(": ", 1) for line in fh if line.startswith("- ") and ": " in line)
+        if kv.get("source_hash") != kernel_source_hash():
+            return None
+        fetch = float(kv["fetch_kib_per_dispatch"]) * float(kv["fetch_scale"])
+        write = float(kv["write_kib_per_dispatch"]) * float(kv["write_scale"])
+        return (fetch + write) * 1024.0
+    except (OSError, KeyError, ValueError):
+        return None
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -172,7 +210,7 @@ def cpu_baseline(budget_s: float = 12.0):
     except Exception:
         pass
     reps, t_total = 0, 0.0
-    while t_total < budget_s and reps < 20:
+    while t_total < budget_s and reps < 1000:
         t0 = time.perf_counter()
         oracle.ag_gemm(d["a_shards"], d["b"])
         t_total += time.perf_counter() - t0
@@ -238,8 +276,12 @@ def main():
                                "bf16 (gathered M=8192), B 4096x1792 bf16, C 8192x1792 fp32, 128x128 units landing "
                                "in a seeded random order", "arrival": "emulated", "sets_rotated": N_SETS},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": ag_algorithmic_bytes(s)},
     }
+    traffic = measured_traffic()
+    if traffic is not None:
+        result["roofline"]["traffic"] = round(traffic)
     if not a.no_secondary:
         sec = {}
         _, calls_r = setup_ag(ctx, resident=True)
