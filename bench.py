@@ -79,7 +79,8 @@ def parse():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default="",
-                    help="profiling: run only this op (ag, ag_resident, rs, ar, rs_emulated, ar_emulated, moe, copy)")
+                    help="profiling: run only this op (ag, ag_resident, ag_identity, rs, ar, rs_emulated, ar_emulated, moe, "
+                         "copy)")
     return ap.parse_args()
 
 
@@ -117,7 +118,7 @@ def time_calls(fns, steps, warmup):
 
 
 # ------------------------------------------------------------------------------------------------
-def setup_ag(ctx, resident: bool):
+def setup_ag(ctx, resident: bool, identity: bool = False):
     import torch
     import communication_gemm_role_amd as mk
     import workloads as wl
@@ -138,7 +139,7 @@ def setup_ag(ctx, resident: bool):
         else:
             ag[:s.m_shard].copy_(shards[0])
             shards[0] = ag[:s.m_shard]
-            opts = mk.Opts(arrival_mode=mk.MK_ARRIVAL_EMULATED, arrival_order=order)
+            opts = mk.Opts(arrival_mode=mk.MK_ARRIVAL_EMULATED, arrival_order=None if identity else order)
         calls.append(lambda sh=shards, b=b, ag=ag, c=c, o=opts: mk.mk_ag_gemm(ctx, sh, s.world, 0, b, ag, c, opts=o))
     return s, calls
 
@@ -232,8 +233,8 @@ def main():
     ctx = mk.Context(0)
 
     if a.only:
-        if a.only in ("ag", "ag_resident"):
-            _, calls = setup_ag(ctx, a.only == "ag_resident")
+        if a.only in ("ag", "ag_resident", "ag_identity"):
+            _, calls = setup_ag(ctx, a.only == "ag_resident", identity=a.only == "ag_identity")
         elif a.only in ("rs", "ar"):
             _, calls = setup_reduce(ctx, a.only)
         elif a.only in ("rs_emulated", "ar_emulated"):

@@ -11,6 +11,7 @@ from __future__ import annotations
 import argparse
 import concurrent.futures as cf
 import os
+import re
 import subprocess
 import sys
 
@@ -27,8 +28,17 @@ ARCH = "gfx950"
 HIP_FLAGS = [
     "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-Wall", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",  # no packed fp32 VALU ops
+    # Clang copies a by-value kernel parameter struct into private memory and relies on InstCombine
+    # to read it from the kernel-argument segment instead; InstCombine gives up past 300 uses of the
+    # copy, which leaves the whole struct in scratch and every parameter read in the hot loops a
+    # scratch load.  The role kernels use their parameters more often than that.
+    "-mllvm", "-instcombine-max-copied-from-constant-users=4096",
+    "-Rpass-analysis=kernel-resource-usage",  # per-kernel resource remarks, checked below
     "-I", INCLUDE, "-I", CSRC,
 ]
+# A kernel's register spills or a scratch area the size of a parameter struct mean the hot loop
+# reads memory it should not; the build refuses them.
+MAX_SCRATCH_BYTES = 128
 SOURCES = ["mk_ag_gemm.hip", "mk_gemm_reduce.hip", "mk_moe.hip", "mk_selftest.hip", "mk_api.cpp"]
 
 
@@ -39,10 +49,31 @@ def _run(cmd):
     return r.stdout
 
 
+def check_resources(src: str, remarks: str) -> list:
+    """Parse the kernel-resource-usage remarks of one compile; raise on spills or large scratch."""
+    kernels, cur = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"remark:\s+(Function Name|VGPRs|AGPRs|ScratchSize \[bytes/lane\]|VGPRs Spill|"
+                      r"LDS Size \[bytes/block\]): (\S+)", line)
+        if not m:
+            continue
+        key, val = m.group(1), m.group(2)
+        if key == "Function Name":
+            cur = {"kernel": val}
+            kernels.append(cur)
+        elif cur is not None:
+            cur[key.split(" [")[0]] = int(val)
+    for k in kernels:
+        if k.get("VGPRs Spill", 0) > 0 or k.get("ScratchSize", 0) >= MAX_SCRATCH_BYTES:
+            raise RuntimeError(f"{src}: kernel {k['kernel']} spills or uses scratch: {k}")
+    return kernels
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    _run([HIPCC, *HIP_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+    out = _run([HIPCC, *HIP_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+    check_resources(src, out)
     return obj
 
 

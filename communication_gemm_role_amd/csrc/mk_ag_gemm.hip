@@ -9,7 +9,8 @@
 // number of SMs per role):
 //   workgroups [0, n_copy)          copy: for queue positions cid, cid + n_copy, ... of the
 //                                   arrival order, copy that unit of a peer shard into its
-//                                   rows of a_gathered, then raise the unit's ready flag.
+//                                   rows of a_gathered (staged through LDS), then raise the
+//                                   unit's ready flag.
 //                                   Copy workgroups never wait, so they always finish.
 //   workgroups [n_copy, grid)       compute: 256 x 256 output tiles of C.  In emulated mode the
 //                                   K loop visits K-units (unit_cols columns of K) ready-first:
@@ -42,32 +43,41 @@ __device__ __forceinline__ int ag_identity_unit(const AgParams& p, int pos) {
   return ur * p.n_ucols + uc;
 }
 
-// Units move in batches of 12 sixteen-byte chunks per thread (3 units of 128x128, 6 of 64x128 or
-// 12 of 64x64 with 512 threads).  Per batch: write-through stores of the batch, then the loads of
-// the next batch, then a wait that covers only the stores (the next batch's 12 loads stay in
-// flight), a barrier and the flags of the landed units.  A slot past the end of this workgroup's queue (or a dropped
-// unit) uses an empty buffer window, so every batch issues the same instruction count.
-template <int PER_T>
-__device__ __forceinline__ void ag_copy_batched(const AgParams& p, int cid) {
-  constexpr int UB = 12 / PER_T;  // units per batch
-  const int tid = threadIdx.x;
+// Every wave moves its own share of each unit global -> LDS (DMA) -> VGPRs -> global through two
+// 64 KiB batch slots (the stage buffers, idle in a copy workgroup): while one batch is stored, the
+// next is landing and the one after is requested, so up to 128 KiB of loads are in flight per CU
+// and no register holds data in flight.  A batch is 2 units of 128x128, 4 of 64x128 / 128x64 or 8
+// of 64x64; IPU is a unit's DMA instructions per wave (1 KiB each).  Stores are write-through;
+// a batch's flags are raised once every wave's stores of it have completed.  Slots past the end of
+// this workgroup's queue (and a dropped unit) use empty buffer windows, so every batch issues the
+// same instructions and the vmcnt arithmetic below holds: per batch and wave 8 DMA loads and 8
+// stores, completing in issue order.  The two slots are distinct LDS arrays named statically in an
+// unrolled loop, so the compiler can see that reads of one never alias the DMA into the other.
+template <int IPU>
+__device__ __forceinline__ void ag_copy_dma(const AgParams& p, int cid, char* st0, char* st1) {
+  constexpr int UPB = 8 / IPU;  // units per batch
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int cpr = p.unit_cols >> 3;  // 16-byte chunks per unit row
   const uint32_t ldb = (uint32_t)p.k * 2u;
   const uint32_t extent = ((uint32_t)(p.unit_rows - 1) * (uint32_t)p.k + (uint32_t)p.unit_cols) * 2u;
   const int n_units = p.n_urows * p.n_ucols;
   const int n_mine = p.n_order > cid ? (p.n_order - cid + p.n_copy - 1) / p.n_copy : 0;
-  uint32_t off[PER_T];  // per-thread byte offset of each chunk inside a unit
+  const int nb = (n_mine + UPB - 1) / UPB;
+  // The arrival order is constant for the launch: reading it through the constant address space
+  // makes the loads scalar, off the vector-memory counter the pipeline waits on.
+  const __attribute__((address_space(4))) int32_t* order = (const __attribute__((address_space(4))) int32_t*)p.order;
+  uint32_t off[IPU];  // byte offset inside a unit of this lane's chunk, per instruction of the unit
 #pragma unroll
-  for (int c = 0; c < PER_T; ++c) {
-    const int ch = tid + c * AG_THREADS;
-    const int row = ch / cpr, cc = ch - row * cpr;
-    off[c] = (uint32_t)row * ldb + (uint32_t)cc * 16u;
+  for (int i = 0; i < IPU; ++i) {
+    const int c = (wave * IPU + i) * 64 + lane;
+    const int row = c / cpr, cc = c - row * cpr;
+    off[i] = (uint32_t)row * ldb + (uint32_t)cc * 16u;
   }
   auto unit_at = [&](int i) -> int {  // i-th unit of this workgroup's queue, or -1
     if (i >= n_mine) return -1;
     const int pos = cid + i * p.n_copy;
     if (pos + 1 == p.drop_pos) return -1;  // testing: this unit never lands
-    const int u = p.order ? p.order[pos] : ag_identity_unit(p, pos);
+    const int u = order ? order[pos] : ag_identity_unit(p, pos);
     return (u < 0 || u >= n_units) ? -1 : u;
   };
   auto src_of = [&](int u) {
@@ -82,53 +92,67 @@ __device__ __forceinline__ void ag_copy_batched(const AgParams& p, int cid) {
     const int ur = u / p.n_ucols, uc = u - ur * p.n_ucols;
     return make_rsrc(p.ag + (size_t)ur * p.unit_rows * p.k + (size_t)uc * p.unit_cols, extent);
   };
-  u32x4 va[UB][PER_T], vb[UB][PER_T];
-  auto load = [&](int i0, u32x4 (&v)[UB][PER_T]) {
+  // this wave's 8 KiB of a slot: instruction q of the batch at +1 KiB * q, lane l at +16 B * l
+  auto dma = [&](int b, char* slot) {
+    char* base = slot + wave * 8192;
 #pragma unroll
-    for (int b = 0; b < UB; ++b) {
-      const auto src = src_of(unit_at(i0 + b));
+    for (int j = 0; j < UPB; ++j) {
+      const auto src = src_of(unit_at(b * UPB + j));
 #pragma unroll
-      for (int c = 0; c < PER_T; ++c) v[b][c] = bload16_nt(src, off[c]);
+      for (int i = 0; i < IPU; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            src, (__attribute__((address_space(3))) void*)(base + (j * IPU + i) * 1024), 16, off[i], 0, 0, 0);
     }
   };
-  auto store = [&](int i0, u32x4 (&v)[UB][PER_T]) {
+  auto store = [&](int b, const char* slot) {
+    const char* base = slot + wave * 8192 + lane * 16;
 #pragma unroll
-    for (int b = 0; b < UB; ++b) {
-      const auto dst = dst_of(unit_at(i0 + b));
+    for (int j = 0; j < UPB; ++j) {
+      const auto dst = dst_of(unit_at(b * UPB + j));
 #pragma unroll
-      for (int c = 0; c < PER_T; ++c) bstore16_sc1(dst, off[c], v[b][c]);
+      for (int i = 0; i < IPU; ++i)
+        bstore16_sc1(dst, off[i], *reinterpret_cast<const u32x4*>(base + (j * IPU + i) * 1024));
     }
   };
-  auto raise = [&](int i0) {
-    __syncthreads();
+  auto raise = [&](int b) {
     if (tid == 0)
-      for (int b = 0; b < UB; ++b) {
-        const int u = unit_at(i0 + b);
+      for (int j = 0; j < UPB; ++j) {
+        const int u = unit_at(b * UPB + j);
         if (u >= 0) flag_store(&p.flags[u], p.epoch);
       }
   };
-  if (n_mine == 0) return;
-  load(0, va);
-  for (int i = 0; i < n_mine; i += 2 * UB) {
-    store(i, va);
-    load(i + UB, vb);  // past the end: empty windows, no traffic
-    wait_vm<12>();     // this batch's stores are acknowledged; the next batch's loads may fly on
-    raise(i);
-    if (i + UB >= n_mine) break;
-    store(i + UB, vb);
-    load(i + 2 * UB, va);
-    wait_vm<12>();
-    raise(i + UB);
+  // Batch b has landed once no more than the instructions issued after its DMA are outstanding:
+  // the stores of b-1 and the DMA of b+1 (only the DMA of 1 for b = 0).  That also covers the
+  // stores of b-2, issued before the DMA of b, whose flags go up after the barrier.
+  auto step = [&](int b, char* slot) {
+    if (b >= nb) return;
+    if (b == 0) wait_vm<8>();
+    else wait_vm<16>();
+    barrier_only();  // the waits above order the stores; no LDS data crosses waves
+    if (b >= 2) raise(b - 2);
+    store(b, slot);
+    dma(b + 2, slot);  // this wave's LDS reads of the slot completed with the stores above
+  };
+  if (nb == 0) return;
+  dma(0, st0);
+  dma(1, st1);
+  for (int b = 0; b < nb; b += 2) {
+    step(b, st0);
+    step(b + 1, st1);
   }
+  wait_vm<0>();
+  __syncthreads();
+  for (int b = nb > 2 ? nb - 2 : 0; b < nb; ++b) raise(b);
 }
 
-__device__ __forceinline__ void ag_copy_role(const AgParams& p, int cid) {
-  // chunks per thread: 1 (64x64), 2 (64x128, 128x64), 4 (128x128)
-  const int per_t = (p.unit_rows * (p.unit_cols >> 3)) / AG_THREADS;
-  if (per_t == 4) ag_copy_batched<4>(p, cid);
-  else if (per_t == 2) ag_copy_batched<2>(p, cid);
-  else ag_copy_batched<1>(p, cid);
-  wait_mem();
+static_assert(AgTile::STAGE >= 65536 && AG_THREADS == 512, "copy slots: 64 KiB stage buffers, 8 waves");
+
+__device__ __forceinline__ void ag_copy_role(const AgParams& p, int cid, char* st0, char* st1) {
+  // DMA instructions per wave per unit: 4 (128x128), 2 (64x128, 128x64), 1 (64x64)
+  const int ipu = (p.unit_rows * p.unit_cols * 2) / (AG_THREADS * 16);
+  if (ipu == 4) ag_copy_dma<4>(p, cid, st0, st1);
+  else if (ipu == 2) ag_copy_dma<2>(p, cid, st0, st1);
+  else ag_copy_dma<1>(p, cid, st0, st1);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -324,7 +348,7 @@ __global__ __launch_bounds__(AG_THREADS, 1) void ag_gemm_kernel(AgParams p) {
   __shared__ uint64_t s_done;
   const int wg = blockIdx.x;
   if (wg < p.n_copy) {
-    ag_copy_role(p, wg);
+    ag_copy_role(p, wg, st0, st1);
     return;
   }
   const int slot = wg - p.n_copy;

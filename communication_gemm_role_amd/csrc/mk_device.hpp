@@ -79,6 +79,18 @@ __device__ __forceinline__ uint64_t wall_ticks() { return __builtin_readsteadyco
 __device__ __forceinline__ uint32_t flag_load(const uint32_t* f) {
   return __hip_atomic_load(const_cast<uint32_t*>(f), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// Workgroup barrier without the memory fence of __syncthreads.  The fence of a workgroup-scope
+// release makes the compiler wait for every outstanding vector-memory operation, stores included,
+// which would drain a copy pipeline at each barrier.  Callers order memory themselves with explicit
+// vmcnt waits before the barrier; the empty asm with a memory clobber keeps the compiler from
+// moving loads or stores across it.
+__device__ __forceinline__ void barrier_only() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ void flag_store(uint32_t* f, uint32_t v) {
   __hip_atomic_store(f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
