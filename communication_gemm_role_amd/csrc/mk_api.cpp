@@ -7,7 +7,7 @@
 
 #include <new>
 
-#include "../../include/mk.h"
+#include "mk.h"
 #include "mk_host_logic.h"
 #include "mk_internal.h"
 

@@ -212,6 +212,7 @@ inline int plan_moe(const Ws& ws, const Opts* o, const void* const* tokens, int 
   const int mode = (o && o->arrival_mode) ? o->arrival_mode : MK_ARRIVAL_EMULATED;
   if (mode != MK_ARRIVAL_RESIDENT && mode != MK_ARRIVAL_EMULATED) return MK_ERR_INVALID_ARG;
   if (top_k > 8 || n_experts > 1024 || (n_experts & 3) || n_local > 64) return MK_ERR_UNSUPPORTED;
+  if (hidden > 4096) return MK_ERR_UNSUPPORTED;  // the dispatch copy moves at most 8 KiB per token row
   if (!mult64(t_local) || !mult64(hidden) || !mult64(ffn)) return MK_ERR_UNSUPPORTED;
   if (o && o->arrival_chunk_tokens && o->arrival_chunk_tokens != 64) return MK_ERR_UNSUPPORTED;
   if (!aligned16(logits) || !aligned16(bias) || !aligned16(w_up) || ((uintptr_t)topk_idx & 3u) ||
@@ -236,7 +237,7 @@ inline int plan_moe(const Ws& ws, const Opts* o, const void* const* tokens, int 
   P->off_tile_cnt = P->off_chunk_cnt + P->n_chunks * n_local;
   P->counters_need = (size_t)P->off_tile_cnt + (size_t)P->max_mtiles;
   if (P->counters_need > ws.n_counters || ws.n_flags < 1) return MK_ERR_WORKSPACE;
-  const int want_copy = (o && o->n_copy_wg) ? o->n_copy_wg : 64;
+  const int want_copy = (o && o->n_copy_wg) ? o->n_copy_wg : 128;  // copy workgroups also take leftover tiles
   int nr = 0;
   int code = split_roles(ws.grid, want_copy, 0, o ? o->n_compute_wg : 0, &P->n_copy, &nr, &P->n_compute);
   if (code != MK_OK) return code;

@@ -7,7 +7,7 @@
 // tokens of every rank are device buffers and their arrival is the copy role.
 //
 // Phases and roles (workgroup ids [0, n_copy) route and copy; the rest compute):
-//   route   each route wave takes 64-token chunks: score = fp32(logit + bias) for every
+//   route   every route wave takes 64-token chunks: score = fp32(logit + bias) for every
 //           expert, top-k by descending score with equal scores to the lower id (insertion
 //           in ascending expert order, replacing only on a strictly larger score), writes
 //           topk_idx and the chunk's row count per local expert.
@@ -15,9 +15,12 @@
 //           into segment offsets and per-(chunk, expert) first slots: an exclusive scan in
 //           chunk order, i.e. ascending global token id inside each expert's segment.  It
 //           also numbers the m-tiles of every segment, then raises the scan flag.
-//   copy    after the scan flag, chunks in the caller's arrival order: every routed
-//           (token, local expert) row is copied straight into its final slot of x_seg, its
-//           token id into seg_token, and the per-m-tile landed-row counter is raised.
+//   copy    after the scan flag, chunks in the caller's arrival order (positions claimed from
+//           a shared counter), a window of up to eight chunks at a time: each wave lists one
+//           chunk's routed (token, slot) rows, then all waves move the rows into their final
+//           slots of x_seg through LDS, and once the window's rows are stored they are added
+//           to their m-tiles' landed-row counters.  A copy workgroup with no chunks left joins
+//           the compute role on the tiles left over after every compute workgroup's first one.
 //   compute after the scan flag, (m-tile, n-tile) jobs of the ragged grouped GEMM: an m-tile
 //           runs once all of its rows have landed; y[slot] = x_seg[slot] @ w_up[expert].
 // Route/copy workgroups never wait on compute workgroups, and have the lowest ids.  The
@@ -27,88 +30,130 @@
 
 namespace mk {
 
-using MoeTile = TileGemmDma<128, 256, 2, 2>;
-constexpr int MOE_KMAX = 8;
+// 256 x 256 output tile, eight waves of 128 x 64, two-stage K loop
+using MoeTile = TileGemmDma<256, 256, 2, 4>;
+constexpr int MOE_WAVES = MoeTile::NW;
+constexpr int MOE_THREADS = MOE_WAVES * 64;
+constexpr int MOE_KMAX = 8;     // top-k
+constexpr int MOE_LMAX = 64;    // local experts
+constexpr int MOE_LIST = 2048;  // (token, slot) rows listed per copy window
 
 int moe_tile_m() { return MoeTile::BM; }
 int moe_tile_n() { return MoeTile::BN; }
 
 struct MoeShared {
-  int list_tok[64 * MOE_KMAX];
-  int list_slot[64 * MOE_KMAX];
-  int n_list;
+  int n_rows[MOE_WAVES];                 // rows of each window chunk
+  int pre[MOE_WAVES + 1];                // their prefix sums
+  int chunk_first[MOE_WAVES][MOE_LMAX];  // first slot of each (window chunk, local expert)
+  int chunk_cnt[MOE_WAVES][MOE_LMAX];    // rows of each (window chunk, local expert)
   int ok;
   int is_last;
-  int seg_off[65];
-  int tile_base[65];
-  int totals[64];
+  int claim;
+  int done;
+  int seg_off[MOE_LMAX + 1];
+  int tile_base[MOE_LMAX + 1];
+  int totals[MOE_LMAX];
 };
 
 __device__ __forceinline__ uint32_t* moe_misc(const MoeParams& p) { return p.counters + p.off_misc; }
-// misc layout: [0] route-done arrivals, [1] exits, [2 .. 2+n_local] m-tile base per expert (prefix)
+// misc layout: [0] route-done arrivals, [1] exits, [2 .. 2+n_local] m-tile base per expert (prefix),
+// [MISC_CLAIM] next arrival position to copy, [MISC_TILE] next leftover GEMM tile
+constexpr int MISC_CLAIM = 100;
+constexpr int MISC_TILE = 101;
 
 // ------------------------------------------------------------------------------------------
 // route (one wave per 64-token chunk)
 // ------------------------------------------------------------------------------------------
+template <int K>
 __device__ __forceinline__ void moe_route_chunk(const MoeParams& p, int chunk, int lane) {
-  const int t = chunk * 64 + lane;
-  float tv[MOE_KMAX];
-  int ti[MOE_KMAX];
+  float tv[K];
+  int ti[K];
 #pragma unroll
-  for (int j = 0; j < MOE_KMAX; ++j) {
+  for (int j = 0; j < K; ++j) {
     tv[j] = 0.f;
     ti[j] = -1;
   }
-  const auto lr = make_rsrc(p.logits + (size_t)t * p.n_experts, (uint32_t)p.n_experts * 4u);
-  const auto brs = make_rsrc(p.bias, (uint32_t)p.n_experts * 4u);
-  for (int e0 = 0; e0 < p.n_experts; e0 += 4) {
-    const f32x4 lg = __builtin_bit_cast(f32x4, bload16(lr, (uint32_t)e0 * 4u));
-    const f32x4 bs = __builtin_bit_cast(f32x4, bload16(brs, (uint32_t)e0 * 4u));
+  // One buffer window for the chunk's 64 logit rows (a per-lane window would be divergent and
+  // turn every load into a loop over the lanes); lane l reads row l.  The bias is the same for
+  // every lane and constant for the launch: scalar loads, a 64-expert block at a time.
+  const auto lr = make_rsrc(p.logits + (size_t)chunk * 64 * p.n_experts, 64u * (uint32_t)p.n_experts * 4u);
+  const uint32_t row_off = (uint32_t)lane * (uint32_t)p.n_experts * 4u;
+  const __attribute__((address_space(4))) f32x4* bias4 = (const __attribute__((address_space(4))) f32x4*)p.bias;
+  for (int e0 = 0; e0 < p.n_experts; e0 += 64) {
+    const int nq = min(16, (p.n_experts - e0) >> 2);  // n_experts is a multiple of 4
+    f32x4 lg[16], bs[16];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float v = lg[q] + bs[q];  // one fp32 add, round to nearest even
-      int id = e0 + q;
+    for (int q = 0; q < 16; ++q) {
+      lg[q] = __builtin_bit_cast(f32x4, bload16(lr, row_off + (uint32_t)(e0 + 4 * q) * 4u));
+      bs[q] = q < nq ? bias4[(e0 >> 2) + q] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
-      for (int j = 0; j < MOE_KMAX; ++j) {
-        if (j < p.top_k) {
-          const bool take = (id >= 0) && ((ti[j] < 0) || (v > tv[j]));  // empty slots sit at the end
-          if (take) {
-            const float fv = tv[j];
-            const int fi = ti[j];
-            tv[j] = v;
-            ti[j] = id;
-            v = fv;
-            id = fi;
-          }
+    for (int q = 0; q < 16; ++q) {
+      if (q >= nq) continue;  // uniform; a break would keep the loop rolled and the arrays in memory
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        int id = e0 + 4 * q + r;
+        float v = lg[q][r] + bs[q][r];  // one fp32 add, round to nearest even
+        // insertion into the descending list: replace only on a strictly larger score (equal
+        // scores keep the lower id, seen first); an empty slot (id -1) takes anything, and once
+        // the carried candidate is an empty slot nothing further changes
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+          const bool take = (id >= 0) && ((ti[j] < 0) || (v > tv[j]));
+          const float fv = tv[j];
+          const int fi = ti[j];
+          tv[j] = take ? v : fv;
+          ti[j] = take ? id : fi;
+          v = take ? fv : v;
+          id = take ? fi : id;
         }
       }
     }
   }
-  const auto tr = make_rsrc(p.topk_idx + (size_t)t * p.top_k, (uint32_t)p.top_k * 4u);
+  const auto tr = make_rsrc(p.topk_idx + (size_t)chunk * 64 * K, 64u * K * 4u);
 #pragma unroll
-  for (int j = 0; j < MOE_KMAX; ++j)
-    if (j < p.top_k) bstore4_sc1(tr, (uint32_t)j * 4u, (uint32_t)ti[j]);
-  // rows of this chunk per local expert
-  uint32_t* cnt = p.counters + p.off_chunk_cnt + (size_t)chunk * p.n_local;
+  for (int j = 0; j < K; ++j) bstore4_sc1(tr, ((uint32_t)lane * K + (uint32_t)j) * 4u, (uint32_t)ti[j]);
+  // rows of this chunk per local expert: lane el stores expert el's count
+  uint32_t mine = 0;
   for (int el = 0; el < p.n_local; ++el) {
     const int e = p.expert_begin + el;
     bool hit = false;
 #pragma unroll
-    for (int j = 0; j < MOE_KMAX; ++j)
-      if (j < p.top_k) hit |= (ti[j] == e);
-    const uint64_t m = __ballot(hit);
-    if (lane == 0) __hip_atomic_store(cnt + el, (uint32_t)__popcll(m), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int j = 0; j < K; ++j) hit |= (ti[j] == e);
+    const uint32_t c = (uint32_t)__popcll(__ballot(hit));
+    mine = lane == el ? c : mine;
   }
+  const auto cr = make_rsrc(p.counters + p.off_chunk_cnt + (size_t)chunk * p.n_local, (uint32_t)p.n_local * 4u);
+  bstore4_sc1(cr, (uint32_t)lane * 4u, mine);  // lanes past n_local fall outside the window
 }
 
-// Exclusive scan of the per-chunk counts (run by one workgroup, the last router).
+template <int K>
+__device__ __forceinline__ void moe_route_all(const MoeParams& p, int first, int stride, int lane) {
+  for (int c = first; c < p.n_chunks; c += stride) moe_route_chunk<K>(p, c, lane);
+}
+
+// Exclusive scan of the per-chunk counts (run by one workgroup, the last router).  Each wave
+// owns local experts wave, wave + 8, ...; a group of 16 x 64 chunk counts is loaded at once.
 __device__ __forceinline__ void moe_scan(const MoeParams& p, MoeShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   uint32_t* cnt = p.counters + p.off_chunk_cnt;
+  const auto cr = make_rsrc(cnt, (uint32_t)p.n_chunks * (uint32_t)p.n_local * 4u);
+  auto load_group = [&](int el, int g0, uint32_t(&v)[16]) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t c = (uint32_t)(g0 + i * 64 + lane);
+      v[i] = bload4_sc1(cr, (c * (uint32_t)p.n_local + (uint32_t)el) * 4u);  // past n_chunks: 0
+    }
+  };
   // pass 1: per-expert totals
-  for (int el = wave; el < p.n_local; el += 4) {
+  for (int el = wave; el < p.n_local; el += MOE_WAVES) {
     uint32_t s = 0;
-    for (int c = lane; c < p.n_chunks; c += 64) s += flag_load(cnt + (size_t)c * p.n_local + el);
+    for (int g0 = 0; g0 < p.n_chunks; g0 += 1024) {
+      uint32_t v[16];
+      load_group(el, g0, v);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s += v[i];
+    }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
     if (lane == 0) sh.totals[el] = (int)s;
@@ -128,178 +173,297 @@ __device__ __forceinline__ void moe_scan(const MoeParams& p, MoeShared& sh) {
   }
   __syncthreads();
   // pass 2: first slot of every (chunk, expert), in chunk order
-  for (int el = wave; el < p.n_local; el += 4) {
+  for (int el = wave; el < p.n_local; el += MOE_WAVES) {
     uint32_t run = (uint32_t)sh.seg_off[el];
-    for (int c0 = 0; c0 < p.n_chunks; c0 += 64) {
-      const int c = c0 + lane;
-      const uint32_t v = c < p.n_chunks ? flag_load(cnt + (size_t)c * p.n_local + el) : 0u;
-      uint32_t inc = v;
+    for (int g0 = 0; g0 < p.n_chunks; g0 += 1024) {
+      uint32_t v[16];
+      load_group(el, g0, v);
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(inc, o);
-        if (lane >= o) inc += y;
+      for (int i = 0; i < 16; ++i) {
+        uint32_t inc = v[i];
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t y = __shfl_up(inc, o);
+          if (lane >= o) inc += y;
+        }
+        const uint32_t c = (uint32_t)(g0 + i * 64 + lane);
+        bstore4_sc1(cr, (c * (uint32_t)p.n_local + (uint32_t)el) * 4u, run + inc - v[i]);  // past the end: dropped
+        run += __shfl(inc, 63);
       }
-      if (c < p.n_chunks) __hip_atomic_store(cnt + (size_t)c * p.n_local + el, run + inc - v, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-      run += __shfl(inc, 63);
     }
   }
-  for (int i = tid; i <= p.n_local; i += 256) {
-    bstore4_sc1(make_rsrc(p.seg_offsets, (uint32_t)(p.n_local + 1) * 4u), (uint32_t)i * 4u, (uint32_t)sh.seg_off[i]);
-    __hip_atomic_store(moe_misc(p) + 2 + i, (uint32_t)sh.tile_base[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const auto so = make_rsrc(p.seg_offsets, (uint32_t)(p.n_local + 1) * 4u);
+  const auto tb = make_rsrc(moe_misc(p) + 2, (uint32_t)(p.n_local + 1) * 4u);
+  for (int i = tid; i <= p.n_local; i += MOE_THREADS) {
+    bstore4_sc1(so, (uint32_t)i * 4u, (uint32_t)sh.seg_off[i]);
+    bstore4_sc1(tb, (uint32_t)i * 4u, (uint32_t)sh.tile_base[i]);
   }
   wait_mem();
   __syncthreads();
   if (tid == 0) flag_store(&p.flags[0], p.epoch);
 }
 
+// Segment offsets and m-tile bases of the scan, into LDS (every workgroup, after the scan flag).
+__device__ __forceinline__ void moe_load_segments(const MoeParams& p, MoeShared& sh) {
+  const auto so = make_rsrc(p.seg_offsets, (uint32_t)(p.n_local + 1) * 4u);
+  const auto tb = make_rsrc(moe_misc(p) + 2, (uint32_t)(p.n_local + 1) * 4u);
+  for (int i = threadIdx.x; i <= p.n_local; i += MOE_THREADS) {
+    sh.seg_off[i] = (int)bload4_sc1(so, (uint32_t)i * 4u);
+    sh.tile_base[i] = (int)bload4_sc1(tb, (uint32_t)i * 4u);
+  }
+}
+
 // ------------------------------------------------------------------------------------------
-// route + copy role
+// copy role
 // ------------------------------------------------------------------------------------------
-__device__ __forceinline__ void moe_copy_role(const MoeParams& p, int cid, MoeShared& sh) {
+// One wave lists the rows of window chunk w (chunk id c): every (token, local expert) pair, in
+// token order per expert, with slot = the expert's first slot for the chunk + rank; it also
+// writes seg_token, and the per-expert first slots and counts go to sh.
+__device__ __forceinline__ void moe_list_chunk(const MoeParams& p, MoeShared& sh, int2* list, int w, int c, int lane) {
+  const int t = c * 64 + lane;
+  int ti[MOE_KMAX];
+  const auto tr = make_rsrc(p.topk_idx + (size_t)c * 64 * p.top_k, 64u * (uint32_t)p.top_k * 4u);
+#pragma unroll
+  for (int j = 0; j < MOE_KMAX; ++j)
+    ti[j] = j < p.top_k ? (int)bload4_sc1(tr, ((uint32_t)lane * (uint32_t)p.top_k + (uint32_t)j) * 4u) : -1;
+  const auto fr = make_rsrc(p.counters + p.off_chunk_cnt + (size_t)c * p.n_local, (uint32_t)p.n_local * 4u);
+  const int first = (int)bload4_sc1(fr, (uint32_t)lane * 4u);  // lane el: first slot of expert el
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const auto st = make_rsrc(p.seg_token, (uint32_t)p.capacity * 4u);
+  int n = 0;
+  for (int el = 0; el < p.n_local; ++el) {
+    const int e = p.expert_begin + el;
+    bool hit = false;
+#pragma unroll
+    for (int j = 0; j < MOE_KMAX; ++j)
+      if (j < p.top_k) hit |= (ti[j] == e);
+    const uint64_t m = __ballot(hit);
+    const int fe = __builtin_amdgcn_readlane(first, el);
+    if (hit) {
+      const int rk = __popcll(m & lt);
+      list[n + rk] = make_int2(t, fe + rk);
+      bstore4_sc1(st, (uint32_t)(fe + rk) * 4u, (uint32_t)t);  // slots past capacity fall outside
+    }
+    if (lane == 0) {
+      sh.chunk_first[w][el] = fe;
+      sh.chunk_cnt[w][el] = __popcll(m);
+    }
+    n += __popcll(m);
+  }
+  if (lane == 0) sh.n_rows[w] = n;
+}
+
+// Add the stored rows of window chunk j to its m-tiles' counters (wave 0; lane el: expert el).
+__device__ __forceinline__ void moe_raise_chunk(const MoeParams& p, const MoeShared& sh, int j, int lane) {
+  if (lane >= p.n_local) return;
+  const int cnt = sh.chunk_cnt[j][lane];
+  if (cnt == 0) return;
+  const int first = sh.chunk_first[j][lane];
+  const int off_e = sh.seg_off[lane], tb = sh.tile_base[lane];
+  int s = first;
+  const int s_end = min(first + cnt, p.capacity);
+  while (s < s_end) {
+    const int mt = (s - off_e) / MoeTile::BM;
+    const int hi = min(s_end, off_e + (mt + 1) * MoeTile::BM);
+    atomic_add_agent(p.counters + p.off_tile_cnt + tb + mt, (uint32_t)(hi - s));
+    s = hi;
+  }
+}
+
+// Rows move global -> LDS (DMA) -> VGPRs -> global through the two 64 KiB stage buffers, as in
+// the AllGather copy: batch b gives wave w the window rows (8b + w) * RPB + i, i < RPB, each
+// IPR 1 KiB DMA instructions (RPB * IPR = 8 per wave and batch; lanes past a row's end fall
+// outside its buffer window).  Per batch and wave: 8 DMA loads and 8 stores, completing in issue
+// order, so batch b has landed at vmcnt <= 16 (8 for b = 0).  The window's chunks raise their
+// m-tile counters after the last store: counter atomics inside the loop would come in a
+// data-dependent number, and the compiler would then drain the whole pipeline before every LDS
+// read.  An m-tile spans chunks from the whole token range, so under a random arrival order it
+// completes near the end of the dispatch either way.
+template <int IPR>
+__device__ __forceinline__ void moe_copy_window(const MoeParams& p, const MoeShared& sh, const int2* list, int stride,
+                                                int n_win, char* st0, char* st1) {
+  constexpr int RPB = 8 / IPR;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // route: chunks (cid*4 + wave) + i * (n_copy*4)
-  for (int c = cid * 4 + wave; c < p.n_chunks; c += p.n_copy * 4) moe_route_chunk(p, c, lane);
+  (void)tid;
+  const int R = sh.pre[n_win];
+  const int nb = (R + 8 * RPB - 1) / (8 * RPB);
+  const uint32_t row_b = (uint32_t)p.hidden * 2u;
+  auto row_at = [&](int r) -> int2 {  // list entry of window row r, or (-1, -1)
+    if (r >= R) return make_int2(-1, -1);
+    int j = 0;
+    while (j + 1 < n_win && sh.pre[j + 1] <= r) ++j;
+    return list[j * stride + (r - sh.pre[j])];
+  };
+  auto src_of = [&](int t) {
+    if (t < 0) return make_rsrc(p.x_seg, 0u);
+    const int r = t / p.t_local, i = t - r * p.t_local;
+    return make_rsrc(p.tokens[r] + (size_t)i * p.hidden, row_b);
+  };
+  auto dst_of = [&](int slot) {
+    if (slot < 0 || slot >= p.capacity) return make_rsrc(p.x_seg, 0u);
+    return make_rsrc(p.x_seg + (size_t)slot * p.hidden, row_b);
+  };
+  auto dma = [&](int b, char* slot) {
+    char* base = slot + wave * 8192;
+#pragma unroll
+    for (int i = 0; i < RPB; ++i) {
+      const int2 e = row_at((b * 8 + wave) * RPB + i);
+      const auto src = src_of(__builtin_amdgcn_readfirstlane(e.x));
+#pragma unroll
+      for (int q = 0; q < IPR; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            src, (__attribute__((address_space(3))) void*)(base + (i * IPR + q) * 1024), 16,
+            (uint32_t)(q * 64 + lane) * 16u, 0, 0, 0);
+    }
+  };
+  auto store = [&](int b, const char* slot) {
+    const char* base = slot + wave * 8192 + lane * 16;
+#pragma unroll
+    for (int i = 0; i < RPB; ++i) {
+      const int2 e = row_at((b * 8 + wave) * RPB + i);
+      const auto dst = dst_of(__builtin_amdgcn_readfirstlane(e.y));
+#pragma unroll
+      for (int q = 0; q < IPR; ++q)
+        bstore16_sc1(dst, (uint32_t)(q * 64 + lane) * 16u,
+                     *reinterpret_cast<const u32x4*>(base + (i * IPR + q) * 1024));
+    }
+  };
+  auto step = [&](int b, char* slot) {
+    if (b >= nb) return;
+    if (b == 0) wait_vm<8>();
+    else wait_vm<16>();
+    barrier_only();  // no LDS data crosses waves; the barrier keeps the waves in step
+    store(b, slot);
+    dma(b + 2, slot);  // this wave's LDS reads of the slot completed with the stores above
+  };
+  if (nb > 0) {
+    dma(0, st0);
+    dma(1, st1);
+    for (int b = 0; b < nb; b += 2) {
+      step(b, st0);
+      step(b + 1, st1);
+    }
+  }
+  wait_vm<0>();
+  __syncthreads();
+  if (wave == 0)
+    for (int j = 0; j < n_win; ++j) moe_raise_chunk(p, sh, j, lane);
+  __syncthreads();  // the next window rewrites the lists and chunk tables
+}
+
+// Arrival positions are claimed from a shared counter, one per listing wave, so the positions
+// are taken in the caller's arrival order and a copy workgroup that finishes early takes more.
+template <int IPR>
+__device__ __forceinline__ void moe_dispatch(const MoeParams& p, MoeShared& sh, int2* list, char* st0, char* st1) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // window: one chunk per listing wave, each with room for its largest possible row count; no
+  // more chunks than give every copy workgroup about two windows, so the chunks spread over all
+  // of them (the last window to finish ends the dispatch)
+  const int stride = 64 * min(p.top_k, p.n_local);
+  const int cw = max(1, min(min(MOE_WAVES, MOE_LIST / stride), p.n_chunks / (2 * p.n_copy)));
+  const __attribute__((address_space(4))) int32_t* order = (const __attribute__((address_space(4))) int32_t*)p.order;
+  if (tid == 0) sh.done = 0;
+  while (true) {
+    if (wave < cw) {
+      int pos = 0;
+      if (lane == 0) pos = (int)atomic_add_agent(moe_misc(p) + MISC_CLAIM, 1u);
+      pos = __builtin_amdgcn_readfirstlane(pos);
+      int c = -1;
+      if (pos < p.n_chunks) {
+        c = (p.emulated && order) ? order[pos] : pos;
+        if (pos + 1 == p.drop_pos || c < 0 || c >= p.n_chunks) c = -1;  // testing: a dropped chunk never lands
+      } else if (lane == 0) {
+        sh.done = 1;  // the queue is exhausted: this is the last window
+      }
+      if (c >= 0) {
+        moe_list_chunk(p, sh, list + wave * stride, wave, c, lane);
+      } else {
+        if (lane == 0) sh.n_rows[wave] = 0;
+        for (int el = lane; el < p.n_local; el += 64) sh.chunk_cnt[wave][el] = 0;
+      }
+    }
+    __syncthreads();
+    if (tid == 0) {
+      sh.pre[0] = 0;
+      for (int j = 0; j < cw; ++j) sh.pre[j + 1] = sh.pre[j] + sh.n_rows[j];
+    }
+    __syncthreads();
+    const bool last = sh.done != 0;
+    moe_copy_window<IPR>(p, sh, list, stride, cw, st0, st1);  // ends with a barrier
+    if (last) break;
+  }
+}
+
+__device__ __forceinline__ void moe_copy_role(const MoeParams& p, int cid, MoeShared& sh, int2* list, char* st0,
+                                              char* st1) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // route: chunks (cid * 8 + wave) + i * (n_copy * 8)
+  const int c0 = cid * MOE_WAVES + wave, cs = p.n_copy * MOE_WAVES;
+  switch (p.top_k) {
+    case 1: moe_route_all<1>(p, c0, cs, lane); break;
+    case 2: moe_route_all<2>(p, c0, cs, lane); break;
+    case 3: moe_route_all<3>(p, c0, cs, lane); break;
+    case 4: moe_route_all<4>(p, c0, cs, lane); break;
+    case 5: moe_route_all<5>(p, c0, cs, lane); break;
+    case 6: moe_route_all<6>(p, c0, cs, lane); break;
+    case 7: moe_route_all<7>(p, c0, cs, lane); break;
+    default: moe_route_all<8>(p, c0, cs, lane); break;
+  }
   wait_mem();
   __syncthreads();
   if (tid == 0) sh.is_last = atomic_add_agent(moe_misc(p) + 0, 1u) == (uint32_t)(p.n_copy - 1);
   __syncthreads();
   if (sh.is_last) moe_scan(p, sh);
 
-  // dispatch
   if (tid == 0) sh.ok = spin_until_eq(&p.flags[0], p.epoch, p.timeout_ticks, p.status);
   __syncthreads();
   if (!sh.ok) return;
-  const int tile_m = MoeTile::BM;
-  const uint32_t row_b = (uint32_t)p.hidden * 2u;
-  const int cpr = p.hidden >> 3;  // 16-byte chunks per token row
-  for (int pos = cid; pos < p.n_chunks; pos += p.n_copy) {
-    if (pos + 1 == p.drop_pos) continue;
-    const int c = p.emulated && p.order ? p.order[pos] : pos;
-    if (c < 0 || c >= p.n_chunks) continue;
-    const int g0 = c * 64;
-    const int r = g0 / p.t_local, i0 = g0 - r * p.t_local;
-    if (wave == 0) {
-      const int t = g0 + lane;
-      int ti[MOE_KMAX];
-      const auto tr = make_rsrc(p.topk_idx + (size_t)t * p.top_k, (uint32_t)p.top_k * 4u);
-#pragma unroll
-      for (int j = 0; j < MOE_KMAX; ++j) ti[j] = j < p.top_k ? (int)bload4_sc1(tr, (uint32_t)j * 4u) : -1;
-      const uint32_t* base = p.counters + p.off_chunk_cnt + (size_t)c * p.n_local;
-      const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-      int n = 0;
-      for (int el = 0; el < p.n_local; ++el) {
-        const int e = p.expert_begin + el;
-        bool hit = false;
-#pragma unroll
-        for (int j = 0; j < MOE_KMAX; ++j)
-          if (j < p.top_k) hit |= (ti[j] == e);
-        const uint64_t m = __ballot(hit);
-        if (hit) {
-          const int rk = __popcll(m & lt);
-          sh.list_tok[n + rk] = t;
-          sh.list_slot[n + rk] = (int)flag_load(base + el) + rk;
-        }
-        n += __popcll(m);
-      }
-      if (lane == 0) sh.n_list = n;
-    }
-    __syncthreads();
-    const int n = sh.n_list;
-    // copy rows: wave w takes rows w, w+4, ...; 64 lanes x 16 B per instruction
-    for (int i = wave; i < n; i += 4) {
-      const int slot = sh.list_slot[i];
-      if (slot >= p.capacity) continue;
-      const int t = sh.list_tok[i];
-      const auto src = make_rsrc(p.tokens[r] + (size_t)(i0 + (t - g0)) * p.hidden, row_b);
-      const auto dst = make_rsrc(p.x_seg + (size_t)slot * p.hidden, row_b);
-      for (int cc0 = 0; cc0 < cpr; cc0 += 64 * 8) {
-        u32x4 v[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int cc = cc0 + q * 64 + lane;
-          if (cc < cpr) v[q] = bload16_nt(src, (uint32_t)cc * 16u);
-        }
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int cc = cc0 + q * 64 + lane;
-          if (cc < cpr) bstore16_sc1(dst, (uint32_t)cc * 16u, v[q]);
-        }
-      }
-      if (lane == 0) bstore4_sc1(make_rsrc(p.seg_token + slot, 4u), 0u, (uint32_t)t);
-    }
-    wait_mem();
-    __syncthreads();
-    // landed rows per m-tile: each local expert's rows of this chunk are a contiguous slot range
-    if (wave == 0) {
-      // per local expert: rows of this chunk (ballot over the chunk's tokens), first slot from the scan
-      const int t = g0 + lane;
-      int ti[MOE_KMAX];
-      const auto tr = make_rsrc(p.topk_idx + (size_t)t * p.top_k, (uint32_t)p.top_k * 4u);
-#pragma unroll
-      for (int j = 0; j < MOE_KMAX; ++j) ti[j] = j < p.top_k ? (int)bload4_sc1(tr, (uint32_t)j * 4u) : -1;
-      const uint32_t* base = p.counters + p.off_chunk_cnt + (size_t)c * p.n_local;
-      for (int el = 0; el < p.n_local; ++el) {
-        const int e = p.expert_begin + el;
-        bool hit = false;
-#pragma unroll
-        for (int j = 0; j < MOE_KMAX; ++j)
-          if (j < p.top_k) hit |= (ti[j] == e);
-        const int cnt_e = __popcll(__ballot(hit));
-        if (cnt_e == 0) continue;
-        if (lane == 0) {
-          const int first = (int)flag_load(base + el);
-          const uint32_t* misc = moe_misc(p);
-          // slot -> (expert-relative row) -> m-tile; clip to capacity
-          const int off_e = (int)flag_load((const uint32_t*)p.seg_offsets + el);
-          const int tb = (int)flag_load(misc + 2 + el);
-          int s = first;
-          const int s_end = min(first + cnt_e, p.capacity);
-          while (s < s_end) {
-            const int mt = (s - off_e) / tile_m;
-            const int tile_end = off_e + (mt + 1) * tile_m;
-            const int hi = min(s_end, tile_end);
-            atomic_add_agent(p.counters + p.off_tile_cnt + tb + mt, (uint32_t)(hi - s));
-            s = hi;
-          }
-        }
-      }
-    }
-    __syncthreads();
-  }
+  moe_load_segments(p, sh);
+  __syncthreads();
+  // DMA instructions per row and wave, rounded up to a power of two (8 for hidden 4096)
+  const int cpr = p.hidden >> 3;  // 16-byte pieces per row
+  if (cpr > 256) moe_dispatch<8>(p, sh, list, st0, st1);
+  else if (cpr > 128) moe_dispatch<4>(p, sh, list, st0, st1);
+  else if (cpr > 64) moe_dispatch<2>(p, sh, list, st0, st1);
+  else moe_dispatch<1>(p, sh, list, st0, st1);
 }
 
 // ------------------------------------------------------------------------------------------
 // compute role: ragged grouped GEMM
 // ------------------------------------------------------------------------------------------
-__device__ __forceinline__ void moe_compute_role(const MoeParams& p, int slot, char* st0, char* st1, char* st2, MoeShared& sh) {
+// Grouped-GEMM tiles: `first` (a static tile of this workgroup, or -1), then leftover tiles
+// n_compute, n_compute + 1, ... claimed from a shared counter by every workgroup that has finished
+// its own work (compute workgroups after their static tile, copy workgroups after the dispatch).
+__device__ __forceinline__ void moe_gemm_tiles(const MoeParams& p, MoeShared& sh, int first, char* st0, char* st1,
+                                               char* st2) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (tid == 0) sh.ok = spin_until_eq(&p.flags[0], p.epoch, p.timeout_ticks, p.status);
-  __syncthreads();
-  if (!sh.ok) return;
-  for (int i = tid; i <= p.n_local; i += 256) {
-    sh.seg_off[i] = (int)flag_load((const uint32_t*)p.seg_offsets + i);
-    sh.tile_base[i] = (int)flag_load(moe_misc(p) + 2 + i);
-  }
-  __syncthreads();
   MoeTile g;
   const int wm = wave / MoeTile::WN, wn = wave % MoeTile::WN;
   const int n_mt = sh.tile_base[p.n_local];
   const int n_tiles = n_mt * p.tiles_n;
   const int nk = p.hidden >> 6;
-  const int C = p.n_compute;
-  const int rs = ((C & 7) == 0) ? (slot & 7) * (C >> 3) + (slot >> 3) : slot;
   const uint32_t lda_b = (uint32_t)p.hidden * 2u, ldb_b = (uint32_t)p.ffn * 2u;
   g.init(wm, wn, lane, lda_b, ldb_b);
-  for (int t = rs; t < n_tiles; t += C) {
+  int t = first;
+  while (true) {
+    if (t < 0) {
+      if (tid == 0) sh.claim = p.n_compute + (int)atomic_add_agent(moe_misc(p) + MISC_TILE, 1u);
+      __syncthreads();
+      t = sh.claim;
+    }
+    if (t >= n_tiles) break;
     const int gm = t / p.tiles_n, tn = t - gm * p.tiles_n;
+    t = -1;
     int el = 0;
     while (el + 1 < p.n_local && sh.tile_base[el + 1] <= gm) ++el;
     const int mt = gm - sh.tile_base[el];
     const int row0 = sh.seg_off[el] + mt * MoeTile::BM;
     int rows_valid = min(MoeTile::BM, sh.seg_off[el + 1] - row0);
     rows_valid = min(rows_valid, p.capacity - row0);
-    if (rows_valid <= 0) continue;
+    if (rows_valid <= 0) {
+      __syncthreads();  // every thread has read sh.claim before the next claim rewrites it
+      continue;
+    }
     const int n0 = tn * MoeTile::BN;
     const int cols_valid = min(MoeTile::BN, p.ffn - n0);
     // wait until every row of this m-tile has landed
@@ -317,7 +481,7 @@ __device__ __forceinline__ void moe_compute_role(const MoeParams& p, int slot, c
       g.dma_b(b_col + rb, b_col_bytes - rb, ldb_b, dst, wave);
     };
     g.zero();
-    k_loop3(g, nk, st0, st1, st2, load_step, [](int) {});
+    k_loop(g, nk, st0, st1, st2, [](int) {}, load_step, [](int) {});
     g.epilogue(st0, st1, wm, wn, lane, wave, [&](int row, int col, f32x4 v) {
       if (row < rows_valid && col < cols_valid)
         *reinterpret_cast<f32x4*>(p.y + (size_t)(row0 + row) * p.ffn + (n0 + col)) = v;
@@ -326,14 +490,34 @@ __device__ __forceinline__ void moe_compute_role(const MoeParams& p, int slot, c
   }
 }
 
-__global__ __launch_bounds__(256, 1) void moe_kernel(MoeParams p) {
+__device__ __forceinline__ void moe_compute_role(const MoeParams& p, int slot, char* st0, char* st1, char* st2,
+                                                 MoeShared& sh) {
+  const int tid = threadIdx.x;
+  if (tid == 0) sh.ok = spin_until_eq(&p.flags[0], p.epoch, p.timeout_ticks, p.status);
+  __syncthreads();
+  if (!sh.ok) return;
+  moe_load_segments(p, sh);
+  __syncthreads();
+  // XCD-aware static tile: workgroup w runs on XCD w % 8, consecutive tiles (same expert and
+  // m-tile, so the same A rows) go to one XCD
+  const int C = p.n_compute;
+  const int rs = ((C & 7) == 0) ? (slot & 7) * (C >> 3) + (slot >> 3) : slot;
+  moe_gemm_tiles(p, sh, rs, st0, st1, st2);
+}
+
+static_assert(MoeTile::STAGE >= 65536 && MOE_THREADS == 512, "copy slots: 64 KiB stage buffers, 8 waves");
+
+__global__ __launch_bounds__(MOE_THREADS, 1) void moe_kernel(MoeParams p) {
   __shared__ __attribute__((aligned(16))) char st0[MoeTile::STAGE];
   __shared__ __attribute__((aligned(16))) char st1[MoeTile::STAGE];
-  __shared__ __attribute__((aligned(16))) char st2[MoeTile::STAGE];
+  __shared__ __attribute__((aligned(16))) char st2[k_stages<MoeTile>() == 3 ? MoeTile::STAGE : 16];
+  __shared__ int2 list[MOE_LIST];
   __shared__ MoeShared sh;
   const int wg = blockIdx.x;
-  if (wg < p.n_copy) moe_copy_role(p, wg, sh);
-  else if (wg - p.n_copy < p.n_compute) moe_compute_role(p, wg - p.n_copy, st0, st1, st2, sh);
+  if (wg < p.n_copy) {
+    moe_copy_role(p, wg, sh, list, st0, st1);
+    if (sh.ok) moe_gemm_tiles(p, sh, -1, st0, st1, st2);  // then help with leftover tiles
+  } else if (wg - p.n_copy < p.n_compute) moe_compute_role(p, wg - p.n_copy, st0, st1, st2, sh);
   // exit accounting: the last workgroup out re-zeroes the counters for the next call
   wait_mem();
   __syncthreads();
@@ -341,17 +525,19 @@ __global__ __launch_bounds__(256, 1) void moe_kernel(MoeParams p) {
   __syncthreads();
   if (sh.is_last) {
     const int n_mt_max = p.max_mtiles;
-    for (int i = threadIdx.x; i < n_mt_max; i += 256)
+    for (int i = threadIdx.x; i < n_mt_max; i += MOE_THREADS)
       __hip_atomic_store(p.counters + p.off_tile_cnt + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (threadIdx.x == 0) {
       __hip_atomic_store(moe_misc(p) + 0, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(moe_misc(p) + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(moe_misc(p) + MISC_CLAIM, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(moe_misc(p) + MISC_TILE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
 
 hipError_t launch_moe(const MoeParams& p, int grid, hipStream_t s) {
-  hipLaunchKernelGGL(moe_kernel, dim3(grid), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(moe_kernel, dim3(grid), dim3(MOE_THREADS), 0, s, p);
   return hipGetLastError();
 }
 

@@ -9,7 +9,7 @@
 //   mode 2  same addresses with ordinary loads: a diagnostic, not a guarantee -- the consumer's
 //           XCD may keep a stale L2 copy of a line another XCD rewrote, which is why no kernel
 //           re-reads an address that was rewritten within the launch.
-#include "../../include/mk.h"
+#include "mk.h"
 #include "mk_device.hpp"
 #include "mk_internal.h"
 

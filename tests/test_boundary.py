@@ -213,6 +213,8 @@ def test_plan_moe(hostlib):
     assert moe(hostlib, top_k=9, E=16)[0] == UNSUP
     assert moe(hostlib, eb=60)[0] == INVALID  # experts past n_experts
     assert moe(hostlib, t_local=100)[0] == UNSUP
+    assert moe(hostlib, hidden=4160)[0] == UNSUP  # token rows above 8 KiB
+    assert moe(hostlib, hidden=320)[0] == MK_OK
     assert moe(hostlib, E=66)[0] == UNSUP  # rows of logits must be 16-byte multiples
     assert moe(hostlib, logits=0x10004)[0] == UNSUP
     assert moe(hostlib, cap=-1)[0] == INVALID
