@@ -1,6 +1,6 @@
 """Benchmark of the fused AllGather+GEMM hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--no-cpu] [--only OP]
 
 Headline: fused AG+GEMM TFLOP/s on the column-parallel MLP up-projection share
 (W=8 emulated ranks, A shards 1024x4096 bf16 -> gathered M=8192, B 4096x1792 bf16,
@@ -9,9 +9,14 @@ the compute role consumes them.  One step = one mk_ag_gemm call; inputs are resi
 in HBM before timing starts.  Four copies of every buffer rotate between steps so
 consecutive calls never hit in the 256 MiB Infinity Cache.
 
-Secondary (same JSON line): the same kernel with every tile pre-resident (slowdown of
-the fused arrival), GEMM+ReduceScatter and GEMM+AllReduce (epilogue GB/s) and MoE
-dispatch + grouped GEMM, each timed with HIP events on the launch stream.
+Reported beside it (same JSON line): kernel-time percentiles; a traced call's phase spans
+(copy-phase GB/s, the shader clock the kernel actually ran at); the same kernel with every
+tile pre-resident (slowdown of the fused arrival); two comparators for context only (a vendor
+BLAS bf16 GEMM of the same shape, and "copy kernels, then the GEMM kernel" as separate
+launches); GEMM+ReduceScatter and GEMM+AllReduce (TFLOP/s and epilogue GB/s, resident and
+with landing); MoE dispatch + grouped GEMM (routed rows, phase spans, grouped-GEMM TFLOP/s
+over its compute span, dispatch GB/s).  Everything is timed with HIP events on the stream
+the kernels are launched on.
 
 cpu_baseline: the fp64 oracle of the same workload, timed on the host cores.
 """
@@ -20,6 +25,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import platform
 import sys
 import time
 
@@ -30,7 +36,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
+N_CU, MFMA_FLOP_PER_CLK_CU = 256, 4096  # bf16 dense: 256 CUs x 4096 flop/clk
 N_SETS = 4
+TRACE_UNTOUCHED = -1
 
 # HBM traffic of the AG+GEMM kernel comes from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) kept
 # in profiles/, each scaled by what the same counter reads for a plain copy of known size.  The
@@ -79,8 +87,8 @@ def parse():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default="",
-                    help="profiling: run only this op (ag, ag_resident, ag_identity, rs, ar, rs_emulated, ar_emulated, moe, "
-                         "copy)")
+                    help="profiling: run only this op (ag, ag_resident, ag_identity, rs, ar, rs_emulated, ar_emulated, "
+                         "moe, copy)")
     return ap.parse_args()
 
 
@@ -99,8 +107,9 @@ def _i32(x):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).cuda()
 
 
-def time_calls(fns, steps, warmup):
-    """Run fns[i % len(fns)] warmup + steps times; return (wall ms per step, mean kernel ms per launch)."""
+def time_stats(fns, steps, warmup) -> dict:
+    """Run fns[i % len(fns)] warmup + steps times.  Returns wall ms per step and the per-launch
+    kernel times (HIP events on the current stream, where the calls launch): mean, p10, p50, p90."""
     import torch
     for i in range(warmup):
         fns[i % len(fns)]()
@@ -113,12 +122,56 @@ def time_calls(fns, steps, warmup):
         ev[i][1].record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
-    kern = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    return wall, kern
+    k = np.array([a.elapsed_time(b) for a, b in ev])
+    return {"wall_ms": wall, "kernel_ms": float(k.mean()), "p10": float(np.percentile(k, 10)),
+            "p50": float(np.percentile(k, 50)), "p90": float(np.percentile(k, 90))}
+
+
+def time_calls(fns, steps, warmup):
+    t = time_stats(fns, steps, warmup)
+    return t["wall_ms"], t["kernel_ms"]
+
+
+# ------------------------------------------------------------------------------------------------
+# trace records (mk_opts.trace): 8 int64 per workgroup; wall-clock ticks are 100 MHz
+# ------------------------------------------------------------------------------------------------
+def new_trace(ctx):
+    import torch
+    return torch.full((ctx.grid * 8,), TRACE_UNTOUCHED, dtype=torch.int64, device="cuda")
+
+
+def trace_records(tr) -> np.ndarray:
+    r = tr.cpu().numpy().reshape(-1, 8)
+    return r[r[:, 0] != TRACE_UNTOUCHED]
+
+
+def us(ticks) -> float:
+    return float(ticks) / 100.0
+
+
+def clock_ghz(rec) -> float:
+    """Average shader clock over the workgroups' lifetimes: cycles / wall time."""
+    cyc = float((rec[:, 3] - rec[:, 1]).sum())
+    wall = float((rec[:, 2] - rec[:, 0]).sum())
+    return cyc / wall * 0.1 if wall > 0 else float("nan")
+
+
+def traced_call(ctx, fn, opts):
+    """One untimed call with tracing on; returns its records."""
+    import torch
+    tr = new_trace(ctx)
+    opts.trace = tr
+    try:
+        fn()
+        torch.cuda.synchronize()
+    finally:
+        opts.trace = None
+    return trace_records(tr)
 
 
 # ------------------------------------------------------------------------------------------------
 def setup_ag(ctx, resident: bool, identity: bool = False):
+    """Four rotating buffer sets; returns (shape, calls, opts) with one Opts shared by the calls."""
     import torch
     import communication_gemm_role_amd as mk
     import workloads as wl
@@ -127,6 +180,10 @@ def setup_ag(ctx, resident: bool, identity: bool = False):
     order = _i32(wl.ag_arrival_order(s, trial=0))
     shards0 = [_bf16(x) for x in d["a_shards"]]
     b0 = _bf16(d["b"])
+    if resident:
+        opts = mk.Opts(arrival_mode=mk.MK_ARRIVAL_RESIDENT)
+    else:
+        opts = mk.Opts(arrival_mode=mk.MK_ARRIVAL_EMULATED, arrival_order=None if identity else order)
     calls = []
     for _ in range(N_SETS):
         shards = [x.clone() for x in shards0]
@@ -135,12 +192,53 @@ def setup_ag(ctx, resident: bool, identity: bool = False):
         c = torch.empty((s.m, s.n), dtype=torch.float32, device="cuda")
         if resident:
             ag.copy_(torch.cat(shards, 0))
-            opts = mk.Opts(arrival_mode=mk.MK_ARRIVAL_RESIDENT)
         else:
             ag[:s.m_shard].copy_(shards[0])
             shards[0] = ag[:s.m_shard]
-            opts = mk.Opts(arrival_mode=mk.MK_ARRIVAL_EMULATED, arrival_order=None if identity else order)
-        calls.append(lambda sh=shards, b=b, ag=ag, c=c, o=opts: mk.mk_ag_gemm(ctx, sh, s.world, 0, b, ag, c, opts=o))
+        calls.append(lambda sh=shards, b=b, ag=ag, c=c: mk.mk_ag_gemm(ctx, sh, s.world, 0, b, ag, c, opts=opts))
+    return s, calls, opts
+
+
+def setup_ag_two_launch(ctx):
+    """Comparator: the peer shards copied into the gathered A by separate copy kernels, then the
+    GEMM kernel on resident data (overlap only at kernel boundaries)."""
+    import torch
+    import communication_gemm_role_amd as mk
+    import workloads as wl
+    s = wl.AG_MLP
+    d = wl.gen_ag(s, run=0)
+    shards0 = [_bf16(x) for x in d["a_shards"]]
+    b0 = _bf16(d["b"])
+    opts = mk.Opts(arrival_mode=mk.MK_ARRIVAL_RESIDENT)
+    calls = []
+    for _ in range(N_SETS):
+        shards = [x.clone() for x in shards0]
+        b = b0.clone()
+        ag = torch.empty((s.m, s.k), dtype=torch.bfloat16, device="cuda")
+        ag[:s.m_shard].copy_(shards[0])
+        c = torch.empty((s.m, s.n), dtype=torch.float32, device="cuda")
+
+        def step(sh=shards, b=b, ag=ag, c=c):
+            for r in range(1, s.world):
+                ag[r * s.m_shard:(r + 1) * s.m_shard].copy_(sh[r])
+            mk.mk_ag_gemm(ctx, None, s.world, 0, b, ag, c, opts=opts)
+        calls.append(step)
+    return s, calls
+
+
+def setup_vendor_gemm():
+    """Comparator: torch.matmul (the vendor BLAS) on the same bf16 shape, bf16 output."""
+    import torch
+    import workloads as wl
+    s = wl.AG_MLP
+    d = wl.gen_ag(s, run=0)
+    a0 = torch.cat([_bf16(x) for x in d["a_shards"]], 0)
+    b0 = _bf16(d["b"])
+    calls = []
+    for _ in range(N_SETS):
+        a, b = a0.clone(), b0.clone()
+        out = torch.empty((s.m, s.n), dtype=torch.bfloat16, device="cuda")
+        calls.append(lambda a=a, b=b, out=out: torch.matmul(a, b, out=out))
     return s, calls
 
 
@@ -170,6 +268,15 @@ def setup_reduce(ctx, op: str, emulated: bool = False, n_reduce: int = 0):
     return s, calls
 
 
+def reduce_bytes(sh, op: str, emulated: bool):
+    """Algorithmic HBM bytes of one RS/AR call: (epilogue, total)."""
+    rows = sh.m_slice if op == "rs" else sh.m
+    peers = (sh.world - 1) * rows * sh.n * 4
+    epi = peers + rows * sh.n * 4 + ((sh.world - 1) * sh.m_slice * sh.n * 4 if op == "rs" else 0)
+    total = epi + sh.m * sh.k * 2 + sh.k * sh.n * 2 + (2 * peers if emulated else 0)
+    return epi, total
+
+
 def setup_moe(ctx):
     import torch
     import communication_gemm_role_amd as mk
@@ -180,6 +287,7 @@ def setup_moe(ctx):
     t0 = [_bf16(t) for t in d["tokens"]]
     lg0, bs0, w0 = _f32(d["logits"]), _f32(d["bias"]), _bf16(d["w_up"])
     calls, offsets = [], []
+    opts = mk.Opts(arrival_order=order)
     for _ in range(2):  # 2 sets: ~1 GiB each
         toks = [t.clone() for t in t0]
         lg, bs, w = lg0.clone(), bs0.clone(), w0.clone()
@@ -188,12 +296,32 @@ def setup_moe(ctx):
         segt = torch.empty((s.capacity,), dtype=torch.int32, device="cuda")
         x = torch.empty((s.capacity, s.hidden), dtype=torch.bfloat16, device="cuda")
         y = torch.empty((s.capacity, s.ffn), device="cuda")
-        o = mk.Opts(arrival_order=order)
         offsets.append(offs)
         calls.append(lambda toks=toks, lg=lg, bs=bs, w=w, topk=topk, offs=offs, segt=segt, x=x, y=y:
                      mk.mk_moe_dispatch_gemm(ctx, toks, lg, bs, s.top_k, s.expert_begin, w, topk, offs, segt, x, y,
-                                             opts=o))
-    return s, offsets, calls
+                                             opts=opts))
+    return s, offsets, calls, opts
+
+
+def cpu_info() -> dict:
+    model = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas, threads = "unknown", None
+    try:
+        from threadpoolctl import threadpool_info
+        info = [x for x in threadpool_info() if x.get("user_api") == "blas"]
+        if info:
+            blas, threads = info[0].get("internal_api", "unknown"), int(info[0]["num_threads"])
+    except Exception:
+        pass
+    return {"cpu": model, "affinity_cores": len(os.sched_getaffinity(0)), "blas": blas, "blas_threads": threads}
 
 
 def cpu_baseline(budget_s: float = 12.0):
@@ -202,14 +330,8 @@ def cpu_baseline(budget_s: float = 12.0):
     import workloads as wl
     s = wl.AG_MLP
     d = wl.gen_ag(s, run=0)
-    threads = os.cpu_count()
-    try:
-        from threadpoolctl import threadpool_info
-        info = [x for x in threadpool_info() if x.get("user_api") == "blas"]
-        if info:
-            threads = int(info[0]["num_threads"])
-    except Exception:
-        pass
+    ci = cpu_info()
+    threads = ci["blas_threads"] or ci["affinity_cores"]
     reps, t_total = 0, 0.0
     while t_total < budget_s and reps < 1000:
         t0 = time.perf_counter()
@@ -218,8 +340,44 @@ def cpu_baseline(budget_s: float = 12.0):
         reps += 1
     t = t_total / reps
     return {"value": s.flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"full AG+GEMM workload (W=8, M=8192, N=1792, K=4096) in fp64, {reps} repetitions, "
-                      f"{t:.2f} s each"}
+            "sample": f"full AG+GEMM workload (W=8, M=8192, N=1792, K=4096) in fp64 NumPy matmul, {reps} "
+                      f"repetitions, {t:.2f} s each; the oracle computes in fp64 while the GPU uses bf16 MFMA, "
+                      "so the ratio is context, not a like-for-like speed claim",
+            "host": ci}
+
+
+def ag_trace_summary(rec, s) -> dict:
+    t0 = rec[:, 0].min()
+    cp, co = rec[rec[:, 4] == 0], rec[rec[:, 4] == 1]
+    out = {"kernel_span_us": round(us(rec[:, 2].max() - t0), 2), "shader_clock_GHz": round(clock_ghz(co), 3)}
+    if len(cp):
+        copy_end = cp[:, 5].max()
+        copy_bytes = 2 * (s.world - 1) * s.m_shard * s.k * 2
+        out["copy_span_us"] = round(us(copy_end - t0), 2)
+        out["copy_GBs"] = round(copy_bytes / (us(copy_end - t0) * 1e-6) / 1e9, 1)
+    ready = co[co[:, 5] > 0, 5]
+    if len(ready):
+        out["first_operands_ready_us"] = {"min": round(us(ready.min() - t0), 2),
+                                          "median": round(us(np.median(ready) - t0), 2),
+                                          "max": round(us(ready.max() - t0), 2)}
+    return out
+
+
+def moe_trace_summary(rec, s, R) -> dict:
+    t0 = rec[:, 0].min()
+    cp, co = rec[rec[:, 4] == 0], rec[rec[:, 4] == 1]
+    route_end, scan_seen, disp_end = cp[:, 5].max(), cp[:, 6].min(), cp[:, 7].max()
+    ready = co[co[:, 5] > 0, 5]
+    end = rec[:, 2].max()
+    out = {"kernel_span_us": round(us(end - t0), 2), "routing_done_us": round(us(route_end - t0), 2),
+           "scan_seen_us": round(us(scan_seen - t0), 2), "dispatch_done_us": round(us(disp_end - t0), 2),
+           "dispatch_GBs": round(16384 * R / (us(disp_end - scan_seen) * 1e-6) / 1e9, 1),
+           "shader_clock_GHz": round(clock_ghz(rec), 3)}
+    if len(ready):
+        span = us(end - ready.min())
+        out["gemm_span_us"] = round(span, 2)
+        out["gemm_tflops_over_span"] = round(s.flops(R) / (span * 1e-6) / 1e12, 1)
+    return out
 
 
 def main():
@@ -234,13 +392,13 @@ def main():
 
     if a.only:
         if a.only in ("ag", "ag_resident", "ag_identity"):
-            _, calls = setup_ag(ctx, a.only == "ag_resident", identity=a.only == "ag_identity")
+            _, calls, _ = setup_ag(ctx, a.only == "ag_resident", identity=a.only == "ag_identity")
         elif a.only in ("rs", "ar"):
             _, calls = setup_reduce(ctx, a.only)
         elif a.only in ("rs_emulated", "ar_emulated"):
             _, calls = setup_reduce(ctx, a.only[:2], emulated=True)
         elif a.only == "moe":
-            _, _, calls = setup_moe(ctx)
+            _, _, calls, _ = setup_moe(ctx)
         elif a.only == "copy":
             # calibration for the HBM byte counters: a plain device copy of 256 MiB per launch
             src = torch.empty(64 << 20, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -248,18 +406,23 @@ def main():
             calls = [lambda: dst.copy_(src)]
         else:
             raise SystemExit(f"unknown --only {a.only}")
-        wall, kern = time_calls(calls, a.steps, a.warmup)
+        t = time_stats(calls, a.steps, a.warmup)
         st = ctx.status()
-        print(json.dumps({"only": a.only, "ms_per_step": wall, "kernel_ms": kern, "status": st}), flush=True)
+        print(json.dumps({"only": a.only, "ms_per_step": t["wall_ms"], "kernel_ms": t["kernel_ms"], "status": st}),
+              flush=True)
         return
 
-    s, calls = setup_ag(ctx, resident=False)
-    wall, kern = time_calls(calls, a.steps, a.warmup)
+    s, calls, opts = setup_ag(ctx, resident=False)
+    t = time_stats(calls, a.steps, a.warmup)
     status = ctx.status()
     if status != mk.MK_OK:
         raise SystemExit(f"device status {status}: {mk.strerror(status)}")
-    value = s.flops / (wall * 1e-3) / 1e12
-    achieved = s.flops / (kern * 1e-3) / 1e12
+    rec = traced_call(ctx, calls[0], opts)
+    tr = ag_trace_summary(rec, s)
+    value = s.flops / (t["wall_ms"] * 1e-3) / 1e12
+    achieved = s.flops / (t["kernel_ms"] * 1e-3) / 1e12
+    clk = tr["shader_clock_GHz"]
+    peak_clk = N_CU * MFMA_FLOP_PER_CLK_CU * clk * 1e9 / 1e12
     result = {
         "metric": "fused AG+GEMM TFLOP/s on 1 MI355X and % of bf16 MFMA peak; RS/AR epilogue GB/s",
         "value": round(value, 2),
@@ -267,7 +430,7 @@ def main():
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
-        "ms_per_step": round(wall, 5),
+        "ms_per_step": round(t["wall_ms"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -278,35 +441,60 @@ def main():
                                "in a seeded random order", "arrival": "emulated", "sets_rotated": N_SETS},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": ag_algorithmic_bytes(s)},
+                     "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": ag_algorithmic_bytes(s),
+                     "measured_clock_GHz": clk, "peak_at_measured_clock": round(peak_clk, 1),
+                     "frac_at_measured_clock": round(achieved / peak_clk, 4) if peak_clk > 0 else None},
+        "kernel_ms": {k: round(v, 5) for k, v in t.items() if k != "wall_ms"},
+        "trace": tr,
+        "env": {"gpu": torch.cuda.get_device_name(0), "hip": torch.version.hip, "torch": torch.__version__},
     }
     traffic = measured_traffic()
     if traffic is not None:
         result["roofline"]["traffic"] = round(traffic)
+    del calls
     if not a.no_secondary:
         sec = {}
-        _, calls_r = setup_ag(ctx, resident=True)
-        w_r, k_r = time_calls(calls_r, 30, 3)
-        sec["ag_resident"] = {"kernel_ms": round(k_r, 5), "tflops": round(s.flops / (k_r * 1e-3) / 1e12, 2),
-                              "fused_slowdown": round(kern / k_r - 1.0, 4)}
+        _, calls_r, _ = setup_ag(ctx, resident=True)
+        tr_ = time_stats(calls_r, 30, 3)
+        sec["ag_resident"] = {"kernel_ms": round(tr_["kernel_ms"], 5),
+                              "tflops": round(s.flops / (tr_["kernel_ms"] * 1e-3) / 1e12, 2),
+                              "fused_slowdown": round(t["kernel_ms"] / tr_["kernel_ms"] - 1.0, 4)}
         del calls_r
+        _, calls_2 = setup_ag_two_launch(ctx)
+        t2 = time_stats(calls_2, 30, 3)
+        sec["ag_copy_then_gemm"] = {"ms_per_step": round(t2["kernel_ms"], 5),
+                                    "tflops": round(s.flops / (t2["kernel_ms"] * 1e-3) / 1e12, 2),
+                                    "note": "comparator: 7 copy kernels then the GEMM kernel, separate launches"}
+        del calls_2
+        _, calls_v = setup_vendor_gemm()
+        tv = time_stats(calls_v, 30, 3)
+        sec["vendor_gemm"] = {"kernel_ms": round(tv["kernel_ms"], 5),
+                              "tflops": round(s.flops / (tv["kernel_ms"] * 1e-3) / 1e12, 2),
+                              "note": "comparator: torch.matmul bf16 -> bf16 on the gathered shape, operands resident"}
+        del calls_v
+        torch.cuda.empty_cache()
         for op in ("rs", "ar"):
-            sh, cr = setup_reduce(ctx, op)
-            w_, k_ = time_calls(cr, 30, 3)
-            rows = sh.m_slice if op == "rs" else sh.m
-            epi = (sh.world - 1) * rows * sh.n * 4 + rows * sh.n * 4 + (
-                (sh.world - 1) * sh.m_slice * sh.n * 4 if op == "rs" else 0)
-            total = epi + sh.m * sh.k * 2 + sh.k * sh.n * 2
-            sec[op] = {"kernel_ms": round(k_, 5), "tflops": round(sh.flops / (k_ * 1e-3) / 1e12, 2),
-                       "epilogue_GBs": round(epi / (k_ * 1e-3) / 1e9, 1),
-                       "total_GBs": round(total / (k_ * 1e-3) / 1e9, 1),
-                       "hbm_frac": round(total / (k_ * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-            del cr
-            torch.cuda.empty_cache()
-        sm, offs, cm = setup_moe(ctx)
-        w_, k_ = time_calls(cm, 20, 2)
-        R = int(offs[0][-1].item())  # routed rows, as the kernel computed them
-        sec["moe"] = {"kernel_ms": round(k_, 5), "routed_rows": R, "tflops": round(sm.flops(R) / (k_ * 1e-3) / 1e12, 2)}
+            for emulated in (False, True):
+                sh, cr = setup_reduce(ctx, op, emulated=emulated)
+                tt = time_stats(cr, 30, 3)
+                k_ = tt["kernel_ms"]
+                epi, total = reduce_bytes(sh, op, emulated)
+                sec[op + ("_landing" if emulated else "")] = {
+                    "kernel_ms": round(k_, 5), "tflops": round(sh.flops / (k_ * 1e-3) / 1e12, 2),
+                    "epilogue_GBs": round(epi / (k_ * 1e-3) / 1e9, 1),
+                    "total_GBs": round(total / (k_ * 1e-3) / 1e9, 1),
+                    "hbm_frac": round(total / (k_ * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+                del cr
+                torch.cuda.empty_cache()
+        sm, offs, cm, mopts = setup_moe(ctx)
+        tm = time_stats(cm, 20, 2)
+        o = offs[0].cpu().numpy()
+        R = int(o[-1])
+        mrec = traced_call(ctx, cm[0], mopts)
+        sec["moe"] = {"kernel_ms": round(tm["kernel_ms"], 5), "routed_rows": R,
+                      "rows_per_expert": np.diff(o).tolist(),
+                      "tflops": round(sm.flops(R) / (tm["kernel_ms"] * 1e-3) / 1e12, 2),
+                      "trace": moe_trace_summary(mrec, sm, R)}
         del cm
         st = ctx.status()
         if st != mk.MK_OK:

@@ -52,12 +52,15 @@ class mk_opts(ctypes.Structure):
         ("arrival_chunk_tokens", ctypes.c_int),
         ("timeout_us", ctypes.c_int64),
         ("test_drop_unit", ctypes.c_int),
+        ("trace", ctypes.c_void_p),
     ]
 
 
 @dataclass
 class Opts:
-    """Python-side mk_opts; ``arrival_order`` is an int32 CUDA tensor (or None)."""
+    """Python-side mk_opts; ``arrival_order`` is an int32 CUDA tensor (or None); ``trace`` is an
+    int64 CUDA tensor of at least ``ctx.grid * 8`` elements (or None), filled with one 8-slot
+    record per workgroup as documented for ``mk_opts.trace`` (see ``trace_records``)."""
     n_copy_wg: int = 0
     n_compute_wg: int = 0
     n_reduce_wg: int = 0
@@ -68,6 +71,7 @@ class Opts:
     arrival_chunk_tokens: int = 0
     timeout_us: int = 0
     test_drop_unit: int = 0
+    trace: object = None
 
     def to_c(self) -> mk_opts:
         o = mk_opts()
@@ -85,6 +89,9 @@ class Opts:
         o.arrival_chunk_tokens = self.arrival_chunk_tokens
         o.timeout_us = self.timeout_us
         o.test_drop_unit = self.test_drop_unit
+        if self.trace is not None:
+            _check(self.trace, "int64", "trace")
+            o.trace = self.trace.data_ptr()
         return o
 
 
@@ -127,7 +134,7 @@ def strerror(code: int) -> str:
 
 def _check(t, dtype: str, name: str):
     import torch
-    want = {"bf16": torch.bfloat16, "f32": torch.float32, "int32": torch.int32}[dtype]
+    want = {"bf16": torch.bfloat16, "f32": torch.float32, "int32": torch.int32, "int64": torch.int64}[dtype]
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != want:
@@ -156,9 +163,11 @@ def _ptr_array(ts: Sequence, dtype: str, name: str, allow_none_at: Optional[int]
     return arr
 
 
-def _opts_ptr(opts: Optional[Opts]):
+def _opts_ptr(opts: Optional[Opts], ctx: "Context"):
     if opts is None:
         return None, None
+    if opts.trace is not None and opts.trace.numel() < ctx.grid * 8:
+        raise ValueError(f"trace needs {ctx.grid * 8} int64 elements (8 per workgroup), got {opts.trace.numel()}")
     o = opts.to_c()
     return ctypes.byref(o), o
 
@@ -225,7 +234,7 @@ def mk_ag_gemm(ctx: Context, a_shards: Sequence, world: int, rank: int, b, a_gat
     if a_gathered.shape[1] != k or c.shape != (m, n) or m % world:
         raise ValueError("shape mismatch")
     shards = _ptr_array(a_shards, "bf16", "a_shards") if a_shards is not None else None
-    op, _keep = _opts_ptr(opts)
+    op, _keep = _opts_ptr(opts, ctx)
     _call(lib().mk_ag_gemm(ctx.handle, _stream_ptr(stream), shards, world, rank, m // world, k, b.data_ptr(), n,
                            a_gathered.data_ptr(), c.data_ptr(), op), "mk_ag_gemm")
 
@@ -241,7 +250,7 @@ def mk_gemm_rs(ctx: Context, a, b, world: int, rank: int, peer_partials: Sequenc
     n = b.shape[1]
     peers = _ptr_array(peer_partials, "f32", "peer_partials")
     ob = _ptr_array(outbox, "f32", "outbox")
-    op, _keep = _opts_ptr(opts)
+    op, _keep = _opts_ptr(opts, ctx)
     _call(lib().mk_gemm_rs(ctx.handle, _stream_ptr(stream), a.data_ptr(), b.data_ptr(), m, n, k, world, rank, peers,
                            owned_out.data_ptr(), ob, op), "mk_gemm_rs")
 
@@ -256,7 +265,7 @@ def mk_gemm_ar(ctx: Context, a, b, world: int, rank: int, peer_partials: Sequenc
     m, k = a.shape
     n = b.shape[1]
     peers = _ptr_array(peer_partials, "f32", "peer_partials")
-    op, _keep = _opts_ptr(opts)
+    op, _keep = _opts_ptr(opts, ctx)
     _call(lib().mk_gemm_ar(ctx.handle, _stream_ptr(stream), a.data_ptr(), b.data_ptr(), m, n, k, world, rank, peers,
                            out.data_ptr(), op), "mk_gemm_ar")
 
@@ -281,7 +290,7 @@ def mk_moe_dispatch_gemm(ctx: Context, tokens: Sequence, logits, bias, top_k: in
     n_experts = logits.shape[1]
     cap = x_seg.shape[0]
     toks = _ptr_array(tokens, "bf16", "tokens")
-    op, _keep = _opts_ptr(opts)
+    op, _keep = _opts_ptr(opts, ctx)
     _call(lib().mk_moe_dispatch_gemm(ctx.handle, _stream_ptr(stream), toks, world, t_local, hidden, logits.data_ptr(),
                                      bias.data_ptr(), n_experts, top_k, expert_begin, n_local, w_up.data_ptr(), ffn,
                                      topk_idx.data_ptr(), seg_offsets.data_ptr(), seg_token.data_ptr(),

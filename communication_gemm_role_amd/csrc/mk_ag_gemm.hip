@@ -297,6 +297,7 @@ __device__ __forceinline__ void ag_compute_role(const AgParams& p, int slot, cha
       for (int j = 0; j < n_pre; ++j) bad |= __builtin_amdgcn_readfirstlane(s_sched[j]) < 0;
       if (bad) return;  // before any MFMA of this tile
     }
+    if (t == rs) trace_mark(p.trace, 5);
     // A failed wait (watchdog or another workgroup's fault) inside the K loop does not leave the
     // loop: the remaining steps drain on K-unit 0 (in bounds, result discarded) and the tile's
     // stores are skipped.  Keeping the loop single-exit keeps the accumulators in AGPRs.
@@ -348,11 +349,15 @@ __global__ __launch_bounds__(AG_THREADS, 1) void ag_gemm_kernel(AgParams p) {
   __shared__ uint64_t s_done;
   const int wg = blockIdx.x;
   if (wg < p.n_copy) {
+    trace_begin(p.trace, ROLE_COPY);
     ag_copy_role(p, wg, st0, st1);
-    return;
+    trace_mark(p.trace, 5);
+  } else {
+    trace_begin(p.trace, ROLE_COMPUTE);
+    const int slot = wg - p.n_copy;
+    if (slot < p.n_compute) ag_compute_role(p, slot, st0, st1, st2, s_sched, &s_done);
   }
-  const int slot = wg - p.n_copy;
-  if (slot < p.n_compute) ag_compute_role(p, slot, st0, st1, st2, s_sched, &s_done);
+  trace_end(p.trace);
 }
 
 hipError_t launch_ag_gemm(const AgParams& p, int grid, hipStream_t s) {

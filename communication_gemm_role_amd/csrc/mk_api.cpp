@@ -209,6 +209,7 @@ int mk_ag_gemm(mk_ctx* ctx, void* stream, const uint16_t* const* a_shards, int w
   p.tiles_n = P.tiles_n;
   p.epoch = ctx->epoch;
   p.timeout_ticks = timeout_ticks(opts);
+  p.trace = opts ? opts->trace : nullptr;
   return mk::launch_ag_gemm(p, P.n_copy + P.n_compute, s) == hipSuccess ? MK_OK : MK_ERR_HIP;
 }
 
@@ -264,6 +265,7 @@ static int gemm_reduce(int is_rs, mk_ctx* ctx, void* stream, const uint16_t* a, 
   p.own_tile_end = P.own_tile_end;
   p.epoch = ctx->epoch;
   p.timeout_ticks = timeout_ticks(opts);
+  p.trace = opts ? opts->trace : nullptr;
   return mk::launch_gemm_reduce(p, P.n_copy + P.n_reduce + P.n_compute, s) == hipSuccess ? MK_OK : MK_ERR_HIP;
 }
 
@@ -329,6 +331,7 @@ int mk_moe_dispatch_gemm(mk_ctx* ctx, void* stream, const uint16_t* const* token
   p.max_mtiles = P.max_mtiles;
   p.epoch = ctx->epoch;
   p.timeout_ticks = timeout_ticks(opts);
+  p.trace = opts ? opts->trace : nullptr;
   p.off_chunk_cnt = P.off_chunk_cnt;
   p.off_tile_cnt = P.off_tile_cnt;
   p.off_misc = P.off_misc;

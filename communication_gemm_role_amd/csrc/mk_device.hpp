@@ -80,6 +80,30 @@ __device__ __forceinline__ uint32_t flag_load(const uint32_t* f) {
   return __hip_atomic_load(const_cast<uint32_t*>(f), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Per-workgroup trace record (8 uint64 per workgroup, slots as documented for mk_opts.trace),
+// written by thread 0 with ordinary vector stores when the caller asked for one.
+__device__ __forceinline__ void trace_put(uint64_t* tr, int slot, uint64_t v) {
+  if (tr && threadIdx.x == 0) tr[(size_t)blockIdx.x * 8 + slot] = v;
+}
+__device__ __forceinline__ void trace_mark(uint64_t* tr, int slot) { trace_put(tr, slot, wall_ticks()); }
+__device__ __forceinline__ void trace_begin(uint64_t* tr, int role) {
+  if (tr && threadIdx.x == 0) {
+    uint64_t* r = tr + (size_t)blockIdx.x * 8;
+    r[0] = wall_ticks();
+    r[1] = __builtin_readcyclecounter();
+    r[4] = (uint64_t)role;
+    r[5] = r[6] = r[7] = 0;
+  }
+}
+__device__ __forceinline__ void trace_end(uint64_t* tr) {
+  if (tr && threadIdx.x == 0) {
+    uint64_t* r = tr + (size_t)blockIdx.x * 8;
+    r[2] = wall_ticks();
+    r[3] = __builtin_readcyclecounter();
+  }
+}
+constexpr int ROLE_COPY = 0, ROLE_COMPUTE = 1, ROLE_REDUCE = 2;
+
 // Workgroup barrier without the memory fence of __syncthreads.  The fence of a workgroup-scope
 // release makes the compiler wait for every outstanding vector-memory operation, stores included,
 // which would drain a copy pipeline at each barrier.  Callers order memory themselves with explicit

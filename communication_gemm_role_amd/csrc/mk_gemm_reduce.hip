@@ -211,6 +211,7 @@ __device__ __forceinline__ void red_compute_role(const RedParams& p, int slot, c
       g.dma_b(b_col + rb, b_col_bytes - rb, ldb_b, dst, wave);
     };
     g.zero();
+    if (t == rs) trace_mark(p.trace, 5);  // operands are resident: ready at once
     k_loop(g, nk, st0, st1, st2, [](int) {}, load_step, [](int) {});
 
     int lr0, lr1;
@@ -264,15 +265,19 @@ __global__ __launch_bounds__(T::NW * 64, 1) void gemm_reduce_kernel(RedParams p)
   __shared__ int s_ok;
   const int wg = blockIdx.x;
   if (wg < p.n_copy) {
+    trace_begin(p.trace, ROLE_COPY);
     red_copy_role<T::NW * 64>(p, wg);
-    return;
-  }
-  if (wg < p.n_copy + p.n_reduce) {
+    trace_mark(p.trace, 5);
+  } else if (wg < p.n_copy + p.n_reduce) {
+    trace_begin(p.trace, ROLE_REDUCE);
     red_reduce_role<T>(p, wg - p.n_copy, &s_ok);
-    return;
+    trace_mark(p.trace, 5);
+  } else {
+    trace_begin(p.trace, ROLE_COMPUTE);
+    const int slot = wg - p.n_copy - p.n_reduce;
+    if (slot < p.n_compute) red_compute_role<T>(p, slot, st0, st1, st2, &s_ok);
   }
-  const int slot = wg - p.n_copy - p.n_reduce;
-  if (slot < p.n_compute) red_compute_role<T>(p, slot, st0, st1, st2, &s_ok);
+  trace_end(p.trace);
 }
 
 template <class T>

@@ -39,6 +39,7 @@ struct AgParams {
   int tiles_m, tiles_n;
   uint32_t epoch;
   uint64_t timeout_ticks;
+  uint64_t* trace;  // per-workgroup trace records, or nullptr
 };
 
 struct RedParams {
@@ -62,6 +63,7 @@ struct RedParams {
   int own_tile_begin, own_tile_end;  // tile rows overlapping the owned slice (RS) or all (AR)
   uint32_t epoch;
   uint64_t timeout_ticks;
+  uint64_t* trace;  // per-workgroup trace records, or nullptr
 };
 
 struct MoeParams {
@@ -85,6 +87,7 @@ struct MoeParams {
   int tiles_n, max_mtiles;         // grouped-GEMM tiling: n-tiles per expert, bound on m-tiles
   uint32_t epoch;
   uint64_t timeout_ticks;
+  uint64_t* trace;  // per-workgroup trace records, or nullptr
   // counter layout (offsets into `counters`)
   int off_chunk_cnt;   // [n_chunks * n_local] per-chunk routed counts
   int off_tile_cnt;    // [max_mtiles] rows landed per global m-tile

@@ -411,6 +411,7 @@ __device__ __forceinline__ void moe_copy_role(const MoeParams& p, int cid, MoeSh
   }
   wait_mem();
   __syncthreads();
+  trace_mark(p.trace, 5);
   if (tid == 0) sh.is_last = atomic_add_agent(moe_misc(p) + 0, 1u) == (uint32_t)(p.n_copy - 1);
   __syncthreads();
   if (sh.is_last) moe_scan(p, sh);
@@ -418,6 +419,7 @@ __device__ __forceinline__ void moe_copy_role(const MoeParams& p, int cid, MoeSh
   if (tid == 0) sh.ok = spin_until_eq(&p.flags[0], p.epoch, p.timeout_ticks, p.status);
   __syncthreads();
   if (!sh.ok) return;
+  trace_mark(p.trace, 6);
   moe_load_segments(p, sh);
   __syncthreads();
   // DMA instructions per row and wave, rounded up to a power of two (8 for hidden 4096)
@@ -445,6 +447,7 @@ __device__ __forceinline__ void moe_gemm_tiles(const MoeParams& p, MoeShared& sh
   const uint32_t lda_b = (uint32_t)p.hidden * 2u, ldb_b = (uint32_t)p.ffn * 2u;
   g.init(wm, wn, lane, lda_b, ldb_b);
   int t = first;
+  bool traced = false;
   while (true) {
     if (t < 0) {
       if (tid == 0) sh.claim = p.n_compute + (int)atomic_add_agent(moe_misc(p) + MISC_TILE, 1u);
@@ -471,6 +474,8 @@ __device__ __forceinline__ void moe_gemm_tiles(const MoeParams& p, MoeShared& sh
       sh.ok = spin_until_ge(p.counters + p.off_tile_cnt + gm, (uint32_t)rows_valid, p.timeout_ticks, p.status);
     __syncthreads();
     if (!sh.ok) return;
+    if (first >= 0 && !traced) trace_mark(p.trace, 5);  // a compute workgroup's static tile is ready
+    traced = true;
     const char* a_tile = reinterpret_cast<const char*>(p.x_seg + (size_t)row0 * p.hidden);
     const uint32_t a_tile_bytes = (uint32_t)rows_valid * lda_b;
     const char* b_col = reinterpret_cast<const char*>(p.w_up + (size_t)el * p.hidden * p.ffn + n0);
@@ -515,9 +520,15 @@ __global__ __launch_bounds__(MOE_THREADS, 1) void moe_kernel(MoeParams p) {
   __shared__ MoeShared sh;
   const int wg = blockIdx.x;
   if (wg < p.n_copy) {
+    trace_begin(p.trace, ROLE_COPY);
     moe_copy_role(p, wg, sh, list, st0, st1);
+    trace_mark(p.trace, 7);
     if (sh.ok) moe_gemm_tiles(p, sh, -1, st0, st1, st2);  // then help with leftover tiles
-  } else if (wg - p.n_copy < p.n_compute) moe_compute_role(p, wg - p.n_copy, st0, st1, st2, sh);
+  } else {
+    trace_begin(p.trace, ROLE_COMPUTE);
+    if (wg - p.n_copy < p.n_compute) moe_compute_role(p, wg - p.n_copy, st0, st1, st2, sh);
+  }
+  trace_end(p.trace);
   // exit accounting: the last workgroup out re-zeroes the counters for the next call
   wait_mem();
   __syncthreads();

@@ -80,6 +80,22 @@ typedef struct mk_opts {
   int test_drop_unit; /* testing: position in arrival_order that the copy role skips, so the
                          consumer of that unit must time out (-1 or 0 = none; values are
                          1-based positions)                                                   */
+  uint64_t* trace;    /* DEVICE array of mk_ctx_grid(ctx) * 8 uint64, or NULL (no tracing).
+                         When set, thread 0 of every workgroup of the call writes its record
+                         i * 8 + [0..7] (i = workgroup id; workgroups the call does not launch
+                         are left untouched):
+                           [0] wall-clock ticks (100 MHz) at start  [1] shader cycles at start
+                           [2] wall-clock ticks at end             [3] shader cycles at end
+                           [4] role: 0 copy, 1 compute, 2 reduce
+                           [5] [6] [7] phase marks in wall-clock ticks, 0 when not reached:
+                             AG, RS/AR copy: [5] its last unit's flag raised
+                             AG, RS/AR compute: [5] first tile's first operands ready
+                             RS/AR reduce: [5] its last pre-sum flag raised
+                             MoE copy: [5] routing done, [6] scan flag seen, [7] its last
+                               dispatched rows counted (before it joins the leftover tiles)
+                             MoE compute: [5] first tile's rows all landed
+                         The caller owns the array; it must stay alive until the call's
+                         stream work completes.                                               */
 } mk_opts;
 
 /* ---- context ------------------------------------------------------------------------ */
