@@ -11,8 +11,10 @@
 //                                   arrival order, copy that unit of a peer shard into its
 //                                   rows of a_gathered (staged through LDS), then raise the
 //                                   unit's ready flag.
-//                                   Copy workgroups never wait, so they always finish.
-//   workgroups [n_copy, grid)       compute: 256 x 256 output tiles of C.  In emulated mode the
+//                                   Copy workgroups never wait while copying, so every unit lands.
+//   workgroups [n_copy, grid)       compute: 256 x 256 output tiles of C, one static tile per
+//                                   workgroup, then (like copy workgroups once they have copied)
+//                                   tiles left over past n_compute.  In emulated mode the
 //                                   K loop visits K-units (unit_cols columns of K) ready-first:
 //                                   wave 0 polls the flags of the tile's unit rows and picks the
 //                                   lowest-numbered K-unit that has fully landed, one unit ahead
@@ -242,8 +244,12 @@ __device__ __forceinline__ int ag_pick_polled(const AgParams& p, int ur0, int n_
   return u;
 }
 
+// Compute role.  Compute workgroup `slot` first runs its static tile (XCD-aware order); tiles from
+// n_compute on are left over and claimed from a shared counter by every workgroup that has
+// finished its own work: compute workgroups after their static tile, copy workgroups (slot -1)
+// after copying.
 __device__ __forceinline__ void ag_compute_role(const AgParams& p, int slot, char* st0, char* st1, char* st2,
-                                                int* s_sched, uint64_t* s_done) {
+                                                int* s_sched, uint64_t* s_done, int* s_claim) {
   AgTile g;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / AgTile::WN, wn = wave % AgTile::WN;
@@ -257,14 +263,22 @@ __device__ __forceinline__ void ag_compute_role(const AgParams& p, int slot, cha
   const int rs = ((C & 7) == 0) ? (slot & 7) * (C >> 3) + (slot >> 3) : slot;
   const uint32_t lda_b = (uint32_t)p.k * 2u, ldb_b = (uint32_t)p.n * 2u;
   g.init(wm, wn, lane, lda_b, ldb_b);
-  // K-units decided before the loop.  Step q+PD is prefetched during step q, and a decision taken
-  // at step q (after its MFMAs) names the unit after the one step q+PD starts; the first decision
-  // falls on the step whose prefetch starts unit ceil(PD/spu), so the prologue decides units
-  // 0 .. ceil(PD/spu).
+  // K-units decided before the loop.  Step q+PD is prefetched at the start of step q, so the unit
+  // that starts at step s must be known by the end of step s-PD-1: a decision taken at the end of
+  // step q (after its MFMAs) names the unit starting at step q+1+PD.  The prologue decides the
+  // units that start at steps 0 .. PD, i.e. ceil((PD+1)/spu) of them.
   constexpr int PD = k_stages<AgTile>() - 1;  // prefetch distance of the K loop
-  const int n_pre = min(n_ku, (PD + spu - 1) / spu + 1);
+  const int n_pre = min(n_ku, (PD + spu) / spu);
 
-  for (int t = rs; t < n_tiles; t += C) {
+  int t = (slot >= 0 && rs < n_tiles) ? rs : -1;
+  bool first = slot >= 0;
+  while (true) {
+    if (t < 0) {
+      if (tid == 0) *s_claim = C + (int)atomic_add_agent(p.counters + CTR_AG_TILE, 1u);
+      __syncthreads();
+      t = *s_claim;  // rewritten only after the next tile's barriers
+      if (t >= n_tiles) break;
+    }
     const int tm = t / p.tiles_n, tn = t - tm * p.tiles_n;
     const int m0 = tm * AgTile::BM, n0 = tn * AgTile::BN;
     const int rows_valid = min(AgTile::BM, p.m - m0), cols_valid = min(AgTile::BN, p.n - n0);
@@ -297,7 +311,8 @@ __device__ __forceinline__ void ag_compute_role(const AgParams& p, int slot, cha
       for (int j = 0; j < n_pre; ++j) bad |= __builtin_amdgcn_readfirstlane(s_sched[j]) < 0;
       if (bad) return;  // before any MFMA of this tile
     }
-    if (t == rs) trace_mark(p.trace, 5);
+    if (first) trace_mark(p.trace, 5);
+    first = false;
     // A failed wait (watchdog or another workgroup's fault) inside the K loop does not leave the
     // loop: the remaining steps drain on K-unit 0 (in bounds, result discarded) and the tile's
     // stores are skipped.  Keeping the loop single-exit keeps the accumulators in AGPRs.
@@ -311,11 +326,11 @@ __device__ __forceinline__ void ag_compute_role(const AgParams& p, int slot, cha
       aborted |= u < 0;
       return u < 0 ? 0 : u;
     };
-    // the unit decided at step q (when step q+PD starts a unit, the one after it), or -1
+    // the unit decided at the end of step q: the one that starts at step q+1+PD, or -1
     auto decided_at = [&](int q) -> int {
-      const int pf = q + PD;
-      if (!p.emulated || pf >= nk || pf % spu) return -1;
-      const int jn = pf / spu + 1;
+      const int s = q + 1 + PD;
+      if (!p.emulated || s >= nk || s % spu) return -1;
+      const int jn = s / spu;
       return (jn >= n_pre && jn < n_ku) ? jn : -1;
     };
     auto before_load = [&](int q) {
@@ -338,6 +353,7 @@ __device__ __forceinline__ void ag_compute_role(const AgParams& p, int slot, cha
     });
     __syncthreads();  // the next tile's prologue reuses the LDS
     if (aborted) break;
+    t = -1;
   }
 }
 
@@ -347,17 +363,27 @@ __global__ __launch_bounds__(AG_THREADS, 1) void ag_gemm_kernel(AgParams p) {
   __shared__ __attribute__((aligned(16))) char st2[k_stages<AgTile>() == 3 ? AgTile::STAGE : 16];
   __shared__ int s_sched[64];
   __shared__ uint64_t s_done;
+  __shared__ int s_claim;
   const int wg = blockIdx.x;
   if (wg < p.n_copy) {
     trace_begin(p.trace, ROLE_COPY);
     ag_copy_role(p, wg, st0, st1);
     trace_mark(p.trace, 5);
+    __syncthreads();  // the copy's LDS slots become the GEMM's stage buffers
+    ag_compute_role(p, -1, st0, st1, st2, s_sched, &s_done, &s_claim);  // then help with leftover tiles
   } else {
     trace_begin(p.trace, ROLE_COMPUTE);
     const int slot = wg - p.n_copy;
-    if (slot < p.n_compute) ag_compute_role(p, slot, st0, st1, st2, s_sched, &s_done);
+    if (slot < p.n_compute) ag_compute_role(p, slot, st0, st1, st2, s_sched, &s_done, &s_claim);
   }
   trace_end(p.trace);
+  // exit accounting: the last workgroup out re-zeroes the tile counter for the next call (every
+  // workgroup's last claim returned before it counts its exit)
+  __syncthreads();
+  if (threadIdx.x == 0 && atomic_add_agent(p.counters + CTR_AG_EXIT, 1u) == gridDim.x - 1) {
+    __hip_atomic_store(p.counters + CTR_AG_TILE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(p.counters + CTR_AG_EXIT, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 hipError_t launch_ag_gemm(const AgParams& p, int grid, hipStream_t s) {

@@ -210,6 +210,7 @@ int mk_ag_gemm(mk_ctx* ctx, void* stream, const uint16_t* const* a_shards, int w
   p.epoch = ctx->epoch;
   p.timeout_ticks = timeout_ticks(opts);
   p.trace = opts ? opts->trace : nullptr;
+  p.counters = ctx->counters;
   return mk::launch_ag_gemm(p, P.n_copy + P.n_compute, s) == hipSuccess ? MK_OK : MK_ERR_HIP;
 }
 

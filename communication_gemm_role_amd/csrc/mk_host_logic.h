@@ -110,7 +110,9 @@ inline int plan_ag(const Ws& ws, const Opts* o, const void* const* a_shards, int
     if (o && o->arrival_order && !aligned16(o->arrival_order) && ((uintptr_t)o->arrival_order & 3u)) return MK_ERR_UNSUPPORTED;
     P->drop_pos = (o && o->test_drop_unit > 0) ? o->test_drop_unit : 0;
   }
-  const int want_copy = P->emulated ? ((o && o->n_copy_wg) ? o->n_copy_wg : 32) : 0;
+  // copy workgroups take the tiles left over past the compute role once they have copied, so a
+  // large copy role lands the shards sooner without leaving tiles for a second round
+  const int want_copy = P->emulated ? ((o && o->n_copy_wg) ? o->n_copy_wg : 160) : 0;
   if (P->emulated && P->n_order > 0 && want_copy == 0) return MK_ERR_INVALID_ARG;
   int nr = 0;
   int code = split_roles(ws.grid, P->emulated ? want_copy : 0, 0, o ? o->n_compute_wg : 0, &P->n_copy, &nr, &P->n_compute);

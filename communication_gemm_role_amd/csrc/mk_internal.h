@@ -23,6 +23,11 @@ struct mk_ctx {
 
 namespace mk {
 
+// Context counters [0, 128) hold per-call bookkeeping, each left zero by the kernel that uses it:
+// MoE uses [0, 2+n_local] and [100, 101] (see mk_moe.hip); AllGather+GEMM uses [110, 111].
+constexpr int CTR_AG_TILE = 110;  // next leftover AG tile
+constexpr int CTR_AG_EXIT = 111;  // AG workgroups that have exited
+
 struct AgParams {
   const uint16_t* shards[MK_MAX_WORLD];
   const uint16_t* b;
@@ -30,6 +35,7 @@ struct AgParams {
   float* c;
   const int32_t* order;
   uint32_t* flags;
+  uint32_t* counters;  // context counters (CTR_AG_*)
   int* status;
   int world, rank, m_shard, m, n, k;
   int unit_rows, unit_cols, n_ucols, n_urows;

@@ -111,7 +111,8 @@ def test_plan_ag_full_workload(hostlib):
     assert p["n_order"] == 8 * 8 * 32 and p["local_in_place"] == 0  # shard 0 at another address: copied too
     code, p = ag(hostlib, shards="inplace")
     assert code == MK_OK and p["local_in_place"] == 1 and p["n_order"] == 7 * 8 * 32
-    assert (p["n_copy"], p["n_compute"], p["tiles_m"], p["tiles_n"]) == (32, 224, 32, 7)
+    # 160 copy workgroups (they take the tiles left over past the 96 static compute tiles)
+    assert (p["n_copy"], p["n_compute"], p["tiles_m"], p["tiles_n"]) == (160, 96, 32, 7)
     # resident: no copy role, and the compute role is cut to the 224 tiles (whole XCD rounds)
     code, p = ag(hostlib, shards="none", opts=Opts(arrival_mode=RESIDENT))
     assert code == MK_OK and (p["n_copy"], p["n_compute"]) == (0, 224)
