@@ -151,26 +151,31 @@ __device__ __forceinline__ void red_reduce_role(const RedParams& p, int rid, int
     const auto dst = make_rsrc(p.out + off, extent);
     const int total = rows * cpr;
     for (int base = 0; base < total; base += NT * 4) {
-      f32x4 s[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 1
-      for (int q = 0; q < p.world - 1; ++q) {
-        const auto src = make_rsrc(peer_src(p, q) + off, extent);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int c = base + tid + i * NT;
-          const int row = c / cpr, cc = c - row * cpr;
-          if (c < total && cc < ccols)
-            s[i] += __builtin_bit_cast(f32x4, bload16_nt(src, ((uint32_t)row * (uint32_t)p.n + (uint32_t)cc * 4u) * 4u));
-        }
-      }
+      // byte offsets of this thread's 4 chunks; a chunk outside the tile gets an offset past
+      // every window, so its loads read 0 and its store is dropped
+      uint32_t o[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int c = base + tid + i * NT;
         const int row = c / cpr, cc = c - row * cpr;
-        if (c < total && cc < ccols)
-          bstore16_sc1(dst, ((uint32_t)row * (uint32_t)p.n + (uint32_t)cc * 4u) * 4u, __builtin_bit_cast(u32x4, s[i]));
+        o[i] = (c < total && cc < ccols) ? ((uint32_t)row * (uint32_t)p.n + (uint32_t)cc * 4u) * 4u : 0xfffffff0u;
+      }
+      // every peer's loads first (up to 4 x 7 in flight), then the sums
+      f32x4 t[4][MK_MAX_WORLD - 1];
+#pragma unroll
+      for (int q = 0; q < MK_MAX_WORLD - 1; ++q) {
+        if (q >= p.world - 1) break;
+        const auto src = make_rsrc(peer_src(p, q) + off, extent);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t[i][q] = __builtin_bit_cast(f32x4, bload16_nt(src, o[i]));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < MK_MAX_WORLD - 1; ++q)
+          if (q < p.world - 1) s += t[i][q];
+        bstore16_sc1(dst, o[i], __builtin_bit_cast(u32x4, s));
       }
     }
     wait_mem();
@@ -234,24 +239,62 @@ __device__ __forceinline__ void red_compute_role(const RedParams& p, int slot, c
       if (!*s_ok) return;
     }
     const int own0 = p.is_rs ? p.rank * p.m_slice : 0;
-    g.epilogue(st0, st1, wm, wn, lane, wave, [&](int row, int col, f32x4 v) {
-      if (row >= rows_valid || col >= cols_valid) return;
-      const int grow = m0 + row, gcol = n0 + col;
+    // A 32-row slab lies inside one owner's slice (slices and valid row counts are multiples of
+    // 64 rows) and inside or outside the valid rows as a whole.  Every load a slab's reduction
+    // needs is issued before any of its adds, so the loads overlap instead of each waiting for
+    // the one before.
+    constexpr int Q = T::SLAB_Q;
+    g.epilogue_slab(st0, st1, wm, wn, lane, wave, [&](int srow, f32x4(&v)[Q], const int(&r)[Q], const int(&c)[Q]) {
+      if (srow >= rows_valid) return;
       if (p.is_rs) {
-        const int owner = grow / p.m_slice;
+        const int owner = (m0 + srow) / p.m_slice;
         if (owner != p.rank) {  // unreduced partial of another rank's slice -> its outbox
-          const int lrow = grow - owner * p.m_slice;
-          *reinterpret_cast<f32x4*>(p.outbox[owner] + (size_t)lrow * p.n + gcol) = v;
+          float* ob = p.outbox[owner] + (size_t)(m0 - owner * p.m_slice) * p.n + n0;
+#pragma unroll
+          for (int q = 0; q < Q; ++q)
+            if (c[q] < cols_valid) *reinterpret_cast<f32x4*>(ob + (size_t)r[q] * p.n + c[q]) = v[q];
           return;
         }
       }
-      const size_t o = (size_t)(grow - own0) * p.n + gcol;
+      const size_t base = (size_t)(m0 - own0) * p.n + n0;
       if (presum) {
-        v += *reinterpret_cast<const f32x4*>(p.out + o);
+        f32x4 t[Q];
+#pragma unroll
+        for (int q = 0; q < Q; ++q)
+          t[q] = c[q] < cols_valid ? *reinterpret_cast<const f32x4*>(p.out + base + (size_t)r[q] * p.n + c[q])
+                                   : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < Q; ++q)
+          if (c[q] < cols_valid) *reinterpret_cast<f32x4*>(p.out + base + (size_t)r[q] * p.n + c[q]) = v[q] + t[q];
       } else {
-        for (int q = 0; q < p.world - 1; ++q) v += *reinterpret_cast<const f32x4*>(peer_src(p, q) + o);
+        // values per group: G * (world - 1) loads in flight (one value with the eight-wave tile,
+        // whose accumulators leave less room)
+        constexpr int G = T::NW == 8 ? 1 : 2;
+        static_assert(Q % G == 0, "slab values split into whole groups");
+#pragma unroll
+        for (int g0 = 0; g0 < Q; g0 += G) {
+          f32x4 t[G][MK_MAX_WORLD - 1];
+#pragma unroll
+          for (int pq = 0; pq < MK_MAX_WORLD - 1; ++pq) {
+            if (pq >= p.world - 1) break;
+            const float* src = peer_src(p, pq) + base;
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi)
+              t[gi][pq] = c[g0 + gi] < cols_valid
+                              ? *reinterpret_cast<const f32x4*>(src + (size_t)r[g0 + gi] * p.n + c[g0 + gi])
+                              : f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+#pragma unroll
+          for (int gi = 0; gi < G; ++gi) {
+            f32x4 s = v[g0 + gi];
+#pragma unroll
+            for (int pq = 0; pq < MK_MAX_WORLD - 1; ++pq)
+              if (pq < p.world - 1) s += t[gi][pq];
+            if (c[g0 + gi] < cols_valid)
+              *reinterpret_cast<f32x4*>(p.out + base + (size_t)r[g0 + gi] * p.n + c[g0 + gi]) = s;
+          }
+        }
       }
-      *reinterpret_cast<f32x4*>(p.out + o) = v;
     });
     __syncthreads();  // the next tile's prologue reuses the LDS
   }

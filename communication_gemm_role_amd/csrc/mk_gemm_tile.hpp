@@ -363,6 +363,43 @@ struct TileGemmDma {
       __builtin_amdgcn_wave_barrier();
     }
   }
+
+  // As epilogue(), but hands `f` all of this lane's values of one 32-row slab at once, so an
+  // epilogue that loads other data per value (peer partials) can have all those loads in flight
+  // together: f(slab_row0, v, rows, cols) with SLAB_Q values; rows and cols are tile-relative and
+  // slab_row0 is the slab's first row.
+  static constexpr int SLAB_Q = (32 * (WTN / 4)) / 64;
+  template <class F>
+  __device__ __forceinline__ void epilogue_slab(char* st_lo, char* st_hi, int wm, int wn, int lane_in, int wave,
+                                                F&& f) {
+    int lane = lane_in;
+    asm volatile("" : "+v"(lane));
+    float* wl = reinterpret_cast<float*>((wave < NW / 2 ? st_lo : st_hi) + (wave % (NW / 2)) * EPI_WAVE);
+    constexpr int C4 = WTN / 4;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          wl[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * EPI_STRIDE + j * 32 + (lane & 31)] = acc[i][j][r];
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
+      f32x4 v[SLAB_Q];
+      int rows[SLAB_Q], cols[SLAB_Q];
+#pragma unroll
+      for (int q = 0; q < SLAB_Q; ++q) {
+        const int idx = q * 64 + lane;
+        const int row = idx / C4, c4 = idx - row * C4;
+        v[q] = *reinterpret_cast<const f32x4*>(wl + row * EPI_STRIDE + c4 * 4);
+        rows[q] = wm * WTM + i * 32 + row;
+        cols[q] = wn * WTN + c4 * 4;
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
+      f(wm * WTM + i * 32, v, rows, cols);
+    }
+  }
 };
 
 // s_waitcnt immediate that waits until at most `n` vector-memory operations of this wave are
