@@ -23,6 +23,7 @@
 // dispatched first; every wait is bounded by the watchdog.
 #include "mk_internal.h"
 #include "mk_gemm_tile.hpp"
+#include "mk_copy_ring.hpp"
 
 namespace mk {
 
@@ -45,28 +46,19 @@ __device__ __forceinline__ int ag_identity_unit(const AgParams& p, int pos) {
   return ur * p.n_ucols + uc;
 }
 
-// Every wave moves its own share of each unit global -> LDS (DMA) -> VGPRs -> global through two
-// 64 KiB batch slots (the stage buffers, idle in a copy workgroup): while one batch is stored, the
-// next is landing and the one after is requested, so up to 128 KiB of loads are in flight per CU
-// and no register holds data in flight.  A batch is 2 units of 128x128, 4 of 64x128 / 128x64 or 8
-// of 64x64; IPU is a unit's DMA instructions per wave (1 KiB each).  Stores are write-through;
-// a batch's flags are raised once every wave's stores of it have completed.  Slots past the end of
-// this workgroup's queue (and a dropped unit) use empty buffer windows, so every batch issues the
-// same instructions and the vmcnt arithmetic below holds: per batch and wave 8 DMA loads and 8
-// stores, completing in issue order.  The two slots are distinct LDS arrays named statically in an
-// unrolled loop, so the compiler can see that reads of one never alias the DMA into the other.
+// Units move through the two-slot LDS ring of mk_copy_ring.hpp (the stage buffers are idle in a
+// copy workgroup): 8 KiB per wave and batch, i.e. 2 units of 128x128, 4 of 64x128 / 128x64 or
+// 8 of 64x64.  IPU is a unit's DMA instructions per wave (1 KiB each).  The arrival order is read
+// through the constant address space, so its loads are scalar, off the vector-memory counter the
+// ring waits on.
 template <int IPU>
 __device__ __forceinline__ void ag_copy_dma(const AgParams& p, int cid, char* st0, char* st1) {
-  constexpr int UPB = 8 / IPU;  // units per batch
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int cpr = p.unit_cols >> 3;  // 16-byte chunks per unit row
   const uint32_t ldb = (uint32_t)p.k * 2u;
   const uint32_t extent = ((uint32_t)(p.unit_rows - 1) * (uint32_t)p.k + (uint32_t)p.unit_cols) * 2u;
   const int n_units = p.n_urows * p.n_ucols;
   const int n_mine = p.n_order > cid ? (p.n_order - cid + p.n_copy - 1) / p.n_copy : 0;
-  const int nb = (n_mine + UPB - 1) / UPB;
-  // The arrival order is constant for the launch: reading it through the constant address space
-  // makes the loads scalar, off the vector-memory counter the pipeline waits on.
   const __attribute__((address_space(4))) int32_t* order = (const __attribute__((address_space(4))) int32_t*)p.order;
   uint32_t off[IPU];  // byte offset inside a unit of this lane's chunk, per instruction of the unit
 #pragma unroll
@@ -94,57 +86,8 @@ __device__ __forceinline__ void ag_copy_dma(const AgParams& p, int cid, char* st
     const int ur = u / p.n_ucols, uc = u - ur * p.n_ucols;
     return make_rsrc(p.ag + (size_t)ur * p.unit_rows * p.k + (size_t)uc * p.unit_cols, extent);
   };
-  // this wave's 8 KiB of a slot: instruction q of the batch at +1 KiB * q, lane l at +16 B * l
-  auto dma = [&](int b, char* slot) {
-    char* base = slot + wave * 8192;
-#pragma unroll
-    for (int j = 0; j < UPB; ++j) {
-      const auto src = src_of(unit_at(b * UPB + j));
-#pragma unroll
-      for (int i = 0; i < IPU; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            src, (__attribute__((address_space(3))) void*)(base + (j * IPU + i) * 1024), 16, off[i], 0, 0, 0);
-    }
-  };
-  auto store = [&](int b, const char* slot) {
-    const char* base = slot + wave * 8192 + lane * 16;
-#pragma unroll
-    for (int j = 0; j < UPB; ++j) {
-      const auto dst = dst_of(unit_at(b * UPB + j));
-#pragma unroll
-      for (int i = 0; i < IPU; ++i)
-        bstore16_sc1(dst, off[i], *reinterpret_cast<const u32x4*>(base + (j * IPU + i) * 1024));
-    }
-  };
-  auto raise = [&](int b) {
-    if (tid == 0)
-      for (int j = 0; j < UPB; ++j) {
-        const int u = unit_at(b * UPB + j);
-        if (u >= 0) flag_store(&p.flags[u], p.epoch);
-      }
-  };
-  // Batch b has landed once no more than the instructions issued after its DMA are outstanding:
-  // the stores of b-1 and the DMA of b+1 (only the DMA of 1 for b = 0).  That also covers the
-  // stores of b-2, issued before the DMA of b, whose flags go up after the barrier.
-  auto step = [&](int b, char* slot) {
-    if (b >= nb) return;
-    if (b == 0) wait_vm<8>();
-    else wait_vm<16>();
-    barrier_only();  // the waits above order the stores; no LDS data crosses waves
-    if (b >= 2) raise(b - 2);
-    store(b, slot);
-    dma(b + 2, slot);  // this wave's LDS reads of the slot completed with the stores above
-  };
-  if (nb == 0) return;
-  dma(0, st0);
-  dma(1, st1);
-  for (int b = 0; b < nb; b += 2) {
-    step(b, st0);
-    step(b + 1, st1);
-  }
-  wait_vm<0>();
-  __syncthreads();
-  for (int b = nb > 2 ? nb - 2 : 0; b < nb; ++b) raise(b);
+  copy_ring<8, IPU>(n_mine, st0, st1, off, unit_at, src_of, dst_of,
+                    [&](int u) { flag_store(&p.flags[u], p.epoch); });
 }
 
 static_assert(AgTile::STAGE >= 65536 && AG_THREADS == 512, "copy slots: 64 KiB stage buffers, 8 waves");

@@ -11,7 +11,8 @@
 //
 // Roles, in workgroup-id order (each waits only on lower ids, which dispatch first):
 //   [0, n_copy)                 copy (emulated mode): lands peer-partial units in the inbox in
-//                               the caller's arrival order and raises each unit's flag.
+//                               the caller's arrival order and raises each unit's flag, then
+//                               joins the compute role on tiles left over past n_compute.
 //   [n_copy, n_copy+n_reduce)   reduce: for each owned tile, waits for its peer units, sums the
 //                               peer partials with coalesced 16-byte fp32 loads, writes the sum
 //                               into the output tile and raises the tile's pre-sum flag.
@@ -21,6 +22,7 @@
 //                               last so the reduce role has had the whole GEMM to pre-sum them.
 #include "mk_internal.h"
 #include "mk_gemm_tile.hpp"
+#include "mk_copy_ring.hpp"
 
 namespace mk {
 
@@ -30,6 +32,7 @@ using RedSkinny = TileGemmDma<128, 64, 4, 1>;  // few output rows (decode-like, 
 static inline bool red_skinny(int m, int n) { (void)n; return m <= 512; }
 int red_tile_m(int m, int n) { return red_skinny(m, n) ? RedSkinny::BM : RedBig::BM; }
 int red_tile_n(int m, int n) { return red_skinny(m, n) ? RedSkinny::BN : RedBig::BN; }
+int red_tile_waves(int m, int n) { return red_skinny(m, n) ? RedSkinny::NW : RedBig::NW; }
 
 // Peer partial q (0..world-2) is rank q < rank ? q : q + 1.
 __device__ __forceinline__ int peer_rank(int rank, int q) { return q < rank ? q : q + 1; }
@@ -42,46 +45,58 @@ __device__ __forceinline__ const float* peer_src(const RedParams& p, int q) {
 // ------------------------------------------------------------------------------------------
 // copy role (emulated landing of peer partials)
 // ------------------------------------------------------------------------------------------
-template <int NT>
-__device__ __forceinline__ void red_copy_role(const RedParams& p, int cid) {
-  const int tid = threadIdx.x;
-  const int cpr = p.unit_cols >> 2;             // 16-byte chunks per unit row (fp32)
-  const int per_t = (p.unit_rows * cpr) / NT;   // 1024 (64x64) .. 4096 (128x128) chunks over NT threads
-  const uint32_t ldb = (uint32_t)p.n * 4u;
+// Peer partials land in the inbox through the two-slot LDS ring of mk_copy_ring.hpp: 8 KiB per
+// wave and batch; IPU is a unit's DMA instructions per wave (a 64x64 fp32 unit is 16 KiB).
+template <class T, int IPU>
+__device__ __forceinline__ void red_copy_dma(const RedParams& p, int cid, char* st0, char* st1) {
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int cpr = p.unit_cols >> 2;  // 16-byte chunks per unit row (fp32)
+  const uint32_t ld = (uint32_t)p.n * 4u;
+  const uint32_t extent = ((uint32_t)(p.unit_rows - 1) * (uint32_t)p.n + (uint32_t)p.unit_cols) * 4u;
   const int n_units = (p.world - 1) * p.units_per_peer;
-  for (int pos = cid; pos < p.n_order; pos += p.n_copy) {
-    if (pos + 1 == p.drop_pos) continue;
-    const int u = p.order ? p.order[pos] : pos;
-    if (u < 0 || u >= n_units) continue;
+  const int n_mine = p.n_order > cid ? (p.n_order - cid + p.n_copy - 1) / p.n_copy : 0;
+  const __attribute__((address_space(4))) int32_t* order = (const __attribute__((address_space(4))) int32_t*)p.order;
+  uint32_t off[IPU];  // byte offset inside a unit of this lane's chunk, per instruction of the unit
+#pragma unroll
+  for (int i = 0; i < IPU; ++i) {
+    const int c = (wave * IPU + i) * 64 + lane;
+    const int row = c / cpr, cc = c - row * cpr;
+    off[i] = (uint32_t)row * ld + (uint32_t)cc * 16u;
+  }
+  auto unit_at = [&](int i) -> int {  // i-th unit of this workgroup's queue, or -1
+    if (i >= n_mine) return -1;
+    const int pos = cid + i * p.n_copy;
+    if (pos + 1 == p.drop_pos) return -1;  // testing: this unit never lands
+    const int u = order ? order[pos] : pos;
+    return (u < 0 || u >= n_units) ? -1 : u;
+  };
+  auto elem_of = [&](int u) -> size_t {  // first element of unit u inside a partial
     const int q = u / p.units_per_peer, w = u - q * p.units_per_peer;
     const int ur = w / p.n_ucols, uc = w - ur * p.n_ucols;
-    const size_t off = (size_t)ur * p.unit_rows * p.n + (size_t)uc * p.unit_cols;
-    const uint32_t extent = ((uint32_t)(p.unit_rows - 1) * (uint32_t)p.n + (uint32_t)p.unit_cols) * 4u;
-    const auto src = make_rsrc(p.peers[peer_rank(p.rank, q)] + off, extent);
-    const auto dst = make_rsrc(p.inbox + (size_t)q * p.p_rows * p.n + off, extent);
-#pragma unroll
-    for (int h = 0; h < 16; h += 8) {
-      if (h >= per_t) break;
-      u32x4 v[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (h + i < per_t) {
-          const int c = tid + (h + i) * NT;
-          const int row = c / cpr, cc = c - row * cpr;
-          v[i] = bload16_nt(src, (uint32_t)row * ldb + (uint32_t)cc * 16u);
-        }
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (h + i < per_t) {
-          const int c = tid + (h + i) * NT;
-          const int row = c / cpr, cc = c - row * cpr;
-          bstore16_sc1(dst, (uint32_t)row * ldb + (uint32_t)cc * 16u, v[i]);
-        }
-    }
-    wait_mem();
-    __syncthreads();
-    if (tid == 0) flag_store(&p.flags[u], p.epoch);
-  }
+    return (size_t)ur * p.unit_rows * p.n + (size_t)uc * p.unit_cols;
+  };
+  auto src_of = [&](int u) {
+    if (u < 0) return make_rsrc(p.inbox, 0u);
+    const int q = u / p.units_per_peer;
+    return make_rsrc(p.peers[peer_rank(p.rank, q)] + elem_of(u), extent);
+  };
+  auto dst_of = [&](int u) {
+    if (u < 0) return make_rsrc(p.inbox, 0u);
+    const int q = u / p.units_per_peer;
+    return make_rsrc(p.inbox + (size_t)q * p.p_rows * p.n + elem_of(u), extent);
+  };
+  copy_ring<8, IPU>(n_mine, st0, st1, off, unit_at, src_of, dst_of,
+                    [&](int u) { flag_store(&p.flags[u], p.epoch); });
+}
+
+template <class T>
+__device__ __forceinline__ void red_copy_role(const RedParams& p, int cid, char* st0, char* st1) {
+  // DMA instructions per wave per unit (the planner keeps them within 8)
+  const int ipu = (p.unit_rows * p.unit_cols * 4) / (T::NW * 64 * 16);
+  if (ipu >= 8) red_copy_dma<T, 8>(p, cid, st0, st1);
+  else if (ipu == 4) red_copy_dma<T, 4>(p, cid, st0, st1);
+  else if (ipu == 2) red_copy_dma<T, 2>(p, cid, st0, st1);
+  else red_copy_dma<T, 1>(p, cid, st0, st1);
 }
 
 // Rows of the owned region covered by tile row tm: [lr0, lr1) in partial coordinates
@@ -189,9 +204,15 @@ __device__ __forceinline__ void red_reduce_role(const RedParams& p, int rid, int
 // compute role
 // ------------------------------------------------------------------------------------------
 template <class T>
-__device__ __forceinline__ void red_compute_role(const RedParams& p, int slot, char* st0, char* st1, char* st2, int* s_ok) {
+// Compute role.  Compute workgroup `slot` first runs its static tile; tiles from n_compute on are
+// left over and claimed, in logical order (owned tiles last), from a shared counter by every
+// workgroup that has finished its own work: compute workgroups after their static tile, copy
+// workgroups (slot -1) after landing their units.
+__device__ __forceinline__ void red_compute_role(const RedParams& p, int slot, char* st0, char* st1, char* st2, int* s_ok,
+                                                 int* s_claim) {
   T g;
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / T::WN, wn = wave % T::WN;
   const int n_tiles = p.tiles_m * p.tiles_n;
   const int nk = p.k >> 6;
@@ -200,7 +221,15 @@ __device__ __forceinline__ void red_compute_role(const RedParams& p, int slot, c
   const uint32_t lda_b = (uint32_t)p.k * 2u, ldb_b = (uint32_t)p.n * 2u;
   g.init(wm, wn, lane, lda_b, ldb_b);
 
-  for (int t = rs; t < n_tiles; t += C) {
+  int t = (slot >= 0 && rs < n_tiles) ? rs : -1;
+  bool first = slot >= 0;
+  while (true) {
+    if (t < 0) {
+      if (tid == 0) *s_claim = C + (int)atomic_add_agent(p.counters + CTR_RED_TILE, 1u);
+      __syncthreads();
+      t = *s_claim;  // rewritten only after the next tile's barriers
+      if (t >= n_tiles) break;
+    }
     // logical tile rows start right after the owned rows, so owned tiles come last
     const int tml = t / p.tiles_n, tn = t - tml * p.tiles_n;
     const int tm = (tml + p.own_tile_end) % p.tiles_m;
@@ -216,7 +245,8 @@ __device__ __forceinline__ void red_compute_role(const RedParams& p, int slot, c
       g.dma_b(b_col + rb, b_col_bytes - rb, ldb_b, dst, wave);
     };
     g.zero();
-    if (t == rs) trace_mark(p.trace, 5);  // operands are resident: ready at once
+    if (first) trace_mark(p.trace, 5);  // operands are resident: ready at once
+    first = false;
     k_loop(g, nk, st0, st1, st2, [](int) {}, load_step, [](int) {});
 
     int lr0, lr1;
@@ -297,20 +327,30 @@ __device__ __forceinline__ void red_compute_role(const RedParams& p, int slot, c
       }
     });
     __syncthreads();  // the next tile's prologue reuses the LDS
+    t = -1;
   }
+}
+
+// The first two stage buffers double as the copy ring's slots: 8 KiB per wave.
+template <class T>
+constexpr int red_stage_bytes() {
+  return T::STAGE > T::NW * 8192 ? T::STAGE : T::NW * 8192;
 }
 
 template <class T>
 __global__ __launch_bounds__(T::NW * 64, 1) void gemm_reduce_kernel(RedParams p) {
-  __shared__ __attribute__((aligned(16))) char st0[T::STAGE];
-  __shared__ __attribute__((aligned(16))) char st1[T::STAGE];
+  __shared__ __attribute__((aligned(16))) char st0[red_stage_bytes<T>()];
+  __shared__ __attribute__((aligned(16))) char st1[red_stage_bytes<T>()];
   __shared__ __attribute__((aligned(16))) char st2[k_stages<T>() == 3 ? T::STAGE : 16];
   __shared__ int s_ok;
+  __shared__ int s_claim;
   const int wg = blockIdx.x;
   if (wg < p.n_copy) {
     trace_begin(p.trace, ROLE_COPY);
-    red_copy_role<T::NW * 64>(p, wg);
+    red_copy_role<T>(p, wg, st0, st1);
     trace_mark(p.trace, 5);
+    __syncthreads();  // the ring's LDS slots become the GEMM's stage buffers
+    red_compute_role<T>(p, -1, st0, st1, st2, &s_ok, &s_claim);  // then help with leftover tiles
   } else if (wg < p.n_copy + p.n_reduce) {
     trace_begin(p.trace, ROLE_REDUCE);
     red_reduce_role<T>(p, wg - p.n_copy, &s_ok);
@@ -318,9 +358,16 @@ __global__ __launch_bounds__(T::NW * 64, 1) void gemm_reduce_kernel(RedParams p)
   } else {
     trace_begin(p.trace, ROLE_COMPUTE);
     const int slot = wg - p.n_copy - p.n_reduce;
-    if (slot < p.n_compute) red_compute_role<T>(p, slot, st0, st1, st2, &s_ok);
+    if (slot < p.n_compute) red_compute_role<T>(p, slot, st0, st1, st2, &s_ok, &s_claim);
   }
   trace_end(p.trace);
+  // exit accounting: the last workgroup out re-zeroes the tile counter for the next call (every
+  // workgroup's last claim returned before it counts its exit)
+  __syncthreads();
+  if (threadIdx.x == 0 && atomic_add_agent(p.counters + CTR_RED_EXIT, 1u) == gridDim.x - 1) {
+    __hip_atomic_store(p.counters + CTR_RED_TILE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(p.counters + CTR_RED_EXIT, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 template <class T>

@@ -131,7 +131,7 @@ struct RedPlan {
 
 inline int plan_reduce(const Ws& ws, const Opts* o, int is_rs, const void* a, const void* b, int m, int n, int k,
                        int world, int rank, const void* const* peers, const void* out, void* const* outbox,
-                       int tile_m, int tile_n, RedPlan* P) {
+                       int tile_m, int tile_n, int tile_waves, RedPlan* P) {
   if (!a || !b || !out) return MK_ERR_INVALID_ARG;
   if (world < 1 || world > kMaxWorld || rank < 0 || rank >= world) return MK_ERR_INVALID_ARG;
   if (m <= 0 || n <= 0 || k <= 0) return MK_ERR_INVALID_ARG;
@@ -156,10 +156,17 @@ inline int plan_reduce(const Ws& ws, const Opts* o, int is_rs, const void* a, co
   }
   if ((uint64_t)m * k * 2 >= k4G || (uint64_t)k * n * 2 >= k4G || (uint64_t)m * n * 4 >= k4G) return MK_ERR_UNSUPPORTED;
   P->p_rows = is_rs ? P->m_slice : m;
-  const bool big = (P->p_rows % 128 == 0) && (n % 128 == 0);
-  int ur = o && o->arrival_unit_rows ? o->arrival_unit_rows : (big ? 128 : 64);
-  int uc = o && o->arrival_unit_cols ? o->arrival_unit_cols : (big ? 128 : 64);
+  // The copy ring moves at most 8 KiB of a unit per wave and batch: the largest unit that fits the
+  // kernel's wave count and divides the partial.
+  if (tile_waves <= 0) return MK_ERR_INVALID_ARG;
+  const long max_unit = 8192L * tile_waves;
+  int ur_d = 64, uc_d = 64;
+  if (P->p_rows % 128 == 0 && n % 128 == 0 && 128 * 128 * 4 <= max_unit) ur_d = uc_d = 128;
+  else if (n % 128 == 0 && 64 * 128 * 4 <= max_unit) uc_d = 128;
+  int ur = o && o->arrival_unit_rows ? o->arrival_unit_rows : ur_d;
+  int uc = o && o->arrival_unit_cols ? o->arrival_unit_cols : uc_d;
   if ((ur != 64 && ur != 128) || (uc != 64 && uc != 128)) return MK_ERR_UNSUPPORTED;
+  if ((long)ur * uc * 4 > max_unit) return MK_ERR_UNSUPPORTED;
   if (P->p_rows % ur || n % uc) return MK_ERR_UNSUPPORTED;
   P->unit_rows = ur;
   P->unit_cols = uc;
@@ -183,7 +190,8 @@ inline int plan_reduce(const Ws& ws, const Opts* o, int is_rs, const void* a, co
   if (P->inbox_need > ws.inbox_bytes) return MK_ERR_WORKSPACE;
   if ((size_t)P->n_units + (size_t)P->tiles_m * P->tiles_n > ws.n_flags) return MK_ERR_WORKSPACE;
   if (P->emulated && o && o->arrival_order && o->arrival_len != P->n_order) return MK_ERR_INVALID_ARG;
-  const int want_copy = P->emulated ? ((o && o->n_copy_wg) ? o->n_copy_wg : 32) : 0;
+  // copy workgroups join the compute role on leftover tiles once their units have landed
+  const int want_copy = P->emulated ? ((o && o->n_copy_wg) ? o->n_copy_wg : 128) : 0;
   const int want_reduce = (world > 1 && o) ? o->n_reduce_wg : 0;
   int code = split_roles(ws.grid, want_copy, want_reduce, o ? o->n_compute_wg : 0, &P->n_copy, &P->n_reduce,
                          &P->n_compute);

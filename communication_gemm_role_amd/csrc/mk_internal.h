@@ -25,8 +25,10 @@ namespace mk {
 
 // Context counters [0, 128) hold per-call bookkeeping, each left zero by the kernel that uses it:
 // MoE uses [0, 2+n_local] and [100, 101] (see mk_moe.hip); AllGather+GEMM uses [110, 111].
-constexpr int CTR_AG_TILE = 110;  // next leftover AG tile
-constexpr int CTR_AG_EXIT = 111;  // AG workgroups that have exited
+constexpr int CTR_AG_TILE = 110;   // next leftover AG tile
+constexpr int CTR_AG_EXIT = 111;   // AG workgroups that have exited
+constexpr int CTR_RED_TILE = 112;  // next leftover RS/AR tile
+constexpr int CTR_RED_EXIT = 113;  // RS/AR workgroups that have exited
 
 struct AgParams {
   const uint16_t* shards[MK_MAX_WORLD];
@@ -58,6 +60,7 @@ struct RedParams {
   const int32_t* order;
   uint32_t* flags;                   // landing flags [n_units], then presum flags [tiles]
   uint32_t* presum_flags;
+  uint32_t* counters;                // context counters (CTR_RED_*)
   int* status;
   int is_rs;
   int m, n, k, world, rank, m_slice;
@@ -111,6 +114,7 @@ int ag_tile_m();
 int ag_tile_n();
 int red_tile_m(int m, int n);
 int red_tile_n(int m, int n);
+int red_tile_waves(int m, int n);
 int moe_tile_m();
 int moe_tile_n();
 

@@ -198,7 +198,10 @@ class RedShape:
 
 
 RS_DOWN = RedShape(m=8192, n=4096, k=1792, world=8, sigma_a=1.0, sigma_b=0.02, sigma_q=1.0, cfg=CFG_RS)
-AR_DECODE = RedShape(m=256, n=8192, k=1024, world=8, sigma_a=1.0, sigma_b=0.02, sigma_q=1.0, cfg=CFG_AR)
+# 64x128 fp32 landing units (32 KiB): the decode-like AR uses a four-wave tile, whose copy ring
+# moves at most 8 KiB of a unit per wave
+AR_DECODE = RedShape(m=256, n=8192, k=1024, world=8, sigma_a=1.0, sigma_b=0.02, sigma_q=1.0, unit_rows=64,
+                     unit_cols=128, cfg=CFG_AR)
 # small versions (same structure, a few tiles and a ragged count of units) for parity at CPU speed
 RS_SMALL = RedShape(m=1024, n=768, k=320, world=8, unit_rows=64, unit_cols=64, cfg=CFG_RS)
 AR_SMALL = RedShape(m=192, n=1152, k=448, world=8, unit_rows=64, unit_cols=64, cfg=CFG_AR)
