@@ -38,6 +38,7 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
 N_CU, MFMA_FLOP_PER_CLK_CU = 256, 4096  # bf16 dense: 256 CUs x 4096 flop/clk
 N_SETS = 4
+SETTLE_MS = 300.0  # sustained launches before a timed region (clock ramp)
 TRACE_UNTOUCHED = -1
 
 # HBM traffic of the AG+GEMM kernel comes from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) kept
@@ -82,8 +83,10 @@ def measured_traffic():
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
+                    help="sustained launches before each timed region, in ms of wall time")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default="",
@@ -107,29 +110,54 @@ def _i32(x):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).cuda()
 
 
-def time_stats(fns, steps, warmup) -> dict:
-    """Run fns[i % len(fns)] warmup + steps times.  Returns wall ms per step and the per-launch
-    kernel times (HIP events on the current stream, where the calls launch): mean, p10, p50, p90."""
+def _region(fns, steps, first=0):
+    """`steps` calls back to back between two HIP events on the current stream (where the calls
+    launch), with a synchronisation on both sides: (wall ms, event ms) per call."""
+    import torch
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        fns[(first + i) % len(fns)]()
+    e1.record()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps, e0.elapsed_time(e1) / steps
+
+
+def time_stats(fns, steps, warmup, settle_ms: float = SETTLE_MS, spread: bool = False) -> dict:
+    """Run fns[i % len(fns)] `warmup` times, then keep launching back to back for at least
+    `settle_ms` of wall time, then time the region: `steps` calls between two HIP events with a
+    synchronisation on both sides.  The part's clocks ramp up over the first few tens of
+    milliseconds of sustained work (the same kernel runs about 20 % slower in its first 50 launches
+    than after 200), so the settle phase is what makes the region a steady-state rate; the first
+    region after the warm-up alone is reported too, as cold_ms.  Returns wall ms per step and
+    kernel_ms (event time of the region per launch).  With spread, a last pass records an event
+    pair around every launch for the per-launch distribution (p10, p50, p90)."""
     import torch
     for i in range(warmup):
         fns[i % len(fns)]()
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    cold_wall, _ = _region(fns, steps)
     t0 = time.perf_counter()
-    for i in range(steps):
-        ev[i][0].record()
-        fns[i % len(fns)]()
-        ev[i][1].record()
-    torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) * 1e3 / steps
-    k = np.array([a.elapsed_time(b) for a, b in ev])
-    return {"wall_ms": wall, "kernel_ms": float(k.mean()), "p10": float(np.percentile(k, 10)),
-            "p50": float(np.percentile(k, 50)), "p90": float(np.percentile(k, 90))}
-
-
-def time_calls(fns, steps, warmup):
-    t = time_stats(fns, steps, warmup)
-    return t["wall_ms"], t["kernel_ms"]
+    n_settle = 0
+    while (time.perf_counter() - t0) * 1e3 < settle_ms:
+        for _ in range(20):
+            fns[n_settle % len(fns)]()
+            n_settle += 1
+        torch.cuda.synchronize()
+    wall, ev = _region(fns, steps)
+    out = {"wall_ms": wall, "kernel_ms": ev, "cold_ms": cold_wall, "settle_launches": n_settle}
+    if spread:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for i in range(steps):
+            evs[i][0].record()
+            fns[i % len(fns)]()
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        k = np.array([a.elapsed_time(b) for a, b in evs])
+        out.update({"per_launch_events_mean": float(k.mean()), "p10": float(np.percentile(k, 10)),
+                    "p50": float(np.percentile(k, 50)), "p90": float(np.percentile(k, 90))})
+    return out
 
 
 # ------------------------------------------------------------------------------------------------
@@ -156,20 +184,23 @@ def clock_ghz(rec) -> float:
     return cyc / wall * 0.1 if wall > 0 else float("nan")
 
 
-def traced_call(ctx, fn, opts):
-    """One untimed call with tracing on; returns its records."""
+def traced_call(ctx, fns, opts, lead: int = 100):
+    """`lead` untraced calls back to back (the clocks stay up), then one call with tracing on;
+    returns its records.  fns: one callable or a list rotated through."""
     import torch
+    fns = fns if isinstance(fns, (list, tuple)) else [fns]
     tr = new_trace(ctx)
-    opts.trace = tr
     try:
-        fn()
+        for i in range(lead):
+            fns[i % len(fns)]()
+        opts.trace = tr
+        fns[lead % len(fns)]()
         torch.cuda.synchronize()
     finally:
         opts.trace = None
     return trace_records(tr)
 
 
-# ------------------------------------------------------------------------------------------------
 def setup_ag(ctx, resident: bool, identity: bool = False):
     """Four rotating buffer sets; returns (shape, calls, opts) with one Opts shared by the calls."""
     import torch
@@ -406,18 +437,19 @@ def main():
             calls = [lambda: dst.copy_(src)]
         else:
             raise SystemExit(f"unknown --only {a.only}")
-        t = time_stats(calls, a.steps, a.warmup)
+        t = time_stats(calls, a.steps, a.warmup, a.settle_ms)
         st = ctx.status()
-        print(json.dumps({"only": a.only, "ms_per_step": t["wall_ms"], "kernel_ms": t["kernel_ms"], "status": st}),
+        print(json.dumps({"only": a.only, "ms_per_step": t["wall_ms"], "kernel_ms": t["kernel_ms"],
+                          "cold_ms": t["cold_ms"], "settle_launches": t["settle_launches"], "status": st}),
               flush=True)
         return
 
     s, calls, opts = setup_ag(ctx, resident=False)
-    t = time_stats(calls, a.steps, a.warmup)
+    t = time_stats(calls, a.steps, a.warmup, a.settle_ms, spread=True)
     status = ctx.status()
     if status != mk.MK_OK:
         raise SystemExit(f"device status {status}: {mk.strerror(status)}")
-    rec = traced_call(ctx, calls[0], opts)
+    rec = traced_call(ctx, calls, opts)
     tr = ag_trace_summary(rec, s)
     value = s.flops / (t["wall_ms"] * 1e-3) / 1e12
     achieved = s.flops / (t["kernel_ms"] * 1e-3) / 1e12
@@ -444,7 +476,11 @@ def main():
                      "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": ag_algorithmic_bytes(s),
                      "measured_clock_GHz": clk, "peak_at_measured_clock": round(peak_clk, 1),
                      "frac_at_measured_clock": round(achieved / peak_clk, 4) if peak_clk > 0 else None},
-        "kernel_ms": {k: round(v, 5) for k, v in t.items() if k != "wall_ms"},
+        "kernel_ms": {k: round(v, 5) for k, v in t.items() if k not in ("wall_ms", "cold_ms", "settle_launches")},
+        "timing": {"region": "steps launches back to back between two HIP events, synchronised on both sides",
+                   "settle_ms": a.settle_ms, "settle_launches": t["settle_launches"],
+                   "cold_ms_per_step": round(t["cold_ms"], 5),
+                   "note": "cold = the same region right after the warm-up steps, before the clocks have ramped"},
         "trace": tr,
         "env": {"gpu": torch.cuda.get_device_name(0), "hip": torch.version.hip, "torch": torch.__version__},
     }
@@ -455,19 +491,19 @@ def main():
     if not a.no_secondary:
         sec = {}
         _, calls_r, _ = setup_ag(ctx, resident=True)
-        tr_ = time_stats(calls_r, 30, 3)
+        tr_ = time_stats(calls_r, 100, 3, a.settle_ms)
         sec["ag_resident"] = {"kernel_ms": round(tr_["kernel_ms"], 5),
                               "tflops": round(s.flops / (tr_["kernel_ms"] * 1e-3) / 1e12, 2),
                               "fused_slowdown": round(t["kernel_ms"] / tr_["kernel_ms"] - 1.0, 4)}
         del calls_r
         _, calls_2 = setup_ag_two_launch(ctx)
-        t2 = time_stats(calls_2, 30, 3)
+        t2 = time_stats(calls_2, 100, 3, a.settle_ms)
         sec["ag_copy_then_gemm"] = {"ms_per_step": round(t2["kernel_ms"], 5),
                                     "tflops": round(s.flops / (t2["kernel_ms"] * 1e-3) / 1e12, 2),
                                     "note": "comparator: 7 copy kernels then the GEMM kernel, separate launches"}
         del calls_2
         _, calls_v = setup_vendor_gemm()
-        tv = time_stats(calls_v, 30, 3)
+        tv = time_stats(calls_v, 100, 3, a.settle_ms)
         sec["vendor_gemm"] = {"kernel_ms": round(tv["kernel_ms"], 5),
                               "tflops": round(s.flops / (tv["kernel_ms"] * 1e-3) / 1e12, 2),
                               "note": "comparator: torch.matmul bf16 -> bf16 on the gathered shape, operands resident"}
@@ -476,7 +512,7 @@ def main():
         for op in ("rs", "ar"):
             for emulated in (False, True):
                 sh, cr = setup_reduce(ctx, op, emulated=emulated)
-                tt = time_stats(cr, 30, 3)
+                tt = time_stats(cr, 100, 3, a.settle_ms)
                 k_ = tt["kernel_ms"]
                 epi, total = reduce_bytes(sh, op, emulated)
                 sec[op + ("_landing" if emulated else "")] = {
@@ -487,10 +523,10 @@ def main():
                 del cr
                 torch.cuda.empty_cache()
         sm, offs, cm, mopts = setup_moe(ctx)
-        tm = time_stats(cm, 20, 2)
+        tm = time_stats(cm, 100, 2, a.settle_ms)
         o = offs[0].cpu().numpy()
         R = int(o[-1])
-        mrec = traced_call(ctx, cm[0], mopts)
+        mrec = traced_call(ctx, cm, mopts)
         sec["moe"] = {"kernel_ms": round(tm["kernel_ms"], 5), "routed_rows": R,
                       "rows_per_expert": np.diff(o).tolist(),
                       "tflops": round(sm.flops(R) / (tm["kernel_ms"] * 1e-3) / 1e12, 2),
