@@ -91,7 +91,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default="",
                     help="profiling: run only this op (ag, ag_resident, ag_identity, rs, ar, rs_emulated, ar_emulated, "
-                         "moe, copy)")
+                         "moe, vendor, copy)")
     return ap.parse_args()
 
 
@@ -430,6 +430,8 @@ def main():
             _, calls = setup_reduce(ctx, a.only[:2], emulated=True)
         elif a.only == "moe":
             _, _, calls, _ = setup_moe(ctx)
+        elif a.only == "vendor":
+            _, calls = setup_vendor_gemm()
         elif a.only == "copy":
             # calibration for the HBM byte counters: a plain device copy of 256 MiB per launch
             src = torch.empty(64 << 20, dtype=torch.float32, device="cuda").fill_(1.0)

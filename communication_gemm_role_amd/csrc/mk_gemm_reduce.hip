@@ -247,7 +247,7 @@ __device__ __forceinline__ void red_compute_role(const RedParams& p, int slot, c
     g.zero();
     if (first) trace_mark(p.trace, 5);  // operands are resident: ready at once
     first = false;
-    k_loop(g, nk, st0, st1, st2, st2, [](int) {}, load_step, [](int) {});
+    k_loop(g, nk, st0, st1, st2, [](int) {}, load_step, [](int) {});
 
     int lr0, lr1;
     owned_rows<T>(p, tm, lr0, lr1);

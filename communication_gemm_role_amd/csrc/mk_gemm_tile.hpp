@@ -1,5 +1,5 @@
 // Compute role core: one BM x BN fp32 output tile of C = A @ B with bf16 operands on gfx950
-// MFMA (v_mfma_f32_32x32x16_bf16), the operands staged in LDS over K steps of BK = 64 or 32.
+// MFMA (v_mfma_f32_32x32x16_bf16), the operands staged in LDS over K steps of BK = 64.
 //
 // NW = WM x WN waves (4 or 8); wave (wm, wn) owns a (BM/WM) x (BN/WN) sub-tile made of 32 x 32
 // MFMA fragments.  MFMA lane layout (checked on the device): for the A operand lane l holds row
@@ -14,21 +14,24 @@
 // the device).  Two such reads give a lane the 8 consecutive k of its column that the MFMA B
 // operand needs.
 //
-// LDS per stage: A [BM][BK] bf16 (2*BK-byte rows), B [BK][BN] bf16 (2*BN-byte rows), both with
+// LDS per stage: A [BM][64] bf16 (128-byte rows), B [64][BN] bf16 (2*BN-byte rows), both with
 // 16-byte chunks XOR-swizzled so that 16 lanes reading the same logical chunk of 16 consecutive
 // rows hit distinct 16-byte groups of the 64 four-byte banks.  The DMA writes each wave's 1 KiB
 // contiguously, so the swizzle is applied on the global side: LDS chunk p of row r receives
 // global chunk p ^ swz(r).
 //
-// BK trades barriers for loads in flight: per K step every wave waits for its own DMA and the
-// workgroup passes one barrier, and the loads of the steps after the next one stay in flight
-// meanwhile.  With BK = 32 a 256 x 256 tile fits four stages in the LDS that two BK = 64 stages
-// take, so three steps (96 KiB) are in flight instead of one (64 KiB); a CU's operand load rate
-// grows with the bytes it has in flight.
+// BK stays 64: each A row then gives a whole 128-byte line per step.  A CU's operand load rate is
+// bounded by the lines it has in flight, so BK = 32 (four stages in the same LDS, three steps in
+// flight) measured slower, its A rows giving half lines.
 #pragma once
 #include "mk_device.hpp"
 
 namespace mk {
+
+// Position of logical 16-byte chunk `c` (0..7) of A row `row` (rows are 128 bytes).  Two rows fill
+// the 64 four-byte banks, so pairs of rows share a pattern: any 16 consecutive rows read at the
+// same logical chunk hit 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int row, int c) { return c ^ ((row >> 1) & 7); }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
@@ -49,56 +52,41 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_at(const char* base, uint
   return make_rsrc(base + off, n);
 }
 
-// Position of logical 16-byte chunk c of A row `row` for rows of ROW_A bytes: 128-byte rows
-// (BK = 64) pair up across the 256 bytes of banks, 64-byte rows (BK = 32) group by four.
-template <int BK>
-__device__ __forceinline__ int swz_a(int row) {
-  if constexpr (BK == 64) return (row >> 1) & 7;
-  else return (row >> 2) & 3;
-}
-
-template <int BM_, int BN_, int WM_, int WN_, int BK_ = 64>
+template <int BM_, int BN_, int WM_, int WN_>
 struct TileGemmDma {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_;
-  static_assert(BK == 64 || BK == 32, "BK is 64 or 32");
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int BK = 64;
   static constexpr int NW = WM * WN;  // waves per workgroup
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
   static_assert(FM * 32 == WTM && FN * 32 == WTN, "wave tile must be a multiple of 32");
-  static constexpr int KK = BK / 16;        // MFMA k sub-steps per stage
-  static constexpr int ROW_A = BK * 2;      // bytes per A row in LDS
-  static constexpr int CPA = ROW_A / 16;    // 16-byte chunks per A row
-  static constexpr int A_ROWS = 1024 / ROW_A;  // A rows per 1 KiB DMA instruction
   static constexpr int STAGE_A = BM * BK * 2;
   static constexpr int STAGE_B = BN * BK * 2;
   static constexpr int STAGE = STAGE_A + STAGE_B;
+  static constexpr int LDS_BYTES = 2 * STAGE;
   static constexpr int A_INSTR = STAGE_A / NW / 1024;  // 1 KiB DMA instructions per wave
   static constexpr int B_INSTR = STAGE_B / NW / 1024;
   static_assert(A_INSTR * NW * 1024 == STAGE_A && B_INSTR * NW * 1024 == STAGE_B,
                 "stage must split into 1 KiB per wave");
-  // A DMA swizzle phases: with 128-byte rows an instruction's 8 rows take one of two phases, and
-  // instruction i of a wave takes phase i&1 when each wave's rows are whole 16-row groups.
-  static_assert(BK == 32 || (BM / NW) % 16 == 0, "each wave's A rows form whole 16-row groups");
-  static_assert((BM / NW) % A_ROWS == 0, "each wave's A rows form whole DMA instructions");
+  static_assert((BM / NW) % 8 == 0, "each wave's A rows form whole 8-row groups");
   static constexpr int ROW_B = BN * 2;  // bytes per B row in LDS
   static_assert(ROW_B <= 1024 && 1024 % ROW_B == 0, "a DMA instruction covers whole B rows");
 
   f32x16 acc[FM][FN];
   // per-lane address parts, computed once (init): everything else is scalar or an immediate
-  uint32_t a_dma[2];   // A DMA byte offset inside an instruction's rows (two swizzle phases)
+  uint32_t a_dma[2];   // A DMA byte offset inside an 8-row group (two swizzle phases)
   uint32_t b_dma[4];   // B DMA byte offset inside an instruction's rows (phase = first row & 3)
-  uint32_t a_rd[KK];   // A operand LDS offset per 16-wide k sub-step
+  uint32_t a_rd[4];    // A operand LDS offset per 16-wide k sub-step
   uint32_t b_rd[FN];   // B operand LDS offset per 32-column fragment
 
   __device__ __forceinline__ void init(int wm, int wn, int lane, uint32_t lda_b, uint32_t ldb_b) {
-    // A DMA: lane -> row lane/CPA of the instruction's rows, LDS chunk lane%CPA <- global chunk
-    // (lane%CPA) ^ swz_a(row).  The instruction's first row is a multiple of A_ROWS, so the
-    // swizzle depends on the lane and (128-byte rows) on the parity of the instruction's 8-row group.
+    // A DMA: lane -> row lane>>3 of an 8-row group, LDS chunk lane&7 <- global chunk p ^ ((r>>1)&7);
+    // the group's first row is a multiple of 8, so the swizzle is ((lane>>4) + 4*(group&1)) & 7.
 #pragma unroll
     for (int ph = 0; ph < 2; ++ph) {
-      const int x = (BK == 64) ? (((lane >> 4) + 4 * ph) & 7) : ((lane >> 4) & 3);
-      a_dma[ph] = (uint32_t)(lane / CPA) * lda_b + (uint32_t)((lane % CPA) ^ x) * 16u;
+      const int x = ((lane >> 4) + 4 * ph) & 7;
+      a_dma[ph] = (uint32_t)(lane >> 3) * lda_b + (uint32_t)((lane & 7) ^ x) * 16u;
     }
     // B DMA: lane -> row (lane*16)/ROW_B of the instruction's rows, chunk ((lane*16)%ROW_B)/16.
 #pragma unroll
@@ -107,12 +95,12 @@ struct TileGemmDma {
       b_dma[ph] = (uint32_t)kr * ldb_b + (uint32_t)(p ^ swz_b<BN>(ph + kr)) * 16u;
     }
     // A operand: row = wm*WTM + i*32 + (lane&31); the row base is a multiple of 32, so the swizzle
-    // term is swz_a(lane&31); logical chunk 2*kk + (lane>>5).
+    // term is ((lane&31)>>1)&7; logical chunk 2*kk + (lane>>5).
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
+    for (int kk = 0; kk < 4; ++kk) {
       const int l32 = lane & 31;
       const int kc = 2 * kk + (lane >> 5);
-      a_rd[kk] = (uint32_t)(wm * WTM + l32) * ROW_A + (uint32_t)((kc ^ swz_a<BK>(l32)) * 16);
+      a_rd[kk] = (uint32_t)(wm * WTM + l32) * 128u + (uint32_t)(swz(l32, kc) * 16);
     }
     // B operand (transposed reads): group g = lane>>4; in-group s: row jr = s>>2 of the 4-row block,
     // 4-column piece q = s&3.  k = kk*16 + 8*(g>>1) + 4*hh + jr, so k&3 = jr.
@@ -141,9 +129,9 @@ struct TileGemmDma {
   __device__ __forceinline__ void dma_a(const char* abase, uint32_t a_bytes, uint32_t lda_b, char* lds, int wave) {
 #pragma unroll
     for (int i = 0; i < A_INSTR; ++i) {
-      const int r0 = wave * (BM / NW) + i * A_ROWS;
+      const int r0 = wave * (BM / NW) + i * 8;
       const auto rs = rsrc_at(abase, a_bytes, (uint32_t)r0 * lda_b);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(lds + r0 * ROW_A), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(lds + r0 * 128), 16,
                                                a_dma[i & 1], 0, 0, 0);
     }
   }
@@ -159,14 +147,14 @@ struct TileGemmDma {
     }
   }
 
-  // One BK stage of MFMAs for this wave from stage `lds`.  Operand fragments are double buffered
-  // across the 16-wide k sub-steps (reads for sub-step kk+1 are issued before the MFMAs of kk),
-  // and a scheduling fence after each sub-step keeps the compiler from hoisting every sub-step's
-  // reads at once, which would need many extra VGPRs.
+  // One BK = 64 stage of MFMAs for this wave from stage `lds`.  Operand fragments are double
+  // buffered across the four 16-wide k sub-steps (reads for sub-step kk+1 are issued before the
+  // MFMAs of kk), and a scheduling fence after each sub-step keeps the compiler from hoisting all
+  // four sub-steps' reads at once, which would need 128 extra VGPRs.
   __device__ __forceinline__ void load_frags(const char* lds, int kk, bf16x8* af, bf16x8* bfr) {
     const char* lb = lds + STAGE_A;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(lds + a_rd[kk] + i * 32 * ROW_A);
+    for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(lds + a_rd[kk] + i * 32 * 128);
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const i16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -180,8 +168,8 @@ struct TileGemmDma {
     bf16x8 af[2][FM], bfr[2][FN];
     load_frags(lds, 0, af[0], bfr[0]);
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      if (kk + 1 < KK) load_frags(lds, kk + 1, af[(kk + 1) & 1], bfr[(kk + 1) & 1]);
+    for (int kk = 0; kk < 4; ++kk) {
+      if (kk + 1 < 4) load_frags(lds, kk + 1, af[(kk + 1) & 1], bfr[(kk + 1) & 1]);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -193,48 +181,32 @@ struct TileGemmDma {
 
   // Epilogue through LDS: each wave stages one 32-row slab of its sub-tile at a time (rows of
   // WTN + 8 floats, so row pairs 4 apart land 128 bytes apart) and hands out row-contiguous
-  // float4s, so the caller issues 16-byte coalesced global accesses.  The waves split into EPI_G
-  // groups, group g staging in the caller's stage buffer g: two groups when half the waves'
-  // staging fits in one stage buffer, else four.  The caller must have passed a barrier after the
-  // last mma() and must barrier again before the stage buffers are reused.
+  // float4s, f(row_in_tile, col_in_tile, value), so the caller issues 16-byte coalesced global
+  // accesses.  The first half of the waves stage in `st_lo`, the second half in `st_hi` (each a
+  // different stage buffer, so the slabs fit after the mainloop).  The caller must have passed a
+  // barrier after the last mma() and must barrier again before the stage buffers are reused.
   static constexpr int EPI_STRIDE = WTN + 8;
   static constexpr int EPI_WAVE = 32 * EPI_STRIDE * 4;
-  static constexpr int EPI_G = (NW / 2) * EPI_WAVE <= STAGE ? 2 : 4;
-  static_assert((NW / EPI_G) * EPI_WAVE <= STAGE, "a group's staging must fit in one stage buffer");
-  static constexpr int SLAB_Q = (32 * (WTN / 4)) / 64;  // float4s per lane per 32-row slab
-
-  __device__ __forceinline__ static float* epi_area(char* s0, char* s1, char* s2, char* s3, int wave) {
-    constexpr int PER = NW / EPI_G;
-    const int g = wave / PER;
-    char* base = g == 0 ? s0 : g == 1 ? s1 : g == 2 ? s2 : s3;
-    return reinterpret_cast<float*>(base + (wave % PER) * EPI_WAVE);
-  }
-  __device__ __forceinline__ void stage_slab(float* wl, int i, int lane) {
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        wl[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * EPI_STRIDE + j * 32 + (lane & 31)] = acc[i][j][r];
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): staged values are in LDS
-    __builtin_amdgcn_wave_barrier();
-  }
-
-  // f(row_in_tile, col_in_tile, value) for every float4 of the tile this wave owns.  s2 and s3
-  // are used only when EPI_G == 4.
+  static_assert((NW / 2) * EPI_WAVE <= STAGE, "half the waves' staging must fit in one stage buffer");
   template <class F>
-  __device__ __forceinline__ void epilogue(char* s0, char* s1, char* s2, char* s3, int wm, int wn, int lane_in,
-                                           int wave, F&& f) {
+  __device__ __forceinline__ void epilogue(char* st_lo, char* st_hi, int wm, int wn, int lane_in, int wave, F&& f) {
     // The staging addresses do not depend on the tile; an opaque copy of the lane id stops the
     // compiler from hoisting all of them out of the persistent tile loop (64+ live registers).
     int lane = lane_in;
     asm volatile("" : "+v"(lane));
-    float* wl = epi_area(s0, s1, s2, s3, wave);
+    float* wl = reinterpret_cast<float*>((wave < NW / 2 ? st_lo : st_hi) + (wave % (NW / 2)) * EPI_WAVE);
     constexpr int C4 = WTN / 4;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      stage_slab(wl, i, lane);
 #pragma unroll
-      for (int q = 0; q < SLAB_Q; ++q) {
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          wl[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * EPI_STRIDE + j * 32 + (lane & 31)] = acc[i][j][r];
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int q = 0; q < (32 * C4) / 64; ++q) {
         const int idx = q * 64 + lane;
         const int row = idx / C4, c4 = idx - row * C4;
         const f32x4 v = *reinterpret_cast<const f32x4*>(wl + row * EPI_STRIDE + c4 * 4);
@@ -244,26 +216,28 @@ struct TileGemmDma {
       __builtin_amdgcn_wave_barrier();
     }
   }
-  template <class F>
-  __device__ __forceinline__ void epilogue(char* s0, char* s1, int wm, int wn, int lane, int wave, F&& f) {
-    static_assert(EPI_G == 2, "this tile stages its epilogue in four stage buffers");
-    epilogue(s0, s1, s0, s1, wm, wn, lane, wave, f);
-  }
 
   // As epilogue(), but hands `f` all of this lane's values of one 32-row slab at once, so an
   // epilogue that loads other data per value (peer partials) can have all those loads in flight
   // together: f(slab_row0, v, rows, cols) with SLAB_Q values; rows and cols are tile-relative and
   // slab_row0 is the slab's first row.
+  static constexpr int SLAB_Q = (32 * (WTN / 4)) / 64;
   template <class F>
-  __device__ __forceinline__ void epilogue_slab(char* s0, char* s1, char* s2, char* s3, int wm, int wn,
-                                                int lane_in, int wave, F&& f) {
+  __device__ __forceinline__ void epilogue_slab(char* st_lo, char* st_hi, int wm, int wn, int lane_in, int wave,
+                                                F&& f) {
     int lane = lane_in;
     asm volatile("" : "+v"(lane));
-    float* wl = epi_area(s0, s1, s2, s3, wave);
+    float* wl = reinterpret_cast<float*>((wave < NW / 2 ? st_lo : st_hi) + (wave % (NW / 2)) * EPI_WAVE);
     constexpr int C4 = WTN / 4;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      stage_slab(wl, i, lane);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          wl[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * EPI_STRIDE + j * 32 + (lane & 31)] = acc[i][j][r];
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
       f32x4 v[SLAB_Q];
       int rows[SLAB_Q], cols[SLAB_Q];
 #pragma unroll
@@ -279,13 +253,7 @@ struct TileGemmDma {
       f(wm * WTM + i * 32, v, rows, cols);
     }
   }
-  template <class F>
-  __device__ __forceinline__ void epilogue_slab(char* s0, char* s1, int wm, int wn, int lane, int wave, F&& f) {
-    static_assert(EPI_G == 2, "this tile stages its epilogue in four stage buffers");
-    epilogue_slab(s0, s1, s0, s1, wm, wn, lane, wave, f);
-  }
 };
-
 
 // s_waitcnt immediate that waits until at most `n` vector-memory operations of this wave are
 // outstanding (expcnt / lgkmcnt left unconstrained).
@@ -359,60 +327,18 @@ __device__ __forceinline__ void k_loop2(G& g, int nk, char* st0, char* st1, Pre&
   }
 }
 
-// Four-stage K loop over static stage buffers st0..st3: the DMA for step q+3 is issued before
-// the MFMAs of step q (into the buffer step q-1 read, which every wave left at the previous
-// barrier), and the end-of-step wait leaves the two newest steps' loads in flight.
-template <class G, class Pre, class Load, class After>
-__device__ __forceinline__ void k_loop4(G& g, int nk, char* st0, char* st1, char* st2, char* st3, Pre&& before_load,
-                                        Load&& load, After&& before_wait) {
-  constexpr int D = G::A_INSTR + G::B_INSTR;
-  load(0, st0);
-  if (nk > 1) load(1, st1);
-  if (nk > 2) load(2, st2);
-  if (nk > 2) wait_vm<2 * D>();
-  else if (nk > 1) wait_vm<D>();
-  else wait_vm<0>();
-  __syncthreads();
-  auto sub = [&](int q, char* cur, char* pf) {
-    if (q >= nk) return;
-    const bool more = q + 3 < nk;
-    before_load(q);
-    if (more) load(q + 3, pf);
-    g.mma(cur);
-    before_wait(q);
-    // step q+1 must have landed: the loads issued after it may stay in flight
-    if (more) wait_vm<2 * D>();
-    else if (q + 3 == nk) wait_vm<D>();
-    else wait_vm<0>();
-    __syncthreads();
-  };
-  for (int q = 0; q < nk; q += 4) {
-    sub(q, st0, st3);
-    sub(q + 1, st1, st0);
-    sub(q + 2, st2, st1);
-    sub(q + 3, st3, st2);
-  }
-}
-
-// Stage buffers a tile's K loop uses: four for BK = 32 tiles, else three when they fit in the
-// 160 KiB of LDS beside a few KiB of bookkeeping, else two.
+// Stage buffers a tile's K loop uses: three when they fit in the 160 KiB of LDS beside a few KiB
+// of bookkeeping, else two.
 template <class G>
 constexpr int k_stages() {
-  if constexpr (G::BK == 32) {
-    static_assert(4 * G::STAGE <= 150 * 1024, "four BK = 32 stages must fit");
-    return 4;
-  } else {
-    return 3 * G::STAGE <= 150 * 1024 ? 3 : 2;
-  }
+  return 3 * G::STAGE <= 150 * 1024 ? 3 : 2;
 }
 
-// The K loop for tile G on its stage count (buffers past that count are unused).
+// The K loop for tile G on its stage count (st2 is unused with two stages).
 template <class G, class Pre, class Load, class After>
-__device__ __forceinline__ void k_loop(G& g, int nk, char* st0, char* st1, char* st2, char* st3, Pre&& before_load,
-                                       Load&& load, After&& before_wait) {
-  if constexpr (k_stages<G>() == 4)
-    k_loop4(g, nk, st0, st1, st2, st3, before_load, load, before_wait);
-  else if constexpr (k_stages<G>() == 3)
+__device__ __forceinline__ void k_loop(G& g, int nk, char* st0, char* st1, char* st2, Pre&& before_load, Load&& load,
+                                       After&& before_wait) {
+  if constexpr (k_stages<G>() == 3)
     k_loop3(g, nk, st0, st1, st2, before_load, load, before_wait);
   else
     k_loop2(g, nk, st0, st1, before_load, load, before_wait);
