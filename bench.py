@@ -296,7 +296,7 @@ def setup_reduce(ctx, op: str, emulated: bool = False, n_reduce: int = 0):
         else:
             out = torch.empty((s.m, s.n), device="cuda")
             calls.append(lambda a=a, b=b, pe=peers, out=out: mk.mk_gemm_ar(ctx, a, b, s.world, 0, pe, out, opts=opts))
-    return s, calls
+    return s, calls, opts
 
 
 def reduce_bytes(sh, op: str, emulated: bool):
@@ -425,9 +425,9 @@ def main():
         if a.only in ("ag", "ag_resident", "ag_identity"):
             _, calls, _ = setup_ag(ctx, a.only == "ag_resident", identity=a.only == "ag_identity")
         elif a.only in ("rs", "ar"):
-            _, calls = setup_reduce(ctx, a.only)
+            _, calls, _ = setup_reduce(ctx, a.only)
         elif a.only in ("rs_emulated", "ar_emulated"):
-            _, calls = setup_reduce(ctx, a.only[:2], emulated=True)
+            _, calls, _ = setup_reduce(ctx, a.only[:2], emulated=True)
         elif a.only == "moe":
             _, _, calls, _ = setup_moe(ctx)
         elif a.only == "vendor":
@@ -513,7 +513,7 @@ def main():
         torch.cuda.empty_cache()
         for op in ("rs", "ar"):
             for emulated in (False, True):
-                sh, cr = setup_reduce(ctx, op, emulated=emulated)
+                sh, cr, _ = setup_reduce(ctx, op, emulated=emulated)
                 tt = time_stats(cr, 100, 3, a.settle_ms)
                 k_ = tt["kernel_ms"]
                 epi, total = reduce_bytes(sh, op, emulated)

@@ -287,7 +287,7 @@ __device__ __forceinline__ void ag_compute_role(const AgParams& p, int slot, cha
         if (lane == 0) s_sched[decided_at(q)] = u;
       }
     };
-    k_loop(g, nk, st0, st1, st2, before_load, load, before_wait);
+    k_loop(g, nk, st0, st1, st2, st2, st2, before_load, load, before_wait);
 
     // epilogue: fp32 C tile, staged through LDS into row-contiguous 16-byte stores
     g.epilogue(st0, st1, wm, wn, lane, wave, [&](int row, int col, f32x4 v) {

@@ -17,6 +17,7 @@ constexpr size_t kDefaultWs = 512ull << 20;
 constexpr size_t kStatusBytes = 256;
 constexpr size_t kCounters = 1u << 20;  // 4 MiB of u32 counters
 constexpr size_t kFlags = 1u << 20;     // 4 MiB of u32 flags
+static_assert(mkh::kCtrBand0 == mk::CTR_RED_BAND0, "host and kernel agree on the RS band counters");
 
 struct DeviceGuard {  // make ctx->device current for the duration of a call
   int prev = -1;
@@ -256,6 +257,7 @@ static int gemm_reduce(int is_rs, mk_ctx* ctx, void* stream, const uint16_t* a, 
   p.units_per_peer = P.units_per_peer;
   p.n_copy = P.n_copy;
   p.n_reduce = P.n_reduce;
+  p.assist = P.assist;
   p.n_compute = P.n_compute;
   p.emulated = P.emulated;
   p.n_order = P.n_order;

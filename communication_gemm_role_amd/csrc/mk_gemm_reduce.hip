@@ -16,10 +16,12 @@
 //   [n_copy, n_copy+n_reduce)   reduce: for each owned tile, waits for its peer units, sums the
 //                               peer partials with coalesced 16-byte fp32 loads, writes the sum
 //                               into the output tile and raises the tile's pre-sum flag.
-//   the rest                    compute: MFMA tile of P; epilogue adds P to the pre-sum (or, with
-//                               no reduce workgroups, sums the peers itself) and stores the owned
-//                               tile, or stores P to the owner's outbox.  Owned tiles are scheduled
-//                               last so the reduce role has had the whole GEMM to pre-sum them.
+//   the rest                    compute: MFMA tile of P; epilogue adds P to the pre-sum (or, for
+//                               AllReduce with no reduce workgroups, sums the peers itself) and
+//                               stores the owned tile, or stores P to the owner's outbox.  Owned
+//                               tiles are scheduled last so the pre-sum is ready for them: done by
+//                               the reduce role, or (ReduceScatter with no reduce workgroups) by
+//                               every workgroup in 64-row bands between its tiles.
 #include "mk_internal.h"
 #include "mk_gemm_tile.hpp"
 #include "mk_copy_ring.hpp"
@@ -136,16 +138,58 @@ __device__ __forceinline__ bool wait_units(const RedParams& p, int lr0, int lr1,
 }
 
 // ------------------------------------------------------------------------------------------
-// reduce role: pre-sum the peers' partials of owned tiles
+// pre-sum of the peers' partials of owned rows
 // ------------------------------------------------------------------------------------------
+// out[lr0, lr1) x [c0, c1) = sum of the peers' partials there (partial coordinates), with every
+// thread's loads of all peers in flight before its adds (up to 4 x 7 per thread).  Write-through
+// stores; the caller waits for them before raising the region's flag or counter.
+template <class T>
+__device__ __forceinline__ void red_sum_peers(const RedParams& p, int lr0, int lr1, int c0, int c1) {
+  constexpr int NT = T::NW * 64;
+  const int tid = threadIdx.x;
+  const int cpr = T::BN >> 2;  // 16-byte chunks per tile row
+  const int rows = lr1 - lr0, cols = c1 - c0;
+  const int ccols = cols >> 2;  // 16-byte chunks per row in this region
+  const uint32_t extent = ((uint32_t)(rows - 1) * (uint32_t)p.n + (uint32_t)cols) * 4u;
+  const size_t off = (size_t)lr0 * p.n + c0;
+  const auto dst = make_rsrc(p.out + off, extent);
+  const int total = rows * cpr;
+  for (int base = 0; base < total; base += NT * 4) {
+    // byte offsets of this thread's 4 chunks; a chunk outside the region gets an offset past
+    // every window, so its loads read 0 and its store is dropped
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = base + tid + i * NT;
+      const int row = c / cpr, cc = c - row * cpr;
+      o[i] = (c < total && cc < ccols) ? ((uint32_t)row * (uint32_t)p.n + (uint32_t)cc * 4u) * 4u : 0xfffffff0u;
+    }
+    f32x4 t[4][MK_MAX_WORLD - 1];
+#pragma unroll
+    for (int q = 0; q < MK_MAX_WORLD - 1; ++q) {
+      if (q < p.world - 1) {  // (no `break`: it would keep t in memory)
+        const auto src = make_rsrc(peer_src(p, q) + off, extent);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t[i][q] = __builtin_bit_cast(f32x4, bload16_nt(src, o[i]));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < MK_MAX_WORLD - 1; ++q)
+        if (q < p.world - 1) s += t[i][q];
+      bstore16_sc1(dst, o[i], __builtin_bit_cast(u32x4, s));
+    }
+  }
+}
+
+// Reduce role: pre-sums whole owned tiles, raising each tile's pre-sum flag.
 template <class T>
 __device__ __forceinline__ void red_reduce_role(const RedParams& p, int rid, int* s_ok) {
-  constexpr int NT = T::NW * 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int own_rows = p.own_tile_end - p.own_tile_begin;
   const int n_jobs = own_rows * p.tiles_n;
-  const uint32_t ld = (uint32_t)p.n * 4u;
-  const int cpr = T::BN >> 2;  // 16-byte chunks per tile row
   for (int job = rid; job < n_jobs; job += p.n_reduce) {
     const int tm = p.own_tile_begin + job / p.tiles_n, tn = job % p.tiles_n;
     int lr0, lr1;
@@ -159,45 +203,52 @@ __device__ __forceinline__ void red_reduce_role(const RedParams& p, int rid, int
       __syncthreads();
       if (!*s_ok) return;
     }
-    const int rows = lr1 - lr0, cols = c1 - c0;
-    const int ccols = cols >> 2;  // 16-byte chunks per row in this tile
-    const uint32_t extent = ((uint32_t)(rows - 1) * (uint32_t)p.n + (uint32_t)cols) * 4u;
-    const size_t off = (size_t)lr0 * p.n + c0;
-    const auto dst = make_rsrc(p.out + off, extent);
-    const int total = rows * cpr;
-    for (int base = 0; base < total; base += NT * 4) {
-      // byte offsets of this thread's 4 chunks; a chunk outside the tile gets an offset past
-      // every window, so its loads read 0 and its store is dropped
-      uint32_t o[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = base + tid + i * NT;
-        const int row = c / cpr, cc = c - row * cpr;
-        o[i] = (c < total && cc < ccols) ? ((uint32_t)row * (uint32_t)p.n + (uint32_t)cc * 4u) * 4u : 0xfffffff0u;
-      }
-      // every peer's loads first (up to 4 x 7 in flight), then the sums
-      f32x4 t[4][MK_MAX_WORLD - 1];
-#pragma unroll
-      for (int q = 0; q < MK_MAX_WORLD - 1; ++q) {
-        if (q >= p.world - 1) break;
-        const auto src = make_rsrc(peer_src(p, q) + off, extent);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) t[i][q] = __builtin_bit_cast(f32x4, bload16_nt(src, o[i]));
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int q = 0; q < MK_MAX_WORLD - 1; ++q)
-          if (q < p.world - 1) s += t[i][q];
-        bstore16_sc1(dst, o[i], __builtin_bit_cast(u32x4, s));
-      }
-    }
+    red_sum_peers<T>(p, lr0, lr1, c0, c1);
     wait_mem();
     __syncthreads();
     if (tid == 0) flag_store(&p.presum_flags[tm * p.tiles_n + tn], p.epoch);
-    (void)ld;
   }
+}
+
+// RS without reduce workgroups: a compute workgroup about to claim a tile first takes pre-sum
+// jobs, 64-row bands of owned tiles, until none is left (or max_jobs are done), adding one to the
+// tile's band counter per band done.  Owned tiles come last in the tile order, so their bands
+// are done by the time their epilogues need them, and the peer reads spread over every
+// workgroup instead of piling up in the owned tiles' epilogues.  Returns false on a timeout or
+// fault.
+template <class T>
+__device__ __forceinline__ bool red_presum_jobs(const RedParams& p, int* s_ok, int* s_claim, int max_jobs) {
+  constexpr int J = T::BM / 64;  // bands per owned tile
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n_jobs = (p.own_tile_end - p.own_tile_begin) * p.tiles_n * J;
+  for (int taken = 0; taken < max_jobs; ++taken) {
+    __syncthreads();  // every thread has read the last claim
+    if (tid == 0) *s_claim = (int)atomic_add_agent(p.counters + CTR_RED_PRESUM, 1u);
+    __syncthreads();
+    const int job = *s_claim;
+    if (job >= n_jobs) return true;
+    const int ot = job / J, band = job - ot * J;
+    const int tm = p.own_tile_begin + ot / p.tiles_n, tn = ot % p.tiles_n;
+    int lr0, lr1;
+    owned_rows<T>(p, tm, lr0, lr1);
+    const int b0 = lr0 + band * 64, b1 = min(lr1, b0 + 64);
+    if (b0 < b1) {
+      const int c0 = tn * T::BN, c1 = min(c0 + T::BN, p.n);
+      if (p.emulated) {
+        if (wave == 0) {
+          const bool ok = wait_units(p, b0, b1, c0, c1, lane);
+          if (lane == 0) *s_ok = ok;
+        }
+        __syncthreads();
+        if (!*s_ok) return false;
+      }
+      red_sum_peers<T>(p, b0, b1, c0, c1);
+      wait_mem();
+    }
+    __syncthreads();
+    if (tid == 0) atomic_add_agent(p.counters + CTR_RED_BAND0 + ot, 1u);
+  }
+  return true;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -208,8 +259,8 @@ template <class T>
 // left over and claimed, in logical order (owned tiles last), from a shared counter by every
 // workgroup that has finished its own work: compute workgroups after their static tile, copy
 // workgroups (slot -1) after landing their units.
-__device__ __forceinline__ void red_compute_role(const RedParams& p, int slot, char* st0, char* st1, char* st2, int* s_ok,
-                                                 int* s_claim) {
+__device__ __forceinline__ void red_compute_role(const RedParams& p, int slot, char* st0, char* st1, char* st2,
+                                                 char* st3, char* st4, int* s_ok, int* s_claim) {
   T g;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -222,10 +273,17 @@ __device__ __forceinline__ void red_compute_role(const RedParams& p, int slot, c
   g.init(wm, wn, lane, lda_b, ldb_b);
 
   int t = (slot >= 0 && rs < n_tiles) ? rs : -1;
-  bool first = slot >= 0;
+  bool first = slot >= 0, claimed = false;
+  // With resident partials, the workgroups of odd XCDs take one pre-sum band before their first
+  // tile: their peer reads (HBM) then overlap the even XCDs' first K loops (mostly L2), and the
+  // two halves reach their epilogues' stores at different times instead of all at once.
+  if (p.assist && !p.emulated && slot >= 0 && (slot & 1) && !red_presum_jobs<T>(p, s_ok, s_claim, 1)) return;
   while (true) {
     if (t < 0) {
+      if (p.assist && !red_presum_jobs<T>(p, s_ok, s_claim, 1 << 30)) return;
       if (tid == 0) *s_claim = C + (int)atomic_add_agent(p.counters + CTR_RED_TILE, 1u);
+      if (!claimed) trace_mark(p.trace, 7);  // first leftover tile claimed (after any pre-sum jobs)
+      claimed = true;
       __syncthreads();
       t = *s_claim;  // rewritten only after the next tile's barriers
       if (t >= n_tiles) break;
@@ -246,19 +304,24 @@ __device__ __forceinline__ void red_compute_role(const RedParams& p, int slot, c
     };
     g.zero();
     if (first) trace_mark(p.trace, 5);  // operands are resident: ready at once
+    k_loop(g, nk, st0, st1, st2, st3, st4, [](int) {}, load_step, [](int) {});
+    if (first) trace_mark(p.trace, 6);  // the first tile's K loop is done; its epilogue follows
     first = false;
-    k_loop(g, nk, st0, st1, st2, [](int) {}, load_step, [](int) {});
 
     int lr0, lr1;
     owned_rows<T>(p, tm, lr0, lr1);
     const bool has_owned = lr1 > lr0;
-    const bool presum = has_owned && p.n_reduce > 0;
+    const bool presum = has_owned && (p.n_reduce > 0 || p.assist);
     if (has_owned) {
-      // the peer data this tile adds must have landed (emulated) or been pre-summed (reduce role)
+      // the peer data this tile adds must have landed (emulated) or been pre-summed (reduce role,
+      // or every band by the compute workgroups' pre-sum jobs)
       if (wave == 0) {
         bool ok = true;
         if (presum) {
-          if (lane == 0) ok = spin_until_eq(&p.presum_flags[tm * p.tiles_n + tn], p.epoch, p.timeout_ticks, p.status);
+          if (lane == 0)
+            ok = p.assist ? spin_until_ge(p.counters + CTR_RED_BAND0 + (tm - p.own_tile_begin) * p.tiles_n + tn,
+                                          (uint32_t)(T::BM / 64), p.timeout_ticks, p.status)
+                          : spin_until_eq(&p.presum_flags[tm * p.tiles_n + tn], p.epoch, p.timeout_ticks, p.status);
           ok = __ballot(!ok) == 0;
         } else if (p.emulated) {
           ok = wait_units(p, lr0, lr1, n0, n0 + cols_valid, lane);
@@ -297,9 +360,9 @@ __device__ __forceinline__ void red_compute_role(const RedParams& p, int slot, c
         for (int q = 0; q < Q; ++q)
           if (c[q] < cols_valid) *reinterpret_cast<f32x4*>(p.out + base + (size_t)r[q] * p.n + c[q]) = v[q] + t[q];
       } else {
-        // values per group: G * (world - 1) loads in flight (one value with the eight-wave tile,
-        // whose accumulators leave less room)
-        constexpr int G = T::NW == 8 ? 1 : 2;
+        // values per group: G * (world - 1) loads in flight.  The eight-wave tile's accumulators
+        // leave room for one value; the four-wave tile (one wave per SIMD) takes the whole slab.
+        constexpr int G = T::NW == 8 ? 1 : Q;
         static_assert(Q % G == 0, "slab values split into whole groups");
 #pragma unroll
         for (int g0 = 0; g0 < Q; g0 += G) {
@@ -341,7 +404,9 @@ template <class T>
 __global__ __launch_bounds__(T::NW * 64, 1) void gemm_reduce_kernel(RedParams p) {
   __shared__ __attribute__((aligned(16))) char st0[red_stage_bytes<T>()];
   __shared__ __attribute__((aligned(16))) char st1[red_stage_bytes<T>()];
-  __shared__ __attribute__((aligned(16))) char st2[k_stages<T>() == 3 ? T::STAGE : 16];
+  __shared__ __attribute__((aligned(16))) char st2[k_stages<T>() >= 3 ? T::STAGE : 16];
+  __shared__ __attribute__((aligned(16))) char st3[k_stages<T>() >= 5 ? T::STAGE : 16];
+  __shared__ __attribute__((aligned(16))) char st4[k_stages<T>() >= 5 ? T::STAGE : 16];
   __shared__ int s_ok;
   __shared__ int s_claim;
   const int wg = blockIdx.x;
@@ -350,7 +415,7 @@ __global__ __launch_bounds__(T::NW * 64, 1) void gemm_reduce_kernel(RedParams p)
     red_copy_role<T>(p, wg, st0, st1);
     trace_mark(p.trace, 5);
     __syncthreads();  // the ring's LDS slots become the GEMM's stage buffers
-    red_compute_role<T>(p, -1, st0, st1, st2, &s_ok, &s_claim);  // then help with leftover tiles
+    red_compute_role<T>(p, -1, st0, st1, st2, st3, st4, &s_ok, &s_claim);  // then help with leftover tiles
   } else if (wg < p.n_copy + p.n_reduce) {
     trace_begin(p.trace, ROLE_REDUCE);
     red_reduce_role<T>(p, wg - p.n_copy, &s_ok);
@@ -358,15 +423,27 @@ __global__ __launch_bounds__(T::NW * 64, 1) void gemm_reduce_kernel(RedParams p)
   } else {
     trace_begin(p.trace, ROLE_COMPUTE);
     const int slot = wg - p.n_copy - p.n_reduce;
-    if (slot < p.n_compute) red_compute_role<T>(p, slot, st0, st1, st2, &s_ok, &s_claim);
+    if (slot < p.n_compute) red_compute_role<T>(p, slot, st0, st1, st2, st3, st4, &s_ok, &s_claim);
   }
   trace_end(p.trace);
-  // exit accounting: the last workgroup out re-zeroes the tile counter for the next call (every
-  // workgroup's last claim returned before it counts its exit)
+  // exit accounting: the last workgroup out re-zeroes the claim and band counters for the next
+  // call (every workgroup's last claim returned, and its last band count or band wait finished,
+  // before it counts its exit)
+  __shared__ int s_last;
   __syncthreads();
-  if (threadIdx.x == 0 && atomic_add_agent(p.counters + CTR_RED_EXIT, 1u) == gridDim.x - 1) {
-    __hip_atomic_store(p.counters + CTR_RED_TILE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(p.counters + CTR_RED_EXIT, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) s_last = atomic_add_agent(p.counters + CTR_RED_EXIT, 1u) == gridDim.x - 1;
+  __syncthreads();
+  if (s_last) {
+    if (p.assist) {
+      const int n_own = (p.own_tile_end - p.own_tile_begin) * p.tiles_n;
+      for (int i = threadIdx.x; i < n_own; i += T::NW * 64)
+        __hip_atomic_store(p.counters + CTR_RED_BAND0 + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (threadIdx.x == 0) {
+      __hip_atomic_store(p.counters + CTR_RED_TILE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(p.counters + CTR_RED_PRESUM, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(p.counters + CTR_RED_EXIT, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 

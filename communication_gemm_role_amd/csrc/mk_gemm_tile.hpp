@@ -327,18 +327,66 @@ __device__ __forceinline__ void k_loop2(G& g, int nk, char* st0, char* st1, Pre&
   }
 }
 
-// Stage buffers a tile's K loop uses: three when they fit in the 160 KiB of LDS beside a few KiB
-// of bookkeeping, else two.
-template <class G>
-constexpr int k_stages() {
-  return 3 * G::STAGE <= 150 * 1024 ? 3 : 2;
+// Waits until at most n steps' DMA (D instructions each) of this wave are outstanding, n in [0, 3].
+template <int D>
+__device__ __forceinline__ void wait_steps(int n) {
+  switch (n) {
+    case 3: wait_vm<3 * D>(); break;
+    case 2: wait_vm<2 * D>(); break;
+    case 1: wait_vm<D>(); break;
+    default: wait_vm<0>(); break;
+  }
 }
 
-// The K loop for tile G on its stage count (st2 is unused with two stages).
+// Five-stage K loop over static stage buffers st0..st4, for tiles whose stages are small: the DMA
+// for step q+4 is issued before the MFMAs of step q (into the buffer step q-1 read, which every
+// wave left at the previous barrier), and the end-of-step wait leaves the three newest steps'
+// loads in flight, so a CU has four steps of loads outstanding at the top of each step.
 template <class G, class Pre, class Load, class After>
-__device__ __forceinline__ void k_loop(G& g, int nk, char* st0, char* st1, char* st2, Pre&& before_load, Load&& load,
-                                       After&& before_wait) {
-  if constexpr (k_stages<G>() == 3)
+__device__ __forceinline__ void k_loop5(G& g, int nk, char* st0, char* st1, char* st2, char* st3, char* st4,
+                                        Pre&& before_load, Load&& load, After&& before_wait) {
+  constexpr int S = 5, D = G::A_INSTR + G::B_INSTR;
+  static_assert((S - 2) * D <= 63, "vmcnt is 6 bits");
+  load(0, st0);
+  if (nk > 1) load(1, st1);
+  if (nk > 2) load(2, st2);
+  if (nk > 3) load(3, st3);
+  wait_steps<D>(min(S - 1, nk) - 1);  // step 0 has landed
+  __syncthreads();
+  auto sub = [&](int q, char* cur, char* pf) {
+    if (q >= nk) return;
+    before_load(q);
+    if (q + S - 1 < nk) load(q + S - 1, pf);
+    g.mma(cur);
+    before_wait(q);
+    // step q+1 must have landed: the steps issued after it may stay in flight
+    wait_steps<D>(max(0, min(S - 2, nk - 2 - q)));
+    __syncthreads();
+  };
+  for (int q = 0; q < nk; q += S) {
+    sub(q, st0, st4);
+    sub(q + 1, st1, st0);
+    sub(q + 2, st2, st1);
+    sub(q + 3, st3, st2);
+    sub(q + 4, st4, st3);
+  }
+}
+
+// Stage buffers a tile's K loop uses: five when they fit in 120 KiB (small tiles, whose loads
+// would otherwise be latency-bound), else three when they fit in the 160 KiB of LDS beside a few
+// KiB of bookkeeping, else two.
+template <class G>
+constexpr int k_stages() {
+  return 5 * G::STAGE <= 120 * 1024 ? 5 : 3 * G::STAGE <= 150 * 1024 ? 3 : 2;
+}
+
+// The K loop for tile G on its stage count (buffers past that count are unused).
+template <class G, class Pre, class Load, class After>
+__device__ __forceinline__ void k_loop(G& g, int nk, char* st0, char* st1, char* st2, char* st3, char* st4,
+                                       Pre&& before_load, Load&& load, After&& before_wait) {
+  if constexpr (k_stages<G>() == 5)
+    k_loop5(g, nk, st0, st1, st2, st3, st4, before_load, load, before_wait);
+  else if constexpr (k_stages<G>() == 3)
     k_loop3(g, nk, st0, st1, st2, before_load, load, before_wait);
   else
     k_loop2(g, nk, st0, st1, before_load, load, before_wait);

@@ -28,7 +28,7 @@ int mkh_plan_reduce(size_t n_flags, size_t n_counters, size_t inbox_bytes, int g
       mkh::plan_reduce(ws, o, is_rs, a, b, m, n, k, world, rank, peers, out_buf, outbox, tile_m, tile_n, tile_waves, &P);
   const long long v[] = {P.m_slice, P.p_rows, P.unit_rows, P.unit_cols, P.n_ucols, P.units_per_peer, P.n_units,
                          P.emulated, P.n_order, P.drop_pos, P.n_copy, P.n_reduce, P.n_compute, P.tiles_m, P.tiles_n,
-                         P.own_tile_begin, P.own_tile_end, (long long)P.inbox_need};
+                         P.own_tile_begin, P.own_tile_end, (long long)P.inbox_need, P.assist};
   for (unsigned i = 0; i < sizeof(v) / sizeof(v[0]); ++i) out[i] = v[i];
   return code;
 }

@@ -21,6 +21,7 @@ namespace mkh {
 
 constexpr int kMaxWorld = 8;
 constexpr uint64_t k4G = 1ull << 32;
+constexpr int kCtrBand0 = 128;  // first RS band counter in the context counters (CTR_RED_BAND0)
 
 struct Opts {  // mk_opts with defaults applied by the caller's struct (0 = default)
   int n_copy_wg, n_compute_wg, n_reduce_wg, arrival_mode;
@@ -126,6 +127,7 @@ inline int plan_ag(const Ws& ws, const Opts* o, const void* const* a_shards, int
 struct RedPlan {
   int m_slice, p_rows, unit_rows, unit_cols, n_ucols, units_per_peer, n_units, emulated, n_order, drop_pos;
   int n_copy, n_reduce, n_compute, tiles_m, tiles_n, own_tile_begin, own_tile_end;
+  int assist;  // RS with peers and no reduce workgroups: compute workgroups pre-sum owned tiles
   size_t inbox_need;
 };
 
@@ -190,13 +192,22 @@ inline int plan_reduce(const Ws& ws, const Opts* o, int is_rs, const void* a, co
   if (P->inbox_need > ws.inbox_bytes) return MK_ERR_WORKSPACE;
   if ((size_t)P->n_units + (size_t)P->tiles_m * P->tiles_n > ws.n_flags) return MK_ERR_WORKSPACE;
   if (P->emulated && o && o->arrival_order && o->arrival_len != P->n_order) return MK_ERR_INVALID_ARG;
-  // copy workgroups join the compute role on leftover tiles once their units have landed
-  const int want_copy = P->emulated ? ((o && o->n_copy_wg) ? o->n_copy_wg : 128) : 0;
+  // copy workgroups join the compute role on leftover tiles once their units have landed, so by
+  // default 7/8 of the workgroups not asked to reduce land units (a multiple of 8; measured:
+  // landing ends sooner and the leftover tiles spread over more workgroups)
   const int want_reduce = (world > 1 && o) ? o->n_reduce_wg : 0;
+  const int copy_q = ((ws.grid - want_reduce) * 7 / 8) & ~7;
+  const int copy_d = copy_q > 8 ? copy_q : 8;
+  const int want_copy = P->emulated ? ((o && o->n_copy_wg) ? o->n_copy_wg : copy_d) : 0;
   int code = split_roles(ws.grid, want_copy, want_reduce, o ? o->n_compute_wg : 0, &P->n_copy, &P->n_reduce,
                          &P->n_compute);
   if (code != MK_OK) return code;
   if (world == 1) P->n_reduce = 0;
+  // Without reduce workgroups, RS compute workgroups pre-sum the owned tiles' peer partials in
+  // 64-row bands between their tiles, one band counter per owned tile after the fixed counters.
+  P->assist = (is_rs && world > 1 && P->n_reduce == 0) ? 1 : 0;
+  const size_t n_own = (size_t)(P->own_tile_end - P->own_tile_begin) * P->tiles_n;
+  if (P->assist && kCtrBand0 + n_own > ws.n_counters) return MK_ERR_WORKSPACE;
   return MK_OK;
 }
 
@@ -247,7 +258,11 @@ inline int plan_moe(const Ws& ws, const Opts* o, const void* const* tokens, int 
   P->off_tile_cnt = P->off_chunk_cnt + P->n_chunks * n_local;
   P->counters_need = (size_t)P->off_tile_cnt + (size_t)P->max_mtiles;
   if (P->counters_need > ws.n_counters || ws.n_flags < 1) return MK_ERR_WORKSPACE;
-  const int want_copy = (o && o->n_copy_wg) ? o->n_copy_wg : 128;  // copy workgroups also take leftover tiles
+  // 7/8 of the workgroups route and dispatch, then take grouped-GEMM tiles with the rest: the
+  // m-tiles complete only near the end of the dispatch (token-ordered segments), so the compute
+  // workgroups mostly wait until then (measured best of 96..224)
+  const int copy_q = (ws.grid * 7 / 8) & ~7;
+  const int want_copy = (o && o->n_copy_wg) ? o->n_copy_wg : (copy_q > 8 ? copy_q : 8);
   int nr = 0;
   int code = split_roles(ws.grid, want_copy, 0, o ? o->n_compute_wg : 0, &P->n_copy, &nr, &P->n_compute);
   if (code != MK_OK) return code;

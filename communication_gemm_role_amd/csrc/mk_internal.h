@@ -29,6 +29,8 @@ constexpr int CTR_AG_TILE = 110;   // next leftover AG tile
 constexpr int CTR_AG_EXIT = 111;   // AG workgroups that have exited
 constexpr int CTR_RED_TILE = 112;  // next leftover RS/AR tile
 constexpr int CTR_RED_EXIT = 113;  // RS/AR workgroups that have exited
+constexpr int CTR_RED_PRESUM = 114;  // next RS pre-sum job (64-row band of an owned tile)
+constexpr int CTR_RED_BAND0 = 128;   // RS: bands pre-summed per owned tile, [own tiles] from here
 
 struct AgParams {
   const uint16_t* shards[MK_MAX_WORLD];
@@ -67,6 +69,7 @@ struct RedParams {
   int p_rows;                        // rows of one peer partial (RS: m_slice, AR: m)
   int unit_rows, unit_cols, n_ucols, units_per_peer;
   int n_copy, n_reduce, n_compute;
+  int assist;                        // RS without reduce workgroups: compute workgroups pre-sum
   int emulated, n_order, drop_pos;
   int tiles_m, tiles_n;
   int own_tile_begin, own_tile_end;  // tile rows overlapping the owned slice (RS) or all (AR)

@@ -89,7 +89,9 @@ typedef struct mk_opts {
                            [4] role: 0 copy, 1 compute, 2 reduce
                            [5] [6] [7] phase marks in wall-clock ticks, 0 when not reached:
                              AG, RS/AR copy: [5] its last unit's flag raised
-                             AG, RS/AR compute: [5] first tile's first operands ready
+                             AG, RS/AR compute: [5] first tile's first operands ready;
+                               RS/AR also [6] first tile's K loop done (its epilogue follows)
+                               and [7] first leftover tile claimed (after any pre-sum jobs)
                              RS/AR reduce: [5] its last pre-sum flag raised
                              MoE copy: [5] routing done, [6] scan flag seen, [7] its last
                                dispatched rows counted (before it joins the leftover tiles)

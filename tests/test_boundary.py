@@ -159,13 +159,13 @@ def red(hostlib, is_rs=1, m=8192, n=4096, k=1792, world=8, rank=0, opts=None, ti
         if j != rank and j != drop_peer:
             peers[j] = 0x400000000 + j * 0x10000000
             ob[j] = 0x500000000 + j * 0x10000000
-    out = (ctypes.c_longlong * 20)()
+    out = (ctypes.c_longlong * 24)()
     code = hostlib.mkh_plan_reduce(ctypes.c_size_t(NF), ctypes.c_size_t(NC), ctypes.c_size_t(inbox), GRID,
                                    ctypes.byref(opts) if opts else None, is_rs, P(a), P(0x20000), m, n, k, world,
                                    rank, peers, P(0x30000), ob, tile[0], tile[1], tile[2], out)
     keys = ["m_slice", "p_rows", "unit_rows", "unit_cols", "n_ucols", "units_per_peer", "n_units", "emulated",
             "n_order", "drop_pos", "n_copy", "n_reduce", "n_compute", "tiles_m", "tiles_n", "own_tile_begin",
-            "own_tile_end", "inbox_need"]
+            "own_tile_end", "inbox_need", "assist"]
     return code, dict(zip(keys, list(out)))
 
 
@@ -191,7 +191,21 @@ def test_plan_rs_and_ar(hostlib):
     assert red(hostlib, inbox=1 << 20)[0] == WS  # emulated landing needs the inbox
     assert red(hostlib, inbox=1 << 20, opts=Opts(arrival_mode=RESIDENT))[0] == MK_OK
     code, p = red(hostlib, opts=Opts(n_reduce_wg=32))
-    assert (p["n_copy"], p["n_reduce"], p["n_compute"]) == (128, 32, 96)
+    assert (p["n_copy"], p["n_reduce"], p["n_compute"]) == (192, 32, 32)
+    code, p = red(hostlib)
+    assert (p["n_copy"], p["n_reduce"], p["n_compute"]) == (224, 0, 32)
+    code, p = red(hostlib, opts=Opts(arrival_mode=RESIDENT))
+    assert (p["n_copy"], p["n_reduce"], p["n_compute"]) == (0, 0, 256)
+
+
+def test_plan_rs_presum_assist(hostlib):
+    """RS with peers and no reduce workgroups pre-sums owned tiles in the compute role (one band
+    counter per owned tile after the fixed counters); a reduce role or AllReduce turns it off."""
+    assert red(hostlib)[1]["assist"] == 1
+    assert red(hostlib, opts=Opts(arrival_mode=RESIDENT))[1]["assist"] == 1
+    assert red(hostlib, opts=Opts(n_reduce_wg=16))[1]["assist"] == 0
+    assert red(hostlib, is_rs=0, m=256, n=8192, k=1024, tile=(128, 64, 4))[1]["assist"] == 0
+    assert red(hostlib, world=1)[1]["assist"] == 0
 
 
 def moe(hostlib, world=8, t_local=4096, hidden=4096, E=64, top_k=2, eb=0, nl=8, ffn=1536, cap=65536, opts=None,
@@ -213,6 +227,7 @@ def test_plan_moe(hostlib):
     code, p = moe(hostlib)
     assert code == MK_OK
     assert (p["n_tokens"], p["n_chunks"], p["tiles_n"]) == (32768, 512, 6)
+    assert (p["n_copy"], p["n_compute"]) == (224, 32)  # 7/8 of the workgroups route and dispatch
     assert p["max_mtiles"] == 65536 // 128 + 8 + 1
     assert p["off_tile_cnt"] == 128 + 512 * 8 and p["counters_need"] <= NC
     assert moe(hostlib, top_k=65)[0] == INVALID

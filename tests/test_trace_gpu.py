@@ -104,7 +104,7 @@ def test_trace_rs_small_with_reduce(ctx):
         outs.append(host(own))
         if traced:
             rec = _records(tr)
-            _check_ordered(rec, {0: [5], 1: [5], 2: [5]})
+            _check_ordered(rec, {0: [5], 1: [5, 6, 7], 2: [5]})
             assert set(np.unique(rec[:, 4])) == {0, 1, 2}, "copy, compute and reduce roles all ran"
     assert_exact(outs[1], outs[0], "owned slice with trace vs without")
 
