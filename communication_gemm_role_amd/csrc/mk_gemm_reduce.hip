@@ -302,17 +302,26 @@ __device__ __forceinline__ void red_compute_role(const RedParams& p, int slot, c
       g.dma_a(a_tile + ca, a_tile_bytes - ca, lda_b, dst, wave);
       g.dma_b(b_col + rb, b_col_bytes - rb, ldb_b, dst, wave);
     };
+    int lr0, lr1;
+    owned_rows<T>(p, tm, lr0, lr1);
+    const bool has_owned = lr1 > lr0;
+    // AllReduce with resident partials and no reduce workgroups: on odd XCDs a workgroup sums its
+    // static tile's peer partials into the output before the K loop (HBM reads that overlap the
+    // even XCDs' K loops, which are mostly L2 hits), and its epilogue then only adds P; the even
+    // XCDs keep summing the peers in their epilogues, while the odd ones run their K loops.
+    const bool self_presum = has_owned && !p.is_rs && !p.emulated && p.n_reduce == 0 && first && (slot & 1);
+    if (self_presum) {
+      red_sum_peers<T>(p, lr0, lr1, n0, n0 + cols_valid);
+      wait_mem();
+    }
     g.zero();
     if (first) trace_mark(p.trace, 5);  // operands are resident: ready at once
     k_loop(g, nk, st0, st1, st2, st3, st4, [](int) {}, load_step, [](int) {});
     if (first) trace_mark(p.trace, 6);  // the first tile's K loop is done; its epilogue follows
     first = false;
 
-    int lr0, lr1;
-    owned_rows<T>(p, tm, lr0, lr1);
-    const bool has_owned = lr1 > lr0;
-    const bool presum = has_owned && (p.n_reduce > 0 || p.assist);
-    if (has_owned) {
+    const bool presum = has_owned && (p.n_reduce > 0 || p.assist || self_presum);
+    if (has_owned && !self_presum) {
       // the peer data this tile adds must have landed (emulated) or been pre-summed (reduce role,
       // or every band by the compute workgroups' pre-sum jobs)
       if (wave == 0) {

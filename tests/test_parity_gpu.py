@@ -409,14 +409,21 @@ def test_moe_capacity_overflow(ctx):
 
 
 def test_calls_do_not_leak_state(ctx):
-    """Back-to-back calls of different ops on one context: epoch-tagged flags need no clearing."""
-    from gpu_util import assert_close, host
+    """Back-to-back calls of different ops on one context: epoch-tagged flags need no clearing,
+    and the counters each kernel uses (leftover tiles, RS pre-sum bands, MoE) are left zeroed, so
+    a call never sees a previous call's counts (integer inputs: any stale pre-sum would show)."""
+    from gpu_util import assert_close, assert_exact, host
     mk = _mk()
     s = wl.AG_TINY
     d = wl.gen_ag(s, run=3)
+    sr = wl.RS_SMALL
     for t in range(3):
         _, c = _run_ag(ctx, s, d, order=wl.ag_arrival_order(s, trial=t))
         assert_close(host(c), oracle.ag_gemm(d["a_shards"], d["b"])[1], f"C call {t}")
+        dr = wl.gen_reduce(sr, "rs", run=t, kind="int")
+        own, _ = _run_red(ctx, "rs", sr, dr, mk.MK_ARRIVAL_RESIDENT)
+        own_ref, _ = oracle.gemm_rs(dr["a"], dr["b"], dr["peers"], sr.world, sr.rank)
+        assert_exact(host(own), own_ref.astype(np.float32), f"RS owned slice call {t}")
         sm = wl.MOE_SMALL
         dm = wl.gen_moe(sm, run=t)
         st, *_ = _run_moe(ctx, sm, dm)
