@@ -15,12 +15,13 @@
 //           into segment offsets and per-(chunk, expert) first slots: an exclusive scan in
 //           chunk order, i.e. ascending global token id inside each expert's segment.  It
 //           also numbers the m-tiles of every segment, then raises the scan flag.
-//   copy    after the scan flag, chunks in the caller's arrival order (positions claimed from
-//           a shared counter), a window of up to eight chunks at a time: each wave lists one
-//           chunk's routed (token, slot) rows, then all waves move the rows into their final
-//           slots of x_seg through LDS, and once the window's rows are stored they are added
-//           to their m-tiles' landed-row counters.  A copy workgroup with no chunks left joins
-//           the compute role on the tiles left over after every compute workgroup's first one.
+//   copy    after the scan flag, chunks in the caller's arrival order (copy workgroup cid takes
+//           positions cid, cid + n_copy, ...), a window of up to eight chunks at a time: each
+//           wave lists one chunk's routed (token, slot) rows, then all waves move the rows into
+//           their final slots of x_seg through LDS, and once the window's rows are stored they
+//           are added to their m-tiles' landed-row counters.  A copy workgroup with no chunks
+//           left joins the compute role on the tiles left over after every compute workgroup's
+//           first one.
 //   compute after the scan flag, (m-tile, n-tile) jobs of the ragged grouped GEMM: an m-tile
 //           runs once all of its rows have landed; y[slot] = x_seg[slot] @ w_up[expert].
 // Route/copy workgroups never wait on compute workgroups, and have the lowest ids.  The
@@ -49,7 +50,6 @@ struct MoeShared {
   int ok;
   int is_last;
   int claim;
-  int done;
   int seg_off[MOE_LMAX + 1];
   int tile_base[MOE_LMAX + 1];
   int totals[MOE_LMAX];
@@ -57,8 +57,7 @@ struct MoeShared {
 
 __device__ __forceinline__ uint32_t* moe_misc(const MoeParams& p) { return p.counters + p.off_misc; }
 // misc layout: [0] route-done arrivals, [1] exits, [2 .. 2+n_local] m-tile base per expert (prefix),
-// [MISC_CLAIM] next arrival position to copy, [MISC_TILE] next leftover GEMM tile
-constexpr int MISC_CLAIM = 100;
+// [MISC_TILE] next leftover GEMM tile
 constexpr int MISC_TILE = 101;
 
 // ------------------------------------------------------------------------------------------
@@ -288,20 +287,26 @@ __device__ __forceinline__ void moe_copy_window(const MoeParams& p, const MoeSha
   const int R = sh.pre[n_win];
   const int nb = (R + 8 * RPB - 1) / (8 * RPB);
   const uint32_t row_b = (uint32_t)p.hidden * 2u;
+  // The lookups below are branch-free (selects, a fixed unrolled scan): a branch inside the copy
+  // loop made the compiler drain every outstanding DMA (vmcnt(0)) before each batch's LDS reads,
+  // as it could no longer tell that they read the other slot.
   auto row_at = [&](int r) -> int2 {  // list entry of window row r, or (-1, -1)
-    if (r >= R) return make_int2(-1, -1);
     int j = 0;
-    while (j + 1 < n_win && sh.pre[j + 1] <= r) ++j;
-    return list[j * stride + (r - sh.pre[j])];
+#pragma unroll
+    for (int k = 1; k < MOE_WAVES; ++k) j += (k < n_win && sh.pre[k] <= r) ? 1 : 0;
+    const int idx = min(j * stride + (r - sh.pre[j]), MOE_LIST - 1);
+    const int2 e = list[idx];
+    return r < R ? e : make_int2(-1, -1);
   };
   auto src_of = [&](int t) {
-    if (t < 0) return make_rsrc(p.x_seg, 0u);
-    const int r = t / p.t_local, i = t - r * p.t_local;
-    return make_rsrc(p.tokens[r] + (size_t)i * p.hidden, row_b);
+    const int tt = t < 0 ? 0 : t;
+    const int r = tt / p.t_local, i = tt - r * p.t_local;
+    const uint16_t* row = p.tokens[r] + (size_t)i * p.hidden;
+    return make_rsrc(t < 0 ? (const uint16_t*)p.x_seg : row, t < 0 ? 0u : row_b);
   };
   auto dst_of = [&](int slot) {
-    if (slot < 0 || slot >= p.capacity) return make_rsrc(p.x_seg, 0u);
-    return make_rsrc(p.x_seg + (size_t)slot * p.hidden, row_b);
+    const bool ok = slot >= 0 && slot < p.capacity;
+    return make_rsrc(p.x_seg + (ok ? (size_t)slot * p.hidden : (size_t)0), ok ? row_b : 0u);
   };
   auto dma = [&](int b, char* slot) {
     char* base = slot + wave * 8192;
@@ -351,30 +356,25 @@ __device__ __forceinline__ void moe_copy_window(const MoeParams& p, const MoeSha
   __syncthreads();  // the next window rewrites the lists and chunk tables
 }
 
-// Arrival positions are claimed from a shared counter, one per listing wave, so the positions
-// are taken in the caller's arrival order and a copy workgroup that finishes early takes more.
+// Copy workgroup cid takes the arrival positions cid, cid + n_copy, cid + 2 n_copy, ... (the
+// caller's order, a round of positions across the copy workgroups at a time), in windows of as
+// many chunks as the listing waves and the LDS row list hold: every listing wave lists one chunk,
+// then all waves move the window's rows.  With the default role split a workgroup's positions
+// fit one window, so it pays one listing round trip and one pipeline fill and drain.
 template <int IPR>
-__device__ __forceinline__ void moe_dispatch(const MoeParams& p, MoeShared& sh, int2* list, char* st0, char* st1) {
+__device__ __forceinline__ void moe_dispatch(const MoeParams& p, int cid, MoeShared& sh, int2* list, char* st0,
+                                             char* st1) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // window: one chunk per listing wave, each with room for its largest possible row count; no
-  // more chunks than give every copy workgroup about two windows, so the chunks spread over all
-  // of them (the last window to finish ends the dispatch)
-  const int stride = 64 * min(p.top_k, p.n_local);
-  const int cw = max(1, min(min(MOE_WAVES, MOE_LIST / stride), p.n_chunks / (2 * p.n_copy)));
+  const int stride = 64 * min(p.top_k, p.n_local);  // room for a chunk's largest row count
+  const int cw = max(1, min(MOE_WAVES, MOE_LIST / stride));
+  const int n_mine = cid < p.n_chunks ? (p.n_chunks - cid + p.n_copy - 1) / p.n_copy : 0;
   const __attribute__((address_space(4))) int32_t* order = (const __attribute__((address_space(4))) int32_t*)p.order;
-  if (tid == 0) sh.done = 0;
-  while (true) {
-    if (wave < cw) {
-      int pos = 0;
-      if (lane == 0) pos = (int)atomic_add_agent(moe_misc(p) + MISC_CLAIM, 1u);
-      pos = __builtin_amdgcn_readfirstlane(pos);
-      int c = -1;
-      if (pos < p.n_chunks) {
-        c = (p.emulated && order) ? order[pos] : pos;
-        if (pos + 1 == p.drop_pos || c < 0 || c >= p.n_chunks) c = -1;  // testing: a dropped chunk never lands
-      } else if (lane == 0) {
-        sh.done = 1;  // the queue is exhausted: this is the last window
-      }
+  for (int w0 = 0; w0 < n_mine; w0 += cw) {
+    const int n_win = min(cw, n_mine - w0);
+    if (wave < n_win) {
+      const int pos = cid + (w0 + wave) * p.n_copy;
+      int c = (p.emulated && order) ? order[pos] : pos;
+      if (pos + 1 == p.drop_pos || c < 0 || c >= p.n_chunks) c = -1;  // testing: a dropped chunk never lands
       if (c >= 0) {
         moe_list_chunk(p, sh, list + wave * stride, wave, c, lane);
       } else {
@@ -385,12 +385,10 @@ __device__ __forceinline__ void moe_dispatch(const MoeParams& p, MoeShared& sh, 
     __syncthreads();
     if (tid == 0) {
       sh.pre[0] = 0;
-      for (int j = 0; j < cw; ++j) sh.pre[j + 1] = sh.pre[j] + sh.n_rows[j];
+      for (int j = 0; j < n_win; ++j) sh.pre[j + 1] = sh.pre[j] + sh.n_rows[j];
     }
     __syncthreads();
-    const bool last = sh.done != 0;
-    moe_copy_window<IPR>(p, sh, list, stride, cw, st0, st1);  // ends with a barrier
-    if (last) break;
+    moe_copy_window<IPR>(p, sh, list, stride, n_win, st0, st1);  // ends with a barrier
   }
 }
 
@@ -424,10 +422,10 @@ __device__ __forceinline__ void moe_copy_role(const MoeParams& p, int cid, MoeSh
   __syncthreads();
   // DMA instructions per row and wave, rounded up to a power of two (8 for hidden 4096)
   const int cpr = p.hidden >> 3;  // 16-byte pieces per row
-  if (cpr > 256) moe_dispatch<8>(p, sh, list, st0, st1);
-  else if (cpr > 128) moe_dispatch<4>(p, sh, list, st0, st1);
-  else if (cpr > 64) moe_dispatch<2>(p, sh, list, st0, st1);
-  else moe_dispatch<1>(p, sh, list, st0, st1);
+  if (cpr > 256) moe_dispatch<8>(p, cid, sh, list, st0, st1);
+  else if (cpr > 128) moe_dispatch<4>(p, cid, sh, list, st0, st1);
+  else if (cpr > 64) moe_dispatch<2>(p, cid, sh, list, st0, st1);
+  else moe_dispatch<1>(p, cid, sh, list, st0, st1);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -541,7 +539,6 @@ __global__ __launch_bounds__(MOE_THREADS, 1) void moe_kernel(MoeParams p) {
     if (threadIdx.x == 0) {
       __hip_atomic_store(moe_misc(p) + 0, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(moe_misc(p) + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(moe_misc(p) + MISC_CLAIM, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(moe_misc(p) + MISC_TILE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
