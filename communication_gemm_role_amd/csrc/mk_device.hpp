@@ -152,14 +152,17 @@ __device__ __forceinline__ bool spin_until_eq(const uint32_t* f, uint32_t want, 
   }
 }
 
-// Spin (one lane) until *c >= want (counters).
+// Spin (one lane) until *c >= want (counters).  Counter waits (a grouped-GEMM m-tile's landed
+// rows, an RS owned tile's pre-summed bands) expect a large count and many workgroups wait on the
+// same few counters, so the poll backs off about a microsecond: polling as fast as the flag waits
+// measurably slowed the MoE dispatch's own stores and loads.
 __device__ __forceinline__ bool spin_until_ge(const uint32_t* c, uint32_t want, uint64_t timeout_ticks,
                                               int* status) {
   if (flag_load(c) >= want) return true;
   const uint64_t t0 = wall_ticks();
   int n = 0;
   while (true) {
-    __builtin_amdgcn_s_sleep(1);
+    __builtin_amdgcn_s_sleep(32);
     if (flag_load(c) >= want) return true;
     if ((++n & 15) == 0) {
       if (status_bad(status)) return false;
