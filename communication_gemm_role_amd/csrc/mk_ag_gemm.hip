@@ -1,304 +1,15 @@
-// AllGather + GEMM, one rank's share, as one persistent launch.
+// AllGather + GEMM, one rank's share, as one persistent launch (roles in mk_ag_roles.hpp).
 //
 // Operation (mKernel write-up, news.chathome.org page, five-fused-kernels table,
 // AllGather + GEMM row): each rank holds one row shard of A; while the other shards
 // arrive, the local GEMM consumes A tiles as soon as they land.  Here the other ranks'
 // shards are device buffers and "arrival" is the copy role.
-//
-// Roles (section "mKernel的功能" of the same page: CTAs self-assign roles, a per-shape
-// number of SMs per role):
-//   workgroups [0, n_copy)          copy: for queue positions cid, cid + n_copy, ... of the
-//                                   arrival order, copy that unit of a peer shard into its
-//                                   rows of a_gathered (staged through LDS), then raise the
-//                                   unit's ready flag.
-//                                   Copy workgroups never wait while copying, so every unit lands.
-//   workgroups [n_copy, grid)       compute: 256 x 256 output tiles of C, one static tile per
-//                                   workgroup, then (like copy workgroups once they have copied)
-//                                   tiles left over past n_compute.  In emulated mode the
-//                                   K loop visits K-units (unit_cols columns of K) ready-first:
-//                                   wave 0 polls the flags of the tile's unit rows and picks the
-//                                   lowest-numbered K-unit that has fully landed, one unit ahead
-//                                   of the prefetch, so landed data is consumed immediately.
-// A compute workgroup only ever waits on copy workgroups, which have lower ids and are therefore
-// dispatched first; every wait is bounded by the watchdog.
-#include "mk_internal.h"
-#include "mk_gemm_tile.hpp"
-#include "mk_copy_ring.hpp"
+#include "mk_ag_roles.hpp"
 
 namespace mk {
 
-// 256 x 256 output tile, eight waves of 128 x 64: one k-step moves 64 KiB of operands for 8.4 MFLOP.
-using AgTile = TileGemmDma<256, 256, 2, 4>;
-constexpr int AG_THREADS = AgTile::NW * 64;
-
 int ag_tile_m() { return AgTile::BM; }
 int ag_tile_n() { return AgTile::BN; }
-
-// ------------------------------------------------------------------------------------------
-// copy role
-// ------------------------------------------------------------------------------------------
-__device__ __forceinline__ int ag_identity_unit(const AgParams& p, int pos) {
-  // queue position -> unit id, rank-major then row-major, skipping the local shard when in place
-  const int spr = p.m_shard / p.unit_rows;
-  int ur = pos / p.n_ucols;
-  const int uc = pos - ur * p.n_ucols;
-  if (p.local_in_place && ur >= p.rank * spr) ur += spr;
-  return ur * p.n_ucols + uc;
-}
-
-// Units move through the two-slot LDS ring of mk_copy_ring.hpp (the stage buffers are idle in a
-// copy workgroup): 8 KiB per wave and batch, i.e. 2 units of 128x128, 4 of 64x128 / 128x64 or
-// 8 of 64x64.  IPU is a unit's DMA instructions per wave (1 KiB each).  The arrival order is read
-// through the constant address space, so its loads are scalar, off the vector-memory counter the
-// ring waits on.
-template <int IPU>
-__device__ __forceinline__ void ag_copy_dma(const AgParams& p, int cid, char* st0, char* st1) {
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int cpr = p.unit_cols >> 3;  // 16-byte chunks per unit row
-  const uint32_t ldb = (uint32_t)p.k * 2u;
-  const uint32_t extent = ((uint32_t)(p.unit_rows - 1) * (uint32_t)p.k + (uint32_t)p.unit_cols) * 2u;
-  const int n_units = p.n_urows * p.n_ucols;
-  const int n_mine = p.n_order > cid ? (p.n_order - cid + p.n_copy - 1) / p.n_copy : 0;
-  const __attribute__((address_space(4))) int32_t* order = (const __attribute__((address_space(4))) int32_t*)p.order;
-  uint32_t off[IPU];  // byte offset inside a unit of this lane's chunk, per instruction of the unit
-#pragma unroll
-  for (int i = 0; i < IPU; ++i) {
-    const int c = (wave * IPU + i) * 64 + lane;
-    const int row = c / cpr, cc = c - row * cpr;
-    off[i] = (uint32_t)row * ldb + (uint32_t)cc * 16u;
-  }
-  auto unit_at = [&](int i) -> int {  // i-th unit of this workgroup's queue, or -1
-    if (i >= n_mine) return -1;
-    const int pos = cid + i * p.n_copy;
-    if (pos + 1 == p.drop_pos) return -1;  // testing: this unit never lands
-    const int u = order ? order[pos] : ag_identity_unit(p, pos);
-    return (u < 0 || u >= n_units) ? -1 : u;
-  };
-  auto src_of = [&](int u) {
-    if (u < 0) return make_rsrc(p.ag, 0u);
-    const int ur = u / p.n_ucols, uc = u - ur * p.n_ucols;
-    const int grow = ur * p.unit_rows;
-    const int r = grow / p.m_shard, srow = grow - r * p.m_shard;
-    return make_rsrc(p.shards[r] + (size_t)srow * p.k + (size_t)uc * p.unit_cols, extent);
-  };
-  auto dst_of = [&](int u) {
-    if (u < 0) return make_rsrc(p.ag, 0u);
-    const int ur = u / p.n_ucols, uc = u - ur * p.n_ucols;
-    return make_rsrc(p.ag + (size_t)ur * p.unit_rows * p.k + (size_t)uc * p.unit_cols, extent);
-  };
-  copy_ring<8, IPU>(n_mine, st0, st1, off, unit_at, src_of, dst_of,
-                    [&](int u) { flag_store(&p.flags[u], p.epoch); });
-}
-
-static_assert(AgTile::STAGE >= 65536 && AG_THREADS == 512, "copy slots: 64 KiB stage buffers, 8 waves");
-
-__device__ __forceinline__ void ag_copy_role(const AgParams& p, int cid, char* st0, char* st1) {
-  // DMA instructions per wave per unit: 4 (128x128), 2 (64x128, 128x64), 1 (64x64)
-  const int ipu = (p.unit_rows * p.unit_cols * 2) / (AG_THREADS * 16);
-  if (ipu == 4) ag_copy_dma<4>(p, cid, st0, st1);
-  else if (ipu == 2) ag_copy_dma<2>(p, cid, st0, st1);
-  else ag_copy_dma<1>(p, cid, st0, st1);
-}
-
-// ------------------------------------------------------------------------------------------
-// compute role
-// ------------------------------------------------------------------------------------------
-// Wave 0: is unit row `ur` always present (local shard already in place)?
-__device__ __forceinline__ bool ag_row_local(const AgParams& p, int ur) {
-  const int spr = p.m_shard / p.unit_rows;
-  return p.local_in_place && ur >= p.rank * spr && ur < (p.rank + 1) * spr;
-}
-
-// Wave 0, all lanes: landed-K-unit mask for the tile's unit rows [ur0, ur0 + n_ur).
-__device__ __forceinline__ uint64_t ag_ready_mask(const AgParams& p, int ur0, int n_ur, uint64_t all, int lane) {
-  uint64_t ready = all;
-  for (int q = 0; q < n_ur; ++q) {
-    const int ur = ur0 + q;
-    if (ag_row_local(p, ur)) continue;
-    const bool up = lane < p.n_ucols && flag_load(&p.flags[ur * p.n_ucols + lane]) == p.epoch;
-    ready &= __ballot(up);
-  }
-  return ready;
-}
-
-// Wave 0: pick the next K-unit (lowest landed, not yet scheduled); -1 on timeout or fault.
-// Every value that steers control flow here is wave-uniform (ballots, readfirstlane), so all 64
-// lanes take the same path and every ballot sees every unit's flag.  The scheduled-set mask lives
-// in LDS (volatile: re-read each call) so no register is held across the MFMA loop for it.
-__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return ((uint64_t)hi << 32) | lo;
-}
-
-__device__ __forceinline__ int ag_pick(const AgParams& p, int ur0, int n_ur, uint64_t* s_done, int lane) {
-  volatile uint64_t* vd = s_done;
-  const uint64_t all = (p.n_ucols >= 64) ? ~0ull : ((1ull << p.n_ucols) - 1ull);
-  const uint64_t done = uniform64(*vd);
-  uint64_t cand = ag_ready_mask(p, ur0, n_ur, all, lane) & ~done;
-  if (!cand) {
-    const uint64_t t0 = wall_ticks();
-    int n = 0;
-    while (true) {
-      __builtin_amdgcn_s_sleep(2);
-      cand = ag_ready_mask(p, ur0, n_ur, all, lane) & ~done;
-      if (cand) break;
-      if ((++n & 7) == 0) {
-        const bool bad = __builtin_amdgcn_readfirstlane(status_bad(p.status) ? 1 : 0) != 0;
-        if (bad) return -1;
-        if (wall_ticks() - t0 > p.timeout_ticks) {
-          if (lane == 0) raise_status(p.status, ST_TIMEOUT);
-          return -1;
-        }
-      }
-    }
-  }
-  const int u = __builtin_ctzll(cand);
-  *vd = done | (1ull << u);  // every lane stores the same value
-  return u;
-}
-
-// Wave 0: flags of the tile's non-local unit rows for K-unit `lane`, loaded without waiting (the
-// values are consumed after the step's MFMAs, so the load latency hides behind them).
-struct AgPoll {
-  uint32_t f[4];
-};
-__device__ __forceinline__ void ag_poll_issue(const AgParams& p, int ur0, int n_ur, int lane, AgPoll& pl) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int ur = ur0 + q;
-    pl.f[q] = (q < n_ur && !ag_row_local(p, ur) && lane < p.n_ucols) ? flag_load(&p.flags[ur * p.n_ucols + lane])
-                                                                       : p.epoch;
-  }
-}
-// Wave 0: pick from an issued poll (falling back to the blocking ag_pick when nothing is ready).
-__device__ __forceinline__ int ag_pick_polled(const AgParams& p, int ur0, int n_ur, uint64_t* s_done, int lane,
-                                              const AgPoll& pl) {
-  const uint64_t all = (p.n_ucols >= 64) ? ~0ull : ((1ull << p.n_ucols) - 1ull);
-  uint64_t ready = all;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) ready &= __ballot(lane >= p.n_ucols || pl.f[q] == p.epoch);
-  volatile uint64_t* vd = s_done;
-  const uint64_t done = uniform64(*vd);
-  const uint64_t cand = ready & ~done;
-  if (!cand) return ag_pick(p, ur0, n_ur, s_done, lane);
-  const int u = __builtin_ctzll(cand);
-  *vd = done | (1ull << u);
-  return u;
-}
-
-// Compute role.  Compute workgroup `slot` first runs its static tile (XCD-aware order); tiles from
-// n_compute on are left over and claimed from a shared counter by every workgroup that has
-// finished its own work: compute workgroups after their static tile, copy workgroups (slot -1)
-// after copying.
-__device__ __forceinline__ void ag_compute_role(const AgParams& p, int slot, char* st0, char* st1, char* st2,
-                                                int* s_sched, uint64_t* s_done, int* s_claim) {
-  AgTile g;
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / AgTile::WN, wn = wave % AgTile::WN;
-  const int n_tiles = p.tiles_m * p.tiles_n;
-  const int nk = p.k >> 6;
-  const int spu = p.unit_cols >> 6;  // k-steps per K-unit
-  const int n_ku = p.n_ucols;
-  const int C = p.n_compute;
-  // XCD-aware slot order: workgroup w runs on XCD w % 8; consecutive logical tiles (which share
-  // A row blocks) go to one XCD so its L2 keeps reusing them.
-  const int rs = ((C & 7) == 0) ? (slot & 7) * (C >> 3) + (slot >> 3) : slot;
-  const uint32_t lda_b = (uint32_t)p.k * 2u, ldb_b = (uint32_t)p.n * 2u;
-  g.init(wm, wn, lane, lda_b, ldb_b);
-  // K-units decided before the loop.  Step q+PD is prefetched at the start of step q, so the unit
-  // that starts at step s must be known by the end of step s-PD-1: a decision taken at the end of
-  // step q (after its MFMAs) names the unit starting at step q+1+PD.  The prologue decides the
-  // units that start at steps 0 .. PD, i.e. ceil((PD+1)/spu) of them.
-  constexpr int PD = k_stages<AgTile>() - 1;  // prefetch distance of the K loop
-  const int n_pre = min(n_ku, (PD + spu) / spu);
-
-  int t = (slot >= 0 && rs < n_tiles) ? rs : -1;
-  bool first = slot >= 0;
-  while (true) {
-    if (t < 0) {
-      if (tid == 0) *s_claim = C + (int)atomic_add_agent(p.counters + CTR_AG_TILE, 1u);
-      __syncthreads();
-      t = *s_claim;  // rewritten only after the next tile's barriers
-      if (t >= n_tiles) break;
-    }
-    const int tm = t / p.tiles_n, tn = t - tm * p.tiles_n;
-    const int m0 = tm * AgTile::BM, n0 = tn * AgTile::BN;
-    const int rows_valid = min(AgTile::BM, p.m - m0), cols_valid = min(AgTile::BN, p.n - n0);
-    const int ur0 = m0 / p.unit_rows, n_ur = rows_valid / p.unit_rows;
-    // Operand windows of the k-step: A rows of the tile from the step's first column, B rows of
-    // the step from column n0.  Only scalar values change from step to step.
-    const char* a_tile = reinterpret_cast<const char*>(p.ag + (size_t)m0 * p.k);
-    const uint32_t a_tile_bytes = (uint32_t)rows_valid * lda_b;
-    const char* b_col = reinterpret_cast<const char*>(p.b + n0);
-    const uint32_t b_col_bytes = ((uint32_t)p.k * (uint32_t)p.n - (uint32_t)n0) * 2u;
-    auto load_step = [&](int ks, char* dst) {
-      const uint32_t ca = (uint32_t)ks * 128u;         // byte column of the step in A
-      const uint32_t rb = (uint32_t)ks * 64u * ldb_b;  // byte row of the step in B
-      g.dma_a(a_tile + ca, a_tile_bytes - ca, lda_b, dst, wave);
-      g.dma_b(b_col + rb, b_col_bytes - rb, ldb_b, dst, wave);
-    };
-
-    g.zero();
-    if (p.emulated) {
-      if (wave == 0) {
-        *(volatile uint64_t*)s_done = 0;
-        for (int j = 0; j < n_pre; ++j) {
-          const int u = ag_pick(p, ur0, n_ur, s_done, lane);
-          if (lane == 0) s_sched[j] = u;
-          if (u < 0) break;
-        }
-      }
-      __syncthreads();
-      bool bad = false;
-      for (int j = 0; j < n_pre; ++j) bad |= __builtin_amdgcn_readfirstlane(s_sched[j]) < 0;
-      if (bad) return;  // before any MFMA of this tile
-    }
-    if (first) trace_mark(p.trace, 5);
-    first = false;
-    // A failed wait (watchdog or another workgroup's fault) inside the K loop does not leave the
-    // loop: the remaining steps drain on K-unit 0 (in bounds, result discarded) and the tile's
-    // stores are skipped.  Keeping the loop single-exit keeps the accumulators in AGPRs.
-    bool aborted = false;
-    AgPoll pl;
-    bool polled = false;
-    auto unit_of = [&](int q) -> int {  // K-unit of step q
-      const int j = q / spu;
-      if (!p.emulated) return j;
-      const int u = __builtin_amdgcn_readfirstlane(s_sched[j]);
-      aborted |= u < 0;
-      return u < 0 ? 0 : u;
-    };
-    // the unit decided at the end of step q: the one that starts at step q+1+PD, or -1
-    auto decided_at = [&](int q) -> int {
-      const int s = q + 1 + PD;
-      if (!p.emulated || s >= nk || s % spu) return -1;
-      const int jn = s / spu;
-      return (jn >= n_pre && jn < n_ku) ? jn : -1;
-    };
-    auto before_load = [&](int q) {
-      polled = decided_at(q) >= 0 && wave == 0;
-      if (polled) ag_poll_issue(p, ur0, n_ur, lane, pl);
-    };
-    auto load = [&](int q, char* dst) { load_step(unit_of(q) * spu + q % spu, dst); };
-    auto before_wait = [&](int q) {
-      if (polled) {
-        const int u = ag_pick_polled(p, ur0, n_ur, s_done, lane, pl);
-        if (lane == 0) s_sched[decided_at(q)] = u;
-      }
-    };
-    k_loop(g, nk, st0, st1, st2, st2, st2, before_load, load, before_wait);
-
-    // epilogue: fp32 C tile, staged through LDS into row-contiguous 16-byte stores
-    g.epilogue(st0, st1, wm, wn, lane, wave, [&](int row, int col, f32x4 v) {
-      if (!aborted && row < rows_valid && col < cols_valid)
-        *reinterpret_cast<f32x4*>(p.c + (size_t)(m0 + row) * p.n + (n0 + col)) = v;
-    });
-    __syncthreads();  // the next tile's prologue reuses the LDS
-    if (aborted) break;
-    t = -1;
-  }
-}
 
 __global__ __launch_bounds__(AG_THREADS, 1) void ag_gemm_kernel(AgParams p) {
   __shared__ __attribute__((aligned(16))) char st0[AgTile::STAGE];
