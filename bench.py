@@ -15,7 +15,8 @@ tile pre-resident (slowdown of the fused arrival); two comparators for context o
 BLAS bf16 GEMM of the same shape, and "copy kernels, then the GEMM kernel" as separate
 launches); GEMM+ReduceScatter and GEMM+AllReduce (TFLOP/s and epilogue GB/s, resident and
 with landing); MoE dispatch + grouped GEMM (routed rows, phase spans, grouped-GEMM TFLOP/s
-over its compute span, dispatch GB/s).  Everything is timed with HIP events on the stream
+over its compute span, dispatch GB/s); the MLP block in one launch (AllGather + up-projection,
+gelu, down-projection + ReduceScatter) beside the same three steps as separate calls.  Everything is timed with HIP events on the stream
 the kernels are launched on.
 
 cpu_baseline: the fp64 oracle of the same workload, timed on the host cores.
@@ -91,7 +92,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default="",
                     help="profiling: run only this op (ag, ag_resident, ag_identity, rs, ar, rs_emulated, ar_emulated, "
-                         "moe, vendor, copy)")
+                         "moe, mlp, mlp_resident, mlp_unfused, vendor, copy)")
     return ap.parse_args()
 
 
@@ -334,6 +335,83 @@ def setup_moe(ctx):
     return s, offsets, calls, opts
 
 
+def setup_mlp(ctx, resident: bool = False):
+    """MLP block in one launch (AllGather + up-projection, gelu, down-projection + ReduceScatter),
+    two rotating buffer sets; returns (shape, calls, opts)."""
+    import torch
+    import communication_gemm_role_amd as mk
+    import workloads as wl
+    s = wl.MLP_FULL
+    d = wl.gen_mlp(s, run=0)
+    sh0 = [_bf16(x) for x in d["a_shards"]]
+    bu0, bd0 = _bf16(d["b_up"]), _bf16(d["b_down"])
+    p0 = [None if p is None else _f32(p) for p in d["peers"]]
+    if resident:
+        opts = mk.Opts(arrival_mode=mk.MK_ARRIVAL_RESIDENT)
+    else:
+        opts = mk.Opts(arrival_mode=mk.MK_ARRIVAL_EMULATED, arrival_unit_rows=s.unit_rows,
+                       arrival_unit_cols=s.unit_cols, arrival_order=_i32(wl.ag_arrival_order(s.ag, trial=0)))
+    calls = []
+    for _ in range(2):
+        shards = [x.clone() for x in sh0]
+        bu, bd = bu0.clone(), bd0.clone()
+        peers = [None if p is None else p.clone() for p in p0]
+        ag = torch.empty((s.m, s.k), dtype=torch.bfloat16, device="cuda")
+        if resident:
+            ag.copy_(torch.cat(shards, 0))
+        else:
+            ag[:s.m_shard].copy_(shards[0])
+            shards[0] = ag[:s.m_shard]
+        h = torch.empty((s.m, s.n_up), dtype=torch.bfloat16, device="cuda")
+        own = torch.empty((s.m_shard, s.n_out), device="cuda")
+        ob = [None] + [torch.empty((s.m_shard, s.n_out), device="cuda") for _ in range(1, s.world)]
+        calls.append(lambda sh=shards, bu=bu, bd=bd, pe=peers, ag=ag, h=h, own=own, ob=ob:
+                     mk.mk_mlp_ag_rs(ctx, sh, s.world, 0, bu, bd, pe, ag, h, own, ob, opts=opts))
+    return s, calls, opts
+
+
+def setup_mlp_unfused(ctx):
+    """Comparator: the same block as three steps, mk_ag_gemm (fp32 U), torch's gelu and bf16
+    conversion, then mk_gemm_rs on H (peers' partials resident)."""
+    import torch
+    import communication_gemm_role_amd as mk
+    import workloads as wl
+    s = wl.MLP_FULL
+    d = wl.gen_mlp(s, run=0)
+    sh0 = [_bf16(x) for x in d["a_shards"]]
+    bu0, bd0 = _bf16(d["b_up"]), _bf16(d["b_down"])
+    p0 = [None if p is None else _f32(p) for p in d["peers"]]
+    o_ag = mk.Opts(arrival_mode=mk.MK_ARRIVAL_EMULATED, arrival_unit_rows=s.unit_rows, arrival_unit_cols=s.unit_cols,
+                   arrival_order=_i32(wl.ag_arrival_order(s.ag, trial=0)))
+    o_rs = mk.Opts(arrival_mode=mk.MK_ARRIVAL_RESIDENT)
+    calls = []
+    for _ in range(2):
+        shards = [x.clone() for x in sh0]
+        bu, bd = bu0.clone(), bd0.clone()
+        peers = [None if p is None else p.clone() for p in p0]
+        ag = torch.empty((s.m, s.k), dtype=torch.bfloat16, device="cuda")
+        ag[:s.m_shard].copy_(shards[0])
+        shards[0] = ag[:s.m_shard]
+        u = torch.empty((s.m, s.n_up), device="cuda")
+        own = torch.empty((s.m_shard, s.n_out), device="cuda")
+        ob = [None] + [torch.empty((s.m_shard, s.n_out), device="cuda") for _ in range(1, s.world)]
+
+        def step(sh=shards, bu=bu, bd=bd, pe=peers, ag=ag, u=u, own=own, ob=ob):
+            mk.mk_ag_gemm(ctx, sh, s.world, 0, bu, ag, u, opts=o_ag)
+            h = torch.nn.functional.gelu(u).to(torch.bfloat16)
+            mk.mk_gemm_rs(ctx, h, bd, s.world, 0, pe, own, ob, opts=o_rs)
+        calls.append(step)
+    return s, calls
+
+
+def mlp_trace_summary(rec) -> dict:
+    t0 = rec[:, 0].min()
+    up = rec[:, 6]
+    return {"kernel_span_us": round(us(rec[:, 2].max() - t0), 2), "shader_clock_GHz": round(clock_ghz(rec), 3),
+            "up_projection_done_us": {"min": round(us(up.min() - t0), 2), "median": round(us(np.median(up) - t0), 2),
+                                      "max": round(us(up.max() - t0), 2)}}
+
+
 def cpu_info() -> dict:
     model = platform.processor() or ""
     try:
@@ -430,6 +508,10 @@ def main():
             _, calls, _ = setup_reduce(ctx, a.only[:2], emulated=True)
         elif a.only == "moe":
             _, _, calls, _ = setup_moe(ctx)
+        elif a.only in ("mlp", "mlp_resident"):
+            _, calls, _ = setup_mlp(ctx, resident=a.only == "mlp_resident")
+        elif a.only == "mlp_unfused":
+            _, calls = setup_mlp_unfused(ctx)
         elif a.only == "vendor":
             _, calls = setup_vendor_gemm()
         elif a.only == "copy":
@@ -534,6 +616,26 @@ def main():
                       "tflops": round(sm.flops(R) / (tm["kernel_ms"] * 1e-3) / 1e12, 2),
                       "trace": moe_trace_summary(mrec, sm, R)}
         del cm
+        torch.cuda.empty_cache()
+        ms_, cmlp, mlopts = setup_mlp(ctx)
+        tml = time_stats(cmlp, 100, 3, a.settle_ms)
+        mlrec = traced_call(ctx, cmlp, mlopts)
+        del cmlp
+        _, cmlr, _ = setup_mlp(ctx, resident=True)
+        tmr = time_stats(cmlr, 100, 3, a.settle_ms)
+        del cmlr
+        _, cmu = setup_mlp_unfused(ctx)
+        tmu = time_stats(cmu, 100, 3, a.settle_ms)
+        del cmu
+        torch.cuda.empty_cache()
+        sec["mlp"] = {"kernel_ms": round(tml["kernel_ms"], 5),
+                      "tflops": round(ms_.flops / (tml["kernel_ms"] * 1e-3) / 1e12, 2),
+                      "resident_kernel_ms": round(tmr["kernel_ms"], 5),
+                      "unfused_ms": round(tmu["kernel_ms"], 5),
+                      "unfused_tflops": round(ms_.flops / (tmu["kernel_ms"] * 1e-3) / 1e12, 2),
+                      "trace": mlp_trace_summary(mlrec),
+                      "note": "W=8 emulated ranks, A shards 1024x4096, B_up 4096x1792, B_down 1792x4096, peers' "
+                              "partials resident; unfused = mk_ag_gemm, torch gelu + bf16, mk_gemm_rs"}
         st = ctx.status()
         if st != mk.MK_OK:
             raise SystemExit(f"device status {st}: {mk.strerror(st)}")

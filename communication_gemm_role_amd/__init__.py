@@ -30,7 +30,7 @@ MK_ARRIVAL_RESIDENT = 1
 MK_ARRIVAL_EMULATED = 2
 
 EXPORTED = ["mk_ctx_create", "mk_ctx_destroy", "mk_ctx_status", "mk_ctx_reset", "mk_ctx_grid", "mk_strerror",
-            "mk_selftest_flags", "mk_ag_gemm", "mk_gemm_rs", "mk_gemm_ar", "mk_moe_dispatch_gemm"]
+            "mk_selftest_flags", "mk_ag_gemm", "mk_gemm_rs", "mk_gemm_ar", "mk_moe_dispatch_gemm", "mk_mlp_ag_rs"]
 
 
 class MkError(RuntimeError):
@@ -118,8 +118,10 @@ def lib() -> ctypes.CDLL:
         L.mk_gemm_ar.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp]
         L.mk_moe_dispatch_gemm.argtypes = [vp, vp, vp, i, i, i, vp, vp, i, i, i, i, vp, i, vp, vp, vp, vp, vp, i, vp]
         L.mk_selftest_flags.argtypes = [i, i, i, i, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+        L.mk_mlp_ag_rs.argtypes = [vp, vp, vp, i, i, i, i, vp, i, vp, i, vp, vp, vp, vp, vp, vp]
         for name in ("mk_ctx_create", "mk_ctx_destroy", "mk_ctx_status", "mk_ctx_reset", "mk_ctx_grid",
-                     "mk_selftest_flags", "mk_ag_gemm", "mk_gemm_rs", "mk_gemm_ar", "mk_moe_dispatch_gemm"):
+                     "mk_selftest_flags", "mk_ag_gemm", "mk_gemm_rs", "mk_gemm_ar", "mk_moe_dispatch_gemm",
+                     "mk_mlp_ag_rs"):
             getattr(L, name).restype = i
         _lib_handle = L
     return _lib_handle
@@ -298,6 +300,34 @@ def mk_moe_dispatch_gemm(ctx: Context, tokens: Sequence, logits, bias, top_k: in
           "mk_moe_dispatch_gemm")
 
 
-__all__ = ["Context", "Opts", "MkError", "mk_selftest_flags", "mk_ag_gemm", "mk_gemm_rs", "mk_gemm_ar", "mk_moe_dispatch_gemm", "lib",
+def mk_mlp_ag_rs(ctx: Context, a_shards: Sequence, world: int, rank: int, b_up, b_down, peer_partials: Sequence,
+                 a_gathered, h, owned_out, outbox: Sequence, opts: Optional[Opts] = None, stream=None) -> None:
+    """MLP block in one launch (see mk.h): AllGather + up-projection, gelu, down-projection +
+    ReduceScatter.  a_shards as in mk_ag_gemm; b_up [k, n_up], b_down [n_up, n_out] bf16;
+    peer_partials[j] [m_shard, n_out] fp32 (None at rank); a_gathered [world*m_shard, k] bf16,
+    h [world*m_shard, n_up] bf16, owned_out [m_shard, n_out] fp32 and outbox[j] [m_shard, n_out]
+    fp32 (None at rank) are outputs."""
+    _check(b_up, "bf16", "b_up")
+    _check(b_down, "bf16", "b_down")
+    _check(a_gathered, "bf16", "a_gathered")
+    _check(h, "bf16", "h")
+    _check(owned_out, "f32", "owned_out")
+    k, n_up = b_up.shape
+    n_out = b_down.shape[1]
+    m = a_gathered.shape[0]
+    if (a_gathered.shape[1] != k or b_down.shape[0] != n_up or h.shape != (m, n_up) or m % world
+            or owned_out.shape != (m // world, n_out)):
+        raise ValueError("shape mismatch")
+    shards = _ptr_array(a_shards, "bf16", "a_shards") if a_shards is not None else None
+    peers = _ptr_array(peer_partials, "f32", "peer_partials")
+    ob = _ptr_array(outbox, "f32", "outbox")
+    op, _keep = _opts_ptr(opts, ctx)
+    _call(lib().mk_mlp_ag_rs(ctx.handle, _stream_ptr(stream), shards, world, rank, m // world, k, b_up.data_ptr(),
+                             n_up, b_down.data_ptr(), n_out, peers, a_gathered.data_ptr(), h.data_ptr(),
+                             owned_out.data_ptr(), ob, op), "mk_mlp_ag_rs")
+
+
+__all__ = ["Context", "Opts", "MkError", "mk_selftest_flags", "mk_ag_gemm", "mk_gemm_rs", "mk_gemm_ar", "mk_moe_dispatch_gemm",
+           "mk_mlp_ag_rs", "lib",
            "strerror", "MK_OK", "MK_ERR_INVALID_ARG", "MK_ERR_UNSUPPORTED", "MK_ERR_WORKSPACE", "MK_ERR_HIP",
            "MK_ERR_TIMEOUT", "MK_ERR_CAPACITY", "MK_ARRIVAL_RESIDENT", "MK_ARRIVAL_EMULATED", "EXPORTED"]

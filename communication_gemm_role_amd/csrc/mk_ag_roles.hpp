@@ -190,6 +190,20 @@ __device__ __forceinline__ int ag_pick_polled(const AgParams& p, int ur0, int n_
 // n_compute on are left over and claimed from a shared counter by every workgroup that has
 // finished its own work: compute workgroups after their static tile, copy workgroups (slot -1)
 // after copying.
+// The MLP block's activation: gelu(x) = x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2)), in fp32.
+__device__ __forceinline__ float gelu_f32(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// EPI 0: fp32 C tile.  EPI 1 (MLP up-projection): H = bf16(gelu(acc)), write-through (the
+// down-projection reads it from other XCDs), then h_ready[tile row] += 1 once every wave's stores
+// of the tile have completed.
+template <int EPI = 0>
 __device__ __forceinline__ void ag_compute_role(const AgParams& p, int slot, char* st0, char* st1, char* st2,
                                                 int* s_sched, uint64_t* s_done, int* s_claim) {
   AgTile g;
@@ -288,12 +302,26 @@ __device__ __forceinline__ void ag_compute_role(const AgParams& p, int slot, cha
     };
     k_loop(g, nk, st0, st1, st2, st2, st2, before_load, load, before_wait);
 
-    // epilogue: fp32 C tile, staged through LDS into row-contiguous 16-byte stores
-    g.epilogue(st0, st1, wm, wn, lane, wave, [&](int row, int col, f32x4 v) {
-      if (!aborted && row < rows_valid && col < cols_valid)
-        *reinterpret_cast<f32x4*>(p.c + (size_t)(m0 + row) * p.n + (n0 + col)) = v;
-    });
-    __syncthreads();  // the next tile's prologue reuses the LDS
+    // epilogue: the tile staged through LDS into row-contiguous 16-byte stores
+    if constexpr (EPI == 0) {
+      g.epilogue(st0, st1, wm, wn, lane, wave, [&](int row, int col, f32x4 v) {
+        if (!aborted && row < rows_valid && col < cols_valid)
+          *reinterpret_cast<f32x4*>(p.c + (size_t)(m0 + row) * p.n + (n0 + col)) = v;
+      });
+      __syncthreads();  // the next tile's prologue reuses the LDS
+    } else {
+      const auto h_rs = make_rsrc(p.h, (uint32_t)p.m * (uint32_t)p.n * 2u);
+      g.epilogue(st0, st1, wm, wn, lane, wave, [&](int row, int col, f32x4 v) {
+        if (!aborted && row < rows_valid && col < cols_valid) {
+          const uint32_t b0 = bf16_rne(gelu_f32(v[0])), b1 = bf16_rne(gelu_f32(v[1]));
+          const uint32_t b2 = bf16_rne(gelu_f32(v[2])), b3 = bf16_rne(gelu_f32(v[3]));
+          bstore8_sc1(h_rs, (uint32_t)((m0 + row) * p.n + (n0 + col)) * 2u, u32x2{b0 | (b1 << 16), b2 | (b3 << 16)});
+        }
+      });
+      wait_mem();       // this tile's H stores have completed ...
+      __syncthreads();  // ... in every wave (and the next tile's prologue reuses the LDS)
+      if (!aborted && tid == 0) atomic_add_agent(p.h_ready + tm, 1u);
+    }
     if (aborted) break;
     t = -1;
   }

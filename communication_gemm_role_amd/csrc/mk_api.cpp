@@ -18,6 +18,7 @@ constexpr size_t kStatusBytes = 256;
 constexpr size_t kCounters = 1u << 20;  // 4 MiB of u32 counters
 constexpr size_t kFlags = 1u << 20;     // 4 MiB of u32 flags
 static_assert(mkh::kCtrBand0 == mk::CTR_RED_BAND0, "host and kernel agree on the RS band counters");
+static_assert(mkh::kCtrHready0 == mk::CTR_MLP_HREADY0, "host and kernel agree on the MLP row-block counters");
 
 struct DeviceGuard {  // make ctx->device current for the duration of a call
   int prev = -1;
@@ -282,6 +283,95 @@ int mk_gemm_rs(mk_ctx* ctx, void* stream, const uint16_t* a, const uint16_t* b, 
 int mk_gemm_ar(mk_ctx* ctx, void* stream, const uint16_t* a, const uint16_t* b, int m, int n, int k, int world,
                int rank, const float* const* peer_partials, float* out, const mk_opts* opts) {
   return gemm_reduce(0, ctx, stream, a, b, m, n, k, world, rank, peer_partials, out, nullptr, opts);
+}
+
+int mk_mlp_ag_rs(mk_ctx* ctx, void* stream, const uint16_t* const* a_shards, int world, int rank, int m_shard, int k,
+                 const uint16_t* b_up, int n_up, const uint16_t* b_down, int n_out, const float* const* peer_partials,
+                 uint16_t* a_gathered, uint16_t* h, float* owned_out, float* const* outbox, const mk_opts* opts) {
+  if (!ctx) return MK_ERR_INVALID_ARG;
+  const mkh::Opts o = to_opts(opts);
+  const int M = world * m_shard;  // validated by the plan; only picks the tile shapes here
+  mkh::MlpPlan P;
+  int code = mkh::plan_mlp(ws_of(ctx), opts ? &o : nullptr, (const void* const*)a_shards, world, rank, m_shard, k,
+                           b_up, n_up, b_down, n_out, (const void* const*)peer_partials, a_gathered, h, owned_out,
+                           (void* const*)outbox, mk::ag_tile_m(), mk::ag_tile_n(), mk::red_tile_m(M, n_out),
+                           mk::red_tile_n(M, n_out), mk::red_tile_waves(M, n_out), &P);
+  if (code != MK_OK) return code;
+  DeviceGuard g(ctx->device);
+  if (!g.ok) return MK_ERR_HIP;
+  hipStream_t s = (hipStream_t)stream;
+  if ((code = next_epoch(ctx, s)) != MK_OK) return code;
+  mk::MlpParams p;
+  memset(&p, 0, sizeof(p));
+  mk::AgParams& a = p.ag;
+  for (int r = 0; r < world; ++r) a.shards[r] = a_shards ? a_shards[r] : nullptr;
+  a.b = b_up;
+  a.ag = a_gathered;
+  a.c = nullptr;
+  a.h = h;
+  a.h_ready = ctx->counters + mk::CTR_MLP_HREADY0;
+  a.order = (P.ag.emulated && opts) ? (const int32_t*)opts->arrival_order : nullptr;
+  a.flags = ctx->flags;
+  a.status = ctx->status;
+  a.world = world;
+  a.rank = rank;
+  a.m_shard = m_shard;
+  a.m = P.ag.m;
+  a.n = n_up;
+  a.k = k;
+  a.unit_rows = P.ag.unit_rows;
+  a.unit_cols = P.ag.unit_cols;
+  a.n_ucols = P.ag.n_ucols;
+  a.n_urows = P.ag.n_urows;
+  a.n_copy = P.ag.n_copy;
+  a.n_compute = P.ag.n_compute;
+  a.emulated = P.ag.emulated;
+  a.local_in_place = P.ag.local_in_place;
+  a.n_order = P.ag.n_order;
+  a.drop_pos = P.ag.drop_pos;
+  a.tiles_m = P.ag.tiles_m;
+  a.tiles_n = P.ag.tiles_n;
+  a.epoch = ctx->epoch;
+  a.timeout_ticks = timeout_ticks(opts);
+  a.trace = opts ? opts->trace : nullptr;
+  a.counters = ctx->counters;
+  mk::RedParams& d = p.red;
+  d.a = h;
+  d.b = b_down;
+  for (int j = 0; j < world; ++j) {
+    d.peers[j] = (j == rank || !peer_partials) ? nullptr : peer_partials[j];
+    d.outbox[j] = (j == rank || !outbox) ? nullptr : outbox[j];
+  }
+  d.out = owned_out;
+  d.inbox = (float*)ctx->inbox;
+  d.flags = ctx->flags;
+  d.presum_flags = ctx->flags + P.ag.n_urows * P.ag.n_ucols;
+  d.status = ctx->status;
+  d.is_rs = 1;
+  d.m = M;
+  d.n = n_out;
+  d.k = n_up;
+  d.world = world;
+  d.rank = rank;
+  d.m_slice = P.red.m_slice;
+  d.p_rows = P.red.p_rows;
+  d.unit_rows = P.red.unit_rows;
+  d.unit_cols = P.red.unit_cols;
+  d.n_ucols = P.red.n_ucols;
+  d.units_per_peer = P.red.units_per_peer;
+  d.n_compute = P.red.n_compute;
+  d.assist = P.red.assist;
+  d.tiles_m = P.red.tiles_m;
+  d.tiles_n = P.red.tiles_n;
+  d.own_tile_begin = P.red.own_tile_begin;
+  d.own_tile_end = P.red.own_tile_end;
+  d.epoch = ctx->epoch;
+  d.timeout_ticks = timeout_ticks(opts);
+  d.trace = nullptr;  // the trace records keep phase 1's marks
+  d.counters = ctx->counters;
+  d.a_ready = ctx->counters + mk::CTR_MLP_HREADY0;
+  d.a_ready_need = (uint32_t)P.ag.tiles_n;
+  return mk::launch_mlp(p, ws_of(ctx).grid, s) == hipSuccess ? MK_OK : MK_ERR_HIP;
 }
 
 int mk_moe_dispatch_gemm(mk_ctx* ctx, void* stream, const uint16_t* const* tokens, int world, int t_local,

@@ -64,6 +64,9 @@ __device__ __forceinline__ void bstore16(__amdgpu_buffer_rsrc_t r, uint32_t off,
 __device__ __forceinline__ void bstore16_sc1(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, CP_SC1);
 }
+__device__ __forceinline__ void bstore8_sc1(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, CP_SC1);
+}
 __device__ __forceinline__ void bstore4(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v) {
   __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, CP_DEFAULT);
 }

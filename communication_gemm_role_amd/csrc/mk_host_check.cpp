@@ -33,6 +33,22 @@ int mkh_plan_reduce(size_t n_flags, size_t n_counters, size_t inbox_bytes, int g
   return code;
 }
 
+int mkh_plan_mlp(size_t n_flags, size_t n_counters, size_t inbox_bytes, int grid, const mkh::Opts* o,
+                 const void* const* a_shards, int world, int rank, int m_shard, int k, const void* b_up, int n_up,
+                 const void* b_down, int n_out, const void* const* peers, const void* a_gathered, const void* h,
+                 const void* out, void* const* outbox, long long* out_fields) {
+  mkh::Ws ws{n_flags, n_counters, inbox_bytes, grid};
+  mkh::MlpPlan P{};
+  const int M = world * m_shard;
+  const int red_m = M > 512 ? 256 : 128, red_n = M > 512 ? 256 : 64, red_w = M > 512 ? 8 : 4;  // the kernels' tiles
+  const int code = mkh::plan_mlp(ws, o, a_shards, world, rank, m_shard, k, b_up, n_up, b_down, n_out, peers,
+                                 a_gathered, h, out, outbox, 256, 256, red_m, red_n, red_w, &P);
+  const long long v[] = {P.ag.n_copy, P.ag.n_compute, P.ag.tiles_m, P.ag.tiles_n, P.red.n_compute, P.red.tiles_m,
+                         P.red.tiles_n, P.red.own_tile_begin, P.red.own_tile_end, P.red.assist};
+  for (unsigned i = 0; i < sizeof(v) / sizeof(v[0]); ++i) out_fields[i] = v[i];
+  return code;
+}
+
 int mkh_plan_moe(size_t n_flags, size_t n_counters, size_t inbox_bytes, int grid, const mkh::Opts* o,
                  const void* const* tokens, int world, int t_local, int hidden, const void* logits, const void* bias,
                  int n_experts, int top_k, int expert_begin, int n_local, const void* w_up, int ffn,

@@ -4,6 +4,7 @@
 #pragma once
 #include <stddef.h>
 #include <stdint.h>
+#include <string.h>
 
 #ifndef MK_OK
 #define MK_OK 0
@@ -22,6 +23,7 @@ namespace mkh {
 constexpr int kMaxWorld = 8;
 constexpr uint64_t k4G = 1ull << 32;
 constexpr int kCtrBand0 = 128;  // first RS band counter in the context counters (CTR_RED_BAND0)
+constexpr int kCtrHready0 = 4096;  // first MLP row-block counter of H (CTR_MLP_HREADY0)
 
 struct Opts {  // mk_opts with defaults applied by the caller's struct (0 = default)
   int n_copy_wg, n_compute_wg, n_reduce_wg, arrival_mode;
@@ -208,6 +210,40 @@ inline int plan_reduce(const Ws& ws, const Opts* o, int is_rs, const void* a, co
   P->assist = (is_rs && world > 1 && P->n_reduce == 0) ? 1 : 0;
   const size_t n_own = (size_t)(P->own_tile_end - P->own_tile_begin) * P->tiles_n;
   if (P->assist && kCtrBand0 + n_own > ws.n_counters) return MK_ERR_WORKSPACE;
+  return MK_OK;
+}
+
+// ---- MLP block: AllGather + up-projection, gelu, down-projection + ReduceScatter ----------------
+// The first phase is planned as mk_ag_gemm over [world*m_shard, k] @ [k, n_up] (its arrival mode,
+// units and role split as given), the second as a resident mk_gemm_rs over H [world*m_shard, n_up]
+// @ [n_up, n_out] on every workgroup; both use 256-row tiles, so a tile row of the second phase is
+// one row block of H.
+struct MlpPlan {
+  AgPlan ag;
+  RedPlan red;
+};
+
+inline int plan_mlp(const Ws& ws, const Opts* o, const void* const* a_shards, int world, int rank, int m_shard, int k,
+                    const void* b_up, int n_up, const void* b_down, int n_out, const void* const* peers,
+                    const void* a_gathered, const void* h, const void* out, void* const* outbox, int ag_tile_m,
+                    int ag_tile_n, int red_tile_m, int red_tile_n, int red_tile_waves, MlpPlan* P) {
+  if (!h || !b_down) return MK_ERR_INVALID_ARG;
+  int code = plan_ag(ws, o, a_shards, world, rank, m_shard, k, b_up, n_up, a_gathered, h, ag_tile_m, ag_tile_n, &P->ag);
+  if (code != MK_OK) return code;
+  // workgroups beyond the up-projection's roles go straight to the down-projection
+  if (P->ag.n_copy + P->ag.n_compute > ws.grid) return MK_ERR_UNSUPPORTED;
+  Opts r;
+  memset(&r, 0, sizeof(r));
+  r.arrival_mode = MK_ARRIVAL_RESIDENT;  // the peers' partials of the down-projection are resident
+  r.timeout_us = o ? o->timeout_us : 0;
+  code = plan_reduce(ws, &r, 1, h, b_down, world * m_shard, n_out, n_up, world, rank, peers, out, outbox, red_tile_m,
+                     red_tile_n, red_tile_waves, &P->red);
+  if (code != MK_OK) return code;
+  if (red_tile_m != ag_tile_m || red_tile_waves * 64 != 512) return MK_ERR_UNSUPPORTED;  // one H block per tile row
+  if (P->red.n_copy || P->red.n_reduce || P->red.n_compute != ws.grid) return MK_ERR_UNSUPPORTED;
+  const size_t n_own = (size_t)(P->red.own_tile_end - P->red.own_tile_begin) * P->red.tiles_n;
+  if (kCtrBand0 + n_own > (size_t)kCtrHready0 || kCtrHready0 + (size_t)P->ag.tiles_m > ws.n_counters)
+    return MK_ERR_WORKSPACE;
   return MK_OK;
 }
 

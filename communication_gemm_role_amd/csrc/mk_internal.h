@@ -31,6 +31,8 @@ constexpr int CTR_RED_TILE = 112;  // next leftover RS/AR tile
 constexpr int CTR_RED_EXIT = 113;  // RS/AR workgroups that have exited
 constexpr int CTR_RED_PRESUM = 114;  // next RS pre-sum job (64-row band of an owned tile)
 constexpr int CTR_RED_BAND0 = 128;   // RS: bands pre-summed per owned tile, [own tiles] from here
+constexpr int CTR_MLP_EXIT = 115;    // MLP workgroups that have exited
+constexpr int CTR_MLP_HREADY0 = 4096;  // MLP: up-projection tiles stored per 256-row block of H
 
 struct AgParams {
   const uint16_t* shards[MK_MAX_WORLD];
@@ -50,6 +52,10 @@ struct AgParams {
   uint32_t epoch;
   uint64_t timeout_ticks;
   uint64_t* trace;  // per-workgroup trace records, or nullptr
+  // MLP up-projection (the MLP kernel only): the epilogue stores H = bf16(gelu(acc)) instead of
+  // C and adds one to h_ready[tile row] once a tile's stores have completed
+  uint16_t* h;
+  uint32_t* h_ready;
 };
 
 struct RedParams {
@@ -76,6 +82,18 @@ struct RedParams {
   uint32_t epoch;
   uint64_t timeout_ticks;
   uint64_t* trace;  // per-workgroup trace records, or nullptr
+  // A produced in the same launch (the MLP kernel's H): a tile of tile row tm waits until
+  // a_ready[tm] >= a_ready_need before its K loop; nullptr when A is an input
+  const uint32_t* a_ready;
+  uint32_t a_ready_need;
+};
+
+// MLP block (up-projection with AllGather, activation, down-projection with ReduceScatter) in one
+// launch: the AllGather+GEMM roles produce H, then every workgroup runs the GEMM+RS compute role
+// on it.
+struct MlpParams {
+  AgParams ag;
+  RedParams red;
 };
 
 struct MoeParams {
@@ -110,6 +128,7 @@ struct MoeParams {
 hipError_t launch_ag_gemm(const AgParams& p, int grid, hipStream_t s);
 hipError_t launch_gemm_reduce(const RedParams& p, int grid, hipStream_t s);
 hipError_t launch_moe(const MoeParams& p, int grid, hipStream_t s);
+hipError_t launch_mlp(const MlpParams& p, int grid, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t s);
 
 // Tile sizes the host needs for scheduling and validation

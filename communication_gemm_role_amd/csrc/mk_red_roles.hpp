@@ -313,6 +313,11 @@ __device__ __forceinline__ void red_compute_role(const RedParams& p, int slot, c
       red_sum_peers<T>(p, lr0, lr1, n0, n0 + cols_valid);
       wait_mem();
     }
+    if (p.a_ready) {  // A is produced in this launch (the MLP kernel's H): its rows must be complete
+      if (tid == 0) *s_ok = spin_until_ge(p.a_ready + tm, p.a_ready_need, p.timeout_ticks, p.status);
+      __syncthreads();
+      if (!*s_ok) return;
+    }
     g.zero();
     if (first) trace_mark(p.trace, 5);  // operands are resident: ready at once
     k_loop(g, nk, st0, st1, st2, st3, st4, [](int) {}, load_step, [](int) {});

@@ -12,6 +12,11 @@
  *   mk_gemm_ar            GEMM + AllReduce
  *   mk_moe_dispatch_gemm  MoE token dispatch + per-expert grouped GEMM
  *
+ * and, from the same page's roadmap section (the transformer-layer megakernel as the next
+ * step), the MLP block built from two of them in one launch:
+ *
+ *   mk_mlp_ag_rs          AllGather + up-projection GEMM, gelu, down-projection GEMM + ReduceScatter
+ *
  * Each call is ONE kernel launch.  Inside it, workgroups take a role from their
  * id and a per-shape split: copy (lands peer data in a given order and raises a
  * per-unit ready flag), compute (bf16 MFMA tiles with fp32 accumulation, which
@@ -202,6 +207,30 @@ int mk_moe_dispatch_gemm(mk_ctx* ctx, void* stream, const uint16_t* const* token
                          int expert_begin, int n_local_experts, const uint16_t* w_up, int ffn, int32_t* topk_idx,
                          int32_t* seg_offsets, int32_t* seg_token, uint16_t* x_seg, float* y, int capacity_rows,
                          const mk_opts* opts);
+
+/* ---- MLP block: AllGather + GEMM, gelu, GEMM + ReduceScatter ---------------------------
+ * Roadmap section of the same page (the transformer-layer megakernel) built from the AllGather +
+ * GEMM and GEMM + ReduceScatter rows of the five-fused-kernels table, in ONE launch: the
+ * column-parallel up-projection consumes A tiles as they land, its epilogue applies the
+ * activation, and the row-parallel down-projection starts on each 256-row block of H as soon as
+ * that block is complete, reducing each output tile with the peers' partials.  Rank `rank`'s share:
+ *   a_shards[r] [m_shard, k] bf16, a_gathered [world*m_shard, k] bf16 OUT   as in mk_ag_gemm
+ *   b_up [k, n_up] bf16, b_down [n_up, n_out] bf16      the local weights
+ *   h [world*m_shard, n_up] bf16, OUT                   h = bf16(gelu(a_gathered @ b_up)), gelu(x) =
+ *                                                       x * Phi(x) = x (1 + erf(x / sqrt 2)) / 2, in
+ *                                                       fp32, rounded to nearest even
+ *   peer_partials[j] [m_shard, n_out] fp32, j != rank   peer j's partial of THIS rank's rows of the
+ *                                                       down-projection, resident
+ *   owned_out [m_shard, n_out] fp32, OUT                (h @ b_down)[own rows] + sum_j peer_partials[j]
+ *   outbox[j] [m_shard, n_out] fp32, j != rank, OUT     (h @ b_down)[rows of rank j]
+ * The arrival mode, order and units apply to A as in mk_ag_gemm; the role split (n_copy_wg,
+ * n_compute_wg) to the up-projection, after which every workgroup works on the down-projection.
+ * Sizes: as mk_ag_gemm for (m_shard, k, n_up) and as mk_gemm_rs for (world*m_shard, n_out, n_up),
+ * with world*m_shard > 512 (256-row tiles in both phases).  Trace records: marks [5] as
+ * mk_ag_gemm, [6] the workgroup's up-projection work done. */
+int mk_mlp_ag_rs(mk_ctx* ctx, void* stream, const uint16_t* const* a_shards, int world, int rank, int m_shard, int k,
+                 const uint16_t* b_up, int n_up, const uint16_t* b_down, int n_out, const float* const* peer_partials,
+                 uint16_t* a_gathered, uint16_t* h, float* owned_out, float* const* outbox, const mk_opts* opts);
 
 #ifdef __cplusplus
 }

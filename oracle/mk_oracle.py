@@ -34,7 +34,12 @@ Readings where the pages are silent (each is also listed in the design notes):
      scores to the lower expert id; no softmax, no capacity limit, no drop;
   R6 inside an expert's segment tokens appear in ascending global token id;
      a token routed to two local experts appears once in each segment;
-  R7 gate weights are not applied to the grouped-GEMM output.
+  R7 gate weights are not applied to the grouped-GEMM output;
+  R16 the MLP block (the page's roadmap section: the transformer-layer megakernel
+     as the next step) is the AllGather + GEMM up-projection, the activation
+     gelu(x) = x * Phi(x) (Phi the standard normal CDF), H stored as bf16 (the
+     down-projection's operand type, rounded to nearest, ties to even), then the
+     GEMM + ReduceScatter down-projection of H.
 """
 from __future__ import annotations
 
@@ -114,6 +119,42 @@ def gemm_ar(a: np.ndarray, b: np.ndarray, peer_partials: Sequence[Optional[np.nd
 
 
 # ----------------------------------------------------------------------------------------
+# MLP block (roadmap section: transformer-layer megakernel), reading R16
+# ----------------------------------------------------------------------------------------
+def gelu(x: np.ndarray) -> np.ndarray:
+    """gelu(x) = x * Phi(x) = x * (1 + erf(x / sqrt 2)) / 2, in fp64 (erf from scipy)."""
+    from scipy.special import erf
+    x = np.asarray(x, dtype=np.float64)
+    return x * 0.5 * (1.0 + erf(x / np.sqrt(2.0)))
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Nearest bf16 value of each fp64 value, ties to even (returned in fp64, exact).  bf16 keeps
+    8 significant bits: with x = f * 2**e, 0.5 <= |f| < 1, the spacing is 2**(e - 8), and
+    np.rint rounds halves to even.  Normal range only (|x| >= 2**-126 or 0)."""
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)
+    scale = np.ldexp(1.0, e - 8)
+    return np.rint(x / scale) * scale
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns of values already representable in bf16 (e.g. round_bf16's output)."""
+    return (np.asarray(x, dtype=np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def mlp_ag_rs(a_shards: Sequence[np.ndarray], b_up: np.ndarray, b_down: np.ndarray,
+              peer_partials: Sequence[Optional[np.ndarray]], world: int, rank: int) -> dict:
+    """MLP block, one rank's share (reading R16): A gathered as in ag_gemm, U = A @ B_up,
+    H = bf16(gelu(U)), then the GEMM + ReduceScatter of H @ B_down as in gemm_rs.
+    Returns dict(a_gathered, u (fp64), h (fp64 values of the bf16 H), own, outbox)."""
+    a, u = ag_gemm(a_shards, b_up)
+    h = round_bf16(gelu(u))
+    own, outbox = gemm_rs(h, b_down, peer_partials, world, rank)
+    return {"a_gathered": a, "u": u, "h": h, "own": own, "outbox": outbox}
+
+
+# ----------------------------------------------------------------------------------------
 # MoE dispatch + grouped GEMM
 # ----------------------------------------------------------------------------------------
 def moe_scores(logits: np.ndarray, bias: np.ndarray) -> np.ndarray:
@@ -185,5 +226,5 @@ def max_rel_err(out: np.ndarray, ref: np.ndarray) -> float:
 
 __all__ = [
     "bf16_to_f64", "allgather", "ag_gemm", "gemm_rs", "gemm_ar", "moe_scores", "moe_route", "moe_segments",
-    "moe_dispatch_gemm", "rms", "max_rel_err",
+    "moe_dispatch_gemm", "gelu", "round_bf16", "bf16_bits", "mlp_ag_rs", "rms", "max_rel_err",
 ]

@@ -329,7 +329,116 @@ def pin_moe(impl):
         assert abs(float(r1["y"][t, 5]) - _fsum_dot(tok_all[t], d["w_up"][0][:, 5])) <= 1e-12 * 10
 
 
-ALL_PINS = [pin_bf16, pin_ag, pin_rs, pin_ar, pin_moe]
+# --------------------------------------------------------------------------------------
+# MLP block (reading R16): gelu, bf16 rounding of H, the composition
+# --------------------------------------------------------------------------------------
+# standard normal CDF from printed tables: Phi(1), Phi(2) and 1 - Phi(2)
+_PHI1, _PHI2, _Q2 = 0.8413447460685429, 0.9772498680518208, 0.022750131948179195
+_BF16_POS = None
+
+
+def _bf16_positive_values():
+    """Every positive finite normal bf16 value, ascending, from its bit fields."""
+    global _BF16_POS
+    if _BF16_POS is None:
+        _BF16_POS = np.array([_exact_value(b) for b in range(0x0080, 0x7F80)], dtype=np.float64)
+    return _BF16_POS
+
+
+def _round_bf16_brute(x: float) -> float:
+    """Nearest bf16 value by bisection over the value list; ties to the even bit pattern."""
+    v = _bf16_positive_values()
+    ax = abs(x)
+    if ax == 0.0:
+        return 0.0
+    i = int(np.searchsorted(v, ax))
+    if i < len(v) and v[i] == ax:
+        r = ax
+    else:
+        lo, hi = v[i - 1], v[i]
+        if ax - lo < hi - ax:
+            r = lo
+        elif hi - ax < ax - lo:
+            r = hi
+        else:  # tie: the pattern with an even last bit (index parity = pattern parity here)
+            r = lo if (0x0080 + i - 1) % 2 == 0 else hi
+    return math.copysign(r, x)
+
+
+def _gelu_brute(x: float) -> float:
+    return x * 0.5 * (1.0 + math.erf(x / math.sqrt(2.0)))
+
+
+def pin_mlp(impl):
+    # gelu against table values, the odd-part identity gelu(x) - gelu(-x) = x, and the tails
+    g = impl.gelu(np.array([0.0, 1.0, -1.0, 2.0, -2.0, 10.0, -10.0]))
+    assert g[0] == 0.0
+    assert abs(g[1] - _PHI1) <= 1e-15 and abs(g[2] - (_PHI1 - 1.0)) <= 1e-15
+    assert abs(g[3] - 2 * _PHI2) <= 2e-15 and abs(g[4] + 2 * _Q2) <= 1e-15
+    assert g[5] == 10.0 and -1e-20 < g[6] <= 0.0
+    x = np.random.default_rng(11).standard_normal(257) * 3
+    assert np.max(np.abs(impl.gelu(x) - impl.gelu(-x) - x)) <= 1e-14
+    # bf16 rounding: bf16 values are fixed points, ties go to even, everything else to nearest
+    vals = _bf16_positive_values()[::37]
+    assert np.array_equal(impl.round_bf16(vals), vals) and np.array_equal(impl.round_bf16(-vals), -vals)
+    ties = [(1 + 2 ** -8, 1.0), (1 + 3 * 2 ** -8, 1 + 2 ** -6), (-(1 + 2 ** -8), -1.0), (3 * 2 ** -9, 3 * 2 ** -9),
+            (1 + 2 ** -8 + 2 ** -30, 1 + 2 ** -7), (255.5, 256.0), (254.5, 254.0), (0.0, 0.0)]
+    got = impl.round_bf16(np.array([t for t, _ in ties]))
+    assert [float(v) for v in got] == [r for _, r in ties], got
+    r = np.random.default_rng(12).standard_normal(400) * np.exp(np.random.default_rng(13).uniform(-20, 20, 400))
+    assert [float(v) for v in impl.round_bf16(r)] == [_round_bf16_brute(float(v)) for v in r]
+    bits = impl.bf16_bits(impl.round_bf16(r[:50]))
+    assert [_exact_value(int(b)) for b in bits] == [_round_bf16_brute(float(v)) for v in r[:50]]
+
+    # the composition, brute force on a tiny case: u by fsum, gelu per element, rounded by bisection
+    sh = wl.MLPShape(world=2, m_shard=64, k=64, n_up=64, n_out=64, rank=1)
+    d = wl.gen_mlp(sh, run=3)
+    res = impl.mlp_ag_rs(d["a_shards"], d["b_up"], d["b_down"], d["peers"], sh.world, sh.rank)
+    a = np.concatenate(d["a_shards"])
+    assert np.array_equal(np.asarray(res["a_gathered"]), a)
+    hb = {}
+    for i in range(sh.m):
+        for c in range(sh.n_up):
+            hb[i, c] = _round_bf16_brute(_gelu_brute(_fsum_dot(a[i], d["b_up"][:, c])))
+    h = np.asarray(res["h"], np.float64)
+    assert all(h[i, c] == v for (i, c), v in hb.items())
+    bd = oracle_bf16(d["b_down"])
+    ms = sh.m_shard
+    for (i, j) in [(0, 0), (ms - 1, sh.n_out - 1), (17, 40), (33, 5)]:
+        row = sh.rank * ms + i
+        ref = math.fsum([hb[row, c] * bd[c, j] for c in range(sh.n_up)] + [float(d["peers"][0][i, j])])
+        assert abs(float(res["own"][i, j]) - ref) <= 1e-12 * max(1.0, abs(ref)), (i, j)
+        ob = math.fsum(hb[i, c] * bd[c, j] for c in range(sh.n_up))  # rank 0's rows, unreduced
+        assert abs(float(res["outbox"][0][i, j]) - ob) <= 1e-12 * max(1.0, abs(ob))
+    assert res["outbox"][1] is None
+
+    # closed forms: A = 0 gives H = 0, the owned rows are the peers' sum and the outboxes zero
+    z = dict(d, a_shards=[np.zeros_like(x) for x in d["a_shards"]])
+    res = impl.mlp_ag_rs(z["a_shards"], z["b_up"], z["b_down"], z["peers"], sh.world, sh.rank)
+    assert not np.any(np.asarray(res["h"])) and not np.any(np.asarray(res["outbox"][0]))
+    assert np.array_equal(np.asarray(res["own"], np.float64), np.asarray(d["peers"][0], np.float64))
+    # integer inputs: U is 0 or a multiple of 16, where gelu is the identity in fp64 and H is exact
+    si = wl.MLPShape(world=4, m_shard=64, k=128, n_up=192, n_out=64, rank=2)
+    di = wl.gen_mlp(si, run=4, kind="int")
+    res = impl.mlp_ag_rs(di["a_shards"], di["b_up"], di["b_down"], di["peers"], si.world, si.rank)
+    ai = np.concatenate([oracle_bf16(x) for x in di["a_shards"]]).astype(np.int64)
+    ui = ai @ oracle_bf16(di["b_up"]).astype(np.int64)
+    assert np.all(ui % 16 == 0) and np.array_equal(np.asarray(res["h"], np.float64), ui.astype(np.float64))
+    pi = ui @ oracle_bf16(di["b_down"]).astype(np.int64)
+    own = pi[si.rank * si.m_shard:(si.rank + 1) * si.m_shard] + sum(
+        di["peers"][j].astype(np.int64) for j in range(si.world) if j != si.rank)
+    assert np.array_equal(np.asarray(res["own"], np.float64), own.astype(np.float64))
+
+
+def oracle_bf16(bits):
+    """bf16 bits -> fp64 through the bit fields (not the oracle's widening)."""
+    b = np.asarray(bits, dtype=np.uint16)
+    flat = np.array([_exact_value(int(x)) for x in np.unique(b)], dtype=np.float64)
+    lut = dict(zip(np.unique(b).tolist(), flat.tolist()))
+    return np.vectorize(lambda x: lut[int(x)], otypes=[np.float64])(b)
+
+
+ALL_PINS = [pin_bf16, pin_ag, pin_rs, pin_ar, pin_moe, pin_mlp]
 
 
 def run_all(impl):
@@ -340,7 +449,7 @@ def run_all(impl):
             p(impl)
         except AssertionError:
             failed.append(p.__name__)
-        except (ValueError, IndexError, TypeError, KeyError) as e:  # a broken mutant may also crash
+        except (ValueError, IndexError, TypeError, KeyError, AttributeError) as e:  # a broken mutant may crash
             failed.append(p.__name__ + ":" + type(e).__name__)
     return failed
 

@@ -242,3 +242,40 @@ def test_plan_moe(hostlib):
     assert moe(hostlib, opts=Opts(arrival_chunk_tokens=32))[0] == UNSUP
     assert moe(hostlib, opts=Opts(arrival_order=0x9000, arrival_len=3))[0] == INVALID
     assert moe(hostlib, opts=Opts(arrival_order=0x9000, arrival_len=512))[0] == MK_OK
+
+
+def mlp(hostlib, world=8, rank=0, m_shard=1024, k=4096, n_up=1792, n_out=4096, opts=None, h=0x600000000,
+        drop_peer=None):
+    arr = (ctypes.c_void_p * world)()
+    peers = (ctypes.c_void_p * world)()
+    ob = (ctypes.c_void_p * world)()
+    for r in range(world):
+        arr[r] = 0x300000000 + r * 0x10000000
+        if r != rank and r != drop_peer:
+            peers[r] = 0x700000000 + r * 0x10000000
+            ob[r] = 0x800000000 + r * 0x10000000
+    out = (ctypes.c_longlong * 16)()
+    code = hostlib.mkh_plan_mlp(ctypes.c_size_t(NF), ctypes.c_size_t(NC), ctypes.c_size_t(INBOX), GRID,
+                                ctypes.byref(opts) if opts else None, arr, world, rank, m_shard, k, P(0x10000), n_up,
+                                P(0x20000), n_out, peers, P(0x100000000), P(h), P(0x900000000), ob, out)
+    keys = ["ag_copy", "ag_compute", "ag_tiles_m", "ag_tiles_n", "red_compute", "red_tiles_m", "red_tiles_n",
+            "own_tile_begin", "own_tile_end", "assist"]
+    return code, dict(zip(keys, list(out)))
+
+
+def test_plan_mlp(hostlib):
+    """The MLP block plans its up-projection as mk_ag_gemm (role split, units) and its
+    down-projection as a resident mk_gemm_rs on every workgroup, over the same 256-row tiles."""
+    code, p = mlp(hostlib)
+    assert code == MK_OK
+    assert (p["ag_copy"], p["ag_compute"], p["ag_tiles_m"], p["ag_tiles_n"]) == (160, 96, 32, 7)
+    assert (p["red_compute"], p["red_tiles_m"], p["red_tiles_n"], p["assist"]) == (256, 32, 16, 1)
+    assert (p["own_tile_begin"], p["own_tile_end"]) == (0, 4)
+    code, p = mlp(hostlib, rank=5)
+    assert code == MK_OK and (p["own_tile_begin"], p["own_tile_end"]) == (20, 24)
+    assert mlp(hostlib, opts=Opts(arrival_mode=RESIDENT))[1]["ag_copy"] == 0
+    assert mlp(hostlib, world=4, m_shard=128)[0] == UNSUP  # 512 rows: the down-projection would use 128-row tiles
+    assert mlp(hostlib, n_up=1800)[0] == UNSUP  # not a multiple of 64
+    assert mlp(hostlib, h=0)[0] == INVALID
+    assert mlp(hostlib, h=0x600000004)[0] == UNSUP  # misaligned H
+    assert mlp(hostlib, drop_peer=3)[0] == INVALID  # missing peer partial of the down-projection

@@ -161,7 +161,68 @@ def _moe_wrong_token_numbering(tokens, logits, bias, top_k, expert_begin, n_loca
     return res
 
 
+def _gelu_tanh(x):
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (x + 0.044715 * x ** 3)))
+
+
+def _gelu_minus(x):
+    from scipy.special import erf
+    x = np.asarray(x, dtype=np.float64)
+    return x * 0.5 * (1.0 - erf(x / np.sqrt(2.0)))
+
+
+def _round_bf16_truncate(x):
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)
+    scale = np.ldexp(1.0, e - 8)
+    return np.trunc(x / scale) * scale
+
+
+def _round_bf16_ties_up(x):
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)
+    scale = np.ldexp(1.0, e - 8)
+    return np.sign(x) * np.floor(np.abs(x) / scale + 0.5) * scale
+
+
+def _mlp_no_activation(a_shards, b_up, b_down, peers, world, rank):
+    a, u = M.ag_gemm(a_shards, b_up)
+    h = M.round_bf16(u)
+    own, outbox = M.gemm_rs(h, b_down, peers, world, rank)
+    return {"a_gathered": a, "u": u, "h": h, "own": own, "outbox": outbox}
+
+
+def _mlp_h_unrounded(a_shards, b_up, b_down, peers, world, rank):
+    a, u = M.ag_gemm(a_shards, b_up)
+    h = M.gelu(u)
+    own, outbox = M.gemm_rs(h, b_down, peers, world, rank)
+    return {"a_gathered": a, "u": u, "h": h, "own": own, "outbox": outbox}
+
+
+def _mlp_rounded_before_gelu(a_shards, b_up, b_down, peers, world, rank):
+    a, u = M.ag_gemm(a_shards, b_up)
+    h = M.round_bf16(M.gelu(M.round_bf16(u)))
+    own, outbox = M.gemm_rs(h, b_down, peers, world, rank)
+    return {"a_gathered": a, "u": u, "h": h, "own": own, "outbox": outbox}
+
+
+def _mlp_rs_rank0(a_shards, b_up, b_down, peers, world, rank):
+    a, u = M.ag_gemm(a_shards, b_up)
+    h = M.round_bf16(M.gelu(u))
+    own, outbox = M.gemm_rs(h, b_down, peers, world, 0)
+    return {"a_gathered": a, "u": u, "h": h, "own": own, "outbox": outbox}
+
+
 MUTANTS = {
+    "gelu_tanh_approximation": ("gelu", _gelu_tanh),
+    "gelu_one_minus_erf": ("gelu", _gelu_minus),
+    "round_bf16_truncates": ("round_bf16", _round_bf16_truncate),
+    "round_bf16_ties_away": ("round_bf16", _round_bf16_ties_up),
+    "mlp_no_activation": ("mlp_ag_rs", _mlp_no_activation),
+    "mlp_h_not_rounded": ("mlp_ag_rs", _mlp_h_unrounded),
+    "mlp_rounds_before_gelu": ("mlp_ag_rs", _mlp_rounded_before_gelu),
+    "mlp_reduces_for_rank0": ("mlp_ag_rs", _mlp_rs_rank0),
     "bf16_shift15": ("bf16_to_f64", _bf16_shift15),
     "bf16_as_fp16": ("bf16_to_f64", _bf16_via_f16),
     "gather_reversed": ("allgather", _allgather_reversed),

@@ -410,8 +410,9 @@ def test_moe_capacity_overflow(ctx):
 
 def test_calls_do_not_leak_state(ctx):
     """Back-to-back calls of different ops on one context: epoch-tagged flags need no clearing,
-    and the counters each kernel uses (leftover tiles, RS pre-sum bands, MoE) are left zeroed, so
-    a call never sees a previous call's counts (integer inputs: any stale pre-sum would show)."""
+    and the counters each kernel uses (leftover tiles, RS pre-sum bands, MoE, the MLP block's H
+    row counts) are left zeroed, so a call never sees a previous call's counts (integer inputs:
+    any stale pre-sum would show)."""
     from gpu_util import assert_close, assert_exact, host
     mk = _mk()
     s = wl.AG_TINY
@@ -428,3 +429,134 @@ def test_calls_do_not_leak_state(ctx):
         dm = wl.gen_moe(sm, run=t)
         st, *_ = _run_moe(ctx, sm, dm)
         assert st == mk.MK_OK
+        sl = wl.replace(wl.MLP_SMALL, rank=t)
+        dl = wl.gen_mlp(sl, run=t, kind="int")
+        _, _, own, _ = _run_mlp(ctx, sl, dl, wl.ag_arrival_order(sl.ag, trial=t))
+        ref = oracle.mlp_ag_rs(dl["a_shards"], dl["b_up"], dl["b_down"], dl["peers"], sl.world, t)
+        assert_exact(host(own), ref["own"].astype(np.float32), f"MLP owned slice call {t}")
+
+
+# ----------------------------------------------------------------------------------------------
+# MLP block: AllGather + up-projection, gelu, down-projection + ReduceScatter in one launch
+# ----------------------------------------------------------------------------------------------
+def _run_mlp(ctx, shape, data, order=None, mode=None):
+    from gpu_util import dev_bf16, dev_f32, dev_i32
+    mk = _mk()
+    W, r, ms = shape.world, shape.rank, shape.m_shard
+    shards = [dev_bf16(s) for s in data["a_shards"]]
+    ag = torch.empty((shape.m, shape.k), dtype=torch.bfloat16, device="cuda")
+    ag.view(torch.int16).fill_(0x7FC0)
+    h = torch.empty((shape.m, shape.n_up), dtype=torch.bfloat16, device="cuda")
+    h.view(torch.int16).fill_(0x7FC0)
+    if mode == mk.MK_ARRIVAL_RESIDENT:
+        ag.copy_(torch.cat(shards, 0))
+    else:
+        ag[r * ms:(r + 1) * ms].copy_(shards[r])
+        shards[r] = ag[r * ms:(r + 1) * ms]
+    peers = [None if p is None else dev_f32(p) for p in data["peers"]]
+    own = torch.full((ms, shape.n_out), float("nan"), device="cuda")
+    outbox = [None if j == r else torch.full((ms, shape.n_out), float("nan"), device="cuda") for j in range(W)]
+    opts = mk.Opts(arrival_mode=mode or 0, arrival_unit_rows=shape.unit_rows, arrival_unit_cols=shape.unit_cols,
+                   arrival_order=dev_i32(order) if order is not None else None)
+    mk.mk_mlp_ag_rs(ctx, shards, W, r, dev_bf16(data["b_up"]), dev_bf16(data["b_down"]), peers, ag, h, own, outbox,
+                    opts=opts)
+    assert ctx.status() == mk.MK_OK
+    return ag, h, own, outbox
+
+
+def _assert_h(h_bits, h_ref, what, max_frac=1e-2):
+    """H is fp32 gelu(fp32 U) rounded to bf16 on the GPU and the bf16 rounding of fp64 gelu(fp64 U)
+    in the oracle: the two may differ by one bf16 step where the fp32 value lies within its own
+    rounding error of a rounding boundary (rare), or by a negligible amount where U is within
+    that error of zero.  Returns |H - H_ref| for the down-projection's error budget."""
+    out = oracle.bf16_to_f64(h_bits)
+    ref = np.asarray(h_ref, np.float64)
+    assert not np.isnan(out).any(), f"{what}: NaN (an element never written)"
+    diff = np.abs(out - ref)
+    mag = np.abs(ref)
+    step = np.where(mag > 0, np.exp2(np.floor(np.log2(np.where(mag > 0, mag, 1.0))) - 7), 0.0)
+    floor = 2.0 ** -20 * oracle.rms(ref)
+    bad = diff > np.maximum(step, floor)
+    assert not bad.any(), f"{what}: {bad.sum()} elements beyond one bf16 step, first at {np.argwhere(bad)[0].tolist()}"
+    frac = float(np.mean(diff > 0))
+    assert frac <= max_frac, f"{what}: {frac:.3%} of elements differ by one bf16 step"
+    return diff
+
+
+def _assert_close_down(out, ref, dh, b_down, what):
+    """Down-projection output against the oracle's.  The oracle's value is the expected one; the
+    budget is the GEMM tolerance plus the linear effect of the H differences that _assert_h has
+    bounded to one bf16 step each: |out - ref| <= TOL * RMS(ref) + |H - H_ref| @ |B_down|."""
+    from gpu_util import TOL
+    out = np.asarray(out, np.float64)
+    assert not np.isnan(out).any(), f"{what}: NaN in output"
+    prop = dh @ np.abs(oracle.bf16_to_f64(b_down))
+    excess = np.abs(out - ref) - (TOL * oracle.rms(ref) + prop)
+    assert (excess <= 0).all(), (f"{what}: {int((excess > 0).sum())} elements beyond the budget, worst by "
+                                 f"{excess.max():.3e} at {np.unravel_index(np.argmax(excess), excess.shape)}")
+
+
+@pytest.mark.parametrize("mode", ["emulated", "resident"])
+@pytest.mark.parametrize("rank", [0, 2])
+def test_mlp_small(ctx, mode, rank):
+    """Several tiles with ragged N tails in both GEMMs (n_up 448, n_out 320), 64x64 units."""
+    from gpu_util import assert_exact, host, host_bits
+    mk = _mk()
+    s = wl.replace(wl.MLP_SMALL, rank=rank)
+    d = wl.gen_mlp(s, run=rank)
+    em = mode == "emulated"
+    order = wl.ag_arrival_order(s.ag, trial=rank) if em else None
+    ag, h, own, outbox = _run_mlp(ctx, s, d, order, mk.MK_ARRIVAL_EMULATED if em else mk.MK_ARRIVAL_RESIDENT)
+    ref = oracle.mlp_ag_rs(d["a_shards"], d["b_up"], d["b_down"], d["peers"], s.world, rank)
+    assert_exact(host_bits(ag), ref["a_gathered"], "a_gathered")
+    dh = _assert_h(host_bits(h), ref["h"], "H")
+    ms = s.m_shard
+    _assert_close_down(host(own), ref["own"], dh[rank * ms:(rank + 1) * ms], d["b_down"], "owned slice")
+    for j in range(s.world):
+        if j != rank:
+            _assert_close_down(host(outbox[j]), ref["outbox"][j], dh[j * ms:(j + 1) * ms], d["b_down"],
+                               f"outbox[{j}]")
+
+
+@pytest.mark.parametrize("mode", ["emulated", "resident"])
+def test_mlp_small_integer(ctx, mode):
+    """Integer inputs: every up-projection output is 0 or a multiple of 16, where gelu is the
+    identity in fp32 as in fp64, so H and every reduced output are exact."""
+    from gpu_util import assert_exact, host, host_bits
+    mk = _mk()
+    s = wl.replace(wl.MLP_SMALL, rank=1)
+    d = wl.gen_mlp(s, run=3, kind="int")
+    em = mode == "emulated"
+    order = wl.ag_arrival_order(s.ag, trial=5, variant="reversed") if em else None
+    _, h, own, outbox = _run_mlp(ctx, s, d, order, mk.MK_ARRIVAL_EMULATED if em else mk.MK_ARRIVAL_RESIDENT)
+    ref = oracle.mlp_ag_rs(d["a_shards"], d["b_up"], d["b_down"], d["peers"], s.world, 1)
+    assert_exact(host_bits(h), oracle.bf16_bits(ref["h"]), "H (integer)")
+    assert_exact(host(own), ref["own"].astype(np.float32), "owned slice (integer)")
+    for j in (0, 2, 3):
+        assert_exact(host(outbox[j]), ref["outbox"][j].astype(np.float32), f"outbox[{j}] (integer)")
+
+
+@pytest.mark.parametrize("mode", ["emulated", "resident"])
+def test_mlp_full_sampled(ctx, mode):
+    """The full block (W=8, 1024-row shards, K 4096, n_up 1792, n_out 4096), bench launch
+    configuration; the oracle computes 16 sampled rows of every rank's slice."""
+    from gpu_util import assert_exact, host, host_bits, log
+    mk = _mk()
+    s = wl.MLP_FULL
+    d = wl.gen_mlp(s, run=0)
+    em = mode == "emulated"
+    log(f"mlp full {mode}: launching")
+    ag, h, own, outbox = _run_mlp(ctx, s, d, wl.ag_arrival_order(s.ag, trial=0) if em else None,
+                                  mk.MK_ARRIVAL_EMULATED if em else mk.MK_ARRIVAL_RESIDENT)
+    torch.cuda.synchronize()
+    assert_exact(host_bits(ag), oracle.allgather(d["a_shards"]), "a_gathered")
+    lr = np.sort(np.random.default_rng(6).choice(s.m_shard, 16, replace=False))
+    ref = oracle.mlp_ag_rs([a[lr] for a in d["a_shards"]], d["b_up"], d["b_down"],
+                           [None if p is None else p[lr] for p in d["peers"]], s.world, 0)
+    rows = np.concatenate([j * s.m_shard + lr for j in range(s.world)])
+    dh = _assert_h(host_bits(h)[rows], ref["h"], "H sampled rows")
+    n = len(lr)
+    _assert_close_down(host(own)[lr], ref["own"], dh[:n], d["b_down"], "owned slice rows")
+    for j in range(1, s.world):
+        _assert_close_down(host(outbox[j])[lr], ref["outbox"][j], dh[j * n:(j + 1) * n], d["b_down"],
+                           f"outbox[{j}] rows")

@@ -29,6 +29,7 @@ CFG_AG = 2
 CFG_RS = 3
 CFG_AR = 4
 CFG_MOE = 5
+CFG_MLP = 6
 ORDER_STREAM = 99  # second SeedSequence word for arrival orders
 
 
@@ -321,3 +322,73 @@ __all__ = [
     "reduce_peer_units", "reduce_arrival_order", "moe_arrival_order", "f32_to_bf16_bits", "normal_bf16",
     "normal_f32", "int_bf16", "int_f32", "permutation", "rng", "replace",
 ]
+
+
+# --------------------------------------------------------------------------------------
+# MLP block: AllGather + up-projection, gelu, down-projection + ReduceScatter
+# --------------------------------------------------------------------------------------
+@dataclass(frozen=True)
+class MLPShape:
+    """The up-projection is the AllGather + GEMM shape (world, m_shard, k, n_up); the
+    down-projection is GEMM + ReduceScatter over [world*m_shard, n_out] with K = n_up."""
+    world: int
+    m_shard: int
+    k: int
+    n_up: int
+    n_out: int
+    sigma_a: float = 1.0
+    sigma_up: float = 1.0 / 16.0
+    sigma_down: float = 1.0 / 16.0
+    sigma_q: float = 1.0
+    unit_rows: int = 64
+    unit_cols: int = 64
+    rank: int = 0
+    cfg: int = CFG_MLP
+
+    @property
+    def m(self) -> int:
+        return self.world * self.m_shard
+
+    @property
+    def ag(self) -> AGShape:
+        """The up-projection's AllGather + GEMM shape (for its arrival units and orders)."""
+        return AGShape(world=self.world, m_shard=self.m_shard, k=self.k, n=self.n_up, unit_rows=self.unit_rows,
+                       unit_cols=self.unit_cols, rank=self.rank, cfg=self.cfg)
+
+    @property
+    def flops(self) -> float:
+        return 2.0 * self.m * self.k * self.n_up + 2.0 * self.m * self.n_up * self.n_out
+
+
+# several tiles and ragged tails in both phases (n_up = 1.75 tiles, n_out = 1.25 tiles)
+MLP_SMALL = MLPShape(world=4, m_shard=256, k=256, n_up=448, n_out=320)
+# the AllGather + GEMM up-projection of the MLP workload followed by the ReduceScatter
+# down-projection of the row-parallel workload (its K is the up-projection's N)
+MLP_FULL = MLPShape(world=8, m_shard=1024, k=4096, n_up=1792, n_out=4096, sigma_up=0.02, sigma_down=0.02,
+                    unit_rows=128, unit_cols=128)
+
+
+def gen_mlp(shape: MLPShape, run: int = 0, kind: str = "normal") -> dict:
+    """A shards (tensor ids 0..W-1), B_up (W), B_down (W+1), peer partials of this rank's rows of the
+    down-projection (W+2+j).  kind "int": A in {0, 16}, B_up in {0, 1}, so every up-projection
+    output is 0 or a multiple of 16 (gelu is then the identity to fp64 and bf16 precision for
+    k <= 256), B_down and the partials small integers: every result is exact."""
+    W, ms = shape.world, shape.m_shard
+    if kind == "normal":
+        shards = [normal_bf16(shape.cfg, r, run, (ms, shape.k), shape.sigma_a) for r in range(W)]
+        b_up = normal_bf16(shape.cfg, W, run, (shape.k, shape.n_up), shape.sigma_up)
+        b_down = normal_bf16(shape.cfg, W + 1, run, (shape.n_up, shape.n_out), shape.sigma_down)
+        peers = [None if j == shape.rank else normal_f32(shape.cfg, W + 2 + j, run, (ms, shape.n_out), shape.sigma_q)
+                 for j in range(W)]
+    elif kind == "int":
+        if shape.k > 256:
+            raise ValueError("integer MLP inputs stay exact only for k <= 256")
+        shards = [f32_to_bf16_bits(16.0 * rng(shape.cfg, r, run).integers(0, 2, size=(ms, shape.k)).astype(np.float32))
+                  for r in range(W)]
+        b_up = int_bf16(shape.cfg, W, run, (shape.k, shape.n_up), 0, 1)
+        b_down = int_bf16(shape.cfg, W + 1, run, (shape.n_up, shape.n_out), -2, 2)
+        peers = [None if j == shape.rank else int_f32(shape.cfg, W + 2 + j, run, (ms, shape.n_out))
+                 for j in range(W)]
+    else:
+        raise ValueError(kind)
+    return {"a_shards": shards, "b_up": b_up, "b_down": b_down, "peers": peers}
