@@ -16,7 +16,9 @@ BLAS bf16 GEMM of the same shape, and "copy kernels, then the GEMM kernel" as se
 launches); GEMM+ReduceScatter and GEMM+AllReduce (TFLOP/s and epilogue GB/s, resident and
 with landing); MoE dispatch + grouped GEMM (routed rows, phase spans, grouped-GEMM TFLOP/s
 over its compute span, dispatch GB/s); the MLP block in one launch (AllGather + up-projection,
-gelu, down-projection + ReduceScatter) beside the same three steps as separate calls.  Everything is timed with HIP events on the stream
+gelu, down-projection + ReduceScatter) beside the same three steps as separate calls; and, with
+peer units paced to the xGMI link rate (7 x 153 GB/s), AG, RS and AR at the default role split
+and at the split the library's tuner picks.  Everything is timed with HIP events on the stream
 the kernels are launched on.
 
 cpu_baseline: the fp64 oracle of the same workload, timed on the host cores.
@@ -40,6 +42,7 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
 N_CU, MFMA_FLOP_PER_CLK_CU = 256, 4096  # bf16 dense: 256 CUs x 4096 flop/clk
 N_SETS = 4
 SETTLE_MS = 300.0  # sustained launches before a timed region (clock ramp)
+LINK_GBPS = 7 * 153.0  # one MI355X's xGMI: 7 links x 153 GB/s into each GPU
 TRACE_UNTOUCHED = -1
 
 # HBM traffic of the AG+GEMM kernel comes from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) kept
@@ -92,7 +95,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default="",
                     help="profiling: run only this op (ag, ag_resident, ag_identity, rs, ar, rs_emulated, ar_emulated, "
-                         "moe, mlp, mlp_resident, mlp_unfused, vendor, copy)")
+                         "moe, mlp, mlp_resident, mlp_unfused, ag_link, rs_link, ar_link, mlp_link, vendor, copy)")
+    ap.add_argument("--n-copy", type=int, default=0, help="with --only *_link: copy workgroups (0: default)")
     return ap.parse_args()
 
 
@@ -202,7 +206,7 @@ def traced_call(ctx, fns, opts, lead: int = 100):
     return trace_records(tr)
 
 
-def setup_ag(ctx, resident: bool, identity: bool = False):
+def setup_ag(ctx, resident: bool, identity: bool = False, gbps: float = 0.0, n_copy: int = 0):
     """Four rotating buffer sets; returns (shape, calls, opts) with one Opts shared by the calls."""
     import torch
     import communication_gemm_role_amd as mk
@@ -215,7 +219,8 @@ def setup_ag(ctx, resident: bool, identity: bool = False):
     if resident:
         opts = mk.Opts(arrival_mode=mk.MK_ARRIVAL_RESIDENT)
     else:
-        opts = mk.Opts(arrival_mode=mk.MK_ARRIVAL_EMULATED, arrival_order=None if identity else order)
+        opts = mk.Opts(arrival_mode=mk.MK_ARRIVAL_EMULATED, arrival_order=None if identity else order,
+                       arrival_gbps=gbps, n_copy_wg=n_copy)
     calls = []
     for _ in range(N_SETS):
         shards = [x.clone() for x in shards0]
@@ -274,7 +279,7 @@ def setup_vendor_gemm():
     return s, calls
 
 
-def setup_reduce(ctx, op: str, emulated: bool = False, n_reduce: int = 0):
+def setup_reduce(ctx, op: str, emulated: bool = False, n_reduce: int = 0, gbps: float = 0.0, n_copy: int = 0):
     import torch
     import communication_gemm_role_amd as mk
     import workloads as wl
@@ -284,7 +289,7 @@ def setup_reduce(ctx, op: str, emulated: bool = False, n_reduce: int = 0):
     p0 = [None if p is None else _f32(p) for p in d["peers"]]
     order = _i32(wl.reduce_arrival_order(s, op)) if emulated else None
     opts = mk.Opts(arrival_mode=mk.MK_ARRIVAL_EMULATED if emulated else mk.MK_ARRIVAL_RESIDENT, arrival_order=order,
-                   n_reduce_wg=n_reduce)
+                   n_reduce_wg=n_reduce, arrival_gbps=gbps if emulated else 0.0, n_copy_wg=n_copy if emulated else 0)
     calls = []
     for _ in range(N_SETS):
         a, b = a0.clone(), b0.clone()
@@ -335,7 +340,7 @@ def setup_moe(ctx):
     return s, offsets, calls, opts
 
 
-def setup_mlp(ctx, resident: bool = False):
+def setup_mlp(ctx, resident: bool = False, gbps: float = 0.0):
     """MLP block in one launch (AllGather + up-projection, gelu, down-projection + ReduceScatter),
     two rotating buffer sets; returns (shape, calls, opts)."""
     import torch
@@ -350,7 +355,8 @@ def setup_mlp(ctx, resident: bool = False):
         opts = mk.Opts(arrival_mode=mk.MK_ARRIVAL_RESIDENT)
     else:
         opts = mk.Opts(arrival_mode=mk.MK_ARRIVAL_EMULATED, arrival_unit_rows=s.unit_rows,
-                       arrival_unit_cols=s.unit_cols, arrival_order=_i32(wl.ag_arrival_order(s.ag, trial=0)))
+                       arrival_unit_cols=s.unit_cols, arrival_order=_i32(wl.ag_arrival_order(s.ag, trial=0)),
+                       arrival_gbps=gbps)
     calls = []
     for _ in range(2):
         shards = [x.clone() for x in sh0]
@@ -402,6 +408,51 @@ def setup_mlp_unfused(ctx):
             mk.mk_gemm_rs(ctx, h, bd, s.world, 0, pe, own, ob, opts=o_rs)
         calls.append(step)
     return s, calls
+
+
+def tune_and_time(ctx, kind: str, gbps: float, settle_ms: float) -> dict:
+    """Role-split tuning at a link rate: the library's tuner picks n_copy_wg among the candidates,
+    then the default and the chosen split are each timed like every other secondary."""
+    import torch
+    import communication_gemm_role_amd as mk
+    import workloads as wl
+    if kind == "ag":
+        s, calls, opts = setup_ag(ctx, False, gbps=gbps)
+        d = wl.gen_ag(s, run=0)
+        shards = [_bf16(x) for x in d["a_shards"]]
+        b = _bf16(d["b"])
+        ag = torch.empty((s.m, s.k), dtype=torch.bfloat16, device="cuda")
+        ag[:s.m_shard].copy_(shards[0])
+        shards[0] = ag[:s.m_shard]
+        c = torch.empty((s.m, s.n), device="cuda")
+        cands = [16, 24, 32, 48, 64, 96, 128, 160, 192]
+        best, us = mk.mk_ag_gemm_tune(ctx, shards, s.world, 0, b, ag, c, cands, reps=30, opts=opts)
+        del shards, b, ag, c
+        setup = lambda nc: setup_ag(ctx, False, gbps=gbps, n_copy=nc)[1]
+    else:
+        sh, calls, opts = setup_reduce(ctx, kind, emulated=True, gbps=gbps)
+        d = wl.gen_reduce(sh, kind, run=0)
+        a, b = _bf16(d["a"]), _bf16(d["b"])
+        peers = [None if p is None else _f32(p) for p in d["peers"]]
+        cands = [16, 32, 48, 64, 96, 128, 160, 192, 224]
+        if kind == "rs":
+            own = torch.empty((sh.m_slice, sh.n), device="cuda")
+            ob = [None] + [torch.empty((sh.m_slice, sh.n), device="cuda") for _ in range(1, sh.world)]
+            best, us = mk.mk_gemm_rs_tune(ctx, a, b, sh.world, 0, peers, own, ob, cands, reps=30, opts=opts)
+        else:
+            out = torch.empty((sh.m, sh.n), device="cuda")
+            best, us = mk.mk_gemm_ar_tune(ctx, a, b, sh.world, 0, peers, out, cands, reps=30, opts=opts)
+        del a, b, peers
+        setup = lambda nc: setup_reduce(ctx, kind, emulated=True, gbps=gbps, n_copy=nc)[1]
+    t_def = time_stats(calls, 100, 3, settle_ms)["kernel_ms"]
+    del calls
+    torch.cuda.empty_cache()
+    cb = setup(best)
+    t_best = time_stats(cb, 100, 3, settle_ms)["kernel_ms"]
+    del cb
+    torch.cuda.empty_cache()
+    return {"default_kernel_ms": round(t_def, 5), "tuned_n_copy": best, "tuned_kernel_ms": round(t_best, 5),
+            "tuner_us": dict(zip([str(c) for c in cands], [round(u, 1) for u in us]))}
 
 
 def mlp_trace_summary(rec) -> dict:
@@ -502,6 +553,12 @@ def main():
     if a.only:
         if a.only in ("ag", "ag_resident", "ag_identity"):
             _, calls, _ = setup_ag(ctx, a.only == "ag_resident", identity=a.only == "ag_identity")
+        elif a.only == "ag_link":
+            _, calls, _ = setup_ag(ctx, False, gbps=LINK_GBPS, n_copy=a.n_copy)
+        elif a.only in ("rs_link", "ar_link"):
+            _, calls, _ = setup_reduce(ctx, a.only[:2], emulated=True, gbps=LINK_GBPS, n_copy=a.n_copy)
+        elif a.only == "mlp_link":
+            _, calls, _ = setup_mlp(ctx, gbps=LINK_GBPS)
         elif a.only in ("rs", "ar"):
             _, calls, _ = setup_reduce(ctx, a.only)
         elif a.only in ("rs_emulated", "ar_emulated"):
@@ -636,6 +693,13 @@ def main():
                       "trace": mlp_trace_summary(mlrec),
                       "note": "W=8 emulated ranks, A shards 1024x4096, B_up 4096x1792, B_down 1792x4096, peers' "
                               "partials resident; unfused = mk_ag_gemm, torch gelu + bf16, mk_gemm_rs"}
+        link = {"gbps": LINK_GBPS, "note": "peer units paced to 7 xGMI links x 153 GB/s (mk_opts.arrival_gbps); "
+                                          "tuned = the fastest n_copy_wg found by mk_*_tune, then timed"}
+        for kind in ("ag", "rs", "ar"):
+            link[kind] = tune_and_time(ctx, kind, LINK_GBPS, a.settle_ms)
+        link["ag"]["tuned_tflops"] = round(s.flops / (link["ag"]["tuned_kernel_ms"] * 1e-3) / 1e12, 2)
+        link["ag"]["exposed_vs_resident"] = round(link["ag"]["tuned_kernel_ms"] / tr_["kernel_ms"] - 1.0, 4)
+        sec["link_rate"] = link
         st = ctx.status()
         if st != mk.MK_OK:
             raise SystemExit(f"device status {st}: {mk.strerror(st)}")

@@ -30,7 +30,8 @@ MK_ARRIVAL_RESIDENT = 1
 MK_ARRIVAL_EMULATED = 2
 
 EXPORTED = ["mk_ctx_create", "mk_ctx_destroy", "mk_ctx_status", "mk_ctx_reset", "mk_ctx_grid", "mk_strerror",
-            "mk_selftest_flags", "mk_ag_gemm", "mk_gemm_rs", "mk_gemm_ar", "mk_moe_dispatch_gemm", "mk_mlp_ag_rs"]
+            "mk_selftest_flags", "mk_ag_gemm", "mk_gemm_rs", "mk_gemm_ar", "mk_moe_dispatch_gemm", "mk_mlp_ag_rs",
+            "mk_ag_gemm_tune", "mk_gemm_rs_tune", "mk_gemm_ar_tune"]
 
 
 class MkError(RuntimeError):
@@ -53,6 +54,7 @@ class mk_opts(ctypes.Structure):
         ("timeout_us", ctypes.c_int64),
         ("test_drop_unit", ctypes.c_int),
         ("trace", ctypes.c_void_p),
+        ("arrival_gbps", ctypes.c_double),
     ]
 
 
@@ -72,6 +74,7 @@ class Opts:
     timeout_us: int = 0
     test_drop_unit: int = 0
     trace: object = None
+    arrival_gbps: float = 0.0
 
     def to_c(self) -> mk_opts:
         o = mk_opts()
@@ -89,6 +92,7 @@ class Opts:
         o.arrival_chunk_tokens = self.arrival_chunk_tokens
         o.timeout_us = self.timeout_us
         o.test_drop_unit = self.test_drop_unit
+        o.arrival_gbps = self.arrival_gbps
         if self.trace is not None:
             _check(self.trace, "int64", "trace")
             o.trace = self.trace.data_ptr()
@@ -119,9 +123,13 @@ def lib() -> ctypes.CDLL:
         L.mk_moe_dispatch_gemm.argtypes = [vp, vp, vp, i, i, i, vp, vp, i, i, i, i, vp, i, vp, vp, vp, vp, vp, i, vp]
         L.mk_selftest_flags.argtypes = [i, i, i, i, ctypes.POINTER(i64), ctypes.POINTER(i64)]
         L.mk_mlp_ag_rs.argtypes = [vp, vp, vp, i, i, i, i, vp, i, vp, i, vp, vp, vp, vp, vp, vp]
+        tune = [vp, i, i, vp, vp]  # candidates, count, reps, us_per_call, best
+        L.mk_ag_gemm_tune.argtypes = L.mk_ag_gemm.argtypes + tune
+        L.mk_gemm_rs_tune.argtypes = L.mk_gemm_rs.argtypes + tune
+        L.mk_gemm_ar_tune.argtypes = L.mk_gemm_ar.argtypes + tune
         for name in ("mk_ctx_create", "mk_ctx_destroy", "mk_ctx_status", "mk_ctx_reset", "mk_ctx_grid",
                      "mk_selftest_flags", "mk_ag_gemm", "mk_gemm_rs", "mk_gemm_ar", "mk_moe_dispatch_gemm",
-                     "mk_mlp_ag_rs"):
+                     "mk_mlp_ag_rs", "mk_ag_gemm_tune", "mk_gemm_rs_tune", "mk_gemm_ar_tune"):
             getattr(L, name).restype = i
         _lib_handle = L
     return _lib_handle
@@ -272,6 +280,63 @@ def mk_gemm_ar(ctx: Context, a, b, world: int, rank: int, peer_partials: Sequenc
                            out.data_ptr(), op), "mk_gemm_ar")
 
 
+def _tune(fn, name, args, candidates, reps):
+    cand = (ctypes.c_int * len(candidates))(*[int(c) for c in candidates])
+    us = (ctypes.c_float * len(candidates))()
+    best = ctypes.c_int(0)
+    _call(fn(*args, cand, len(candidates), int(reps), us, ctypes.byref(best)), name)
+    return best.value, [float(u) for u in us]
+
+
+def mk_ag_gemm_tune(ctx: Context, a_shards: Sequence, world: int, rank: int, b, a_gathered, c, candidates: Sequence,
+                    reps: int = 20, opts: Optional[Opts] = None, stream=None):
+    """Role-split tuning of mk_ag_gemm (see mk.h): times each n_copy_wg in `candidates` with the
+    other options of `opts`; returns (fastest n_copy_wg, [us per call or -1 per candidate])."""
+    _check(b, "bf16", "b")
+    _check(a_gathered, "bf16", "a_gathered")
+    _check(c, "f32", "c")
+    k, n = b.shape
+    m = a_gathered.shape[0]
+    if a_gathered.shape[1] != k or c.shape != (m, n) or m % world:
+        raise ValueError("shape mismatch")
+    shards = _ptr_array(a_shards, "bf16", "a_shards") if a_shards is not None else None
+    op, _keep = _opts_ptr(opts, ctx)
+    return _tune(lib().mk_ag_gemm_tune, "mk_ag_gemm_tune",
+                 (ctx.handle, _stream_ptr(stream), shards, world, rank, m // world, k, b.data_ptr(), n,
+                  a_gathered.data_ptr(), c.data_ptr(), op), candidates, reps)
+
+
+def mk_gemm_rs_tune(ctx: Context, a, b, world: int, rank: int, peer_partials: Sequence, owned_out, outbox: Sequence,
+                    candidates: Sequence, reps: int = 20, opts: Optional[Opts] = None, stream=None):
+    """Role-split tuning of mk_gemm_rs (see mk.h); returns (fastest n_copy_wg, [us per call or -1])."""
+    _check(a, "bf16", "a")
+    _check(b, "bf16", "b")
+    _check(owned_out, "f32", "owned_out")
+    m, k = a.shape
+    n = b.shape[1]
+    peers = _ptr_array(peer_partials, "f32", "peer_partials")
+    ob = _ptr_array(outbox, "f32", "outbox")
+    op, _keep = _opts_ptr(opts, ctx)
+    return _tune(lib().mk_gemm_rs_tune, "mk_gemm_rs_tune",
+                 (ctx.handle, _stream_ptr(stream), a.data_ptr(), b.data_ptr(), m, n, k, world, rank, peers,
+                  owned_out.data_ptr(), ob, op), candidates, reps)
+
+
+def mk_gemm_ar_tune(ctx: Context, a, b, world: int, rank: int, peer_partials: Sequence, out, candidates: Sequence,
+                    reps: int = 20, opts: Optional[Opts] = None, stream=None):
+    """Role-split tuning of mk_gemm_ar (see mk.h); returns (fastest n_copy_wg, [us per call or -1])."""
+    _check(a, "bf16", "a")
+    _check(b, "bf16", "b")
+    _check(out, "f32", "out")
+    m, k = a.shape
+    n = b.shape[1]
+    peers = _ptr_array(peer_partials, "f32", "peer_partials")
+    op, _keep = _opts_ptr(opts, ctx)
+    return _tune(lib().mk_gemm_ar_tune, "mk_gemm_ar_tune",
+                 (ctx.handle, _stream_ptr(stream), a.data_ptr(), b.data_ptr(), m, n, k, world, rank, peers,
+                  out.data_ptr(), op), candidates, reps)
+
+
 def mk_moe_dispatch_gemm(ctx: Context, tokens: Sequence, logits, bias, top_k: int, expert_begin: int, w_up,
                          topk_idx, seg_offsets, seg_token, x_seg, y, opts: Optional[Opts] = None,
                          stream=None) -> None:
@@ -328,6 +393,6 @@ def mk_mlp_ag_rs(ctx: Context, a_shards: Sequence, world: int, rank: int, b_up, 
 
 
 __all__ = ["Context", "Opts", "MkError", "mk_selftest_flags", "mk_ag_gemm", "mk_gemm_rs", "mk_gemm_ar", "mk_moe_dispatch_gemm",
-           "mk_mlp_ag_rs", "lib",
+           "mk_mlp_ag_rs", "mk_ag_gemm_tune", "mk_gemm_rs_tune", "mk_gemm_ar_tune", "lib",
            "strerror", "MK_OK", "MK_ERR_INVALID_ARG", "MK_ERR_UNSUPPORTED", "MK_ERR_WORKSPACE", "MK_ERR_HIP",
            "MK_ERR_TIMEOUT", "MK_ERR_CAPACITY", "MK_ARRIVAL_RESIDENT", "MK_ARRIVAL_EMULATED", "EXPORTED"]

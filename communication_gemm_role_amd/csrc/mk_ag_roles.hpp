@@ -12,7 +12,8 @@
 //                                   arrival order, copy that unit of a peer shard into its
 //                                   rows of a_gathered (staged through LDS), then raise the
 //                                   unit's ready flag.
-//                                   Copy workgroups never wait while copying, so every unit lands.
+//                                   Copy workgroups wait on nothing while copying but the clock
+//                                   (link-rate pacing, bounded by the host), so every unit lands.
 //   workgroups [n_copy, grid)       compute: 256 x 256 output tiles of C, one static tile per
 //                                   workgroup, then (like copy workgroups once they have copied)
 //                                   tiles left over past n_compute.  In emulated mode the
@@ -85,8 +86,12 @@ __device__ __forceinline__ void ag_copy_dma(const AgParams& p, int cid, char* st
     const int ur = u / p.n_ucols, uc = u - ur * p.n_ucols;
     return make_rsrc(p.ag + (size_t)ur * p.unit_rows * p.k + (size_t)uc * p.unit_cols, extent);
   };
+  const uint64_t t0 = wall_ticks();
   copy_ring<8, IPU>(n_mine, st0, st1, off, unit_at, src_of, dst_of,
-                    [&](int u) { flag_store(&p.flags[u], p.epoch); });
+                    [&](int u) { flag_store(&p.flags[u], p.epoch); },
+                    [&](int i) {  // queue entry i is arrival position cid + i * n_copy
+                      if (p.pace_q16) wait_wall_until(t0 + (((uint64_t)(cid + i * p.n_copy) * p.pace_q16) >> 16));
+                    });
 }
 
 static_assert(AgTile::STAGE >= 65536 && AG_THREADS == 512, "copy slots: 64 KiB stage buffers, 8 waves");

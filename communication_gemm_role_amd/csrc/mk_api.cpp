@@ -48,6 +48,7 @@ mkh::Opts to_opts(const mk_opts* o) {
   r.arrival_chunk_tokens = o->arrival_chunk_tokens;
   r.timeout_us = o->timeout_us;
   r.test_drop_unit = o->test_drop_unit;
+  r.arrival_gbps = o->arrival_gbps;
   return r;
 }
 
@@ -204,6 +205,7 @@ int mk_ag_gemm(mk_ctx* ctx, void* stream, const uint16_t* const* a_shards, int w
   p.n_copy = P.n_copy;
   p.n_compute = P.n_compute;
   p.emulated = P.emulated;
+  p.pace_q16 = P.pace_q16;
   p.local_in_place = P.local_in_place;
   p.n_order = P.n_order;
   p.drop_pos = P.drop_pos;
@@ -261,6 +263,7 @@ static int gemm_reduce(int is_rs, mk_ctx* ctx, void* stream, const uint16_t* a, 
   p.assist = P.assist;
   p.n_compute = P.n_compute;
   p.emulated = P.emulated;
+  p.pace_q16 = P.pace_q16;
   p.n_order = P.n_order;
   p.drop_pos = P.drop_pos;
   p.tiles_m = P.tiles_m;
@@ -326,6 +329,7 @@ int mk_mlp_ag_rs(mk_ctx* ctx, void* stream, const uint16_t* const* a_shards, int
   a.n_copy = P.ag.n_copy;
   a.n_compute = P.ag.n_compute;
   a.emulated = P.ag.emulated;
+  a.pace_q16 = P.ag.pace_q16;
   a.local_in_place = P.ag.local_in_place;
   a.n_order = P.ag.n_order;
   a.drop_pos = P.ag.drop_pos;
@@ -430,6 +434,103 @@ int mk_moe_dispatch_gemm(mk_ctx* ctx, void* stream, const uint16_t* const* token
   p.off_tile_cnt = P.off_tile_cnt;
   p.off_misc = P.off_misc;
   return mk::launch_moe(p, P.n_copy + P.n_compute, s) == hipSuccess ? MK_OK : MK_ERR_HIP;
+}
+
+}  // extern "C"
+
+// ---- role-split tuning ------------------------------------------------------------------------------
+namespace {
+
+// Times call(n_copy) for each candidate on the stream: two untimed calls, then `reps` calls between
+// two events.  us_out[i] is the mean time per call in microseconds, or -1 where the planner rejects
+// that split (MK_ERR_INVALID_ARG / MK_ERR_UNSUPPORTED: the candidate does not fit, which is not an
+// error of the tuning).  Stops at the first HIP error or device-side status (watchdog, ...).
+template <class Call>
+int tune_split(mk_ctx* ctx, void* stream, const int* cand, int n_cand, int reps, float* us_out, int* best,
+               Call&& call) {
+  if (!ctx || !cand || n_cand <= 0 || reps <= 0 || !us_out || !best) return MK_ERR_INVALID_ARG;
+  DeviceGuard g(ctx->device);
+  if (!g.ok) return MK_ERR_HIP;
+  hipStream_t s = (hipStream_t)stream;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipEventCreate(&e0) != hipSuccess) return MK_ERR_HIP;
+  if (hipEventCreate(&e1) != hipSuccess) {
+    (void)hipEventDestroy(e0);
+    return MK_ERR_HIP;
+  }
+  int code = MK_OK, rejected = MK_OK, found = 0;
+  float best_us = 0.f;
+  for (int i = 0; i < n_cand; ++i) us_out[i] = -1.f;
+  for (int i = 0; i < n_cand && code == MK_OK; ++i) {
+    int c = call(cand[i]);
+    if (c == MK_ERR_INVALID_ARG || c == MK_ERR_UNSUPPORTED) {
+      if (rejected == MK_OK) rejected = c;
+      continue;
+    }
+    if (c == MK_OK) c = call(cand[i]);
+    if (c == MK_OK && hipEventRecord(e0, s) != hipSuccess) c = MK_ERR_HIP;
+    for (int r = 0; r < reps && c == MK_OK; ++r) c = call(cand[i]);
+    if (c == MK_OK && (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess)) c = MK_ERR_HIP;
+    if (c == MK_OK) c = mk_ctx_status(ctx, stream);
+    float ms = 0.f;
+    if (c == MK_OK && hipEventElapsedTime(&ms, e0, e1) != hipSuccess) c = MK_ERR_HIP;
+    if (c != MK_OK) {
+      code = c;
+      break;
+    }
+    us_out[i] = ms * 1000.f / (float)reps;
+    if (!found || us_out[i] < best_us) {
+      best_us = us_out[i];
+      *best = cand[i];
+      found = 1;
+    }
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (code == MK_OK && !found) code = rejected;
+  return code;
+}
+
+mk_opts opts_copy(const mk_opts* o) {
+  mk_opts r;
+  if (o) r = *o;
+  else memset(&r, 0, sizeof(r));
+  return r;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mk_ag_gemm_tune(mk_ctx* ctx, void* stream, const uint16_t* const* a_shards, int world, int rank, int m_shard,
+                    int k, const uint16_t* b, int n, uint16_t* a_gathered, float* c, const mk_opts* opts,
+                    const int* n_copy_candidates, int n_candidates, int reps, float* us_per_call, int* best_n_copy) {
+  mk_opts o = opts_copy(opts);
+  return tune_split(ctx, stream, n_copy_candidates, n_candidates, reps, us_per_call, best_n_copy, [&](int nc) {
+    o.n_copy_wg = nc;
+    return mk_ag_gemm(ctx, stream, a_shards, world, rank, m_shard, k, b, n, a_gathered, c, &o);
+  });
+}
+
+int mk_gemm_rs_tune(mk_ctx* ctx, void* stream, const uint16_t* a, const uint16_t* b, int m, int n, int k, int world,
+                    int rank, const float* const* peer_partials, float* owned_out, float* const* outbox,
+                    const mk_opts* opts, const int* n_copy_candidates, int n_candidates, int reps,
+                    float* us_per_call, int* best_n_copy) {
+  mk_opts o = opts_copy(opts);
+  return tune_split(ctx, stream, n_copy_candidates, n_candidates, reps, us_per_call, best_n_copy, [&](int nc) {
+    o.n_copy_wg = nc;
+    return mk_gemm_rs(ctx, stream, a, b, m, n, k, world, rank, peer_partials, owned_out, outbox, &o);
+  });
+}
+
+int mk_gemm_ar_tune(mk_ctx* ctx, void* stream, const uint16_t* a, const uint16_t* b, int m, int n, int k, int world,
+                    int rank, const float* const* peer_partials, float* out, const mk_opts* opts,
+                    const int* n_copy_candidates, int n_candidates, int reps, float* us_per_call, int* best_n_copy) {
+  mk_opts o = opts_copy(opts);
+  return tune_split(ctx, stream, n_copy_candidates, n_candidates, reps, us_per_call, best_n_copy, [&](int nc) {
+    o.n_copy_wg = nc;
+    return mk_gemm_ar(ctx, stream, a, b, m, n, k, world, rank, peer_partials, out, &o);
+  });
 }
 
 }  // extern "C"

@@ -23,9 +23,13 @@ namespace mk {
 // lands).  src_of(u) / dst_of(u): buffer windows of unit u's first byte (u < 0: any empty window).
 // off[k]: this lane's byte offset inside a unit for the unit's k-th instruction (k < IPU).
 // raise(u): publish unit u (called by thread 0 only, after its stores have completed).
-template <int IPB, int IPU, class UnitAt, class SrcOf, class DstOf, class Raise>
+// pace(i): called by every wave before it requests a batch, with i the batch's last queue entry
+// (link-rate pacing: no unit is requested before its own arrival time, the batch's earlier units
+// wait for the last one; pace only waits on the clock, so the vmcnt arithmetic below holds).
+template <int IPB, int IPU, class UnitAt, class SrcOf, class DstOf, class Raise, class Pace>
 __device__ __forceinline__ void copy_ring(int n_units, char* slot0, char* slot1, const uint32_t (&off)[IPU],
-                                          UnitAt&& unit_at, SrcOf&& src_of, DstOf&& dst_of, Raise&& raise) {
+                                          UnitAt&& unit_at, SrcOf&& src_of, DstOf&& dst_of, Raise&& raise,
+                                          Pace&& pace) {
   constexpr int UPB = IPB / IPU;  // units per batch
   static_assert(UPB * IPU == IPB && UPB >= 1, "a batch holds whole units");
   static_assert(2 * IPB <= 63, "vmcnt is 6 bits");
@@ -33,6 +37,7 @@ __device__ __forceinline__ void copy_ring(int n_units, char* slot0, char* slot1,
   const int nb = (n_units + UPB - 1) / UPB;
   // this wave's IPB KiB of a slot: instruction k of the batch at +1 KiB * k, lane l at +16 B * l
   auto dma = [&](int b, char* slot) {
+    if (b < nb) pace(min((b + 1) * UPB, n_units) - 1);
     char* base = slot + wave * IPB * 1024;
 #pragma unroll
     for (int j = 0; j < UPB; ++j) {

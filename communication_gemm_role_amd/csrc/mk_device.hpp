@@ -79,6 +79,12 @@ __device__ __forceinline__ void wait_mem() { __builtin_amdgcn_s_waitcnt(0); }
 
 __device__ __forceinline__ uint64_t wall_ticks() { return __builtin_readsteadycounter(); }  // 100 MHz
 
+// Every lane of a wave: sleep until the wall clock reaches `deadline` (link-rate pacing of a copy
+// role; the host bounds the deadline well inside the watchdog).
+__device__ __forceinline__ void wait_wall_until(uint64_t deadline) {
+  while ((int64_t)(wall_ticks() - deadline) < 0) __builtin_amdgcn_s_sleep(2);
+}
+
 __device__ __forceinline__ uint32_t flag_load(const uint32_t* f) {
   return __hip_atomic_load(const_cast<uint32_t*>(f), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

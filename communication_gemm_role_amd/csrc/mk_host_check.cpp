@@ -8,12 +8,13 @@ extern "C" {
 
 int mkh_plan_ag(size_t n_flags, size_t n_counters, size_t inbox_bytes, int grid, const mkh::Opts* o,
                 const void* const* a_shards, int world, int rank, int m_shard, int k, const void* b, int n,
-                const void* a_gathered, const void* c, int tile_m, int tile_n, int* out) {
+                const void* a_gathered, const void* c, int tile_m, int tile_n, long long* out) {
   mkh::Ws ws{n_flags, n_counters, inbox_bytes, grid};
   mkh::AgPlan P{};
   const int code = mkh::plan_ag(ws, o, a_shards, world, rank, m_shard, k, b, n, a_gathered, c, tile_m, tile_n, &P);
-  const int v[] = {P.m, P.unit_rows, P.unit_cols, P.n_urows, P.n_ucols, P.n_order, P.local_in_place, P.emulated,
-                   P.drop_pos, P.n_copy, P.n_compute, P.tiles_m, P.tiles_n};
+  const long long v[] = {P.m, P.unit_rows, P.unit_cols, P.n_urows, P.n_ucols, P.n_order, P.local_in_place,
+                         P.emulated, P.drop_pos, P.n_copy, P.n_compute, P.tiles_m, P.tiles_n,
+                         (long long)P.pace_q16};
   for (unsigned i = 0; i < sizeof(v) / sizeof(v[0]); ++i) out[i] = v[i];
   return code;
 }
@@ -28,7 +29,8 @@ int mkh_plan_reduce(size_t n_flags, size_t n_counters, size_t inbox_bytes, int g
       mkh::plan_reduce(ws, o, is_rs, a, b, m, n, k, world, rank, peers, out_buf, outbox, tile_m, tile_n, tile_waves, &P);
   const long long v[] = {P.m_slice, P.p_rows, P.unit_rows, P.unit_cols, P.n_ucols, P.units_per_peer, P.n_units,
                          P.emulated, P.n_order, P.drop_pos, P.n_copy, P.n_reduce, P.n_compute, P.tiles_m, P.tiles_n,
-                         P.own_tile_begin, P.own_tile_end, (long long)P.inbox_need, P.assist};
+                         P.own_tile_begin, P.own_tile_end, (long long)P.inbox_need, P.assist,
+                         (long long)P.pace_q16};
   for (unsigned i = 0; i < sizeof(v) / sizeof(v[0]); ++i) out[i] = v[i];
   return code;
 }

@@ -31,6 +31,7 @@ struct Opts {  // mk_opts with defaults applied by the caller's struct (0 = defa
   int arrival_len, arrival_unit_rows, arrival_unit_cols, arrival_chunk_tokens;
   int64_t timeout_us;
   int test_drop_unit;
+  double arrival_gbps;
 };
 
 struct Ws {  // workspace capacities of a context
@@ -67,7 +68,25 @@ inline int fit_compute(int n_compute, int tiles, const Opts* o) {
 struct AgPlan {
   int m, unit_rows, unit_cols, n_urows, n_ucols, n_order, local_in_place, emulated, drop_pos;
   int n_copy, n_compute, tiles_m, tiles_n;
+  uint64_t pace_q16;  // link-rate pacing: wall-clock ticks per arrival position, Q16 (0: unpaced)
 };
+
+// Link-rate pacing of a copy role (mk_opts.arrival_gbps): arrival position i is not copied before
+// i * unit_bytes / rate after the copy workgroup starts.  The device wall clock runs at 100 MHz,
+// so a position takes unit_bytes / (gbps * 1e9) * 1e8 ticks, kept in Q16 fixed point.  The whole
+// order must land well inside the watchdog, or a consumer would time out waiting for it.
+inline int plan_pace(const Opts* o, bool emulated, int n_order, long unit_bytes, uint64_t* pace_q16) {
+  *pace_q16 = 0;
+  const double g = o ? o->arrival_gbps : 0.0;
+  if (g == 0.0) return MK_OK;
+  if (!(g > 0.0) || !(g < 1e9)) return MK_ERR_INVALID_ARG;  // negative, NaN or infinite
+  if (!emulated || n_order == 0) return MK_OK;                // nothing arrives
+  const double ticks = (double)unit_bytes / (g * 1e9) * 1e8;
+  const int64_t timeout_us = (o->timeout_us > 0) ? o->timeout_us : 2000000;
+  if (ticks * n_order / 100.0 > 0.5 * (double)timeout_us) return MK_ERR_INVALID_ARG;
+  *pace_q16 = (uint64_t)(ticks * 65536.0 + 0.5);
+  return MK_OK;
+}
 
 inline int plan_ag(const Ws& ws, const Opts* o, const void* const* a_shards, int world, int rank, int m_shard, int k,
                    const void* b, int n, const void* a_gathered, const void* c, int tile_m, int tile_n, AgPlan* P) {
@@ -122,7 +141,7 @@ inline int plan_ag(const Ws& ws, const Opts* o, const void* const* a_shards, int
   if (code != MK_OK) return code;
   if (P->emulated && P->n_order == 0) P->n_copy = 0;
   P->n_compute = fit_compute(P->n_compute, P->tiles_m * P->tiles_n, o);
-  return MK_OK;
+  return plan_pace(o, P->emulated, P->n_order, (long)ur * uc * 2, &P->pace_q16);
 }
 
 // ---- GEMM + ReduceScatter / AllReduce -----------------------------------------------------------
@@ -131,6 +150,7 @@ struct RedPlan {
   int n_copy, n_reduce, n_compute, tiles_m, tiles_n, own_tile_begin, own_tile_end;
   int assist;  // RS with peers and no reduce workgroups: compute workgroups pre-sum owned tiles
   size_t inbox_need;
+  uint64_t pace_q16;  // link-rate pacing, as AgPlan::pace_q16
 };
 
 inline int plan_reduce(const Ws& ws, const Opts* o, int is_rs, const void* a, const void* b, int m, int n, int k,
@@ -210,7 +230,7 @@ inline int plan_reduce(const Ws& ws, const Opts* o, int is_rs, const void* a, co
   P->assist = (is_rs && world > 1 && P->n_reduce == 0) ? 1 : 0;
   const size_t n_own = (size_t)(P->own_tile_end - P->own_tile_begin) * P->tiles_n;
   if (P->assist && kCtrBand0 + n_own > ws.n_counters) return MK_ERR_WORKSPACE;
-  return MK_OK;
+  return plan_pace(o, P->emulated, P->n_order, (long)ur * uc * 4, &P->pace_q16);
 }
 
 // ---- MLP block: AllGather + up-projection, gelu, down-projection + ReduceScatter ----------------

@@ -52,6 +52,7 @@ struct AgParams {
   uint32_t epoch;
   uint64_t timeout_ticks;
   uint64_t* trace;  // per-workgroup trace records, or nullptr
+  uint64_t pace_q16;  // copy role: wall-clock ticks per arrival position, Q16 (0: unpaced)
   // MLP up-projection (the MLP kernel only): the epilogue stores H = bf16(gelu(acc)) instead of
   // C and adds one to h_ready[tile row] once a tile's stores have completed
   uint16_t* h;
@@ -82,6 +83,7 @@ struct RedParams {
   uint32_t epoch;
   uint64_t timeout_ticks;
   uint64_t* trace;  // per-workgroup trace records, or nullptr
+  uint64_t pace_q16;  // copy role: wall-clock ticks per arrival position, Q16 (0: unpaced)
   // A produced in the same launch (the MLP kernel's H): a tile of tile row tm waits until
   // a_ready[tm] >= a_ready_need before its K loop; nullptr when A is an input
   const uint32_t* a_ready;

@@ -86,8 +86,12 @@ __device__ __forceinline__ void red_copy_dma(const RedParams& p, int cid, char* 
     const int q = u / p.units_per_peer;
     return make_rsrc(p.inbox + (size_t)q * p.p_rows * p.n + elem_of(u), extent);
   };
+  const uint64_t t0 = wall_ticks();
   copy_ring<8, IPU>(n_mine, st0, st1, off, unit_at, src_of, dst_of,
-                    [&](int u) { flag_store(&p.flags[u], p.epoch); });
+                    [&](int u) { flag_store(&p.flags[u], p.epoch); },
+                    [&](int i) {  // queue entry i is arrival position cid + i * n_copy
+                      if (p.pace_q16) wait_wall_until(t0 + (((uint64_t)(cid + i * p.n_copy) * p.pace_q16) >> 16));
+                    });
 }
 
 template <class T>

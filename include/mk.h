@@ -16,6 +16,7 @@
  * step), the MLP block built from two of them in one launch:
  *
  *   mk_mlp_ag_rs          AllGather + up-projection GEMM, gelu, down-projection GEMM + ReduceScatter
+ *   mk_*_tune             time candidate role splits of an operation and report the fastest
  *
  * Each call is ONE kernel launch.  Inside it, workgroups take a role from their
  * id and a per-shape split: copy (lands peer data in a given order and raises a
@@ -103,6 +104,18 @@ typedef struct mk_opts {
                              MoE compute: [5] first tile's rows all landed
                          The caller owns the array; it must stay alive until the call's
                          stream work completes.                                               */
+  double arrival_gbps; /* EMULATED AG, RS/AR and MLP landing: the rank's total inbound link rate
+                         in GB/s (1e9 bytes/s).  Arrival position i of the order (i = 0, 1, ...)
+                         is not copied before i * unit_bytes / rate after the copy workgroup
+                         starts, so units land at that rate instead of as fast as the copy
+                         role can move them (a copy workgroup moves 8 KiB per wave at a time,
+                         e.g. two 128x128 bf16 units; such a batch starts at its later unit's
+                         time, so its earlier unit lands up to n_copy positions late); 7 links x 153 GB/s = 1071 models one MI355X's
+                         xGMI links (section "mKernel的功能" of the news.chathome.org page: the
+                         intra-node leg runs over the peer links while the GEMM computes).
+                         0: unpaced.  Negative, non-finite, or so low that the whole order would
+                         take more than half of timeout_us: MK_ERR_INVALID_ARG.  Ignored in
+                         RESIDENT mode and by MoE.                                             */
 } mk_opts;
 
 /* ---- context ------------------------------------------------------------------------ */
@@ -231,6 +244,32 @@ int mk_moe_dispatch_gemm(mk_ctx* ctx, void* stream, const uint16_t* const* token
 int mk_mlp_ag_rs(mk_ctx* ctx, void* stream, const uint16_t* const* a_shards, int world, int rank, int m_shard, int k,
                  const uint16_t* b_up, int n_up, const uint16_t* b_down, int n_out, const float* const* peer_partials,
                  uint16_t* a_gathered, uint16_t* h, float* owned_out, float* const* outbox, const mk_opts* opts);
+
+/* ---- role-split tuning -------------------------------------------------------------------
+ * Section "mKernel的功能" of the news.chathome.org page: the number of SMs given to each role is
+ * chosen per shape.  These calls time the matching operation once per candidate number of copy
+ * workgroups (mk_opts.n_copy_wg; 0 = the per-shape default) with every other option as given --
+ * in particular arrival_mode, arrival_order and arrival_gbps, since the best split depends on the
+ * link rate -- and report the fastest.  Arguments before `opts` are those of the operation; its
+ * outputs are overwritten by the timed calls (they end holding the last candidate's result).
+ *   n_copy_candidates[n_candidates]  host array of splits to try
+ *   reps                             timed calls per candidate, after two untimed ones
+ *   us_per_call[n_candidates]        host array, OUT: mean microseconds per call between two events
+ *                                    on `stream`; -1 where the planner rejects the candidate
+ *   best_n_copy                      host, OUT: the fastest candidate
+ * Returns MK_OK if at least one candidate ran; the planner's code if every candidate was rejected;
+ * the first HIP error or device status (e.g. MK_ERR_TIMEOUT) otherwise, after which the results
+ * are undefined.  Synchronises `stream` once per candidate. */
+int mk_ag_gemm_tune(mk_ctx* ctx, void* stream, const uint16_t* const* a_shards, int world, int rank, int m_shard,
+                    int k, const uint16_t* b, int n, uint16_t* a_gathered, float* c, const mk_opts* opts,
+                    const int* n_copy_candidates, int n_candidates, int reps, float* us_per_call, int* best_n_copy);
+int mk_gemm_rs_tune(mk_ctx* ctx, void* stream, const uint16_t* a, const uint16_t* b, int m, int n, int k, int world,
+                    int rank, const float* const* peer_partials, float* owned_out, float* const* outbox,
+                    const mk_opts* opts, const int* n_copy_candidates, int n_candidates, int reps,
+                    float* us_per_call, int* best_n_copy);
+int mk_gemm_ar_tune(mk_ctx* ctx, void* stream, const uint16_t* a, const uint16_t* b, int m, int n, int k, int world,
+                    int rank, const float* const* peer_partials, float* out, const mk_opts* opts,
+                    const int* n_copy_candidates, int n_candidates, int reps, float* us_per_call, int* best_n_copy);
 
 #ifdef __cplusplus
 }

@@ -60,6 +60,25 @@ def test_binding_names_match_header():
         assert callable(getattr(mk, op))
 
 
+def declared_param_counts():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for name, params in re.findall(r"\b(mk_\w+)\s*\(([^)]*)\)\s*;", text):
+        params = params.strip()
+        out[name] = 0 if params in ("", "void") else params.count(",") + 1
+    return out
+
+
+def test_binding_argument_counts_match_header(gpulib):
+    """Every ctypes prototype the binding sets up has the header's number of parameters."""
+    import communication_gemm_role_amd as mk
+    L = mk.lib()
+    counts = declared_param_counts()
+    assert set(counts) == set(mk.EXPORTED)
+    for name, n in counts.items():
+        assert len(getattr(L, name).argtypes) == n, f"{name}: {len(getattr(L, name).argtypes)} argtypes, header has {n}"
+
+
 def test_null_context_is_rejected_synchronously(gpulib):
     vp = ctypes.c_void_p
     gpulib.mk_strerror.restype = ctypes.c_char_p
@@ -79,7 +98,7 @@ class Opts(ctypes.Structure):
                 ("arrival_mode", ctypes.c_int), ("arrival_order", ctypes.c_void_p), ("arrival_len", ctypes.c_int),
                 ("arrival_unit_rows", ctypes.c_int), ("arrival_unit_cols", ctypes.c_int),
                 ("arrival_chunk_tokens", ctypes.c_int), ("timeout_us", ctypes.c_int64),
-                ("test_drop_unit", ctypes.c_int)]
+                ("test_drop_unit", ctypes.c_int), ("arrival_gbps", ctypes.c_double)]
 
 
 NF, NC, INBOX, GRID = 1 << 20, 1 << 20, 256 << 20, 256
@@ -95,12 +114,12 @@ def ag(hostlib, world=8, rank=0, m_shard=1024, k=4096, n=1792, shards="peers", o
         arr[rank] = ag_ptr + rank * m_shard * k * 2
     elif shards == "none":
         arr = None
-    out = (ctypes.c_int * 16)()
+    out = (ctypes.c_longlong * 16)()
     code = hostlib.mkh_plan_ag(ctypes.c_size_t(NF), ctypes.c_size_t(NC), ctypes.c_size_t(INBOX), GRID,
                                ctypes.byref(opts) if opts else None, arr, world, rank, m_shard, k, P(b), n, P(ag_ptr),
                                P(c), 256, 256, out)
     keys = ["m", "unit_rows", "unit_cols", "n_urows", "n_ucols", "n_order", "local_in_place", "emulated", "drop_pos",
-            "n_copy", "n_compute", "tiles_m", "tiles_n"]
+            "n_copy", "n_compute", "tiles_m", "tiles_n", "pace_q16"]
     return code, dict(zip(keys, list(out)))
 
 
@@ -165,7 +184,7 @@ def red(hostlib, is_rs=1, m=8192, n=4096, k=1792, world=8, rank=0, opts=None, ti
                                    rank, peers, P(0x30000), ob, tile[0], tile[1], tile[2], out)
     keys = ["m_slice", "p_rows", "unit_rows", "unit_cols", "n_ucols", "units_per_peer", "n_units", "emulated",
             "n_order", "drop_pos", "n_copy", "n_reduce", "n_compute", "tiles_m", "tiles_n", "own_tile_begin",
-            "own_tile_end", "inbox_need", "assist"]
+            "own_tile_end", "inbox_need", "assist", "pace_q16"]
     return code, dict(zip(keys, list(out)))
 
 
@@ -279,3 +298,24 @@ def test_plan_mlp(hostlib):
     assert mlp(hostlib, h=0)[0] == INVALID
     assert mlp(hostlib, h=0x600000004)[0] == UNSUP  # misaligned H
     assert mlp(hostlib, drop_peer=3)[0] == INVALID  # missing peer partial of the down-projection
+
+
+def test_plan_link_rate_pacing(hostlib):
+    """mk_opts.arrival_gbps: arrival position i is copied no earlier than i * unit_bytes / rate; the
+    plan carries wall-clock ticks (100 MHz) per position in Q16."""
+    code, p = ag(hostlib, opts=Opts(arrival_gbps=1071.0))  # 7 xGMI links x 153 GB/s
+    assert code == MK_OK
+    unit = 128 * 128 * 2
+    assert p["pace_q16"] == round(unit / 1071e9 * 1e8 * 65536)
+    assert ag(hostlib, opts=Opts())[1]["pace_q16"] == 0
+    assert ag(hostlib, opts=Opts(arrival_mode=RESIDENT, arrival_gbps=5.0))[1]["pace_q16"] == 0  # nothing arrives
+    for bad in (-1.0, float("nan"), float("inf")):
+        assert ag(hostlib, opts=Opts(arrival_gbps=bad))[0] == INVALID
+        assert ag(hostlib, opts=Opts(arrival_mode=RESIDENT, arrival_gbps=bad))[0] == INVALID
+    # 2048 units of 32 KiB take 67 ms at 1 GB/s: beyond half of a 100 ms watchdog, inside 2 s
+    assert ag(hostlib, opts=Opts(arrival_gbps=1.0, timeout_us=100000))[0] == INVALID
+    assert ag(hostlib, opts=Opts(arrival_gbps=1.0))[0] == MK_OK
+    code, p = red(hostlib, opts=Opts(arrival_gbps=1071.0))
+    assert code == MK_OK and p["pace_q16"] == round(128 * 128 * 4 / 1071e9 * 1e8 * 65536)
+    assert red(hostlib, opts=Opts(arrival_mode=RESIDENT, arrival_gbps=1071.0))[1]["pace_q16"] == 0
+    assert red(hostlib, opts=Opts(arrival_gbps=-5.0))[0] == INVALID

@@ -37,7 +37,7 @@ def _mk():
 # ----------------------------------------------------------------------------------------------
 # AllGather + GEMM
 # ----------------------------------------------------------------------------------------------
-def _run_ag(ctx, shape, data, order=None, mode=None, in_place=True, poison=False, n_copy=0):
+def _run_ag(ctx, shape, data, order=None, mode=None, in_place=True, poison=False, n_copy=0, **extra):
     from gpu_util import dev_bf16, dev_i32
     mk = _mk()
     W, r = shape.world, shape.rank
@@ -53,7 +53,7 @@ def _run_ag(ctx, shape, data, order=None, mode=None, in_place=True, poison=False
         ag[r * shape.m_shard:(r + 1) * shape.m_shard].copy_(shards[r])
         shards[r] = ag[r * shape.m_shard:(r + 1) * shape.m_shard]
     opts = mk.Opts(arrival_mode=mode or 0, arrival_unit_rows=shape.unit_rows, arrival_unit_cols=shape.unit_cols,
-                   arrival_order=dev_i32(order) if order is not None else None, n_copy_wg=n_copy)
+                   arrival_order=dev_i32(order) if order is not None else None, n_copy_wg=n_copy, **extra)
     mk.mk_ag_gemm(ctx, shards, W, r, b, ag, c, opts=opts)
     assert ctx.status() == mk.MK_OK
     return ag, c
@@ -154,7 +154,7 @@ def test_ag_full_integer_order_invariant(ctx):
 # ----------------------------------------------------------------------------------------------
 # GEMM + ReduceScatter / AllReduce
 # ----------------------------------------------------------------------------------------------
-def _run_red(ctx, op, shape, data, mode, order=None, n_reduce=0, n_copy=0):
+def _run_red(ctx, op, shape, data, mode, order=None, n_reduce=0, n_copy=0, **extra):
     from gpu_util import dev_bf16, dev_f32, dev_i32
     mk = _mk()
     W, r = shape.world, shape.rank
@@ -162,7 +162,7 @@ def _run_red(ctx, op, shape, data, mode, order=None, n_reduce=0, n_copy=0):
     peers = [None if p is None else dev_f32(p) for p in data["peers"]]
     opts = mk.Opts(arrival_mode=mode, n_reduce_wg=n_reduce, n_copy_wg=n_copy,
                    arrival_unit_rows=shape.unit_rows, arrival_unit_cols=shape.unit_cols,
-                   arrival_order=dev_i32(order) if order is not None else None)
+                   arrival_order=dev_i32(order) if order is not None else None, **extra)
     if op == "rs":
         own = torch.full((shape.m_slice, shape.n), float("nan"), device="cuda")
         outbox = [None if j == r else torch.full((shape.m_slice, shape.n), float("nan"), device="cuda")
@@ -439,7 +439,7 @@ def test_calls_do_not_leak_state(ctx):
 # ----------------------------------------------------------------------------------------------
 # MLP block: AllGather + up-projection, gelu, down-projection + ReduceScatter in one launch
 # ----------------------------------------------------------------------------------------------
-def _run_mlp(ctx, shape, data, order=None, mode=None):
+def _run_mlp(ctx, shape, data, order=None, mode=None, **extra):
     from gpu_util import dev_bf16, dev_f32, dev_i32
     mk = _mk()
     W, r, ms = shape.world, shape.rank, shape.m_shard
@@ -457,7 +457,7 @@ def _run_mlp(ctx, shape, data, order=None, mode=None):
     own = torch.full((ms, shape.n_out), float("nan"), device="cuda")
     outbox = [None if j == r else torch.full((ms, shape.n_out), float("nan"), device="cuda") for j in range(W)]
     opts = mk.Opts(arrival_mode=mode or 0, arrival_unit_rows=shape.unit_rows, arrival_unit_cols=shape.unit_cols,
-                   arrival_order=dev_i32(order) if order is not None else None)
+                   arrival_order=dev_i32(order) if order is not None else None, **extra)
     mk.mk_mlp_ag_rs(ctx, shards, W, r, dev_bf16(data["b_up"]), dev_bf16(data["b_down"]), peers, ag, h, own, outbox,
                     opts=opts)
     assert ctx.status() == mk.MK_OK
@@ -560,3 +560,143 @@ def test_mlp_full_sampled(ctx, mode):
     for j in range(1, s.world):
         _assert_close_down(host(outbox[j])[lr], ref["outbox"][j], dh[j * n:(j + 1) * n], d["b_down"],
                            f"outbox[{j}] rows")
+
+
+# ----------------------------------------------------------------------------------------------
+# Link-rate pacing (mk_opts.arrival_gbps): results unchanged, units land no faster than the rate
+# ----------------------------------------------------------------------------------------------
+def _trace_buf(ctx):
+    return torch.full((ctx.grid * 8,), -1, dtype=torch.int64, device="cuda")
+
+
+def _landing_us(tr):
+    """Wall-clock span from the first workgroup's start to the last copy workgroup's last flag."""
+    r = tr.cpu().numpy().reshape(-1, 8)
+    r = r[r[:, 0] != -1]
+    cp = r[r[:, 4] == 0]
+    return (cp[:, 5].max() - r[:, 0].min()) / 100.0
+
+
+def _min_landing_us(n_order, unit_bytes, gbps):
+    # arrival position i is not copied before i * unit_bytes / rate (the last one is n_order - 1)
+    return (n_order - 1) * unit_bytes / (gbps * 1e9) * 1e6
+
+
+def test_ag_paced(ctx):
+    from gpu_util import assert_exact, host, host_bits
+    s = wl.AG_TINY
+    d = wl.gen_ag(s, run=4, kind="int")
+    order = wl.ag_arrival_order(s, trial=3)
+    tr = _trace_buf(ctx)
+    gbps = 2.0
+    ag, c = _run_ag(ctx, s, d, order=order, poison=True, arrival_gbps=gbps, trace=tr)
+    a_ref, c_ref = oracle.ag_gemm(d["a_shards"], d["b"])
+    assert_exact(host_bits(ag), a_ref, "a_gathered (paced)")
+    assert_exact(host(c), c_ref.astype(np.float32), "C (paced, integer inputs)")
+    need = _min_landing_us(len(order), s.unit_rows * s.unit_cols * 2, gbps)
+    got = _landing_us(tr)
+    assert got >= 0.95 * need, f"units landed in {got:.1f} us, the rate allows no less than {need:.1f} us"
+
+
+@pytest.mark.parametrize("op", ["rs", "ar"])
+def test_reduce_paced(ctx, op):
+    from gpu_util import assert_exact, host
+    mk = _mk()
+    s = wl.RS_SMALL if op == "rs" else wl.AR_SMALL
+    d = wl.gen_reduce(s, op, run=5, kind="int")
+    order = wl.reduce_arrival_order(s, op, trial=2)
+    tr = _trace_buf(ctx)
+    gbps = 20.0
+    out, outbox = _run_red(ctx, op, s, d, mk.MK_ARRIVAL_EMULATED, order, arrival_gbps=gbps, trace=tr)
+    if op == "rs":
+        own_ref, ob_ref = oracle.gemm_rs(d["a"], d["b"], d["peers"], s.world, s.rank)
+        assert_exact(host(out), own_ref.astype(np.float32), "RS owned slice (paced)")
+        for j in range(1, s.world):
+            assert_exact(host(outbox[j]), ob_ref[j].astype(np.float32), f"RS outbox[{j}] (paced)")
+    else:
+        ref = oracle.gemm_ar(d["a"], d["b"], d["peers"], s.world, s.rank)
+        assert_exact(host(out), ref.astype(np.float32), "AR out (paced)")
+    need = _min_landing_us(len(order), s.unit_rows * s.unit_cols * 4, gbps)
+    got = _landing_us(tr)
+    assert got >= 0.95 * need, f"units landed in {got:.1f} us, the rate allows no less than {need:.1f} us"
+
+
+def test_mlp_paced(ctx):
+    from gpu_util import assert_exact, host, host_bits
+    s = wl.replace(wl.MLP_SMALL, rank=3)
+    d = wl.gen_mlp(s, run=6, kind="int")
+    _, h, own, _ = _run_mlp(ctx, s, d, wl.ag_arrival_order(s.ag, trial=4), arrival_gbps=5.0)
+    ref = oracle.mlp_ag_rs(d["a_shards"], d["b_up"], d["b_down"], d["peers"], s.world, 3)
+    assert_exact(host_bits(h), oracle.bf16_bits(ref["h"]), "H (paced, integer)")
+    assert_exact(host(own), ref["own"].astype(np.float32), "owned slice (paced, integer)")
+
+
+def test_ag_full_at_link_rate(ctx):
+    """The full AllGather+GEMM at the MI355X's 7 x 153 GB/s of xGMI: sampled rows, landing span."""
+    from gpu_util import assert_close, assert_exact, host, host_bits, log
+    mk = _mk()
+    s = wl.AG_MLP
+    d = wl.gen_ag(s, run=0)
+    order = wl.ag_arrival_order(s, trial=0)
+    tr = _trace_buf(ctx)
+    log("ag full at link rate: launching")
+    ag, c = _run_ag(ctx, s, d, order=order, mode=mk.MK_ARRIVAL_EMULATED, arrival_gbps=1071.0, trace=tr)
+    torch.cuda.synchronize()
+    assert_exact(host_bits(ag), oracle.allgather(d["a_shards"]), "a_gathered")
+    rows = np.sort(np.random.default_rng(8).choice(s.m, 32, replace=False))
+    _, c_ref = oracle.ag_gemm([d["a_shards"][i // s.m_shard][i % s.m_shard][None, :] for i in rows], d["b"])
+    assert_close(host(c)[rows], c_ref, "C sampled rows (link rate)")
+    need = _min_landing_us(len(order), s.unit_rows * s.unit_cols * 2, 1071.0)
+    got = _landing_us(tr)
+    assert got >= 0.95 * need, f"units landed in {got:.1f} us, the rate allows no less than {need:.1f} us"
+
+
+# ----------------------------------------------------------------------------------------------
+# Role-split tuning: every candidate is timed, rejected splits report -1, results stay exact
+# ----------------------------------------------------------------------------------------------
+def test_ag_tune(ctx):
+    from gpu_util import assert_exact, dev_bf16, dev_i32, host
+    mk = _mk()
+    s = wl.AG_TINY
+    d = wl.gen_ag(s, run=7, kind="int")
+    b = dev_bf16(d["b"])
+    shards = [dev_bf16(x) for x in d["a_shards"]]
+    ag = torch.empty((s.m, s.k), dtype=torch.bfloat16, device="cuda")
+    ag[:s.m_shard].copy_(shards[0])  # the local shard in place (rank 0), as the order assumes
+    shards[0] = ag[:s.m_shard]
+    c = torch.empty((s.m, s.n), dtype=torch.float32, device="cuda")
+    opts = mk.Opts(arrival_mode=mk.MK_ARRIVAL_EMULATED, arrival_order=dev_i32(wl.ag_arrival_order(s, trial=1)),
+                   arrival_unit_rows=s.unit_rows, arrival_unit_cols=s.unit_cols, arrival_gbps=50.0)
+    cands = [4, 16, 100000, 64, 0]
+    best, us = mk.mk_ag_gemm_tune(ctx, shards, s.world, s.rank, b, ag, c, cands, reps=5, opts=opts)
+    assert us[2] == -1.0, "a split beyond the grid is rejected"
+    assert all(u > 0 for i, u in enumerate(us) if i != 2)
+    assert best in (4, 16, 64, 0) and us[cands.index(best)] == min(u for u in us if u > 0)
+    assert_exact(host(c), oracle.ag_gemm(d["a_shards"], d["b"])[1].astype(np.float32), "C after tuning")
+    with pytest.raises(mk.MkError):
+        mk.mk_ag_gemm_tune(ctx, shards, s.world, s.rank, b, ag, c, [100000, 200000], reps=2, opts=opts)
+
+
+@pytest.mark.parametrize("op", ["rs", "ar"])
+def test_reduce_tune(ctx, op):
+    from gpu_util import assert_exact, dev_bf16, dev_f32, dev_i32, host
+    mk = _mk()
+    s = wl.RS_SMALL if op == "rs" else wl.AR_SMALL
+    d = wl.gen_reduce(s, op, run=8, kind="int")
+    a, b = dev_bf16(d["a"]), dev_bf16(d["b"])
+    peers = [None if p is None else dev_f32(p) for p in d["peers"]]
+    opts = mk.Opts(arrival_mode=mk.MK_ARRIVAL_EMULATED, arrival_order=dev_i32(wl.reduce_arrival_order(s, op)),
+                   arrival_unit_rows=s.unit_rows, arrival_unit_cols=s.unit_cols)
+    cands = [8, 64, 0, 192]
+    if op == "rs":
+        own = torch.empty((s.m_slice, s.n), device="cuda")
+        ob = [None] + [torch.empty((s.m_slice, s.n), device="cuda") for _ in range(1, s.world)]
+        best, us = mk.mk_gemm_rs_tune(ctx, a, b, s.world, 0, peers, own, ob, cands, reps=5, opts=opts)
+        own_ref, _ = oracle.gemm_rs(d["a"], d["b"], d["peers"], s.world, 0)
+        assert_exact(host(own), own_ref.astype(np.float32), "RS owned slice after tuning")
+    else:
+        out = torch.empty((s.m, s.n), device="cuda")
+        best, us = mk.mk_gemm_ar_tune(ctx, a, b, s.world, 0, peers, out, cands, reps=5, opts=opts)
+        ref = oracle.gemm_ar(d["a"], d["b"], d["peers"], s.world, 0)
+        assert_exact(host(out), ref.astype(np.float32), "AR out after tuning")
+    assert all(u > 0 for u in us) and best == cands[int(np.argmin(us))]
