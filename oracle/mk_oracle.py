@@ -39,7 +39,12 @@ Readings where the pages are silent (each is also listed in the design notes):
      as the next step) is the AllGather + GEMM up-projection, the activation
      gelu(x) = x * Phi(x) (Phi the standard normal CDF), H stored as bf16 (the
      down-projection's operand type, rounded to nearest, ties to even), then the
-     GEMM + ReduceScatter down-projection of H.
+     GEMM + ReduceScatter down-projection of H;
+  R18 ring attention (five-fused-kernels table, Ring Attention row) is the attention of this
+     rank's queries over the keys and values of every rank's sequence shard, with no mask (the
+     pages name no causal variant) and the usual softmax scale 1/sqrt(head_dim) unless given;
+     the ring only changes the order in which key blocks are visited, which softmax does not
+     see.  ``lse`` is the natural log of the softmax denominator.
 """
 from __future__ import annotations
 
@@ -155,6 +160,29 @@ def mlp_ag_rs(a_shards: Sequence[np.ndarray], b_up: np.ndarray, b_down: np.ndarr
 
 
 # ----------------------------------------------------------------------------------------
+# Ring attention (five-fused-kernels table, Ring Attention row), reading R18
+# ----------------------------------------------------------------------------------------
+def ring_attention(q: np.ndarray, k_shards: Sequence[np.ndarray], v_shards: Sequence[np.ndarray],
+                   scale: Optional[float] = None):
+    """One rank's share: q [H, S, D] and every rank's k/v shards [H, S_j, D] as bf16 bits.
+    Scores s[h, i, t] = scale * q[h, i] . k[h, t] over the keys t of all shards in rank order,
+    out[h, i] = sum_t softmax_t(s[h, i, :]) v[h, t], lse[h, i] = log sum_t exp(s[h, i, t]).
+    Returns (out [H, S, D], lse [H, S]) in fp64."""
+    qf = bf16_to_f64(q)
+    kf = np.concatenate([bf16_to_f64(k) for k in k_shards], axis=1)
+    vf = np.concatenate([bf16_to_f64(v) for v in v_shards], axis=1)
+    d = qf.shape[-1]
+    sc = 1.0 / np.sqrt(d) if not scale else float(scale)
+    s = sc * np.matmul(qf, np.swapaxes(kf, 1, 2))
+    m = s.max(axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    l_ = e.sum(axis=-1, keepdims=True)
+    out = np.matmul(e, vf) / l_
+    lse = (m + np.log(l_))[..., 0]
+    return out, lse
+
+
+# ----------------------------------------------------------------------------------------
 # MoE dispatch + grouped GEMM
 # ----------------------------------------------------------------------------------------
 def moe_scores(logits: np.ndarray, bias: np.ndarray) -> np.ndarray:
@@ -226,5 +254,5 @@ def max_rel_err(out: np.ndarray, ref: np.ndarray) -> float:
 
 __all__ = [
     "bf16_to_f64", "allgather", "ag_gemm", "gemm_rs", "gemm_ar", "moe_scores", "moe_route", "moe_segments",
-    "moe_dispatch_gemm", "gelu", "round_bf16", "bf16_bits", "mlp_ag_rs", "rms", "max_rel_err",
+    "moe_dispatch_gemm", "gelu", "round_bf16", "bf16_bits", "mlp_ag_rs", "ring_attention", "rms", "max_rel_err",
 ]

@@ -430,6 +430,63 @@ def pin_mlp(impl):
     assert np.array_equal(np.asarray(res["own"], np.float64), own.astype(np.float64))
 
 
+def pin_ring(impl):
+    # brute force on a tiny case: scores, exponentials and sums per element with math.fsum, from
+    # the shards one by one (not the concatenated keys)
+    sh = wl.RingShape(world=3, heads=2, s_local=4, d=8, sigma=1.0, rank=1)
+    d = wl.gen_ring(sh, run=2)
+    out, lse = impl.ring_attention(d["q"], d["k_shards"], d["v_shards"])
+    q = oracle_bf16(d["q"])
+    ks = [oracle_bf16(k) for k in d["k_shards"]]
+    vs = [oracle_bf16(v) for v in d["v_shards"]]
+    sc = 1.0 / math.sqrt(sh.d)
+    for h in range(sh.heads):
+        for i in range(sh.s_local):
+            scores, vals = [], []
+            for j in range(sh.world):
+                for t in range(sh.s_local):
+                    scores.append(sc * math.fsum(q[h, i, c] * ks[j][h, t, c] for c in range(sh.d)))
+                    vals.append(vs[j][h, t])
+            mx = max(scores)
+            w = [math.exp(x - mx) for x in scores]
+            den = math.fsum(w)
+            for c in range(sh.d):
+                ref = math.fsum(wi * v[c] for wi, v in zip(w, vals)) / den
+                assert abs(float(out[h, i, c]) - ref) <= 1e-12, (h, i, c)
+            assert abs(float(lse[h, i]) - (mx + math.log(den))) <= 1e-12
+    # an explicit scale is honoured: scale 2/sqrt(d) equals the default on doubled queries' scores
+    o2, l2 = impl.ring_attention(d["q"], d["k_shards"], d["v_shards"], scale=2.0 / math.sqrt(sh.d))
+    qq = _bf16(2.0 * q)  # exact: doubling a bf16 value
+    o3, l3 = impl.ring_attention(qq, d["k_shards"], d["v_shards"])
+    assert np.max(np.abs(np.asarray(o2) - np.asarray(o3))) <= 1e-12 and np.max(np.abs(np.asarray(l2) - np.asarray(l3))) <= 1e-12
+    # closed form: zero queries weigh every key equally (out = mean of all values, lse = log N)
+    z = np.zeros_like(d["q"])
+    oz, lz = impl.ring_attention(z, d["k_shards"], d["v_shards"])
+    mean = np.mean(np.concatenate(vs, axis=1), axis=1)
+    assert np.max(np.abs(np.asarray(oz) - mean[:, None, :])) <= 1e-12
+    assert np.max(np.abs(np.asarray(lz) - math.log(sh.world * sh.s_local))) <= 1e-12
+    # one dominant key (score 64, every other key 0) selects that key's value
+    k1 = np.zeros((sh.heads, sh.s_local, sh.d), np.float32)
+    k1[:, 2, 0] = 1.0
+    ksh = [_bf16(k1) if j == 2 else _bf16(np.zeros_like(k1)) for j in range(sh.world)]
+    qd = np.zeros((sh.heads, sh.s_local, sh.d), np.float32)
+    qd[:, :, 0] = 64.0 * math.sqrt(sh.d)  # score 64 for that key, 0 for the rest
+    od, _ = impl.ring_attention(_bf16(qd), ksh, d["v_shards"])
+    assert np.max(np.abs(np.asarray(od) - vs[2][:, 2, :][:, None, :])) <= 1e-12
+    # the ring's order does not matter: shards visited in any rotation give the same result
+    rot = [1, 2, 0]
+    orr, lr = impl.ring_attention(d["q"], [d["k_shards"][j] for j in rot], [d["v_shards"][j] for j in rot])
+    assert np.max(np.abs(np.asarray(orr) - np.asarray(out))) <= 1e-13 and np.max(np.abs(np.asarray(lr) - np.asarray(lse))) <= 1e-13
+    # shifting every key by a constant vector c shifts each query's scores by scale*q.c: same out
+    c = np.zeros(sh.d, np.float32)
+    c[3] = 2.0
+    kshift = [_bf16(k + c) for k in ks]
+    if all(np.array_equal(oracle_bf16(a), k + c) for a, k in zip(kshift, ks)):  # shift exact in bf16
+        os_, ls_ = impl.ring_attention(d["q"], kshift, d["v_shards"])
+        assert np.max(np.abs(np.asarray(os_) - np.asarray(out))) <= 1e-12
+        assert np.max(np.abs(np.asarray(ls_) - np.asarray(lse) - sc * 2.0 * q[:, :, 3])) <= 1e-12
+
+
 def oracle_bf16(bits):
     """bf16 bits -> fp64 through the bit fields (not the oracle's widening)."""
     b = np.asarray(bits, dtype=np.uint16)
@@ -438,7 +495,7 @@ def oracle_bf16(bits):
     return np.vectorize(lambda x: lut[int(x)], otypes=[np.float64])(b)
 
 
-ALL_PINS = [pin_bf16, pin_ag, pin_rs, pin_ar, pin_moe, pin_mlp]
+ALL_PINS = [pin_bf16, pin_ag, pin_rs, pin_ar, pin_moe, pin_mlp, pin_ring]
 
 
 def run_all(impl):

@@ -214,7 +214,60 @@ def _mlp_rs_rank0(a_shards, b_up, b_down, peers, world, rank):
     return {"a_gathered": a, "u": u, "h": h, "own": own, "outbox": outbox}
 
 
+def _ring_parts(q, k_shards, v_shards, scale):
+    qf = M.bf16_to_f64(q)
+    kf = np.concatenate([M.bf16_to_f64(k) for k in k_shards], axis=1)
+    vf = np.concatenate([M.bf16_to_f64(v) for v in v_shards], axis=1)
+    sc = 1.0 / np.sqrt(qf.shape[-1]) if not scale else float(scale)
+    return qf, kf, vf, sc
+
+
+def _ring_no_scale(q, k_shards, v_shards, scale=None):
+    return M.ring_attention(q, k_shards, v_shards, scale=1.0)
+
+
+def _ring_scale_ignored(q, k_shards, v_shards, scale=None):
+    return M.ring_attention(q, k_shards, v_shards)
+
+
+def _ring_local_only(q, k_shards, v_shards, scale=None):
+    return M.ring_attention(q, k_shards[:1], v_shards[:1], scale=scale)
+
+
+def _ring_softmax_over_queries(q, k_shards, v_shards, scale=None):
+    qf, kf, vf, sc = _ring_parts(q, k_shards, v_shards, scale)
+    s = sc * np.matmul(qf, np.swapaxes(kf, 1, 2))
+    e = np.exp(s - s.max(axis=-2, keepdims=True))
+    l_ = e.sum(axis=-2, keepdims=True)
+    return np.matmul(e / l_, vf), np.log(l_.sum(axis=-1))
+
+
+def _ring_unnormalized(q, k_shards, v_shards, scale=None):
+    qf, kf, vf, sc = _ring_parts(q, k_shards, v_shards, scale)
+    s = sc * np.matmul(qf, np.swapaxes(kf, 1, 2))
+    m = s.max(axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    return np.matmul(e, vf), (m + np.log(e.sum(axis=-1, keepdims=True)))[..., 0]
+
+
+def _ring_lse_without_max(q, k_shards, v_shards, scale=None):
+    out, lse = M.ring_attention(q, k_shards, v_shards, scale=scale)
+    qf, kf, _, sc = _ring_parts(q, k_shards, v_shards, scale)
+    return out, lse - (sc * np.matmul(qf, np.swapaxes(kf, 1, 2))).max(axis=-1)
+
+
+def _ring_values_are_keys(q, k_shards, v_shards, scale=None):
+    return M.ring_attention(q, k_shards, k_shards, scale=scale)
+
+
 MUTANTS = {
+    "ring_no_scale": ("ring_attention", _ring_no_scale),
+    "ring_scale_ignored": ("ring_attention", _ring_scale_ignored),
+    "ring_local_only": ("ring_attention", _ring_local_only),
+    "ring_softmax_over_queries": ("ring_attention", _ring_softmax_over_queries),
+    "ring_unnormalized": ("ring_attention", _ring_unnormalized),
+    "ring_lse_without_max": ("ring_attention", _ring_lse_without_max),
+    "ring_values_are_keys": ("ring_attention", _ring_values_are_keys),
     "gelu_tanh_approximation": ("gelu", _gelu_tanh),
     "gelu_one_minus_erf": ("gelu", _gelu_minus),
     "round_bf16_truncates": ("round_bf16", _round_bf16_truncate),
@@ -250,7 +303,7 @@ MUTANTS = {
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_pins_catch_mutant(name, monkeypatch):
     attr, fn = MUTANTS[name]
-    if attr in ("moe_dispatch_gemm",):
+    if attr in ("moe_dispatch_gemm", "ring_attention"):
         # wrap the original, so keep a handle before patching
         orig = getattr(M, attr)
 

@@ -30,6 +30,7 @@ CFG_RS = 3
 CFG_AR = 4
 CFG_MOE = 5
 CFG_MLP = 6
+CFG_RING = 7
 ORDER_STREAM = 99  # second SeedSequence word for arrival orders
 
 
@@ -392,3 +393,65 @@ def gen_mlp(shape: MLPShape, run: int = 0, kind: str = "normal") -> dict:
     else:
         raise ValueError(kind)
     return {"a_shards": shards, "b_up": b_up, "b_down": b_down, "peers": peers}
+
+
+# --------------------------------------------------------------------------------------
+# Ring attention
+# --------------------------------------------------------------------------------------
+@dataclass(frozen=True)
+class RingShape:
+    """Sequence-parallel attention: every rank holds s_local queries, keys and values of each
+    head; rank `rank`'s share attends over all world * s_local keys."""
+    world: int
+    heads: int
+    s_local: int
+    d: int = 128
+    sigma: float = 1.0
+    rank: int = 0
+    cfg: int = CFG_RING
+
+    @property
+    def n_blk(self) -> int:
+        return self.s_local // 64
+
+    @property
+    def flops(self) -> float:
+        """Q K^T and P V: 4 * heads * s_local * (world * s_local) * d."""
+        return 4.0 * self.heads * self.s_local * self.world * self.s_local * self.d
+
+
+# several query tiles and key blocks per head
+RING_SMALL = RingShape(world=4, heads=2, s_local=256, rank=1)
+# 8 ranks x 4096 tokens (32768 in all), 8 heads of 128: one 128-query item per CU
+RING_FULL = RingShape(world=8, heads=8, s_local=4096)
+
+
+def gen_ring(shape: RingShape, run: int = 0) -> dict:
+    """q (tensor id 0), k shards (1 + j), v shards (1 + world + j), N(0, sigma^2) rounded to bf16."""
+    sz = (shape.heads, shape.s_local, shape.d)
+    q = normal_bf16(shape.cfg, 0, run, sz, shape.sigma)
+    ks = [normal_bf16(shape.cfg, 1 + j, run, sz, shape.sigma) for j in range(shape.world)]
+    vs = [normal_bf16(shape.cfg, 1 + shape.world + j, run, sz, shape.sigma) for j in range(shape.world)]
+    return {"q": q, "k_shards": ks, "v_shards": vs}
+
+
+def ring_peer_units(shape: RingShape) -> np.ndarray:
+    """Unit ids of the peers' 64-key K and V blocks in the ring's order: step t = 1, 2, ... brings
+    rank (rank - t) mod world, head by head, block by block, K (even id) before V (odd id)."""
+    per = shape.heads * shape.n_blk * 2
+    out = []
+    for t in range(1, shape.world):
+        j = (shape.rank - t) % shape.world
+        out.extend(range(j * per, (j + 1) * per))
+    return np.asarray(out, dtype=np.int32)
+
+
+def ring_arrival_order(shape: RingShape, trial: int = 0, variant: str = "ring") -> np.ndarray:
+    units = ring_peer_units(shape)
+    if variant == "ring":
+        return units.copy()
+    if variant == "flat":
+        return units[permutation(shape.cfg, trial, len(units))]
+    if variant == "reversed":
+        return units[::-1].copy()
+    raise ValueError(variant)
