@@ -95,7 +95,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default="",
                     help="profiling: run only this op (ag, ag_resident, ag_identity, rs, ar, rs_emulated, ar_emulated, "
-                         "moe, mlp, mlp_resident, mlp_unfused, ag_link, rs_link, ar_link, mlp_link, vendor, copy)")
+                         "moe, mlp, mlp_resident, mlp_unfused, ag_link, rs_link, ar_link, mlp_link, ring, ring_resident, "
+                         "ring_link, vendor, copy)")
     ap.add_argument("--n-copy", type=int, default=0, help="with --only *_link: copy workgroups (0: default)")
     return ap.parse_args()
 
@@ -410,6 +411,33 @@ def setup_mlp_unfused(ctx):
     return s, calls
 
 
+def setup_ring(ctx, resident: bool = False, gbps: float = 0.0, n_copy: int = 0):
+    """Ring attention, one rank's share (8 ranks x 4096 tokens, 8 heads of 128), two buffer sets."""
+    import torch
+    import communication_gemm_role_amd as mk
+    import workloads as wl
+    s = wl.RING_FULL
+    d = wl.gen_ring(s, run=0)
+    q0 = _bf16(d["q"])
+    k0 = [_bf16(k) for k in d["k_shards"]]
+    v0 = [_bf16(v) for v in d["v_shards"]]
+    if resident:
+        opts = mk.Opts(arrival_mode=mk.MK_ARRIVAL_RESIDENT)
+    else:
+        opts = mk.Opts(arrival_mode=mk.MK_ARRIVAL_EMULATED, arrival_order=_i32(wl.ring_arrival_order(s)),
+                       arrival_gbps=gbps, n_copy_wg=n_copy)
+    calls = []
+    for _ in range(2):
+        q, ks, vs = q0.clone(), [k.clone() for k in k0], [v.clone() for v in v0]
+        out = torch.empty((s.heads, s.s_local, s.d), device="cuda")
+        lse = torch.empty((s.heads, s.s_local), device="cuda")
+        kr = None if resident else torch.empty((s.world, s.heads, s.s_local, s.d), dtype=torch.bfloat16, device="cuda")
+        vr = None if resident else torch.empty_like(kr)
+        calls.append(lambda q=q, ks=ks, vs=vs, out=out, lse=lse, kr=kr, vr=vr:
+                     mk.mk_ring_attention(ctx, q, ks, vs, 0, out, lse, kr, vr, opts=opts))
+    return s, calls, opts
+
+
 def tune_and_time(ctx, kind: str, gbps: float, settle_ms: float) -> dict:
     """Role-split tuning at a link rate: the library's tuner picks n_copy_wg among the candidates,
     then the default and the chosen split are each timed like every other secondary."""
@@ -559,6 +587,9 @@ def main():
             _, calls, _ = setup_reduce(ctx, a.only[:2], emulated=True, gbps=LINK_GBPS, n_copy=a.n_copy)
         elif a.only == "mlp_link":
             _, calls, _ = setup_mlp(ctx, gbps=LINK_GBPS)
+        elif a.only in ("ring", "ring_resident", "ring_link"):
+            _, calls, _ = setup_ring(ctx, resident=a.only == "ring_resident",
+                                     gbps=LINK_GBPS if a.only == "ring_link" else 0.0, n_copy=a.n_copy)
         elif a.only in ("rs", "ar"):
             _, calls, _ = setup_reduce(ctx, a.only)
         elif a.only in ("rs_emulated", "ar_emulated"):
@@ -693,6 +724,28 @@ def main():
                       "trace": mlp_trace_summary(mlrec),
                       "note": "W=8 emulated ranks, A shards 1024x4096, B_up 4096x1792, B_down 1792x4096, peers' "
                               "partials resident; unfused = mk_ag_gemm, torch gelu + bf16, mk_gemm_rs"}
+        rsh, crg, ropts = setup_ring(ctx)
+        trg = time_stats(crg, 50, 3, a.settle_ms)
+        rrec = traced_call(ctx, crg, ropts, lead=20)
+        del crg
+        _, crr, _ = setup_ring(ctx, resident=True)
+        trr = time_stats(crr, 50, 3, a.settle_ms)
+        del crr
+        _, crl, _ = setup_ring(ctx, gbps=LINK_GBPS)
+        trl = time_stats(crl, 50, 3, a.settle_ms)
+        del crl
+        torch.cuda.empty_cache()
+        cp = rrec[rrec[:, 4] == 0]
+        sec["ring_attention"] = {
+            "kernel_ms": round(trg["kernel_ms"], 5), "tflops": round(rsh.flops / (trg["kernel_ms"] * 1e-3) / 1e12, 2),
+            "resident_kernel_ms": round(trr["kernel_ms"], 5),
+            "link_rate_kernel_ms": round(trl["kernel_ms"], 5),
+            "trace": {"kernel_span_us": round(us(rrec[:, 2].max() - rrec[:, 0].min()), 2),
+                      "ring_landed_us": round(us(cp[:, 5].max() - rrec[:, 0].min()), 2) if len(cp) else None,
+                      "shader_clock_GHz": round(clock_ghz(rrec), 3)},
+            "note": "8 ranks x 4096 tokens, 8 heads of 128, no mask; peers' K/V blocks land in ring order (32 copy "
+                    "workgroups); flops = 4*heads*s_local*(world*s_local)*128 (P enters as two bf16 terms: the "
+                    "P.V MFMAs are issued twice)"}
         link = {"gbps": LINK_GBPS, "note": "peer units paced to 7 xGMI links x 153 GB/s (mk_opts.arrival_gbps); "
                                           "tuned = the fastest n_copy_wg found by mk_*_tune, then timed"}
         for kind in ("ag", "rs", "ar"):

@@ -31,7 +31,7 @@ MK_ARRIVAL_EMULATED = 2
 
 EXPORTED = ["mk_ctx_create", "mk_ctx_destroy", "mk_ctx_status", "mk_ctx_reset", "mk_ctx_grid", "mk_strerror",
             "mk_selftest_flags", "mk_ag_gemm", "mk_gemm_rs", "mk_gemm_ar", "mk_moe_dispatch_gemm", "mk_mlp_ag_rs",
-            "mk_ag_gemm_tune", "mk_gemm_rs_tune", "mk_gemm_ar_tune"]
+            "mk_ag_gemm_tune", "mk_gemm_rs_tune", "mk_gemm_ar_tune", "mk_ring_attention"]
 
 
 class MkError(RuntimeError):
@@ -123,13 +123,14 @@ def lib() -> ctypes.CDLL:
         L.mk_moe_dispatch_gemm.argtypes = [vp, vp, vp, i, i, i, vp, vp, i, i, i, i, vp, i, vp, vp, vp, vp, vp, i, vp]
         L.mk_selftest_flags.argtypes = [i, i, i, i, ctypes.POINTER(i64), ctypes.POINTER(i64)]
         L.mk_mlp_ag_rs.argtypes = [vp, vp, vp, i, i, i, i, vp, i, vp, i, vp, vp, vp, vp, vp, vp]
+        L.mk_ring_attention.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, ctypes.c_float, vp, vp, vp, vp, vp]
         tune = [vp, i, i, vp, vp]  # candidates, count, reps, us_per_call, best
         L.mk_ag_gemm_tune.argtypes = L.mk_ag_gemm.argtypes + tune
         L.mk_gemm_rs_tune.argtypes = L.mk_gemm_rs.argtypes + tune
         L.mk_gemm_ar_tune.argtypes = L.mk_gemm_ar.argtypes + tune
         for name in ("mk_ctx_create", "mk_ctx_destroy", "mk_ctx_status", "mk_ctx_reset", "mk_ctx_grid",
                      "mk_selftest_flags", "mk_ag_gemm", "mk_gemm_rs", "mk_gemm_ar", "mk_moe_dispatch_gemm",
-                     "mk_mlp_ag_rs", "mk_ag_gemm_tune", "mk_gemm_rs_tune", "mk_gemm_ar_tune"):
+                     "mk_mlp_ag_rs", "mk_ag_gemm_tune", "mk_gemm_rs_tune", "mk_gemm_ar_tune", "mk_ring_attention"):
             getattr(L, name).restype = i
         _lib_handle = L
     return _lib_handle
@@ -280,6 +281,40 @@ def mk_gemm_ar(ctx: Context, a, b, world: int, rank: int, peer_partials: Sequenc
                            out.data_ptr(), op), "mk_gemm_ar")
 
 
+def mk_ring_attention(ctx: Context, q, k_shards: Sequence, v_shards: Sequence, rank: int, out, lse=None,
+                      k_ring=None, v_ring=None, softmax_scale: float = 0.0, opts: Optional[Opts] = None,
+                      stream=None) -> None:
+    """Ring attention, one rank's share (see mk.h).  q [heads, s_local, d] bf16; k_shards[j] and
+    v_shards[j] [heads, s_local, d] bf16 for every rank j; out [heads, s_local, d] fp32 (out);
+    lse [heads, s_local] fp32 (out, optional); k_ring / v_ring [world, heads, s_local, d] bf16
+    landing buffers (emulated arrival)."""
+    _check(q, "bf16", "q")
+    _check(out, "f32", "out")
+    heads, s_local, d = q.shape
+    world = len(k_shards)
+    if len(v_shards) != world or out.shape != q.shape:
+        raise ValueError("shape mismatch")
+    if lse is not None:
+        _check(lse, "f32", "lse")
+        if lse.shape != (heads, s_local):
+            raise ValueError("shape mismatch")
+    for t in list(k_shards) + list(v_shards):
+        if tuple(t.shape) != tuple(q.shape):
+            raise ValueError("shape mismatch")
+    for t, name in ((k_ring, "k_ring"), (v_ring, "v_ring")):
+        if t is not None:
+            _check(t, "bf16", name)
+            if tuple(t.shape) != (world, heads, s_local, d):
+                raise ValueError("shape mismatch")
+    ks = _ptr_array(k_shards, "bf16", "k_shards")
+    vs = _ptr_array(v_shards, "bf16", "v_shards")
+    op, _keep = _opts_ptr(opts, ctx)
+    _call(lib().mk_ring_attention(ctx.handle, _stream_ptr(stream), q.data_ptr(), ks, vs, world, rank, heads, s_local,
+                                  d, float(softmax_scale), k_ring.data_ptr() if k_ring is not None else None,
+                                  v_ring.data_ptr() if v_ring is not None else None, out.data_ptr(),
+                                  lse.data_ptr() if lse is not None else None, op), "mk_ring_attention")
+
+
 def _tune(fn, name, args, candidates, reps):
     cand = (ctypes.c_int * len(candidates))(*[int(c) for c in candidates])
     us = (ctypes.c_float * len(candidates))()
@@ -393,6 +428,6 @@ def mk_mlp_ag_rs(ctx: Context, a_shards: Sequence, world: int, rank: int, b_up, 
 
 
 __all__ = ["Context", "Opts", "MkError", "mk_selftest_flags", "mk_ag_gemm", "mk_gemm_rs", "mk_gemm_ar", "mk_moe_dispatch_gemm",
-           "mk_mlp_ag_rs", "mk_ag_gemm_tune", "mk_gemm_rs_tune", "mk_gemm_ar_tune", "lib",
+           "mk_mlp_ag_rs", "mk_ag_gemm_tune", "mk_gemm_rs_tune", "mk_gemm_ar_tune", "mk_ring_attention", "lib",
            "strerror", "MK_OK", "MK_ERR_INVALID_ARG", "MK_ERR_UNSUPPORTED", "MK_ERR_WORKSPACE", "MK_ERR_HIP",
            "MK_ERR_TIMEOUT", "MK_ERR_CAPACITY", "MK_ARRIVAL_RESIDENT", "MK_ARRIVAL_EMULATED", "EXPORTED"]

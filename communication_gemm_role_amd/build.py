@@ -39,7 +39,8 @@ HIP_FLAGS = [
 # A kernel's register spills or a scratch area the size of a parameter struct mean the hot loop
 # reads memory it should not; the build refuses them.
 MAX_SCRATCH_BYTES = 128
-SOURCES = ["mk_ag_gemm.hip", "mk_gemm_reduce.hip", "mk_moe.hip", "mk_mlp.hip", "mk_selftest.hip", "mk_api.cpp"]
+SOURCES = ["mk_ag_gemm.hip", "mk_gemm_reduce.hip", "mk_moe.hip", "mk_mlp.hip", "mk_ring_attn.hip", "mk_selftest.hip",
+           "mk_api.cpp"]
 
 
 def _run(cmd):

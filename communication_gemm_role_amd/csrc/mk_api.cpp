@@ -436,6 +436,57 @@ int mk_moe_dispatch_gemm(mk_ctx* ctx, void* stream, const uint16_t* const* token
   return mk::launch_moe(p, P.n_copy + P.n_compute, s) == hipSuccess ? MK_OK : MK_ERR_HIP;
 }
 
+int mk_ring_attention(mk_ctx* ctx, void* stream, const uint16_t* q, const uint16_t* const* k_shards,
+                      const uint16_t* const* v_shards, int world, int rank, int heads, int s_local, int head_dim,
+                      float softmax_scale, uint16_t* k_ring, uint16_t* v_ring, float* out, float* lse,
+                      const mk_opts* opts) {
+  if (!ctx) return MK_ERR_INVALID_ARG;
+  const mkh::Opts o = to_opts(opts);
+  mkh::RaPlan P;
+  int code = mkh::plan_ring_attn(ws_of(ctx), opts ? &o : nullptr, q, (const void* const*)k_shards,
+                                 (const void* const*)v_shards, world, rank, heads, s_local, head_dim, softmax_scale,
+                                 k_ring, v_ring, out, lse, &P);
+  if (code != MK_OK) return code;
+  DeviceGuard g(ctx->device);
+  if (!g.ok) return MK_ERR_HIP;
+  hipStream_t s = (hipStream_t)stream;
+  if ((code = next_epoch(ctx, s)) != MK_OK) return code;
+  mk::RaParams p;
+  memset(&p, 0, sizeof(p));
+  p.q = q;
+  for (int r = 0; r < world; ++r) {
+    p.k_src[r] = k_shards[r];
+    p.v_src[r] = v_shards[r];
+  }
+  p.k_ring = k_ring;
+  p.v_ring = v_ring;
+  p.out = out;
+  p.lse = lse;
+  p.order = (P.emulated && opts) ? (const int32_t*)opts->arrival_order : nullptr;
+  p.flags = ctx->flags;
+  p.counters = ctx->counters;
+  p.status = ctx->status;
+  p.scale_log2 = P.scale * 1.4426950408889634f;
+  p.world = world;
+  p.rank = rank;
+  p.heads = heads;
+  p.s_local = s_local;
+  p.n_blk = P.n_blk;
+  p.n_qt = P.n_qt;
+  p.n_items = P.n_items;
+  p.n_units = P.n_units;
+  p.n_copy = P.n_copy;
+  p.n_compute = P.n_compute;
+  p.emulated = P.emulated;
+  p.n_order = P.n_order;
+  p.drop_pos = P.drop_pos;
+  p.epoch = ctx->epoch;
+  p.timeout_ticks = timeout_ticks(opts);
+  p.trace = opts ? opts->trace : nullptr;
+  p.pace_q16 = P.pace_q16;
+  return mk::launch_ring_attn(p, ws_of(ctx).grid, s) == hipSuccess ? MK_OK : MK_ERR_HIP;
+}
+
 }  // extern "C"
 
 // ---- role-split tuning ------------------------------------------------------------------------------

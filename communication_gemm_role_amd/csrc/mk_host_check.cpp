@@ -51,6 +51,21 @@ int mkh_plan_mlp(size_t n_flags, size_t n_counters, size_t inbox_bytes, int grid
   return code;
 }
 
+int mkh_plan_ring_attn(size_t n_flags, size_t n_counters, size_t inbox_bytes, int grid, const mkh::Opts* o,
+                       const void* q, const void* const* k_shards, const void* const* v_shards, int world, int rank,
+                       int heads, int s_local, int head_dim, float scale, const void* k_ring, const void* v_ring,
+                       const void* out, const void* lse, long long* out_fields, float* scale_out) {
+  mkh::Ws ws{n_flags, n_counters, inbox_bytes, grid};
+  mkh::RaPlan P{};
+  const int code = mkh::plan_ring_attn(ws, o, q, k_shards, v_shards, world, rank, heads, s_local, head_dim, scale,
+                                       k_ring, v_ring, out, lse, &P);
+  const long long v[] = {P.n_blk, P.n_qt, P.n_items, P.n_units, P.emulated, P.n_order, P.drop_pos, P.n_copy,
+                         P.n_compute, (long long)P.pace_q16};
+  for (unsigned i = 0; i < sizeof(v) / sizeof(v[0]); ++i) out_fields[i] = v[i];
+  *scale_out = P.scale;
+  return code;
+}
+
 int mkh_plan_moe(size_t n_flags, size_t n_counters, size_t inbox_bytes, int grid, const mkh::Opts* o,
                  const void* const* tokens, int world, int t_local, int hidden, const void* logits, const void* bias,
                  int n_experts, int top_k, int expert_begin, int n_local, const void* w_up, int ffn,

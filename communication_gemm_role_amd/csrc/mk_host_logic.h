@@ -5,6 +5,7 @@
 #include <stddef.h>
 #include <stdint.h>
 #include <string.h>
+#include <math.h>
 
 #ifndef MK_OK
 #define MK_OK 0
@@ -265,6 +266,63 @@ inline int plan_mlp(const Ws& ws, const Opts* o, const void* const* a_shards, in
   if (kCtrBand0 + n_own > (size_t)kCtrHready0 || kCtrHready0 + (size_t)P->ag.tiles_m > ws.n_counters)
     return MK_ERR_WORKSPACE;
   return MK_OK;
+}
+
+// ---- Ring attention -----------------------------------------------------------------------------
+// Items are (head, 128-query tile); K/V move in 64-key blocks of 16 KiB, one flag each for K and V
+// of every (rank, head, block).  Only head dimension 128 is implemented.
+struct RaPlan {
+  int n_blk, n_qt, n_items, n_units, emulated, n_order, drop_pos, n_copy, n_compute;
+  float scale;
+  uint64_t pace_q16;
+};
+
+constexpr int kRaHeadDim = 128;
+
+inline int plan_ring_attn(const Ws& ws, const Opts* o, const void* q, const void* const* k_shards,
+                          const void* const* v_shards, int world, int rank, int heads, int s_local, int head_dim,
+                          float scale, const void* k_ring, const void* v_ring, const void* out, const void* lse,
+                          RaPlan* P) {
+  if (!q || !k_shards || !v_shards || !out) return MK_ERR_INVALID_ARG;
+  if (world < 1 || world > kMaxWorld || rank < 0 || rank >= world) return MK_ERR_INVALID_ARG;
+  if (heads <= 0 || s_local <= 0 || head_dim <= 0) return MK_ERR_INVALID_ARG;
+  if (!(scale >= 0.f) || !(scale < 3.0e38f)) return MK_ERR_INVALID_ARG;  // negative, NaN or infinite
+  const int mode = (o && o->arrival_mode) ? o->arrival_mode : MK_ARRIVAL_EMULATED;
+  if (mode != MK_ARRIVAL_RESIDENT && mode != MK_ARRIVAL_EMULATED) return MK_ERR_INVALID_ARG;
+  for (int r = 0; r < world; ++r)
+    if (!k_shards[r] || !v_shards[r]) return MK_ERR_INVALID_ARG;
+  if (head_dim != kRaHeadDim || s_local % 128) return MK_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(out) || ((uintptr_t)lse & 3u)) return MK_ERR_UNSUPPORTED;
+  for (int r = 0; r < world; ++r)
+    if (!aligned16(k_shards[r]) || !aligned16(v_shards[r])) return MK_ERR_UNSUPPORTED;
+  const uint64_t shard = (uint64_t)heads * (uint64_t)s_local * head_dim * 2;
+  if (shard * (uint64_t)world >= k4G) return MK_ERR_UNSUPPORTED;
+  P->scale = scale > 0.f ? scale : 1.f / sqrtf((float)head_dim);
+  P->n_blk = s_local / 64;
+  P->n_qt = s_local / 128;
+  P->n_items = heads * P->n_qt;
+  P->n_units = world * heads * P->n_blk * 2;
+  P->emulated = mode == MK_ARRIVAL_EMULATED && world > 1;
+  if ((size_t)P->n_units > ws.n_flags) return MK_ERR_WORKSPACE;
+  P->n_order = 0;
+  P->drop_pos = 0;
+  if (P->emulated) {
+    if (!k_ring || !v_ring) return MK_ERR_INVALID_ARG;
+    if (!aligned16(k_ring) || !aligned16(v_ring)) return MK_ERR_UNSUPPORTED;
+    P->n_order = (world - 1) * heads * P->n_blk * 2;
+    if (o && o->arrival_order && o->arrival_len != P->n_order) return MK_ERR_INVALID_ARG;
+    if (o && o->arrival_order && ((uintptr_t)o->arrival_order & 3u)) return MK_ERR_UNSUPPORTED;
+    P->drop_pos = (o && o->test_drop_unit > 0) ? o->test_drop_unit : 0;
+  }
+  // The ring moves world-1 shards of K and V (117 MB at 8 ranks x 8 heads x 4096 keys), a small
+  // part of the attention's time: a few copy workgroups keep ahead of the compute role, which
+  // waits on the ring order, and then take leftover items.
+  const int want_copy = P->emulated ? ((o && o->n_copy_wg) ? o->n_copy_wg : 32) : 0;
+  int nr = 0;
+  int code = split_roles(ws.grid, want_copy, 0, o ? o->n_compute_wg : 0, &P->n_copy, &nr, &P->n_compute);
+  if (code != MK_OK) return code;
+  P->n_compute = fit_compute(P->n_compute, P->n_items, o);
+  return plan_pace(o, P->emulated, P->n_order, 64L * head_dim * 2, &P->pace_q16);
 }
 
 // ---- MoE dispatch + grouped GEMM ----------------------------------------------------------------

@@ -33,6 +33,9 @@ constexpr int CTR_RED_PRESUM = 114;  // next RS pre-sum job (64-row band of an o
 constexpr int CTR_RED_BAND0 = 128;   // RS: bands pre-summed per owned tile, [own tiles] from here
 constexpr int CTR_MLP_EXIT = 115;    // MLP workgroups that have exited
 constexpr int CTR_MLP_HREADY0 = 4096;  // MLP: up-projection tiles stored per 256-row block of H
+constexpr int CTR_RA_ITEM = 116;  // next leftover ring-attention item
+constexpr int CTR_RA_EXIT = 117;  // ring-attention workgroups that have exited
+constexpr int RA_D = 128;         // ring attention: head dimension
 
 struct AgParams {
   const uint16_t* shards[MK_MAX_WORLD];
@@ -126,11 +129,35 @@ struct MoeParams {
   int off_misc;        // [0] route done, [1] exit count
 };
 
+// Ring attention, one rank's share: queries [heads, s_local, 128] against every rank's K/V shard.
+struct RaParams {
+  const uint16_t* q;                     // [heads, s_local, d]
+  const uint16_t* k_src[MK_MAX_WORLD];   // rank j's K shard [heads, s_local, d] (peers: copy sources)
+  const uint16_t* v_src[MK_MAX_WORLD];
+  uint16_t* k_ring;                      // EMULATED: landing buffers [world, heads, s_local, d]
+  uint16_t* v_ring;
+  float* out;                            // [heads, s_local, d]
+  float* lse;                            // [heads, s_local] or nullptr
+  const int32_t* order;
+  uint32_t* flags;                       // one per K or V block of every rank: [world * heads * n_blk * 2]
+  uint32_t* counters;
+  int* status;
+  float scale_log2;                      // softmax scale times log2(e)
+  int world, rank, heads, s_local;
+  int n_blk, n_qt, n_items, n_units;     // 64-key blocks per shard, 128-query tiles, items, flag slots
+  int n_copy, n_compute, emulated, n_order, drop_pos;
+  uint32_t epoch;
+  uint64_t timeout_ticks;
+  uint64_t* trace;
+  uint64_t pace_q16;
+};
+
 // Launchers (stream-ordered; return hipError_t of the launch)
 hipError_t launch_ag_gemm(const AgParams& p, int grid, hipStream_t s);
 hipError_t launch_gemm_reduce(const RedParams& p, int grid, hipStream_t s);
 hipError_t launch_moe(const MoeParams& p, int grid, hipStream_t s);
 hipError_t launch_mlp(const MlpParams& p, int grid, hipStream_t s);
+hipError_t launch_ring_attn(const RaParams& p, int grid, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t s);
 
 // Tile sizes the host needs for scheduling and validation

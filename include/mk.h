@@ -16,6 +16,7 @@
  * step), the MLP block built from two of them in one launch:
  *
  *   mk_mlp_ag_rs          AllGather + up-projection GEMM, gelu, down-projection GEMM + ReduceScatter
+ *   mk_ring_attention     ring K/V exchange + FlashAttention (sequence parallel)
  *   mk_*_tune             time candidate role splits of an operation and report the fastest
  *
  * Each call is ONE kernel launch.  Inside it, workgroups take a role from their
@@ -115,7 +116,7 @@ typedef struct mk_opts {
                          intra-node leg runs over the peer links while the GEMM computes).
                          0: unpaced.  Negative, non-finite, or so low that the whole order would
                          take more than half of timeout_us: MK_ERR_INVALID_ARG.  Ignored in
-                         RESIDENT mode and by MoE.                                             */
+                         RESIDENT mode and by MoE.  Ring attention: unit_bytes = 16 KiB.       */
 } mk_opts;
 
 /* ---- context ------------------------------------------------------------------------ */
@@ -244,6 +245,32 @@ int mk_moe_dispatch_gemm(mk_ctx* ctx, void* stream, const uint16_t* const* token
 int mk_mlp_ag_rs(mk_ctx* ctx, void* stream, const uint16_t* const* a_shards, int world, int rank, int m_shard, int k,
                  const uint16_t* b_up, int n_up, const uint16_t* b_down, int n_out, const float* const* peer_partials,
                  uint16_t* a_gathered, uint16_t* h, float* owned_out, float* const* outbox, const mk_opts* opts);
+
+/* ---- Ring attention ------------------------------------------------------------------
+ * Five-fused-kernels table, Ring Attention row: sequence-parallel attention across ranks, the
+ * ring rotating K/V blocks while the local FlashAttention consumes the block received before,
+ * both inside one persistent kernel.  Rank `rank`'s share, no mask:
+ *   q [heads, s_local, head_dim] bf16                  this rank's queries
+ *   k_shards[j], v_shards[j] [heads, s_local, head_dim] bf16, j in [0, world): every rank's keys
+ *                         and values (entry `rank` is this rank's own, read in place)
+ *   out [heads, s_local, head_dim] fp32, OUT           out[h,i] = sum_t softmax_t(scale * q[h,i].k[h,t]) v[h,t]
+ *                         over the world*s_local keys t of all ranks (rank order; the order does
+ *                         not change the result beyond fp32 rounding)
+ *   lse [heads, s_local] fp32, OUT or NULL             natural log of sum_t exp(scale * q[h,i].k[h,t])
+ *   softmax_scale                                       0: 1/sqrt(head_dim); otherwise finite, > 0
+ *   k_ring, v_ring [world, heads, s_local, head_dim] bf16, OUT (EMULATED, world > 1): the ring's
+ *                         landing buffers; slot j receives rank j's shard (slot `rank` untouched)
+ * EMULATED mode lands peers' blocks of 64 keys (K and V separately, 16 KiB each): unit id
+ * ((j*heads + h)*(s_local/64) + b)*2 + (0 for K, 1 for V) for rank j != rank; arrival_order, if
+ * given, lists those (world-1)*heads*(s_local/64)*2 ids; NULL = the ring's order (step t = 1,
+ * 2, ... brings rank (rank - t) mod world, each step head by head, block by block, K before V).
+ * RESIDENT mode reads every shard in place.  arrival_gbps paces the ring (see mk_opts).
+ * Sizes: head_dim 128, s_local a multiple of 128; world*heads*s_local*head_dim*2 < 4 GiB.
+ * Trace records: copy [5] as mk_ag_gemm; compute [5] first item started. */
+int mk_ring_attention(mk_ctx* ctx, void* stream, const uint16_t* q, const uint16_t* const* k_shards,
+                      const uint16_t* const* v_shards, int world, int rank, int heads, int s_local, int head_dim,
+                      float softmax_scale, uint16_t* k_ring, uint16_t* v_ring, float* out, float* lse,
+                      const mk_opts* opts);
 
 /* ---- role-split tuning -------------------------------------------------------------------
  * Section "mKernel的功能" of the news.chathome.org page: the number of SMs given to each role is

@@ -319,3 +319,44 @@ def test_plan_link_rate_pacing(hostlib):
     assert code == MK_OK and p["pace_q16"] == round(128 * 128 * 4 / 1071e9 * 1e8 * 65536)
     assert red(hostlib, opts=Opts(arrival_mode=RESIDENT, arrival_gbps=1071.0))[1]["pace_q16"] == 0
     assert red(hostlib, opts=Opts(arrival_gbps=-5.0))[0] == INVALID
+
+
+def ring(hostlib, world=8, rank=0, heads=8, s_local=4096, d=128, scale=0.0, opts=None, ring_bufs=True, drop=None):
+    ks = (ctypes.c_void_p * world)()
+    vs = (ctypes.c_void_p * world)()
+    for j in range(world):
+        if j != drop:
+            ks[j] = 0x300000000 + j * 0x10000000
+            vs[j] = 0x400000000 + j * 0x10000000
+    out = (ctypes.c_longlong * 16)()
+    sc = ctypes.c_float(0.0)
+    code = hostlib.mkh_plan_ring_attn(ctypes.c_size_t(NF), ctypes.c_size_t(NC), ctypes.c_size_t(INBOX), GRID,
+                                      ctypes.byref(opts) if opts else None, P(0x10000), ks, vs, world, rank, heads,
+                                      s_local, d, ctypes.c_float(scale), P(0x500000000 if ring_bufs else 0),
+                                      P(0x600000000 if ring_bufs else 0), P(0x700000000), P(0x800000000), out,
+                                      ctypes.byref(sc))
+    keys = ["n_blk", "n_qt", "n_items", "n_units", "emulated", "n_order", "drop_pos", "n_copy", "n_compute", "pace_q16"]
+    return code, dict(zip(keys, list(out)), scale=sc.value)
+
+
+def test_plan_ring_attention(hostlib):
+    """Items (head, 128-query tile), 64-key K and V blocks with one flag each, the default role
+    split, the default softmax scale and the argument checks."""
+    code, p = ring(hostlib)
+    assert code == MK_OK
+    assert (p["n_blk"], p["n_qt"], p["n_items"]) == (64, 32, 256)
+    assert p["n_units"] == 8 * 8 * 64 * 2 and p["n_order"] == 7 * 8 * 64 * 2
+    assert (p["n_copy"], p["n_compute"]) == (32, 224) and p["emulated"] == 1
+    assert abs(p["scale"] - 128 ** -0.5) < 1e-7
+    assert abs(ring(hostlib, scale=0.25)[1]["scale"] - 0.25) < 1e-9
+    code, p = ring(hostlib, opts=Opts(arrival_mode=RESIDENT), ring_bufs=False)
+    assert code == MK_OK and (p["n_copy"], p["n_order"], p["emulated"]) == (0, 0, 0)
+    assert ring(hostlib, world=1, ring_bufs=False)[0] == MK_OK  # nothing arrives
+    assert ring(hostlib, ring_bufs=False)[0] == INVALID  # emulated needs the landing buffers
+    assert ring(hostlib, d=64)[0] == UNSUP
+    assert ring(hostlib, s_local=4160)[0] == UNSUP  # not a multiple of 128
+    assert ring(hostlib, scale=-1.0)[0] == INVALID and ring(hostlib, scale=float("nan"))[0] == INVALID
+    assert ring(hostlib, drop=3)[0] == INVALID
+    assert ring(hostlib, rank=8)[0] == INVALID
+    assert ring(hostlib, world=8, heads=64, s_local=32768)[0] == UNSUP  # 8 x 512 MiB shards: 4 GiB
+    assert ring(hostlib, opts=Opts(arrival_gbps=1071.0))[1]["pace_q16"] == round(16384 / 1071e9 * 1e8 * 65536)

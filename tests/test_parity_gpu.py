@@ -434,6 +434,11 @@ def test_calls_do_not_leak_state(ctx):
         _, _, own, _ = _run_mlp(ctx, sl, dl, wl.ag_arrival_order(sl.ag, trial=t))
         ref = oracle.mlp_ag_rs(dl["a_shards"], dl["b_up"], dl["b_down"], dl["peers"], sl.world, t)
         assert_exact(host(own), ref["own"].astype(np.float32), f"MLP owned slice call {t}")
+        sa = wl.replace(wl.RING_SMALL, rank=t)
+        da = wl.gen_ring(sa, run=t)
+        st, out, *_ = _run_ring(ctx, sa, da, wl.ring_arrival_order(sa, trial=t, variant="flat"))
+        assert st == mk.MK_OK
+        assert_close(host(out), oracle.ring_attention(da["q"], da["k_shards"], da["v_shards"])[0], f"ring call {t}")
 
 
 # ----------------------------------------------------------------------------------------------
@@ -700,3 +705,114 @@ def test_reduce_tune(ctx, op):
         ref = oracle.gemm_ar(d["a"], d["b"], d["peers"], s.world, 0)
         assert_exact(host(out), ref.astype(np.float32), "AR out after tuning")
     assert all(u > 0 for u in us) and best == cands[int(np.argmin(us))]
+
+
+# ----------------------------------------------------------------------------------------------
+# Ring attention: one rank's share, peers' K/V blocks landing in ring order (or any order)
+# ----------------------------------------------------------------------------------------------
+def _run_ring(ctx, shape, data, order=None, mode=None, lse=True, **extra):
+    from gpu_util import dev_bf16, dev_i32
+    mk = _mk()
+    W, H, S, D = shape.world, shape.heads, shape.s_local, shape.d
+    q = dev_bf16(data["q"])
+    ks = [dev_bf16(k) for k in data["k_shards"]]
+    vs = [dev_bf16(v) for v in data["v_shards"]]
+    out = torch.full((H, S, D), float("nan"), device="cuda")
+    ls = torch.full((H, S), float("nan"), device="cuda") if lse else None
+    kr = torch.empty((W, H, S, D), dtype=torch.bfloat16, device="cuda")
+    vr = torch.empty((W, H, S, D), dtype=torch.bfloat16, device="cuda")
+    kr.view(torch.int16).fill_(0x7FC0)
+    vr.view(torch.int16).fill_(0x7FC0)
+    opts = mk.Opts(arrival_mode=mode or 0, arrival_order=dev_i32(order) if order is not None else None, **extra)
+    mk.mk_ring_attention(ctx, q, ks, vs, shape.rank, out, ls, kr, vr, opts=opts)
+    st = ctx.status()
+    return st, out, ls, kr, vr
+
+
+@pytest.mark.parametrize("mode,variant", [("emulated", "ring"), ("emulated", "flat"), ("emulated", "reversed"),
+                                          ("resident", None)])
+def test_ring_small(ctx, mode, variant):
+    """Several query tiles and key blocks per head (world 4, 2 heads, 256 tokens per rank)."""
+    from gpu_util import assert_close, assert_exact, host, host_bits
+    mk = _mk()
+    s = wl.RING_SMALL
+    d = wl.gen_ring(s, run=1)
+    em = mode == "emulated"
+    order = wl.ring_arrival_order(s, trial=3, variant=variant) if em else None
+    st, out, lse, kr, vr = _run_ring(ctx, s, d, order, mk.MK_ARRIVAL_EMULATED if em else mk.MK_ARRIVAL_RESIDENT)
+    assert st == mk.MK_OK
+    ref, lref = oracle.ring_attention(d["q"], d["k_shards"], d["v_shards"])
+    assert_close(host(out), ref, "out")
+    assert_close(host(lse), lref, "lse")
+    if em:  # every peer shard landed bit for bit; the own slot is never written
+        for j in range(s.world):
+            if j != s.rank:
+                assert_exact(host_bits(kr[j]), d["k_shards"][j], f"k_ring[{j}]")
+                assert_exact(host_bits(vr[j]), d["v_shards"][j], f"v_ring[{j}]")
+        assert (host_bits(kr[s.rank]) == 0x7FC0).all()
+
+
+def test_ring_scale_and_no_lse(ctx):
+    from gpu_util import assert_close, host
+    mk = _mk()
+    s = wl.replace(wl.RING_SMALL, rank=3)
+    d = wl.gen_ring(s, run=2)
+    from gpu_util import dev_bf16
+    st, out, _, _, _ = _run_ring(ctx, s, d, None, mk.MK_ARRIVAL_EMULATED, lse=False)
+    assert st == mk.MK_OK
+    assert_close(host(out), oracle.ring_attention(d["q"], d["k_shards"], d["v_shards"])[0], "out (no lse)")
+    q, ks, vs = dev_bf16(d["q"]), [dev_bf16(k) for k in d["k_shards"]], [dev_bf16(v) for v in d["v_shards"]]
+    out2 = torch.empty_like(out)
+    mk.mk_ring_attention(ctx, q, ks, vs, s.rank, out2, None, None, None, softmax_scale=0.3,
+                         opts=mk.Opts(arrival_mode=mk.MK_ARRIVAL_RESIDENT))
+    assert ctx.status() == mk.MK_OK
+    assert_close(host(out2), oracle.ring_attention(d["q"], d["k_shards"], d["v_shards"], scale=0.3)[0], "out (scale)")
+
+
+@pytest.mark.parametrize("mode", ["emulated", "resident"])
+def test_ring_full_sampled(ctx, mode):
+    """8 ranks x 4096 tokens, 8 heads of 128, bench launch configuration; sampled queries."""
+    from gpu_util import assert_close, host, log
+    mk = _mk()
+    s = wl.RING_FULL
+    d = wl.gen_ring(s, run=0)
+    em = mode == "emulated"
+    log(f"ring full {mode}: launching")
+    st, out, lse, _, _ = _run_ring(ctx, s, d, wl.ring_arrival_order(s) if em else None,
+                                   mk.MK_ARRIVAL_EMULATED if em else mk.MK_ARRIVAL_RESIDENT)
+    assert st == mk.MK_OK
+    rows = np.sort(np.random.default_rng(9).choice(s.s_local, 24, replace=False))
+    ref, lref = oracle.ring_attention(d["q"][:, rows], d["k_shards"], d["v_shards"])
+    assert_close(host(out)[:, rows], ref, "out sampled queries")
+    assert_close(host(lse)[:, rows], lref, "lse sampled queries")
+
+
+def test_ring_paced(ctx):
+    from gpu_util import assert_close, host
+    mk = _mk()
+    s = wl.RING_SMALL
+    d = wl.gen_ring(s, run=3)
+    tr = _trace_buf(ctx)
+    gbps = 20.0
+    order = wl.ring_arrival_order(s)
+    st, out, _, _, _ = _run_ring(ctx, s, d, order, mk.MK_ARRIVAL_EMULATED, arrival_gbps=gbps, trace=tr)
+    assert st == mk.MK_OK
+    assert_close(host(out), oracle.ring_attention(d["q"], d["k_shards"], d["v_shards"])[0], "out (paced)")
+    need = _min_landing_us(len(order), 64 * 128 * 2, gbps)
+    got = _landing_us(tr)
+    assert got >= 0.95 * need, f"blocks landed in {got:.1f} us, the rate allows no less than {need:.1f} us"
+
+
+def test_ring_dropped_block_times_out(ctx):
+    """A block that never lands: the items waiting for it time out, the status says so, and the
+    context works again after a reset."""
+    from gpu_util import assert_close, host
+    mk = _mk()
+    s = wl.RING_SMALL
+    d = wl.gen_ring(s, run=4)
+    st, *_ = _run_ring(ctx, s, d, wl.ring_arrival_order(s), mk.MK_ARRIVAL_EMULATED, timeout_us=20000, test_drop_unit=5)
+    assert st == mk.MK_ERR_TIMEOUT
+    ctx.reset()
+    st, out, *_ = _run_ring(ctx, s, d, wl.ring_arrival_order(s), mk.MK_ARRIVAL_EMULATED)
+    assert st == mk.MK_OK
+    assert_close(host(out), oracle.ring_attention(d["q"], d["k_shards"], d["v_shards"])[0], "out after reset")
