@@ -128,9 +128,18 @@ __device__ __forceinline__ void ra_lanes(RaLanes& L, int lane) {
   }
 }
 
-__device__ __forceinline__ uint32_t ra_bf16_rne(float x) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, x);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // finite, non-NaN inputs (softmax weights)
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two softmax weights as packed bf16 hi and lo terms: hi = bf16(p), lo = bf16(p - hi), both
+// rounded to nearest even by the hardware's packed conversion (v_cvt_pk_bf16_f32), one
+// instruction per pair and term.
+__device__ __forceinline__ void ra_split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  const f32x2 v = {a, b};
+  const bf16x2 h = __builtin_convertvector(v, bf16x2);
+  const f32x2 r = v - __builtin_convertvector(h, f32x2);  // exact: p - hi fits in fp32
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
 }
 
 __device__ __forceinline__ void ra_compute_role(const RaParams& p, int slot, char* st0, char* st1, char* st2,
@@ -243,27 +252,25 @@ __device__ __forceinline__ void ra_compute_role(const RaParams& p, int slot, cha
       sum += __shfl_xor(sum, 32);
       l_run = l_run * alpha + sum;
       m_run = m_new;
+      // rescale only when some query's running max moved (alpha == 1 everywhere else: a no-op); after
+      // the first blocks the max of a query's scores rarely moves
+      if (__builtin_amdgcn_readfirstlane((int)(__ballot(alpha != 1.f) != 0)))
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+          for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
       // O^T += V^T P^T, P^T as hi + lo bf16 terms
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         bf16x8 ph, pl;
         {
-          uint32_t hb[8], lb[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float v = s[kk >> 1][8 * (kk & 1) + e];
-            hb[e] = ra_bf16_rne(v);
-            lb[e] = ra_bf16_rne(v - __builtin_bit_cast(float, hb[e] << 16));
-          }
           u32x4 hw, lw;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            hw[e] = hb[2 * e] | (hb[2 * e + 1] << 16);
-            lw[e] = lb[2 * e] | (lb[2 * e + 1] << 16);
+            uint32_t hv, lv;
+            ra_split2(s[kk >> 1][8 * (kk & 1) + 2 * e], s[kk >> 1][8 * (kk & 1) + 2 * e + 1], hv, lv);
+            hw[e] = hv;
+            lw[e] = lv;
           }
           ph = __builtin_bit_cast(bf16x8, hw);
           pl = __builtin_bit_cast(bf16x8, lw);
