@@ -70,10 +70,17 @@ def check_resources(src: str, remarks: str) -> list:
     return kernels
 
 
+# Per-source extra flags.  Ring attention: keep MFMA operands and results in VGPRs (the kernel
+# fits in 205 of them at one wave per SIMD); left to itself the compiler puts the score and output
+# accumulators in AGPRs and copies them to VGPRs and back for every softmax step (~180 extra
+# instructions per 64-key block).
+SOURCE_FLAGS = {"mk_ring_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    out = _run([HIPCC, *HIP_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+    out = _run([HIPCC, *HIP_FLAGS, *SOURCE_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj])
     check_resources(src, out)
     return obj
 
