@@ -212,23 +212,50 @@ __device__ __forceinline__ void ra_compute_role(const RaParams& p, int slot, cha
                                                  16, L.v_dma, 0, 0, 0);
       }
     };
-    // one 64-key block from stage `lds`
+    // one 64-key block from stage `lds`.  Operand fragments are read ahead of their MFMAs (K two
+    // k-steps ahead, V^T one step ahead and its first step before the softmax, whose VALU work
+    // hides that latency); the scheduling fences keep the compiler from collapsing the order into
+    // read-wait-MFMA pairs (with one wave per SIMD every LDS latency would be exposed) or from
+    // hoisting every read at once (registers).
+    auto kread = [&](const char* lds, int kk, int f) -> bf16x8 {
+      const int c = 2 * kk + half, row = 32 * f + (lane & 31);
+      return *reinterpret_cast<const bf16x8*>(lds + L.k_rd + 32 * f * RA_ROW + ((c ^ (row & 15)) << 4));
+    };
+    auto vread = [&](const char* lds, int kk, bf16x8* v) {
+      const char* vb = lds + RA_BLK + 16 * kk * RA_ROW;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(const_cast<char*>(vb) + L.v_rd[i]));
+        const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(const_cast<char*>(vb) + L.v_rd[i] + 8 * RA_ROW));
+        v[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    };
     auto step = [&](const char* lds) {
       f32x16 s[2];
 #pragma unroll
       for (int f = 0; f < 2; ++f)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[f][r] = 0.f;
+      bf16x8 kb[3][2];
+      kb[0][0] = kread(lds, 0, 0);
+      kb[0][1] = kread(lds, 0, 1);
+      kb[1][0] = kread(lds, 1, 0);
+      kb[1][1] = kread(lds, 1, 1);
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
-        const int c = 2 * kk + half;
-#pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          const int row = 32 * f + (lane & 31);
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(lds + L.k_rd + 32 * f * RA_ROW + ((c ^ (row & 15)) << 4));
-          s[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[f], 0, 0, 0);
+        if (kk + 2 < 8) {
+          kb[(kk + 2) % 3][0] = kread(lds, kk + 2, 0);
+          kb[(kk + 2) % 3][1] = kread(lds, kk + 2, 1);
         }
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[kk % 3][0], qf[kk], s[0], 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[kk % 3][1], qf[kk], s[1], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      bf16x8 vf[2][4];
+      vread(lds, 0, vf[0]);
+      __builtin_amdgcn_sched_barrier(0);
       // online softmax of this lane's query over the block (the other half of its keys is in lane ^ 32)
       float mx = -__builtin_inff();
 #pragma unroll
@@ -262,6 +289,7 @@ __device__ __forceinline__ void ra_compute_role(const RaParams& p, int slot, cha
       // O^T += V^T P^T, P^T as hi + lo bf16 terms
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
+        if (kk + 1 < 4) vread(lds, kk + 1, vf[(kk + 1) & 1]);
         bf16x8 ph, pl;
         {
           u32x4 hw, lw;
@@ -275,17 +303,12 @@ __device__ __forceinline__ void ra_compute_role(const RaParams& p, int slot, cha
           ph = __builtin_bit_cast(bf16x8, hw);
           pl = __builtin_bit_cast(bf16x8, lw);
         }
-        const char* vb = lds + RA_BLK + 16 * kk * RA_ROW;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(const_cast<char*>(vb) + L.v_rd[i]));
-          const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(const_cast<char*>(vb) + L.v_rd[i] + 8 * RA_ROW));
-          const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
-          o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, ph, o[i], 0, 0, 0);
-          o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pl, o[i], 0, 0, 0);
+          o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kk & 1][i], ph, o[i], 0, 0, 0);
+          o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kk & 1][i], pl, o[i], 0, 0, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
 
