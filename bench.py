@@ -743,7 +743,7 @@ def main():
             "trace": {"kernel_span_us": round(us(rrec[:, 2].max() - rrec[:, 0].min()), 2),
                       "ring_landed_us": round(us(cp[:, 5].max() - rrec[:, 0].min()), 2) if len(cp) else None,
                       "shader_clock_GHz": round(clock_ghz(rrec), 3)},
-            "note": "8 ranks x 4096 tokens, 8 heads of 128, no mask; peers' K/V blocks land in ring order (32 copy "
+            "note": "8 ranks x 4096 tokens, 8 heads of 128, no mask; peers' K/V blocks land in ring order (192 copy "
                     "workgroups); flops = 4*heads*s_local*(world*s_local)*128 (P enters as two bf16 terms: the "
                     "P.V MFMAs are issued twice)"}
         link = {"gbps": LINK_GBPS, "note": "peer units paced to 7 xGMI links x 153 GB/s (mk_opts.arrival_gbps); "

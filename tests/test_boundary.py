@@ -346,7 +346,7 @@ def test_plan_ring_attention(hostlib):
     assert code == MK_OK
     assert (p["n_blk"], p["n_qt"], p["n_items"]) == (64, 32, 256)
     assert p["n_units"] == 8 * 8 * 64 * 2 and p["n_order"] == 7 * 8 * 64 * 2
-    assert (p["n_copy"], p["n_compute"]) == (32, 224) and p["emulated"] == 1
+    assert (p["n_copy"], p["n_compute"]) == (192, 64) and p["emulated"] == 1
     assert abs(p["scale"] - 128 ** -0.5) < 1e-7
     assert abs(ring(hostlib, scale=0.25)[1]["scale"] - 0.25) < 1e-9
     code, p = ring(hostlib, opts=Opts(arrival_mode=RESIDENT), ring_bufs=False)
