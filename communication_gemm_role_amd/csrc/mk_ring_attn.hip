@@ -21,7 +21,11 @@
 //                            first and then the ring steps in order, waiting for each peer block's
 //                            K and V flags before requesting it.
 //
-// Compute item: four waves, 32 queries each.  Per 64-key block (three LDS stages, DMA-fed):
+// Compute item: eight waves, two per SIMD: four query groups of 32 queries, each split over the
+// two 32-key halves of every 64-key block (wave w: queries 32*(w%4).., keys 32*(w/4).. of each
+// block), so one wave's softmax runs while the other wave of its SIMD issues MFMAs; the two halves'
+// softmax states are merged at the end of the item.  Per 32-key half-block (three LDS stages of
+// 64-key blocks, DMA-fed):
 //   S^T = K Q^T       (v_mfma_f32_32x32x16_bf16: A = K rows from LDS, B = Q^T kept in registers),
 //   online softmax    per query column: running max and sum in fp32, exp2 with the scale folded
 //                     into log2 units; a query's 64 values sit in two lanes (l and l + 32);
@@ -38,15 +42,17 @@
 
 namespace mk {
 
-constexpr int RA_NW = 4;             // waves per workgroup
+constexpr int RA_NW = 8;             // waves per workgroup: 4 query groups x 2 key halves
 constexpr int RA_THREADS = RA_NW * 64;
-constexpr int RA_BQ = RA_NW * 32;    // queries per item
+constexpr int RA_QG = 4;             // query groups of 32
+constexpr int RA_BQ = RA_QG * 32;    // queries per item
 constexpr int RA_BK = 64;            // keys per block
 constexpr int RA_ROW = RA_D * 2;     // bytes per K/V row (head dim 128, bf16)
 constexpr int RA_BLK = RA_BK * RA_ROW;  // 16 KiB: one block of K or of V
 constexpr int RA_STAGE = 2 * RA_BLK;    // K then V
 constexpr int RA_INSTR = RA_BLK / RA_NW / 1024;  // 1 KiB DMA instructions per wave per block
-static_assert(RA_INSTR == 4, "a wave moves 16 rows of K and 16 of V per block");
+static_assert(RA_INSTR == 2, "a wave moves 8 rows of K and 8 of V per block");
+constexpr int RA_CP_IPB = RA_STAGE / RA_NW / 1024;  // copy ring: KiB per wave and batch (a slot = a stage)
 
 // ------------------------------------------------------------------------------------------
 // copy role
@@ -91,7 +97,7 @@ __device__ __forceinline__ void ra_copy_role(const RaParams& p, int cid, char* s
                      (uint32_t)RA_BLK);
   };
   const uint64_t t0 = wall_ticks();
-  copy_ring<8, IPU>(n_mine, st0, st1, off, unit_at, src_of, dst_of,
+  copy_ring<RA_CP_IPB, IPU>(n_mine, st0, st1, off, unit_at, src_of, dst_of,
                     [&](int u) { flag_store(&p.flags[u], p.epoch); },
                     [&](int i) {  // queue entry i is arrival position cid + i * n_copy
                       if (p.pace_q16) wait_wall_until(t0 + (((uint64_t)(cid + i * p.n_copy) * p.pace_q16) >> 16));
@@ -108,10 +114,12 @@ struct RaLanes {
   uint32_t v_rd[4];          // V^T operand read per 32-wide d fragment (key step 0, first half)
 };
 
-__device__ __forceinline__ void ra_lanes(RaLanes& L, int lane) {
+__device__ __forceinline__ void ra_lanes(RaLanes& L, int lane, int wave) {
+  // instruction i of wave w moves rows 8w + 4i + (lane>>4) of the block (4 rows of 256 bytes)
   const int rr = lane >> 4, c = lane & 15;
 #pragma unroll
-  for (int i = 0; i < RA_INSTR; ++i) L.k_dma[i] = (uint32_t)rr * RA_ROW + (uint32_t)(c ^ ((4 * i + rr) & 15)) * 16u;
+  for (int i = 0; i < RA_INSTR; ++i)
+    L.k_dma[i] = (uint32_t)rr * RA_ROW + (uint32_t)(c ^ ((8 * (wave & 1) + 4 * i + rr) & 15)) * 16u;
   L.v_dma = (uint32_t)rr * RA_ROW + (uint32_t)(c ^ (4 * (rr & 3))) * 16u;
   // K as the A operand: row = key lane%32, 16-byte chunk 2*kk + lane/32 (swizzled by row & 15)
   L.k_rd = (uint32_t)(lane & 31) * RA_ROW;
@@ -146,8 +154,9 @@ __device__ __forceinline__ void ra_compute_role(const RaParams& p, int slot, cha
                                                 int* s_claim) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;
+  const int qg = wave & 3, kh = wave >> 2;  // query group, key half of every block
   RaLanes L;
-  ra_lanes(L, lane);
+  ra_lanes(L, lane, wave);
   const int C = p.n_compute;
   const int rs = ((C & 7) == 0) ? (slot & 7) * (C >> 3) + (slot >> 3) : slot;  // XCD-aware: one head per L2
   const int nb = p.world * p.n_blk;  // blocks per item
@@ -162,7 +171,7 @@ __device__ __forceinline__ void ra_compute_role(const RaParams& p, int slot, cha
       if (t >= p.n_items) break;
     }
     const int h = t / p.n_qt, qt = t - h * p.n_qt;
-    const int q0 = qt * RA_BQ + wave * 32;  // this wave's first query
+    const int q0 = qt * RA_BQ + qg * 32;  // this wave's first query
     // Q^T as the B operand, kept in registers: lane holds query q0 + lane%32, d = 16*kk + 8*half .. +7
     bf16x8 qf[8];
     {
@@ -203,7 +212,7 @@ __device__ __forceinline__ void ra_compute_role(const RaParams& p, int slot, cha
       const char* vb = reinterpret_cast<const char*>(ring ? p.v_ring + (size_t)j * shard_elems + e : p.v_src[j] + e);
 #pragma unroll
       for (int i = 0; i < RA_INSTR; ++i) {
-        const int r0 = wave * 16 + 4 * i;  // this instruction's 4 rows of the block
+        const int r0 = wave * 8 + 4 * i;  // this instruction's 4 rows of the block
         __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(kb + r0 * RA_ROW, 4u * RA_ROW),
                                                  (__attribute__((address_space(3))) void*)(dst + r0 * RA_ROW), 16,
                                                  L.k_dma[i], 0, 0, 0);
@@ -215,7 +224,7 @@ __device__ __forceinline__ void ra_compute_role(const RaParams& p, int slot, cha
     // one 64-key block from stage `lds`.  Operand fragments are read ahead of their MFMAs (K two
     // k-steps ahead, V^T one step ahead and its first step before the softmax, whose VALU work
     // hides that latency); the scheduling fences keep the compiler from collapsing the order into
-    // read-wait-MFMA pairs (with one wave per SIMD every LDS latency would be exposed) or from
+    // read-wait-MFMA pairs (with two waves per SIMD most LDS latency would still be exposed) or from
     // hoisting every read at once (registers).
     auto kread = [&](const char* lds, int kk, int f) -> bf16x8 {
       const int c = 2 * kk + half, row = 32 * f + (lane & 31);
@@ -232,50 +241,40 @@ __device__ __forceinline__ void ra_compute_role(const RaParams& p, int slot, cha
         v[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     };
+    // this wave's half (keys 32*kh .. 32*kh + 31) of one 64-key block from stage `lds`
     auto step = [&](const char* lds) {
-      f32x16 s[2];
+      f32x16 sc;
 #pragma unroll
-      for (int f = 0; f < 2; ++f)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[f][r] = 0.f;
-      bf16x8 kb[3][2];
-      kb[0][0] = kread(lds, 0, 0);
-      kb[0][1] = kread(lds, 0, 1);
-      kb[1][0] = kread(lds, 1, 0);
-      kb[1][1] = kread(lds, 1, 1);
+      for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+      bf16x8 kb[3];
+      kb[0] = kread(lds, 0, kh);
+      kb[1] = kread(lds, 1, kh);
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
-        if (kk + 2 < 8) {
-          kb[(kk + 2) % 3][0] = kread(lds, kk + 2, 0);
-          kb[(kk + 2) % 3][1] = kread(lds, kk + 2, 1);
-        }
-        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[kk % 3][0], qf[kk], s[0], 0, 0, 0);
-        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[kk % 3][1], qf[kk], s[1], 0, 0, 0);
+        if (kk + 2 < 8) kb[(kk + 2) % 3] = kread(lds, kk + 2, kh);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[kk % 3], qf[kk], sc, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
       bf16x8 vf[2][4];
-      vread(lds, 0, vf[0]);
+      vread(lds, 2 * kh, vf[0]);
       __builtin_amdgcn_sched_barrier(0);
-      // online softmax of this lane's query over the block (the other half of its keys is in lane ^ 32)
+      // online softmax of this lane's query over the half-block (the other 16 of its keys are in
+      // lane ^ 32)
       float mx = -__builtin_inff();
 #pragma unroll
-      for (int f = 0; f < 2; ++f)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s[f][r] *= p.scale_log2;
-          mx = fmaxf(mx, s[f][r]);
-        }
+      for (int r = 0; r < 16; ++r) {
+        sc[r] *= p.scale_log2;
+        mx = fmaxf(mx, sc[r]);
+      }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       float sum = 0.f;
 #pragma unroll
-      for (int f = 0; f < 2; ++f)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s[f][r] = __builtin_amdgcn_exp2f(s[f][r] - m_new);
-          sum += s[f][r];
-        }
+      for (int r = 0; r < 16; ++r) {
+        sc[r] = __builtin_amdgcn_exp2f(sc[r] - m_new);
+        sum += sc[r];
+      }
       sum += __shfl_xor(sum, 32);
       l_run = l_run * alpha + sum;
       m_run = m_new;
@@ -286,17 +285,17 @@ __device__ __forceinline__ void ra_compute_role(const RaParams& p, int slot, cha
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
-      // O^T += V^T P^T, P^T as hi + lo bf16 terms
+      // O^T += V^T P^T over the half-block's two 16-key steps, P^T as hi + lo bf16 terms
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        if (kk + 1 < 4) vread(lds, kk + 1, vf[(kk + 1) & 1]);
+      for (int j = 0; j < 2; ++j) {
+        if (j == 0) vread(lds, 2 * kh + 1, vf[1]);
         bf16x8 ph, pl;
         {
           u32x4 hw, lw;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             uint32_t hv, lv;
-            ra_split2(s[kk >> 1][8 * (kk & 1) + 2 * e], s[kk >> 1][8 * (kk & 1) + 2 * e + 1], hv, lv);
+            ra_split2(sc[8 * j + 2 * e], sc[8 * j + 2 * e + 1], hv, lv);
             hw[e] = hv;
             lw[e] = lv;
           }
@@ -305,8 +304,8 @@ __device__ __forceinline__ void ra_compute_role(const RaParams& p, int slot, cha
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kk & 1][i], ph, o[i], 0, 0, 0);
-          o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kk & 1][i], pl, o[i], 0, 0, 0);
+          o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j][i], ph, o[i], 0, 0, 0);
+          o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j][i], pl, o[i], 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -343,24 +342,48 @@ __device__ __forceinline__ void ra_compute_role(const RaParams& p, int slot, cha
       sub(q + 2, st2, st1);
     }
 
-    // a wave that timed out (or saw another workgroup's fault) voids the item for all four
+    // a wave that timed out (or saw another workgroup's fault) voids the item for all eight
     aborted = __syncthreads_or(aborted) != 0;
-    // O = O^T / l; lane holds query q0 + lane%32, d = 32*i + 8*(r/4) + 4*half + r%4
     if (!aborted) {
-      const float inv = 1.f / l_run;
-      float* orow = p.out + ((size_t)h * p.s_local + q0 + (lane & 31)) * RA_D;
+      // key half 1 hands its softmax state (running max and sum, O^T) to key half 0 of the same
+      // queries through the idle stage buffers (every wave has left the K loop's last barrier)
+      float* xo = reinterpret_cast<float*>((qg < 2 ? st0 : st1) + (qg & 1) * 16384);
+      float* xm = reinterpret_cast<float*>(st2) + qg * 128;
+      if (kh == 1) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          f32x4 v;
+          for (int r = 0; r < 16; ++r) xo[(i * 16 + r) * 64 + lane] = o[i][r];
+        xm[lane] = m_run;
+        xm[64 + lane] = l_run;
+      }
+      __syncthreads();
+      if (kh == 0) {
+        // merge: m = max(m0, m1); O^T = O0 2^(m0 - m) + O1 2^(m1 - m), the sums likewise
+        const float m1 = xm[lane], l1 = xm[64 + lane];
+        const float m = fmaxf(m_run, m1);
+        const float a0 = __builtin_amdgcn_exp2f(m_run - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
+        const float l = l_run * a0 + l1 * a1;
+        const float inv = 1.f / l;
+        // O = O^T / l; lane holds query q0 + lane%32, d = 32*i + 8*(r/4) + 4*half + r%4
+        float* orow = p.out + ((size_t)h * p.s_local + q0 + (lane & 31)) * RA_D;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = o[i][4 * g4 + e] * inv;
-          *reinterpret_cast<f32x4*>(orow + 32 * i + 8 * g4 + 4 * half) = v;
-        }
-      if (p.lse && half == 0)
-        p.lse[(size_t)h * p.s_local + q0 + lane] = (m_run + __builtin_amdgcn_logf(l_run)) * 0.69314718055994531f;
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            f32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * g4 + e;
+              v[e] = (o[i][r] * a0 + xo[(i * 16 + r) * 64 + lane] * a1) * inv;
+            }
+            *reinterpret_cast<f32x4*>(orow + 32 * i + 8 * g4 + 4 * half) = v;
+          }
+        if (p.lse && half == 0)
+          p.lse[(size_t)h * p.s_local + q0 + lane] = (m + __builtin_amdgcn_logf(l)) * 0.69314718055994531f;
+      }
     }
+    __syncthreads();  // the next item's loads reuse the stage buffers
     if (aborted) break;
     t = -1;
   }
@@ -372,7 +395,8 @@ __global__ __launch_bounds__(RA_THREADS, 1) void ring_attn_kernel(RaParams p) {
   __shared__ __attribute__((aligned(16))) char st2[RA_STAGE];
   __shared__ int s_claim;
   __shared__ int s_last;
-  static_assert(RA_THREADS * 8 * 1024 / 64 == RA_STAGE, "copy slots: 8 KiB per wave fill one stage buffer");
+  static_assert(RA_NW * RA_CP_IPB * 1024 == RA_STAGE && RA_CP_IPB % RA_INSTR == 0,
+                "copy slots: RA_CP_IPB KiB per wave fill one stage buffer with whole units");
   const int wg = blockIdx.x;
   if (wg < p.n_copy) {
     trace_begin(p.trace, ROLE_COPY);
