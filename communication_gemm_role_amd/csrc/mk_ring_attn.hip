@@ -260,19 +260,20 @@ __device__ __forceinline__ void ra_compute_role(const RaParams& p, int slot, cha
       __builtin_amdgcn_sched_barrier(0);
       // online softmax of this lane's query over the half-block (the other 16 of its keys are in
       // lane ^ 32)
+      // The scale (in log2 units; the planner admits only positive scales) is applied inside the
+      // exponent: the max is taken on the raw scores (rounding is monotone, so scaling the raw max
+      // gives the max of the scaled scores) and each weight is exp2(fma(s, scale, -max)).
+      const float c = p.scale_log2;
       float mx = -__builtin_inff();
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sc[r] *= p.scale_log2;
-        mx = fmaxf(mx, sc[r]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       float sum = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        sc[r] = __builtin_amdgcn_exp2f(sc[r] - m_new);
+        sc[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], c, -m_new));
         sum += sc[r];
       }
       sum += __shfl_xor(sum, 32);
