@@ -432,6 +432,8 @@ int mk_moe_dispatch_gemm(mk_ctx* ctx, void* stream, const uint16_t* const* token
   p.trace = opts ? opts->trace : nullptr;
   p.off_chunk_cnt = P.off_chunk_cnt;
   p.off_tile_cnt = P.off_tile_cnt;
+  p.off_chunk_rows = P.off_chunk_rows;
+  p.off_pos_pre = P.off_pos_pre;
   p.off_misc = P.off_misc;
   return mk::launch_moe(p, P.n_copy + P.n_compute, s) == hipSuccess ? MK_OK : MK_ERR_HIP;
 }

@@ -330,7 +330,7 @@ inline int plan_ring_attn(const Ws& ws, const Opts* o, const void* q, const void
 // ---- MoE dispatch + grouped GEMM ----------------------------------------------------------------
 struct MoePlan {
   int n_tokens, n_chunks, emulated, drop_pos, n_copy, n_compute, tiles_n, max_mtiles;
-  int off_misc, off_chunk_cnt, off_tile_cnt;
+  int off_misc, off_chunk_cnt, off_tile_cnt, off_chunk_rows, off_pos_pre;
   size_t counters_need;
 };
 
@@ -372,7 +372,9 @@ inline int plan_moe(const Ws& ws, const Opts* o, const void* const* tokens, int 
   P->off_misc = 0;
   P->off_chunk_cnt = 128;
   P->off_tile_cnt = P->off_chunk_cnt + P->n_chunks * n_local;
-  P->counters_need = (size_t)P->off_tile_cnt + (size_t)P->max_mtiles;
+  P->off_chunk_rows = P->off_tile_cnt + P->max_mtiles;
+  P->off_pos_pre = P->off_chunk_rows + P->n_chunks;
+  P->counters_need = (size_t)P->off_pos_pre + (size_t)P->n_chunks + 1;
   if (P->counters_need > ws.n_counters || ws.n_flags < 1) return MK_ERR_WORKSPACE;
   // 7/8 of the workgroups route and dispatch, then take grouped-GEMM tiles with the rest: the
   // m-tiles complete only near the end of the dispatch (token-ordered segments), so the compute

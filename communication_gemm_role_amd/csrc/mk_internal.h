@@ -126,6 +126,8 @@ struct MoeParams {
   // counter layout (offsets into `counters`)
   int off_chunk_cnt;   // [n_chunks * n_local] per-chunk routed counts
   int off_tile_cnt;    // [max_mtiles] rows landed per global m-tile
+  int off_chunk_rows;  // [n_chunks] routed rows (all local experts) per chunk
+  int off_pos_pre;     // [n_chunks + 1] rows of the arrival positions before each, in arrival order
   int off_misc;        // [0] route done, [1] exit count
 };
 

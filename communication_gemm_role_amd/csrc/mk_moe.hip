@@ -15,11 +15,13 @@
 //           into segment offsets and per-(chunk, expert) first slots: an exclusive scan in
 //           chunk order, i.e. ascending global token id inside each expert's segment.  It
 //           also numbers the m-tiles of every segment, then raises the scan flag.
-//   copy    after the scan flag, chunks in the caller's arrival order (copy workgroup cid takes
-//           positions cid, cid + n_copy, ...), a window of up to eight chunks at a time: each
-//           wave lists one chunk's routed (token, slot) rows, then all waves move the rows into
-//           their final slots of x_seg through LDS, and once the window's rows are stored they
-//           are added to their m-tiles' landed-row counters.  A copy workgroup with no chunks
+//   copy    after the scan flag, the routed rows in the caller's arrival order of chunks, split
+//           evenly: copy workgroup cid takes rows [R cid / n_copy, R (cid + 1) / n_copy) of that
+//           stream (the scan also lays out each arrival position's first row), a window of up to
+//           eight chunks at a time: each wave lists one chunk's routed (token, slot) rows, then
+//           all waves move the workgroup's part of them into their final slots of x_seg through
+//           LDS, and once the window's rows are stored they are added to their m-tiles'
+//           landed-row counters.  A copy workgroup with no chunks
 //           left joins the compute role on the tiles left over after every compute workgroup's
 //           first one.
 //   compute after the scan flag, (m-tile, n-tile) jobs of the ragged grouped GEMM: an m-tile
@@ -43,7 +45,9 @@ int moe_tile_m() { return MoeTile::BM; }
 int moe_tile_n() { return MoeTile::BN; }
 
 struct MoeShared {
-  int n_rows[MOE_WAVES];                 // rows of each window chunk
+  int n_rows[MOE_WAVES];                 // rows of each window chunk this workgroup moves
+  int lo[MOE_WAVES];                     // first of them in the chunk's row list
+  int p0, p1;                            // first and last arrival position of this workgroup's rows
   int pre[MOE_WAVES + 1];                // their prefix sums
   int chunk_first[MOE_WAVES][MOE_LMAX];  // first slot of each (window chunk, local expert)
   int chunk_cnt[MOE_WAVES][MOE_LMAX];    // rows of each (window chunk, local expert)
@@ -124,6 +128,11 @@ __device__ __forceinline__ void moe_route_chunk(const MoeParams& p, int chunk, i
   }
   const auto cr = make_rsrc(p.counters + p.off_chunk_cnt + (size_t)chunk * p.n_local, (uint32_t)p.n_local * 4u);
   bstore4_sc1(cr, (uint32_t)lane * 4u, mine);  // lanes past n_local fall outside the window
+  uint32_t tot = mine;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o);
+  const auto rr = make_rsrc(p.counters + p.off_chunk_rows + chunk, 4u);
+  if (lane == 0) bstore4_sc1(rr, 0u, tot);
 }
 
 template <int K>
@@ -197,6 +206,40 @@ __device__ __forceinline__ void moe_scan(const MoeParams& p, MoeShared& sh) {
     bstore4_sc1(so, (uint32_t)i * 4u, (uint32_t)sh.seg_off[i]);
     bstore4_sc1(tb, (uint32_t)i * 4u, (uint32_t)sh.tile_base[i]);
   }
+  // pass 3: first row of every arrival position in the stream of routed rows in arrival order
+  // (exclusive scan of the chunks' row totals taken in the caller's order), for the copy split
+  {
+    const auto rr = make_rsrc(p.counters + p.off_chunk_rows, (uint32_t)p.n_chunks * 4u);
+    const auto pp = make_rsrc(p.counters + p.off_pos_pre, (uint32_t)(p.n_chunks + 1) * 4u);
+    const int32_t* order = (p.emulated && p.order) ? p.order : nullptr;
+    uint32_t carry = 0;
+    for (int base = 0; base < p.n_chunks; base += MOE_THREADS) {
+      const int i = base + tid;
+      uint32_t v = 0;
+      if (i < p.n_chunks) {
+        const int c = order ? order[i] : i;
+        if (c >= 0 && c < p.n_chunks) v = bload4_sc1(rr, (uint32_t)c * 4u);
+      }
+      uint32_t inc = v;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(inc, o);
+        if (lane >= o) inc += y;
+      }
+      if (lane == 63) sh.pre[wave] = (int)inc;  // wave totals
+      __syncthreads();
+      uint32_t wpre = 0, btot = 0;
+      for (int w = 0; w < MOE_WAVES; ++w) {
+        const uint32_t t = (uint32_t)sh.pre[w];
+        wpre += w < wave ? t : 0u;
+        btot += t;
+      }
+      if (i < p.n_chunks) bstore4_sc1(pp, (uint32_t)i * 4u, carry + wpre + inc - v);
+      carry += btot;
+      __syncthreads();  // sh.pre is rewritten by the next group
+    }
+    if (tid == 0) bstore4_sc1(pp, (uint32_t)p.n_chunks * 4u, carry);
+  }
   wait_mem();
   __syncthreads();
   if (tid == 0) flag_store(&p.flags[0], p.epoch);
@@ -252,15 +295,24 @@ __device__ __forceinline__ void moe_list_chunk(const MoeParams& p, MoeShared& sh
   if (lane == 0) sh.n_rows[w] = n;
 }
 
-// Add the stored rows of window chunk j to its m-tiles' counters (wave 0; lane el: expert el).
+// Add the stored rows of window chunk j (its list entries [lo, lo + n_rows)) to their m-tiles'
+// counters (wave 0; lane el: expert el).  The list holds the chunk's rows expert by expert, so
+// expert el's rows are entries [cum, cum + cnt) with cum the rows of the experts before it.
 __device__ __forceinline__ void moe_raise_chunk(const MoeParams& p, const MoeShared& sh, int j, int lane) {
-  if (lane >= p.n_local) return;
-  const int cnt = sh.chunk_cnt[j][lane];
-  if (cnt == 0) return;
-  const int first = sh.chunk_first[j][lane];
+  const int cnt = lane < p.n_local ? sh.chunk_cnt[j][lane] : 0;
+  int inc = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(inc, o);
+    if (lane >= o) inc += y;
+  }
+  const int cum = inc - cnt;
+  const int a = max(sh.lo[j], cum), b = min(sh.lo[j] + sh.n_rows[j], cum + cnt);
+  if (lane >= p.n_local || b <= a) return;
+  const int first = sh.chunk_first[j][lane] + (a - cum);
   const int off_e = sh.seg_off[lane], tb = sh.tile_base[lane];
   int s = first;
-  const int s_end = min(first + cnt, p.capacity);
+  const int s_end = min(first + (b - a), p.capacity);
   while (s < s_end) {
     const int mt = (s - off_e) / MoeTile::BM;
     const int hi = min(s_end, off_e + (mt + 1) * MoeTile::BM);
@@ -294,7 +346,7 @@ __device__ __forceinline__ void moe_copy_window(const MoeParams& p, const MoeSha
     int j = 0;
 #pragma unroll
     for (int k = 1; k < MOE_WAVES; ++k) j += (k < n_win && sh.pre[k] <= r) ? 1 : 0;
-    const int idx = min(j * stride + (r - sh.pre[j]), MOE_LIST - 1);
+    const int idx = min(j * stride + sh.lo[j] + (r - sh.pre[j]), MOE_LIST - 1);
     const int2 e = list[idx];
     return r < R ? e : make_int2(-1, -1);
   };
@@ -356,30 +408,55 @@ __device__ __forceinline__ void moe_copy_window(const MoeParams& p, const MoeSha
   __syncthreads();  // the next window rewrites the lists and chunk tables
 }
 
-// Copy workgroup cid takes the arrival positions cid, cid + n_copy, cid + 2 n_copy, ... (the
-// caller's order, a round of positions across the copy workgroups at a time), in windows of as
-// many chunks as the listing waves and the LDS row list hold: every listing wave lists one chunk,
-// then all waves move the window's rows.  With the default role split a workgroup's positions
-// fit one window, so it pays one listing round trip and one pipeline fill and drain.
+// Copy workgroup cid takes rows [R cid / n_copy, R (cid + 1) / n_copy) of the routed rows taken
+// in the caller's arrival order of chunks (R of them), so every workgroup moves the same number of
+// rows whatever the chunks' sizes: it finds the arrival positions holding its first and last row
+// (the scan laid out each position's first row), and takes those positions in windows of as many
+// chunks as the listing waves and the LDS row list hold: every listing wave lists one chunk,
+// then all waves move the window's part of the rows.  With the default role split a workgroup's
+// rows span a few chunks: one window, one listing round trip and one pipeline fill and drain.
 template <int IPR>
 __device__ __forceinline__ void moe_dispatch(const MoeParams& p, int cid, MoeShared& sh, int2* list, char* st0,
                                              char* st1) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int stride = 64 * min(p.top_k, p.n_local);  // room for a chunk's largest row count
   const int cw = max(1, min(MOE_WAVES, MOE_LIST / stride));
-  const int n_mine = cid < p.n_chunks ? (p.n_chunks - cid + p.n_copy - 1) / p.n_copy : 0;
   const __attribute__((address_space(4))) int32_t* order = (const __attribute__((address_space(4))) int32_t*)p.order;
-  for (int w0 = 0; w0 < n_mine; w0 += cw) {
-    const int n_win = min(cw, n_mine - w0);
+  const auto pp = make_rsrc(p.counters + p.off_pos_pre, (uint32_t)(p.n_chunks + 1) * 4u);
+  const int total = (int)__builtin_amdgcn_readfirstlane(bload4_sc1(pp, (uint32_t)p.n_chunks * 4u));
+  const int r0 = (int)((int64_t)total * cid / p.n_copy), r1 = (int)((int64_t)total * (cid + 1) / p.n_copy);
+  if (r0 >= r1) return;
+  // the positions holding rows r0 and r1 - 1: position i holds rows [pre[i], pre[i + 1])
+  if (tid == 0) sh.p0 = sh.p1 = -1;
+  __syncthreads();
+  for (int base = 0; base < p.n_chunks; base += MOE_THREADS) {
+    const int i = base + tid;
+    if (i < p.n_chunks) {
+      const int a = (int)bload4_sc1(pp, (uint32_t)i * 4u), b = (int)bload4_sc1(pp, (uint32_t)(i + 1) * 4u);
+      if (a <= r0 && r0 < b) sh.p0 = i;
+      if (a < r1 && r1 <= b) sh.p1 = i;
+    }
+  }
+  __syncthreads();
+  const int p0 = __builtin_amdgcn_readfirstlane(*(volatile int*)&sh.p0);
+  const int p1 = __builtin_amdgcn_readfirstlane(*(volatile int*)&sh.p1);
+  if (p0 < 0 || p1 < p0) return;  // cannot happen for a consistent prefix
+  for (int w0 = p0; w0 <= p1; w0 += cw) {
+    const int n_win = min(cw, p1 - w0 + 1);
     if (wave < n_win) {
-      const int pos = cid + (w0 + wave) * p.n_copy;
+      const int pos = w0 + wave;
       int c = (p.emulated && order) ? order[pos] : pos;
       if (pos + 1 == p.drop_pos || c < 0 || c >= p.n_chunks) c = -1;  // testing: a dropped chunk never lands
-      if (c >= 0) {
+      const int pre = (int)bload4_sc1(pp, (uint32_t)pos * 4u), nxt = (int)bload4_sc1(pp, (uint32_t)(pos + 1) * 4u);
+      const int lo = max(r0, pre) - pre, hi = min(r1, nxt) - pre;
+      if (c >= 0 && hi > lo) {
         moe_list_chunk(p, sh, list + wave * stride, wave, c, lane);
       } else {
-        if (lane == 0) sh.n_rows[wave] = 0;
         for (int el = lane; el < p.n_local; el += 64) sh.chunk_cnt[wave][el] = 0;
+      }
+      if (lane == 0) {  // after the listing's own n_rows: this workgroup's part of the chunk
+        sh.lo[wave] = lo;
+        sh.n_rows[wave] = (c >= 0 && hi > lo) ? hi - lo : 0;
       }
     }
     __syncthreads();
