@@ -33,7 +33,7 @@ constexpr int CTR_RED_PRESUM = 114;  // next RS pre-sum job (64-row band of an o
 constexpr int CTR_RED_BAND0 = 128;   // RS: bands pre-summed per owned tile, [own tiles] from here
 constexpr int CTR_MLP_EXIT = 115;    // MLP workgroups that have exited
 constexpr int CTR_MLP_HREADY0 = 4096;  // MLP: up-projection tiles stored per 256-row block of H
-constexpr int CTR_RA_ITEM = 116;  // next leftover ring-attention item
+constexpr int CTR_RA_XITEM0 = 118;  // next leftover ring-attention item of each XCD's block, [8] from here
 constexpr int CTR_RA_EXIT = 117;  // ring-attention workgroups that have exited
 constexpr int RA_D = 128;         // ring attention: head dimension
 

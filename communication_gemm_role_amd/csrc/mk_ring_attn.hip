@@ -150,6 +150,37 @@ __device__ __forceinline__ void ra_split2(float a, float b, uint32_t& hi, uint32
   lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
 }
 
+// Items and XCDs.  Items (head-major, so consecutive items share a head's K and V) are dealt to
+// the 8 XCDs in contiguous blocks, and a workgroup on XCD x (workgroup w runs on XCD w % 8)
+// computes items of x's block, so a head's keys and values are pulled into one L2 (one head per
+// XCD at 8 heads).  The compute workgroups on XCD x take the head of its block as static items;
+// the rest is claimed from XCD x's counter by the workgroups on x that have finished their own
+// work (copy workgroups after landing their blocks), and by other XCDs' once theirs are exhausted.
+struct RaXcd {
+  int b, n, n_static;  // block [b, b + n) of XCD x; its first n_static items are static
+};
+__device__ __forceinline__ RaXcd ra_xcd(const RaParams& p, int x) {
+  RaXcd r;
+  r.b = x * (p.n_items >> 3) + min(x, p.n_items & 7);
+  r.n = (p.n_items >> 3) + (x < (p.n_items & 7) ? 1 : 0);
+  const int off = (x - p.n_copy) & 7;  // first compute workgroup on XCD x: id n_copy + off
+  const int c_x = p.n_compute > off ? (p.n_compute - off + 7) >> 3 : 0;
+  r.n_static = min(c_x, r.n);
+  return r;
+}
+// Thread 0: the next leftover item for a workgroup on XCD x (its own block first), or n_items.
+__device__ __forceinline__ int ra_claim(const RaParams& p, int x) {
+  for (int i = 0; i < 8; ++i) {
+    const int xx = (x + i) & 7;
+    const RaXcd z = ra_xcd(p, xx);
+    const uint32_t left = (uint32_t)(z.n - z.n_static);
+    if (left == 0 || flag_load(p.counters + CTR_RA_XITEM0 + xx) >= left) continue;
+    const uint32_t idx = atomic_add_agent(p.counters + CTR_RA_XITEM0 + xx, 1u);
+    if (idx < left) return z.b + z.n_static + (int)idx;
+  }
+  return p.n_items;
+}
+
 __device__ __forceinline__ void ra_compute_role(const RaParams& p, int slot, char* st0, char* st1, char* st2,
                                                 int* s_claim) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -157,15 +188,19 @@ __device__ __forceinline__ void ra_compute_role(const RaParams& p, int slot, cha
   const int qg = wave & 3, kh = wave >> 2;  // query group, key half of every block
   RaLanes L;
   ra_lanes(L, lane, wave);
-  const int C = p.n_compute;
-  const int rs = ((C & 7) == 0) ? (slot & 7) * (C >> 3) + (slot >> 3) : slot;  // XCD-aware: one head per L2
+  const int x = blockIdx.x & 7;
   const int nb = p.world * p.n_blk;  // blocks per item
   const size_t shard_elems = (size_t)p.heads * p.s_local * RA_D;
-  int t = (slot >= 0 && rs < p.n_items) ? rs : -1;
+  int t = -1;
+  if (slot >= 0) {  // this compute workgroup's static item: its index among XCD x's compute workgroups
+    const RaXcd z = ra_xcd(p, x);
+    const int j = (int)(blockIdx.x - (p.n_copy + ((x - p.n_copy) & 7))) >> 3;
+    t = j < z.n_static ? z.b + j : -1;
+  }
   bool first = slot >= 0;
   while (true) {
     if (t < 0) {
-      if (tid == 0) *s_claim = C + (int)atomic_add_agent(p.counters + CTR_RA_ITEM, 1u);
+      if (tid == 0) *s_claim = ra_claim(p, x);
       __syncthreads();
       t = *s_claim;
       if (t >= p.n_items) break;
@@ -415,7 +450,8 @@ __global__ __launch_bounds__(RA_THREADS, 1) void ring_attn_kernel(RaParams p) {
   if (threadIdx.x == 0) s_last = atomic_add_agent(p.counters + CTR_RA_EXIT, 1u) == gridDim.x - 1;
   __syncthreads();
   if (s_last && threadIdx.x == 0) {
-    __hip_atomic_store(p.counters + CTR_RA_ITEM, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int xx = 0; xx < 8; ++xx)
+      __hip_atomic_store(p.counters + CTR_RA_XITEM0 + xx, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(p.counters + CTR_RA_EXIT, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
