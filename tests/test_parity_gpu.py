@@ -253,7 +253,7 @@ def test_ar_full_sampled(ctx, mode):
 # ----------------------------------------------------------------------------------------------
 # MoE dispatch + grouped GEMM
 # ----------------------------------------------------------------------------------------------
-def _run_moe(ctx, shape, data, order=None, mode=None, cap=None):
+def _run_moe(ctx, shape, data, order=None, mode=None, cap=None, **extra):
     from gpu_util import dev_bf16, dev_f32, dev_i32
     mk = _mk()
     cap = shape.capacity if cap is None else cap
@@ -263,7 +263,7 @@ def _run_moe(ctx, shape, data, order=None, mode=None, cap=None):
     segt = torch.full((cap,), -7, dtype=torch.int32, device="cuda")
     x = torch.zeros((cap, shape.hidden), dtype=torch.bfloat16, device="cuda")
     y = torch.full((cap, shape.ffn), float("nan"), device="cuda")
-    opts = mk.Opts(arrival_mode=mode or 0, arrival_order=dev_i32(order) if order is not None else None)
+    opts = mk.Opts(arrival_mode=mode or 0, arrival_order=dev_i32(order) if order is not None else None, **extra)
     mk.mk_moe_dispatch_gemm(ctx, toks, dev_f32(data["logits"]), dev_f32(data["bias"]), shape.top_k,
                             shape.expert_begin, dev_bf16(data["w_up"]), topk, offs, segt, x, y, opts=opts)
     st = ctx.status()
@@ -289,6 +289,27 @@ def test_moe_small(ctx, kind, variant, trial):
         assert_exact(host(y)[:R], ref["y"].astype(np.float32), "y (integer)")
     else:
         assert_close(host(y)[:R], ref["y"], "y")
+
+
+@pytest.mark.parametrize("n_copy", [1, 2, 8, 40, 248])
+def test_moe_row_split_role_splits(ctx, n_copy):
+    """The dispatch splits the routed rows evenly over the copy workgroups: with 1 or 2 a workgroup's
+    rows span all 24 chunks or half of them, in several listing windows of 8 chunks, with 248 a
+    workgroup moves a few rows of one or two chunks; bit-exact layout and integer-exact grouped GEMM
+    either way."""
+    from gpu_util import assert_exact, host, host_bits, log
+    mk = _mk()
+    s = wl.MOE_SMALL
+    d = wl.gen_moe(s, run=3, kind="int")
+    log(f"moe row split n_copy={n_copy}: launching")
+    st, topk, offs, segt, x, y = _run_moe(ctx, s, d, order=wl.moe_arrival_order(s, 4, "flat"), n_copy_wg=n_copy)
+    assert st == mk.MK_OK
+    ref = oracle.moe_dispatch_gemm(d["tokens"], d["logits"], d["bias"], s.top_k, s.expert_begin, s.n_local, d["w_up"])
+    R = int(ref["seg_offsets"][-1])
+    assert_exact(host(offs), ref["seg_offsets"], "seg_offsets")
+    assert_exact(host(segt)[:R], ref["seg_token"], "seg_token")
+    assert_exact(host_bits(x)[:R], ref["x_seg"], "x_seg")
+    assert_exact(host(y)[:R], ref["y"].astype(np.float32), "y (integer)")
 
 
 def test_moe_forced_routing(ctx):
@@ -750,6 +771,25 @@ def test_ring_small(ctx, mode, variant):
                 assert_exact(host_bits(kr[j]), d["k_shards"][j], f"k_ring[{j}]")
                 assert_exact(host_bits(vr[j]), d["v_shards"][j], f"v_ring[{j}]")
         assert (host_bits(kr[s.rank]) == 0x7FC0).all()
+
+
+@pytest.mark.parametrize("n_copy", [8, 64, 248])
+def test_ring_role_splits(ctx, n_copy):
+    """32 items (8 heads x 4 query tiles) dealt to the XCDs in blocks of 4: with 248 copy workgroups
+    one item per XCD is static and three are claimed from the XCD's counter, with 64 or 8 every
+    item is static and the spare workgroups find nothing to claim; every split gives the oracle's
+    result."""
+    from gpu_util import assert_close, host, log
+    mk = _mk()
+    s = wl.RingShape(world=4, heads=8, s_local=512, rank=2)
+    d = wl.gen_ring(s, run=4)
+    log(f"ring role split n_copy={n_copy}: launching")
+    st, out, lse, _, _ = _run_ring(ctx, s, d, wl.ring_arrival_order(s, trial=1, variant="flat"), mk.MK_ARRIVAL_EMULATED,
+                                   n_copy_wg=n_copy)
+    assert st == mk.MK_OK
+    ref, lref = oracle.ring_attention(d["q"], d["k_shards"], d["v_shards"])
+    assert_close(host(out), ref, "out")
+    assert_close(host(lse), lref, "lse")
 
 
 def test_ring_scale_and_no_lse(ctx):
