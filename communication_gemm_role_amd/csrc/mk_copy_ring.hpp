@@ -1,5 +1,7 @@
 // Copy-role data mover shared by the AllGather and GEMM+ReduceScatter/AllReduce kernels: units
 // of a workgroup's arrival queue go global -> LDS (DMA) -> VGPRs -> global through two LDS slots.
+// A source unit is read once, so its loads are non-temporal (they should not displace the
+// compute role's operands from L2).
 //
 // Every wave moves its own share of each unit, so no LDS data crosses waves: while one batch is
 // being stored, the next is landing and the one after is requested, so up to two batches of loads
@@ -45,7 +47,7 @@ __device__ __forceinline__ void copy_ring(int n_units, char* slot0, char* slot1,
 #pragma unroll
       for (int i = 0; i < IPU; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            src, (__attribute__((address_space(3))) void*)(base + (j * IPU + i) * 1024), 16, off[i], 0, 0, 0);
+            src, (__attribute__((address_space(3))) void*)(base + (j * IPU + i) * 1024), 16, off[i], 0, 0, CP_NT);
     }
   };
   auto store = [&](int b, const char* slot) {
