@@ -310,8 +310,8 @@ __device__ __forceinline__ void ag_compute_role(const AgParams& p, int slot, cha
     // epilogue: the tile staged through LDS into row-contiguous 16-byte stores
     if constexpr (EPI == 0) {
       g.epilogue(st0, st1, wm, wn, lane, wave, [&](int row, int col, f32x4 v) {
-        if (!aborted && row < rows_valid && col < cols_valid)
-          *reinterpret_cast<f32x4*>(p.c + (size_t)(m0 + row) * p.n + (n0 + col)) = v;
+        if (!aborted && row < rows_valid && col < cols_valid)  // C is written once: streaming stores
+          __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p.c + (size_t)(m0 + row) * p.n + (n0 + col)));
       });
       __syncthreads();  // the next tile's prologue reuses the LDS
     } else {

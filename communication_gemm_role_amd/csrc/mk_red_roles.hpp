@@ -362,7 +362,8 @@ __device__ __forceinline__ void red_compute_role(const RedParams& p, int slot, c
           float* ob = p.outbox[owner] + (size_t)(m0 - owner * p.m_slice) * p.n + n0;
 #pragma unroll
           for (int q = 0; q < Q; ++q)
-            if (c[q] < cols_valid) *reinterpret_cast<f32x4*>(ob + (size_t)r[q] * p.n + c[q]) = v[q];
+            if (c[q] < cols_valid)  // written once, read by no one here: streaming stores
+              __builtin_nontemporal_store(v[q], reinterpret_cast<f32x4*>(ob + (size_t)r[q] * p.n + c[q]));
           return;
         }
       }
