@@ -564,7 +564,7 @@ __device__ __forceinline__ void moe_gemm_tiles(const MoeParams& p, MoeShared& sh
     k_loop(g, nk, st0, st1, st2, st2, st2, [](int) {}, load_step, [](int) {});
     g.epilogue(st0, st1, wm, wn, lane, wave, [&](int row, int col, f32x4 v) {
       if (row < rows_valid && col < cols_valid)
-        *reinterpret_cast<f32x4*>(p.y + (size_t)(row0 + row) * p.ffn + (n0 + col)) = v;
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p.y + (size_t)(row0 + row) * p.ffn + (n0 + col)));
     });
     __syncthreads();  // the next tile's prologue reuses the LDS
   }
