@@ -376,7 +376,8 @@ __device__ __forceinline__ void red_compute_role(const RedParams& p, int slot, c
                                    : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int q = 0; q < Q; ++q)
-          if (c[q] < cols_valid) *reinterpret_cast<f32x4*>(p.out + base + (size_t)r[q] * p.n + c[q]) = v[q] + t[q];
+          if (c[q] < cols_valid)  // the final value: nothing reads it back here
+            __builtin_nontemporal_store(v[q] + t[q], reinterpret_cast<f32x4*>(p.out + base + (size_t)r[q] * p.n + c[q]));
       } else {
         // values per group: G * (world - 1) loads in flight.  The eight-wave tile's accumulators
         // leave room for one value; the four-wave tile (one wave per SIMD) takes the whole slab.
@@ -402,7 +403,7 @@ __device__ __forceinline__ void red_compute_role(const RedParams& p, int slot, c
             for (int pq = 0; pq < MK_MAX_WORLD - 1; ++pq)
               if (pq < p.world - 1) s += t[gi][pq];
             if (c[g0 + gi] < cols_valid)
-              *reinterpret_cast<f32x4*>(p.out + base + (size_t)r[g0 + gi] * p.n + c[g0 + gi]) = s;
+              __builtin_nontemporal_store(s, reinterpret_cast<f32x4*>(p.out + base + (size_t)r[g0 + gi] * p.n + c[g0 + gi]));
           }
         }
       }

@@ -413,7 +413,7 @@ __device__ __forceinline__ void ra_compute_role(const RaParams& p, int slot, cha
               const int r = 4 * g4 + e;
               v[e] = (o[i][r] * a0 + xo[(i * 16 + r) * 64 + lane] * a1) * inv;
             }
-            *reinterpret_cast<f32x4*>(orow + 32 * i + 8 * g4 + 4 * half) = v;
+            __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(orow + 32 * i + 8 * g4 + 4 * half));
           }
         if (p.lse && half == 0)
           p.lse[(size_t)h * p.s_local + q0 + lane] = (m + __builtin_amdgcn_logf(l)) * 0.69314718055994531f;
