@@ -23,8 +23,14 @@ struct mk_ctx {
 
 namespace mk {
 
-// Context counters [0, 128) hold per-call bookkeeping, each left zero by the kernel that uses it:
-// MoE uses [0, 2+n_local] and [100, 101] (see mk_moe.hip); AllGather+GEMM uses [110, 111].
+// Context counters: every kernel leaves each counter it wrote at zero when its last workgroup
+// exits, so operations can share one context without a reset in between.  Layout:
+//   [0, 2 + n_local]   MoE: route-done, exits, m-tile base per local expert (n_local <= 64)
+//   [101]              MoE: next leftover grouped-GEMM tile
+//   [110, 125]         AllGather+GEMM, RS/AR, MLP and ring-attention claims and exit counts (below)
+//   [128, ...)         per-call tables: RS band counters (one per owned tile); MoE per-chunk counts,
+//                      m-tile row counters, chunk row totals and arrival-position prefix
+//   [4096, ...)        MLP: tiles stored per 256-row block of H
 constexpr int CTR_AG_TILE = 110;   // next leftover AG tile
 constexpr int CTR_AG_EXIT = 111;   // AG workgroups that have exited
 constexpr int CTR_RED_TILE = 112;  // next leftover RS/AR tile

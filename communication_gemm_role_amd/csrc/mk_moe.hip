@@ -1,10 +1,11 @@
 // MoE token dispatch + per-expert grouped GEMM, one rank's share, as one persistent launch.
 //
 // Operation (mKernel write-up, news.chathome.org page, five-fused-kernels table, MoE
-// Dispatch + GEMM row): tokens are routed to the ranks of their experts and the
-// per-expert grouped GEMM runs in the same kernel on tokens as they arrive, with no
-// staging-buffer round trip.  Here this rank owns experts [expert_begin, +n_local); the
-// tokens of every rank are device buffers and their arrival is the copy role.
+// Dispatch + GEMM row): for each local expert e, y[seg e] = x_seg[seg e] @ w_up[e], where
+// segment e of x_seg stacks the token rows whose top-k routing picked e.  The dispatch writes
+// each routed row straight into its place in x_seg and the grouped GEMM reads it from there,
+// in the same launch.  Here this rank owns experts [expert_begin, +n_local); the tokens of
+// every rank are device buffers and their arrival is the copy role.
 //
 // Phases and roles (workgroup ids [0, n_copy) route and copy; the rest compute):
 //   route   every route wave takes 64-token chunks: score = fp32(logit + bias) for every
@@ -34,7 +35,7 @@
 namespace mk {
 
 // 256 x 256 output tile, eight waves of 128 x 64, two-stage K loop
-using MoeTile = TileGemmDma<256, 256, 2, 4>;
+using MoeTile = TileGemmDma<mk_tiles::kMoe.bm, mk_tiles::kMoe.bn, mk_tiles::kMoe.wm, mk_tiles::kMoe.wn>;
 constexpr int MOE_WAVES = MoeTile::NW;
 constexpr int MOE_THREADS = MOE_WAVES * 64;
 constexpr int MOE_KMAX = 8;     // top-k
@@ -610,14 +611,17 @@ __global__ __launch_bounds__(MOE_THREADS, 1) void moe_kernel(MoeParams p) {
   if (threadIdx.x == 0) sh.is_last = atomic_add_agent(moe_misc(p) + 1, 1u) == (uint32_t)(gridDim.x - 1);
   __syncthreads();
   if (sh.is_last) {
-    const int n_mt_max = p.max_mtiles;
-    for (int i = threadIdx.x; i < n_mt_max; i += MOE_THREADS)
-      __hip_atomic_store(p.counters + p.off_tile_cnt + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (threadIdx.x == 0) {
-      __hip_atomic_store(moe_misc(p) + 0, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(moe_misc(p) + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(moe_misc(p) + MISC_TILE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    // Every counter this call wrote goes back to zero, not only the ones it needs zeroed itself:
+    // the per-chunk tables and m-tile counters share the context counters with other operations
+    // (the RS band counters, the MLP row-block counters), which start from zero.  The tables are
+    // contiguous, from the per-chunk counts to the end of the arrival-position prefix.
+    const int end = p.off_pos_pre + p.n_chunks + 1;
+    for (int i = p.off_chunk_cnt + threadIdx.x; i < end; i += MOE_THREADS)
+      __hip_atomic_store(p.counters + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // misc: route-done, exits, the m-tile base per expert, the leftover-tile claim
+    for (int i = threadIdx.x; i < 2 + p.n_local + 1; i += MOE_THREADS)
+      __hip_atomic_store(moe_misc(p) + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) __hip_atomic_store(moe_misc(p) + MISC_TILE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
