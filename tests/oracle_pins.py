@@ -495,7 +495,42 @@ def oracle_bf16(bits):
     return np.vectorize(lambda x: lut[int(x)], otypes=[np.float64])(b)
 
 
-ALL_PINS = [pin_bf16, pin_ag, pin_rs, pin_ar, pin_moe, pin_mlp, pin_ring]
+def pin_acceptance(impl):
+    """RMS and the relative error that every float parity verdict uses."""
+    g = _golden("acceptance_hand.json")
+    for case in g["cases"]:
+        ref = np.asarray(case["ref"], np.float64)
+        out = np.asarray(case["out"], np.float64)
+        want_rms = math.sqrt(case["rms_sq"])
+        assert abs(impl.rms(ref) - want_rms) <= 1e-15 * want_rms, (case["ref"], impl.rms(ref), want_rms)
+        want_err = case["err_num"] / want_rms
+        got = impl.max_rel_err(out, ref)
+        assert abs(got - want_err) <= 1e-15 * max(want_err, 1e-300), (case["out"], got, want_err)
+    # brute force on a random buffer: a Python loop over the elements, math.fsum for the mean square
+    rng = np.random.default_rng(7)
+    ref = rng.normal(0.0, 3.0, size=(13, 17))
+    out = ref + rng.normal(0.0, 1e-3, size=ref.shape)
+    flat_r = [float(x) for x in ref.ravel()]
+    flat_o = [float(x) for x in out.ravel()]
+    r_bf = math.sqrt(math.fsum(x * x for x in flat_r) / len(flat_r))
+    e_bf = max(abs(o - r) for o, r in zip(flat_o, flat_r)) / r_bf
+    assert abs(impl.rms(ref) - r_bf) <= 1e-13 * r_bf
+    assert abs(impl.max_rel_err(out, ref) - e_bf) <= 1e-12 * e_bf
+    # the error is taken against the reference's RMS, not the output's: a large output that hits
+    # the reference within 1e-3 of its RMS passes, whatever its own size
+    assert impl.max_rel_err(ref * (1 + 1e-6), ref) <= 1e-6 * np.max(np.abs(ref)) / r_bf * (1 + 1e-9)
+    # homogeneity: RMS scales with |c|, the relative error does not change
+    assert abs(impl.rms(-4.0 * ref) - 4.0 * r_bf) <= 1e-13 * r_bf
+    assert abs(impl.max_rel_err(-4.0 * out, -4.0 * ref) - e_bf) <= 1e-12 * e_bf
+    # one element off by d in an otherwise exact buffer of n equal values v: error d / |v|
+    v = np.full(1000, -0.5)
+    o = v.copy()
+    o[537] += 0.002
+    assert abs(impl.max_rel_err(o, v) - 0.004) <= 1e-15
+    assert impl.max_rel_err(v, v) == 0.0
+
+
+ALL_PINS = [pin_bf16, pin_ag, pin_rs, pin_ar, pin_moe, pin_mlp, pin_ring, pin_acceptance]
 
 
 def run_all(impl):

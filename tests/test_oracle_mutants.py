@@ -260,7 +260,65 @@ def _ring_values_are_keys(q, k_shards, v_shards, scale=None):
     return M.ring_attention(q, k_shards, k_shards, scale=scale)
 
 
+def _rms_no_sqrt(x):
+    x = np.asarray(x, dtype=np.float64)
+    return float(np.mean(x * x)) if x.size else 0.0
+
+
+def _rms_mean_abs(x):
+    x = np.asarray(x, dtype=np.float64)
+    return float(np.mean(np.abs(x))) if x.size else 0.0
+
+
+def _rms_sum_not_mean(x):
+    x = np.asarray(x, dtype=np.float64)
+    return float(np.sqrt(np.sum(x * x))) if x.size else 0.0
+
+
+def _rms_max(x):
+    x = np.asarray(x, dtype=np.float64)
+    return float(np.max(np.abs(x))) if x.size else 0.0
+
+
+def _err_max_abs_out(out, ref):
+    r = M.rms(ref)
+    d = float(np.max(np.abs(np.asarray(out, np.float64))))
+    return d / r if r > 0 else d
+
+
+def _err_rms_of_out(out, ref):
+    out = np.asarray(out, np.float64)
+    d = float(np.max(np.abs(out - np.asarray(ref, np.float64))))
+    r = M.rms(out)
+    return d / r if r > 0 else d
+
+
+def _err_signed(out, ref):
+    d = float(np.max(np.asarray(out, np.float64) - np.asarray(ref, np.float64)))
+    r = M.rms(ref)
+    return d / r if r > 0 else d
+
+
+def _err_mean_diff(out, ref):
+    d = float(np.mean(np.abs(np.asarray(out, np.float64) - np.asarray(ref, np.float64))))
+    r = M.rms(ref)
+    return d / r if r > 0 else d
+
+
+def _err_absolute(out, ref):
+    return float(np.max(np.abs(np.asarray(out, np.float64) - np.asarray(ref, np.float64))))
+
+
 MUTANTS = {
+    "rms_no_sqrt": ("rms", _rms_no_sqrt),
+    "rms_mean_abs": ("rms", _rms_mean_abs),
+    "rms_sum_not_mean": ("rms", _rms_sum_not_mean),
+    "rms_is_max_abs": ("rms", _rms_max),
+    "err_max_abs_out": ("max_rel_err", _err_max_abs_out),
+    "err_rms_of_out": ("max_rel_err", _err_rms_of_out),
+    "err_signed_difference": ("max_rel_err", _err_signed),
+    "err_mean_difference": ("max_rel_err", _err_mean_diff),
+    "err_not_relative": ("max_rel_err", _err_absolute),
     "ring_no_scale": ("ring_attention", _ring_no_scale),
     "ring_scale_ignored": ("ring_attention", _ring_scale_ignored),
     "ring_local_only": ("ring_attention", _ring_local_only),
