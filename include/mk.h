@@ -12,11 +12,17 @@
  *   mk_gemm_ar            GEMM + AllReduce
  *   mk_moe_dispatch_gemm  MoE token dispatch + per-expert grouped GEMM
  *
- * and, from the same page's roadmap section (the transformer-layer megakernel as the next
- * step), the MLP block built from two of them in one launch:
+ * the fifth row of the same table (Ring Attention):
+ *
+ *   mk_ring_attention     ring K/V exchange + FlashAttention (sequence parallel)
+ *
+ * from the same page's roadmap section (the transformer-layer megakernel as the next step), the
+ * MLP block built from two of the fused ops in one launch:
  *
  *   mk_mlp_ag_rs          AllGather + up-projection GEMM, gelu, down-projection GEMM + ReduceScatter
- *   mk_ring_attention     ring K/V exchange + FlashAttention (sequence parallel)
+ *
+ * and, from section "mKernel的功能" (the number of SMs per role is chosen per shape), the tuners:
+ *
  *   mk_*_tune             time candidate role splits of an operation and report the fastest
  *
  * Each call is ONE kernel launch.  Inside it, workgroups take a role from their
@@ -143,15 +149,20 @@ const char* mk_strerror(int code);
  * kernels' pattern: a payload is written once per launch and never read before its flag);
  * mode 1: the same addresses every round, device-coherent consumer loads; mode 2: the same
  * addresses with ordinary loads (diagnostic only: another XCD's L2 may hold a stale copy).
+ * Modes 3-5 use fresh addresses and the kernels' own load paths: mode 3, the consumer reads the
+ * payload by a buffer load straight into LDS (as the compute role stages its operands); mode 4,
+ * the producer also lands it as the copy role does (non-temporal buffer load of a source unit
+ * into LDS, then write-through stores); mode 5, the producer publishes by a counter increment
+ * and the consumer waits for the count before its LDS load (the MoE m-tile handshake).
  * Allocates and frees its own device memory and synchronises the device.  Returns MK_OK with
  * *mismatches = payload words that did not match and *timeouts = 1 if a wait hit the 2 s watchdog;
- * MK_ERR_INVALID_ARG for mode not in [0,2], pairs not in [1,128], rounds < 1, or
- * pairs*rounds > 262144 in mode 0; MK_ERR_HIP on a runtime failure. */
+ * MK_ERR_INVALID_ARG for mode not in [0,5], pairs not in [1,128], rounds < 1, or
+ * pairs*rounds > 262144 with fresh addresses (131072 in mode 4); MK_ERR_HIP on a runtime failure. */
 int mk_selftest_flags(int device, int mode, int pairs, int rounds, int64_t* mismatches, int64_t* timeouts);
 
 /* ---- AllGather + GEMM ----------------------------------------------------------------
- * Five-fused-kernels table, AllGather + GEMM row: every rank holds one row shard of A; while
- * the shards of the other ranks arrive, the local GEMM consumes each A tile as soon as it lands.
+ * Five-fused-kernels table, AllGather + GEMM row: c = [A_0; ...; A_{world-1}] @ b with A_r the row
+ * shard of rank r; a K-unit of a tile's rows is multiplied as soon as it has landed.
  *   a_shards[r]  [m_shard, k] bf16, r in [0, world)     (host array of device pointers)
  *   b            [k, n] bf16 (the local, fully resident operand)
  *   a_gathered   [world*m_shard, k] bf16, OUT: shard r lands at rows [r*m_shard, (r+1)*m_shard)
@@ -166,8 +177,9 @@ int mk_ag_gemm(mk_ctx* ctx, void* stream, const uint16_t* const* a_shards, int w
                int k, const uint16_t* b, int n, uint16_t* a_gathered, float* c, const mk_opts* opts);
 
 /* ---- GEMM + ReduceScatter -------------------------------------------------------------
- * Five-fused-kernels table, GEMM + ReduceScatter row: C = A @ B is reduce-scattered; each output
- * tile is reduced and handed to its owner as soon as it is produced.  Rank j owns rows
+ * Five-fused-kernels table, GEMM + ReduceScatter row: the sum over ranks of the partials A_j @ B_j,
+ * each rank receiving only its own row slice of it; a tile of this rank's partial is added in or
+ * sent on right after its K loop.  Rank j owns rows
  * [j*m/world, (j+1)*m/world).  This call is rank `rank`'s share:
  *   a [m, k] bf16, b [k, n] bf16                 local operands; P = a @ b is this rank's partial
  *   peer_partials[j] [m/world, n] fp32, j != rank  peer j's partial of THIS rank's slice
@@ -184,8 +196,8 @@ int mk_gemm_rs(mk_ctx* ctx, void* stream, const uint16_t* a, const uint16_t* b, 
                const mk_opts* opts);
 
 /* ---- GEMM + AllReduce -----------------------------------------------------------------
- * Five-fused-kernels table, GEMM + AllReduce row: C = A @ B in one launch, and every output tile
- * is reduced with the partial outputs of all ranks as soon as it is produced.
+ * Five-fused-kernels table, GEMM + AllReduce row: every rank receives the whole sum over ranks of
+ * the partials A_j @ B_j; a tile of this rank's partial is added in right after its K loop.
  *   a [m, k] bf16, b [k, n] bf16; peer_partials[j] [m, n] fp32 for j != rank
  *   out [m, n] fp32, OUT: a @ b + sum_j peer_partials[j]
  * Landing units and modes as in mk_gemm_rs, over [m, n] partials.
@@ -194,9 +206,9 @@ int mk_gemm_ar(mk_ctx* ctx, void* stream, const uint16_t* a, const uint16_t* b, 
                int rank, const float* const* peer_partials, float* out, const mk_opts* opts);
 
 /* ---- MoE dispatch + grouped GEMM ------------------------------------------------------
- * Five-fused-kernels table, MoE Dispatch + GEMM row: tokens are routed to their experts and the
- * per-expert grouped GEMM runs in the same kernel on tokens as they arrive, with no staging
- * round trip (each token row lands directly in its final slot).  This call is the share of the
+ * Five-fused-kernels table, MoE Dispatch + GEMM row: route every token to its top_k experts, gather
+ * the rows routed to each local expert into one segment and multiply the segment by that
+ * expert's weight, in one launch (each token row lands directly in its final slot).  This call is the share of the
  * rank that owns experts [expert_begin, expert_begin + n_local_experts):
  *   tokens[r] [t_local, hidden] bf16, r in [0, world); global token id g = r*t_local + i
  *   logits [world*t_local, n_experts] fp32; bias [n_experts] fp32
@@ -247,9 +259,9 @@ int mk_mlp_ag_rs(mk_ctx* ctx, void* stream, const uint16_t* const* a_shards, int
                  uint16_t* a_gathered, uint16_t* h, float* owned_out, float* const* outbox, const mk_opts* opts);
 
 /* ---- Ring attention ------------------------------------------------------------------
- * Five-fused-kernels table, Ring Attention row: sequence-parallel attention across ranks, the
- * ring rotating K/V blocks while the local FlashAttention consumes the block received before,
- * both inside one persistent kernel.  Rank `rank`'s share, no mask:
+ * Five-fused-kernels table, Ring Attention row: sequence-parallel attention of this rank's queries
+ * over every rank's keys and values, the peers' K/V blocks travelling round the ring and each
+ * block attended to once it is present, in one launch.  Rank `rank`'s share, no mask:
  *   q [heads, s_local, head_dim] bf16                  this rank's queries
  *   k_shards[j], v_shards[j] [heads, s_local, head_dim] bf16, j in [0, world): every rank's keys
  *                         and values (entry `rank` is this rank's own, read in place)

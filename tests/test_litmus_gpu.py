@@ -6,7 +6,10 @@ on different XCDs exchange thousands of payloads.
   launch and never read before its flag) must never mismatch;
 * reused addresses + device-coherent loads must never mismatch;
 * reused addresses + ordinary loads is only reported: another XCD's L2 may keep a stale copy of a
-  rewritten line, which is why no kernel re-reads an address rewritten within the launch.
+  rewritten line, which is why no kernel re-reads an address rewritten within the launch;
+* fresh addresses over the load paths the kernels take must never mismatch: the compute role's
+  buffer loads straight into LDS, the copy role's non-temporal loads into LDS followed by
+  write-through stores, and the MoE counter handshake (atomic increment, count wait).
 """
 import pytest
 
@@ -33,6 +36,15 @@ def test_reused_addresses_coherent_loads():
     assert timeouts == 0 and mismatches == 0
 
 
+@pytest.mark.parametrize("mode,what", [(3, "consumer reads by buffer load into LDS (compute role operands)"),
+                                       (4, "producer lands by non-temporal DMA + write-through stores (copy role)"),
+                                       (5, "counter increment and count wait, then LDS load (MoE m-tiles)")])
+def test_fresh_addresses_kernel_load_paths(mode, what):
+    mk = _mk()
+    mismatches, timeouts = mk.mk_selftest_flags(0, mode=mode, pairs=64, rounds=2048)
+    assert timeouts == 0 and mismatches == 0, what
+
+
 def test_reused_addresses_plain_loads_is_reported(capsys):
     mk = _mk()
     mismatches, timeouts = mk.mk_selftest_flags(0, mode=2, pairs=64, rounds=4096)
@@ -42,6 +54,7 @@ def test_reused_addresses_plain_loads_is_reported(capsys):
 
 def test_selftest_rejects_bad_arguments():
     mk = _mk()
-    for kw in (dict(mode=3), dict(pairs=0), dict(pairs=129), dict(rounds=0), dict(mode=0, pairs=128, rounds=4096)):
+    for kw in (dict(mode=6), dict(mode=-1), dict(pairs=0), dict(pairs=129), dict(rounds=0),
+               dict(mode=0, pairs=128, rounds=4096), dict(mode=4, pairs=128, rounds=2048)):
         with pytest.raises(mk.MkError):
             mk.mk_selftest_flags(0, **kw)
