@@ -96,7 +96,7 @@ def parse():
     ap.add_argument("--only", default="",
                     help="profiling: run only this op (ag, ag_resident, ag_identity, rs, ar, rs_emulated, ar_emulated, "
                          "moe, mlp, mlp_resident, mlp_unfused, ag_link, rs_link, ar_link, mlp_link, ring, ring_resident, "
-                         "ring_link, vendor, copy)")
+                         "ring_link, vendor, rs_unfused, ar_unfused, copy)")
     ap.add_argument("--n-copy", type=int, default=0, help="with --only *_link: copy workgroups (0: default)")
     return ap.parse_args()
 
@@ -304,6 +304,35 @@ def setup_reduce(ctx, op: str, emulated: bool = False, n_reduce: int = 0, gbps: 
             out = torch.empty((s.m, s.n), device="cuda")
             calls.append(lambda a=a, b=b, pe=peers, out=out: mk.mk_gemm_ar(ctx, a, b, s.world, 0, pe, out, opts=opts))
     return s, calls, opts
+
+
+def setup_reduce_unfused(op: str):
+    """Comparator: the vendor BLAS GEMM (torch.matmul, bf16 out) of this rank's partial, then a
+    separate sum of the owned rows with the resident peer partials (torch adds, fp32): the
+    reduction after the GEMM at kernel boundaries.  RS's outbox slices are left as views of the
+    GEMM output (a collective would send them)."""
+    import torch
+    import workloads as wl
+    s = wl.RS_DOWN if op == "rs" else wl.AR_DECODE
+    d = wl.gen_reduce(s, op, run=0)
+    a0, b0 = _bf16(d["a"]), _bf16(d["b"])
+    p0 = [_f32(p) for p in d["peers"] if p is not None]
+    rows = s.m_slice if op == "rs" else s.m
+    calls = []
+    for _ in range(N_SETS):
+        a, b = a0.clone(), b0.clone()
+        peers = [p.clone() for p in p0]
+        prod = torch.empty((s.m, s.n), dtype=torch.bfloat16, device="cuda")
+        out = torch.empty((rows, s.n), dtype=torch.float32, device="cuda")
+
+        def step(a=a, b=b, pe=peers, prod=prod, out=out):
+            torch.matmul(a, b, out=prod)
+            torch.add(pe[0], pe[1], out=out)
+            for p in pe[2:]:
+                out.add_(p)
+            out.add_(prod[:rows])
+        calls.append(step)
+    return s, calls
 
 
 def reduce_bytes(sh, op: str, emulated: bool):
@@ -600,6 +629,8 @@ def main():
             _, calls, _ = setup_mlp(ctx, resident=a.only == "mlp_resident")
         elif a.only == "mlp_unfused":
             _, calls = setup_mlp_unfused(ctx)
+        elif a.only in ("rs_unfused", "ar_unfused"):
+            _, calls = setup_reduce_unfused(a.only[:2])
         elif a.only == "vendor":
             _, calls = setup_vendor_gemm()
         elif a.only == "copy":
@@ -694,6 +725,13 @@ def main():
                     "hbm_frac": round(total / (k_ * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
                 del cr
                 torch.cuda.empty_cache()
+            _, cu = setup_reduce_unfused(op)
+            tu = time_stats(cu, 100, 3, a.settle_ms)
+            sec[op]["unfused_ms"] = round(tu["kernel_ms"], 5)
+            sec[op]["unfused_note"] = ("comparator: torch.matmul bf16 -> bf16, then torch adds of the peer "
+                                       "partials into the owned rows (fp32), separate launches")
+            del cu
+            torch.cuda.empty_cache()
         sm, offs, cm, mopts = setup_moe(ctx)
         tm = time_stats(cm, 100, 2, a.settle_ms)
         o = offs[0].cpu().numpy()

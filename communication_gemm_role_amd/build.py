@@ -5,6 +5,8 @@
 libmk.so        every HIP translation unit of csrc/ plus the C ABI, for --offload-arch=gfx950
 libmk_host.so   csrc/mk_host_check.cpp built with g++ alone (no HIP), for CPU tests of the
                 argument validation and planning; --sanitize-host adds ASan/UBSan to it
+_build/mk_host_plan_test   (tests only) csrc/mk_host_plan_test.cpp under ASan/UBSan, see
+                build_host_plan_test
 """
 from __future__ import annotations
 
@@ -103,6 +105,21 @@ def build_host_lib(sanitize: bool = False) -> str:
     _run(cmd + [os.path.join(CSRC, "mk_host_check.cpp"), "-o", tmp])
     os.replace(tmp, HOSTLIB)
     return HOSTLIB
+
+
+PLAN_TEST = os.path.join(BUILD, "mk_host_plan_test")
+
+
+def build_host_plan_test() -> str:
+    """The CPU driver over the host planning functions (csrc/mk_host_plan_test.cpp), built with g++
+    alone under AddressSanitizer and UndefinedBehaviorSanitizer, every finding fatal."""
+    os.makedirs(BUILD, exist_ok=True)
+    cmd = ["g++", "-O1", "-g", "-std=c++17", "-Wall", "-I", CSRC, "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", "-fno-omit-frame-pointer"]
+    tmp = PLAN_TEST + ".tmp"
+    _run(cmd + [os.path.join(CSRC, "mk_host_plan_test.cpp"), "-o", tmp])
+    os.replace(tmp, PLAN_TEST)
+    return PLAN_TEST
 
 
 def build(sanitize_host: bool = False) -> None:

@@ -1,9 +1,10 @@
 // AllGather + GEMM, one rank's share, as one persistent launch (roles in mk_ag_roles.hpp).
 //
 // Operation (mKernel write-up, news.chathome.org page, five-fused-kernels table,
-// AllGather + GEMM row): each rank holds one row shard of A; while the other shards
-// arrive, the local GEMM consumes A tiles as soon as they land.  Here the other ranks'
-// shards are device buffers and "arrival" is the copy role.
+// AllGather + GEMM row): C = [A_0; A_1; ...; A_{W-1}] @ B, rank r holding the row shard A_r
+// and B being local.  The product does not wait for the gather: a K-unit of a tile's rows
+// enters the tile's K loop as soon as it is present.  Here the other ranks' shards are
+// device buffers and their arrival is the copy role.
 #include "mk_ag_roles.hpp"
 
 namespace mk {

@@ -2,9 +2,10 @@
 // ag_gemm_kernel (mk_ag_gemm.hip) and the MLP kernel (mk_mlp.hip).
 //
 // Operation (mKernel write-up, news.chathome.org page, five-fused-kernels table,
-// AllGather + GEMM row): each rank holds one row shard of A; while the other shards
-// arrive, the local GEMM consumes A tiles as soon as they land.  Here the other ranks'
-// shards are device buffers and "arrival" is the copy role.
+// AllGather + GEMM row): C = [A_0; A_1; ...; A_{W-1}] @ B, rank r holding the row shard A_r
+// and B being local.  The product does not wait for the gather: a K-unit of a tile's rows
+// enters the tile's K loop as soon as it is present.  Here the other ranks' shards are
+// device buffers and their arrival is the copy role.
 //
 // Roles (section "mKernel的功能" of the same page: CTAs self-assign roles, a per-shape
 // number of SMs per role):
@@ -31,7 +32,7 @@
 namespace mk {
 
 // 256 x 256 output tile, eight waves of 128 x 64: one k-step moves 64 KiB of operands for 8.4 MFLOP.
-using AgTile = TileGemmDma<256, 256, 2, 4>;
+using AgTile = TileGemmDma<mk_tiles::kAg.bm, mk_tiles::kAg.bn, mk_tiles::kAg.wm, mk_tiles::kAg.wn>;
 constexpr int AG_THREADS = AgTile::NW * 64;
 
 // ------------------------------------------------------------------------------------------

@@ -293,7 +293,10 @@ int mk_mlp_ag_rs(mk_ctx* ctx, void* stream, const uint16_t* const* a_shards, int
                  uint16_t* a_gathered, uint16_t* h, float* owned_out, float* const* outbox, const mk_opts* opts) {
   if (!ctx) return MK_ERR_INVALID_ARG;
   const mkh::Opts o = to_opts(opts);
-  const int M = world * m_shard;  // validated by the plan; only picks the tile shapes here
+  // only picks the tile shapes here (the plan validates the sizes); widened so that no argument
+  // can overflow it
+  const long long m_all = (long long)world * (long long)m_shard;
+  const int M = m_all > 0x7fffffffLL ? 0x7fffffff : (int)m_all;
   mkh::MlpPlan P;
   int code = mkh::plan_mlp(ws_of(ctx), opts ? &o : nullptr, (const void* const*)a_shards, world, rank, m_shard, k,
                            b_up, n_up, b_down, n_out, (const void* const*)peer_partials, a_gathered, h, owned_out,

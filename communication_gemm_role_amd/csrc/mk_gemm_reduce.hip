@@ -2,9 +2,10 @@
 // mk_red_roles.hpp).
 //
 // Operations (mKernel write-up, news.chathome.org page, five-fused-kernels table, GEMM +
-// AllReduce and GEMM + ReduceScatter rows): C = A @ B is computed in one launch and each
-// output tile is reduced with the other ranks' partials as soon as it is produced; for the
-// reduce-scatter every tile goes to the rank that owns its rows.
+// AllReduce and GEMM + ReduceScatter rows): rank j holds a partial P_j = A_j @ B_j of the same
+// [M, N] output.  AllReduce: every rank ends with sum_j P_j.  ReduceScatter: rank r ends with
+// sum_j P_j on its own row slice only.  A tile of P enters the reduction right after its K loop,
+// inside the same launch.
 #include "mk_red_roles.hpp"
 
 namespace mk {

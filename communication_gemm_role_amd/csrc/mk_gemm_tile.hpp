@@ -25,6 +25,7 @@
 // flight) measured slower, its A rows giving half lines.
 #pragma once
 #include "mk_device.hpp"
+#include "mk_tiles.h"
 
 namespace mk {
 

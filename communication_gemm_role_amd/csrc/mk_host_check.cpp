@@ -3,6 +3,7 @@
 // returns the status code the matching mk_* entry point would return before launching, and
 // fills `out` with the plan fields in declaration order.
 #include "mk_host_logic.h"
+#include "mk_tiles.h"
 
 extern "C" {
 
@@ -41,10 +42,11 @@ int mkh_plan_mlp(size_t n_flags, size_t n_counters, size_t inbox_bytes, int grid
                  const void* out, void* const* outbox, long long* out_fields) {
   mkh::Ws ws{n_flags, n_counters, inbox_bytes, grid};
   mkh::MlpPlan P{};
-  const int M = world * m_shard;
-  const int red_m = M > 512 ? 256 : 128, red_n = M > 512 ? 256 : 64, red_w = M > 512 ? 8 : 4;  // the kernels' tiles
+  const long long rows = (long long)world * m_shard;  // the kernels' tiles for this many output rows
+  const mk_tiles::Shape& red = rows <= mk_tiles::kRedSkinnyMaxRows ? mk_tiles::kRedSkinny : mk_tiles::kRedBig;
   const int code = mkh::plan_mlp(ws, o, a_shards, world, rank, m_shard, k, b_up, n_up, b_down, n_out, peers,
-                                 a_gathered, h, out, outbox, 256, 256, red_m, red_n, red_w, &P);
+                                 a_gathered, h, out, outbox, mk_tiles::kAg.bm, mk_tiles::kAg.bn, red.bm, red.bn,
+                                 red.waves(), &P);
   const long long v[] = {P.ag.n_copy, P.ag.n_compute, P.ag.tiles_m, P.ag.tiles_n, P.red.n_compute, P.red.tiles_m,
                          P.red.tiles_n, P.red.own_tile_begin, P.red.own_tile_end, P.red.assist};
   for (unsigned i = 0; i < sizeof(v) / sizeof(v[0]); ++i) out_fields[i] = v[i];

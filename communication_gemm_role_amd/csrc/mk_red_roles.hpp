@@ -2,9 +2,10 @@
 // kernels that run them are gemm_reduce_kernel (mk_gemm_reduce.hip) and the MLP kernel (mk_mlp.hip).
 //
 // Operations (mKernel write-up, news.chathome.org page, five-fused-kernels table, GEMM +
-// AllReduce and GEMM + ReduceScatter rows): C = A @ B is computed in one launch and each
-// output tile is reduced with the other ranks' partials as soon as it is produced; for the
-// reduce-scatter every tile goes to the rank that owns its rows.
+// AllReduce and GEMM + ReduceScatter rows): rank j holds a partial P_j = A_j @ B_j of the same
+// [M, N] output.  AllReduce: every rank ends with sum_j P_j.  ReduceScatter: rank r ends with
+// sum_j P_j on its own row slice only.  A tile of P enters the reduction right after its K loop,
+// inside the same launch.
 //
 // This rank's partial is P = A @ B.  Owned rows (RS: the rank's slice; AR: all rows) need
 // out = P + sum of the peers' partials; in RS every other tile goes unreduced to the outbox
@@ -30,10 +31,12 @@
 
 namespace mk {
 
-using RedBig = TileGemmDma<256, 256, 2, 4>;   // wide outputs (e.g. 8192 x 4096), eight waves
-using RedSkinny = TileGemmDma<128, 64, 4, 1>;  // few output rows (decode-like, m <= 512)
+// wide outputs (e.g. 8192 x 4096), eight waves; few output rows (decode-like), four waves
+using RedBig = TileGemmDma<mk_tiles::kRedBig.bm, mk_tiles::kRedBig.bn, mk_tiles::kRedBig.wm, mk_tiles::kRedBig.wn>;
+using RedSkinny =
+    TileGemmDma<mk_tiles::kRedSkinny.bm, mk_tiles::kRedSkinny.bn, mk_tiles::kRedSkinny.wm, mk_tiles::kRedSkinny.wn>;
 
-inline bool red_skinny(int m, int n) { (void)n; return m <= 512; }
+inline bool red_skinny(int m, int n) { (void)n; return mk_tiles::red_skinny(m); }
 
 // Peer partial q (0..world-2) is rank q < rank ? q : q + 1.
 __device__ __forceinline__ int peer_rank(int rank, int q) { return q < rank ? q : q + 1; }

@@ -1,13 +1,11 @@
 // Ring attention, one rank's share, as one persistent launch.
 //
 // Operation (mKernel write-up, news.chathome.org page, five-fused-kernels table, Ring Attention
-// row): sequence-parallel attention across ranks; every ring step rotates the K/V blocks one rank
-// further while the local FlashAttention consumes the block received before, compute and ring
-// transfer running concurrently inside one persistent kernel.  Rank r holds the queries of its
-// sequence shard and, after the ring has gone round, has attended over every rank's keys:
+// row).  Rank r holds the queries of its sequence shard; the answer it needs is
 //   out[h, i, :] = sum_j softmax_j(scale * q[h, i] . k[h, j]) v[h, j, :]   over all world * s_local keys
-// (no mask: the pages name no causal variant).  Here the other ranks' K/V shards are device
-// buffers and the ring transfer is the copy role.
+// (no mask: the pages name no causal variant).  The peers' K/V shards travel round the ring, and
+// the attention starts on each peer block once that block is present, inside the same launch.
+// Here the other ranks' K/V shards are device buffers and the ring transfer is the copy role.
 //
 // Roles:
 //   workgroups [0, n_copy)   copy: for arrival positions cid, cid + n_copy, ... land a 64-key
