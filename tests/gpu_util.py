@@ -30,9 +30,11 @@ def host(t: torch.Tensor) -> np.ndarray:
 
 
 def assert_close(out, ref, what: str, tol: float = TOL):
-    err = oracle.max_rel_err(np.asarray(out, np.float64), ref)
-    assert err <= tol, f"{what}: max|out-ref|/RMS(ref) = {err:.3e} > {tol:.1e}"
+    assert np.shape(out) == np.shape(ref), f"{what}: shape {np.shape(out)} vs {np.shape(ref)}"
     assert not np.isnan(np.asarray(out)).any(), f"{what}: NaN in output"
+    err = oracle.max_rel_err(np.asarray(out, np.float64), ref)
+    print(f"{what}: max|out-ref|/RMS(ref) = {err:.3e} over {np.size(ref)} elements", flush=True)
+    assert err <= tol, f"{what}: max|out-ref|/RMS(ref) = {err:.3e} > {tol:.1e}"
     return err
 
 

@@ -522,22 +522,34 @@ def _run_mlp(ctx, shape, data, order=None, mode=None, **extra):
     return ag, h, own, outbox
 
 
-def _assert_h(h_bits, h_ref, what, max_frac=1e-2):
-    """H is fp32 gelu(fp32 U) rounded to bf16 on the GPU and the bf16 rounding of fp64 gelu(fp64 U)
-    in the oracle: the two may differ by one bf16 step where the fp32 value lies within its own
-    rounding error of a rounding boundary (rare), or by a negligible amount where U is within
-    that error of zero.  Returns |H - H_ref| for the down-projection's error budget."""
+GELU_LIP = 1.13  # max |gelu'(x)| = Phi(x) + x phi(x), reached near x = 1.41 (1.1289...)
+
+
+def _assert_h(h_bits, h_ref, u_ref, what, max_frac=1e-2):
+    """H is bf16(gelu_f32(U_gpu)) on the GPU, with U_gpu the fp32 up-projection, and the bf16 rounding
+    of fp64 gelu(fp64 U) in the oracle.  U_gpu is an fp32 GEMM output, so it is held to the same rule
+    as every fp32 output: |U_gpu - U| <= TOL * RMS(U).  gelu moves that by at most GELU_LIP times as
+    much, and the two roundings by at most one bf16 step of the larger value, so
+        |H - H_ref| <= step(max(|H|, |H_ref|)) + GELU_LIP * TOL * RMS(U)
+    for every element.  In practice U_gpu is far closer than TOL: the two differ by one step only
+    where gelu(U) lies within fp32 error of a rounding boundary, so at most max_frac of the elements
+    may differ at all.  Returns |H - H_ref| for the down-projection's error budget."""
+    from gpu_util import TOL, log
     out = oracle.bf16_to_f64(h_bits)
     ref = np.asarray(h_ref, np.float64)
     assert not np.isnan(out).any(), f"{what}: NaN (an element never written)"
     diff = np.abs(out - ref)
-    mag = np.abs(ref)
+    mag = np.maximum(np.abs(ref), np.abs(out))
     step = np.where(mag > 0, np.exp2(np.floor(np.log2(np.where(mag > 0, mag, 1.0))) - 7), 0.0)
-    floor = 2.0 ** -20 * oracle.rms(ref)
-    bad = diff > np.maximum(step, floor)
-    assert not bad.any(), f"{what}: {bad.sum()} elements beyond one bf16 step, first at {np.argwhere(bad)[0].tolist()}"
+    slack = GELU_LIP * TOL * oracle.rms(u_ref)
+    bad = diff > step + slack
+    assert not bad.any(), f"{what}: {bad.sum()} elements beyond one bf16 step + {slack:.3e}, first at " \
+                          f"{np.argwhere(bad)[0].tolist()}"
     frac = float(np.mean(diff > 0))
-    assert frac <= max_frac, f"{what}: {frac:.3%} of elements differ by one bf16 step"
+    assert frac <= max_frac, f"{what}: {frac:.3%} of elements differ"
+    over = diff > step
+    log(f"{what}: {frac:.4%} of elements differ from the oracle's; {int(over.sum())} by more than one step "
+        f"(largest excess {float(np.max(diff - step)) if over.any() else 0.0:.3e}, allowed {slack:.3e})")
     return diff
 
 
@@ -567,7 +579,7 @@ def test_mlp_small(ctx, mode, rank):
     ag, h, own, outbox = _run_mlp(ctx, s, d, order, mk.MK_ARRIVAL_EMULATED if em else mk.MK_ARRIVAL_RESIDENT)
     ref = oracle.mlp_ag_rs(d["a_shards"], d["b_up"], d["b_down"], d["peers"], s.world, rank)
     assert_exact(host_bits(ag), ref["a_gathered"], "a_gathered")
-    dh = _assert_h(host_bits(h), ref["h"], "H")
+    dh = _assert_h(host_bits(h), ref["h"], ref["u"], "H")
     ms = s.m_shard
     _assert_close_down(host(own), ref["own"], dh[rank * ms:(rank + 1) * ms], d["b_down"], "owned slice")
     for j in range(s.world):
@@ -609,7 +621,7 @@ def test_mlp_full(ctx, mode):
     torch.cuda.synchronize()
     ref = oracle.mlp_ag_rs(d["a_shards"], d["b_up"], d["b_down"], d["peers"], s.world, 0)
     assert_exact(host_bits(ag), ref["a_gathered"], "a_gathered")
-    dh = _assert_h(host_bits(h), ref["h"], "H")
+    dh = _assert_h(host_bits(h), ref["h"], ref["u"], "H")
     ms = s.m_shard
     _assert_close_down(host(own), ref["own"], dh[:ms], d["b_down"], "owned slice")
     for j in range(1, s.world):
