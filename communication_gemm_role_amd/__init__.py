@@ -31,7 +31,7 @@ MK_ARRIVAL_EMULATED = 2
 
 EXPORTED = ["mk_ctx_create", "mk_ctx_destroy", "mk_ctx_status", "mk_ctx_reset", "mk_ctx_grid", "mk_strerror",
             "mk_selftest_flags", "mk_ag_gemm", "mk_gemm_rs", "mk_gemm_ar", "mk_moe_dispatch_gemm", "mk_mlp_ag_rs",
-            "mk_ag_gemm_tune", "mk_gemm_rs_tune", "mk_gemm_ar_tune", "mk_ring_attention"]
+            "mk_ag_gemm_tune", "mk_gemm_rs_tune", "mk_gemm_ar_tune", "mk_ring_attention", "mk_ag_gemm_noalloc"]
 
 
 class MkError(RuntimeError):
@@ -123,6 +123,7 @@ def lib() -> ctypes.CDLL:
         L.mk_moe_dispatch_gemm.argtypes = [vp, vp, vp, i, i, i, vp, vp, i, i, i, i, vp, i, vp, vp, vp, vp, vp, i, vp]
         L.mk_selftest_flags.argtypes = [i, i, i, i, ctypes.POINTER(i64), ctypes.POINTER(i64)]
         L.mk_mlp_ag_rs.argtypes = [vp, vp, vp, i, i, i, i, vp, i, vp, i, vp, vp, vp, vp, vp, vp]
+        L.mk_ag_gemm_noalloc.argtypes = [vp, vp, i, i, i, i, vp, i, vp, vp, vp, vp]
         L.mk_ring_attention.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, ctypes.c_float, vp, vp, vp, vp, vp]
         tune = [vp, i, i, vp, vp]  # candidates, count, reps, us_per_call, best
         L.mk_ag_gemm_tune.argtypes = L.mk_ag_gemm.argtypes + tune
@@ -130,7 +131,8 @@ def lib() -> ctypes.CDLL:
         L.mk_gemm_ar_tune.argtypes = L.mk_gemm_ar.argtypes + tune
         for name in ("mk_ctx_create", "mk_ctx_destroy", "mk_ctx_status", "mk_ctx_reset", "mk_ctx_grid",
                      "mk_selftest_flags", "mk_ag_gemm", "mk_gemm_rs", "mk_gemm_ar", "mk_moe_dispatch_gemm",
-                     "mk_mlp_ag_rs", "mk_ag_gemm_tune", "mk_gemm_rs_tune", "mk_gemm_ar_tune", "mk_ring_attention"):
+                     "mk_mlp_ag_rs", "mk_ag_gemm_tune", "mk_gemm_rs_tune", "mk_gemm_ar_tune", "mk_ring_attention",
+                     "mk_ag_gemm_noalloc"):
             getattr(L, name).restype = i
         _lib_handle = L
     return _lib_handle
@@ -248,6 +250,34 @@ def mk_ag_gemm(ctx: Context, a_shards: Sequence, world: int, rank: int, b, a_gat
     op, _keep = _opts_ptr(opts, ctx)
     _call(lib().mk_ag_gemm(ctx.handle, _stream_ptr(stream), shards, world, rank, m // world, k, b.data_ptr(), n,
                            a_gathered.data_ptr(), c.data_ptr(), op), "mk_ag_gemm")
+
+
+def mk_ag_gemm_noalloc(a_shards: Sequence, world: int, rank: int, b, a_gathered, c, status,
+                       opts: Optional[Opts] = None, stream=None) -> None:
+    """AllGather+GEMM without a context or any allocation (see mk.h), on the current device: as
+    mk_ag_gemm, with `status` a one-element int32 device tensor that receives MK_OK or the device
+    fault code when the kernel ends."""
+    import torch
+    _check(b, "bf16", "b")
+    _check(a_gathered, "bf16", "a_gathered")
+    _check(c, "f32", "c")
+    _check(status, "int32", "status")
+    if status.numel() < 1:
+        raise ValueError("status needs one int32 element")
+    k, n = b.shape
+    m = a_gathered.shape[0]
+    if a_gathered.shape[1] != k or c.shape != (m, n) or m % world:
+        raise ValueError("shape mismatch")
+    shards = _ptr_array(a_shards, "bf16", "a_shards") if a_shards is not None else None
+    op, _keep = None, None
+    if opts is not None:
+        cu = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+        if opts.trace is not None and opts.trace.numel() < cu * 8:
+            raise ValueError(f"trace needs {cu * 8} int64 elements (8 per workgroup), got {opts.trace.numel()}")
+        _keep = opts.to_c()
+        op = ctypes.byref(_keep)
+    _call(lib().mk_ag_gemm_noalloc(_stream_ptr(stream), shards, world, rank, m // world, k, b.data_ptr(), n,
+                                   a_gathered.data_ptr(), c.data_ptr(), status.data_ptr(), op), "mk_ag_gemm_noalloc")
 
 
 def mk_gemm_rs(ctx: Context, a, b, world: int, rank: int, peer_partials: Sequence, owned_out, outbox: Sequence,

@@ -38,6 +38,9 @@ __global__ __launch_bounds__(AG_THREADS, 1) void ag_gemm_kernel(AgParams p) {
   if (threadIdx.x == 0 && atomic_add_agent(p.counters + CTR_AG_EXIT, 1u) == gridDim.x - 1) {
     __hip_atomic_store(p.counters + CTR_AG_TILE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(p.counters + CTR_AG_EXIT, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // every other workgroup's faults were recorded before it counted its exit
+    if (p.status_out)
+      *p.status_out = __hip_atomic_exchange(p.status, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include "mk.h"
@@ -74,6 +75,47 @@ int next_epoch(mk_ctx* c, hipStream_t s) {
   }
   ++c->epoch;
   return MK_OK;
+}
+
+// Kernel parameters of an AllGather + GEMM call from its plan; the workspace (flags, counters,
+// status word) and the epoch are the caller's: a context's, or the static scratch array's.
+mk::AgParams ag_params(const mkh::AgPlan& P, const uint16_t* const* a_shards, int world, int rank, int m_shard, int k,
+                       const uint16_t* b, int n, uint16_t* a_gathered, float* c, const mk_opts* opts, uint32_t* flags,
+                       uint32_t* counters, int* status, uint32_t epoch, int* status_out) {
+  mk::AgParams p;
+  memset(&p, 0, sizeof(p));
+  for (int r = 0; r < world; ++r) p.shards[r] = a_shards ? a_shards[r] : nullptr;
+  p.b = b;
+  p.ag = a_gathered;
+  p.c = c;
+  p.order = (P.emulated && opts) ? (const int32_t*)opts->arrival_order : nullptr;
+  p.flags = flags;
+  p.status = status;
+  p.world = world;
+  p.rank = rank;
+  p.m_shard = m_shard;
+  p.m = P.m;
+  p.n = n;
+  p.k = k;
+  p.unit_rows = P.unit_rows;
+  p.unit_cols = P.unit_cols;
+  p.n_ucols = P.n_ucols;
+  p.n_urows = P.n_urows;
+  p.n_copy = P.n_copy;
+  p.n_compute = P.n_compute;
+  p.emulated = P.emulated;
+  p.pace_q16 = P.pace_q16;
+  p.local_in_place = P.local_in_place;
+  p.n_order = P.n_order;
+  p.drop_pos = P.drop_pos;
+  p.tiles_m = P.tiles_m;
+  p.tiles_n = P.tiles_n;
+  p.epoch = epoch;
+  p.timeout_ticks = timeout_ticks(opts);
+  p.trace = opts ? opts->trace : nullptr;
+  p.counters = counters;
+  p.status_out = status_out;
+  return p;
 }
 
 }  // namespace
@@ -183,38 +225,8 @@ int mk_ag_gemm(mk_ctx* ctx, void* stream, const uint16_t* const* a_shards, int w
   if (!g.ok) return MK_ERR_HIP;
   hipStream_t s = (hipStream_t)stream;
   if ((code = next_epoch(ctx, s)) != MK_OK) return code;
-  mk::AgParams p;
-  memset(&p, 0, sizeof(p));
-  for (int r = 0; r < world; ++r) p.shards[r] = a_shards ? a_shards[r] : nullptr;
-  p.b = b;
-  p.ag = a_gathered;
-  p.c = c;
-  p.order = (P.emulated && opts) ? (const int32_t*)opts->arrival_order : nullptr;
-  p.flags = ctx->flags;
-  p.status = ctx->status;
-  p.world = world;
-  p.rank = rank;
-  p.m_shard = m_shard;
-  p.m = P.m;
-  p.n = n;
-  p.k = k;
-  p.unit_rows = P.unit_rows;
-  p.unit_cols = P.unit_cols;
-  p.n_ucols = P.n_ucols;
-  p.n_urows = P.n_urows;
-  p.n_copy = P.n_copy;
-  p.n_compute = P.n_compute;
-  p.emulated = P.emulated;
-  p.pace_q16 = P.pace_q16;
-  p.local_in_place = P.local_in_place;
-  p.n_order = P.n_order;
-  p.drop_pos = P.drop_pos;
-  p.tiles_m = P.tiles_m;
-  p.tiles_n = P.tiles_n;
-  p.epoch = ctx->epoch;
-  p.timeout_ticks = timeout_ticks(opts);
-  p.trace = opts ? opts->trace : nullptr;
-  p.counters = ctx->counters;
+  const mk::AgParams p = ag_params(P, a_shards, world, rank, m_shard, k, b, n, a_gathered, c, opts, ctx->flags,
+                                   ctx->counters, ctx->status, ctx->epoch, nullptr);
   return mk::launch_ag_gemm(p, P.n_copy + P.n_compute, s) == hipSuccess ? MK_OK : MK_ERR_HIP;
 }
 
@@ -590,3 +602,86 @@ int mk_gemm_ar_tune(mk_ctx* ctx, void* stream, const uint16_t* a, const uint16_t
 }
 
 }  // extern "C"
+
+// ---- AllGather + GEMM without allocation ------------------------------------------------------------
+// The ready flags, counters and status word live in a static device array instead of a context's
+// workspace.  In host code `scratch` names a host-side stand-in, not the device array: its device
+// address is taken once per device with hipGetSymbolAddress and only that address is used.
+namespace {
+
+constexpr size_t kScratchStatusWords = 64;  // the status word, padded to 256 bytes
+constexpr size_t kScratchCounters = 128;    // the AllGather + GEMM claim and exit counters sit at 110, 111
+constexpr size_t kScratchFlags = 16384;     // one epoch flag per arrival unit
+constexpr size_t kScratchWords = kScratchStatusWords + kScratchCounters + kScratchFlags;
+static_assert(mk::CTR_AG_EXIT < (int)kScratchCounters, "the AllGather + GEMM counters fit the static counters");
+constexpr int kMaxDevices = 64;
+
+struct ScratchDev {
+  uint32_t* ptr;   // device address of `scratch` on this device (null until set up)
+  uint32_t epoch;  // call number on this device; a flag is up when it equals the current epoch
+  int n_cu;
+};
+ScratchDev g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+}  // namespace
+
+static __device__ __align__(256) uint32_t scratch[kScratchWords];
+
+namespace {
+
+// Once per device, with that device current: the array's device address, the grid size, and a
+// zero fill of the array on `s` (a fill kernel, not a memset).  Nothing here allocates.
+int scratch_setup(int dev, hipStream_t s, ScratchDev** out) {
+  if (dev < 0 || dev >= kMaxDevices) return MK_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ScratchDev& d = g_scratch[dev];
+  if (!d.ptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MK_ERR_HIP;
+    int n_cu = 0;
+    if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0)
+      return MK_ERR_HIP;
+    if (mk::launch_fill_u32((uint32_t*)ptr, 0u, kScratchWords, s) != hipSuccess) return MK_ERR_HIP;
+    d.ptr = (uint32_t*)ptr;
+    d.n_cu = n_cu;
+    d.epoch = 0;
+  }
+  *out = &d;
+  return MK_OK;
+}
+
+}  // namespace
+
+extern "C" int mk_ag_gemm_noalloc(void* stream, const uint16_t* const* a_shards, int world, int rank, int m_shard,
+                                  int k, const uint16_t* b, int n, uint16_t* a_gathered, float* c, int* status,
+                                  const mk_opts* opts) {
+  if (!status || ((uintptr_t)status & 3u)) return MK_ERR_INVALID_ARG;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MK_ERR_HIP;
+  hipStream_t s = (hipStream_t)stream;
+  ScratchDev* d = nullptr;
+  int code = scratch_setup(dev, s, &d);
+  if (code != MK_OK) return code;
+  uint32_t* status_word = d->ptr;
+  uint32_t* counters = d->ptr + kScratchStatusWords;
+  uint32_t* flags = counters + kScratchCounters;
+  const mkh::Ws ws{kScratchFlags, kScratchCounters, 0, d->n_cu};
+  const mkh::Opts o = to_opts(opts);
+  mkh::AgPlan P;
+  code = mkh::plan_ag(ws, opts ? &o : nullptr, (const void* const*)a_shards, world, rank, m_shard, k, b, n, a_gathered,
+                      c, mk::ag_tile_m(), mk::ag_tile_n(), &P);
+  if (code != MK_OK) return code;  // MK_ERR_WORKSPACE: more arrival units than static flags
+  uint32_t epoch;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (d->epoch >= 0xFFFFFF00u) {  // restart the epochs on cleared flags
+      if (mk::launch_fill_u32(flags, 0u, kScratchFlags, s) != hipSuccess) return MK_ERR_HIP;
+      d->epoch = 0;
+    }
+    epoch = ++d->epoch;
+  }
+  const mk::AgParams p = ag_params(P, a_shards, world, rank, m_shard, k, b, n, a_gathered, c, opts, flags, counters,
+                                   (int*)status_word, epoch, status);
+  return mk::launch_ag_gemm(p, P.n_copy + P.n_compute, s) == hipSuccess ? MK_OK : MK_ERR_HIP;
+}

@@ -66,6 +66,9 @@ struct AgParams {
   // C and adds one to h_ready[tile row] once a tile's stores have completed
   uint16_t* h;
   uint32_t* h_ready;
+  // when set, the last workgroup out moves the status word here and clears it (the call without a
+  // context reports device faults through a caller-owned output instead of mk_ctx_status)
+  int* status_out;
 };
 
 struct RedParams {

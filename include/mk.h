@@ -176,6 +176,22 @@ int mk_selftest_flags(int device, int mode, int pairs, int rounds, int64_t* mism
 int mk_ag_gemm(mk_ctx* ctx, void* stream, const uint16_t* const* a_shards, int world, int rank, int m_shard,
                int k, const uint16_t* b, int n, uint16_t* a_gathered, float* c, const mk_opts* opts);
 
+/* ---- AllGather + GEMM without allocation ------------------------------------------------
+ * For callers that cannot allocate device memory or create a context: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same operation, arguments
+ * and options as mk_ag_gemm, on the CURRENT device, with no context: the ready flags, counters and
+ * status word live in a static device array of the library (66 KiB per device, held until the
+ * process ends), set up on the first call on a device.  No call allocates or frees memory.
+ *   status   DEVICE int, OUT (4-byte aligned, not NULL): when the kernel ends it holds MK_OK,
+ *            MK_ERR_TIMEOUT (a wait hit opts.timeout_us) -- the codes mk_ctx_status would return
+ * Limits: at most 16384 arrival units ((world*m_shard/unit_rows) * (k/unit_cols)); more return
+ * MK_ERR_WORKSPACE.  Every call on a device shares that device's array: calls must be ordered on
+ * one stream (or synchronised); calls that overlap on one GPU race.  Argument errors return
+ * synchronously as for mk_ag_gemm; MK_ERR_HIP if the device array cannot be set up or the launch
+ * fails. */
+int mk_ag_gemm_noalloc(void* stream, const uint16_t* const* a_shards, int world, int rank, int m_shard, int k,
+                       const uint16_t* b, int n, uint16_t* a_gathered, float* c, int* status, const mk_opts* opts);
+
 /* ---- GEMM + ReduceScatter -------------------------------------------------------------
  * Five-fused-kernels table, GEMM + ReduceScatter row: the sum over ranks of the partials A_j @ B_j,
  * each rank receiving only its own row slice of it; a tile of this rank's partial is added in or
