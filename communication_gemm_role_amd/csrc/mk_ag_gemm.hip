@@ -9,28 +9,40 @@
 
 namespace mk {
 
-int ag_tile_m() { return AgTile::BM; }
-int ag_tile_n() { return AgTile::BN; }
+int ag_tile_m() { return TileGemm16::BM; }
+int ag_tile_n() { return TileGemm16::BN; }
 
+// Roles: workgroups [0, n_copy) copy (land peer units in the caller's order), then compute; the rest
+// compute from the start.  Static tiles are XCD-aware: workgroup w runs on XCD w % 8, and the k-th
+// of n workgroups taking static tiles owns logical tile (k % 8) * (n / 8) + k / 8, so an XCD's
+// tiles are consecutive (whole tile rows, sharing their A rows in its L2).  When the compute
+// workgroups alone can hold every tile they do; otherwise every workgroup owns one (copy
+// workgroups start theirs after copying) and tiles past the grid are claimed from a counter.
 __global__ __launch_bounds__(AG_THREADS, 1) void ag_gemm_kernel(AgParams p) {
-  __shared__ __attribute__((aligned(16))) char st0[AgTile::STAGE];
-  __shared__ __attribute__((aligned(16))) char st1[AgTile::STAGE];
-  __shared__ __attribute__((aligned(16))) char st2[k_stages<AgTile>() == 3 ? AgTile::STAGE : 16];
+  using G = TileGemm16;
+  __shared__ __attribute__((aligned(16))) char a0[G::SLOT_A];
+  __shared__ __attribute__((aligned(16))) char a1[G::SLOT_A];
+  __shared__ __attribute__((aligned(16))) char a2[G::SLOT_A];
+  __shared__ __attribute__((aligned(16))) char b0[G::SLOT_B];
+  __shared__ __attribute__((aligned(16))) char b1[G::SLOT_B];
   __shared__ int s_sched[64];
-  __shared__ uint64_t s_done;
   __shared__ int s_claim;
-  const int wg = blockIdx.x;
+  __shared__ __attribute__((aligned(16))) uint32_t s_poll[4 * 64];
+  const int wg = blockIdx.x, grid = gridDim.x, n_tiles = p.tiles_m * p.tiles_n;
+  const bool compute_only = n_tiles <= p.n_compute;
+  const int k = compute_only ? wg - p.n_copy : wg, n = compute_only ? p.n_compute : grid;
+  const int rs = k < 0 ? -1 : (n & 7) == 0 ? (k & 7) * (n >> 3) + (k >> 3) : k;
+  const int t_static = rs < n_tiles ? rs : -1;
   if (wg < p.n_copy) {
     trace_begin(p.trace, ROLE_COPY);
-    ag_copy_role(p, wg, st0, st1);
+    ag_copy_role<32>(p, wg, a0, a1);
     trace_mark(p.trace, 5);
     __syncthreads();  // the copy's LDS slots become the GEMM's stage buffers
-    ag_compute_role(p, -1, st0, st1, st2, s_sched, &s_done, &s_claim);  // then help with leftover tiles
   } else {
     trace_begin(p.trace, ROLE_COMPUTE);
-    const int slot = wg - p.n_copy;
-    if (slot < p.n_compute) ag_compute_role(p, slot, st0, st1, st2, s_sched, &s_done, &s_claim);
   }
+  const bool is_copy = wg < p.n_copy;
+  ag_compute_role16(p, t_static, !is_copy, is_copy, a0, a1, a2, b0, b1, s_sched, &s_claim, s_poll);
   trace_end(p.trace);
   // exit accounting: the last workgroup out re-zeroes the tile counter for the next call (every
   // workgroup's last claim returned before it counts its exit)

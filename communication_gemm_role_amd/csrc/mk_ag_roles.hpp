@@ -27,6 +27,7 @@
 #pragma once
 #include "mk_internal.h"
 #include "mk_gemm_tile.hpp"
+#include "mk_gemm_tile16.hpp"
 #include "mk_copy_ring.hpp"
 
 namespace mk {
@@ -48,11 +49,11 @@ __device__ __forceinline__ int ag_identity_unit(const AgParams& p, int pos) {
 }
 
 // Units move through the two-slot LDS ring of mk_copy_ring.hpp (the stage buffers are idle in a
-// copy workgroup): 8 KiB per wave and batch, i.e. 2 units of 128x128, 4 of 64x128 / 128x64 or
-// 8 of 64x64.  IPU is a unit's DMA instructions per wave (1 KiB each).  The arrival order is read
-// through the constant address space, so its loads are scalar, off the vector-memory counter the
-// ring waits on.
-template <int IPU>
+// copy workgroup): IPB KiB per wave and batch -- 8 (64 KiB slots: 2 units of 128x128, 4 of
+// 64x128 / 128x64 or 8 of 64x64) or 4 (32 KiB slots: half as many).  IPU is a unit's DMA
+// instructions per wave (1 KiB each).  The arrival order is read through the constant address
+// space, so its loads are scalar, off the vector-memory counter the ring waits on.
+template <int IPB, int IPU>
 __device__ __forceinline__ void ag_copy_dma(const AgParams& p, int cid, char* st0, char* st1) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int cpr = p.unit_cols >> 3;  // 16-byte chunks per unit row
@@ -88,21 +89,25 @@ __device__ __forceinline__ void ag_copy_dma(const AgParams& p, int cid, char* st
     return make_rsrc(p.ag + (size_t)ur * p.unit_rows * p.k + (size_t)uc * p.unit_cols, extent);
   };
   const uint64_t t0 = wall_ticks();
-  copy_ring<8, IPU>(n_mine, st0, st1, off, unit_at, src_of, dst_of,
+  copy_ring<IPB, IPU>(n_mine, st0, st1, off, unit_at, src_of, dst_of,
                     [&](int u) { flag_store(&p.flags[u], p.epoch); },
                     [&](int i) {  // queue entry i is arrival position cid + i * n_copy
                       if (p.pace_q16) wait_wall_until(t0 + (((uint64_t)(cid + i * p.n_copy) * p.pace_q16) >> 16));
                     });
 }
 
-static_assert(AgTile::STAGE >= 65536 && AG_THREADS == 512, "copy slots: 64 KiB stage buffers, 8 waves");
+static_assert(AG_THREADS == 512, "copy slots hold 8 waves' batches");
 
+// SLOT_KIB: bytes of each of the two ring slots, in KiB (64 or 32)
+template <int SLOT_KIB>
 __device__ __forceinline__ void ag_copy_role(const AgParams& p, int cid, char* st0, char* st1) {
+  constexpr int IPB = SLOT_KIB / 8;  // KiB per wave and batch
+  static_assert(IPB == 8 || IPB == 4, "64 or 32 KiB slots");
   // DMA instructions per wave per unit: 4 (128x128), 2 (64x128, 128x64), 1 (64x64)
   const int ipu = (p.unit_rows * p.unit_cols * 2) / (AG_THREADS * 16);
-  if (ipu == 4) ag_copy_dma<4>(p, cid, st0, st1);
-  else if (ipu == 2) ag_copy_dma<2>(p, cid, st0, st1);
-  else ag_copy_dma<1>(p, cid, st0, st1);
+  if (ipu == 4) ag_copy_dma<IPB, 4>(p, cid, st0, st1);
+  else if (ipu == 2) ag_copy_dma<IPB, 2>(p, cid, st0, st1);
+  else ag_copy_dma<IPB, 1>(p, cid, st0, st1);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -128,18 +133,17 @@ __device__ __forceinline__ uint64_t ag_ready_mask(const AgParams& p, int ur0, in
 
 // Wave 0: pick the next K-unit (lowest landed, not yet scheduled); -1 on timeout or fault.
 // Every value that steers control flow here is wave-uniform (ballots, readfirstlane), so all 64
-// lanes take the same path and every ballot sees every unit's flag.  The scheduled-set mask lives
-// in LDS (volatile: re-read each call) so no register is held across the MFMA loop for it.
+// lanes take the same path and every ballot sees every unit's flag.  The scheduled-set mask `done`
+// is wave 0's own (uniform, in scalar registers): kept in LDS as a volatile value it became a
+// flat access, whose wait drained the K loop's operand loads in flight at every decision.
 __device__ __forceinline__ uint64_t uniform64(uint64_t v) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
   return ((uint64_t)hi << 32) | lo;
 }
 
-__device__ __forceinline__ int ag_pick(const AgParams& p, int ur0, int n_ur, uint64_t* s_done, int lane) {
-  volatile uint64_t* vd = s_done;
+__device__ __forceinline__ int ag_pick(const AgParams& p, int ur0, int n_ur, uint64_t& done, int lane) {
   const uint64_t all = (p.n_ucols >= 64) ? ~0ull : ((1ull << p.n_ucols) - 1ull);
-  const uint64_t done = uniform64(*vd);
   uint64_t cand = ag_ready_mask(p, ur0, n_ur, all, lane) & ~done;
   if (!cand) {
     const uint64_t t0 = wall_ticks();
@@ -159,7 +163,7 @@ __device__ __forceinline__ int ag_pick(const AgParams& p, int ur0, int n_ur, uin
     }
   }
   const int u = __builtin_ctzll(cand);
-  *vd = done | (1ull << u);  // every lane stores the same value
+  done = uniform64(done | (1ull << u));
   return u;
 }
 
@@ -176,19 +180,84 @@ __device__ __forceinline__ void ag_poll_issue(const AgParams& p, int ur0, int n_
                                                                        : p.epoch;
   }
 }
+// Wave 0: as ag_poll_issue, through one buffer window over the tile's flag rows (one per-lane
+// offset, the row in the scalar offset: four fewer 64-bit addresses held across the MFMAs).  Lanes
+// past n_ucols read the next row's flags, which the ready mask ignores.
+__device__ __forceinline__ void ag_poll_issue_rows(const AgParams& p, int ur0, int n_ur, int lane, AgPoll& pl) {
+  const auto rs = make_rsrc(p.flags + (size_t)ur0 * p.n_ucols, (uint32_t)(n_ur * p.n_ucols) * 4u);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)lane * 4u, (uint32_t)(q * p.n_ucols) * 4u, CP_SC1);
+    pl.f[q] = (q < n_ur && !ag_row_local(p, ur0 + q)) ? v : p.epoch;
+  }
+}
+
+// Wave 0: the flags of the tile's unit rows [ur0, ur0 + n_ur) (at most 4) for K-unit `lane`,
+// requested straight into LDS (s_poll[q][lane]), so no register is held while the loads are in
+// flight across a step's MFMAs.  Lanes past n_ucols read the next row's flags, which the ready
+// mask ignores.
+__device__ __forceinline__ void ag_poll_lds(const AgParams& p, int ur0, int n_ur, uint32_t* s_poll) {
+  const auto rs = make_rsrc(p.flags + (size_t)ur0 * p.n_ucols, (uint32_t)(n_ur * p.n_ucols) * 4u);
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(s_poll + q * 64), 4,
+                                             (uint32_t)(threadIdx.x & 63) * 4u, (uint32_t)(q * p.n_ucols) * 4u, 0,
+                                             CP_SC1);
+}
+// Wave 0: landed-K-unit mask of a poll in LDS (uniform); the caller has waited for its DMA.
+__device__ __forceinline__ uint64_t ag_ready_lds(const AgParams& p, int ur0, int n_ur, int lane,
+                                                 const uint32_t* s_poll) {
+  uint64_t ready = (p.n_ucols >= 64) ? ~0ull : ((1ull << p.n_ucols) - 1ull);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const bool skip = q >= n_ur || ag_row_local(p, ur0 + q);
+    ready &= __ballot(skip || lane >= p.n_ucols || s_poll[q * 64 + lane] == p.epoch);
+  }
+  return uniform64(ready);
+}
+
+// Wave 0: nothing new has landed in the poll: poll again (sleeping between polls) until a unit
+// not in `done` has landed.  Returns the new ready mask, or 0 on timeout or when another workgroup
+// has recorded a fault.  Reuses the poll's registers, so the K loop that inlines it keeps its
+// register budget.
+__device__ __forceinline__ uint64_t ag_repoll_until_new(const AgParams& p, int ur0, int n_ur, int lane,
+                                                        uint32_t* s_poll, uint64_t done) {
+  const uint64_t t0 = wall_ticks();
+  for (int n = 1;; ++n) {
+    __builtin_amdgcn_s_sleep(2);
+    ag_poll_lds(p, ur0, n_ur, s_poll);
+    wait_vm<0>();
+    const uint64_t ready = ag_ready_lds(p, ur0, n_ur, lane, s_poll);
+    if (ready & ~done) return ready;
+    if ((n & 7) == 0) {
+      if (__builtin_amdgcn_readfirstlane(status_bad(p.status) ? 1 : 0)) return 0;
+      if (wall_ticks() - t0 > p.timeout_ticks) {
+        if (lane == 0) raise_status(p.status, ST_TIMEOUT);
+        return 0;
+      }
+    }
+  }
+}
+
+// Wave 0: landed-K-unit mask of an issued poll (uniform).
+__device__ __forceinline__ uint64_t ag_ready_polled(const AgParams& p, int lane, const AgPoll& pl) {
+  uint64_t ready = (p.n_ucols >= 64) ? ~0ull : ((1ull << p.n_ucols) - 1ull);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) ready &= __ballot(lane >= p.n_ucols || pl.f[q] == p.epoch);
+  return uniform64(ready);
+}
+
 // Wave 0: pick from an issued poll (falling back to the blocking ag_pick when nothing is ready).
-__device__ __forceinline__ int ag_pick_polled(const AgParams& p, int ur0, int n_ur, uint64_t* s_done, int lane,
+__device__ __forceinline__ int ag_pick_polled(const AgParams& p, int ur0, int n_ur, uint64_t& done, int lane,
                                               const AgPoll& pl) {
   const uint64_t all = (p.n_ucols >= 64) ? ~0ull : ((1ull << p.n_ucols) - 1ull);
   uint64_t ready = all;
 #pragma unroll
   for (int q = 0; q < 4; ++q) ready &= __ballot(lane >= p.n_ucols || pl.f[q] == p.epoch);
-  volatile uint64_t* vd = s_done;
-  const uint64_t done = uniform64(*vd);
   const uint64_t cand = ready & ~done;
-  if (!cand) return ag_pick(p, ur0, n_ur, s_done, lane);
+  if (!cand) return ag_pick(p, ur0, n_ur, done, lane);
   const int u = __builtin_ctzll(cand);
-  *vd = done | (1ull << u);
+  done = uniform64(done | (1ull << u));
   return u;
 }
 
@@ -211,7 +280,7 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 // of the tile have completed.
 template <int EPI = 0>
 __device__ __forceinline__ void ag_compute_role(const AgParams& p, int slot, char* st0, char* st1, char* st2,
-                                                int* s_sched, uint64_t* s_done, int* s_claim) {
+                                                int* s_sched, int* s_claim) {
   AgTile g;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / AgTile::WN, wn = wave % AgTile::WN;
@@ -259,11 +328,12 @@ __device__ __forceinline__ void ag_compute_role(const AgParams& p, int slot, cha
     };
 
     g.zero();
+    uint64_t done = 0;  // wave 0: K-units scheduled for this tile
     if (p.emulated) {
       if (wave == 0) {
-        *(volatile uint64_t*)s_done = 0;
+        done = 0;
         for (int j = 0; j < n_pre; ++j) {
-          const int u = ag_pick(p, ur0, n_ur, s_done, lane);
+          const int u = ag_pick(p, ur0, n_ur, done, lane);
           if (lane == 0) s_sched[j] = u;
           if (u < 0) break;
         }
@@ -302,7 +372,7 @@ __device__ __forceinline__ void ag_compute_role(const AgParams& p, int slot, cha
     auto load = [&](int q, char* dst) { load_step(unit_of(q) * spu + q % spu, dst); };
     auto before_wait = [&](int q) {
       if (polled) {
-        const int u = ag_pick_polled(p, ur0, n_ur, s_done, lane, pl);
+        const int u = ag_pick_polled(p, ur0, n_ur, done, lane, pl);
         if (lane == 0) s_sched[decided_at(q)] = u;
       }
     };
@@ -329,6 +399,215 @@ __device__ __forceinline__ void ag_compute_role(const AgParams& p, int slot, cha
       if (!aborted && tid == 0) atomic_add_agent(p.h_ready + tm, 1u);
     }
     if (aborted) break;
+    t = -1;
+  }
+}
+
+// One tile of the AllGather + GEMM kernel on the 256 x 224 core (mk_gemm_tile16.hpp), A loaded two
+// steps ahead.  EMU: some of the tile's units have not landed yet, and the K loop visits K-units
+// ready-first: before a step's DMA, wave 0 polls the flags of the tile's unit rows (straight into
+// LDS), and after the step's MFMAs it names the lowest landed K-unit not yet scheduled as the one
+// that starts four steps later (three steps of lead: the A of a step is requested two steps ahead,
+// and every wave reads the schedule one step before that, so the LDS read's latency hides behind a
+// step of MFMAs instead of delaying the DMA).  Once every unit of the tile's rows has landed, wave 0
+// schedules the rest in ascending order and stops polling.  Without EMU every operand of the tile
+// is present and the K loop runs in K order with no hooks.  Returns false if a wait failed (the
+// tile's stores were skipped).
+template <bool EMU>
+__device__ __forceinline__ bool ag_tile16(const AgParams& p, int t, char* a0, char* a1, char* a2, char* b0, char* b1,
+                                          int* s_sched, uint32_t* s_poll) {
+  using G = TileGemm16;
+  G g;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / G::WN, wn = wave % G::WN;
+  const int nk = p.k >> 6;
+  const int spu = p.unit_cols >> 6;  // k-steps per K-unit
+  const int n_ku = p.n_ucols;
+  const uint64_t all = (n_ku >= 64) ? ~0ull : ((1ull << n_ku) - 1ull);
+  const uint32_t lda_b = (uint32_t)p.k * 2u, ldb_b = (uint32_t)p.n * 2u;
+  g.init(wm, wn, wave, lane, lda_b, ldb_b);
+  // a decision at the end of step q names the unit starting at step q + 1 + PD
+  constexpr int PD = 3;
+  const int n_pre = min(n_ku, (PD + spu) / spu);  // units starting at steps 0 .. PD, decided up front
+  {
+    const int tm = t / p.tiles_n, tn = t - tm * p.tiles_n;
+    const int m0 = tm * G::BM, n0 = tn * G::BN;
+    const int rows_valid = min(G::BM, p.m - m0), cols_valid = min(G::BN, p.n - n0);
+    const int ur0 = m0 / p.unit_rows, n_ur = rows_valid / p.unit_rows;
+    const char* a_tile = reinterpret_cast<const char*>(p.ag + (size_t)m0 * p.k);
+    const uint32_t a_tile_bytes = (uint32_t)rows_valid * lda_b;
+    const char* b_col = reinterpret_cast<const char*>(p.b + n0);
+    const uint32_t b_col_bytes = ((uint32_t)p.k * (uint32_t)p.n - (uint32_t)n0) * 2u;
+    g.zero();
+    uint64_t done = 0;    // wave 0: K-units scheduled for this tile
+    bool all_in = false;  // wave 0: every unit has landed and the whole schedule is written
+    if constexpr (EMU) {
+      if (wave == 0) {
+        for (int j = 0; j < n_pre; ++j) {
+          const int u = ag_pick(p, ur0, n_ur, done, lane);
+          if (lane == 0) s_sched[j] = u;
+          if (u < 0) break;
+        }
+      }
+      __syncthreads();
+      bool bad = false;
+      for (int j = 0; j < n_pre; ++j) bad |= __builtin_amdgcn_readfirstlane(s_sched[j]) < 0;
+      if (bad) return false;  // before any MFMA of this tile
+    }
+    // A failed wait (watchdog or another workgroup's fault) inside the K loop does not leave the
+    // loop: the remaining steps drain on K-unit 0 (in bounds, result discarded) and the tile's
+    // stores are skipped.
+    bool aborted = false;
+    // EMU: K offsets (in steps of 64) of the next B (step q+1) and A (step q+2) DMA, and the raw
+    // schedule entry of step q+3's unit, read one step ahead
+    int ks_b = 0, ks_a = 0, raw_n = 0;
+    auto decode = [&](int raw, int s) -> int {
+      const int u = __builtin_amdgcn_readfirstlane(raw);
+      aborted |= u < 0;
+      return (u < 0 ? 0 : u) * spu + s % spu;
+    };
+    auto dma_a = [&](int ks, char* dst) {
+      const uint32_t ca = (uint32_t)ks * 128u;
+      g.dma_a(a_tile + ca, a_tile_bytes - ca, lda_b, dst, wave);
+    };
+    auto dma_b = [&](int ks, char* dst) {
+      const uint32_t rb = (uint32_t)ks * 64u * ldb_b;
+      g.dma_b(b_col + rb, b_col_bytes - rb, dst, wave);
+    };
+    auto prologue = [&](char* pa0, char* pb0, char* pa1) {
+      const int k0 = EMU ? decode(s_sched[0], 0) : 0;
+      const int k1 = nk > 1 ? (EMU ? decode(s_sched[1 / spu], 1) : 1) : 0;
+      dma_a(k0, pa0);
+      dma_b(k0, pb0);
+      if (nk > 1) dma_a(k1, pa1);
+      ks_b = k1;
+      raw_n = (EMU && nk > 2) ? s_sched[2 / spu] : 0;
+    };
+    auto load_a = [&](int s, char* dst) { dma_a(EMU ? ks_a : s, dst); };
+    auto load_b = [&](int s, char* dst) { dma_b(EMU ? ks_b : s, dst); };
+    bool polled = false;
+    auto decided_at = [&](int q) -> int {  // the unit decided at the end of step q, or -1
+      const int s = q + 1 + PD;
+      if (s >= nk || s % spu) return -1;
+      const int jn = s / spu;
+      return (jn >= n_pre && jn < n_ku) ? jn : -1;
+    };
+    auto before_load = [&](int q) {
+      if constexpr (EMU) {
+        ks_a = decode(raw_n, q + 2);
+        polled = wave == 0 && !all_in && decided_at(q) >= 0;
+        if (polled) ag_poll_lds(p, ur0, n_ur, s_poll);
+      }
+    };
+    auto after_load = [&](int q) {
+      if constexpr (EMU) {
+        ks_b = ks_a;
+        raw_n = q + 3 < nk ? s_sched[(q + 3) / spu] : 0;
+      }
+    };
+    auto before_wait = [&](int q) {
+      if constexpr (EMU) {
+        if (polled) {
+          const int jn = decided_at(q);
+          // the poll was requested before this step's B and A DMA: only those may still be in flight
+          // (wave 0 issues 4 B and 4 A instructions per step)
+          wait_vm<4 + G::A_INSTR>();
+          uint64_t ready = ag_ready_lds(p, ur0, n_ur, lane, s_poll);
+          if ((ready & ~done) == 0) ready = ag_repoll_until_new(p, ur0, n_ur, lane, s_poll, done);
+          if (ready == 0) {  // timeout or fault: the loop drains on K-unit 0 and skips the stores
+            if (lane == 0) s_sched[jn] = -1;
+          } else if (ready == all) {  // every unit is here: the rest in ascending order
+            for (int j = jn; j < n_ku; ++j) {
+              const int u = __builtin_ctzll(~done & all);
+              done |= 1ull << u;
+              if (lane == 0) s_sched[j] = u;
+            }
+            all_in = true;
+          } else {
+            const int u = __builtin_ctzll(ready & ~done);
+            done |= 1ull << u;
+            if (lane == 0) s_sched[jn] = u;
+          }
+        }
+      }
+    };
+    k_loop_a3b2(g, nk, a0, a1, a2, b0, b1, prologue, load_a, load_b, before_load, after_load, before_wait);
+
+    // epilogue: the tile staged through two A slots (four waves each) into row-contiguous 16-byte
+    // stores; C is written once and read by no one here: streaming stores
+    float* wl = reinterpret_cast<float*>((wave < 4 ? a0 : a1) + (wave & 3) * G::EPI_WAVE);
+    g.epilogue(wl, wm, wn, lane, [&](int row, int col, f32x4 v) {
+      if (!aborted && row < rows_valid && col < cols_valid)
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p.c + (size_t)(m0 + row) * p.n + (n0 + col)));
+    });
+    __syncthreads();  // the next tile's prologue reuses the LDS
+    return !aborted;
+  }
+}
+
+// Wave 0: spin (sleeping between polls) until every K-unit of unit rows [ur0, ur0 + n_ur) has
+// landed; false on timeout or when another workgroup has recorded a fault.
+__device__ __forceinline__ bool ag_wait_rows(const AgParams& p, int ur0, int n_ur, int lane) {
+  const uint64_t all = (p.n_ucols >= 64) ? ~0ull : ((1ull << p.n_ucols) - 1ull);
+  const uint64_t t0 = wall_ticks();
+  for (int n = 0; uniform64(ag_ready_mask(p, ur0, n_ur, all, lane)) != all; ++n) {
+    __builtin_amdgcn_s_sleep(2);
+    if ((n & 7) == 7) {
+      if (__builtin_amdgcn_readfirstlane(status_bad(p.status) ? 1 : 0)) return false;
+      if (wall_ticks() - t0 > p.timeout_ticks) {
+        if (lane == 0) raise_status(p.status, ST_TIMEOUT);
+        return false;
+      }
+    }
+  }
+  return true;
+}
+
+// Compute role of the AllGather + GEMM kernel.  The workgroup first runs tile t_static (-1: none),
+// then tiles left over past the grid, claimed from a shared counter.  With emulated arrival, wave 0
+// looks at the flags of a tile's unit rows first: when every unit has landed the tile runs the K
+// loop without hooks (K order, as with resident operands); otherwise a workgroup that starts its
+// tiles only after copying (wait_landed) waits until they have -- its copy ends near the end of
+// the landing, and the loop without hooks is faster than the ready-first one by more than the
+// wait -- and the others run the ready-first loop, consuming each K-unit as soon as it has landed.
+// mark_ready: record the first tile's operands-ready time in trace slot 5 (compute workgroups; a
+// copy workgroup's slot 5 holds the end of its copy).
+__device__ __forceinline__ void ag_compute_role16(const AgParams& p, int t_static, bool mark_ready, bool wait_landed,
+                                                  char* a0, char* a1, char* a2, char* b0, char* b1, int* s_sched,
+                                                  int* s_claim, uint32_t* s_poll) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n_tiles = p.tiles_m * p.tiles_n;
+  bool first = mark_ready;
+  int t = t_static;
+  while (true) {
+    if (t < 0) {
+      if (tid == 0) *s_claim = (int)gridDim.x + (int)atomic_add_agent(p.counters + CTR_AG_TILE, 1u);
+      __syncthreads();
+      t = *s_claim;  // rewritten only after the tile's barriers
+      __syncthreads();
+      if (t >= n_tiles) break;
+    }
+    bool emu = false;
+    if (p.emulated) {
+      const int m0 = (t / p.tiles_n) * TileGemm16::BM;
+      const int ur0 = m0 / p.unit_rows, n_ur = min(TileGemm16::BM, p.m - m0) / p.unit_rows;
+      if (wave == 0) {
+        const uint64_t all = (p.n_ucols >= 64) ? ~0ull : ((1ull << p.n_ucols) - 1ull);
+        int state = uniform64(ag_ready_mask(p, ur0, n_ur, all, lane)) == all ? 0 : 1;  // 0: landed, 1: not yet
+        if (state == 1 && wait_landed) state = ag_wait_rows(p, ur0, n_ur, lane) ? 0 : 2;  // 2: failed
+        if (lane == 0) *s_claim = state;
+      }
+      __syncthreads();
+      const int state = *s_claim;
+      __syncthreads();
+      if (state == 2) break;
+      emu = state == 1;
+    }
+    if (first) trace_mark(p.trace, 5);
+    first = false;
+    const bool ok = emu ? ag_tile16<true>(p, t, a0, a1, a2, b0, b1, s_sched, s_poll)
+                        : ag_tile16<false>(p, t, a0, a1, a2, b0, b1, s_sched, s_poll);
+    if (!ok) break;
     t = -1;
   }
 }

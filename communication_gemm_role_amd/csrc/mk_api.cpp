@@ -312,7 +312,7 @@ int mk_mlp_ag_rs(mk_ctx* ctx, void* stream, const uint16_t* const* a_shards, int
   mkh::MlpPlan P;
   int code = mkh::plan_mlp(ws_of(ctx), opts ? &o : nullptr, (const void* const*)a_shards, world, rank, m_shard, k,
                            b_up, n_up, b_down, n_out, (const void* const*)peer_partials, a_gathered, h, owned_out,
-                           (void* const*)outbox, mk::ag_tile_m(), mk::ag_tile_n(), mk::red_tile_m(M, n_out),
+                           (void* const*)outbox, mk::mlp_tile_m(), mk::mlp_tile_n(), mk::red_tile_m(M, n_out),
                            mk::red_tile_n(M, n_out), mk::red_tile_waves(M, n_out), &P);
   if (code != MK_OK) return code;
   DeviceGuard g(ctx->device);

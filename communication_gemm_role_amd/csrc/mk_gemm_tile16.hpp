@@ -1,0 +1,231 @@
+// Compute role core for the AllGather + GEMM kernel: one 256 x 224 fp32 output tile of C = A @ B
+// with bf16 operands on v_mfma_f32_16x16x32_bf16, eight waves of 64 x 112 (4 x 7 fragments of
+// 16 x 16).  At N = 1792 the 224-column tiles give 32 x 8 = 256 tiles, one per CU of an MI355X.
+//
+// MFMA lane layout (16 x 16 x 32, checked on the device against the 32 x 32 x 16 core): the A
+// operand of lane l is row l%16, k = 8*(l/16) .. +7; the B operand is column l%16 with the same
+// k; accumulator element r of lane l is row 4*(l/16) + r, column l%16.
+//
+// Operands go global -> LDS by buffer_load ... lds, 16 bytes per lane.  LDS per k-step of 64:
+//   A slot  256 rows x 128 B (32 KiB); 16-byte chunks XOR-swizzled by row pair (chunk p of row r
+//           holds global chunk p ^ ((r >> 1) & 7)), so 16 lanes reading one logical chunk of 16
+//           consecutive rows hit 64 distinct banks;
+//   B slot  64 k-rows x 448 B (28 KiB), not swizzled: a 16-lane group of a transposed read covers
+//           four consecutive k-rows, whose 448-byte rows start 48 banks apart, so the group's 32
+//           bytes per row fall in four disjoint bank ranges (measured: an XOR swizzle of the chunks by
+//           k-row block changed neither the LDS bank-conflict counter nor the time), and a fragment's
+//           address is one base plus 32 bytes per fragment.
+// The B operand is read with ds_read_b64_tr_b16: in each 16-lane group, lane i receives element
+// i%4 of the 8-byte pieces addressed by lanes 4j + i/4 (j = 0..3); a group reading k-rows
+// 8g + j, columns 4q..4q+3 (lane 4j + q) gives lane i column i of those four k-rows, and a second
+// read four rows down completes the lane's 8 consecutive k.
+//
+// The K loop (k_loop_a3b2) keeps A in three slots loaded two steps ahead and B in two slots one
+// step ahead (3 x 32 + 2 x 28 = 152 KiB): the A rows of a tile row are shared by the tiles of
+// one XCD and come from HBM, so they get the longer lead.
+#pragma once
+#include "mk_gemm_tile.hpp"
+
+namespace mk {
+
+struct TileGemm16 {
+  static constexpr int BM = mk_tiles::kAg16.bm, BN = mk_tiles::kAg16.bn, BK = 64;
+  static constexpr int WM = mk_tiles::kAg16.wm, WN = mk_tiles::kAg16.wn, NW = WM * WN;
+  static constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 16, FN = WTN / 16;
+  static_assert(BM == 256 && BN == 224 && WM == 4 && WN == 2, "the layout below is written for 256 x 224, 4 x 2 waves");
+  static constexpr int ROW_A = BK * 2, ROW_B = BN * 2;  // bytes per LDS row
+  static constexpr int SLOT_A = BM * ROW_A;              // 32 KiB
+  static constexpr int SLOT_B = BK * ROW_B;              // 28 KiB
+  static constexpr int A_INSTR = SLOT_A / NW / 1024;     // 1 KiB DMA instructions per wave and step
+  static constexpr int B_INSTR = SLOT_B / 1024;          // 28 per step: waves 0-3 issue 4, waves 4-7 issue 3
+  static_assert(A_INSTR == 4 && B_INSTR == 28, "A: 4 per wave; B: 4 x 4 + 4 x 3");
+
+  f32x4 acc[FM][FN];
+  uint32_t a_dma[2];   // A DMA byte offset inside an 8-row group (two swizzle phases)
+  uint32_t b_dma[4];   // B DMA byte offset inside the step's rows, per instruction of this wave
+  uint32_t a_rd[2];    // A operand LDS offset per 32-wide k sub-step
+  uint32_t b_rd;       // B operand LDS offset of fragment 0's first transposed read (fragment j: + 32 j)
+
+  // first LDS KiB of this wave's B instructions: waves 0-3 take 4 each, waves 4-7 take 3 each
+  __device__ static int b_ins(int wave, int i) { return wave < 4 ? 4 * wave + i : 16 + 3 * (wave - 4) + i; }
+
+  __device__ __forceinline__ void init(int wm, int wn, int wave, int lane, uint32_t lda_b, uint32_t ldb_b) {
+#pragma unroll
+    for (int ph = 0; ph < 2; ++ph) {
+      const int x = ((lane >> 4) + 4 * ph) & 7;
+      a_dma[ph] = (uint32_t)(lane >> 3) * lda_b + (uint32_t)((lane & 7) ^ x) * 16u;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int o = b_ins(wave, i) * 1024 + lane * 16;  // LDS byte of this lane's chunk
+      const int r = o / ROW_B, p = (o % ROW_B) >> 4;
+      b_dma[i] = (uint32_t)r * ldb_b + (uint32_t)p * 16u;
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int row = wm * WTM + (lane & 15);
+      const int c = 4 * s + (lane >> 4);
+      a_rd[s] = (uint32_t)row * ROW_A + (uint32_t)((c ^ ((row >> 1) & 7)) * 16);
+    }
+    const int g = lane >> 4, jr = (lane & 15) >> 2, q = lane & 3;
+    // lane 4 jr + q of group g: k-row 8 g + jr (the second read four rows down), columns 4q .. 4q+3
+    b_rd = (uint32_t)(8 * g + jr) * ROW_B + (uint32_t)(wn * WTN + 4 * q) * 2u;
+  }
+
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // A k-step into slot `la`: abase points at (row m0, the step's first column); a_bytes = bytes from
+  // there to the end of the valid rows (rows past it read as zeros).
+  __device__ __forceinline__ void dma_a(const char* abase, uint32_t a_bytes, uint32_t lda_b, char* la, int wave) {
+#pragma unroll
+    for (int i = 0; i < A_INSTR; ++i) {
+      const int r0 = wave * (BM / NW) + i * 8;
+      const auto rs = rsrc_at(abase, a_bytes, (uint32_t)r0 * lda_b);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(la + r0 * ROW_A), 16,
+                                               a_dma[i & 1], 0, 0, 0);
+    }
+  }
+  // B k-step into slot `lb`: bbase points at (the step's first k-row, column n0); b_bytes = bytes from
+  // there to the end of the window (columns past the matrix read as zeros only at its very end; the
+  // caller clips ragged columns at the store).
+  __device__ __forceinline__ void dma_b(const char* bbase, uint32_t b_bytes, char* lb, int wave) {
+    const auto rs = make_rsrc(bbase, __builtin_amdgcn_readfirstlane(b_bytes));
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(lb + b_ins(wave, i) * 1024),
+                                               16, b_dma[i], 0, 0, 0);
+    if (wave < 4)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(lb + b_ins(wave, 3) * 1024),
+                                               16, b_dma[3], 0, 0, 0);
+  }
+
+  __device__ __forceinline__ void b_frag(const char* lb, int s, int j, bf16x8& bf) {
+    const i16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(const_cast<char*>(lb) + b_rd + 32 * j + (32 * s) * ROW_B));
+    const i16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(const_cast<char*>(lb) + b_rd + 32 * j + (32 * s + 4) * ROW_B));
+    bf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+  // One k-step of 64: two sub-steps of 32, one sub-step's fragments live at a time (the other wave
+  // of the SIMD issues MFMAs while this one waits for its LDS reads; measured as fast as reading
+  // the second sub-step's fragments ahead, with 44 fewer live registers).
+  __device__ __forceinline__ void mma(const char* la, const char* lb) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      bf16x8 af[FM], bf[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(la + a_rd[s] + i * 16 * ROW_A);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) b_frag(lb, s, j, bf[j]);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // Epilogue: each wave stages one 16-row slab of its sub-tile at a time in `wl` (16 x 112 floats,
+  // rows padded to 116) and hands out row-contiguous float4s f(row_in_tile, col_in_tile, value).
+  static constexpr int EPI_STRIDE = WTN + 4;
+  static constexpr int EPI_WAVE = 16 * EPI_STRIDE * 4;  // 7424 bytes
+  static_assert(4 * EPI_WAVE <= SLOT_A, "four waves' staging fits one A slot");
+  template <class F>
+  __device__ __forceinline__ void epilogue(float* wl, int wm, int wn, int lane_in, F&& f) {
+    int lane = lane_in;  // opaque copy: keeps the staging addresses out of the persistent loop
+    asm volatile("" : "+v"(lane));
+    constexpr int C4 = WTN / 4;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) wl[(4 * (lane >> 4) + r) * EPI_STRIDE + j * 16 + (lane & 15)] = acc[i][j][r];
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int q = 0; q < (16 * C4) / 64; ++q) {
+        const int idx = q * 64 + lane;
+        const int row = idx / C4, c4 = idx - row * C4;
+        f(wm * WTM + i * 16 + row, wn * WTN + c4 * 4, *reinterpret_cast<const f32x4*>(wl + row * EPI_STRIDE + c4 * 4));
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+};
+
+// K loop over three A slots (a0..a2, loaded two steps ahead) and two B slots (b0, b1, one step
+// ahead).  Step q issues B(q+1) and then A(q+2), runs the MFMAs of step q, and waits until only
+// A(q+2) may still be in flight, so every A load has two steps of MFMA work to land and every B
+// load one.  prologue(a0, b0, a1) issues A(0), B(0) and, when nk > 1, A(1), in that order;
+// load_a(step, slot) / load_b(step, slot) issue one step's DMA.  Hooks for the emulated arrival:
+// before_load(q) runs before the step's DMA, after_load(q) right after it (before the MFMAs),
+// before_wait(q) after the MFMAs.
+// The steady state runs in groups of six steps (the slot pattern's period) with no condition
+// inside a step, so the compiler's wait insertion sees straight-line code and leaves the A loads
+// in flight; the last steps run with conditions.  Barriers carry no memory fence: the explicit
+// vmcnt wait orders the DMA, and lgkmcnt(0) retires this wave's LDS reads of the slot that the
+// next step overwrites.
+template <class G, class Prologue, class LoadA, class LoadB, class Pre, class Post, class After>
+__device__ __forceinline__ void k_loop_a3b2(G& g, int nk, char* a0, char* a1, char* a2, char* b0, char* b1,
+                                            Prologue&& prologue, LoadA&& load_a, LoadB&& load_b, Pre&& before_load,
+                                            Post&& after_load, After&& before_wait) {
+  constexpr int DA = G::A_INSTR;
+  prologue(a0, b0, a1);
+  if (nk > 1) wait_vm<DA>();
+  else wait_vm<0>();
+  __syncthreads();
+  auto step = [&](int q, char* ca, char* cb, char* pa, char* pb) {
+    before_load(q);
+    load_b(q + 1, pb);
+    load_a(q + 2, pa);
+    after_load(q);
+    g.mma(ca, cb);
+    before_wait(q);
+    wait_vm<DA>();
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    barrier_only();
+  };
+  auto last = [&](int q, char* ca, char* cb, char* pa, char* pb) {
+    if (q >= nk) return;
+    before_load(q);
+    if (q + 1 < nk) load_b(q + 1, pb);
+    const bool more = q + 2 < nk;
+    if (more) load_a(q + 2, pa);
+    after_load(q);
+    g.mma(ca, cb);
+    before_wait(q);
+    if (more) wait_vm<DA>();
+    else wait_vm<0>();
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    barrier_only();
+  };
+  int q = 0;
+  for (; q + 8 <= nk; q += 6) {
+    step(q + 0, a0, b0, a2, b1);
+    step(q + 1, a1, b1, a0, b0);
+    step(q + 2, a2, b0, a1, b1);
+    step(q + 3, a0, b1, a2, b0);
+    step(q + 4, a1, b0, a0, b1);
+    step(q + 5, a2, b1, a1, b0);
+  }
+  // at most seven steps remain, starting at slot phase 0
+  last(q + 0, a0, b0, a2, b1);
+  last(q + 1, a1, b1, a0, b0);
+  last(q + 2, a2, b0, a1, b1);
+  last(q + 3, a0, b1, a2, b0);
+  last(q + 4, a1, b0, a0, b1);
+  last(q + 5, a2, b1, a1, b0);
+  last(q + 6, a0, b0, a2, b1);
+  wait_vm<0>();
+  __syncthreads();
+}
+
+}  // namespace mk

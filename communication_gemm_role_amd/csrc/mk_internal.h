@@ -174,6 +174,8 @@ hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t s);
 // Tile sizes the host needs for scheduling and validation
 int ag_tile_m();
 int ag_tile_n();
+int mlp_tile_m();  // the MLP block's up-projection tile
+int mlp_tile_n();
 int red_tile_m(int m, int n);
 int red_tile_n(int m, int n);
 int red_tile_waves(int m, int n);

@@ -22,6 +22,9 @@
 
 namespace mk {
 
+int mlp_tile_m() { return AgTile::BM; }
+int mlp_tile_n() { return AgTile::BN; }
+
 static_assert(AgTile::BM == RedBig::BM, "a 256-row block of H is one tile row of both phases");
 static_assert(AG_THREADS == RedBig::NW * 64, "both phases run eight-wave workgroups");
 
@@ -30,7 +33,6 @@ __global__ __launch_bounds__(AG_THREADS, 1) void mlp_kernel(MlpParams p) {
   __shared__ __attribute__((aligned(16))) char st1[AgTile::STAGE];
   __shared__ __attribute__((aligned(16))) char st2[16];
   __shared__ int s_sched[64];
-  __shared__ uint64_t s_done;
   __shared__ int s_claim;
   __shared__ int s_ok;
   __shared__ int s_last;
@@ -40,14 +42,14 @@ __global__ __launch_bounds__(AG_THREADS, 1) void mlp_kernel(MlpParams p) {
   // phase 1: AllGather + up-projection
   if (wg < p.ag.n_copy) {
     trace_begin(p.ag.trace, ROLE_COPY);
-    ag_copy_role(p.ag, wg, st0, st1);
+    ag_copy_role<64>(p.ag, wg, st0, st1);
     trace_mark(p.ag.trace, 5);
     __syncthreads();  // the copy's LDS slots become the GEMM's stage buffers
-    ag_compute_role<1>(p.ag, -1, st0, st1, st2, s_sched, &s_done, &s_claim);
+    ag_compute_role<1>(p.ag, -1, st0, st1, st2, s_sched, &s_claim);
   } else {
     trace_begin(p.ag.trace, ROLE_COMPUTE);
     const int slot = wg - p.ag.n_copy;
-    if (slot < p.ag.n_compute) ag_compute_role<1>(p.ag, slot, st0, st1, st2, s_sched, &s_done, &s_claim);
+    if (slot < p.ag.n_compute) ag_compute_role<1>(p.ag, slot, st0, st1, st2, s_sched, &s_claim);
   }
   __syncthreads();
   trace_mark(p.ag.trace, 6);  // phase 1 done for this workgroup
