@@ -25,7 +25,7 @@ __global__ __launch_bounds__(AG_THREADS, 1) void ag_gemm_kernel(AgParams p) {
   __shared__ __attribute__((aligned(16))) char a2[G::SLOT_A];
   __shared__ __attribute__((aligned(16))) char b0[G::SLOT_B];
   __shared__ __attribute__((aligned(16))) char b1[G::SLOT_B];
-  __shared__ int s_sched[64];
+  __shared__ int s_sched[AG_SCHED_WORDS];
   __shared__ int s_claim;
   __shared__ __attribute__((aligned(16))) uint32_t s_poll[4 * 64];
   const int wg = blockIdx.x, grid = gridDim.x, n_tiles = p.tiles_m * p.tiles_n;

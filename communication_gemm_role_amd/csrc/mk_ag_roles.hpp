@@ -403,6 +403,11 @@ __device__ __forceinline__ void ag_compute_role(const AgParams& p, int slot, cha
   }
 }
 
+// s_sched: entries 0 .. n_ucols - 1 name the K-unit each unit slot of the tile's K loop takes;
+// entry AG_SCHED_ALL_IN says that every entry is written (the loop no longer polls).
+constexpr int AG_SCHED_ALL_IN = 64;
+constexpr int AG_SCHED_WORDS = AG_SCHED_ALL_IN + 1;
+
 // One tile of the AllGather + GEMM kernel on the 256 x 224 core (mk_gemm_tile16.hpp), A loaded two
 // steps ahead.  EMU: some of the tile's units have not landed yet, and the K loop visits K-units
 // ready-first: before a step's DMA, wave 0 polls the flags of the tile's unit rows (straight into
@@ -443,6 +448,7 @@ __device__ __forceinline__ bool ag_tile16(const AgParams& p, int t, char* a0, ch
     bool all_in = false;  // wave 0: every unit has landed and the whole schedule is written
     if constexpr (EMU) {
       if (wave == 0) {
+        if (lane == 0) s_sched[AG_SCHED_ALL_IN] = 0;
         for (int j = 0; j < n_pre; ++j) {
           const int u = ag_pick(p, ur0, n_ur, done, lane);
           if (lane == 0) s_sched[j] = u;
@@ -492,21 +498,23 @@ __device__ __forceinline__ bool ag_tile16(const AgParams& p, int t, char* a0, ch
       const int jn = s / spu;
       return (jn >= n_pre && jn < n_ku) ? jn : -1;
     };
-    auto before_load = [&](int q) {
+    auto before_load = [&](int q, auto ph) {
       if constexpr (EMU) {
         ks_a = decode(raw_n, q + 2);
-        polled = wave == 0 && !all_in && decided_at(q) >= 0;
-        if (polled) ag_poll_lds(p, ur0, n_ur, s_poll);
+        if constexpr (decltype(ph)::heavy) {
+          polled = wave == 0 && !all_in && decided_at(q) >= 0;
+          if (polled) ag_poll_lds(p, ur0, n_ur, s_poll);
+        }
       }
     };
-    auto after_load = [&](int q) {
+    auto after_load = [&](int q, auto) {
       if constexpr (EMU) {
         ks_b = ks_a;
         raw_n = q + 3 < nk ? s_sched[(q + 3) / spu] : 0;
       }
     };
-    auto before_wait = [&](int q) {
-      if constexpr (EMU) {
+    auto before_wait = [&](int q, auto ph) {
+      if constexpr (EMU && decltype(ph)::heavy) {
         if (polled) {
           const int jn = decided_at(q);
           // the poll was requested before this step's B and A DMA: only those may still be in flight
@@ -523,6 +531,7 @@ __device__ __forceinline__ bool ag_tile16(const AgParams& p, int t, char* a0, ch
               if (lane == 0) s_sched[j] = u;
             }
             all_in = true;
+            if (lane == 0) s_sched[AG_SCHED_ALL_IN] = 1;
           } else {
             const int u = __builtin_ctzll(ready & ~done);
             done |= 1ull << u;
@@ -531,7 +540,12 @@ __device__ __forceinline__ bool ag_tile16(const AgParams& p, int t, char* a0, ch
         }
       }
     };
-    k_loop_a3b2(g, nk, a0, a1, a2, b0, b1, prologue, load_a, load_b, before_load, after_load, before_wait);
+    // every unit scheduled: the rest of the loop runs without the polling and deciding code
+    auto leave = [&]() -> bool {
+      if constexpr (EMU) return __builtin_amdgcn_readfirstlane(s_sched[AG_SCHED_ALL_IN]) != 0;
+      else return true;
+    };
+    k_loop_a3b2(g, nk, a0, a1, a2, b0, b1, prologue, load_a, load_b, before_load, after_load, before_wait, leave);
 
     // epilogue: the tile staged through two A slots (four waves each) into row-contiguous 16-byte
     // stores; C is written once and read by no one here: streaming stores

@@ -165,57 +165,67 @@ struct TileGemm16 {
 // ahead).  Step q issues B(q+1) and then A(q+2), runs the MFMAs of step q, and waits until only
 // A(q+2) may still be in flight, so every A load has two steps of MFMA work to land and every B
 // load one.  prologue(a0, b0, a1) issues A(0), B(0) and, when nk > 1, A(1), in that order;
-// load_a(step, slot) / load_b(step, slot) issue one step's DMA.  Hooks for the emulated arrival:
-// before_load(q) runs before the step's DMA, after_load(q) right after it (before the MFMAs),
-// before_wait(q) after the MFMAs.
+// load_a(step, slot) / load_b(step, slot) issue one step's DMA.  Hooks for the emulated arrival,
+// each called with a Phase tag: before_load(q, ph) runs before the step's DMA, after_load(q, ph)
+// right after it (before the MFMAs), before_wait(q, ph) after the MFMAs.
 // The steady state runs in groups of six steps (the slot pattern's period) with no condition
 // inside a step, so the compiler's wait insertion sees straight-line code and leaves the A loads
-// in flight; the last steps run with conditions.  Barriers carry no memory fence: the explicit
-// vmcnt wait orders the DMA, and lgkmcnt(0) retires this wave's LDS reads of the slot that the
-// next step overwrites.
-template <class G, class Prologue, class LoadA, class LoadB, class Pre, class Post, class After>
+// in flight; the last steps run with conditions.  It has two phases: groups with the hooks'
+// full work (Phase<true>) while leave() is false -- evaluated between groups, uniform across the
+// workgroup -- and then groups with Phase<false>, whose hooks do the light part only, so that the
+// heavy part's code and registers stay out of the rest of the loop.  The last steps run with
+// Phase<true>.  Barriers carry no memory fence: the explicit vmcnt wait orders the DMA, and
+// lgkmcnt(0) retires this wave's LDS reads of the slot that the next step overwrites.
+template <bool HEAVY>
+struct Phase {
+  static constexpr bool heavy = HEAVY;
+};
+
+template <class G, class Prologue, class LoadA, class LoadB, class Pre, class Post, class After, class Leave>
 __device__ __forceinline__ void k_loop_a3b2(G& g, int nk, char* a0, char* a1, char* a2, char* b0, char* b1,
                                             Prologue&& prologue, LoadA&& load_a, LoadB&& load_b, Pre&& before_load,
-                                            Post&& after_load, After&& before_wait) {
+                                            Post&& after_load, After&& before_wait, Leave&& leave) {
   constexpr int DA = G::A_INSTR;
   prologue(a0, b0, a1);
   if (nk > 1) wait_vm<DA>();
   else wait_vm<0>();
   __syncthreads();
-  auto step = [&](int q, char* ca, char* cb, char* pa, char* pb) {
-    before_load(q);
+  auto step = [&](auto ph, int q, char* ca, char* cb, char* pa, char* pb) {
+    before_load(q, ph);
     load_b(q + 1, pb);
     load_a(q + 2, pa);
-    after_load(q);
+    after_load(q, ph);
     g.mma(ca, cb);
-    before_wait(q);
+    before_wait(q, ph);
     wait_vm<DA>();
     __builtin_amdgcn_s_waitcnt(0xc07f);
     barrier_only();
   };
+  auto group = [&](auto ph, int q) {
+    step(ph, q + 0, a0, b0, a2, b1);
+    step(ph, q + 1, a1, b1, a0, b0);
+    step(ph, q + 2, a2, b0, a1, b1);
+    step(ph, q + 3, a0, b1, a2, b0);
+    step(ph, q + 4, a1, b0, a0, b1);
+    step(ph, q + 5, a2, b1, a1, b0);
+  };
   auto last = [&](int q, char* ca, char* cb, char* pa, char* pb) {
     if (q >= nk) return;
-    before_load(q);
+    before_load(q, Phase<true>{});
     if (q + 1 < nk) load_b(q + 1, pb);
     const bool more = q + 2 < nk;
     if (more) load_a(q + 2, pa);
-    after_load(q);
+    after_load(q, Phase<true>{});
     g.mma(ca, cb);
-    before_wait(q);
+    before_wait(q, Phase<true>{});
     if (more) wait_vm<DA>();
     else wait_vm<0>();
     __builtin_amdgcn_s_waitcnt(0xc07f);
     barrier_only();
   };
   int q = 0;
-  for (; q + 8 <= nk; q += 6) {
-    step(q + 0, a0, b0, a2, b1);
-    step(q + 1, a1, b1, a0, b0);
-    step(q + 2, a2, b0, a1, b1);
-    step(q + 3, a0, b1, a2, b0);
-    step(q + 4, a1, b0, a0, b1);
-    step(q + 5, a2, b1, a1, b0);
-  }
+  for (; q + 8 <= nk && !leave(); q += 6) group(Phase<true>{}, q);
+  for (; q + 8 <= nk; q += 6) group(Phase<false>{}, q);
   // at most seven steps remain, starting at slot phase 0
   last(q + 0, a0, b0, a2, b1);
   last(q + 1, a1, b1, a0, b0);
