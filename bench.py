@@ -50,7 +50,7 @@ TRACE_UNTOUCHED = -1
 # figures are valid only for the kernel they were taken on: the file records a hash of the sources
 # that make up the kernel and its launch, and the traffic is reported as null once they differ.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ag_gemm_kernel_mlp_ag_traffic.md")
-KERNEL_SOURCES = ["mk_ag_gemm.hip", "mk_ag_roles.hpp", "mk_copy_ring.hpp", "mk_gemm_tile.hpp", "mk_device.hpp",
+KERNEL_SOURCES = ["mk_ag_gemm.hip", "mk_ag_roles.hpp", "mk_copy_ring.hpp", "mk_gemm_tile.hpp", "mk_gemm_tile16.hpp", "mk_tiles.h", "mk_device.hpp",
                   "mk_internal.h", "mk_host_logic.h", "mk_api.cpp"]
 
 
