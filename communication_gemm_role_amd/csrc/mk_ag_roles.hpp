@@ -547,9 +547,9 @@ __device__ __forceinline__ bool ag_tile16(const AgParams& p, int t, char* a0, ch
     };
     k_loop_a3b2(g, nk, a0, a1, a2, b0, b1, prologue, load_a, load_b, before_load, after_load, before_wait, leave);
 
-    // epilogue: the tile staged through two A slots (four waves each) into row-contiguous 16-byte
-    // stores; C is written once and read by no one here: streaming stores
-    float* wl = reinterpret_cast<float*>((wave < 4 ? a0 : a1) + (wave & 3) * G::EPI_WAVE);
+    // epilogue: the tile staged through the A slots into row-contiguous 16-byte stores; C is
+    // written once and read by no one here: streaming stores
+    float* wl = G::epi_buf(wave, a0, a1, a2);
     g.epilogue(wl, wm, wn, lane, [&](int row, int col, f32x4 v) {
       if (!aborted && row < rows_valid && col < cols_valid)
         __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p.c + (size_t)(m0 + row) * p.n + (n0 + col)));

@@ -238,7 +238,7 @@ static int gemm_reduce(int is_rs, mk_ctx* ctx, void* stream, const uint16_t* a, 
   mkh::RedPlan P;
   int code = mkh::plan_reduce(ws_of(ctx), opts ? &o : nullptr, is_rs, a, b, m, n, k, world, rank,
                               (const void* const*)peers, out, (void* const*)outbox, mk::red_tile_m(m, n),
-                              mk::red_tile_n(m, n), mk::red_tile_waves(m, n), &P);
+                              mk::red_tile_n(m, n), mk::red_tile_waves(m, n), mk::red_ring_kib(m, n), &P);
   if (code != MK_OK) return code;
   DeviceGuard g(ctx->device);
   if (!g.ok) return MK_ERR_HIP;

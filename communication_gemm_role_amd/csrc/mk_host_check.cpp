@@ -23,11 +23,11 @@ int mkh_plan_ag(size_t n_flags, size_t n_counters, size_t inbox_bytes, int grid,
 int mkh_plan_reduce(size_t n_flags, size_t n_counters, size_t inbox_bytes, int grid, const mkh::Opts* o, int is_rs,
                     const void* a, const void* b, int m, int n, int k, int world, int rank, const void* const* peers,
                     const void* out_buf, void* const* outbox, int tile_m, int tile_n, int tile_waves,
-                    long long* out) {
+                    int ring_kib, long long* out) {
   mkh::Ws ws{n_flags, n_counters, inbox_bytes, grid};
   mkh::RedPlan P{};
-  const int code =
-      mkh::plan_reduce(ws, o, is_rs, a, b, m, n, k, world, rank, peers, out_buf, outbox, tile_m, tile_n, tile_waves, &P);
+  const int code = mkh::plan_reduce(ws, o, is_rs, a, b, m, n, k, world, rank, peers, out_buf, outbox, tile_m, tile_n,
+                                    tile_waves, ring_kib, &P);
   const long long v[] = {P.m_slice, P.p_rows, P.unit_rows, P.unit_cols, P.n_ucols, P.units_per_peer, P.n_units,
                          P.emulated, P.n_order, P.drop_pos, P.n_copy, P.n_reduce, P.n_compute, P.tiles_m, P.tiles_n,
                          P.own_tile_begin, P.own_tile_end, (long long)P.inbox_need, P.assist,
@@ -43,7 +43,7 @@ int mkh_plan_mlp(size_t n_flags, size_t n_counters, size_t inbox_bytes, int grid
   mkh::Ws ws{n_flags, n_counters, inbox_bytes, grid};
   mkh::MlpPlan P{};
   const long long rows = (long long)world * m_shard;  // the kernels' tiles for this many output rows
-  const mk_tiles::Shape& red = rows <= mk_tiles::kRedSkinnyMaxRows ? mk_tiles::kRedSkinny : mk_tiles::kRedBig;
+  const mk_tiles::Shape& red = rows <= mk_tiles::kRedSkinnyMaxRows ? mk_tiles::kRedSkinny : mk_tiles::kMlpDown;
   const int code = mkh::plan_mlp(ws, o, a_shards, world, rank, m_shard, k, b_up, n_up, b_down, n_out, peers,
                                  a_gathered, h, out, outbox, mk_tiles::kAg.bm, mk_tiles::kAg.bn, red.bm, red.bn,
                                  red.waves(), &P);

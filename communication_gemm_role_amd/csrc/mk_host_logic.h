@@ -156,7 +156,7 @@ struct RedPlan {
 
 inline int plan_reduce(const Ws& ws, const Opts* o, int is_rs, const void* a, const void* b, int m, int n, int k,
                        int world, int rank, const void* const* peers, const void* out, void* const* outbox,
-                       int tile_m, int tile_n, int tile_waves, RedPlan* P) {
+                       int tile_m, int tile_n, int tile_waves, int ring_kib, RedPlan* P) {
   if (!a || !b || !out) return MK_ERR_INVALID_ARG;
   if (world < 1 || world > kMaxWorld || rank < 0 || rank >= world) return MK_ERR_INVALID_ARG;
   if (m <= 0 || n <= 0 || k <= 0) return MK_ERR_INVALID_ARG;
@@ -181,10 +181,10 @@ inline int plan_reduce(const Ws& ws, const Opts* o, int is_rs, const void* a, co
   }
   if ((uint64_t)m * k * 2 >= k4G || (uint64_t)k * n * 2 >= k4G || (uint64_t)m * n * 4 >= k4G) return MK_ERR_UNSUPPORTED;
   P->p_rows = is_rs ? P->m_slice : m;
-  // The copy ring moves at most 8 KiB of a unit per wave and batch: the largest unit that fits the
-  // kernel's wave count and divides the partial.
-  if (tile_waves <= 0) return MK_ERR_INVALID_ARG;
-  const long max_unit = 8192L * tile_waves;
+  // The copy ring moves at most ring_kib KiB of a unit per wave and batch: the largest unit that
+  // fits the kernel's ring and divides the partial.
+  if (tile_waves <= 0 || ring_kib <= 0) return MK_ERR_INVALID_ARG;
+  const long max_unit = 1024L * ring_kib * tile_waves;
   int ur_d = 64, uc_d = 64;
   if (P->p_rows % 128 == 0 && n % 128 == 0 && 128 * 128 * 4 <= max_unit) ur_d = uc_d = 128;
   else if (n % 128 == 0 && 64 * 128 * 4 <= max_unit) uc_d = 128;
@@ -257,8 +257,9 @@ inline int plan_mlp(const Ws& ws, const Opts* o, const void* const* a_shards, in
   memset(&r, 0, sizeof(r));
   r.arrival_mode = MK_ARRIVAL_RESIDENT;  // the peers' partials of the down-projection are resident
   r.timeout_us = o ? o->timeout_us : 0;
+  // (resident: no unit moves, so the ring size only bounds unit sizes nobody asked for)
   code = plan_reduce(ws, &r, 1, h, b_down, world * m_shard, n_out, n_up, world, rank, peers, out, outbox, red_tile_m,
-                     red_tile_n, red_tile_waves, &P->red);
+                     red_tile_n, red_tile_waves, 8, &P->red);
   if (code != MK_OK) return code;
   if (red_tile_m != ag_tile_m || red_tile_waves * 64 != 512) return MK_ERR_UNSUPPORTED;  // one H block per tile row
   if (P->red.n_copy || P->red.n_reduce || P->red.n_compute != ws.grid) return MK_ERR_UNSUPPORTED;

@@ -147,12 +147,12 @@ void red_case(const mkh::Ws& ws, const mkh::Opts* o, int is_rs, int m, int n, in
   ++g_calls;
   const int code = mkh::plan_reduce(ws, o, is_rs, P(0x70000000), P(0x71000000), m, n, k, world, rank,
                                     ptr_kind == 3 ? nullptr : peers, P(0x72000000), ptr_kind == 4 ? nullptr : outbox,
-                                    t.bm, t.bn, t.waves(), &R);
+                                    t.bm, t.bn, t.waves(), t.ring_kib, &R);
   if (code != MK_OK) return;
   ++g_ok;
   CHECK(world >= 1 && world <= mkh::kMaxWorld && rank >= 0 && rank < world);
   CHECK(R.p_rows == (is_rs ? m / world : m) && R.p_rows % R.unit_rows == 0 && n % R.unit_cols == 0);
-  CHECK((long long)R.unit_rows * R.unit_cols * 4 <= 8192LL * t.waves());
+  CHECK((long long)R.unit_rows * R.unit_cols * 4 <= 1024LL * t.ring_kib * t.waves());
   CHECK((long long)R.n_units == (long long)(world - 1) * R.units_per_peer);
   CHECK(R.inbox_need <= ws.inbox_bytes);
   CHECK((size_t)R.n_units + (size_t)R.tiles_m * R.tiles_n <= ws.n_flags);
@@ -174,7 +174,7 @@ void mlp_case(const mkh::Ws& ws, const mkh::Opts* o, int world, int rank, int m_
     outbox[j] = (void*)(0x60000000 + 0x100000 * (uintptr_t)j);
   }
   const long long rows = (long long)world * m_shard;
-  const mk_tiles::Shape& t = rows <= mk_tiles::kRedSkinnyMaxRows ? mk_tiles::kRedSkinny : mk_tiles::kRedBig;
+  const mk_tiles::Shape& t = rows <= mk_tiles::kRedSkinnyMaxRows ? mk_tiles::kRedSkinny : mk_tiles::kMlpDown;
   mkh::MlpPlan M{};
   ++g_calls;
   const int code = mkh::plan_mlp(ws, o, shards, world, rank, m_shard, k, P(0x30000000), n_up, P(0x31000000), n_out,

@@ -179,6 +179,7 @@ int mlp_tile_n();
 int red_tile_m(int m, int n);
 int red_tile_n(int m, int n);
 int red_tile_waves(int m, int n);
+int red_ring_kib(int m, int n);  // KiB per wave and batch of the copy ring (bounds the landing unit)
 int moe_tile_m();
 int moe_tile_n();
 

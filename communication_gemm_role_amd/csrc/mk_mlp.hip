@@ -25,8 +25,10 @@ namespace mk {
 int mlp_tile_m() { return AgTile::BM; }
 int mlp_tile_n() { return AgTile::BN; }
 
-static_assert(AgTile::BM == RedBig::BM, "a 256-row block of H is one tile row of both phases");
-static_assert(AG_THREADS == RedBig::NW * 64, "both phases run eight-wave workgroups");
+static_assert(AgTile::BM == MlpDown::BM, "a 256-row block of H is one tile row of both phases");
+static_assert(AG_THREADS == MlpDown::NW * 64, "both phases run eight-wave workgroups");
+static_assert(MlpDown::BM == RedBig::BM && MlpDown::BN == RedBig::BN && MlpDown::NW == RedBig::NW,
+              "the planner's reduce tile (red_tile_m/n/waves) is also the down-projection's");
 
 __global__ __launch_bounds__(AG_THREADS, 1) void mlp_kernel(MlpParams p) {
   __shared__ __attribute__((aligned(16))) char st0[AgTile::STAGE];
@@ -36,8 +38,8 @@ __global__ __launch_bounds__(AG_THREADS, 1) void mlp_kernel(MlpParams p) {
   __shared__ int s_claim;
   __shared__ int s_ok;
   __shared__ int s_last;
-  static_assert(k_stages<AgTile>() == 2 && k_stages<RedBig>() == 2, "two 64 KiB stage buffers");
-  static_assert(red_stage_bytes<RedBig>() == AgTile::STAGE, "the stage buffers serve both phases");
+  static_assert(k_stages<AgTile>() == 2 && k_stages<MlpDown>() == 2, "two 64 KiB stage buffers");
+  static_assert(red_stage_bytes<MlpDown>() == AgTile::STAGE, "the stage buffers serve both phases");
   const int wg = blockIdx.x;
   // phase 1: AllGather + up-projection
   if (wg < p.ag.n_copy) {
@@ -55,7 +57,7 @@ __global__ __launch_bounds__(AG_THREADS, 1) void mlp_kernel(MlpParams p) {
   trace_mark(p.ag.trace, 6);  // phase 1 done for this workgroup
   // phase 2: down-projection + ReduceScatter on H; every workgroup is a compute workgroup
   if (!status_bad(p.red.status) && wg < p.red.n_compute)
-    red_compute_role<RedBig>(p.red, wg, st0, st1, st2, st2, st2, &s_ok, &s_claim);
+    red_compute_role<MlpDown>(p.red, wg, st0, st1, st2, st2, st2, &s_ok, &s_claim);
   trace_end(p.ag.trace);
   // exit accounting: the last workgroup out re-zeroes every counter the two phases used
   __syncthreads();

@@ -27,14 +27,34 @@
 #pragma once
 #include "mk_internal.h"
 #include "mk_gemm_tile.hpp"
+#include "mk_gemm_tile16.hpp"
 #include "mk_copy_ring.hpp"
 
 namespace mk {
 
-// wide outputs (e.g. 8192 x 4096), eight waves; few output rows (decode-like), four waves
-using RedBig = TileGemmDma<mk_tiles::kRedBig.bm, mk_tiles::kRedBig.bn, mk_tiles::kRedBig.wm, mk_tiles::kRedBig.wn>;
+// wide outputs (e.g. 8192 x 4096): eight waves on the 16 x 16 x 32 core, A two steps ahead in
+// three 32 KiB slots and B in two; few output rows (decode-like): four waves; the MLP block's
+// down-projection: eight waves on the two-stage 32 x 32 x 16 core (its LDS is shared with the
+// up-projection's stages)
+using RedBig = TileGemm16T<mk_tiles::kRedBig.bn>;
+static_assert(RedBig::BM == mk_tiles::kRedBig.bm && RedBig::WM == mk_tiles::kRedBig.wm &&
+                  RedBig::WN == mk_tiles::kRedBig.wn, "kRedBig is the 16 x 16 x 32 core");
 using RedSkinny =
     TileGemmDma<mk_tiles::kRedSkinny.bm, mk_tiles::kRedSkinny.bn, mk_tiles::kRedSkinny.wm, mk_tiles::kRedSkinny.wn>;
+using MlpDown = TileGemmDma<mk_tiles::kMlpDown.bm, mk_tiles::kMlpDown.bn, mk_tiles::kMlpDown.wm, mk_tiles::kMlpDown.wn>;
+
+// Cores with separate A and B slots (mk_gemm_tile16.hpp) against the two-stage TileGemmDma.
+template <class T>
+constexpr bool kCore16 = false;
+template <int BN>
+constexpr bool kCore16<TileGemm16T<BN>> = true;
+
+// KiB per wave and batch of the copy ring, whose two slots are the first two stage buffers:
+// 32 KiB A slots (4 KiB per wave) on the 16 x 16 x 32 core, else 8 KiB per wave.
+template <class T>
+constexpr int red_ring_kib() {
+  return kCore16<T> ? mk_tiles::kRedBig.ring_kib : 8;
+}
 
 inline bool red_skinny(int m, int n) { (void)n; return mk_tiles::red_skinny(m); }
 
@@ -49,8 +69,9 @@ __device__ __forceinline__ const float* peer_src(const RedParams& p, int q) {
 // ------------------------------------------------------------------------------------------
 // copy role (emulated landing of peer partials)
 // ------------------------------------------------------------------------------------------
-// Peer partials land in the inbox through the two-slot LDS ring of mk_copy_ring.hpp: 8 KiB per
-// wave and batch; IPU is a unit's DMA instructions per wave (a 64x64 fp32 unit is 16 KiB).
+// Peer partials land in the inbox through the two-slot LDS ring of mk_copy_ring.hpp:
+// red_ring_kib<T>() KiB per wave and batch; IPU is a unit's DMA instructions per wave (a 64x64
+// fp32 unit is 16 KiB).
 template <class T, int IPU>
 __device__ __forceinline__ void red_copy_dma(const RedParams& p, int cid, char* st0, char* st1) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -90,7 +111,7 @@ __device__ __forceinline__ void red_copy_dma(const RedParams& p, int cid, char* 
     return make_rsrc(p.inbox + (size_t)q * p.p_rows * p.n + elem_of(u), extent);
   };
   const uint64_t t0 = wall_ticks();
-  copy_ring<8, IPU>(n_mine, st0, st1, off, unit_at, src_of, dst_of,
+  copy_ring<red_ring_kib<T>(), IPU>(n_mine, st0, st1, off, unit_at, src_of, dst_of,
                     [&](int u) { flag_store(&p.flags[u], p.epoch); },
                     [&](int i) {  // queue entry i is arrival position cid + i * n_copy
                       if (p.pace_q16) wait_wall_until(t0 + (((uint64_t)(cid + i * p.n_copy) * p.pace_q16) >> 16));
@@ -99,10 +120,15 @@ __device__ __forceinline__ void red_copy_dma(const RedParams& p, int cid, char* 
 
 template <class T>
 __device__ __forceinline__ void red_copy_role(const RedParams& p, int cid, char* st0, char* st1) {
-  // DMA instructions per wave per unit (the planner keeps them within 8)
+  // DMA instructions per wave per unit (the planner keeps them within red_ring_kib<T>())
   const int ipu = (p.unit_rows * p.unit_cols * 4) / (T::NW * 64 * 16);
-  if (ipu >= 8) red_copy_dma<T, 8>(p, cid, st0, st1);
-  else if (ipu == 4) red_copy_dma<T, 4>(p, cid, st0, st1);
+  if constexpr (red_ring_kib<T>() >= 8) {
+    if (ipu >= 8) {
+      red_copy_dma<T, 8>(p, cid, st0, st1);
+      return;
+    }
+  }
+  if (ipu >= 4) red_copy_dma<T, 4>(p, cid, st0, st1);
   else if (ipu == 2) red_copy_dma<T, 2>(p, cid, st0, st1);
   else red_copy_dma<T, 1>(p, cid, st0, st1);
 }
@@ -276,7 +302,8 @@ __device__ __forceinline__ void red_compute_role(const RedParams& p, int slot, c
   const int C = p.n_compute;
   const int rs = ((C & 7) == 0) ? (slot & 7) * (C >> 3) + (slot >> 3) : slot;
   const uint32_t lda_b = (uint32_t)p.k * 2u, ldb_b = (uint32_t)p.n * 2u;
-  g.init(wm, wn, lane, lda_b, ldb_b);
+  if constexpr (kCore16<T>) g.init(wm, wn, wave, lane, lda_b, ldb_b);
+  else g.init(wm, wn, lane, lda_b, ldb_b);
 
   int t = (slot >= 0 && rs < n_tiles) ? rs : -1;
   bool first = slot >= 0, claimed = false;
@@ -303,10 +330,14 @@ __device__ __forceinline__ void red_compute_role(const RedParams& p, int slot, c
     const uint32_t a_tile_bytes = (uint32_t)rows_valid * lda_b;
     const char* b_col = reinterpret_cast<const char*>(p.b + n0);
     const uint32_t b_col_bytes = ((uint32_t)p.k * (uint32_t)p.n - (uint32_t)n0) * 2u;
-    auto load_step = [&](int ks, char* dst) {
-      const uint32_t ca = (uint32_t)ks * 128u, rb = (uint32_t)ks * 64u * ldb_b;
+    auto dma_a = [&](int ks, char* dst) {
+      const uint32_t ca = (uint32_t)ks * 128u;
       g.dma_a(a_tile + ca, a_tile_bytes - ca, lda_b, dst, wave);
-      g.dma_b(b_col + rb, b_col_bytes - rb, ldb_b, dst, wave);
+    };
+    auto dma_b = [&](int ks, char* dst) {
+      const uint32_t rb = (uint32_t)ks * 64u * ldb_b;
+      if constexpr (kCore16<T>) g.dma_b(b_col + rb, b_col_bytes - rb, dst, wave);
+      else g.dma_b(b_col + rb, b_col_bytes - rb, ldb_b, dst, wave);
     };
     int lr0, lr1;
     owned_rows<T>(p, tm, lr0, lr1);
@@ -327,7 +358,22 @@ __device__ __forceinline__ void red_compute_role(const RedParams& p, int slot, c
     }
     g.zero();
     if (first) trace_mark(p.trace, 5);  // operands are resident: ready at once
-    k_loop(g, nk, st0, st1, st2, st3, st4, [](int) {}, load_step, [](int) {});
+    if constexpr (kCore16<T>) {
+      // st0..st2: A slots, st3, st4: B slots
+      auto prologue = [&](char* pa0, char* pb0, char* pa1) {
+        dma_a(0, pa0);
+        dma_b(0, pb0);
+        if (nk > 1) dma_a(1, pa1);
+      };
+      auto none = [](int, auto) {};
+      k_loop_a3b2(g, nk, st0, st1, st2, st3, st4, prologue, dma_a, dma_b, none, none, none, [] { return true; });
+    } else {
+      auto load_step = [&](int ks, char* dst) {
+        dma_a(ks, dst);
+        dma_b(ks, dst);
+      };
+      k_loop(g, nk, st0, st1, st2, st3, st4, [](int) {}, load_step, [](int) {});
+    }
     if (first) trace_mark(p.trace, 6);  // the first tile's K loop is done; its epilogue follows
     first = false;
 
@@ -352,12 +398,12 @@ __device__ __forceinline__ void red_compute_role(const RedParams& p, int slot, c
       if (!*s_ok) return;
     }
     const int own0 = p.is_rs ? p.rank * p.m_slice : 0;
-    // A 32-row slab lies inside one owner's slice (slices and valid row counts are multiples of
-    // 64 rows) and inside or outside the valid rows as a whole.  Every load a slab's reduction
+    // A slab (16 or 32 rows) lies inside one owner's slice (slices and valid row counts are
+    // multiples of 64 rows) and inside or outside the valid rows as a whole.  Every load a slab's reduction
     // needs is issued before any of its adds, so the loads overlap instead of each waiting for
     // the one before.
     constexpr int Q = T::SLAB_Q;
-    g.epilogue_slab(st0, st1, wm, wn, lane, wave, [&](int srow, f32x4(&v)[Q], const int(&r)[Q], const int(&c)[Q]) {
+    auto store_slab = [&](int srow, f32x4(&v)[Q], const int(&r)[Q], const int(&c)[Q]) {
       if (srow >= rows_valid) return;
       if (p.is_rs) {
         const int owner = (m0 + srow) / p.m_slice;
@@ -410,13 +456,15 @@ __device__ __forceinline__ void red_compute_role(const RedParams& p, int slot, c
           }
         }
       }
-    });
+    };
+    if constexpr (kCore16<T>) g.epilogue_slab(T::epi_buf(wave, st0, st1, st2), wm, wn, lane, store_slab);
+    else g.epilogue_slab(st0, st1, wm, wn, lane, wave, store_slab);
     __syncthreads();  // the next tile's prologue reuses the LDS
     t = -1;
   }
 }
 
-// The first two stage buffers double as the copy ring's slots: 8 KiB per wave.
+// Two-stage cores: the first two stage buffers double as the copy ring's slots, 8 KiB per wave.
 template <class T>
 constexpr int red_stage_bytes() {
   return T::STAGE > T::NW * 8192 ? T::STAGE : T::NW * 8192;

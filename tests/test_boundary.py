@@ -170,7 +170,7 @@ def test_plan_ag_small_units(hostlib):
     assert code == MK_OK and (p["unit_rows"], p["unit_cols"], p["n_order"]) == (64, 64, 12)
 
 
-def red(hostlib, is_rs=1, m=8192, n=4096, k=1792, world=8, rank=0, opts=None, tile=(256, 256, 8), drop_peer=None,
+def red(hostlib, is_rs=1, m=8192, n=4096, k=1792, world=8, rank=0, opts=None, tile=(256, 256, 8, 4), drop_peer=None,
         a=0x10000, inbox=INBOX):
     peers = (ctypes.c_void_p * world)()
     ob = (ctypes.c_void_p * world)()
@@ -181,7 +181,7 @@ def red(hostlib, is_rs=1, m=8192, n=4096, k=1792, world=8, rank=0, opts=None, ti
     out = (ctypes.c_longlong * 24)()
     code = hostlib.mkh_plan_reduce(ctypes.c_size_t(NF), ctypes.c_size_t(NC), ctypes.c_size_t(inbox), GRID,
                                    ctypes.byref(opts) if opts else None, is_rs, P(a), P(0x20000), m, n, k, world,
-                                   rank, peers, P(0x30000), ob, tile[0], tile[1], tile[2], out)
+                                   rank, peers, P(0x30000), ob, tile[0], tile[1], tile[2], tile[3], out)
     keys = ["m_slice", "p_rows", "unit_rows", "unit_cols", "n_ucols", "units_per_peer", "n_units", "emulated",
             "n_order", "drop_pos", "n_copy", "n_reduce", "n_compute", "tiles_m", "tiles_n", "own_tile_begin",
             "own_tile_end", "inbox_need", "assist", "pace_q16"]
@@ -191,18 +191,20 @@ def red(hostlib, is_rs=1, m=8192, n=4096, k=1792, world=8, rank=0, opts=None, ti
 def test_plan_rs_and_ar(hostlib):
     code, p = red(hostlib)
     assert code == MK_OK
-    assert (p["m_slice"], p["units_per_peer"], p["n_units"]) == (1024, 8 * 32, 7 * 256)
+    # the wide tile's copy ring moves 4 KiB per wave and batch (32 KiB slots): 64x128 fp32 units
+    assert (p["unit_rows"], p["unit_cols"]) == (64, 128)
+    assert (p["m_slice"], p["units_per_peer"], p["n_units"]) == (1024, 16 * 32, 7 * 512)
     assert (p["own_tile_begin"], p["own_tile_end"], p["inbox_need"]) == (0, 4, 7 * 1024 * 4096 * 4)
     code, p = red(hostlib, rank=3)
     assert (p["own_tile_begin"], p["own_tile_end"]) == (12, 16)
     # the skinny AR tile has 4 waves: 8 KiB per wave caps a unit at 32 KiB, so 64x128 by default
-    code, p = red(hostlib, is_rs=0, m=256, n=8192, k=1024, tile=(128, 64, 4))
+    code, p = red(hostlib, is_rs=0, m=256, n=8192, k=1024, tile=(128, 64, 4, 8))
     assert code == MK_OK and p["p_rows"] == 256 and (p["unit_rows"], p["unit_cols"]) == (64, 128)
     assert p["n_units"] == 7 * 4 * 64
     assert (p["own_tile_begin"], p["own_tile_end"]) == (0, 2)
-    assert red(hostlib, is_rs=0, m=256, n=8192, k=1024, tile=(128, 64, 4),
+    assert red(hostlib, is_rs=0, m=256, n=8192, k=1024, tile=(128, 64, 4, 8),
                opts=Opts(arrival_unit_rows=128, arrival_unit_cols=128))[0] == UNSUP
-    assert red(hostlib, tile=(256, 256, 0))[0] == INVALID
+    assert red(hostlib, tile=(256, 256, 0, 4))[0] == INVALID
     assert red(hostlib, world=7)[0] == INVALID  # rows not divisible by world
     assert red(hostlib, m=8 * 96)[0] == UNSUP  # slice 96 rows
     assert red(hostlib, drop_peer=2)[0] == INVALID  # missing peer partial
@@ -223,7 +225,7 @@ def test_plan_rs_presum_assist(hostlib):
     assert red(hostlib)[1]["assist"] == 1
     assert red(hostlib, opts=Opts(arrival_mode=RESIDENT))[1]["assist"] == 1
     assert red(hostlib, opts=Opts(n_reduce_wg=16))[1]["assist"] == 0
-    assert red(hostlib, is_rs=0, m=256, n=8192, k=1024, tile=(128, 64, 4))[1]["assist"] == 0
+    assert red(hostlib, is_rs=0, m=256, n=8192, k=1024, tile=(128, 64, 4, 8))[1]["assist"] == 0
     assert red(hostlib, world=1)[1]["assist"] == 0
 
 
@@ -316,7 +318,7 @@ def test_plan_link_rate_pacing(hostlib):
     assert ag(hostlib, opts=Opts(arrival_gbps=1.0, timeout_us=100000))[0] == INVALID
     assert ag(hostlib, opts=Opts(arrival_gbps=1.0))[0] == MK_OK
     code, p = red(hostlib, opts=Opts(arrival_gbps=1071.0))
-    assert code == MK_OK and p["pace_q16"] == round(128 * 128 * 4 / 1071e9 * 1e8 * 65536)
+    assert code == MK_OK and p["pace_q16"] == round(64 * 128 * 4 / 1071e9 * 1e8 * 65536)
     assert red(hostlib, opts=Opts(arrival_mode=RESIDENT, arrival_gbps=1071.0))[1]["pace_q16"] == 0
     assert red(hostlib, opts=Opts(arrival_gbps=-5.0))[0] == INVALID
 

@@ -48,7 +48,7 @@ def test_arrival_orders_are_permutations_of_peer_units():
     m = wl.moe_arrival_order(wl.MOE_FULL)
     assert sorted(m.tolist()) == list(range(512))
     r = wl.reduce_arrival_order(wl.RS_DOWN, "rs")
-    assert sorted(r.tolist()) == list(range(7 * 8 * 32))
+    assert sorted(r.tolist()) == list(range(7 * 16 * 32))  # 7 peers x (1024 / 64) unit rows x (4096 / 128) unit cols
 
 
 def test_tolerance_headroom_on_tiny_ag():

@@ -199,9 +199,11 @@ class RedShape:
         return 2.0 * self.m * self.n * self.k
 
 
-RS_DOWN = RedShape(m=8192, n=4096, k=1792, world=8, sigma_a=1.0, sigma_b=0.02, sigma_q=1.0, cfg=CFG_RS)
-# 64x128 fp32 landing units (32 KiB): the decode-like AR uses a four-wave tile, whose copy ring
-# moves at most 8 KiB of a unit per wave
+# 64x128 fp32 landing units (32 KiB): a batch of the copy ring holds whole units, and the ring moves
+# 4 KiB per wave on the eight-wave wide tile (32 KiB slots) and 8 KiB per wave on the decode-like
+# AR's four-wave tile
+RS_DOWN = RedShape(m=8192, n=4096, k=1792, world=8, sigma_a=1.0, sigma_b=0.02, sigma_q=1.0, unit_rows=64,
+                   unit_cols=128, cfg=CFG_RS)
 AR_DECODE = RedShape(m=256, n=8192, k=1024, world=8, sigma_a=1.0, sigma_b=0.02, sigma_q=1.0, unit_rows=64,
                      unit_cols=128, cfg=CFG_AR)
 # small versions (same structure, a few tiles and a ragged count of units) for parity at CPU speed
