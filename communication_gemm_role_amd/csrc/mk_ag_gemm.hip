@@ -13,11 +13,7 @@ int ag_tile_m() { return TileGemm16::BM; }
 int ag_tile_n() { return TileGemm16::BN; }
 
 // Roles: workgroups [0, n_copy) copy (land peer units in the caller's order), then compute; the rest
-// compute from the start.  Static tiles are XCD-aware: workgroup w runs on XCD w % 8, and the k-th
-// of n workgroups taking static tiles owns logical tile (k % 8) * (n / 8) + k / 8, so an XCD's
-// tiles are consecutive (whole tile rows, sharing their A rows in its L2).  When the compute
-// workgroups alone can hold every tile they do; otherwise every workgroup owns one (copy
-// workgroups start theirs after copying) and tiles past the grid are claimed from a counter.
+// compute from the start (static tiles: ag_static_tile).
 __global__ __launch_bounds__(AG_THREADS, 1) void ag_gemm_kernel(AgParams p) {
   using G = TileGemm16;
   __shared__ __attribute__((aligned(16))) char a0[G::SLOT_A];
@@ -28,11 +24,8 @@ __global__ __launch_bounds__(AG_THREADS, 1) void ag_gemm_kernel(AgParams p) {
   __shared__ int s_sched[AG_SCHED_WORDS];
   __shared__ int s_claim;
   __shared__ __attribute__((aligned(16))) uint32_t s_poll[4 * 64];
-  const int wg = blockIdx.x, grid = gridDim.x, n_tiles = p.tiles_m * p.tiles_n;
-  const bool compute_only = n_tiles <= p.n_compute;
-  const int k = compute_only ? wg - p.n_copy : wg, n = compute_only ? p.n_compute : grid;
-  const int rs = k < 0 ? -1 : (n & 7) == 0 ? (k & 7) * (n >> 3) + (k >> 3) : k;
-  const int t_static = rs < n_tiles ? rs : -1;
+  const int wg = blockIdx.x;
+  const int t_static = ag_static_tile(p, wg, gridDim.x);
   if (wg < p.n_copy) {
     trace_begin(p.trace, ROLE_COPY);
     ag_copy_role<32>(p, wg, a0, a1);
@@ -42,7 +35,7 @@ __global__ __launch_bounds__(AG_THREADS, 1) void ag_gemm_kernel(AgParams p) {
     trace_begin(p.trace, ROLE_COMPUTE);
   }
   const bool is_copy = wg < p.n_copy;
-  ag_compute_role16(p, t_static, !is_copy, is_copy, a0, a1, a2, b0, b1, s_sched, &s_claim, s_poll);
+  ag_compute_role16<0>(p, t_static, !is_copy, is_copy, a0, a1, a2, b0, b1, s_sched, &s_claim, s_poll);
   trace_end(p.trace);
   // exit accounting: the last workgroup out re-zeroes the tile counter for the next call (every
   // workgroup's last claim returned before it counts its exit)

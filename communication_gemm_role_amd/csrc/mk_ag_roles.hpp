@@ -15,13 +15,15 @@
 //                                   unit's ready flag.
 //                                   Copy workgroups wait on nothing while copying but the clock
 //                                   (link-rate pacing, bounded by the host), so every unit lands.
-//   workgroups [n_copy, grid)       compute: 256 x 256 output tiles of C, one static tile per
-//                                   workgroup, then (like copy workgroups once they have copied)
-//                                   tiles left over past n_compute.  In emulated mode the
-//                                   K loop visits K-units (unit_cols columns of K) ready-first:
-//                                   wave 0 polls the flags of the tile's unit rows and picks the
-//                                   lowest-numbered K-unit that has fully landed, one unit ahead
-//                                   of the prefetch, so landed data is consumed immediately.
+//   workgroups [n_copy, grid)       compute: 256 x 224 output tiles of C (one static tile per
+//                                   workgroup, XCD-aware), then (like copy workgroups once they
+//                                   have copied) tiles left over past the grid.  In emulated mode
+//                                   a tile whose units have not all landed runs its K loop over
+//                                   K-units (unit_cols columns of K) ready-first: wave 0 polls the
+//                                   flags of the tile's unit rows and schedules the lowest-numbered
+//                                   K-unit that has fully landed, ahead of the prefetch, so landed
+//                                   data is consumed as it arrives; a copy workgroup waits until its
+//                                   tile's units have landed and runs the loop in K order.
 // A compute workgroup only ever waits on copy workgroups, which have lower ids and are therefore
 // dispatched first; every wait is bounded by the watchdog.
 #pragma once
@@ -32,9 +34,7 @@
 
 namespace mk {
 
-// 256 x 256 output tile, eight waves of 128 x 64: one k-step moves 64 KiB of operands for 8.4 MFLOP.
-using AgTile = TileGemmDma<mk_tiles::kAg.bm, mk_tiles::kAg.bn, mk_tiles::kAg.wm, mk_tiles::kAg.wn>;
-constexpr int AG_THREADS = AgTile::NW * 64;
+constexpr int AG_THREADS = TileGemm16::NW * 64;
 
 // ------------------------------------------------------------------------------------------
 // copy role
@@ -167,31 +167,6 @@ __device__ __forceinline__ int ag_pick(const AgParams& p, int ur0, int n_ur, uin
   return u;
 }
 
-// Wave 0: flags of the tile's non-local unit rows for K-unit `lane`, loaded without waiting (the
-// values are consumed after the step's MFMAs, so the load latency hides behind them).
-struct AgPoll {
-  uint32_t f[4];
-};
-__device__ __forceinline__ void ag_poll_issue(const AgParams& p, int ur0, int n_ur, int lane, AgPoll& pl) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int ur = ur0 + q;
-    pl.f[q] = (q < n_ur && !ag_row_local(p, ur) && lane < p.n_ucols) ? flag_load(&p.flags[ur * p.n_ucols + lane])
-                                                                       : p.epoch;
-  }
-}
-// Wave 0: as ag_poll_issue, through one buffer window over the tile's flag rows (one per-lane
-// offset, the row in the scalar offset: four fewer 64-bit addresses held across the MFMAs).  Lanes
-// past n_ucols read the next row's flags, which the ready mask ignores.
-__device__ __forceinline__ void ag_poll_issue_rows(const AgParams& p, int ur0, int n_ur, int lane, AgPoll& pl) {
-  const auto rs = make_rsrc(p.flags + (size_t)ur0 * p.n_ucols, (uint32_t)(n_ur * p.n_ucols) * 4u);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)lane * 4u, (uint32_t)(q * p.n_ucols) * 4u, CP_SC1);
-    pl.f[q] = (q < n_ur && !ag_row_local(p, ur0 + q)) ? v : p.epoch;
-  }
-}
-
 // Wave 0: the flags of the tile's unit rows [ur0, ur0 + n_ur) (at most 4) for K-unit `lane`,
 // requested straight into LDS (s_poll[q][lane]), so no register is held while the loads are in
 // flight across a step's MFMAs.  Lanes past n_ucols read the next row's flags, which the ready
@@ -239,32 +214,6 @@ __device__ __forceinline__ uint64_t ag_repoll_until_new(const AgParams& p, int u
   }
 }
 
-// Wave 0: landed-K-unit mask of an issued poll (uniform).
-__device__ __forceinline__ uint64_t ag_ready_polled(const AgParams& p, int lane, const AgPoll& pl) {
-  uint64_t ready = (p.n_ucols >= 64) ? ~0ull : ((1ull << p.n_ucols) - 1ull);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) ready &= __ballot(lane >= p.n_ucols || pl.f[q] == p.epoch);
-  return uniform64(ready);
-}
-
-// Wave 0: pick from an issued poll (falling back to the blocking ag_pick when nothing is ready).
-__device__ __forceinline__ int ag_pick_polled(const AgParams& p, int ur0, int n_ur, uint64_t& done, int lane,
-                                              const AgPoll& pl) {
-  const uint64_t all = (p.n_ucols >= 64) ? ~0ull : ((1ull << p.n_ucols) - 1ull);
-  uint64_t ready = all;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) ready &= __ballot(lane >= p.n_ucols || pl.f[q] == p.epoch);
-  const uint64_t cand = ready & ~done;
-  if (!cand) return ag_pick(p, ur0, n_ur, done, lane);
-  const int u = __builtin_ctzll(cand);
-  done = uniform64(done | (1ull << u));
-  return u;
-}
-
-// Compute role.  Compute workgroup `slot` first runs its static tile (XCD-aware order); tiles from
-// n_compute on are left over and claimed from a shared counter by every workgroup that has
-// finished its own work: compute workgroups after their static tile, copy workgroups (slot -1)
-// after copying.
 // The MLP block's activation: gelu(x) = x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2)), in fp32.
 __device__ __forceinline__ float gelu_f32(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
 
@@ -273,134 +222,6 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
   const uint32_t u = __builtin_bit_cast(uint32_t, f);
   if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-
-// EPI 0: fp32 C tile.  EPI 1 (MLP up-projection): H = bf16(gelu(acc)), write-through (the
-// down-projection reads it from other XCDs), then h_ready[tile row] += 1 once every wave's stores
-// of the tile have completed.
-template <int EPI = 0>
-__device__ __forceinline__ void ag_compute_role(const AgParams& p, int slot, char* st0, char* st1, char* st2,
-                                                int* s_sched, int* s_claim) {
-  AgTile g;
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / AgTile::WN, wn = wave % AgTile::WN;
-  const int n_tiles = p.tiles_m * p.tiles_n;
-  const int nk = p.k >> 6;
-  const int spu = p.unit_cols >> 6;  // k-steps per K-unit
-  const int n_ku = p.n_ucols;
-  const int C = p.n_compute;
-  // XCD-aware slot order: workgroup w runs on XCD w % 8; consecutive logical tiles (which share
-  // A row blocks) go to one XCD so its L2 keeps reusing them.
-  const int rs = ((C & 7) == 0) ? (slot & 7) * (C >> 3) + (slot >> 3) : slot;
-  const uint32_t lda_b = (uint32_t)p.k * 2u, ldb_b = (uint32_t)p.n * 2u;
-  g.init(wm, wn, lane, lda_b, ldb_b);
-  // K-units decided before the loop.  Step q+PD is prefetched at the start of step q, so the unit
-  // that starts at step s must be known by the end of step s-PD-1: a decision taken at the end of
-  // step q (after its MFMAs) names the unit starting at step q+1+PD.  The prologue decides the
-  // units that start at steps 0 .. PD, i.e. ceil((PD+1)/spu) of them.
-  constexpr int PD = k_stages<AgTile>() - 1;  // prefetch distance of the K loop
-  const int n_pre = min(n_ku, (PD + spu) / spu);
-
-  int t = (slot >= 0 && rs < n_tiles) ? rs : -1;
-  bool first = slot >= 0;
-  while (true) {
-    if (t < 0) {
-      if (tid == 0) *s_claim = C + (int)atomic_add_agent(p.counters + CTR_AG_TILE, 1u);
-      __syncthreads();
-      t = *s_claim;  // rewritten only after the next tile's barriers
-      if (t >= n_tiles) break;
-    }
-    const int tm = t / p.tiles_n, tn = t - tm * p.tiles_n;
-    const int m0 = tm * AgTile::BM, n0 = tn * AgTile::BN;
-    const int rows_valid = min(AgTile::BM, p.m - m0), cols_valid = min(AgTile::BN, p.n - n0);
-    const int ur0 = m0 / p.unit_rows, n_ur = rows_valid / p.unit_rows;
-    // Operand windows of the k-step: A rows of the tile from the step's first column, B rows of
-    // the step from column n0.  Only scalar values change from step to step.
-    const char* a_tile = reinterpret_cast<const char*>(p.ag + (size_t)m0 * p.k);
-    const uint32_t a_tile_bytes = (uint32_t)rows_valid * lda_b;
-    const char* b_col = reinterpret_cast<const char*>(p.b + n0);
-    const uint32_t b_col_bytes = ((uint32_t)p.k * (uint32_t)p.n - (uint32_t)n0) * 2u;
-    auto load_step = [&](int ks, char* dst) {
-      const uint32_t ca = (uint32_t)ks * 128u;         // byte column of the step in A
-      const uint32_t rb = (uint32_t)ks * 64u * ldb_b;  // byte row of the step in B
-      g.dma_a(a_tile + ca, a_tile_bytes - ca, lda_b, dst, wave);
-      g.dma_b(b_col + rb, b_col_bytes - rb, ldb_b, dst, wave);
-    };
-
-    g.zero();
-    uint64_t done = 0;  // wave 0: K-units scheduled for this tile
-    if (p.emulated) {
-      if (wave == 0) {
-        done = 0;
-        for (int j = 0; j < n_pre; ++j) {
-          const int u = ag_pick(p, ur0, n_ur, done, lane);
-          if (lane == 0) s_sched[j] = u;
-          if (u < 0) break;
-        }
-      }
-      __syncthreads();
-      bool bad = false;
-      for (int j = 0; j < n_pre; ++j) bad |= __builtin_amdgcn_readfirstlane(s_sched[j]) < 0;
-      if (bad) return;  // before any MFMA of this tile
-    }
-    if (first) trace_mark(p.trace, 5);
-    first = false;
-    // A failed wait (watchdog or another workgroup's fault) inside the K loop does not leave the
-    // loop: the remaining steps drain on K-unit 0 (in bounds, result discarded) and the tile's
-    // stores are skipped.  Keeping the loop single-exit keeps the accumulators in AGPRs.
-    bool aborted = false;
-    AgPoll pl;
-    bool polled = false;
-    auto unit_of = [&](int q) -> int {  // K-unit of step q
-      const int j = q / spu;
-      if (!p.emulated) return j;
-      const int u = __builtin_amdgcn_readfirstlane(s_sched[j]);
-      aborted |= u < 0;
-      return u < 0 ? 0 : u;
-    };
-    // the unit decided at the end of step q: the one that starts at step q+1+PD, or -1
-    auto decided_at = [&](int q) -> int {
-      const int s = q + 1 + PD;
-      if (!p.emulated || s >= nk || s % spu) return -1;
-      const int jn = s / spu;
-      return (jn >= n_pre && jn < n_ku) ? jn : -1;
-    };
-    auto before_load = [&](int q) {
-      polled = decided_at(q) >= 0 && wave == 0;
-      if (polled) ag_poll_issue(p, ur0, n_ur, lane, pl);
-    };
-    auto load = [&](int q, char* dst) { load_step(unit_of(q) * spu + q % spu, dst); };
-    auto before_wait = [&](int q) {
-      if (polled) {
-        const int u = ag_pick_polled(p, ur0, n_ur, done, lane, pl);
-        if (lane == 0) s_sched[decided_at(q)] = u;
-      }
-    };
-    k_loop(g, nk, st0, st1, st2, st2, st2, before_load, load, before_wait);
-
-    // epilogue: the tile staged through LDS into row-contiguous 16-byte stores
-    if constexpr (EPI == 0) {
-      g.epilogue(st0, st1, wm, wn, lane, wave, [&](int row, int col, f32x4 v) {
-        if (!aborted && row < rows_valid && col < cols_valid)  // C is written once: streaming stores
-          __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p.c + (size_t)(m0 + row) * p.n + (n0 + col)));
-      });
-      __syncthreads();  // the next tile's prologue reuses the LDS
-    } else {
-      const auto h_rs = make_rsrc(p.h, (uint32_t)p.m * (uint32_t)p.n * 2u);
-      g.epilogue(st0, st1, wm, wn, lane, wave, [&](int row, int col, f32x4 v) {
-        if (!aborted && row < rows_valid && col < cols_valid) {
-          const uint32_t b0 = bf16_rne(gelu_f32(v[0])), b1 = bf16_rne(gelu_f32(v[1]));
-          const uint32_t b2 = bf16_rne(gelu_f32(v[2])), b3 = bf16_rne(gelu_f32(v[3]));
-          bstore8_sc1(h_rs, (uint32_t)((m0 + row) * p.n + (n0 + col)) * 2u, u32x2{b0 | (b1 << 16), b2 | (b3 << 16)});
-        }
-      });
-      wait_mem();       // this tile's H stores have completed ...
-      __syncthreads();  // ... in every wave (and the next tile's prologue reuses the LDS)
-      if (!aborted && tid == 0) atomic_add_agent(p.h_ready + tm, 1u);
-    }
-    if (aborted) break;
-    t = -1;
-  }
 }
 
 // s_sched: entries 0 .. n_ucols - 1 name the K-unit each unit slot of the tile's K loop takes;
@@ -418,7 +239,10 @@ constexpr int AG_SCHED_WORDS = AG_SCHED_ALL_IN + 1;
 // schedules the rest in ascending order and stops polling.  Without EMU every operand of the tile
 // is present and the K loop runs in K order with no hooks.  Returns false if a wait failed (the
 // tile's stores were skipped).
-template <bool EMU>
+// EPI 0: fp32 C tile.  EPI 1 (the MLP block's up-projection): H = bf16(gelu(acc)), write-through
+// (the down-projection reads it from other XCDs), then h_ready[tile row] += 1 once every wave's
+// stores of the tile have completed.
+template <bool EMU, int EPI>
 __device__ __forceinline__ bool ag_tile16(const AgParams& p, int t, char* a0, char* a1, char* a2, char* b0, char* b1,
                                           int* s_sched, uint32_t* s_poll) {
   using G = TileGemm16;
@@ -550,11 +374,25 @@ __device__ __forceinline__ bool ag_tile16(const AgParams& p, int t, char* a0, ch
     // epilogue: the tile staged through the A slots into row-contiguous 16-byte stores; C is
     // written once and read by no one here: streaming stores
     float* wl = G::epi_buf(wave, a0, a1, a2);
-    g.epilogue(wl, wm, wn, lane, [&](int row, int col, f32x4 v) {
-      if (!aborted && row < rows_valid && col < cols_valid)
-        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p.c + (size_t)(m0 + row) * p.n + (n0 + col)));
-    });
-    __syncthreads();  // the next tile's prologue reuses the LDS
+    if constexpr (EPI == 0) {
+      g.epilogue(wl, wm, wn, lane, [&](int row, int col, f32x4 v) {
+        if (!aborted && row < rows_valid && col < cols_valid)
+          __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p.c + (size_t)(m0 + row) * p.n + (n0 + col)));
+      });
+      __syncthreads();  // the next tile's prologue reuses the LDS
+    } else {
+      const auto h_rs = make_rsrc(p.h, (uint32_t)p.m * (uint32_t)p.n * 2u);
+      g.epilogue(wl, wm, wn, lane, [&](int row, int col, f32x4 v) {
+        if (!aborted && row < rows_valid && col < cols_valid) {
+          const uint32_t h0 = bf16_rne(gelu_f32(v[0])), h1 = bf16_rne(gelu_f32(v[1]));
+          const uint32_t h2 = bf16_rne(gelu_f32(v[2])), h3 = bf16_rne(gelu_f32(v[3]));
+          bstore8_sc1(h_rs, (uint32_t)((m0 + row) * p.n + (n0 + col)) * 2u, u32x2{h0 | (h1 << 16), h2 | (h3 << 16)});
+        }
+      });
+      wait_mem();       // this tile's H stores have completed ...
+      __syncthreads();  // ... in every wave (and the next tile's prologue reuses the LDS)
+      if (!aborted && threadIdx.x == 0) atomic_add_agent(p.h_ready + m0 / G::BM, 1u);  // (tm: not kept live across the loop)
+    }
     return !aborted;
   }
 }
@@ -577,6 +415,21 @@ __device__ __forceinline__ bool ag_wait_rows(const AgParams& p, int ur0, int n_u
   return true;
 }
 
+// Static tile of workgroup wg (or -1).  Static tiles are XCD-aware: workgroup w runs on XCD w % 8,
+// and the k-th of n workgroups taking static tiles owns logical tile (k % 8) * (n / 8) + k / 8, so
+// an XCD's tiles are consecutive (whole tile rows, sharing their A rows in its L2).  When the
+// compute workgroups alone can hold every tile they do (k = wg - n_copy, n = n_compute);
+// otherwise every workgroup of the grid owns one (copy workgroups start theirs after copying)
+// and tiles past the grid are claimed from a counter.
+__device__ __forceinline__ int ag_static_tile(const AgParams& p, int wg, int grid) {
+  const int n_tiles = p.tiles_m * p.tiles_n;
+  const bool compute_only = n_tiles <= p.n_compute;
+  const int k = compute_only ? wg - p.n_copy : wg, n = compute_only ? p.n_compute : grid;
+  if (k < 0 || k >= n) return -1;  // not one of the n (a second owner of a tile would count it twice)
+  const int rs = (n & 7) == 0 ? (k & 7) * (n >> 3) + (k >> 3) : k;
+  return rs < n_tiles ? rs : -1;
+}
+
 // Compute role of the AllGather + GEMM kernel.  The workgroup first runs tile t_static (-1: none),
 // then tiles left over past the grid, claimed from a shared counter.  With emulated arrival, wave 0
 // looks at the flags of a tile's unit rows first: when every unit has landed the tile runs the K
@@ -585,7 +438,9 @@ __device__ __forceinline__ bool ag_wait_rows(const AgParams& p, int ur0, int n_u
 // the landing, and the loop without hooks is faster than the ready-first one by more than the
 // wait -- and the others run the ready-first loop, consuming each K-unit as soon as it has landed.
 // mark_ready: record the first tile's operands-ready time in trace slot 5 (compute workgroups; a
-// copy workgroup's slot 5 holds the end of its copy).
+// copy workgroup's slot 5 holds the end of its copy).  READY_FIRST = false leaves the ready-first
+// loop out of the build (the caller sets wait_landed everywhere).
+template <int EPI, bool READY_FIRST = true>
 __device__ __forceinline__ void ag_compute_role16(const AgParams& p, int t_static, bool mark_ready, bool wait_landed,
                                                   char* a0, char* a1, char* a2, char* b0, char* b1, int* s_sched,
                                                   int* s_claim, uint32_t* s_poll) {
@@ -619,8 +474,12 @@ __device__ __forceinline__ void ag_compute_role16(const AgParams& p, int t_stati
     }
     if (first) trace_mark(p.trace, 5);
     first = false;
-    const bool ok = emu ? ag_tile16<true>(p, t, a0, a1, a2, b0, b1, s_sched, s_poll)
-                        : ag_tile16<false>(p, t, a0, a1, a2, b0, b1, s_sched, s_poll);
+    bool ok;
+    if constexpr (READY_FIRST)
+      ok = emu ? ag_tile16<true, EPI>(p, t, a0, a1, a2, b0, b1, s_sched, s_poll)
+               : ag_tile16<false, EPI>(p, t, a0, a1, a2, b0, b1, s_sched, s_poll);
+    else  // wait_landed is set: a tile never starts before its units have landed
+      ok = ag_tile16<false, EPI>(p, t, a0, a1, a2, b0, b1, s_sched, s_poll);
     if (!ok) break;
     t = -1;
   }

@@ -43,9 +43,9 @@ int mkh_plan_mlp(size_t n_flags, size_t n_counters, size_t inbox_bytes, int grid
   mkh::Ws ws{n_flags, n_counters, inbox_bytes, grid};
   mkh::MlpPlan P{};
   const long long rows = (long long)world * m_shard;  // the kernels' tiles for this many output rows
-  const mk_tiles::Shape& red = rows <= mk_tiles::kRedSkinnyMaxRows ? mk_tiles::kRedSkinny : mk_tiles::kMlpDown;
+  const mk_tiles::Shape& red = rows <= mk_tiles::kRedSkinnyMaxRows ? mk_tiles::kRedSkinny : mk_tiles::kRedBig;
   const int code = mkh::plan_mlp(ws, o, a_shards, world, rank, m_shard, k, b_up, n_up, b_down, n_out, peers,
-                                 a_gathered, h, out, outbox, mk_tiles::kAg.bm, mk_tiles::kAg.bn, red.bm, red.bn,
+                                 a_gathered, h, out, outbox, mk_tiles::kAg16.bm, mk_tiles::kAg16.bn, red.bm, red.bn,
                                  red.waves(), &P);
   const long long v[] = {P.ag.n_copy, P.ag.n_compute, P.ag.tiles_m, P.ag.tiles_n, P.red.n_compute, P.red.tiles_m,
                          P.red.tiles_n, P.red.own_tile_begin, P.red.own_tile_end, P.red.assist};

@@ -174,12 +174,12 @@ void mlp_case(const mkh::Ws& ws, const mkh::Opts* o, int world, int rank, int m_
     outbox[j] = (void*)(0x60000000 + 0x100000 * (uintptr_t)j);
   }
   const long long rows = (long long)world * m_shard;
-  const mk_tiles::Shape& t = rows <= mk_tiles::kRedSkinnyMaxRows ? mk_tiles::kRedSkinny : mk_tiles::kMlpDown;
+  const mk_tiles::Shape& t = rows <= mk_tiles::kRedSkinnyMaxRows ? mk_tiles::kRedSkinny : mk_tiles::kRedBig;
   mkh::MlpPlan M{};
   ++g_calls;
   const int code = mkh::plan_mlp(ws, o, shards, world, rank, m_shard, k, P(0x30000000), n_up, P(0x31000000), n_out,
-                                 peers, P(0x10000000), P(0x11000000), P(0x12000000), outbox, mk_tiles::kAg.bm,
-                                 mk_tiles::kAg.bn, t.bm, t.bn, t.waves(), &M);
+                                 peers, P(0x10000000), P(0x11000000), P(0x12000000), outbox, mk_tiles::kAg16.bm,
+                                 mk_tiles::kAg16.bn, t.bm, t.bn, t.waves(), &M);
   if (code != MK_OK) return;
   ++g_ok;
   CHECK(M.ag.n_copy + M.ag.n_compute <= ws.grid && M.red.n_compute == ws.grid);

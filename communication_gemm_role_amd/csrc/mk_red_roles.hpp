@@ -32,16 +32,14 @@
 
 namespace mk {
 
-// wide outputs (e.g. 8192 x 4096): eight waves on the 16 x 16 x 32 core, A two steps ahead in
-// three 32 KiB slots and B in two; few output rows (decode-like): four waves; the MLP block's
-// down-projection: eight waves on the two-stage 32 x 32 x 16 core (its LDS is shared with the
-// up-projection's stages)
+// wide outputs (e.g. 8192 x 4096, also the MLP block's down-projection): eight waves on the
+// 16 x 16 x 32 core, A two steps ahead in three 32 KiB slots and B in two; few output rows
+// (decode-like): four waves on the 32 x 32 x 16 core
 using RedBig = TileGemm16T<mk_tiles::kRedBig.bn>;
 static_assert(RedBig::BM == mk_tiles::kRedBig.bm && RedBig::WM == mk_tiles::kRedBig.wm &&
                   RedBig::WN == mk_tiles::kRedBig.wn, "kRedBig is the 16 x 16 x 32 core");
 using RedSkinny =
     TileGemmDma<mk_tiles::kRedSkinny.bm, mk_tiles::kRedSkinny.bn, mk_tiles::kRedSkinny.wm, mk_tiles::kRedSkinny.wn>;
-using MlpDown = TileGemmDma<mk_tiles::kMlpDown.bm, mk_tiles::kMlpDown.bn, mk_tiles::kMlpDown.wm, mk_tiles::kMlpDown.wn>;
 
 // Cores with separate A and B slots (mk_gemm_tile16.hpp) against the two-stage TileGemmDma.
 template <class T>

@@ -11,10 +11,8 @@ struct Shape {
   constexpr int waves() const { return wm * wn; }
 };
 
-constexpr Shape kAg16{256, 224, 4, 2, 4};       // AllGather + GEMM (16 x 16 x 32 MFMA core)
-constexpr Shape kAg{256, 256, 2, 4, 8};         // the MLP block's up-projection
-constexpr Shape kRedBig{256, 256, 4, 2, 4};     // GEMM + RS / AR with wide outputs (16 x 16 x 32 MFMA core)
-constexpr Shape kMlpDown{256, 256, 2, 4, 8};    // the MLP block's down-projection
+constexpr Shape kAg16{256, 224, 4, 2, 4};       // AllGather + GEMM and the MLP up-projection (16 x 16 x 32 core)
+constexpr Shape kRedBig{256, 256, 4, 2, 4};     // GEMM + RS / AR with wide outputs, MLP down-projection
 constexpr Shape kRedSkinny{128, 64, 4, 1, 8};   // GEMM + RS / AR with few output rows (decode-like)
 constexpr int kRedSkinnyMaxRows = 512;       // outputs of at most this many rows take the skinny tile
 constexpr Shape kMoe{256, 256, 2, 4, 8};        // MoE grouped GEMM

@@ -289,7 +289,7 @@ def test_plan_mlp(hostlib):
     down-projection as a resident mk_gemm_rs on every workgroup, over the same 256-row tiles."""
     code, p = mlp(hostlib)
     assert code == MK_OK
-    assert (p["ag_copy"], p["ag_compute"], p["ag_tiles_m"], p["ag_tiles_n"]) == (160, 96, 32, 7)
+    assert (p["ag_copy"], p["ag_compute"], p["ag_tiles_m"], p["ag_tiles_n"]) == (160, 96, 32, 8)  # 256 x 224 up-projection tiles
     assert (p["red_compute"], p["red_tiles_m"], p["red_tiles_n"], p["assist"]) == (256, 32, 16, 1)
     assert (p["own_tile_begin"], p["own_tile_end"]) == (0, 4)
     code, p = mlp(hostlib, rank=5)
