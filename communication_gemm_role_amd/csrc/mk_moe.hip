@@ -30,12 +30,15 @@
 // Route/copy workgroups never wait on compute workgroups, and have the lowest ids.  The
 // last workgroup to exit re-zeroes the counters, so every call starts from zero.
 #include "mk_internal.h"
-#include "mk_gemm_tile.hpp"
+#include "mk_gemm_tile16.hpp"
 
 namespace mk {
 
-// 256 x 256 output tile, eight waves of 128 x 64, two-stage K loop
-using MoeTile = TileGemmDma<mk_tiles::kMoe.bm, mk_tiles::kMoe.bn, mk_tiles::kMoe.wm, mk_tiles::kMoe.wn>;
+// 256 x 256 output tile on the 16 x 16 x 32 core: eight waves of 64 x 128, A two steps ahead in
+// three 32 KiB LDS slots, B in two
+using MoeTile = TileGemm16T<mk_tiles::kMoe.bn>;
+static_assert(MoeTile::BM == mk_tiles::kMoe.bm && MoeTile::WM == mk_tiles::kMoe.wm && MoeTile::WN == mk_tiles::kMoe.wn,
+              "kMoe is the 16 x 16 x 32 core");
 constexpr int MOE_WAVES = MoeTile::NW;
 constexpr int MOE_THREADS = MOE_WAVES * 64;
 constexpr int MOE_KMAX = 8;     // top-k
@@ -322,8 +325,9 @@ __device__ __forceinline__ void moe_raise_chunk(const MoeParams& p, const MoeSha
   }
 }
 
-// Rows move global -> LDS (DMA) -> VGPRs -> global through the two 64 KiB stage buffers, as in
-// the AllGather copy: batch b gives wave w the window rows (8b + w) * RPB + i, i < RPB, each
+// Rows move global -> LDS (DMA) -> VGPRs -> global through two 64 KiB ring slots, each made of two
+// 32 KiB GEMM slots (waves 0-3 in the first, 4-7 in the second: s0 = lo0/hi0, s1 = lo1/hi1), as
+// in the AllGather copy: batch b gives wave w the window rows (8b + w) * RPB + i, i < RPB, each
 // IPR 1 KiB DMA instructions (RPB * IPR = 8 per wave and batch; lanes past a row's end fall
 // outside its buffer window).  Per batch and wave: 8 DMA loads and 8 stores, completing in issue
 // order, so batch b has landed at vmcnt <= 16 (8 for b = 0).  The window's chunks raise their
@@ -333,7 +337,7 @@ __device__ __forceinline__ void moe_raise_chunk(const MoeParams& p, const MoeSha
 // completes near the end of the dispatch either way.
 template <int IPR>
 __device__ __forceinline__ void moe_copy_window(const MoeParams& p, const MoeShared& sh, const int2* list, int stride,
-                                                int n_win, char* st0, char* st1) {
+                                                int n_win, char* lo0, char* hi0, char* lo1, char* hi1) {
   constexpr int RPB = 8 / IPR;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   (void)tid;
@@ -361,8 +365,10 @@ __device__ __forceinline__ void moe_copy_window(const MoeParams& p, const MoeSha
     const bool ok = slot >= 0 && slot < p.capacity;
     return make_rsrc(p.x_seg + (ok ? (size_t)slot * p.hidden : (size_t)0), ok ? row_b : 0u);
   };
-  auto dma = [&](int b, char* slot) {
-    char* base = slot + wave * 8192;
+  // this wave's 8 KiB of a ring slot
+  char* const w0 = (wave < 4 ? lo0 : hi0) + (wave & 3) * 8192;
+  char* const w1 = (wave < 4 ? lo1 : hi1) + (wave & 3) * 8192;
+  auto dma = [&](int b, char* base) {
 #pragma unroll
     for (int i = 0; i < RPB; ++i) {
       const int2 e = row_at((b * 8 + wave) * RPB + i);
@@ -374,8 +380,8 @@ __device__ __forceinline__ void moe_copy_window(const MoeParams& p, const MoeSha
             (uint32_t)(q * 64 + lane) * 16u, 0, 0, 0);
     }
   };
-  auto store = [&](int b, const char* slot) {
-    const char* base = slot + wave * 8192 + lane * 16;
+  auto store = [&](int b, const char* wbase) {
+    const char* base = wbase + lane * 16;
 #pragma unroll
     for (int i = 0; i < RPB; ++i) {
       const int2 e = row_at((b * 8 + wave) * RPB + i);
@@ -395,11 +401,11 @@ __device__ __forceinline__ void moe_copy_window(const MoeParams& p, const MoeSha
     dma(b + 2, slot);  // this wave's LDS reads of the slot completed with the stores above
   };
   if (nb > 0) {
-    dma(0, st0);
-    dma(1, st1);
+    dma(0, w0);
+    dma(1, w1);
     for (int b = 0; b < nb; b += 2) {
-      step(b, st0);
-      step(b + 1, st1);
+      step(b, w0);
+      step(b + 1, w1);
     }
   }
   wait_vm<0>();
@@ -417,8 +423,8 @@ __device__ __forceinline__ void moe_copy_window(const MoeParams& p, const MoeSha
 // then all waves move the window's part of the rows.  With the default role split a workgroup's
 // rows span a few chunks: one window, one listing round trip and one pipeline fill and drain.
 template <int IPR>
-__device__ __forceinline__ void moe_dispatch(const MoeParams& p, int cid, MoeShared& sh, int2* list, char* st0,
-                                             char* st1) {
+__device__ __forceinline__ void moe_dispatch(const MoeParams& p, int cid, MoeShared& sh, int2* list, char* lo0,
+                                             char* hi0, char* lo1, char* hi1) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int stride = 64 * min(p.top_k, p.n_local);  // room for a chunk's largest row count
   const int cw = max(1, min(MOE_WAVES, MOE_LIST / stride));
@@ -466,12 +472,12 @@ __device__ __forceinline__ void moe_dispatch(const MoeParams& p, int cid, MoeSha
       for (int j = 0; j < n_win; ++j) sh.pre[j + 1] = sh.pre[j] + sh.n_rows[j];
     }
     __syncthreads();
-    moe_copy_window<IPR>(p, sh, list, stride, n_win, st0, st1);  // ends with a barrier
+    moe_copy_window<IPR>(p, sh, list, stride, n_win, lo0, hi0, lo1, hi1);  // ends with a barrier
   }
 }
 
-__device__ __forceinline__ void moe_copy_role(const MoeParams& p, int cid, MoeShared& sh, int2* list, char* st0,
-                                              char* st1) {
+__device__ __forceinline__ void moe_copy_role(const MoeParams& p, int cid, MoeShared& sh, int2* list, char* lo0,
+                                              char* hi0, char* lo1, char* hi1) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // route: chunks (cid * 8 + wave) + i * (n_copy * 8)
   const int c0 = cid * MOE_WAVES + wave, cs = p.n_copy * MOE_WAVES;
@@ -500,10 +506,10 @@ __device__ __forceinline__ void moe_copy_role(const MoeParams& p, int cid, MoeSh
   __syncthreads();
   // DMA instructions per row and wave, rounded up to a power of two (8 for hidden 4096)
   const int cpr = p.hidden >> 3;  // 16-byte pieces per row
-  if (cpr > 256) moe_dispatch<8>(p, cid, sh, list, st0, st1);
-  else if (cpr > 128) moe_dispatch<4>(p, cid, sh, list, st0, st1);
-  else if (cpr > 64) moe_dispatch<2>(p, cid, sh, list, st0, st1);
-  else moe_dispatch<1>(p, cid, sh, list, st0, st1);
+  if (cpr > 256) moe_dispatch<8>(p, cid, sh, list, lo0, hi0, lo1, hi1);
+  else if (cpr > 128) moe_dispatch<4>(p, cid, sh, list, lo0, hi0, lo1, hi1);
+  else if (cpr > 64) moe_dispatch<2>(p, cid, sh, list, lo0, hi0, lo1, hi1);
+  else moe_dispatch<1>(p, cid, sh, list, lo0, hi0, lo1, hi1);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -512,39 +518,51 @@ __device__ __forceinline__ void moe_copy_role(const MoeParams& p, int cid, MoeSh
 // Grouped-GEMM tiles: `first` (a static tile of this workgroup, or -1), then leftover tiles
 // n_compute, n_compute + 1, ... claimed from a shared counter by every workgroup that has finished
 // its own work (compute workgroups after their static tile, copy workgroups after the dispatch).
-__device__ __forceinline__ void moe_gemm_tiles(const MoeParams& p, MoeShared& sh, int first, char* st0, char* st1,
-                                               char* st2) {
+// The K loop runs over five LDS slots (a0..a2: A, b0, b1: B); sh lives in b1 (see moe_kernel),
+// so only sh.claim and sh.ok are used here, between K loops, and the segment table is read from
+// global memory (the scan's output) for every tile.
+__device__ __forceinline__ void moe_gemm_tiles(const MoeParams& p, MoeShared& sh, int first, char* a0, char* a1,
+                                               char* a2, char* b0, char* b1) {
+  using G = MoeTile;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  MoeTile g;
-  const int wm = wave / MoeTile::WN, wn = wave % MoeTile::WN;
-  const int n_mt = sh.tile_base[p.n_local];
-  const int n_tiles = n_mt * p.tiles_n;
+  G g;
+  const int wm = wave / G::WN, wn = wave % G::WN;
   const int nk = p.hidden >> 6;
   const uint32_t lda_b = (uint32_t)p.hidden * 2u, ldb_b = (uint32_t)p.ffn * 2u;
-  g.init(wm, wn, lane, lda_b, ldb_b);
+  g.init(wm, wn, wave, lane, lda_b, ldb_b);
+  // lane i < n_local: segment end seg_off[i + 1] and m-tile base tile_base[i + 1] (entry 0 of both
+  // is 0), written by the scan before its flag
+  const auto so = make_rsrc(p.seg_offsets, (uint32_t)(p.n_local + 1) * 4u);
+  const auto tb = make_rsrc(moe_misc(p) + 2, (uint32_t)(p.n_local + 1) * 4u);
   int t = first;
   bool traced = false;
   while (true) {
     if (t < 0) {
+      __syncthreads();  // every thread has read the last claim
       if (tid == 0) sh.claim = p.n_compute + (int)atomic_add_agent(moe_misc(p) + MISC_TILE, 1u);
       __syncthreads();
       t = sh.claim;
     }
+    const bool in = lane < p.n_local;
+    const int seg_n = in ? (int)bload4_sc1(so, (uint32_t)(lane + 1) * 4u) : 0;
+    const int tb_n = in ? (int)bload4_sc1(tb, (uint32_t)(lane + 1) * 4u) : 0;
+    const int n_mt = __builtin_amdgcn_readlane(tb_n, p.n_local - 1);
+    const int n_tiles = n_mt * p.tiles_n;
     if (t >= n_tiles) break;
     const int gm = t / p.tiles_n, tn = t - gm * p.tiles_n;
     t = -1;
-    int el = 0;
-    while (el + 1 < p.n_local && sh.tile_base[el + 1] <= gm) ++el;
-    const int mt = gm - sh.tile_base[el];
-    const int row0 = sh.seg_off[el] + mt * MoeTile::BM;
-    int rows_valid = min(MoeTile::BM, sh.seg_off[el + 1] - row0);
+    // expert of m-tile gm: the number of experts whose tiles all come before it
+    const int el = (int)__popcll(__ballot(in && tb_n <= gm));
+    const int seg0 = el == 0 ? 0 : __builtin_amdgcn_readlane(seg_n, el - 1);
+    const int seg1 = __builtin_amdgcn_readlane(seg_n, el);
+    const int tb0 = el == 0 ? 0 : __builtin_amdgcn_readlane(tb_n, el - 1);
+    const int mt = gm - tb0;
+    const int row0 = seg0 + mt * G::BM;
+    int rows_valid = min(G::BM, seg1 - row0);
     rows_valid = min(rows_valid, p.capacity - row0);
-    if (rows_valid <= 0) {
-      __syncthreads();  // every thread has read sh.claim before the next claim rewrites it
-      continue;
-    }
-    const int n0 = tn * MoeTile::BN;
-    const int cols_valid = min(MoeTile::BN, p.ffn - n0);
+    if (rows_valid <= 0) continue;
+    const int n0 = tn * G::BN;
+    const int cols_valid = min(G::BN, p.ffn - n0);
     // wait until every row of this m-tile has landed
     if (tid == 0)
       sh.ok = spin_until_ge(p.counters + p.off_tile_cnt + gm, (uint32_t)rows_valid, p.timeout_ticks, p.status);
@@ -556,14 +574,23 @@ __device__ __forceinline__ void moe_gemm_tiles(const MoeParams& p, MoeShared& sh
     const uint32_t a_tile_bytes = (uint32_t)rows_valid * lda_b;
     const char* b_col = reinterpret_cast<const char*>(p.w_up + (size_t)el * p.hidden * p.ffn + n0);
     const uint32_t b_col_bytes = ((uint32_t)p.hidden * (uint32_t)p.ffn - (uint32_t)n0) * 2u;
-    auto load_step = [&](int ks, char* dst) {
-      const uint32_t ca = (uint32_t)ks * 128u, rb = (uint32_t)ks * 64u * ldb_b;
+    auto dma_a = [&](int ks, char* dst) {
+      const uint32_t ca = (uint32_t)ks * 128u;
       g.dma_a(a_tile + ca, a_tile_bytes - ca, lda_b, dst, wave);
-      g.dma_b(b_col + rb, b_col_bytes - rb, ldb_b, dst, wave);
     };
+    auto dma_b = [&](int ks, char* dst) {
+      const uint32_t rb = (uint32_t)ks * 64u * ldb_b;
+      g.dma_b(b_col + rb, b_col_bytes - rb, dst, wave);
+    };
+    auto prologue = [&](char* pa0, char* pb0, char* pa1) {
+      dma_a(0, pa0);
+      dma_b(0, pb0);
+      if (nk > 1) dma_a(1, pa1);
+    };
+    auto none = [](int, auto) {};
     g.zero();
-    k_loop(g, nk, st0, st1, st2, st2, st2, [](int) {}, load_step, [](int) {});
-    g.epilogue(st0, st1, wm, wn, lane, wave, [&](int row, int col, f32x4 v) {
+    k_loop_a3b2(g, nk, a0, a1, a2, b0, b1, prologue, dma_a, dma_b, none, none, none, [] { return true; });
+    g.epilogue(G::epi_buf(wave, a0, a1, a2), wm, wn, lane, [&](int row, int col, f32x4 v) {
       if (row < rows_valid && col < cols_valid)
         __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p.y + (size_t)(row0 + row) * p.ffn + (n0 + col)));
     });
@@ -571,38 +598,44 @@ __device__ __forceinline__ void moe_gemm_tiles(const MoeParams& p, MoeShared& sh
   }
 }
 
-__device__ __forceinline__ void moe_compute_role(const MoeParams& p, int slot, char* st0, char* st1, char* st2,
-                                                 MoeShared& sh) {
+__device__ __forceinline__ void moe_compute_role(const MoeParams& p, int slot, char* a0, char* a1, char* a2, char* b0,
+                                                 char* b1, MoeShared& sh) {
   const int tid = threadIdx.x;
   if (tid == 0) sh.ok = spin_until_eq(&p.flags[0], p.epoch, p.timeout_ticks, p.status);
   __syncthreads();
   if (!sh.ok) return;
-  moe_load_segments(p, sh);
-  __syncthreads();
   // XCD-aware static tile: workgroup w runs on XCD w % 8, consecutive tiles (same expert and
   // m-tile, so the same A rows) go to one XCD
   const int C = p.n_compute;
   const int rs = ((C & 7) == 0) ? (slot & 7) * (C >> 3) + (slot >> 3) : slot;
-  moe_gemm_tiles(p, sh, rs, st0, st1, st2);
+  moe_gemm_tiles(p, sh, rs, a0, a1, a2, b0, b1);
 }
 
-static_assert(MoeTile::STAGE >= 65536 && MOE_THREADS == 512, "copy slots: 64 KiB stage buffers, 8 waves");
+// The five GEMM slots fill the 160 KiB of LDS: the copy role's row list and the shared block sit in
+// the last B slot, which only the K loop uses (copy workgroups finish the dispatch before their
+// first tile; during a K loop no code touches sh).
+constexpr int MOE_SH = MOE_LIST * (int)sizeof(int2);
+static_assert(MOE_SH + (int)sizeof(MoeShared) <= MoeTile::SLOT_B, "row list and shared block fit one B slot");
+static_assert(MOE_THREADS == 512, "ring slots: 8 waves x 8 KiB");
 
 __global__ __launch_bounds__(MOE_THREADS, 1) void moe_kernel(MoeParams p) {
-  __shared__ __attribute__((aligned(16))) char st0[MoeTile::STAGE];
-  __shared__ __attribute__((aligned(16))) char st1[MoeTile::STAGE];
-  __shared__ __attribute__((aligned(16))) char st2[k_stages<MoeTile>() == 3 ? MoeTile::STAGE : 16];
-  __shared__ int2 list[MOE_LIST];
-  __shared__ MoeShared sh;
+  // 256-byte aligned: the swizzled B reads XOR bits 5-7 of the address
+  __shared__ __attribute__((aligned(256))) char a0[MoeTile::SLOT_A];
+  __shared__ __attribute__((aligned(256))) char a1[MoeTile::SLOT_A];
+  __shared__ __attribute__((aligned(256))) char a2[MoeTile::SLOT_A];
+  __shared__ __attribute__((aligned(256))) char b0[MoeTile::SLOT_B];
+  __shared__ __attribute__((aligned(256))) char b1[MoeTile::SLOT_B];
+  int2* list = reinterpret_cast<int2*>(b1);
+  MoeShared& sh = *reinterpret_cast<MoeShared*>(b1 + MOE_SH);
   const int wg = blockIdx.x;
   if (wg < p.n_copy) {
     trace_begin(p.trace, ROLE_COPY);
-    moe_copy_role(p, wg, sh, list, st0, st1);
+    moe_copy_role(p, wg, sh, list, a0, a1, a2, b0);  // ring slots: a0 + a1 and a2 + b0
     trace_mark(p.trace, 7);
-    if (sh.ok) moe_gemm_tiles(p, sh, -1, st0, st1, st2);  // then help with leftover tiles
+    if (sh.ok) moe_gemm_tiles(p, sh, -1, a0, a1, a2, b0, b1);  // then help with leftover tiles
   } else {
     trace_begin(p.trace, ROLE_COMPUTE);
-    if (wg - p.n_copy < p.n_compute) moe_compute_role(p, wg - p.n_copy, st0, st1, st2, sh);
+    if (wg - p.n_copy < p.n_compute) moe_compute_role(p, wg - p.n_copy, a0, a1, a2, b0, b1, sh);
   }
   trace_end(p.trace);
   // exit accounting: the last workgroup out re-zeroes the counters for the next call

@@ -15,7 +15,7 @@ constexpr Shape kAg16{256, 224, 4, 2, 4};       // AllGather + GEMM and the MLP 
 constexpr Shape kRedBig{256, 256, 4, 2, 4};     // GEMM + RS / AR with wide outputs, MLP down-projection
 constexpr Shape kRedSkinny{128, 64, 4, 1, 8};   // GEMM + RS / AR with few output rows (decode-like)
 constexpr int kRedSkinnyMaxRows = 512;       // outputs of at most this many rows take the skinny tile
-constexpr Shape kMoe{256, 256, 2, 4, 8};        // MoE grouped GEMM
+constexpr Shape kMoe{256, 256, 4, 2, 8};        // MoE grouped GEMM (16 x 16 x 32 core; ring: 8 KiB per wave)
 
 constexpr bool red_skinny(int m) { return m <= kRedSkinnyMaxRows; }
 constexpr const Shape& red_shape(int m) { return red_skinny(m) ? kRedSkinny : kRedBig; }
