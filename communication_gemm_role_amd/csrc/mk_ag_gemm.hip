@@ -13,7 +13,7 @@ int ag_tile_m() { return TileGemm16::BM; }
 int ag_tile_n() { return TileGemm16::BN; }
 
 // Roles: workgroups [0, n_copy) copy (land peer units in the caller's order), then compute; the rest
-// compute from the start (static tiles: ag_static_tile).
+// compute from the start (static tiles: ag_static_tile, the local shard's tiles first).
 __global__ __launch_bounds__(AG_THREADS, 1) void ag_gemm_kernel(AgParams p) {
   using G = TileGemm16;
   __shared__ __attribute__((aligned(16))) char a0[G::SLOT_A];
@@ -35,7 +35,13 @@ __global__ __launch_bounds__(AG_THREADS, 1) void ag_gemm_kernel(AgParams p) {
     trace_begin(p.trace, ROLE_COMPUTE);
   }
   const bool is_copy = wg < p.n_copy;
-  ag_compute_role16<0>(p, t_static, !is_copy, is_copy, a0, a1, a2, b0, b1, s_sched, &s_claim, s_poll);
+  // Unpaced, the copy lands every unit within ~20 us, and a tile that waits for its rows and then
+  // runs its K loop in order ends sooner than one that starts on partial rows ready-first (whose
+  // K order differs from the other tiles of its XCD, so their A and B k-slabs stop being shared in
+  // L2): every workgroup waits.  Paced at a link rate the landing takes several times longer, and
+  // compute workgroups consume units ready-first.
+  ag_compute_role16<0>(p, t_static, !is_copy, is_copy || p.pace_q16 == 0, a0, a1, a2, b0, b1, s_sched, &s_claim,
+                       s_poll);
   trace_end(p.trace);
   // exit accounting: the last workgroup out re-zeroes the tile counter for the next call (every
   // workgroup's last claim returned before it counts its exit)

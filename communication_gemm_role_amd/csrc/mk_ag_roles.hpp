@@ -415,19 +415,46 @@ __device__ __forceinline__ bool ag_wait_rows(const AgParams& p, int ur0, int n_u
   return true;
 }
 
-// Static tile of workgroup wg (or -1).  Static tiles are XCD-aware: workgroup w runs on XCD w % 8,
-// and the k-th of n workgroups taking static tiles owns logical tile (k % 8) * (n / 8) + k / 8, so
-// an XCD's tiles are consecutive (whole tile rows, sharing their A rows in its L2).  When the
-// compute workgroups alone can hold every tile they do (k = wg - n_copy, n = n_compute);
-// otherwise every workgroup of the grid owns one (copy workgroups start theirs after copying)
-// and tiles past the grid are claimed from a counter.
+// Tile rows [lt0, lt1) lie wholly inside the local shard's rows when that shard is already in
+// place in a_gathered (emulated arrival): their operands are present at launch.
+__device__ __forceinline__ void ag_local_tile_rows(const AgParams& p, int& lt0, int& lt1) {
+  lt0 = lt1 = 0;
+  if (!p.emulated || !p.local_in_place) return;
+  constexpr int BM = TileGemm16::BM;
+  const int r0 = p.rank * p.m_shard, r1 = r0 + p.m_shard;
+  lt0 = (r0 + BM - 1) / BM;
+  lt1 = max(lt0, r1 / BM);
+}
+
+// Static tile of workgroup wg (or -1).  When the compute workgroups alone can hold every tile they
+// do, in XCD-aware order: the k-th of the n compute workgroups runs on XCD k % 8 (workgroup w runs
+// on XCD w % 8 and n_copy is a multiple of 8) and owns logical tile (k % 8) * (n / 8) + k / 8, so an
+// XCD's tiles are consecutive (whole tile rows, sharing their A rows in its L2).  Otherwise every
+// workgroup of the grid owns one (copy workgroups start theirs after copying; tiles past the grid
+// are claimed from a counter), taken in order of readiness: the compute workgroups, which start at
+// once, take the tiles whose rows are local first, and the copy workgroups the rest, each set
+// XCD-aware in the same way.
 __device__ __forceinline__ int ag_static_tile(const AgParams& p, int wg, int grid) {
   const int n_tiles = p.tiles_m * p.tiles_n;
-  const bool compute_only = n_tiles <= p.n_compute;
-  const int k = compute_only ? wg - p.n_copy : wg, n = compute_only ? p.n_compute : grid;
-  if (k < 0 || k >= n) return -1;  // not one of the n (a second owner of a tile would count it twice)
-  const int rs = (n & 7) == 0 ? (k & 7) * (n >> 3) + (k >> 3) : k;
-  return rs < n_tiles ? rs : -1;
+  if (n_tiles <= p.n_compute) {
+    const int k = wg - p.n_copy, n = p.n_compute;
+    if (k < 0 || k >= n) return -1;  // not one of the n (a second owner of a tile would count it twice)
+    const int rs = (n & 7) == 0 ? (k & 7) * (n >> 3) + (k >> 3) : k;
+    return rs < n_tiles ? rs : -1;
+  }
+  if (wg < 0 || wg >= grid) return -1;
+  const bool comp = wg >= p.n_copy;
+  const int base = comp ? p.n_copy : 0, cnt = comp ? grid - p.n_copy : p.n_copy;
+  const int k = wg - base;
+  const int pos = ((cnt & 7) == 0 && (base & 7) == 0) ? (k & 7) * (cnt >> 3) + (k >> 3) : k;
+  const int s = (comp ? 0 : grid - p.n_copy) + pos;  // place in the readiness order
+  if (s >= n_tiles) return -1;
+  int lt0, lt1;
+  ag_local_tile_rows(p, lt0, lt1);
+  const int first = lt0 * p.tiles_n, nl = (lt1 - lt0) * p.tiles_n;
+  if (s < nl) return first + s;  // the local tile rows, row-major
+  const int r = s - nl;          // then the others, row-major
+  return r < first ? r : r + nl;
 }
 
 // Compute role of the AllGather + GEMM kernel.  The workgroup first runs tile t_static (-1: none),

@@ -133,9 +133,29 @@ inline int plan_ag(const Ws& ws, const Opts* o, const void* const* a_shards, int
     if (o && o->arrival_order && !aligned16(o->arrival_order) && ((uintptr_t)o->arrival_order & 3u)) return MK_ERR_UNSUPPORTED;
     P->drop_pos = (o && o->test_drop_unit > 0) ? o->test_drop_unit : 0;
   }
-  // copy workgroups take the tiles left over past the compute role once they have copied, so a
-  // large copy role lands the shards sooner without leaving tiles for a second round
-  const int want_copy = P->emulated ? ((o && o->n_copy_wg) ? o->n_copy_wg : 160) : 0;
+  // Default role split.  Every workgroup owns one tile and the copy workgroups start theirs once
+  // they have copied.  Unpaced, the compute workgroups are as many as the tiles whose rows are the
+  // local shard (rounded up to whole XCD rounds): they take those tiles and start at once, and every
+  // other workgroup copies, so the shards land as soon as the HBM allows.  Paced at a link rate, 160
+  // copy workgroups (the tuner finds the best split per shape).
+  int want_copy = 0;
+  if (P->emulated) {
+    if (o && o->n_copy_wg) {
+      want_copy = o->n_copy_wg;
+    } else if (o && o->arrival_gbps > 0.0) {
+      want_copy = 160;
+    } else {
+      long lt0 = 0, lt1 = 0;
+      if (P->local_in_place) {
+        lt0 = ((long)rank * m_shard + tile_m - 1) / tile_m;
+        lt1 = ((long)rank * m_shard + m_shard) / tile_m;
+        if (lt1 < lt0) lt1 = lt0;
+      }
+      long nc = ((lt1 - lt0) * P->tiles_n + 7) & ~7L;
+      if (nc < 8) nc = 8;
+      want_copy = ws.grid - nc >= 8 ? (int)(ws.grid - nc) : 8;
+    }
+  }
   if (P->emulated && P->n_order > 0 && want_copy == 0) return MK_ERR_INVALID_ARG;
   int nr = 0;
   int code = split_roles(ws.grid, P->emulated ? want_copy : 0, 0, o ? o->n_compute_wg : 0, &P->n_copy, &nr, &P->n_compute);

@@ -130,8 +130,17 @@ def test_plan_ag_full_workload(hostlib):
     assert p["n_order"] == 8 * 8 * 32 and p["local_in_place"] == 0  # shard 0 at another address: copied too
     code, p = ag(hostlib, shards="inplace")
     assert code == MK_OK and p["local_in_place"] == 1 and p["n_order"] == 7 * 8 * 32
-    # 160 copy workgroups (they take the tiles left over past the 96 static compute tiles)
-    assert (p["n_copy"], p["n_compute"], p["tiles_m"], p["tiles_n"]) == (160, 96, 32, 7)
+    # unpaced: the compute role is as large as the local shard's 4 x 7 tiles, rounded up to whole
+    # XCD rounds (32 workgroups, which take those tiles); every other workgroup copies first
+    assert (p["n_copy"], p["n_compute"], p["tiles_m"], p["tiles_n"]) == (224, 32, 32, 7)
+    code, p = ag(hostlib, shards="inplace", rank=5)
+    assert code == MK_OK and (p["n_copy"], p["n_compute"]) == (224, 32)
+    # no local shard in place: one round of 8 compute workgroups
+    code, p = ag(hostlib)
+    assert code == MK_OK and (p["n_copy"], p["n_compute"]) == (248, 8)
+    # paced at a link rate: 160 copy workgroups
+    code, p = ag(hostlib, shards="inplace", opts=Opts(arrival_gbps=1071.0))
+    assert code == MK_OK and (p["n_copy"], p["n_compute"]) == (160, 96) and p["pace_q16"] > 0
     # resident: no copy role, and the compute role is cut to the 224 tiles (whole XCD rounds)
     code, p = ag(hostlib, shards="none", opts=Opts(arrival_mode=RESIDENT))
     assert code == MK_OK and (p["n_copy"], p["n_compute"]) == (0, 224)
@@ -289,7 +298,9 @@ def test_plan_mlp(hostlib):
     down-projection as a resident mk_gemm_rs on every workgroup, over the same 256-row tiles."""
     code, p = mlp(hostlib)
     assert code == MK_OK
-    assert (p["ag_copy"], p["ag_compute"], p["ag_tiles_m"], p["ag_tiles_n"]) == (160, 96, 32, 8)  # 256 x 224 up-projection tiles
+    # 256 x 224 up-projection tiles; no local shard in place (every shard is copied): one XCD round
+    # of compute workgroups
+    assert (p["ag_copy"], p["ag_compute"], p["ag_tiles_m"], p["ag_tiles_n"]) == (248, 8, 32, 8)
     assert (p["red_compute"], p["red_tiles_m"], p["red_tiles_n"], p["assist"]) == (256, 32, 16, 1)
     assert (p["own_tile_begin"], p["own_tile_end"]) == (0, 4)
     code, p = mlp(hostlib, rank=5)
