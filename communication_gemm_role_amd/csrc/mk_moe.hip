@@ -21,7 +21,7 @@
 //           stream (the scan also lays out each arrival position's first row), a window of up to
 //           eight chunks at a time: each wave lists one chunk's routed (token, slot) rows, then
 //           all waves move the workgroup's part of them into their final slots of x_seg through
-//           LDS, and once the window's rows are stored they are added to their m-tiles'
+//           registers, and once the window's rows are stored they are added to their m-tiles'
 //           landed-row counters.  A copy workgroup with no chunks
 //           left joins the compute role on the tiles left over after every compute workgroup's
 //           first one.
@@ -145,7 +145,11 @@ __device__ __forceinline__ void moe_route_all(const MoeParams& p, int first, int
 }
 
 // Exclusive scan of the per-chunk counts (run by one workgroup, the last router).  Each wave
-// owns local experts wave, wave + 8, ...; a group of 16 x 64 chunk counts is loaded at once.
+// owns local experts wave, wave + 8, ...; a group of 16 x 64 chunk counts is loaded at once.  When
+// every wave owns at most one expert and the chunks fit one group (the usual case), the counts are
+// loaded once and stay in registers from the totals to the per-chunk first slots, and the loads of
+// the arrival-order pass (which does not depend on them) are issued first, so the whole scan waits
+// on memory about twice instead of once per pass.
 __device__ __forceinline__ void moe_scan(const MoeParams& p, MoeShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   uint32_t* cnt = p.counters + p.off_chunk_cnt;
@@ -157,18 +161,42 @@ __device__ __forceinline__ void moe_scan(const MoeParams& p, MoeShared& sh) {
       v[i] = bload4_sc1(cr, (c * (uint32_t)p.n_local + (uint32_t)el) * 4u);  // past n_chunks: 0
     }
   };
+  // rows of the chunk at arrival position i (pass 3's input)
+  const auto rr = make_rsrc(p.counters + p.off_chunk_rows, (uint32_t)p.n_chunks * 4u);
+  const int32_t* order = (p.emulated && p.order) ? p.order : nullptr;
+  auto rows_at = [&](int i) -> uint32_t {
+    if (i >= p.n_chunks) return 0u;
+    const int c = order ? order[i] : i;
+    return (c >= 0 && c < p.n_chunks) ? bload4_sc1(rr, (uint32_t)c * 4u) : 0u;
+  };
+  const bool one_pos = p.n_chunks <= MOE_THREADS;
+  const uint32_t rows0 = one_pos ? rows_at(tid) : 0u;
+  const bool in_regs = p.n_local <= MOE_WAVES && p.n_chunks <= 1024;
+  uint32_t vr[16];
   // pass 1: per-expert totals
-  for (int el = wave; el < p.n_local; el += MOE_WAVES) {
-    uint32_t s = 0;
-    for (int g0 = 0; g0 < p.n_chunks; g0 += 1024) {
-      uint32_t v[16];
-      load_group(el, g0, v);
+  if (in_regs) {
+    if (wave < p.n_local) {
+      load_group(wave, 0, vr);
+      uint32_t s = 0;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s += v[i];
+      for (int i = 0; i < 16; ++i) s += vr[i];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+      if (lane == 0) sh.totals[wave] = (int)s;
     }
+  } else {
+    for (int el = wave; el < p.n_local; el += MOE_WAVES) {
+      uint32_t s = 0;
+      for (int g0 = 0; g0 < p.n_chunks; g0 += 1024) {
+        uint32_t v[16];
+        load_group(el, g0, v);
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
-    if (lane == 0) sh.totals[el] = (int)s;
+        for (int i = 0; i < 16; ++i) s += v[i];
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+      if (lane == 0) sh.totals[el] = (int)s;
+    }
   }
   __syncthreads();
   if (tid == 0) {
@@ -185,22 +213,32 @@ __device__ __forceinline__ void moe_scan(const MoeParams& p, MoeShared& sh) {
   }
   __syncthreads();
   // pass 2: first slot of every (chunk, expert), in chunk order
-  for (int el = wave; el < p.n_local; el += MOE_WAVES) {
-    uint32_t run = (uint32_t)sh.seg_off[el];
-    for (int g0 = 0; g0 < p.n_chunks; g0 += 1024) {
-      uint32_t v[16];
-      load_group(el, g0, v);
+  auto scan_group = [&](int el, int g0, const uint32_t(&v)[16], uint32_t& run) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        uint32_t inc = v[i];
+    for (int i = 0; i < 16; ++i) {
+      uint32_t inc = v[i];
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const uint32_t y = __shfl_up(inc, o);
-          if (lane >= o) inc += y;
-        }
-        const uint32_t c = (uint32_t)(g0 + i * 64 + lane);
-        bstore4_sc1(cr, (c * (uint32_t)p.n_local + (uint32_t)el) * 4u, run + inc - v[i]);  // past the end: dropped
-        run += __shfl(inc, 63);
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(inc, o);
+        if (lane >= o) inc += y;
+      }
+      const uint32_t c = (uint32_t)(g0 + i * 64 + lane);
+      bstore4_sc1(cr, (c * (uint32_t)p.n_local + (uint32_t)el) * 4u, run + inc - v[i]);  // past the end: dropped
+      run += __shfl(inc, 63);
+    }
+  };
+  if (in_regs) {
+    if (wave < p.n_local) {
+      uint32_t run = (uint32_t)sh.seg_off[wave];
+      scan_group(wave, 0, vr, run);
+    }
+  } else {
+    for (int el = wave; el < p.n_local; el += MOE_WAVES) {
+      uint32_t run = (uint32_t)sh.seg_off[el];
+      for (int g0 = 0; g0 < p.n_chunks; g0 += 1024) {
+        uint32_t v[16];
+        load_group(el, g0, v);
+        scan_group(el, g0, v, run);
       }
     }
   }
@@ -213,17 +251,11 @@ __device__ __forceinline__ void moe_scan(const MoeParams& p, MoeShared& sh) {
   // pass 3: first row of every arrival position in the stream of routed rows in arrival order
   // (exclusive scan of the chunks' row totals taken in the caller's order), for the copy split
   {
-    const auto rr = make_rsrc(p.counters + p.off_chunk_rows, (uint32_t)p.n_chunks * 4u);
     const auto pp = make_rsrc(p.counters + p.off_pos_pre, (uint32_t)(p.n_chunks + 1) * 4u);
-    const int32_t* order = (p.emulated && p.order) ? p.order : nullptr;
     uint32_t carry = 0;
     for (int base = 0; base < p.n_chunks; base += MOE_THREADS) {
       const int i = base + tid;
-      uint32_t v = 0;
-      if (i < p.n_chunks) {
-        const int c = order ? order[i] : i;
-        if (c >= 0 && c < p.n_chunks) v = bload4_sc1(rr, (uint32_t)c * 4u);
-      }
+      const uint32_t v = one_pos ? rows0 : rows_at(i);
       uint32_t inc = v;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
@@ -325,29 +357,24 @@ __device__ __forceinline__ void moe_raise_chunk(const MoeParams& p, const MoeSha
   }
 }
 
-// Rows move global -> LDS (DMA) -> VGPRs -> global through two 64 KiB ring slots, each made of two
-// 32 KiB GEMM slots (waves 0-3 in the first, 4-7 in the second: s0 = lo0/hi0, s1 = lo1/hi1), as
-// in the AllGather copy: batch b gives wave w the window rows (8b + w) * RPB + i, i < RPB, each
-// IPR 1 KiB DMA instructions (RPB * IPR = 8 per wave and batch; lanes past a row's end fall
-// outside its buffer window).  Per batch and wave: 8 DMA loads and 8 stores, completing in issue
-// order, so batch b has landed at vmcnt <= 16 (8 for b = 0).  The window's chunks raise their
-// m-tile counters after the last store: counter atomics inside the loop would come in a
-// data-dependent number, and the compiler would then drain the whole pipeline before every LDS
-// read.  An m-tile spans chunks from the whole token range, so under a random arrival order it
-// completes near the end of the dispatch either way.
+// The window's rows move global -> VGPRs -> global: wave w takes window rows w, w + 8, ...,
+// up to RW rows per round (RW * IPR 1 KiB loads, 128 VGPRs of data: the registers the grouped GEMM
+// uses later are free here), so a workgroup's ~32 rows of a default role split are all requested
+// at once and the dispatch costs one round trip to memory instead of one per LDS ring batch.
+// Source rows are read once (non-temporal); the stores are write-through (the grouped GEMM reads
+// x_seg from other XCDs).  Lanes past a row's end fall outside its buffer window.  The window's
+// chunks raise their m-tile counters after the last store: counter atomics inside the loop would
+// come in a data-dependent number.  An m-tile spans chunks from the whole token range, so under a
+// random arrival order it completes near the end of the dispatch either way.
 template <int IPR>
 __device__ __forceinline__ void moe_copy_window(const MoeParams& p, const MoeShared& sh, const int2* list, int stride,
-                                                int n_win, char* lo0, char* hi0, char* lo1, char* hi1) {
-  constexpr int RPB = 8 / IPR;
+                                                int n_win) {
+  constexpr int RW = 32 / IPR;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  (void)tid;
   const int R = sh.pre[n_win];
-  const int nb = (R + 8 * RPB - 1) / (8 * RPB);
   const uint32_t row_b = (uint32_t)p.hidden * 2u;
-  // The lookups below are branch-free (selects, a fixed unrolled scan): a branch inside the copy
-  // loop made the compiler drain every outstanding DMA (vmcnt(0)) before each batch's LDS reads,
-  // as it could no longer tell that they read the other slot.
-  auto row_at = [&](int r) -> int2 {  // list entry of window row r, or (-1, -1)
+  // branch-free lookup (selects, a fixed unrolled scan) of window row r's list entry, or (-1, -1)
+  auto row_at = [&](int r) -> int2 {
     int j = 0;
 #pragma unroll
     for (int k = 1; k < MOE_WAVES; ++k) j += (k < n_win && sh.pre[k] <= r) ? 1 : 0;
@@ -365,50 +392,24 @@ __device__ __forceinline__ void moe_copy_window(const MoeParams& p, const MoeSha
     const bool ok = slot >= 0 && slot < p.capacity;
     return make_rsrc(p.x_seg + (ok ? (size_t)slot * p.hidden : (size_t)0), ok ? row_b : 0u);
   };
-  // this wave's 8 KiB of a ring slot
-  char* const w0 = (wave < 4 ? lo0 : hi0) + (wave & 3) * 8192;
-  char* const w1 = (wave < 4 ? lo1 : hi1) + (wave & 3) * 8192;
-  auto dma = [&](int b, char* base) {
+  for (int r0 = 0; r0 < R; r0 += MOE_WAVES * RW) {
+    u32x4 v[RW][IPR];
+    int2 e[RW];
 #pragma unroll
-    for (int i = 0; i < RPB; ++i) {
-      const int2 e = row_at((b * 8 + wave) * RPB + i);
-      const auto src = src_of(__builtin_amdgcn_readfirstlane(e.x));
+    for (int i = 0; i < RW; ++i) {
+      e[i] = row_at(r0 + i * MOE_WAVES + wave);
+      const auto src = src_of(__builtin_amdgcn_readfirstlane(e[i].x));
 #pragma unroll
-      for (int q = 0; q < IPR; ++q)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            src, (__attribute__((address_space(3))) void*)(base + (i * IPR + q) * 1024), 16,
-            (uint32_t)(q * 64 + lane) * 16u, 0, 0, 0);
+      for (int q = 0; q < IPR; ++q) v[i][q] = bload16_nt(src, (uint32_t)(q * 64 + lane) * 16u);
     }
-  };
-  auto store = [&](int b, const char* wbase) {
-    const char* base = wbase + lane * 16;
 #pragma unroll
-    for (int i = 0; i < RPB; ++i) {
-      const int2 e = row_at((b * 8 + wave) * RPB + i);
-      const auto dst = dst_of(__builtin_amdgcn_readfirstlane(e.y));
+    for (int i = 0; i < RW; ++i) {
+      const auto dst = dst_of(__builtin_amdgcn_readfirstlane(e[i].y));
 #pragma unroll
-      for (int q = 0; q < IPR; ++q)
-        bstore16_sc1(dst, (uint32_t)(q * 64 + lane) * 16u,
-                     *reinterpret_cast<const u32x4*>(base + (i * IPR + q) * 1024));
-    }
-  };
-  auto step = [&](int b, char* slot) {
-    if (b >= nb) return;
-    if (b == 0) wait_vm<8>();
-    else wait_vm<16>();
-    barrier_only();  // no LDS data crosses waves; the barrier keeps the waves in step
-    store(b, slot);
-    dma(b + 2, slot);  // this wave's LDS reads of the slot completed with the stores above
-  };
-  if (nb > 0) {
-    dma(0, w0);
-    dma(1, w1);
-    for (int b = 0; b < nb; b += 2) {
-      step(b, w0);
-      step(b + 1, w1);
+      for (int q = 0; q < IPR; ++q) bstore16_sc1(dst, (uint32_t)(q * 64 + lane) * 16u, v[i][q]);
     }
   }
-  wait_vm<0>();
+  wait_mem();
   __syncthreads();
   if (wave == 0)
     for (int j = 0; j < n_win; ++j) moe_raise_chunk(p, sh, j, lane);
@@ -423,8 +424,7 @@ __device__ __forceinline__ void moe_copy_window(const MoeParams& p, const MoeSha
 // then all waves move the window's part of the rows.  With the default role split a workgroup's
 // rows span a few chunks: one window, one listing round trip and one pipeline fill and drain.
 template <int IPR>
-__device__ __forceinline__ void moe_dispatch(const MoeParams& p, int cid, MoeShared& sh, int2* list, char* lo0,
-                                             char* hi0, char* lo1, char* hi1) {
+__device__ __forceinline__ void moe_dispatch(const MoeParams& p, int cid, MoeShared& sh, int2* list) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int stride = 64 * min(p.top_k, p.n_local);  // room for a chunk's largest row count
   const int cw = max(1, min(MOE_WAVES, MOE_LIST / stride));
@@ -472,12 +472,11 @@ __device__ __forceinline__ void moe_dispatch(const MoeParams& p, int cid, MoeSha
       for (int j = 0; j < n_win; ++j) sh.pre[j + 1] = sh.pre[j] + sh.n_rows[j];
     }
     __syncthreads();
-    moe_copy_window<IPR>(p, sh, list, stride, n_win, lo0, hi0, lo1, hi1);  // ends with a barrier
+    moe_copy_window<IPR>(p, sh, list, stride, n_win);  // ends with a barrier
   }
 }
 
-__device__ __forceinline__ void moe_copy_role(const MoeParams& p, int cid, MoeShared& sh, int2* list, char* lo0,
-                                              char* hi0, char* lo1, char* hi1) {
+__device__ __forceinline__ void moe_copy_role(const MoeParams& p, int cid, MoeShared& sh, int2* list) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // route: chunks (cid * 8 + wave) + i * (n_copy * 8)
   const int c0 = cid * MOE_WAVES + wave, cs = p.n_copy * MOE_WAVES;
@@ -504,12 +503,12 @@ __device__ __forceinline__ void moe_copy_role(const MoeParams& p, int cid, MoeSh
   trace_mark(p.trace, 6);
   moe_load_segments(p, sh);
   __syncthreads();
-  // DMA instructions per row and wave, rounded up to a power of two (8 for hidden 4096)
+  // 1 KiB loads per row and wave, rounded up to a power of two (8 for hidden 4096)
   const int cpr = p.hidden >> 3;  // 16-byte pieces per row
-  if (cpr > 256) moe_dispatch<8>(p, cid, sh, list, lo0, hi0, lo1, hi1);
-  else if (cpr > 128) moe_dispatch<4>(p, cid, sh, list, lo0, hi0, lo1, hi1);
-  else if (cpr > 64) moe_dispatch<2>(p, cid, sh, list, lo0, hi0, lo1, hi1);
-  else moe_dispatch<1>(p, cid, sh, list, lo0, hi0, lo1, hi1);
+  if (cpr > 256) moe_dispatch<8>(p, cid, sh, list);
+  else if (cpr > 128) moe_dispatch<4>(p, cid, sh, list);
+  else if (cpr > 64) moe_dispatch<2>(p, cid, sh, list);
+  else moe_dispatch<1>(p, cid, sh, list);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -613,10 +612,9 @@ __device__ __forceinline__ void moe_compute_role(const MoeParams& p, int slot, c
 
 // The five GEMM slots fill the 160 KiB of LDS: the copy role's row list and the shared block sit in
 // the last B slot, which only the K loop uses (copy workgroups finish the dispatch before their
-// first tile; during a K loop no code touches sh).
+// first tile; during a K loop no code touches sh).  The dispatch moves rows through registers.
 constexpr int MOE_SH = MOE_LIST * (int)sizeof(int2);
 static_assert(MOE_SH + (int)sizeof(MoeShared) <= MoeTile::SLOT_B, "row list and shared block fit one B slot");
-static_assert(MOE_THREADS == 512, "ring slots: 8 waves x 8 KiB");
 
 __global__ __launch_bounds__(MOE_THREADS, 1) void moe_kernel(MoeParams p) {
   // 256-byte aligned: the swizzled B reads XOR bits 5-7 of the address
@@ -630,7 +628,7 @@ __global__ __launch_bounds__(MOE_THREADS, 1) void moe_kernel(MoeParams p) {
   const int wg = blockIdx.x;
   if (wg < p.n_copy) {
     trace_begin(p.trace, ROLE_COPY);
-    moe_copy_role(p, wg, sh, list, a0, a1, a2, b0);  // ring slots: a0 + a1 and a2 + b0
+    moe_copy_role(p, wg, sh, list);
     trace_mark(p.trace, 7);
     if (sh.ok) moe_gemm_tiles(p, sh, -1, a0, a1, a2, b0, b1);  // then help with leftover tiles
   } else {

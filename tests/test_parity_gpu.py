@@ -311,6 +311,33 @@ def test_moe_row_split_role_splits(ctx, n_copy):
     assert_exact(host(y)[:R], ref["y"].astype(np.float32), "y (integer)")
 
 
+@pytest.mark.parametrize("case", ["twelve_local_experts", "1032_chunks"])
+def test_moe_scan_wide(ctx, case):
+    """The scan's general paths: more local experts than waves (each wave scans several experts),
+    and more chunks than one load group or one pass of the arrival-order scan holds (the counts are
+    reloaded per pass and the order's rows are taken in several groups); bit-exact layout and
+    integer-exact grouped GEMM."""
+    from dataclasses import replace
+    from gpu_util import assert_exact, host, host_bits, log
+    mk = _mk()
+    if case == "twelve_local_experts":
+        s = replace(wl.MOE_SMALL, n_experts=24, expert_begin=6, n_local=12)
+    else:
+        s = replace(wl.MOE_SMALL, t_local=8256, hidden=64, ffn=64)
+    assert (s.n_local > 8) or (s.n_chunks > 1024)
+    d = wl.gen_moe(s, run=5, kind="int")
+    log(f"moe scan {case}: n_local={s.n_local} n_chunks={s.n_chunks}: launching")
+    st, topk, offs, segt, x, y = _run_moe(ctx, s, d, order=wl.moe_arrival_order(s, 2, "flat"))
+    assert st == mk.MK_OK
+    ref = oracle.moe_dispatch_gemm(d["tokens"], d["logits"], d["bias"], s.top_k, s.expert_begin, s.n_local, d["w_up"])
+    R = int(ref["seg_offsets"][-1])
+    assert_exact(host(topk), ref["topk_idx"], "topk_idx")
+    assert_exact(host(offs), ref["seg_offsets"], "seg_offsets")
+    assert_exact(host(segt)[:R], ref["seg_token"], "seg_token")
+    assert_exact(host_bits(x)[:R], ref["x_seg"], "x_seg")
+    assert_exact(host(y)[:R], ref["y"].astype(np.float32), "y (integer)")
+
+
 def test_moe_forced_routing(ctx):
     """Huge bias on experts 0 and 1: every token lands in both segments; the other local experts are empty."""
     from gpu_util import assert_close, assert_exact, host
