@@ -345,9 +345,46 @@ __device__ __forceinline__ void red_compute_role(const RedParams& p, int slot, c
     // runs its K loop, mostly L2 hits, undisturbed), and its epilogue then only adds P.  Measured
     // 2 % faster than splitting the XCDs between summing first and summing in the epilogue.
     const bool self_presum = has_owned && !p.is_rs && !p.emulated && p.n_reduce == 0 && first;
+    // The four-wave tile gives each wave one 32-row slab in its epilogue, 8 values of 4 per lane:
+    // the pre-sum of exactly those values is kept in registers (32 per lane) across the K loop
+    // instead of going to the output and back (the lane's slab positions are the epilogue's).
+    constexpr bool REG_PRESUM = !kCore16<T> && T::NW == 4 && T::FM == 1;
+    f32x4 ps[T::SLAB_Q];
     if (self_presum) {
-      red_sum_peers<T>(p, lr0, lr1, n0, n0 + cols_valid);
-      wait_mem();
+      if constexpr (REG_PRESUM) {
+        constexpr int C4 = T::WTN / 4, H = T::SLAB_Q / 2;
+        const size_t base = (size_t)m0 * p.n + n0;
+        // two halves of the lane's values, each with all its peers' loads in flight (112 registers)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          f32x4 t[H][MK_MAX_WORLD - 1];
+#pragma unroll
+          for (int pq = 0; pq < MK_MAX_WORLD - 1; ++pq) {
+            if (pq < p.world - 1) {  // (no `break`: it would keep t in memory)
+              const float* src = peer_src(p, pq) + base;
+#pragma unroll
+              for (int i = 0; i < H; ++i) {
+                const int idx = (h * H + i) * 64 + lane;
+                const int row = wm * T::WTM + idx / C4, col = wn * T::WTN + (idx % C4) * 4;
+                t[i][pq] = (row < rows_valid && col < cols_valid)
+                               ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + (size_t)row * p.n + col))
+                               : f32x4{0.f, 0.f, 0.f, 0.f};
+              }
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < H; ++i) {
+            f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int pq = 0; pq < MK_MAX_WORLD - 1; ++pq)
+              if (pq < p.world - 1) a += t[i][pq];
+            ps[h * H + i] = a;
+          }
+        }
+      } else {
+        red_sum_peers<T>(p, lr0, lr1, n0, n0 + cols_valid);
+        wait_mem();
+      }
     }
     if (p.a_ready) {  // A is produced in this launch (the MLP kernel's H): its rows must be complete
       if (tid == 0) *s_ok = spin_until_ge(p.a_ready + tm, p.a_ready_need, p.timeout_ticks, p.status);
@@ -417,10 +454,20 @@ __device__ __forceinline__ void red_compute_role(const RedParams& p, int slot, c
       const size_t base = (size_t)(m0 - own0) * p.n + n0;
       if (presum) {
         f32x4 t[Q];
+        bool in_regs = false;
+        if constexpr (REG_PRESUM) {
+          in_regs = self_presum;
+          if (in_regs) {
 #pragma unroll
-        for (int q = 0; q < Q; ++q)
-          t[q] = c[q] < cols_valid ? *reinterpret_cast<const f32x4*>(p.out + base + (size_t)r[q] * p.n + c[q])
-                                   : f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int q = 0; q < Q; ++q) t[q] = ps[q];
+          }
+        }
+        if (!in_regs) {
+#pragma unroll
+          for (int q = 0; q < Q; ++q)
+            t[q] = c[q] < cols_valid ? *reinterpret_cast<const f32x4*>(p.out + base + (size_t)r[q] * p.n + c[q])
+                                     : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
         for (int q = 0; q < Q; ++q)
           if (c[q] < cols_valid)  // the final value: nothing reads it back here
