@@ -21,7 +21,7 @@
 //           stream (the scan also lays out each arrival position's first row), a window of up to
 //           eight chunks at a time: each wave lists one chunk's routed (token, slot) rows, then
 //           all waves move the workgroup's part of them into their final slots of x_seg through
-//           registers, and once the window's rows are stored they are added to their m-tiles'
+//           LDS, and once the window's rows are stored they are added to their m-tiles'
 //           landed-row counters.  A copy workgroup with no chunks
 //           left joins the compute role on the tiles left over after every compute workgroup's
 //           first one.
@@ -357,24 +357,29 @@ __device__ __forceinline__ void moe_raise_chunk(const MoeParams& p, const MoeSha
   }
 }
 
-// The window's rows move global -> VGPRs -> global: wave w takes window rows w, w + 8, ...,
-// up to RW rows per round (RW * IPR 1 KiB loads, 128 VGPRs of data: the registers the grouped GEMM
-// uses later are free here), so a workgroup's ~32 rows of a default role split are all requested
-// at once and the dispatch costs one round trip to memory instead of one per LDS ring batch.
-// Source rows are read once (non-temporal); the stores are write-through (the grouped GEMM reads
-// x_seg from other XCDs).  Lanes past a row's end fall outside its buffer window.  The window's
-// chunks raise their m-tile counters after the last store: counter atomics inside the loop would
-// come in a data-dependent number.  An m-tile spans chunks from the whole token range, so under a
-// random arrival order it completes near the end of the dispatch either way.
+// Rows move global -> LDS (DMA) -> VGPRs -> global through two 64 KiB ring slots, each made of two
+// 32 KiB GEMM slots (waves 0-3 in the first, 4-7 in the second: s0 = lo0/hi0, s1 = lo1/hi1), as
+// in the AllGather copy: batch b gives wave w the window rows (8b + w) * RPB + i, i < RPB, each
+// IPR 1 KiB DMA instructions (RPB * IPR = 8 per wave and batch; lanes past a row's end fall
+// outside its buffer window).  Per batch and wave: 8 DMA loads and 8 stores, completing in issue
+// order, so batch b has landed at vmcnt <= 16 (8 for b = 0).  The window's chunks raise their
+// m-tile counters after the last store: counter atomics inside the loop would come in a
+// data-dependent number, and the compiler would then drain the whole pipeline before every LDS
+// read.  An m-tile spans chunks from the whole token range, so under a random arrival order it
+// completes near the end of the dispatch either way.
 template <int IPR>
 __device__ __forceinline__ void moe_copy_window(const MoeParams& p, const MoeShared& sh, const int2* list, int stride,
-                                                int n_win) {
-  constexpr int RW = 32 / IPR;
+                                                int n_win, char* lo0, char* hi0, char* lo1, char* hi1) {
+  constexpr int RPB = 8 / IPR;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  (void)tid;
   const int R = sh.pre[n_win];
+  const int nb = (R + 8 * RPB - 1) / (8 * RPB);
   const uint32_t row_b = (uint32_t)p.hidden * 2u;
-  // branch-free lookup (selects, a fixed unrolled scan) of window row r's list entry, or (-1, -1)
-  auto row_at = [&](int r) -> int2 {
+  // The lookups below are branch-free (selects, a fixed unrolled scan): a branch inside the copy
+  // loop made the compiler drain every outstanding DMA (vmcnt(0)) before each batch's LDS reads,
+  // as it could no longer tell that they read the other slot.
+  auto row_at = [&](int r) -> int2 {  // list entry of window row r, or (-1, -1)
     int j = 0;
 #pragma unroll
     for (int k = 1; k < MOE_WAVES; ++k) j += (k < n_win && sh.pre[k] <= r) ? 1 : 0;
@@ -392,24 +397,50 @@ __device__ __forceinline__ void moe_copy_window(const MoeParams& p, const MoeSha
     const bool ok = slot >= 0 && slot < p.capacity;
     return make_rsrc(p.x_seg + (ok ? (size_t)slot * p.hidden : (size_t)0), ok ? row_b : 0u);
   };
-  for (int r0 = 0; r0 < R; r0 += MOE_WAVES * RW) {
-    u32x4 v[RW][IPR];
-    int2 e[RW];
+  // this wave's 8 KiB of a ring slot
+  char* const w0 = (wave < 4 ? lo0 : hi0) + (wave & 3) * 8192;
+  char* const w1 = (wave < 4 ? lo1 : hi1) + (wave & 3) * 8192;
+  auto dma = [&](int b, char* base) {
 #pragma unroll
-    for (int i = 0; i < RW; ++i) {
-      e[i] = row_at(r0 + i * MOE_WAVES + wave);
-      const auto src = src_of(__builtin_amdgcn_readfirstlane(e[i].x));
+    for (int i = 0; i < RPB; ++i) {
+      const int2 e = row_at((b * 8 + wave) * RPB + i);
+      const auto src = src_of(__builtin_amdgcn_readfirstlane(e.x));
 #pragma unroll
-      for (int q = 0; q < IPR; ++q) v[i][q] = bload16_nt(src, (uint32_t)(q * 64 + lane) * 16u);
+      for (int q = 0; q < IPR; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            src, (__attribute__((address_space(3))) void*)(base + (i * IPR + q) * 1024), 16,
+            (uint32_t)(q * 64 + lane) * 16u, 0, 0, 0);
     }
+  };
+  auto store = [&](int b, const char* wbase) {
+    const char* base = wbase + lane * 16;
 #pragma unroll
-    for (int i = 0; i < RW; ++i) {
-      const auto dst = dst_of(__builtin_amdgcn_readfirstlane(e[i].y));
+    for (int i = 0; i < RPB; ++i) {
+      const int2 e = row_at((b * 8 + wave) * RPB + i);
+      const auto dst = dst_of(__builtin_amdgcn_readfirstlane(e.y));
 #pragma unroll
-      for (int q = 0; q < IPR; ++q) bstore16_sc1(dst, (uint32_t)(q * 64 + lane) * 16u, v[i][q]);
+      for (int q = 0; q < IPR; ++q)
+        bstore16_sc1(dst, (uint32_t)(q * 64 + lane) * 16u,
+                     *reinterpret_cast<const u32x4*>(base + (i * IPR + q) * 1024));
+    }
+  };
+  auto step = [&](int b, char* slot) {
+    if (b >= nb) return;
+    if (b == 0) wait_vm<8>();
+    else wait_vm<16>();
+    barrier_only();  // no LDS data crosses waves; the barrier keeps the waves in step
+    store(b, slot);
+    dma(b + 2, slot);  // this wave's LDS reads of the slot completed with the stores above
+  };
+  if (nb > 0) {
+    dma(0, w0);
+    dma(1, w1);
+    for (int b = 0; b < nb; b += 2) {
+      step(b, w0);
+      step(b + 1, w1);
     }
   }
-  wait_mem();
+  wait_vm<0>();
   __syncthreads();
   if (wave == 0)
     for (int j = 0; j < n_win; ++j) moe_raise_chunk(p, sh, j, lane);
@@ -424,7 +455,8 @@ __device__ __forceinline__ void moe_copy_window(const MoeParams& p, const MoeSha
 // then all waves move the window's part of the rows.  With the default role split a workgroup's
 // rows span a few chunks: one window, one listing round trip and one pipeline fill and drain.
 template <int IPR>
-__device__ __forceinline__ void moe_dispatch(const MoeParams& p, int cid, MoeShared& sh, int2* list) {
+__device__ __forceinline__ void moe_dispatch(const MoeParams& p, int cid, MoeShared& sh, int2* list, char* lo0,
+                                             char* hi0, char* lo1, char* hi1) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int stride = 64 * min(p.top_k, p.n_local);  // room for a chunk's largest row count
   const int cw = max(1, min(MOE_WAVES, MOE_LIST / stride));
@@ -472,11 +504,12 @@ __device__ __forceinline__ void moe_dispatch(const MoeParams& p, int cid, MoeSha
       for (int j = 0; j < n_win; ++j) sh.pre[j + 1] = sh.pre[j] + sh.n_rows[j];
     }
     __syncthreads();
-    moe_copy_window<IPR>(p, sh, list, stride, n_win);  // ends with a barrier
+    moe_copy_window<IPR>(p, sh, list, stride, n_win, lo0, hi0, lo1, hi1);  // ends with a barrier
   }
 }
 
-__device__ __forceinline__ void moe_copy_role(const MoeParams& p, int cid, MoeShared& sh, int2* list) {
+__device__ __forceinline__ void moe_copy_role(const MoeParams& p, int cid, MoeShared& sh, int2* list, char* lo0,
+                                              char* hi0, char* lo1, char* hi1) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // route: chunks (cid * 8 + wave) + i * (n_copy * 8)
   const int c0 = cid * MOE_WAVES + wave, cs = p.n_copy * MOE_WAVES;
@@ -503,12 +536,12 @@ __device__ __forceinline__ void moe_copy_role(const MoeParams& p, int cid, MoeSh
   trace_mark(p.trace, 6);
   moe_load_segments(p, sh);
   __syncthreads();
-  // 1 KiB loads per row and wave, rounded up to a power of two (8 for hidden 4096)
+  // DMA instructions per row and wave, rounded up to a power of two (8 for hidden 4096)
   const int cpr = p.hidden >> 3;  // 16-byte pieces per row
-  if (cpr > 256) moe_dispatch<8>(p, cid, sh, list);
-  else if (cpr > 128) moe_dispatch<4>(p, cid, sh, list);
-  else if (cpr > 64) moe_dispatch<2>(p, cid, sh, list);
-  else moe_dispatch<1>(p, cid, sh, list);
+  if (cpr > 256) moe_dispatch<8>(p, cid, sh, list, lo0, hi0, lo1, hi1);
+  else if (cpr > 128) moe_dispatch<4>(p, cid, sh, list, lo0, hi0, lo1, hi1);
+  else if (cpr > 64) moe_dispatch<2>(p, cid, sh, list, lo0, hi0, lo1, hi1);
+  else moe_dispatch<1>(p, cid, sh, list, lo0, hi0, lo1, hi1);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -612,9 +645,10 @@ __device__ __forceinline__ void moe_compute_role(const MoeParams& p, int slot, c
 
 // The five GEMM slots fill the 160 KiB of LDS: the copy role's row list and the shared block sit in
 // the last B slot, which only the K loop uses (copy workgroups finish the dispatch before their
-// first tile; during a K loop no code touches sh).  The dispatch moves rows through registers.
+// first tile; during a K loop no code touches sh).
 constexpr int MOE_SH = MOE_LIST * (int)sizeof(int2);
 static_assert(MOE_SH + (int)sizeof(MoeShared) <= MoeTile::SLOT_B, "row list and shared block fit one B slot");
+static_assert(MOE_THREADS == 512, "ring slots: 8 waves x 8 KiB");
 
 __global__ __launch_bounds__(MOE_THREADS, 1) void moe_kernel(MoeParams p) {
   // 256-byte aligned: the swizzled B reads XOR bits 5-7 of the address
@@ -628,7 +662,7 @@ __global__ __launch_bounds__(MOE_THREADS, 1) void moe_kernel(MoeParams p) {
   const int wg = blockIdx.x;
   if (wg < p.n_copy) {
     trace_begin(p.trace, ROLE_COPY);
-    moe_copy_role(p, wg, sh, list);
+    moe_copy_role(p, wg, sh, list, a0, a1, a2, b0);  // ring slots: a0 + a1 and a2 + b0
     trace_mark(p.trace, 7);
     if (sh.ok) moe_gemm_tiles(p, sh, -1, a0, a1, a2, b0, b1);  // then help with leftover tiles
   } else {
