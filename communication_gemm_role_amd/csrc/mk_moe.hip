@@ -22,9 +22,9 @@
 //           eight chunks at a time: each wave lists one chunk's routed (token, slot) rows, then
 //           all waves move the workgroup's part of them into their final slots of x_seg through
 //           LDS, and once the window's rows are stored they are added to their m-tiles'
-//           landed-row counters.  A copy workgroup with no chunks
-//           left joins the compute role on the tiles left over after every compute workgroup's
-//           first one.
+//           landed-row counters.  Once every copy workgroup has finished its dispatch, the copy
+//           workgroups join the compute role on the tiles left over after every compute
+//           workgroup's first one.
 //   compute after the scan flag, (m-tile, n-tile) jobs of the ragged grouped GEMM: an m-tile
 //           runs once all of its rows have landed; y[slot] = x_seg[slot] @ w_up[expert].
 // Route/copy workgroups never wait on compute workgroups, and have the lowest ids.  The
@@ -65,8 +65,9 @@ struct MoeShared {
 
 __device__ __forceinline__ uint32_t* moe_misc(const MoeParams& p) { return p.counters + p.off_misc; }
 // misc layout: [0] route-done arrivals, [1] exits, [2 .. 2+n_local] m-tile base per expert (prefix),
-// [MISC_TILE] next leftover GEMM tile
+// [MISC_TILE] next leftover GEMM tile, [MISC_DISP_DONE] copy workgroups done with their dispatch
 constexpr int MISC_TILE = 101;
+constexpr int MISC_DISP_DONE = 102;
 
 // ------------------------------------------------------------------------------------------
 // route (one wave per 64-token chunk)
@@ -664,6 +665,17 @@ __global__ __launch_bounds__(MOE_THREADS, 1) void moe_kernel(MoeParams p) {
     trace_begin(p.trace, ROLE_COPY);
     moe_copy_role(p, wg, sh, list, a0, a1, a2, b0);  // ring slots: a0 + a1 and a2 + b0
     trace_mark(p.trace, 7);
+    // Leftover GEMM tiles only once every copy workgroup has finished its dispatch: the m-tiles of
+    // the smallest experts complete early, and K loops started on them beside the dispatch slowed
+    // the dispatch of their XCDs' other copy workgroups (dispatch end 73 -> 61 us without them).
+    // Copy workgroups wait only on each other's dispatch, which waits on nothing but the scan.
+    if (sh.ok) {
+      if (threadIdx.x == 0) {
+        atomic_add_agent(moe_misc(p) + MISC_DISP_DONE, 1u);
+        sh.ok = spin_until_ge(moe_misc(p) + MISC_DISP_DONE, (uint32_t)p.n_copy, p.timeout_ticks, p.status);
+      }
+      __syncthreads();
+    }
     if (sh.ok) moe_gemm_tiles(p, sh, -1, a0, a1, a2, b0, b1);  // then help with leftover tiles
   } else {
     trace_begin(p.trace, ROLE_COMPUTE);
@@ -687,6 +699,7 @@ __global__ __launch_bounds__(MOE_THREADS, 1) void moe_kernel(MoeParams p) {
     for (int i = threadIdx.x; i < 2 + p.n_local + 1; i += MOE_THREADS)
       __hip_atomic_store(moe_misc(p) + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (threadIdx.x == 0) __hip_atomic_store(moe_misc(p) + MISC_TILE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) __hip_atomic_store(moe_misc(p) + MISC_DISP_DONE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
