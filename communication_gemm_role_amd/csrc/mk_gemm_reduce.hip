@@ -6,6 +6,7 @@
 // [M, N] output.  AllReduce: every rank ends with sum_j P_j.  ReduceScatter: rank r ends with
 // sum_j P_j on its own row slice only.  A tile of P enters the reduction right after its K loop,
 // inside the same launch.
+#include <type_traits>
 #include "mk_red_roles.hpp"
 
 namespace mk {
@@ -88,13 +89,170 @@ __global__ __launch_bounds__(RedBig::NW * 64, 1) void gemm_reduce_kernel16(RedPa
   gemm_reduce_body<RedBig>(p, a0, a1, a2, b0, b1, s, s + 1, s + 2);
 }
 
+// GEMM + AllReduce with resident peer partials on the four-wave tile, one tile per workgroup, in
+// eight waves: waves 0-3 run the tile's K loop and waves 4-7 stream the peers' partials of the same
+// tile beside it, wave 4 + w summing exactly the values that compute wave w holds in its epilogue
+// (one 32-row slab, SLAB_Q values of 4 per lane).  Every wave passes the same barriers, one per
+// k-step (the loop's trip count and conditions depend only on nk), so the peer stream and the K
+// loop pace each other; the barriers carry no memory fence, so each wave's loads stay in flight
+// across them (each wave waits for its own with vmcnt).  Peer q's values go in two halves
+// ("pairs" 2q and 2q + 1); pair j is requested one step before it is added.  After the loop the
+// sums reach the compute waves through the idle stage buffers.
+constexpr int AR_SPLIT_STAGES = 4;
+__global__ __launch_bounds__(2 * RedSkinny::NW * 64, 1) void gemm_ar_split_kernel(RedParams p) {
+  using T = RedSkinny;
+  static_assert(T::NW == 4 && T::FM == 1 && T::WN == 1 && T::WM == 4, "one 32-row slab per compute wave");
+  constexpr int S = AR_SPLIT_STAGES, D = T::A_INSTR + T::B_INSTR, Q = T::SLAB_Q, H = Q / 2, C4 = T::WTN / 4;
+  static_assert(Q == 8 && S * T::STAGE <= 160 * 1024, "layout");
+  __shared__ __attribute__((aligned(16))) char st0[T::STAGE];
+  __shared__ __attribute__((aligned(16))) char st1[T::STAGE];
+  __shared__ __attribute__((aligned(16))) char st2[T::STAGE];
+  __shared__ __attribute__((aligned(16))) char st3[T::STAGE];
+  static_assert(2 * Q * 64 * 16 <= T::STAGE, "two waves' sums fit one stage buffer");
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool comp = wave < T::NW;
+  const int cw = comp ? wave : wave - T::NW;  // the compute wave (slab) this wave works for
+  const int n_tiles = p.tiles_m * p.tiles_n, C = p.n_compute, slot = blockIdx.x;
+  const int rs = ((C & 7) == 0) ? (slot & 7) * (C >> 3) + (slot >> 3) : slot;
+  if (slot >= C || rs >= n_tiles) return;  // the whole workgroup (the launch gives every tile one)
+  trace_begin(p.trace, ROLE_COMPUTE);
+  const int tm = rs / p.tiles_n, tn = rs - tm * p.tiles_n;
+  const int m0 = tm * T::BM, n0 = tn * T::BN;
+  const int rows_valid = min(T::BM, p.m - m0), cols_valid = min(T::BN, p.n - n0);
+  const int nk = p.k >> 6;
+  const uint32_t lda_b = (uint32_t)p.k * 2u, ldb_b = (uint32_t)p.n * 2u;
+  T g;
+  g.init(cw, 0, lane, lda_b, ldb_b);
+  g.zero();
+  const char* a_tile = reinterpret_cast<const char*>(p.a + (size_t)m0 * p.k);
+  const uint32_t a_tile_bytes = (uint32_t)rows_valid * lda_b;
+  const char* b_col = reinterpret_cast<const char*>(p.b + n0);
+  const uint32_t b_col_bytes = ((uint32_t)p.k * (uint32_t)p.n - (uint32_t)n0) * 2u;
+  auto load = [&](int ks, char* st) {  // compute waves only
+    const uint32_t ca = (uint32_t)ks * 128u, rb = (uint32_t)ks * 64u * ldb_b;
+    g.dma_a(a_tile + ca, a_tile_bytes - ca, lda_b, st, cw);
+    g.dma_b(b_col + rb, b_col_bytes - rb, ldb_b, st, cw);
+  };
+  // the peers: value v of this lane is tile row 32 cw + (64 v + lane) / C4, column 4 ((64 v + lane) % C4)
+  const int n_pairs = 2 * (p.world - 1);
+  const size_t base = (size_t)m0 * p.n + n0;
+  f32x4 sum[Q], buf[2][H];
+#pragma unroll
+  for (int v = 0; v < Q; ++v) sum[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto issue = [&](int j, int half, f32x4(&b)[H]) {  // reduce waves: request pair j (half = j & 1)
+    const float* src = peer_src(p, j >> 1) + base;
+#pragma unroll
+    for (int i = 0; i < H; ++i) {
+      const int idx = (half * H + i) * 64 + lane, row = T::WTM * cw + idx / C4, col = (idx % C4) * 4;
+      b[i] = (row < rows_valid && col < cols_valid)
+                 ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + (size_t)row * p.n + col))
+                 : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  auto add = [&](int half, const f32x4(&b)[H]) {
+#pragma unroll
+    for (int i = 0; i < H; ++i) sum[half * H + i] += b[i];
+  };
+  // prologue: steps 0 .. S-2 requested, step 0 landed; pair 0 requested
+  if (comp) {
+#pragma unroll
+    for (int i = 0; i < S - 1; ++i)
+      if (i < nk) load(i, i == 0 ? st0 : i == 1 ? st1 : st2);
+    wait_steps<D>(min(S - 1, nk) - 1);
+  } else if (n_pairs > 0) {
+    issue(0, 0, buf[0]);
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  barrier_only();
+  trace_mark(p.trace, 5);
+  // step q (PAR = q & 1): compute waves request step q + S - 1 into the buffer step q - 1 read and
+  // run step q's MFMAs; reduce waves request pair q + 1 and add pair q
+  auto sub = [&](int q, auto par, char* cur, char* pf) {
+    constexpr int P0 = decltype(par)::value, P1 = 1 - P0;
+    if (q >= nk) return;
+    if (comp) {
+      if (q + S - 1 < nk) load(q + S - 1, pf);
+      g.mma(cur);
+      wait_steps<D>(max(0, min(S - 2, nk - 2 - q)));
+    } else {
+      const bool next = q + 1 < n_pairs;
+      if (next) issue(q + 1, P1, buf[P1]);
+      if (q < n_pairs) {
+        if (next) wait_vm<H>();
+        else wait_vm<0>();
+        add(P0, buf[P0]);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    barrier_only();
+  };
+  using Z = std::integral_constant<int, 0>;
+  using O = std::integral_constant<int, 1>;
+  for (int q = 0; q < nk; q += S) {
+    sub(q, Z{}, st0, st3);
+    sub(q + 1, O{}, st1, st0);
+    sub(q + 2, Z{}, st2, st1);
+    sub(q + 3, O{}, st3, st2);
+  }
+  trace_mark(p.trace, 6);  // the K loop is done
+  if (!comp) {
+    // pairs the loop did not reach: nk (already requested when nk < n_pairs), then the rest
+    if (nk < n_pairs) {
+      wait_vm<0>();
+      if (nk & 1) add(1, buf[1]);
+      else add(0, buf[0]);
+      for (int j = nk + 1; j < n_pairs; ++j) {
+        if (j & 1) {
+          issue(j, 1, buf[1]);
+          wait_vm<0>();
+          add(1, buf[1]);
+        } else {
+          issue(j, 0, buf[0]);
+          wait_vm<0>();
+          add(0, buf[0]);
+        }
+      }
+    }
+    // hand the sums to compute wave cw: (v, lane) at 16 (64 v + lane) of its area
+    float* area = reinterpret_cast<float*>((cw < 2 ? st2 : st3) + (cw & 1) * (Q * 64 * 16));
+#pragma unroll
+    for (int v = 0; v < Q; ++v) *reinterpret_cast<f32x4*>(area + (v * 64 + lane) * 4) = sum[v];
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  barrier_only();
+  if (comp) {
+    const float* area = reinterpret_cast<const float*>((cw < 2 ? st2 : st3) + (cw & 1) * (Q * 64 * 16));
+    g.epilogue_slab(st0, st1, cw, 0, lane, cw, [&](int srow, f32x4(&v)[Q], const int(&r)[Q], const int(&c)[Q]) {
+      (void)srow;
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        const f32x4 t = *reinterpret_cast<const f32x4*>(area + (q * 64 + lane) * 4);
+        if (r[q] < rows_valid && c[q] < cols_valid)  // the final value: nothing reads it back here
+          __builtin_nontemporal_store(v[q] + t, reinterpret_cast<f32x4*>(p.out + base + (size_t)r[q] * p.n + c[q]));
+      }
+    });
+  }
+  trace_end(p.trace);
+}
+
 template <class T>
 static hipError_t launch_t(const RedParams& p, int grid, hipStream_t s) {
   hipLaunchKernelGGL(gemm_reduce_kernel<T>, dim3(grid), dim3(T::NW * 64), 0, s, p);
   return hipGetLastError();
 }
 
+// The split AllReduce kernel serves resident AllReduce on the four-wave tile when every tile has its
+// own workgroup and there is no reduce role; everything else runs the role kernels.
+static bool ar_split(const RedParams& p, int grid) {
+  return !p.is_rs && !p.emulated && p.n_reduce == 0 && p.n_copy == 0 && !p.a_ready && p.world > 1 &&
+         (p.n_compute & 7) == 0 && p.n_compute <= grid && p.tiles_m * p.tiles_n <= p.n_compute;
+}
+
 hipError_t launch_gemm_reduce(const RedParams& p, int grid, hipStream_t s) {
+  if (red_skinny(p.m, p.n) && ar_split(p, grid)) {
+    hipLaunchKernelGGL(gemm_ar_split_kernel, dim3(grid), dim3(2 * RedSkinny::NW * 64), 0, s, p);
+    return hipGetLastError();
+  }
   if (red_skinny(p.m, p.n)) return launch_t<RedSkinny>(p, grid, s);
   hipLaunchKernelGGL(gemm_reduce_kernel16, dim3(grid), dim3(RedBig::NW * 64), 0, s, p);
   return hipGetLastError();
