@@ -41,6 +41,7 @@ constexpr int CTR_MLP_EXIT = 115;    // MLP workgroups that have exited
 constexpr int CTR_MLP_HREADY0 = 4096;  // MLP: up-projection tiles stored per 256-row block of H
 constexpr int CTR_RA_XITEM0 = 118;  // next leftover ring-attention item of each XCD's block, [8] from here
 constexpr int CTR_RA_EXIT = 117;  // ring-attention workgroups that have exited
+constexpr int CTR_RA_LANDED = 126;  // ring-attention copy workgroups that have landed all their blocks
 constexpr int RA_D = 128;         // ring attention: head dimension
 
 struct AgParams {

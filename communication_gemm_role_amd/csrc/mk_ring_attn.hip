@@ -196,6 +196,7 @@ __device__ __forceinline__ void ra_compute_role(const RaParams& p, int slot, cha
     t = j < z.n_static ? z.b + j : -1;
   }
   bool first = slot >= 0;
+  bool landed = false;  // every peer block has landed (this wave saw the copy role's counter)
   while (true) {
     if (t < 0) {
       if (tid == 0) *s_claim = ra_claim(p, x);
@@ -226,9 +227,16 @@ __device__ __forceinline__ void ra_compute_role(const RaParams& p, int slot, cha
     auto unit_of = [&](int q) {  // K unit of block q (V is the next one)
       return ((rank_of(q) * p.heads + h) * p.n_blk + q % p.n_blk) * 2;
     };
-    // every wave waits for the block's K and V itself, then requests its share of them
+    // every wave waits for the block's K and V itself, then requests its share of them; once
+    // every copy workgroup has landed all of its blocks (one counter, every lane reading the same
+    // address), the wave stops polling flags for good
     auto before_load = [&](int q) {
-      if (!p.emulated || rank_of(q) == p.rank) return;
+      if (!p.emulated || rank_of(q) == p.rank || landed) return;
+      if (p.drop_pos == 0 && p.n_copy > 0 &&
+          __builtin_amdgcn_readfirstlane(flag_load(p.counters + CTR_RA_LANDED) >= (uint32_t)p.n_copy ? 1 : 0)) {
+        landed = true;
+        return;
+      }
       const int u = unit_of(q);
       bool ok = true;
       if (lane == 0)
@@ -436,6 +444,9 @@ __global__ __launch_bounds__(RA_THREADS, 1) void ring_attn_kernel(RaParams p) {
     trace_begin(p.trace, ROLE_COPY);
     ra_copy_role(p, wg, st0, st1);
     trace_mark(p.trace, 5);
+    // every unit of this workgroup has been published (the copy ring raised each flag after its
+    // stores completed): count the workgroup as landed
+    if (threadIdx.x == 0) atomic_add_agent(p.counters + CTR_RA_LANDED, 1u);
     __syncthreads();  // the ring's LDS slots become stage buffers
     ra_compute_role(p, -1, st0, st1, st2, &s_claim);
   } else {
@@ -451,6 +462,7 @@ __global__ __launch_bounds__(RA_THREADS, 1) void ring_attn_kernel(RaParams p) {
     for (int xx = 0; xx < 8; ++xx)
       __hip_atomic_store(p.counters + CTR_RA_XITEM0 + xx, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(p.counters + CTR_RA_EXIT, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(p.counters + CTR_RA_LANDED, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
