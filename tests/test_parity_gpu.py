@@ -215,6 +215,22 @@ def test_ar_small(ctx, mode, n_reduce, rank, kind):
         assert_close(host(out), ref, "AR out")
 
 
+@pytest.mark.parametrize("world,rank,m,n,k", [(2, 1, 256, 2048, 192), (5, 3, 192, 1600, 576), (8, 0, 512, 8192, 256)])
+def test_ar_resident_world_and_tile_counts(ctx, world, rank, m, n, k):
+    """Resident AllReduce on the decode-like tile at other world sizes and tile counts: 2 and 5
+    ranks (one or four peers: the peer-streaming waves of the split workgroups take 2 and 8 peer
+    halves, fewer than the k-steps or not), and 512 tiles on the 256 workgroups (more tiles than
+    workgroups: the role kernel with leftover claims); integer inputs, so every sum is exact."""
+    from gpu_util import assert_exact, host, log
+    mk = _mk()
+    s = wl.RedShape(m=m, n=n, k=k, world=world, rank=rank, unit_rows=64, unit_cols=64, cfg=wl.CFG_AR)
+    d = wl.gen_reduce(s, "ar", run=2, kind="int")
+    log(f"ar resident world={world} rank={rank} m={m} n={n} k={k}: launching")
+    out, _ = _run_red(ctx, "ar", s, d, mk.MK_ARRIVAL_RESIDENT)
+    ref = oracle.gemm_ar(d["a"], d["b"], d["peers"], s.world, rank)
+    assert_exact(host(out), ref.astype(np.float32), "AR out")
+
+
 @pytest.mark.parametrize("mode", ["resident", "emulated"])
 def test_rs_full(ctx, mode):
     """The full down-projection GEMM + ReduceScatter (A 8192x1792, B 1792x4096, 7 peer partials),
