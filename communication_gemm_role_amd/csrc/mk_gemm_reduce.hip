@@ -96,9 +96,10 @@ __global__ __launch_bounds__(RedBig::NW * 64, 1) void gemm_reduce_kernel16(RedPa
 // k-step (the loop's trip count and conditions depend only on nk), so the peer stream and the K
 // loop pace each other; the barriers carry no memory fence, so each wave's loads stay in flight
 // across them (each wave waits for its own with vmcnt).  Peer q's values go in two halves
-// ("pairs" 2q and 2q + 1); pair j is requested one step before it is added.  After the loop the
-// sums reach the compute waves through the idle stage buffers.
-constexpr int AR_SPLIT_STAGES = 4;
+// ("pairs" 2q and 2q + 1); pair j is requested AR_PEER_AHEAD steps before it is added, into
+// register buffer j % 4.  After the loop the sums reach the compute waves through the idle stage
+// buffers.
+constexpr int AR_SPLIT_STAGES = 4, AR_PEER_AHEAD = 3;
 __global__ __launch_bounds__(2 * RedSkinny::NW * 64, 1) void gemm_ar_split_kernel(RedParams p) {
   using T = RedSkinny;
   static_assert(T::NW == 4 && T::FM == 1 && T::WN == 1 && T::WM == 4, "one 32-row slab per compute wave");
@@ -116,7 +117,9 @@ __global__ __launch_bounds__(2 * RedSkinny::NW * 64, 1) void gemm_ar_split_kerne
   const int rs = ((C & 7) == 0) ? (slot & 7) * (C >> 3) + (slot >> 3) : slot;
   if (slot >= C || rs >= n_tiles) return;  // the whole workgroup (the launch gives every tile one)
   trace_begin(p.trace, ROLE_COMPUTE);
-  const int tm = rs / p.tiles_n, tn = rs - tm * p.tiles_n;
+  // tiles in column order: an XCD's workgroups (consecutive rs) hold every tile row of their
+  // columns, so each B column block is read from memory once, by one XCD, at the same time
+  const int tn = rs / p.tiles_m, tm = rs - tn * p.tiles_m;
   const int m0 = tm * T::BM, n0 = tn * T::BN;
   const int rows_valid = min(T::BM, p.m - m0), cols_valid = min(T::BN, p.n - n0);
   const int nk = p.k >> 6;
@@ -136,7 +139,9 @@ __global__ __launch_bounds__(2 * RedSkinny::NW * 64, 1) void gemm_ar_split_kerne
   // the peers: value v of this lane is tile row 32 cw + (64 v + lane) / C4, column 4 ((64 v + lane) % C4)
   const int n_pairs = 2 * (p.world - 1);
   const size_t base = (size_t)m0 * p.n + n0;
-  f32x4 sum[Q], buf[2][H];
+  constexpr int LA = AR_PEER_AHEAD;
+  static_assert(LA >= 1 && LA <= 3, "pairs in flight fit the four buffers beside the one being added");
+  f32x4 sum[Q], buf[4][H];
 #pragma unroll
   for (int v = 0; v < Q; ++v) sum[v] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto issue = [&](int j, int half, f32x4(&b)[H]) {  // reduce waves: request pair j (half = j & 1)
@@ -153,66 +158,61 @@ __global__ __launch_bounds__(2 * RedSkinny::NW * 64, 1) void gemm_ar_split_kerne
 #pragma unroll
     for (int i = 0; i < H; ++i) sum[half * H + i] += b[i];
   };
-  // prologue: steps 0 .. S-2 requested, step 0 landed; pair 0 requested
+  // wait until pair q has landed while the pairs requested after it (at most LA) stay in flight
+  auto wait_pair = [&](int q) {
+    const int after = min(LA, n_pairs - 1 - q);
+    if (LA >= 3 && after >= 3) wait_vm<3 * H>();
+    else if (LA >= 2 && after == 2) wait_vm<2 * H>();
+    else if (after == 1) wait_vm<H>();
+    else wait_vm<0>();
+  };
+  // prologue: steps 0 .. S-2 requested, step 0 landed; pairs 0 .. LA-1 requested
   if (comp) {
 #pragma unroll
     for (int i = 0; i < S - 1; ++i)
       if (i < nk) load(i, i == 0 ? st0 : i == 1 ? st1 : st2);
     wait_steps<D>(min(S - 1, nk) - 1);
-  } else if (n_pairs > 0) {
-    issue(0, 0, buf[0]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < LA; ++j)
+      if (j < n_pairs) issue(j, j & 1, buf[j]);
   }
   __builtin_amdgcn_s_waitcnt(0xc07f);
   barrier_only();
   trace_mark(p.trace, 5);
-  // step q (PAR = q & 1): compute waves request step q + S - 1 into the buffer step q - 1 read and
-  // run step q's MFMAs; reduce waves request pair q + 1 and add pair q
-  auto sub = [&](int q, auto par, char* cur, char* pf) {
-    constexpr int P0 = decltype(par)::value, P1 = 1 - P0;
-    if (q >= nk) return;
+  // step q (R = q % 4): compute waves request step q + S - 1 into the buffer step q - 1 read and
+  // run step q's MFMAs; reduce waves request pair q + LA and add pair q.  The loop runs
+  // max(nk, n_pairs) steps, so a short K loop leaves no pair behind (every buffer index stays a
+  // constant: the buffers stay in registers).
+  const int n_steps = max(nk, n_pairs);
+  auto sub = [&](int q, auto r, char* cur, char* pf) {
+    constexpr int R = decltype(r)::value, RN = (R + LA) & 3;
+    if (q >= n_steps) return;
     if (comp) {
-      if (q + S - 1 < nk) load(q + S - 1, pf);
-      g.mma(cur);
-      wait_steps<D>(max(0, min(S - 2, nk - 2 - q)));
+      if (q < nk) {  // (past the K loop the compute waves only pass the barrier)
+        if (q + S - 1 < nk) load(q + S - 1, pf);
+        g.mma(cur);
+        wait_steps<D>(max(0, min(S - 2, nk - 2 - q)));
+      }
     } else {
-      const bool next = q + 1 < n_pairs;
-      if (next) issue(q + 1, P1, buf[P1]);
+      if (q + LA < n_pairs) issue(q + LA, RN & 1, buf[RN]);
       if (q < n_pairs) {
-        if (next) wait_vm<H>();
-        else wait_vm<0>();
-        add(P0, buf[P0]);
+        wait_pair(q);
+        add(R & 1, buf[R]);
       }
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);
     barrier_only();
   };
-  using Z = std::integral_constant<int, 0>;
-  using O = std::integral_constant<int, 1>;
-  for (int q = 0; q < nk; q += S) {
-    sub(q, Z{}, st0, st3);
-    sub(q + 1, O{}, st1, st0);
-    sub(q + 2, Z{}, st2, st1);
-    sub(q + 3, O{}, st3, st2);
+  static_assert(S == 4, "the stage buffers and the peer buffers rotate together");
+  for (int q = 0; q < n_steps; q += S) {
+    sub(q, std::integral_constant<int, 0>{}, st0, st3);
+    sub(q + 1, std::integral_constant<int, 1>{}, st1, st0);
+    sub(q + 2, std::integral_constant<int, 2>{}, st2, st1);
+    sub(q + 3, std::integral_constant<int, 3>{}, st3, st2);
   }
   trace_mark(p.trace, 6);  // the K loop is done
   if (!comp) {
-    // pairs the loop did not reach: nk (already requested when nk < n_pairs), then the rest
-    if (nk < n_pairs) {
-      wait_vm<0>();
-      if (nk & 1) add(1, buf[1]);
-      else add(0, buf[0]);
-      for (int j = nk + 1; j < n_pairs; ++j) {
-        if (j & 1) {
-          issue(j, 1, buf[1]);
-          wait_vm<0>();
-          add(1, buf[1]);
-        } else {
-          issue(j, 0, buf[0]);
-          wait_vm<0>();
-          add(0, buf[0]);
-        }
-      }
-    }
     // hand the sums to compute wave cw: (v, lane) at 16 (64 v + lane) of its area
     float* area = reinterpret_cast<float*>((cw < 2 ? st2 : st3) + (cw & 1) * (Q * 64 * 16));
 #pragma unroll
