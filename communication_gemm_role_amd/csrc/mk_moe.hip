@@ -512,8 +512,10 @@ __device__ __forceinline__ void moe_dispatch(const MoeParams& p, int cid, MoeSha
 __device__ __forceinline__ void moe_copy_role(const MoeParams& p, int cid, MoeShared& sh, int2* list, char* lo0,
                                               char* hi0, char* lo1, char* hi1) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // route: chunks (cid * 8 + wave) + i * (n_copy * 8)
-  const int c0 = cid * MOE_WAVES + wave, cs = p.n_copy * MOE_WAVES;
+  // route: chunks (wave * n_copy + cid) + i * (n_copy * 8), i.e. chunk c on workgroup c % n_copy:
+  // the chunks spread over every copy workgroup, at most one routing wave per SIMD while there are
+  // fewer than 4 n_copy chunks (the top-k insertion is VALU work)
+  const int c0 = wave * p.n_copy + cid, cs = p.n_copy * MOE_WAVES;
   switch (p.top_k) {
     case 1: moe_route_all<1>(p, c0, cs, lane); break;
     case 2: moe_route_all<2>(p, c0, cs, lane); break;
