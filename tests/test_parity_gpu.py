@@ -215,12 +215,14 @@ def test_ar_small(ctx, mode, n_reduce, rank, kind):
         assert_close(host(out), ref, "AR out")
 
 
-@pytest.mark.parametrize("world,rank,m,n,k", [(2, 1, 256, 2048, 192), (5, 3, 192, 1600, 576), (8, 0, 512, 8192, 256)])
+@pytest.mark.parametrize("world,rank,m,n,k", [(2, 1, 256, 2048, 192), (5, 3, 192, 1600, 576), (3, 2, 384, 960, 320),
+                                               (8, 6, 128, 640, 128), (8, 0, 512, 8192, 256)])
 def test_ar_resident_world_and_tile_counts(ctx, world, rank, m, n, k):
-    """Resident AllReduce on the decode-like tile at other world sizes and tile counts: 2 and 5
-    ranks (one or four peers: the peer-streaming waves of the split workgroups take 2 and 8 peer
-    halves, fewer than the k-steps or not), and 512 tiles on the 256 workgroups (more tiles than
-    workgroups: the role kernel with leftover claims); integer inputs, so every sum is exact."""
+    """Resident AllReduce on the decode-like tile at other world sizes and tile counts.  The split
+    workgroups' peer-streaming waves take 2 (world 2), 8 (world 5) and 4 (world 3) peer halves
+    against 3, 9 and 5 k-steps, and 14 halves against 2 k-steps (world 8, k = 128: the loop runs on
+    for the peers after the K loop ends); 512 tiles on the 256 workgroups use the role kernel with
+    leftover claims.  Integer inputs, so every sum is exact."""
     from gpu_util import assert_exact, host, log
     mk = _mk()
     s = wl.RedShape(m=m, n=n, k=k, world=world, rank=rank, unit_rows=64, unit_cols=64, cfg=wl.CFG_AR)
