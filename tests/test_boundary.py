@@ -257,7 +257,7 @@ def test_plan_moe(hostlib):
     code, p = moe(hostlib)
     assert code == MK_OK
     assert (p["n_tokens"], p["n_chunks"], p["tiles_n"]) == (32768, 512, 6)
-    assert (p["n_copy"], p["n_compute"]) == (224, 32)  # 7/8 of the workgroups route and dispatch
+    assert (p["n_copy"], p["n_compute"]) == (240, 16)  # 15/16 of the workgroups route and dispatch
     assert p["max_mtiles"] == 65536 // 128 + 8 + 1
     assert p["off_tile_cnt"] == 128 + 512 * 8 and p["counters_need"] <= NC
     assert moe(hostlib, top_k=65)[0] == INVALID
