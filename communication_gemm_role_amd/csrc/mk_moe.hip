@@ -550,14 +550,15 @@ __device__ __forceinline__ void moe_copy_role(const MoeParams& p, int cid, MoeSh
 // ------------------------------------------------------------------------------------------
 // compute role: ragged grouped GEMM
 // ------------------------------------------------------------------------------------------
-// Grouped-GEMM tiles: `first` (a static tile of this workgroup, or -1), then leftover tiles
-// n_compute, n_compute + 1, ... claimed from a shared counter by every workgroup that has finished
-// its own work (compute workgroups after their static tile, copy workgroups after the dispatch).
-// The K loop runs over five LDS slots (a0..a2: A, b0, b1: B); sh lives in b1 (see moe_kernel),
-// so only sh.claim and sh.ok are used here, between K loops, and the segment table is read from
-// global memory (the scan's output) for every tile.
-__device__ __forceinline__ void moe_gemm_tiles(const MoeParams& p, MoeShared& sh, int first, char* a0, char* a1,
-                                               char* a2, char* b0, char* b1) {
+// Grouped-GEMM tiles: `first` (a compute workgroup's static tile, a copy workgroup's first
+// leftover tile claimed ahead, or -1), then leftover tiles n_compute, n_compute + 1, ... claimed
+// from a shared counter by every workgroup that has finished its own work (compute workgroups
+// after their static tile, copy workgroups after the dispatch); mark_first: trace the first
+// tile's start.  The K loop runs over five LDS slots (a0..a2: A, b0, b1: B); sh lives in b1 (see
+// moe_kernel), so only sh.claim and sh.ok are used here, between K loops, and the segment table
+// is read once from global memory (the scan's output).
+__device__ __forceinline__ void moe_gemm_tiles(const MoeParams& p, MoeShared& sh, int first, bool mark_first,
+                                               char* a0, char* a1, char* a2, char* b0, char* b1) {
   using G = MoeTile;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   G g;
@@ -569,8 +570,14 @@ __device__ __forceinline__ void moe_gemm_tiles(const MoeParams& p, MoeShared& sh
   // is 0), written by the scan before its flag
   const auto so = make_rsrc(p.seg_offsets, (uint32_t)(p.n_local + 1) * 4u);
   const auto tb = make_rsrc(moe_misc(p) + 2, (uint32_t)(p.n_local + 1) * 4u);
+  // the segment table is fixed for the launch: read once
+  const bool in = lane < p.n_local;
+  const int seg_n = in ? (int)bload4_sc1(so, (uint32_t)(lane + 1) * 4u) : 0;
+  const int tb_n = in ? (int)bload4_sc1(tb, (uint32_t)(lane + 1) * 4u) : 0;
+  const int n_mt = __builtin_amdgcn_readlane(tb_n, p.n_local - 1);
+  const int n_tiles = n_mt * p.tiles_n;
   int t = first;
-  bool traced = false;
+  bool traced = !mark_first;
   while (true) {
     if (t < 0) {
       __syncthreads();  // every thread has read the last claim
@@ -578,11 +585,6 @@ __device__ __forceinline__ void moe_gemm_tiles(const MoeParams& p, MoeShared& sh
       __syncthreads();
       t = sh.claim;
     }
-    const bool in = lane < p.n_local;
-    const int seg_n = in ? (int)bload4_sc1(so, (uint32_t)(lane + 1) * 4u) : 0;
-    const int tb_n = in ? (int)bload4_sc1(tb, (uint32_t)(lane + 1) * 4u) : 0;
-    const int n_mt = __builtin_amdgcn_readlane(tb_n, p.n_local - 1);
-    const int n_tiles = n_mt * p.tiles_n;
     if (t >= n_tiles) break;
     const int gm = t / p.tiles_n, tn = t - gm * p.tiles_n;
     t = -1;
@@ -603,7 +605,7 @@ __device__ __forceinline__ void moe_gemm_tiles(const MoeParams& p, MoeShared& sh
       sh.ok = spin_until_ge(p.counters + p.off_tile_cnt + gm, (uint32_t)rows_valid, p.timeout_ticks, p.status);
     __syncthreads();
     if (!sh.ok) return;
-    if (first >= 0 && !traced) trace_mark(p.trace, 5);  // a compute workgroup's static tile is ready
+    if (!traced) trace_mark(p.trace, 5);  // a compute workgroup's static tile is ready
     traced = true;
     const char* a_tile = reinterpret_cast<const char*>(p.x_seg + (size_t)row0 * p.hidden);
     const uint32_t a_tile_bytes = (uint32_t)rows_valid * lda_b;
@@ -643,7 +645,7 @@ __device__ __forceinline__ void moe_compute_role(const MoeParams& p, int slot, c
   // m-tile, so the same A rows) go to one XCD
   const int C = p.n_compute;
   const int rs = ((C & 7) == 0) ? (slot & 7) * (C >> 3) + (slot >> 3) : slot;
-  moe_gemm_tiles(p, sh, rs, a0, a1, a2, b0, b1);
+  moe_gemm_tiles(p, sh, rs, true, a0, a1, a2, b0, b1);
 }
 
 // The five GEMM slots fill the 160 KiB of LDS: the copy role's row list and the shared block sit in
@@ -671,14 +673,17 @@ __global__ __launch_bounds__(MOE_THREADS, 1) void moe_kernel(MoeParams p) {
     // the smallest experts complete early, and K loops started on them beside the dispatch slowed
     // the dispatch of their XCDs' other copy workgroups (dispatch end 73 -> 61 us without them).
     // Copy workgroups wait only on each other's dispatch, which waits on nothing but the scan.
+    // The first leftover tile is claimed before the wait (a claim starts no K loop), so that past
+    // the wait only the tile's own row count stands between a workgroup and its K loop.
     if (sh.ok) {
       if (threadIdx.x == 0) {
         atomic_add_agent(moe_misc(p) + MISC_DISP_DONE, 1u);
+        sh.claim = p.n_compute + (int)atomic_add_agent(moe_misc(p) + MISC_TILE, 1u);
         sh.ok = spin_until_ge(moe_misc(p) + MISC_DISP_DONE, (uint32_t)p.n_copy, p.timeout_ticks, p.status);
       }
       __syncthreads();
     }
-    if (sh.ok) moe_gemm_tiles(p, sh, -1, a0, a1, a2, b0, b1);  // then help with leftover tiles
+    if (sh.ok) moe_gemm_tiles(p, sh, sh.claim, false, a0, a1, a2, b0, b1);  // then help with leftover tiles
   } else {
     trace_begin(p.trace, ROLE_COMPUTE);
     if (wg - p.n_copy < p.n_compute) moe_compute_role(p, wg - p.n_copy, a0, a1, a2, b0, b1, sh);
