@@ -550,11 +550,10 @@ __device__ __forceinline__ void moe_copy_role(const MoeParams& p, int cid, MoeSh
 // ------------------------------------------------------------------------------------------
 // compute role: ragged grouped GEMM
 // ------------------------------------------------------------------------------------------
-// Grouped-GEMM tiles: `first` (a compute workgroup's static tile, a copy workgroup's first
-// leftover tile claimed ahead, or -1), then leftover tiles n_compute, n_compute + 1, ... claimed
-// from a shared counter by every workgroup that has finished its own work (compute workgroups
-// after their static tile, copy workgroups after the dispatch); mark_first: trace the first
-// tile's start.  The K loop runs over five LDS slots (a0..a2: A, b0, b1: B); sh lives in b1 (see
+// Grouped-GEMM tiles: `first` (a compute workgroup's static tile, or -1), then leftover tiles
+// n_compute, n_compute + 1, ... claimed from a shared counter by every workgroup that has finished
+// its own work (compute workgroups after their static tile, copy workgroups after the dispatch);
+// mark_first: trace the first tile's start.  The K loop runs over five LDS slots (a0..a2: A, b0, b1: B); sh lives in b1 (see
 // moe_kernel), so only sh.claim and sh.ok are used here, between K loops, and the segment table
 // is read once from global memory (the scan's output).
 __device__ __forceinline__ void moe_gemm_tiles(const MoeParams& p, MoeShared& sh, int first, bool mark_first,
@@ -673,17 +672,14 @@ __global__ __launch_bounds__(MOE_THREADS, 1) void moe_kernel(MoeParams p) {
     // the smallest experts complete early, and K loops started on them beside the dispatch slowed
     // the dispatch of their XCDs' other copy workgroups (dispatch end 73 -> 61 us without them).
     // Copy workgroups wait only on each other's dispatch, which waits on nothing but the scan.
-    // The first leftover tile is claimed before the wait (a claim starts no K loop), so that past
-    // the wait only the tile's own row count stands between a workgroup and its K loop.
     if (sh.ok) {
       if (threadIdx.x == 0) {
         atomic_add_agent(moe_misc(p) + MISC_DISP_DONE, 1u);
-        sh.claim = p.n_compute + (int)atomic_add_agent(moe_misc(p) + MISC_TILE, 1u);
         sh.ok = spin_until_ge(moe_misc(p) + MISC_DISP_DONE, (uint32_t)p.n_copy, p.timeout_ticks, p.status);
       }
       __syncthreads();
     }
-    if (sh.ok) moe_gemm_tiles(p, sh, sh.claim, false, a0, a1, a2, b0, b1);  // then help with leftover tiles
+    if (sh.ok) moe_gemm_tiles(p, sh, -1, false, a0, a1, a2, b0, b1);  // then help with leftover tiles
   } else {
     trace_begin(p.trace, ROLE_COMPUTE);
     if (wg - p.n_copy < p.n_compute) moe_compute_role(p, wg - p.n_copy, a0, a1, a2, b0, b1, sh);
