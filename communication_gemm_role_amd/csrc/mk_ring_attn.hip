@@ -135,6 +135,14 @@ __device__ __forceinline__ void ra_lanes(RaLanes& L, int lane, int wave) {
 }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// The value lane l ^ 32 holds: one swap of the wave's two halves (v_permlane32_swap, a VALU
+// instruction) instead of a permute through the LDS unit, which the block's operand reads keep busy.
+__device__ __forceinline__ float ra_xor32(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);  // {this half, the other half}
+  return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
+}
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // Two softmax weights as packed bf16 hi and lo terms: hi = bf16(p), lo = bf16(p - hi), both
@@ -308,7 +316,7 @@ __device__ __forceinline__ void ra_compute_role(const RaParams& p, int slot, cha
       float mx = -__builtin_inff();
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+      mx = fmaxf(mx, ra_xor32(mx)) * c;
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       float sum = 0.f;
@@ -317,7 +325,7 @@ __device__ __forceinline__ void ra_compute_role(const RaParams& p, int slot, cha
         sc[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], c, -m_new));
         sum += sc[r];
       }
-      sum += __shfl_xor(sum, 32);
+      sum += ra_xor32(sum);
       l_run = l_run * alpha + sum;
       m_run = m_new;
       // rescale only when some query's running max moved (alpha == 1 everywhere else: a no-op); after
