@@ -64,6 +64,24 @@ struct MoeShared {
 };
 
 __device__ __forceinline__ uint32_t* moe_misc(const MoeParams& p) { return p.counters + p.off_misc; }
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4 and 8 lanes inside each row
+// of 16, then row 0's last lane added to row 1 and row 2's to row 3, then lane 31 added to rows 2
+// and 3 (DPP row shifts and row broadcasts: VALU instructions, where a lane shuffle would be a
+// permute through the LDS unit).  Lanes whose source falls outside add 0.
+__device__ __forceinline__ uint32_t wave_scan_incl(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1, 3
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2, 3
+  return x;
+}
+// the sum over the wave's lanes, in every lane
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_scan_incl(x), 63);
+}
 // misc layout: [0] route-done arrivals, [1] exits, [2 .. 2+n_local] m-tile base per expert (prefix),
 // [MISC_TILE] next leftover GEMM tile, [MISC_DISP_DONE] copy workgroups done with their dispatch
 constexpr int MISC_TILE = 101;
@@ -133,9 +151,7 @@ __device__ __forceinline__ void moe_route_chunk(const MoeParams& p, int chunk, i
   }
   const auto cr = make_rsrc(p.counters + p.off_chunk_cnt + (size_t)chunk * p.n_local, (uint32_t)p.n_local * 4u);
   bstore4_sc1(cr, (uint32_t)lane * 4u, mine);  // lanes past n_local fall outside the window
-  uint32_t tot = mine;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o);
+  const uint32_t tot = wave_sum(mine);
   const auto rr = make_rsrc(p.counters + p.off_chunk_rows + chunk, 4u);
   if (lane == 0) bstore4_sc1(rr, 0u, tot);
 }
@@ -181,8 +197,7 @@ __device__ __forceinline__ void moe_scan(const MoeParams& p, MoeShared& sh) {
       uint32_t s = 0;
 #pragma unroll
       for (int i = 0; i < 16; ++i) s += vr[i];
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+      s = wave_sum(s);
       if (lane == 0) sh.totals[wave] = (int)s;
     }
   } else {
@@ -194,8 +209,7 @@ __device__ __forceinline__ void moe_scan(const MoeParams& p, MoeShared& sh) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) s += v[i];
       }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+      s = wave_sum(s);
       if (lane == 0) sh.totals[el] = (int)s;
     }
   }
@@ -217,15 +231,10 @@ __device__ __forceinline__ void moe_scan(const MoeParams& p, MoeShared& sh) {
   auto scan_group = [&](int el, int g0, const uint32_t(&v)[16], uint32_t& run) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      uint32_t inc = v[i];
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(inc, o);
-        if (lane >= o) inc += y;
-      }
+      const uint32_t inc = wave_scan_incl(v[i]);
       const uint32_t c = (uint32_t)(g0 + i * 64 + lane);
       bstore4_sc1(cr, (c * (uint32_t)p.n_local + (uint32_t)el) * 4u, run + inc - v[i]);  // past the end: dropped
-      run += __shfl(inc, 63);
+      run += (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
     }
   };
   if (in_regs) {
@@ -257,12 +266,7 @@ __device__ __forceinline__ void moe_scan(const MoeParams& p, MoeShared& sh) {
     for (int base = 0; base < p.n_chunks; base += MOE_THREADS) {
       const int i = base + tid;
       const uint32_t v = one_pos ? rows0 : rows_at(i);
-      uint32_t inc = v;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(inc, o);
-        if (lane >= o) inc += y;
-      }
+      const uint32_t inc = wave_scan_incl(v);
       if (lane == 63) sh.pre[wave] = (int)inc;  // wave totals
       __syncthreads();
       uint32_t wpre = 0, btot = 0;
@@ -337,12 +341,7 @@ __device__ __forceinline__ void moe_list_chunk(const MoeParams& p, MoeShared& sh
 // expert el's rows are entries [cum, cum + cnt) with cum the rows of the experts before it.
 __device__ __forceinline__ void moe_raise_chunk(const MoeParams& p, const MoeShared& sh, int j, int lane) {
   const int cnt = lane < p.n_local ? sh.chunk_cnt[j][lane] : 0;
-  int inc = cnt;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(inc, o);
-    if (lane >= o) inc += y;
-  }
+  const int inc = (int)wave_scan_incl((uint32_t)cnt);
   const int cum = inc - cnt;
   const int a = max(sh.lo[j], cum), b = min(sh.lo[j] + sh.n_rows[j], cum + cnt);
   if (lane >= p.n_local || b <= a) return;
