@@ -93,8 +93,8 @@ __global__ __launch_bounds__(RedBig::NW * 64, 1) void gemm_reduce_kernel16(RedPa
 // eight waves: waves 0-3 run the tile's K loop and waves 4-7 stream the peers' partials of the same
 // tile beside it, wave 4 + w summing exactly the values that compute wave w holds in its epilogue
 // (one 32-row slab, SLAB_Q values of 4 per lane).  Every wave passes the same barriers, one per
-// k-step (the loop's trip count and conditions depend only on nk), so the peer stream and the K
-// loop pace each other; the barriers carry no memory fence, so each wave's loads stay in flight
+// step (the loop's trip count and conditions depend only on nk and the peer count), so the peer
+// stream and the K loop pace each other; the barriers carry no memory fence, so each wave's loads stay in flight
 // across them (each wave waits for its own with vmcnt).  Peer q's values go in two halves
 // ("pairs" 2q and 2q + 1); pair j is requested AR_PEER_AHEAD steps before it is added, into
 // register buffer j % 4.  After the loop the sums reach the compute waves through the idle stage
